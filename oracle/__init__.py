@@ -1,0 +1,186 @@
+"""fp64 CPU oracle of the dynamic short convolution (test infrastructure only).
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports, loads or calls it, and the two share no
+code.  The arithmetic lives in ``dsc_oracle.c`` (plain C, double precision,
+direct summation); this module only compiles it with gcc and marshals numpy
+arrays through ctypes.
+
+Definitions followed ("Dynamic Short Convolutions Improve Transformers",
+gist.science technical summary, Methodology): the output is the sum over
+taps k < W of w(t)_k times x_{t-k}, elementwise over channels; w(t) is either
+shared by H consecutive channels (head-wise tying) or w(t) = z_t U (low rank
+R); placement with residual X + conv(X).  Causal zero padding per sequence
+follows the authors' thread (digg.com, "Custom Triton GPU kernels maintain
+wall-clock training efficiency"): the static short convolution being
+generalised is causal.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dsc_oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(out_path: str = LIB_PATH, extra_flags: tuple[str, ...] = ()) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP).  Returns the library path."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", *extra_flags,
+           _SRC, "-o", out_path + ".tmp"]
+    subprocess.run(cmd, check=True)
+    os.replace(out_path + ".tmp", out_path)
+    return out_path
+
+
+def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
+    i64, i32, p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    lib.oracle_abi_version.restype = ctypes.c_int
+    lib.oracle_headwise_fwd.argtypes = [i64, i64, i64, i32, i32, p, p, p, i32, i32, i64, i64, p]
+    lib.oracle_headwise_bwd.argtypes = [i64, i64, i64, i32, i32, p, p, p, p, i32, i32, i64, i64, p, p]
+    lib.oracle_lowrank_fwd.argtypes = [i64, i64, i64, i32, i32, p, p, p, p, i32, i32, i64, i64, p]
+    lib.oracle_lowrank_bwd.argtypes = [i64, i64, i64, i32, i32, p, p, p, p, p, i32, i32, i64, i64,
+                                       p, p, i64, i64, p]
+    for name in ("oracle_headwise_fwd", "oracle_headwise_bwd", "oracle_lowrank_fwd",
+                 "oracle_lowrank_bwd"):
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load (building first if absent) the oracle library."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        _lib = _bind(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _cu(cu_seqlens):
+    if cu_seqlens is None:
+        return None, 0
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    return cu, len(cu) - 1
+
+
+def _check(rc: int, name: str) -> None:
+    if rc != 0:
+        raise ValueError(f"{name} failed with code {rc}")
+
+
+class Oracle:
+    """numpy front end of one oracle library (the default one or a variant)."""
+
+    def __init__(self, lib: ctypes.CDLL | None = None):
+        self.lib = lib if lib is not None else load()
+
+    def headwise_fwd(self, x, w, *, cu_seqlens=None, residual=False, rows=None):
+        """x (B,T,D), w (B,T,D/H,W) -> y (rows, D) for token rows [lo, hi) of B*T (default all)."""
+        x, w = _f64(x), _f64(w)
+        B, T, D = x.shape
+        G, W = w.shape[2], w.shape[3]
+        if G < 1 or D % G:
+            raise ValueError(f"filter groups {G} do not divide D={D}")
+        H = D // G
+        lo, hi = rows if rows is not None else (0, B * T)
+        cu, ns = _cu(cu_seqlens)
+        y = np.empty((hi - lo, D))
+        _check(self.lib.oracle_headwise_fwd(B, T, D, W, H, _ptr(x), _ptr(w), _ptr(cu), ns,
+                                            int(bool(residual)), lo, hi, _ptr(y)), "headwise_fwd")
+        return y.reshape(B, T, D) if rows is None else y
+
+    def headwise_bwd(self, x, w, dy, *, cu_seqlens=None, residual=False, rows=None):
+        """-> (dx, dw) with dx (B,T,D) and dw (B,T,G,W), or compact rows."""
+        x, w, dy = _f64(x), _f64(w), _f64(dy)
+        B, T, D = x.shape
+        G, W = w.shape[2], w.shape[3]
+        if G < 1 or D % G:
+            raise ValueError(f"filter groups {G} do not divide D={D}")
+        H = D // G
+        lo, hi = rows if rows is not None else (0, B * T)
+        cu, ns = _cu(cu_seqlens)
+        dx = np.empty((hi - lo, D))
+        dw = np.empty((hi - lo, G, W))
+        _check(self.lib.oracle_headwise_bwd(B, T, D, W, H, _ptr(x), _ptr(w), _ptr(dy), _ptr(cu), ns,
+                                            int(bool(residual)), lo, hi, _ptr(dx), _ptr(dw)),
+               "headwise_bwd")
+        if rows is None:
+            return dx.reshape(B, T, D), dw.reshape(B, T, G, W)
+        return dx, dw
+
+    def lowrank_fwd(self, x, z, U, W, *, cu_seqlens=None, residual=False, rows=None):
+        """x (B,T,D), z (B,T,R), U (R, D*W) -> y."""
+        x, z, U = _f64(x), _f64(z), _f64(U)
+        B, T, D = x.shape
+        R = z.shape[2]
+        assert U.shape == (R, D * W)
+        lo, hi = rows if rows is not None else (0, B * T)
+        cu, ns = _cu(cu_seqlens)
+        y = np.empty((hi - lo, D))
+        _check(self.lib.oracle_lowrank_fwd(B, T, D, W, R, _ptr(x), _ptr(z), _ptr(U), _ptr(cu), ns,
+                                           int(bool(residual)), lo, hi, _ptr(y)), "lowrank_fwd")
+        return y.reshape(B, T, D) if rows is None else y
+
+    def lowrank_bwd(self, x, z, U, dy, W, *, cu_seqlens=None, residual=False, rows=None,
+                    channels=None):
+        """-> (dx, dz, dU); dx/dz over token rows, dU (R, (d_hi-d_lo)*W) over channels."""
+        x, z, U, dy = _f64(x), _f64(z), _f64(U), _f64(dy)
+        B, T, D = x.shape
+        R = z.shape[2]
+        assert U.shape == (R, D * W)
+        lo, hi = rows if rows is not None else (0, B * T)
+        dlo, dhi = channels if channels is not None else (0, D)
+        cu, ns = _cu(cu_seqlens)
+        dx = np.empty((hi - lo, D))
+        dz = np.empty((hi - lo, R))
+        dU = np.empty((R, (dhi - dlo) * W))
+        _check(self.lib.oracle_lowrank_bwd(B, T, D, W, R, _ptr(x), _ptr(z), _ptr(U), _ptr(dy),
+                                           _ptr(cu), ns, int(bool(residual)), lo, hi, _ptr(dx),
+                                           _ptr(dz), dlo, dhi, _ptr(dU)), "lowrank_bwd")
+        if rows is None:
+            return dx.reshape(B, T, D), dz.reshape(B, T, R), dU
+        return dx, dz, dU
+
+
+_default: Oracle | None = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def headwise_fwd(*a, **k):
+    return default().headwise_fwd(*a, **k)
+
+
+def headwise_bwd(*a, **k):
+    return default().headwise_bwd(*a, **k)
+
+
+def lowrank_fwd(*a, **k):
+    return default().lowrank_fwd(*a, **k)
+
+
+def lowrank_bwd(*a, **k):
+    return default().lowrank_bwd(*a, **k)

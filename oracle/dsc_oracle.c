@@ -1,0 +1,224 @@
+/*
+ * dsc_oracle.c -- plain, slow, fp64 CPU reference of the dynamic short
+ * convolution (forward and backward, head-wise tied and low-rank filters).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no source, header, table or helper
+ * with the HIP library.
+ *
+ * Source of the definitions ("Dynamic Short Convolutions Improve
+ * Transformers", the gist.science technical summaries, es/fr/de/hi):
+ *   - Methodology, "mechanism": for activations x_t the output is the sum
+ *     over taps k = 0..W-1 of w(t)_k (elementwise) x_{t-k}; the filter w(t)
+ *     depends on the token t.
+ *   - Methodology, "parametrization": (1) low-rank factorisation of rank R,
+ *     read as w(t) = z_t U with U of shape (R, D*W); (2) head-wise tying,
+ *     one filter shared by H consecutive channels.
+ *   - Methodology, "placement": residual form X = X + dynamicShortConv(X).
+ * and the authors' thread ("Custom Triton GPU kernels maintain wall-clock
+ * training efficiency", digg.com): the static short convolution being
+ * generalised is depthwise and causal, so x before a sequence start is zero.
+ *
+ * Readings where the pages are silent (each listed in the design notes):
+ *   - tap k = 0 multiplies the current token x_t;
+ *   - x_{t-k} is zero when t-k lies before the first token of t's segment
+ *     (zero left padding per sequence; packed sequences reset causally);
+ *   - channel d uses head-wise filter j = floor(d / H);
+ *   - w has layout (B,T,D/H,W), tap innermost; U is (R, D*W) read as
+ *     (R, D, W), i.e. column d*W + k;
+ *   - no nonlinearity, normalisation or bias is applied to w.
+ * The backward pass is the chain rule of the forward definition for
+ * L = <dy, y>; it is written out directly below.
+ *
+ * Every value is held and accumulated in double.  OpenMP parallelises over
+ * output rows (or dU columns); each output element is a sequential sum in a
+ * fixed order, so results do not depend on the thread count.
+ *
+ * All functions return 0 on success, -1 on allocation failure and -2 on an
+ * invalid argument.  Row outputs cover tokens [n_lo, n_hi) only and are
+ * stored compactly (row n goes to row n - n_lo of the output); dU covers
+ * channels [d_lo, d_hi) only, stored as (R, (d_hi-d_lo)*W).
+ */
+#include <stdint.h>
+#include <stdlib.h>
+
+#define ORACLE_ABI_VERSION 1
+
+int oracle_abi_version(void) { return ORACLE_ABI_VERSION; }
+
+/* First token of the segment of every flattened token n in [0, B*T).
+ * Without cu_seqlens each of the B rows is one sequence; otherwise
+ * cu_seqlens[0..n_seqs] are increasing offsets from 0 to B*T. */
+static int64_t *segment_starts(int64_t B, int64_t T, const int32_t *cu_seqlens, int32_t n_seqs)
+{
+    int64_t N = B * T;
+    int64_t *seg = (int64_t *)malloc((size_t)(N > 0 ? N : 1) * sizeof *seg);
+    if (!seg) return NULL;
+    if (cu_seqlens == NULL || n_seqs == 0) {
+        for (int64_t n = 0; n < N; ++n) seg[n] = (n / T) * T;
+    } else {
+        for (int32_t i = 0; i < n_seqs; ++i)
+            for (int64_t n = cu_seqlens[i]; n < cu_seqlens[i + 1]; ++n) seg[n] = cu_seqlens[i];
+    }
+    return seg;
+}
+
+static int check_common(int64_t B, int64_t T, int64_t D, int32_t W, const int32_t *cu, int32_t n_seqs,
+                        int64_t n_lo, int64_t n_hi)
+{
+    if (B < 1 || T < 1 || D < 1 || W < 1) return -2;
+    if (n_lo < 0 || n_hi < n_lo || n_hi > B * T) return -2;
+    if (cu != NULL && n_seqs > 0) {
+        if (cu[0] != 0 || cu[n_seqs] != B * T) return -2;
+        for (int32_t i = 0; i < n_seqs; ++i)
+            if (cu[i + 1] <= cu[i]) return -2;
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------- head-wise */
+
+/* y[n,d] = rho*x[n,d] + sum_{k<W, n-k >= seg(n)} w[n, d/H, k] * x[n-k, d] */
+int oracle_headwise_fwd(int64_t B, int64_t T, int64_t D, int32_t W, int32_t H,
+                        const double *x, const double *w,
+                        const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual,
+                        int64_t n_lo, int64_t n_hi, double *y)
+{
+    if (check_common(B, T, D, W, cu_seqlens, n_seqs, n_lo, n_hi) || H < 1 || D % H) return -2;
+    const int64_t G = D / H;
+    int64_t *seg = segment_starts(B, T, cu_seqlens, n_seqs);
+    if (!seg) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = n_lo; n < n_hi; ++n) {
+        for (int64_t d = 0; d < D; ++d) {
+            double acc = residual ? x[n * D + d] : 0.0;
+            for (int32_t k = 0; k < W; ++k)
+                if (n - k >= seg[n]) acc += w[(n * G + d / H) * W + k] * x[(n - k) * D + d];
+            y[(n - n_lo) * D + d] = acc;
+        }
+    }
+    free(seg);
+    return 0;
+}
+
+/* Chain rule of the forward for L = <g, y>:
+ *   dx[m,d]   = rho*g[m,d] + sum_{k: m+k < N, m >= seg(m+k)} w[m+k, d/H, k] * g[m+k, d]
+ *   dw[n,j,k] = [n-k >= seg(n)] * sum_{d = jH .. jH+H-1} g[n,d] * x[n-k,d]          */
+int oracle_headwise_bwd(int64_t B, int64_t T, int64_t D, int32_t W, int32_t H,
+                        const double *x, const double *w, const double *g,
+                        const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual,
+                        int64_t n_lo, int64_t n_hi, double *dx, double *dw)
+{
+    if (check_common(B, T, D, W, cu_seqlens, n_seqs, n_lo, n_hi) || H < 1 || D % H) return -2;
+    const int64_t N = B * T, G = D / H;
+    int64_t *seg = segment_starts(B, T, cu_seqlens, n_seqs);
+    if (!seg) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = n_lo; m < n_hi; ++m) {
+        for (int64_t d = 0; d < D; ++d) {
+            double acc = residual ? g[m * D + d] : 0.0;
+            for (int32_t k = 0; k < W; ++k) {
+                int64_t n = m + k;
+                if (n < N && m >= seg[n]) acc += w[(n * G + d / H) * W + k] * g[n * D + d];
+            }
+            dx[(m - n_lo) * D + d] = acc;
+        }
+        for (int64_t j = 0; j < G; ++j) {
+            for (int32_t k = 0; k < W; ++k) {
+                double acc = 0.0;
+                if (m - k >= seg[m])
+                    for (int64_t d = j * H; d < (j + 1) * H; ++d) acc += g[m * D + d] * x[(m - k) * D + d];
+                dw[((m - n_lo) * G + j) * W + k] = acc;
+            }
+        }
+    }
+    free(seg);
+    return 0;
+}
+
+/* ----------------------------------------------------------------- low-rank */
+
+/* Filter of token n, channel d, tap k: w[n,d,k] = sum_r z[n,r] * U[r, d*W+k]. */
+static double lowrank_filter(int64_t D, int32_t W, int32_t R, const double *z, const double *U,
+                             int64_t n, int64_t d, int32_t k)
+{
+    double acc = 0.0;
+    for (int32_t r = 0; r < R; ++r) acc += z[n * R + r] * U[(int64_t)r * D * W + d * W + k];
+    return acc;
+}
+
+/* y[n,d] = rho*x[n,d] + sum_{k<W, n-k >= seg(n)} w[n,d,k] * x[n-k,d], w from z and U */
+int oracle_lowrank_fwd(int64_t B, int64_t T, int64_t D, int32_t W, int32_t R,
+                       const double *x, const double *z, const double *U,
+                       const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual,
+                       int64_t n_lo, int64_t n_hi, double *y)
+{
+    if (check_common(B, T, D, W, cu_seqlens, n_seqs, n_lo, n_hi) || R < 1) return -2;
+    int64_t *seg = segment_starts(B, T, cu_seqlens, n_seqs);
+    if (!seg) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = n_lo; n < n_hi; ++n) {
+        for (int64_t d = 0; d < D; ++d) {
+            double acc = residual ? x[n * D + d] : 0.0;
+            for (int32_t k = 0; k < W; ++k)
+                if (n - k >= seg[n]) acc += lowrank_filter(D, W, R, z, U, n, d, k) * x[(n - k) * D + d];
+            y[(n - n_lo) * D + d] = acc;
+        }
+    }
+    free(seg);
+    return 0;
+}
+
+/* Chain rule for L = <g, y> with w = zU and the per-channel filter gradient
+ *   dwc[n,d,k] = [n-k >= seg(n)] * g[n,d] * x[n-k,d]:
+ *   dx[m,d]        = rho*g[m,d] + sum_{k: m+k < N, m >= seg(m+k)} w[m+k,d,k] * g[m+k,d]
+ *   dz[n,r]        = sum_{d,k} U[r, d*W+k] * dwc[n,d,k]
+ *   dU[r, d*W+k]   = sum_n z[n,r] * dwc[n,d,k]                                      */
+int oracle_lowrank_bwd(int64_t B, int64_t T, int64_t D, int32_t W, int32_t R,
+                       const double *x, const double *z, const double *U, const double *g,
+                       const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual,
+                       int64_t n_lo, int64_t n_hi, double *dx, double *dz,
+                       int64_t d_lo, int64_t d_hi, double *dU)
+{
+    if (check_common(B, T, D, W, cu_seqlens, n_seqs, n_lo, n_hi) || R < 1) return -2;
+    if (d_lo < 0 || d_hi < d_lo || d_hi > D) return -2;
+    const int64_t N = B * T;
+    int64_t *seg = segment_starts(B, T, cu_seqlens, n_seqs);
+    if (!seg) return -1;
+
+#pragma omp parallel for schedule(static)
+    for (int64_t m = n_lo; m < n_hi; ++m) {
+        for (int64_t d = 0; d < D; ++d) {
+            double acc = residual ? g[m * D + d] : 0.0;
+            for (int32_t k = 0; k < W; ++k) {
+                int64_t n = m + k;
+                if (n < N && m >= seg[n]) acc += lowrank_filter(D, W, R, z, U, n, d, k) * g[n * D + d];
+            }
+            dx[(m - n_lo) * D + d] = acc;
+        }
+        for (int32_t r = 0; r < R; ++r) {
+            double acc = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                for (int32_t k = 0; k < W; ++k)
+                    if (m - k >= seg[m])
+                        acc += U[(int64_t)r * D * W + d * W + k] * (g[m * D + d] * x[(m - k) * D + d]);
+            dz[(m - n_lo) * R + r] = acc;
+        }
+    }
+
+    const int64_t DWs = (d_hi - d_lo) * W;
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < DWs; ++c) {
+        const int64_t d = d_lo + c / W;
+        const int32_t k = (int32_t)(c % W);
+        for (int32_t r = 0; r < R; ++r) {
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n)
+                if (n - k >= seg[n]) acc += z[n * R + r] * (g[n * D + d] * x[(n - k) * D + d]);
+            dU[(int64_t)r * DWs + c] = acc;
+        }
+    }
+    free(seg);
+    return 0;
+}

@@ -1,0 +1,345 @@
+"""Pins of the fp64 oracle against facts fixed by the pages and by mathematics.
+
+Every ``pin_*`` function takes an ``oracle.Oracle`` (the real one, or a
+variant with a planted mistake) and raises AssertionError when the oracle
+disagrees with:
+  - hand-worked examples of the defining formula (tests/golden),
+  - the dense banded-matrix brute force (tests/bruteforce.py),
+  - closed forms (impulse response, W = 1 scaling, static filters equal to
+    numpy.convolve, rank-1 low-rank),
+  - the adjoint identity and exact central finite differences of L = <g, y>,
+  - structural identities (segment independence, locality / causality).
+The formula is the one in "Dynamic Short Convolutions Improve Transformers"
+(gist.science technical summary, Methodology): y_t is the sum over k < W of
+w(t)_k times x_{t-k}; the pages state that it generalises the static,
+causal short convolution (authors' thread on digg.com).
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+
+import bruteforce as bf
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "worked_examples.json")
+RTOL = 1e-12
+
+
+def _close(a, b, tol=RTOL, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    scale = max(1.0, float(np.max(np.abs(b))) if b.size else 1.0)
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol * scale, f"{what}: max abs err {err:.3e} (scale {scale:.3e})"
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _hw_case(rng, B, T, D, W, H):
+    x = rng.standard_normal((B, T, D))
+    w = rng.standard_normal((B, T, D // H, W))
+    g = rng.standard_normal((B, T, D))
+    return x, w, g
+
+
+def _lr_case(rng, B, T, D, W, R):
+    x = rng.standard_normal((B, T, D))
+    z = rng.standard_normal((B, T, R))
+    U = rng.standard_normal((R, D * W))
+    g = rng.standard_normal((B, T, D))
+    return x, z, U, g
+
+
+# ------------------------------------------------------------------ golden
+
+
+def pin_golden_worked_examples(orc):
+    with open(GOLDEN) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        x = np.array(c["x"], dtype=np.float64)
+        g = np.array(c["dy"], dtype=np.float64)
+        cu = c["cu_seqlens"]
+        if c["kind"] == "headwise":
+            w = np.array(c["w"], dtype=np.float64)
+            y = orc.headwise_fwd(x, w, cu_seqlens=cu, residual=c["residual"])
+            dx, dw = orc.headwise_bwd(x, w, g, cu_seqlens=cu, residual=c["residual"])
+            _close(y, c["y"], what=c["name"] + " y")
+            _close(dx, c["dx"], what=c["name"] + " dx")
+            _close(dw, c["dw"], what=c["name"] + " dw")
+        else:
+            z = np.array(c["z"], dtype=np.float64)
+            U = np.array(c["U"], dtype=np.float64)
+            y = orc.lowrank_fwd(x, z, U, c["W"], cu_seqlens=cu, residual=c["residual"])
+            dx, dz, dU = orc.lowrank_bwd(x, z, U, g, c["W"], cu_seqlens=cu, residual=c["residual"])
+            _close(y, c["y"], what=c["name"] + " y")
+            _close(dx, c["dx"], what=c["name"] + " dx")
+            _close(dz, c["dz"], what=c["name"] + " dz")
+            _close(dU, c["dU"], what=c["name"] + " dU")
+
+
+# ------------------------------------------------------------- brute force
+
+
+def pin_bruteforce_headwise(orc):
+    rng = _rng(1)
+    for (B, T, D, W, H, cu, res) in [(2, 9, 8, 4, 2, None, False), (1, 11, 6, 3, 3, [0, 4, 5, 11], True),
+                                     (2, 5, 4, 4, 1, [0, 2, 5, 6, 10], False),
+                                     (1, 7, 8, 8, 8, None, True)]:
+        x, w, g = _hw_case(rng, B, T, D, W, H)
+        seg = bf.seg_starts(B, T, cu)
+        pc = bf.perchannel_filters_headwise(w, D)
+        _close(orc.headwise_fwd(x, w, cu_seqlens=cu, residual=res), bf.conv_fwd(x, pc, seg, res),
+               what="headwise y vs band matrix")
+        dx, _ = orc.headwise_bwd(x, w, g, cu_seqlens=cu, residual=res)
+        _close(dx, bf.conv_dx(g, pc, seg, res), what="headwise dx vs band matrix transpose")
+
+
+def pin_bruteforce_lowrank(orc):
+    rng = _rng(2)
+    for (B, T, D, W, R, cu, res) in [(2, 7, 4, 4, 3, None, False), (1, 10, 5, 3, 2, [0, 3, 4, 10], True),
+                                     (1, 6, 2, 1, 4, None, True)]:
+        x, z, U, g = _lr_case(rng, B, T, D, W, R)
+        seg = bf.seg_starts(B, T, cu)
+        pc = bf.perchannel_filters_lowrank(z, U, W)
+        _close(orc.lowrank_fwd(x, z, U, W, cu_seqlens=cu, residual=res), bf.conv_fwd(x, pc, seg, res),
+               what="lowrank y vs band matrix")
+        dx, dz, dU = orc.lowrank_bwd(x, z, U, g, W, cu_seqlens=cu, residual=res)
+        _close(dx, bf.conv_dx(g, pc, seg, res), what="lowrank dx vs band matrix transpose")
+        # dz, dU through the per-channel filter gradient of the brute force:
+        # dL/dw_pc[n,d,k] = g[n,d] * (A_d's column shift of x)[n] (band entries only)
+        N = B * T
+        gf, xf = g.reshape(N, D), x.reshape(N, D)
+        dwpc = np.zeros((N, D, W))
+        for n in range(N):
+            for k in range(W):
+                if n - k >= seg[n]:
+                    dwpc[n, :, k] = gf[n] * xf[n - k]
+        _close(dz.reshape(N, R), np.einsum("ndk,rdk->nr", dwpc, U.reshape(R, D, W)), what="lowrank dz chain")
+        _close(dU, np.einsum("nr,ndk->rdk", z.reshape(N, R), dwpc).reshape(R, D * W), what="lowrank dU chain")
+
+
+# ------------------------------------------------------------ closed forms
+
+
+def pin_impulse_response(orc):
+    """x = e_(s,d): y_t[d] = w_t[j(d), t-s] for 0 <= t-s < W (same segment), else 0."""
+    rng = _rng(3)
+    B, T, D, W, H = 1, 10, 6, 4, 3
+    w = rng.standard_normal((B, T, D // H, W))
+    for s in (0, 3, 8):
+        for d in (0, 4):
+            x = np.zeros((B, T, D))
+            x[0, s, d] = 1.0
+            y = orc.headwise_fwd(x, w)
+            want = np.zeros((B, T, D))
+            for t in range(s, min(s + W, T)):
+                want[0, t, d] = w[0, t, d // H, t - s]
+            _close(y, want, what=f"impulse s={s} d={d}")
+
+
+def pin_static_filter_is_numpy_convolve(orc):
+    """Constant filters over time: the op is the static causal conv (numpy.convolve, truncated)."""
+    rng = _rng(4)
+    B, T, D, W, H = 2, 13, 4, 4, 2
+    c = rng.standard_normal((D // H, W))
+    w = np.broadcast_to(c, (B, T, D // H, W)).copy()
+    x = rng.standard_normal((B, T, D))
+    y = orc.headwise_fwd(x, w)
+    for b in range(B):
+        for d in range(D):
+            _close(y[b, :, d], np.convolve(x[b, :, d], c[d // H])[:T], what="static conv")
+    # low-rank with constant z: static filter z0 U
+    R = 3
+    z0 = rng.standard_normal(R)
+    U = rng.standard_normal((R, D * W))
+    z = np.broadcast_to(z0, (B, T, R)).copy()
+    y = orc.lowrank_fwd(x, z, U, W)
+    filt = (z0 @ U).reshape(D, W)
+    for b in range(B):
+        for d in range(D):
+            _close(y[b, :, d], np.convolve(x[b, :, d], filt[d])[:T], what="static conv low-rank")
+    # static dx is the correlation with the same filter (flip of convolve)
+    g = rng.standard_normal((B, T, D))
+    dx, _ = orc.headwise_bwd(x, w, g)
+    for b in range(B):
+        for d in range(D):
+            full = np.convolve(g[b, ::-1, d], c[d // H])[:T][::-1]
+            _close(dx[b, :, d], full, what="static dx")
+
+
+def pin_width_one_is_scaling(orc):
+    rng = _rng(5)
+    B, T, D, H = 2, 6, 8, 4
+    x = rng.standard_normal((B, T, D))
+    w = rng.standard_normal((B, T, D // H, 1))
+    g = rng.standard_normal((B, T, D))
+    scale = np.repeat(w[..., 0], H, axis=2)
+    for res in (False, True):
+        y = orc.headwise_fwd(x, w, residual=res)
+        _close(y, (res + scale) * x, what="W=1 y")
+        dx, dw = orc.headwise_bwd(x, w, g, residual=res)
+        _close(dx, (res + scale) * g, what="W=1 dx")
+        _close(dw[..., 0], (g * x).reshape(B, T, D // H, H).sum(-1), what="W=1 dw")
+
+
+def pin_rank_one_closed_form(orc):
+    """R = 1: y_t[d] = z_t * (x[:, d] convolved with U[0, d, :])_t."""
+    rng = _rng(6)
+    B, T, D, W = 1, 12, 3, 4
+    x = rng.standard_normal((B, T, D))
+    z = rng.standard_normal((B, T, 1))
+    U = rng.standard_normal((1, D * W))
+    y = orc.lowrank_fwd(x, z, U, W)
+    for d in range(D):
+        conv = np.convolve(x[0, :, d], U[0].reshape(D, W)[d])[:T]
+        _close(y[0, :, d], z[0, :, 0] * conv, what="rank-1")
+
+
+def pin_headwise_equals_perchannel(orc):
+    rng = _rng(7)
+    B, T, D, W, H = 2, 8, 8, 3, 4
+    x, w, g = _hw_case(rng, B, T, D, W, H)
+    wpc = np.repeat(w, H, axis=2)
+    _close(orc.headwise_fwd(x, w, residual=True), orc.headwise_fwd(x, wpc, residual=True),
+           what="head-wise == per-channel y")
+    dx_h, dw_h = orc.headwise_bwd(x, w, g)
+    dx_p, dw_p = orc.headwise_bwd(x, wpc, g)
+    _close(dx_h, dx_p, what="head-wise == per-channel dx")
+    _close(dw_h, dw_p.reshape(B, T, D // H, H, W).sum(3), what="dw == group sum of per-channel dw")
+
+
+# ------------------------------------------------ adjoint / finite differences
+
+
+def pin_adjoint_identity(orc):
+    rng = _rng(8)
+    B, T, D, W, H = 2, 9, 4, 4, 2
+    cu = [0, 3, 9, 12, 18]
+    x, w, g = _hw_case(rng, B, T, D, W, H)
+    y = orc.headwise_fwd(x, w, cu_seqlens=cu)
+    dx, _ = orc.headwise_bwd(x, w, g, cu_seqlens=cu)
+    lhs, rhs = float(np.sum(g * y)), float(np.sum(dx * x))
+    assert abs(lhs - rhs) <= 1e-11 * max(1.0, abs(lhs)), f"adjoint {lhs} vs {rhs}"
+    R = 3
+    xl, z, U, gl = _lr_case(rng, B, T, D, W, R)
+    y = orc.lowrank_fwd(xl, z, U, W, cu_seqlens=cu)
+    dx, dz, dU = orc.lowrank_bwd(xl, z, U, gl, W, cu_seqlens=cu)
+    L = float(np.sum(gl * y))
+    for name, v in (("x", np.sum(dx * xl)), ("z", np.sum(dz * z)), ("U", np.sum(dU * U))):
+        # y is linear (degree-1 homogeneous) in each of x, z, U separately
+        assert abs(L - float(v)) <= 1e-11 * max(1.0, abs(L)), f"Euler identity in {name}: {L} vs {v}"
+
+
+def _fd_grad(f, a, h=1e-3):
+    grad = np.zeros_like(a)
+    flat, gflat = a.reshape(-1), grad.reshape(-1)
+    for i in range(flat.size):
+        old = flat[i]
+        flat[i] = old + h
+        fp = f()
+        flat[i] = old - h
+        fm = f()
+        flat[i] = old
+        gflat[i] = (fp - fm) / (2 * h)
+    return grad
+
+
+def pin_finite_differences_headwise(orc):
+    rng = _rng(9)
+    B, T, D, W, H = 2, 6, 4, 3, 2
+    cu = [0, 4, 6, 12]
+    x, w, g = _hw_case(rng, B, T, D, W, H)
+    for res in (False, True):
+        L = lambda: float(np.sum(g * orc.headwise_fwd(x, w, cu_seqlens=cu, residual=res)))
+        dx, dw = orc.headwise_bwd(x, w, g, cu_seqlens=cu, residual=res)
+        _close(dx, _fd_grad(L, x), tol=1e-8, what="FD dx")
+        _close(dw, _fd_grad(L, w), tol=1e-8, what="FD dw")
+
+
+def pin_finite_differences_lowrank(orc):
+    rng = _rng(10)
+    B, T, D, W, R = 2, 5, 3, 3, 2
+    cu = [0, 2, 5, 7, 10]
+    x, z, U, g = _lr_case(rng, B, T, D, W, R)
+    for res in (False, True):
+        L = lambda: float(np.sum(g * orc.lowrank_fwd(x, z, U, W, cu_seqlens=cu, residual=res)))
+        dx, dz, dU = orc.lowrank_bwd(x, z, U, g, W, cu_seqlens=cu, residual=res)
+        _close(dx, _fd_grad(L, x), tol=1e-8, what="FD dx low-rank")
+        _close(dz, _fd_grad(L, z), tol=1e-8, what="FD dz")
+        _close(dU, _fd_grad(L, U), tol=1e-8, what="FD dU")
+
+
+# ------------------------------------------------------- structural identities
+
+
+def pin_segments_are_independent(orc):
+    """Packed result == every segment run alone as its own sequence (dU sums over segments)."""
+    rng = _rng(11)
+    B, T, D, W, H, R = 2, 10, 4, 4, 2, 3
+    cu = [0, 1, 4, 10, 13, 20]
+    x, w, g = _hw_case(rng, B, T, D, W, H)
+    y = orc.headwise_fwd(x, w, cu_seqlens=cu, residual=True).reshape(B * T, D)
+    dx, dw = orc.headwise_bwd(x, w, g, cu_seqlens=cu, residual=True)
+    dx, dw = dx.reshape(B * T, D), dw.reshape(B * T, D // H, W)
+    xf, wf, gf = x.reshape(B * T, D), w.reshape(B * T, D // H, W), g.reshape(B * T, D)
+    xl, z, U, gl = _lr_case(rng, B, T, D, W, R)
+    yl = orc.lowrank_fwd(xl, z, U, W, cu_seqlens=cu).reshape(B * T, D)
+    dxl, dzl, dUl = orc.lowrank_bwd(xl, z, U, gl, W, cu_seqlens=cu)
+    dxl, dzl = dxl.reshape(B * T, D), dzl.reshape(B * T, R)
+    xlf, zf, glf = xl.reshape(B * T, D), z.reshape(B * T, R), gl.reshape(B * T, D)
+    dU_sum = np.zeros_like(dUl)
+    for a, b in zip(cu[:-1], cu[1:]):
+        L = b - a
+        ys = orc.headwise_fwd(xf[None, a:b], wf[None, a:b], residual=True)[0]
+        dxs, dws = orc.headwise_bwd(xf[None, a:b], wf[None, a:b], gf[None, a:b], residual=True)
+        _close(y[a:b], ys, what=f"segment [{a},{b}) y")
+        _close(dx[a:b], dxs[0], what=f"segment [{a},{b}) dx")
+        _close(dw[a:b], dws[0], what=f"segment [{a},{b}) dw")
+        ysl = orc.lowrank_fwd(xlf[None, a:b], zf[None, a:b], U, W)[0]
+        dxs, dzs, dUs = orc.lowrank_bwd(xlf[None, a:b], zf[None, a:b], U, glf[None, a:b], W)
+        _close(yl[a:b], ysl, what=f"segment [{a},{b}) low-rank y")
+        _close(dxl[a:b], dxs[0], what=f"segment [{a},{b}) low-rank dx")
+        _close(dzl[a:b], dzs[0], what=f"segment [{a},{b}) dz")
+        dU_sum += dUs
+        assert L >= 1
+    _close(dUl, dU_sum, what="dU = sum over segments")
+
+
+def pin_locality_and_causality(orc):
+    """Changing x[s] changes y only at tokens s .. min(s+W-1, end of s's segment)."""
+    rng = _rng(12)
+    B, T, D, W, H = 1, 16, 2, 4, 1
+    cu = [0, 6, 16]
+    x, w, _ = _hw_case(rng, B, T, D, W, H)
+    y0 = orc.headwise_fwd(x, w, cu_seqlens=cu)
+    for s in (0, 4, 5, 6, 14):
+        x1 = x.copy()
+        x1[0, s, 1] += 1.0
+        diff = np.abs(orc.headwise_fwd(x1, w, cu_seqlens=cu) - y0)[0]
+        end = 6 if s < 6 else 16
+        changed = set(np.nonzero(diff.max(axis=1) > 0)[0].tolist())
+        allowed = set(range(s, min(s + W, end)))
+        assert changed <= allowed, f"x[{s}] changed tokens {sorted(changed)} outside {sorted(allowed)}"
+        assert s in changed, f"x[{s}] did not change y[{s}]"
+        assert np.all(diff[:, 0] == 0), "another channel changed"
+
+
+def pin_row_ranges_match_full(orc):
+    """Computing a token range / channel range gives the same values as the full call."""
+    rng = _rng(13)
+    B, T, D, W, R = 2, 7, 4, 4, 2
+    x, z, U, g = _lr_case(rng, B, T, D, W, R)
+    dx, dz, dU = orc.lowrank_bwd(x, z, U, g, W, residual=True)
+    dxr, dzr, dUr = orc.lowrank_bwd(x, z, U, g, W, residual=True, rows=(3, 11), channels=(1, 3))
+    _close(dxr, dx.reshape(B * T, D)[3:11], what="row range dx")
+    _close(dzr, dz.reshape(B * T, R)[3:11], what="row range dz")
+    _close(dUr, dU.reshape(R, D, W)[:, 1:3].reshape(R, 2 * W), what="channel range dU")
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,60 @@
+"""Each plausible mistake planted in a copy of the oracle fails at least one pin.
+
+The copy is compiled with gcc into a temporary directory on the CPU; the
+real oracle source is never modified.
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle
+import pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "dsc_oracle.c")
+
+# (name, exact source fragment, replacement, expected occurrences)
+MUTANTS = [
+    ("drop_residual_fwd", "double acc = residual ? x[n * D + d] : 0.0;", "double acc = 0.0;", 2),
+    ("drop_residual_dx", "double acc = residual ? g[m * D + d] : 0.0;", "double acc = 0.0;", 2),
+    ("unshifted_tap", "w[(n * G + d / H) * W + k] * x[(n - k) * D + d]",
+     "w[(n * G + d / H) * W + k] * x[n * D + d]", 1),
+    ("strict_segment_test", "if (n - k >= seg[n]) acc += w", "if (n - k > seg[n]) acc += w", 1),
+    ("group_modulo", "w[(n * G + d / H) * W + k] * x", "w[(n * G + d % G) * W + k] * x", 1),
+    ("reversed_taps", "w[(n * G + d / H) * W + k] * x", "w[(n * G + d / H) * W + (W - 1 - k)] * x", 1),
+    ("dx_wrong_segment", "if (n < N && m >= seg[n]) acc += w", "if (n < N) acc += w", 1),
+    ("dx_tap_of_m", "acc += w[(n * G + d / H) * W + k] * g[n * D + d];",
+     "acc += w[(m * G + d / H) * W + k] * g[n * D + d];", 1),
+    ("dw_unshifted", "acc += g[m * D + d] * x[(m - k) * D + d];", "acc += g[m * D + d] * x[m * D + d];", 1),
+    ("U_transposed", "U[(int64_t)r * D * W + d * W + k];", "U[(int64_t)r * D * W + k * D + d];", 1),
+    ("lowrank_fwd_no_shift", "lowrank_filter(D, W, R, z, U, n, d, k) * x[(n - k) * D + d]",
+     "lowrank_filter(D, W, R, z, U, n, d, k) * x[n * D + d]", 1),
+    ("lowrank_dx_filter_at_m", "lowrank_filter(D, W, R, z, U, n, d, k) * g[n * D + d]",
+     "lowrank_filter(D, W, R, z, U, m, d, k) * g[n * D + d]", 1),
+    ("dz_transposed_U", "acc += U[(int64_t)r * D * W + d * W + k] * (g[m * D + d]",
+     "acc += U[(int64_t)r * D * W + k * D + d] * (g[m * D + d]", 1),
+    ("dz_missing_mask", "if (m - k >= seg[m])\n                        acc += U", "if (1)\n                        acc += U", 1),
+    ("dU_wrong_z", "acc += z[n * R + r] * (g[n * D + d]", "acc += z[n * R + (R - 1 - r)] * (g[n * D + d]", 1),
+    ("dU_unshifted", "(g[n * D + d] * x[(n - k) * D + d]);", "(g[n * D + d] * x[n * D + d]);", 1),
+    ("segment_from_row", "seg[n] = cu_seqlens[i];", "seg[n] = (n / T) * T;", 1),
+]
+
+
+@pytest.mark.parametrize("name,old,new,count", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, name, old, new, count):
+    src = open(SRC).read()
+    assert src.count(old) == count, f"fragment for {name} found {src.count(old)} times"
+    mutant = tmp_path / "mutant.c"
+    mutant.write_text(src.replace(old, new))
+    so = str(tmp_path / "libmutant.so")
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fopenmp", "-fPIC", "-shared", str(mutant), "-o", so],
+                   check=True)
+    orc = oracle.Oracle(oracle.load(so))
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
