@@ -1,0 +1,169 @@
+/*
+ * dsc.h -- C ABI of the dynamic short convolution library (libdsc.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("Dynamic Short Convolutions Improve Transformers",
+ * gist.science technical summary, Methodology, "mechanism"): for token n of
+ * a sequence and channel d,
+ *
+ *     y[n,d] = rho * x[n,d] + sum_{k=0}^{W-1} w(n)_{d,k} * x[n-k,d]
+ *
+ * with a filter w(n) that belongs to the token.  x[n-k] is zero when n-k lies
+ * before the first token of n's sequence (causal zero padding; the authors'
+ * thread on digg.com describes the static short convolution being
+ * generalised as causal).  rho in {0,1} selects the residual placement
+ * X = X + dynamicShortConv(X) (same summary, Methodology, "placement").
+ * Two filter parametrisations (Methodology, "parametrization"):
+ *   - head-wise tying: one W-tap filter per token shared by H consecutive
+ *     channels, w(n)_{d,k} = w[n, d/H, k];
+ *   - low rank R: w(n)_{d,k} = sum_r z[n,r] * U[r, d*W + k], generated on
+ *     chip and never written to memory (Efficient training implementation,
+ *     fused low-rank kernel).
+ * The backward entry points return the gradients of L = <dy, y>.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *   stream      a hipStream_t passed as void*; NULL selects the null stream.
+ *               Every call is asynchronous on that stream; device faults
+ *               surface at the caller's next synchronisation.
+ *   dtype       DSC_FP32 or DSC_BF16: the element type of every activation,
+ *               filter and z/U tensor of the call.  Arithmetic is fp32
+ *               (fused multiply-add) and each output is rounded once, to
+ *               nearest even, to its storage type.
+ *   B, T, D     batch, tokens per row and channels; tensors named (B,T,D)
+ *               are dense row-major with channels innermost.
+ *   W           taps, 1..8.
+ *   cu_seqlens  NULL with n_seqs == 0: each of the B rows is one sequence.
+ *               Otherwise a DEVICE pointer to int32[n_seqs+1] strictly
+ *               increasing offsets on the flattened N = B*T token axis,
+ *               cu_seqlens[0] = 0 and cu_seqlens[n_seqs] = N; sequences are
+ *               defined by these offsets alone and may cross row boundaries.
+ *               The contents are not validated (a malformed array gives
+ *               undefined results).
+ *   residual    0 or 1 (rho above).
+ *   pointers    DEVICE pointers, each 16-byte aligned.  The caller owns all
+ *               memory; the library allocates nothing, keeps no state and
+ *               is thread-safe.  Inputs are never written.  Every output is
+ *               fully overwritten (nothing accumulates into it).  No output
+ *               may overlap an input or another output (so y = x in place
+ *               is rejected).
+ *
+ * Errors: each entry point checks every host-checkable precondition first
+ * and returns a status without making any HIP call when one fails; a failed
+ * kernel launch returns DSC_ERR_HIP.  dsc_last_error() describes the most
+ * recent failure of the calling thread.
+ */
+#ifndef DSC_H
+#define DSC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSC_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define DSC_API __attribute__((visibility("default")))
+#else
+#define DSC_API
+#endif
+
+typedef enum dsc_dtype { DSC_FP32 = 0, DSC_BF16 = 1 } dsc_dtype;
+
+typedef enum dsc_status {
+    DSC_SUCCESS = 0,
+    DSC_ERR_NULL = 1,        /* a required pointer is NULL                          */
+    DSC_ERR_SHAPE = 2,       /* a size is out of range or inconsistent              */
+    DSC_ERR_UNSUPPORTED = 3, /* valid shape this build does not implement           */
+    DSC_ERR_ALIGNMENT = 4,   /* a pointer is not 16-byte aligned                    */
+    DSC_ERR_ALIAS = 5,       /* an output overlaps an input or another output       */
+    DSC_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required          */
+    DSC_ERR_HIP = 7          /* a HIP call or kernel launch failed                  */
+} dsc_status;
+
+/*
+ * Head-wise forward.  Methodology, "mechanism" and "parametrization (2)":
+ * y[n,d] = rho*x[n,d] + sum_{k<W, n-k in n's sequence} w[n, d/H, k] * x[n-k,d].
+ *
+ *   x  (B,T,D) dtype, in.      w  (B,T,D/H,W) dtype, in (tap innermost).
+ *   y  (B,T,D) dtype, out.
+ *   H  channels per shared filter: 1 <= H, D % H == 0.  This build supports
+ *      H that divides 8 (bf16) / 4 (fp32), or H = 8*2^i (bf16) / 4*2^i (fp32)
+ *      with H <= 64*8 (bf16) / 64*4 (fp32); other H return
+ *      DSC_ERR_UNSUPPORTED.
+ *   D  multiple of 8 (bf16) or 4 (fp32).
+ */
+DSC_API dsc_status dsc_headwise_fwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                            int32_t H, const void *x, const void *w, const int32_t *cu_seqlens,
+                            int32_t n_seqs, int32_t residual, void *y);
+
+/*
+ * Head-wise backward (chain rule of the forward above, for L = <dy, y>):
+ *   dx[m,d]   = rho*dy[m,d] + sum_{k<W, m+k in m's sequence} w[m+k, d/H, k] * dy[m+k,d]
+ *   dw[n,j,k] = [n-k in n's sequence] * sum_{d=jH}^{jH+H-1} dy[n,d] * x[n-k,d]
+ *
+ *   x, dy (B,T,D) in;  w (B,T,D/H,W) in;  dx (B,T,D) out;  dw (B,T,D/H,W) out.
+ *   Same shape rules as dsc_headwise_fwd.
+ */
+DSC_API dsc_status dsc_headwise_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                            int32_t H, const void *x, const void *w, const void *dy,
+                            const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual,
+                            void *dx, void *dw);
+
+/*
+ * Low-rank forward (fused up-projection; Methodology, "parametrization (1)"
+ * and Efficient training implementation, fused low-rank kernel):
+ *   w[n,d,k] = sum_{r<R} z[n,r] * U[r, d*W+k]          (on chip only)
+ *   y[n,d]   = rho*x[n,d] + sum_{k<W, n-k in n's sequence} w[n,d,k] * x[n-k,d]
+ *
+ *   x (B,T,D) in;  z (B,T,R) in;  U (R, D*W) in, read as (R, D, W);
+ *   y (B,T,D) out.  1 <= R <= 128.  D multiple of 8 (bf16) / 4 (fp32).
+ */
+DSC_API dsc_status dsc_lowrank_fwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                           int32_t R, const void *x, const void *z, const void *U,
+                           const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, void *y);
+
+/*
+ * Bytes of device workspace dsc_lowrank_bwd needs for these sizes and dtype
+ * (fp32 accumulators of dz; 0 never happens for valid sizes).  Returns 0 for
+ * invalid sizes.
+ */
+DSC_API size_t dsc_lowrank_bwd_workspace_size(int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                                      int32_t R);
+
+/*
+ * Low-rank backward.  With the per-channel filter gradient
+ *   dwc[n,d,k] = [n-k in n's sequence] * dy[n,d] * x[n-k,d]   (on chip only):
+ *   dx[m,d]      = rho*dy[m,d] + sum_{k<W, m+k in m's sequence} w[m+k,d,k] * dy[m+k,d]
+ *   dz[n,r]      = sum_{d,k} U[r, d*W+k] * dwc[n,d,k]
+ *   dU[r, d*W+k] = sum_n z[n,r] * dwc[n,d,k]
+ *
+ *   x, dy (B,T,D) in;  z (B,T,R) in;  U (R, D*W) in;
+ *   dx (B,T,D) dtype out;  dz (B,T,R) dtype out;  dU (R, D*W) fp32 out.
+ *   workspace: device memory of at least dsc_lowrank_bwd_workspace_size()
+ *   bytes, 16-byte aligned, contents undefined on entry and exit; it must not
+ *   overlap any argument.  dz and dU are sums over many partial products
+ *   accumulated with fp32 atomics: their last bits may differ run to run.
+ */
+DSC_API dsc_status dsc_lowrank_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                           int32_t R, const void *x, const void *z, const void *U, const void *dy,
+                           const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, void *dx,
+                           void *dz, float *dU, void *workspace, size_t workspace_bytes);
+
+/* Static name of a status code. */
+DSC_API const char *dsc_status_string(int status);
+
+/* Description of the calling thread's most recent failed call ("" if none). */
+DSC_API const char *dsc_last_error(void);
+
+/* DSC_ABI_VERSION of the loaded library. */
+DSC_API int dsc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSC_H */

@@ -1,0 +1,134 @@
+"""Thin Python binding of libdsc.so (include/dsc.h).
+
+Argument marshalling only: shapes, dtype codes, device pointers and the
+current HIP stream are read from torch tensors and passed through ctypes;
+every step of the computation runs in the library's HIP kernels.  There is no
+fallback: if libdsc.so is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsc.so")
+
+DSC_FP32, DSC_BF16 = 0, 1
+STATUS = {0: "DSC_SUCCESS", 1: "DSC_ERR_NULL", 2: "DSC_ERR_SHAPE", 3: "DSC_ERR_UNSUPPORTED",
+          4: "DSC_ERR_ALIGNMENT", 5: "DSC_ERR_ALIAS", 6: "DSC_ERR_WORKSPACE", 7: "DSC_ERR_HIP"}
+
+_lib = None
+
+
+class DscError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run python -m input_dependent_short_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, p, i = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int
+        L.dsc_headwise_fwd.argtypes = [p, i, i64, i64, i64, i32, i32, p, p, p, i32, i32, p]
+        L.dsc_headwise_bwd.argtypes = [p, i, i64, i64, i64, i32, i32, p, p, p, p, i32, i32, p, p]
+        L.dsc_lowrank_fwd.argtypes = [p, i, i64, i64, i64, i32, i32, p, p, p, p, i32, i32, p]
+        L.dsc_lowrank_bwd_workspace_size.argtypes = [i, i64, i64, i64, i32, i32]
+        L.dsc_lowrank_bwd_workspace_size.restype = ctypes.c_size_t
+        L.dsc_lowrank_bwd.argtypes = [p, i, i64, i64, i64, i32, i32, p, p, p, p, p, i32, i32, p, p, p,
+                                      p, ctypes.c_size_t]
+        for f in ("dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd",
+                  "dsc_abi_version"):
+            getattr(L, f).restype = ctypes.c_int
+        L.dsc_status_string.argtypes = [i]
+        L.dsc_status_string.restype = ctypes.c_char_p
+        L.dsc_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DSC_FP32
+    if t.dtype == torch.bfloat16:
+        return DSC_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _seq(cu_seqlens: torch.Tensor | None):
+    if cu_seqlens is None:
+        return None, 0
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    return _ptr(cu_seqlens), cu_seqlens.numel() - 1
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise DscError(rc, lib().dsc_last_error().decode())
+
+
+def dsc_headwise_fwd(x, w, y, *, cu_seqlens=None, residual=False, stream=None) -> None:
+    """y = rho*x + dynamic conv of x with head-wise filters w (B,T,D/H,W)."""
+    B, T, D = x.shape
+    G, W = w.shape[2], w.shape[3]
+    cu, ns = _seq(cu_seqlens)
+    _check(lib().dsc_headwise_fwd(_stream(stream), _dtype_code(x), B, T, D, W, D // G if G else 0,
+                                  _ptr(x), _ptr(w), cu, ns, int(bool(residual)), _ptr(y)))
+
+
+def dsc_headwise_bwd(x, w, dy, dx, dw, *, cu_seqlens=None, residual=False, stream=None) -> None:
+    B, T, D = x.shape
+    G, W = w.shape[2], w.shape[3]
+    cu, ns = _seq(cu_seqlens)
+    _check(lib().dsc_headwise_bwd(_stream(stream), _dtype_code(x), B, T, D, W, D // G if G else 0,
+                                  _ptr(x), _ptr(w), _ptr(dy), cu, ns, int(bool(residual)),
+                                  _ptr(dx), _ptr(dw)))
+
+
+def dsc_lowrank_fwd(x, z, U, y, *, W, cu_seqlens=None, residual=False, stream=None) -> None:
+    """y = rho*x + dynamic conv of x with filters z U (U is (R, D*W))."""
+    B, T, D = x.shape
+    R = z.shape[2]
+    cu, ns = _seq(cu_seqlens)
+    _check(lib().dsc_lowrank_fwd(_stream(stream), _dtype_code(x), B, T, D, W, R, _ptr(x), _ptr(z),
+                                 _ptr(U), cu, ns, int(bool(residual)), _ptr(y)))
+
+
+def dsc_lowrank_bwd_workspace_size(dtype: torch.dtype, B: int, T: int, D: int, W: int, R: int) -> int:
+    code = DSC_BF16 if dtype == torch.bfloat16 else DSC_FP32
+    return int(lib().dsc_lowrank_bwd_workspace_size(code, B, T, D, W, R))
+
+
+def dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, workspace=None, *, W, cu_seqlens=None,
+                    residual=False, stream=None) -> None:
+    B, T, D = x.shape
+    R = z.shape[2]
+    cu, ns = _seq(cu_seqlens)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().dsc_lowrank_bwd(_stream(stream), _dtype_code(x), B, T, D, W, R, _ptr(x), _ptr(z),
+                                 _ptr(U), _ptr(dy), cu, ns, int(bool(residual)), _ptr(dx), _ptr(dz),
+                                 _ptr(dU), _ptr(workspace), ws_bytes))
+
+
+def dsc_abi_version() -> int:
+    return int(lib().dsc_abi_version())

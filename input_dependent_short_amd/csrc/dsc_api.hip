@@ -1,0 +1,201 @@
+// dsc_api.hip -- the C ABI of libdsc.so (declared in include/dsc.h):
+// argument validation, then one launch sequence on the caller's stream.
+// Every precondition that the host can check is checked before the first HIP
+// call, so invalid calls never touch the device.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/dsc.h"
+#include "dsc_kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+dsc_status fail(dsc_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+dsc_status ok() {
+    g_last_error[0] = '\0';
+    return DSC_SUCCESS;
+}
+
+struct Range {
+    const char *name;
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// No output range may intersect an input range or another output range.
+dsc_status check_alias(const Range *in, int nin, const Range *out, int nout) {
+    for (int i = 0; i < nout; ++i) {
+        if (out[i].hi <= out[i].lo) continue;
+        for (int j = 0; j < nin; ++j)
+            if (in[j].hi > in[j].lo && out[i].lo < in[j].hi && in[j].lo < out[i].hi)
+                return fail(DSC_ERR_ALIAS, "output %s overlaps input %s", out[i].name, in[j].name);
+        for (int j = i + 1; j < nout; ++j)
+            if (out[j].hi > out[j].lo && out[i].lo < out[j].hi && out[j].lo < out[i].hi)
+                return fail(DSC_ERR_ALIAS, "outputs %s and %s overlap", out[i].name, out[j].name);
+    }
+    return DSC_SUCCESS;
+}
+
+Range rng(const char *name, const void *p, size_t bytes) {
+    return Range{name, (uintptr_t)p, (uintptr_t)p + bytes};
+}
+
+size_t esize(int dtype) { return dtype == DSC_BF16 ? 2 : 4; }
+
+dsc_status check_common(int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                        const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual) {
+    if (dtype != DSC_FP32 && dtype != DSC_BF16) return fail(DSC_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+    if (B < 1 || T < 1 || D < 1) return fail(DSC_ERR_SHAPE, "B, T, D must be >= 1 (got %lld, %lld, %lld)",
+                                             (long long)B, (long long)T, (long long)D);
+    if (B > (int64_t)1 << 40 || T > (int64_t)1 << 40 || B * T > (int64_t)INT32_MAX)
+        return fail(DSC_ERR_SHAPE, "B*T = %lld tokens exceeds 2^31-1", (long long)(B * T));
+    if (D > ((int64_t)1 << 24)) return fail(DSC_ERR_SHAPE, "D = %lld too large", (long long)D);
+    if (W < 1 || W > 8) return fail(DSC_ERR_SHAPE, "W must be in 1..8 (got %d)", W);
+    const int vec = dtype == DSC_BF16 ? 8 : 4;
+    if (D % vec) return fail(DSC_ERR_SHAPE, "D = %lld must be a multiple of %d for this dtype", (long long)D, vec);
+    if (residual != 0 && residual != 1) return fail(DSC_ERR_SHAPE, "residual must be 0 or 1");
+    if ((cu_seqlens == nullptr) != (n_seqs == 0))
+        return fail(DSC_ERR_SHAPE, "cu_seqlens and n_seqs disagree (NULL pointer iff n_seqs == 0)");
+    if (n_seqs < 0 || n_seqs > B * T) return fail(DSC_ERR_SHAPE, "n_seqs = %d out of range", n_seqs);
+    if (cu_seqlens && ((uintptr_t)cu_seqlens & 3u)) return fail(DSC_ERR_ALIGNMENT, "cu_seqlens not 4-byte aligned");
+    return DSC_SUCCESS;
+}
+
+#define DSC_TRY(expr)                        \
+    do {                                     \
+        dsc_status st_ = (expr);             \
+        if (st_ != DSC_SUCCESS) return st_;  \
+    } while (0)
+
+dsc_status launched(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(DSC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+dsc_status dsc_headwise_fwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                            int32_t H, const void *x, const void *w, const int32_t *cu_seqlens,
+                            int32_t n_seqs, int32_t residual, void *y) {
+    DSC_TRY(check_common(dtype, B, T, D, W, cu_seqlens, n_seqs, residual));
+    if (!x || !w || !y) return fail(DSC_ERR_NULL, "x, w and y are required");
+    if (H < 1 || D % H) return fail(DSC_ERR_SHAPE, "H = %d must divide D = %lld", H, (long long)D);
+    const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
+    if (!dsc::headwise_supported(dt, D, H)) return fail(DSC_ERR_UNSUPPORTED, "H = %d not supported", H);
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    const size_t es = esize(dtype), N = (size_t)(B * T);
+    const Range in[] = {rng("x", x, N * D * es), rng("w", w, N * (D / H) * W * es),
+                        rng("cu_seqlens", cu_seqlens, cu_seqlens ? 4u * (n_seqs + 1) : 0)};
+    const Range out[] = {rng("y", y, N * D * es)};
+    DSC_TRY(check_alias(in, 3, out, 1));
+    dsc::HwProblem p{dt, B * T, T, D, W, H, x, w, nullptr, y, nullptr, nullptr, cu_seqlens, n_seqs, residual};
+    return launched(dsc::headwise_fwd(p, (hipStream_t)stream), "dsc_headwise_fwd launch");
+}
+
+dsc_status dsc_headwise_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                            int32_t H, const void *x, const void *w, const void *dy,
+                            const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual,
+                            void *dx, void *dw) {
+    DSC_TRY(check_common(dtype, B, T, D, W, cu_seqlens, n_seqs, residual));
+    if (!x || !w || !dy || !dx || !dw) return fail(DSC_ERR_NULL, "x, w, dy, dx and dw are required");
+    if (H < 1 || D % H) return fail(DSC_ERR_SHAPE, "H = %d must divide D = %lld", H, (long long)D);
+    const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
+    if (!dsc::headwise_supported(dt, D, H)) return fail(DSC_ERR_UNSUPPORTED, "H = %d not supported", H);
+    if (!aligned16(x) || !aligned16(w) || !aligned16(dy) || !aligned16(dx) || !aligned16(dw))
+        return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    const size_t es = esize(dtype), N = (size_t)(B * T);
+    const size_t wb = N * (D / H) * W * es;
+    const Range in[] = {rng("x", x, N * D * es), rng("w", w, wb), rng("dy", dy, N * D * es),
+                        rng("cu_seqlens", cu_seqlens, cu_seqlens ? 4u * (n_seqs + 1) : 0)};
+    const Range out[] = {rng("dx", dx, N * D * es), rng("dw", dw, wb)};
+    DSC_TRY(check_alias(in, 4, out, 2));
+    dsc::HwProblem p{dt, B * T, T, D, W, H, x, w, dy, nullptr, dx, dw, cu_seqlens, n_seqs, residual};
+    return launched(dsc::headwise_bwd(p, (hipStream_t)stream), "dsc_headwise_bwd launch");
+}
+
+dsc_status dsc_lowrank_fwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                           int32_t R, const void *x, const void *z, const void *U,
+                           const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, void *y) {
+    DSC_TRY(check_common(dtype, B, T, D, W, cu_seqlens, n_seqs, residual));
+    if (!x || !z || !U || !y) return fail(DSC_ERR_NULL, "x, z, U and y are required");
+    if (R < 1 || R > 128) return fail(DSC_ERR_SHAPE, "R = %d must be in 1..128", R);
+    if (!aligned16(x) || !aligned16(z) || !aligned16(U) || !aligned16(y))
+        return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
+    const size_t es = esize(dtype), N = (size_t)(B * T);
+    const Range in[] = {rng("x", x, N * D * es), rng("z", z, N * R * es), rng("U", U, (size_t)R * D * W * es),
+                        rng("cu_seqlens", cu_seqlens, cu_seqlens ? 4u * (n_seqs + 1) : 0)};
+    const Range out[] = {rng("y", y, N * D * es)};
+    DSC_TRY(check_alias(in, 4, out, 1));
+    dsc::LrProblem p{dt, B * T, T, D, W, R, x, z, U, nullptr, y, nullptr, nullptr, nullptr, nullptr,
+                     cu_seqlens, n_seqs, residual};
+    return launched(dsc::lowrank_fwd(p, (hipStream_t)stream), "dsc_lowrank_fwd launch");
+}
+
+size_t dsc_lowrank_bwd_workspace_size(int dtype, int64_t B, int64_t T, int64_t D, int32_t W, int32_t R) {
+    if (check_common(dtype, B, T, D, W, nullptr, 0, 0) != DSC_SUCCESS || R < 1 || R > 128) return 0;
+    return dsc::lowrank_bwd_workspace(dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32, B * T, D, W, R);
+}
+
+dsc_status dsc_lowrank_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                           int32_t R, const void *x, const void *z, const void *U, const void *dy,
+                           const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, void *dx,
+                           void *dz, float *dU, void *workspace, size_t workspace_bytes) {
+    DSC_TRY(check_common(dtype, B, T, D, W, cu_seqlens, n_seqs, residual));
+    if (!x || !z || !U || !dy || !dx || !dz || !dU)
+        return fail(DSC_ERR_NULL, "x, z, U, dy, dx, dz and dU are required");
+    if (R < 1 || R > 128) return fail(DSC_ERR_SHAPE, "R = %d must be in 1..128", R);
+    if (!aligned16(x) || !aligned16(z) || !aligned16(U) || !aligned16(dy) || !aligned16(dx) ||
+        !aligned16(dz) || !aligned16(dU))
+        return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
+    const size_t need = dsc::lowrank_bwd_workspace(dt, B * T, D, W, R);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(DSC_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (!aligned16(workspace)) return fail(DSC_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+    }
+    const size_t es = esize(dtype), N = (size_t)(B * T);
+    const Range in[] = {rng("x", x, N * D * es), rng("z", z, N * R * es), rng("U", U, (size_t)R * D * W * es),
+                        rng("dy", dy, N * D * es),
+                        rng("cu_seqlens", cu_seqlens, cu_seqlens ? 4u * (n_seqs + 1) : 0)};
+    const Range out[] = {rng("dx", dx, N * D * es), rng("dz", dz, N * R * es),
+                         rng("dU", dU, (size_t)R * D * W * 4), rng("workspace", workspace, need ? need : 0)};
+    DSC_TRY(check_alias(in, 5, out, 4));
+    float *acc = need ? static_cast<float *>(workspace) : static_cast<float *>(dz);
+    dsc::LrProblem p{dt, B * T, T, D, W, R, x, z, U, dy, nullptr, dx, dz, dU, acc, cu_seqlens, n_seqs, residual};
+    return launched(dsc::lowrank_bwd(p, (hipStream_t)stream), "dsc_lowrank_bwd launch");
+}
+
+const char *dsc_status_string(int status) {
+    switch (status) {
+        case DSC_SUCCESS: return "DSC_SUCCESS";
+        case DSC_ERR_NULL: return "DSC_ERR_NULL";
+        case DSC_ERR_SHAPE: return "DSC_ERR_SHAPE";
+        case DSC_ERR_UNSUPPORTED: return "DSC_ERR_UNSUPPORTED";
+        case DSC_ERR_ALIGNMENT: return "DSC_ERR_ALIGNMENT";
+        case DSC_ERR_ALIAS: return "DSC_ERR_ALIAS";
+        case DSC_ERR_WORKSPACE: return "DSC_ERR_WORKSPACE";
+        case DSC_ERR_HIP: return "DSC_ERR_HIP";
+        default: return "DSC_UNKNOWN_STATUS";
+    }
+}
+
+const char *dsc_last_error(void) { return g_last_error; }
+
+int dsc_abi_version(void) { return DSC_ABI_VERSION; }
+
+}  // extern "C"

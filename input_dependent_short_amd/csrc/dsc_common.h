@@ -1,0 +1,210 @@
+// dsc_common.h -- device helpers shared by the dynamic short convolution
+// kernels (gfx950, wave64).  Internal to libdsc.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsc {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------- element types
+
+// Storage tags.  Values are always widened to fp32 for arithmetic.
+struct F32 {
+    using store_t = float;
+    static constexpr int kVec = 4;  // elements per 16-byte vector
+};
+struct BF16 {
+    using store_t = uint16_t;
+    static constexpr int kVec = 8;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    floatx2 f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float a) {
+    return (uint16_t)(pack_bf16x2(a, 0.f) & 0xffffu);
+}
+
+// 16-byte vector of VEC elements <-> VEC floats.
+template <class E>
+struct Vec16;
+
+template <>
+struct Vec16<F32> {
+    __device__ __forceinline__ static void load(const void *p, float (&v)[4]) {
+        float4 q = *reinterpret_cast<const float4 *>(p);
+        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    }
+    __device__ __forceinline__ static void store(void *p, const float (&v)[4]) {
+        *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+};
+
+template <>
+struct Vec16<BF16> {
+    __device__ __forceinline__ static void load(const void *p, float (&v)[8]) {
+        uint4 q = *reinterpret_cast<const uint4 *>(p);
+        v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
+        v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+        v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z);
+        v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+    }
+    __device__ __forceinline__ static void store(void *p, const float (&v)[8]) {
+        uint4 q;
+        q.x = pack_bf16x2(v[0], v[1]);
+        q.y = pack_bf16x2(v[2], v[3]);
+        q.z = pack_bf16x2(v[4], v[5]);
+        q.w = pack_bf16x2(v[6], v[7]);
+        *reinterpret_cast<uint4 *>(p) = q;
+    }
+};
+
+// One element widened to fp32.
+template <class E>
+__device__ __forceinline__ float load_elem(const typename E::store_t *p) {
+    if constexpr (sizeof(typename E::store_t) == 4) return *p;
+    else return __uint_as_float((uint32_t)*p << 16);
+}
+
+// Largest power of two <= 16 dividing n.
+__host__ __device__ constexpr int pow2_align(int n) {
+    return (n % 16 == 0) ? 16 : (n % 8 == 0) ? 8 : (n % 4 == 0) ? 4 : (n % 2 == 0) ? 2 : 1;
+}
+
+// Contiguous span of NE elements starting at an address aligned to ALIGN bytes:
+// loaded / stored with the widest aligned accesses.
+template <class E, int NE>
+struct Span {
+    using S = typename E::store_t;
+    static constexpr int kBytes = NE * (int)sizeof(S);
+
+    template <int ALIGN>
+    __device__ __forceinline__ static void load(const S *p, float (&v)[NE]) {
+        constexpr int A = ALIGN < kBytes ? ALIGN : pow2_align(kBytes);
+        constexpr int PER = A / (int)sizeof(S) > 0 ? A / (int)sizeof(S) : 1;
+        static_assert(NE % PER == 0, "span split");
+#pragma unroll
+        for (int i = 0; i < NE; i += PER) {
+            if constexpr (A >= 16) {
+                uint4 q = *reinterpret_cast<const uint4 *>(p + i);
+                unpack<4>(&q.x, v, i);
+            } else if constexpr (A == 8) {
+                uint2 q = *reinterpret_cast<const uint2 *>(p + i);
+                unpack<2>(&q.x, v, i);
+            } else if constexpr (A == 4) {
+                uint32_t q = *reinterpret_cast<const uint32_t *>(p + i);
+                unpack<1>(&q, v, i);
+            } else {
+                v[i] = widen(p[i]);
+            }
+        }
+    }
+
+    template <int ALIGN>
+    __device__ __forceinline__ static void store(S *p, const float (&v)[NE]) {
+        constexpr int A = ALIGN < kBytes ? ALIGN : pow2_align(kBytes);
+        constexpr int PER = A / (int)sizeof(S) > 0 ? A / (int)sizeof(S) : 1;
+#pragma unroll
+        for (int i = 0; i < NE; i += PER) {
+            if constexpr (A >= 16) {
+                uint4 q;
+                pack<4>(&q.x, v, i);
+                *reinterpret_cast<uint4 *>(p + i) = q;
+            } else if constexpr (A == 8) {
+                uint2 q;
+                pack<2>(&q.x, v, i);
+                *reinterpret_cast<uint2 *>(p + i) = q;
+            } else if constexpr (A == 4) {
+                uint32_t q;
+                pack<1>(&q, v, i);
+                *reinterpret_cast<uint32_t *>(p + i) = q;
+            } else {
+                p[i] = narrow(v[i]);
+            }
+        }
+    }
+
+   private:
+    __device__ __forceinline__ static float widen(S s) {
+        if constexpr (sizeof(S) == 4) return __builtin_bit_cast(float, s);
+        else return __uint_as_float((uint32_t)s << 16);
+    }
+    __device__ __forceinline__ static S narrow(float f) {
+        if constexpr (sizeof(S) == 4) return f;
+        else return to_bf16(f);
+    }
+    template <int NW>
+    __device__ __forceinline__ static void unpack(const uint32_t *q, float (&v)[NE], int i) {
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            if constexpr (sizeof(S) == 4) {
+                v[i + j] = __uint_as_float(q[j]);
+            } else {
+                v[i + 2 * j] = bf16_lo(q[j]);
+                v[i + 2 * j + 1] = bf16_hi(q[j]);
+            }
+        }
+    }
+    template <int NW>
+    __device__ __forceinline__ static void pack(uint32_t *q, const float (&v)[NE], int i) {
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            if constexpr (sizeof(S) == 4) q[j] = __float_as_uint(v[i + j]);
+            else q[j] = pack_bf16x2(v[i + 2 * j], v[i + 2 * j + 1]);
+        }
+    }
+};
+
+// ----------------------------------------------------------- sequences
+
+// Sequence [start, end) on the flattened token axis that contains token n.
+// Without offsets every row of T tokens is one sequence; otherwise binary
+// search of cu[0..n_seqs] (cu[0] = 0, cu[n_seqs] = N, increasing).
+struct SeqMap {
+    const int32_t *cu;
+    int32_t n_seqs;
+    int64_t T;
+
+    __device__ __forceinline__ void find(int64_t n, int64_t &start, int64_t &end) const {
+        if (cu == nullptr) {
+            start = (n / T) * T;
+            end = start + T;
+            return;
+        }
+        int lo = 0, hi = n_seqs;  // invariant: cu[lo] <= n < cu[hi]
+        while (hi - lo > 1) {
+            int mid = (lo + hi) >> 1;
+            if ((int64_t)cu[mid] <= n) lo = mid;
+            else hi = mid;
+        }
+        start = cu[lo];
+        end = cu[lo + 1];
+    }
+};
+
+// Workgroup id remapped so that consecutive logical blocks run on the same
+// XCD: the dispatcher hands block b to XCD b % 8, and neighbouring tiles share
+// halo rows that then stay in that XCD's L2.  Bijective for any grid size.
+__device__ __forceinline__ int64_t xcd_block_id(int64_t b, int64_t nblocks) {
+    constexpr int kXcd = 8;
+    int64_t q = nblocks / kXcd, r = nblocks % kXcd;
+    int64_t x = b % kXcd;
+    int64_t start = x * q + (x < r ? x : r);
+    return start + b / kXcd;
+}
+
+}  // namespace dsc

@@ -1,0 +1,50 @@
+// dsc_kernels.h -- launchers of the dynamic short convolution kernels.
+// Internal to libdsc.so; the public surface is include/dsc.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dsc_common.h"
+
+namespace dsc {
+
+enum class Dtype { F32 = 0, BF16 = 1 };
+
+// Head-wise problem (validated by the API layer).
+struct HwProblem {
+    Dtype dtype;
+    int64_t N, T, D;
+    int32_t W, H;
+    const void *x, *w, *dy;
+    void *y, *dx, *dw;
+    const int32_t *cu;
+    int32_t n_seqs;
+    int32_t residual;
+};
+
+// Low-rank problem.
+struct LrProblem {
+    Dtype dtype;
+    int64_t N, T, D;
+    int32_t W, R;
+    const void *x, *z, *U, *dy;
+    void *y, *dx, *dz;
+    float *dU;
+    float *dz_acc;  // fp32 accumulator (workspace) when dz is not fp32
+    const int32_t *cu;
+    int32_t n_seqs;
+    int32_t residual;
+};
+
+// Head-wise: whether this build has a kernel for (dtype, H).
+bool headwise_supported(Dtype dt, int64_t D, int32_t H);
+
+hipError_t headwise_fwd(const HwProblem &p, hipStream_t s);
+hipError_t headwise_bwd(const HwProblem &p, hipStream_t s);
+
+size_t lowrank_bwd_workspace(Dtype dt, int64_t N, int64_t D, int32_t W, int32_t R);
+hipError_t lowrank_fwd(const LrProblem &p, hipStream_t s);
+hipError_t lowrank_bwd(const LrProblem &p, hipStream_t s);
+
+}  // namespace dsc

@@ -1,0 +1,111 @@
+"""The C ABI of libdsc.so: exported symbols and host-side argument checks (CPU only).
+
+Every call below fails validation, which the library performs before any HIP
+call, so no GPU is touched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsc.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from input_dependent_short_amd import binding, build
+    if not os.path.exists(binding.LIB_PATH):
+        build.build()
+    return binding.lib()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"DSC_API\s+[\w\s\*]+?\b(dsc_\w+)\s*\(", text)
+
+
+def test_header_declares_the_entry_points():
+    syms = set(declared_symbols())
+    for s in ("dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd",
+              "dsc_lowrank_bwd_workspace_size", "dsc_status_string", "dsc_last_error",
+              "dsc_abi_version"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for s in declared_symbols():
+        assert hasattr(lib, s), f"{s} not exported"
+    assert lib.dsc_abi_version() == 1
+    assert lib.dsc_status_string(5) == b"DSC_ERR_ALIAS"
+
+
+A = 1 << 20          # fake, 16-byte aligned device addresses (never dereferenced)
+P = lambda k: ctypes.c_void_p(A * k)
+S0 = ctypes.c_void_p(0)
+
+
+def hw_fwd(lib, dtype=1, B=1, T=8, D=64, W=4, H=8, x=P(1), w=P(2), cu=None, ns=0, res=0, y=P(3)):
+    return lib.dsc_headwise_fwd(S0, dtype, B, T, D, W, H, x, w, cu, ns, res, y)
+
+
+def test_headwise_fwd_validation(lib):
+    assert hw_fwd(lib, x=None) == 1
+    assert hw_fwd(lib, W=0) == 2 and hw_fwd(lib, W=9) == 2
+    assert hw_fwd(lib, D=60) == 2                 # bf16 needs D % 8 == 0
+    assert hw_fwd(lib, H=7) == 2                  # H must divide D
+    assert hw_fwd(lib, D=48, H=24) == 3           # 3 lanes per group: not built
+    assert hw_fwd(lib, dtype=7) == 3
+    assert hw_fwd(lib, B=0) == 2
+    assert hw_fwd(lib, x=ctypes.c_void_p(A + 2)) == 4
+    assert hw_fwd(lib, y=P(1)) == 5               # in place
+    assert hw_fwd(lib, y=ctypes.c_void_p(A + 64)) == 5   # partial overlap with x
+    assert b"overlaps" in lib.dsc_last_error()
+    assert hw_fwd(lib, res=2) == 2
+    assert hw_fwd(lib, cu=P(9), ns=0) == 2        # pointer without count
+
+
+def test_headwise_fwd_fp32_shape_reaches_launch_only_when_valid(lib):
+    # fp32, D=60, H=4: valid shape; aliasing makes it fail before any HIP call
+    assert hw_fwd(lib, dtype=0, D=60, H=4, y=P(1)) == 5
+
+
+def test_headwise_bwd_validation(lib):
+    f = lambda **k: lib.dsc_headwise_bwd(S0, 1, 1, 8, 64, 4, 8, k.get("x", P(1)), k.get("w", P(2)),
+                                         k.get("dy", P(3)), None, 0, 0, k.get("dx", P(4)),
+                                         k.get("dw", P(5)))
+    assert f(dw=None) == 1
+    assert f(dx=P(3)) == 5                        # dx aliases dy
+    assert f(dw=P(4)) == 5                        # outputs overlap
+    assert f(x=ctypes.c_void_p(A * 1 + 8)) == 4
+
+
+def lr_bwd(lib, ws=P(8), wsb=1 << 20, **k):
+    return lib.dsc_lowrank_bwd(S0, 1, 1, 8, 64, 4, k.get("R", 16), P(1), P(2), P(3), P(4), None, 0, 0,
+                               k.get("dx", P(5)), k.get("dz", P(6)), k.get("dU", P(7)), ws, wsb)
+
+
+def test_lowrank_validation(lib):
+    assert lib.dsc_lowrank_fwd(S0, 1, 1, 8, 64, 4, 0, P(1), P(2), P(3), None, 0, 0, P(4)) == 2
+    assert lib.dsc_lowrank_fwd(S0, 1, 1, 8, 64, 4, 129, P(1), P(2), P(3), None, 0, 0, P(4)) == 2
+    assert lib.dsc_lowrank_fwd(S0, 1, 1, 8, 64, 4, 16, P(1), None, P(3), None, 0, 0, P(4)) == 1
+    assert lib.dsc_lowrank_fwd(S0, 1, 1, 8, 64, 4, 16, P(1), P(2), P(3), None, 0, 0, P(3)) == 5
+    need = lib.dsc_lowrank_bwd_workspace_size(1, 1, 8, 64, 4, 16)
+    assert need >= 8 * 16 * 4
+    assert lib.dsc_lowrank_bwd_workspace_size(0, 1, 8, 64, 4, 16) == 0   # fp32 accumulates in dz
+    assert lib.dsc_lowrank_bwd_workspace_size(1, 1, 8, 63, 4, 16) == 0   # invalid sizes
+    assert lr_bwd(lib, ws=None, wsb=0) == 6
+    assert lr_bwd(lib, wsb=need - 1) == 6
+    assert lr_bwd(lib, ws=P(1)) == 5              # workspace aliases x
+    assert lr_bwd(lib, dU=P(5)) == 5
+    assert lr_bwd(lib, dz=None) == 1
+
+
+def test_binding_raises_with_message(lib):
+    import torch
+    from input_dependent_short_amd import binding
+    x = torch.zeros(1, 8, 60, dtype=torch.bfloat16)
+    w = torch.zeros(1, 8, 60, 4, dtype=torch.bfloat16)
+    with pytest.raises(binding.DscError, match="multiple of 8"):
+        binding.dsc_headwise_fwd(x, w, x, stream=0)

@@ -1,0 +1,184 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small shapes are compared element by element over every output; the five
+workloads run at full size and are compared on sampled token windows (all
+channels) and sampled channel ranges (dU, all tokens), plus full-size
+invariants (every element written, guard bands intact).  Tolerance: normwise
+max-relative error max|gpu - ref| / max|ref| <= 1e-5 (fp32) or 2e-2 (bf16
+inputs, fp32 accumulation).
+"""
+from __future__ import annotations
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, assert_close, run_headwise, run_lowrank, say
+from input_dependent_short_amd import binding, inputs
+from input_dependent_short_amd.inputs import to_f64
+
+pytestmark = pytest.mark.gpu
+
+# (dtype, B, T, D, W, H, residual, segment-length range or None)
+HW_CASES = [
+    ("fp32", 1, 64, 64, 4, 1, False, None),
+    ("fp32", 2, 37, 32, 3, 4, True, None),
+    ("fp32", 1, 2, 16, 4, 2, False, None),
+    ("fp32", 2, 50, 96, 8, 8, True, (1, 9)),
+    ("fp32", 1, 33, 256, 4, 256, False, None),
+    ("bf16", 2, 100, 128, 4, 64, True, None),
+    ("bf16", 1, 77, 64, 4, 16, False, (1, 20)),
+    ("bf16", 3, 19, 48, 1, 8, True, None),
+    ("bf16", 2, 45, 256, 2, 1, False, None),
+    ("bf16", 1, 130, 64, 5, 2, True, (1, 40)),
+    ("bf16", 2, 66, 512, 7, 4, False, None),
+    ("bf16", 1, 40, 1024, 4, 512, True, None),
+    ("bf16", 1, 3, 40, 8, 8, True, None),
+    ("bf16", 4, 65, 2304, 4, 64, True, None),
+    ("bf16", 2, 300, 8192, 4, 16, True, (1, 120)),
+]
+
+# (dtype, B, T, D, W, R, residual, segment-length range or None)
+LR_CASES = [
+    ("fp32", 1, 20, 16, 4, 3, False, None),
+    ("fp32", 2, 33, 32, 3, 8, True, (1, 7)),
+    ("fp32", 1, 9, 8, 1, 1, False, None),
+    ("bf16", 1, 64, 32, 4, 32, False, None),
+    ("bf16", 2, 77, 64, 4, 64, True, None),
+    ("bf16", 1, 100, 40, 4, 5, False, (1, 30)),
+    ("bf16", 2, 31, 96, 3, 100, True, None),
+    ("bf16", 1, 50, 128, 8, 1, False, (1, 9)),
+    ("bf16", 1, 2, 32, 4, 16, False, None),
+    ("bf16", 3, 130, 512, 4, 32, False, None),
+    ("bf16", 1, 200, 128, 2, 128, True, (1, 50)),
+    ("bf16", 1, 130, 512, 4, 64, False, (1, 60)),
+]
+
+
+def _ids(cases, tag):
+    return [f"{tag}-{c[0]}-B{c[1]}T{c[2]}D{c[3]}W{c[4]}{'H' if tag == 'hw' else 'R'}{c[5]}"
+            f"-res{int(c[6])}-{'varlen' if c[7] else 'rows'}" for c in cases]
+
+
+@pytest.mark.parametrize("case", HW_CASES, ids=_ids(HW_CASES, "hw"))
+def test_headwise_small(case):
+    dt, B, T, D, W, H, res, seg = case
+    wl, inp = inputs.small("headwise", B, T, D, W, H=H, dtype=dt, residual=res, varlen=seg is not None,
+                           seglen_range=seg or (1, 8), seed=zlib.crc32(repr(case).encode()) % 1000)
+    say(f"[headwise] {wl.name} residual={res} segments={inp['cu_seqlens']}")
+    y, dx, dw = run_headwise(inp, res)
+    cu = inp["cu_seqlens"]
+    x64, w64, g64 = to_f64(inp["x"]), to_f64(inp["w"]), to_f64(inp["dy"])
+    ry = oracle.headwise_fwd(x64, w64, cu_seqlens=cu, residual=res)
+    rdx, rdw = oracle.headwise_bwd(x64, w64, g64, cu_seqlens=cu, residual=res)
+    tol = TOL[dt]
+    assert_close("y", y, ry, tol)
+    assert_close("dx", dx, rdx, tol)
+    assert_close("dw", dw, rdw, tol)
+
+
+@pytest.mark.parametrize("case", LR_CASES, ids=_ids(LR_CASES, "lr"))
+def test_lowrank_small(case):
+    dt, B, T, D, W, R, res, seg = case
+    wl, inp = inputs.small("lowrank", B, T, D, W, R=R, dtype=dt, residual=res, varlen=seg is not None,
+                           seglen_range=seg or (1, 8), seed=zlib.crc32(repr(case).encode()) % 1000)
+    say(f"[lowrank] {wl.name} residual={res} segments={inp['cu_seqlens']}")
+    y, dx, dz, dU = run_lowrank(inp, W, res, repeat_bwd=2)
+    cu = inp["cu_seqlens"]
+    x64, z64, U64, g64 = (to_f64(inp[k]) for k in ("x", "z", "U", "dy"))
+    ry = oracle.lowrank_fwd(x64, z64, U64, W, cu_seqlens=cu, residual=res)
+    rdx, rdz, rdU = oracle.lowrank_bwd(x64, z64, U64, g64, W, cu_seqlens=cu, residual=res)
+    tol = TOL[dt]
+    assert_close("y", y, ry, tol)
+    assert_close("dx", dx, rdx, tol)
+    assert_close("dz", dz, rdz, tol)
+    assert_close("dU", dU, rdU, tol)
+
+
+def test_headwise_repeat_is_bitwise_identical():
+    wl, inp = inputs.small("headwise", 2, 300, 1024, 4, H=16, dtype="bf16", residual=True, seed=5)
+    say(f"[headwise determinism] {wl.name}")
+    a = run_headwise(inp, True)
+    b = run_headwise(inp, True)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+# ------------------------------------------------------------ full workloads
+
+
+def _windows(N: int, cu) -> list[tuple[int, int]]:
+    """Sampled token windows: start, middle, end, and around segment starts."""
+    wins = [(0, 24), (N // 2 - 7, N // 2 + 17), (N - 24, N)]
+    if cu is not None:
+        starts = [int(s) for s in cu[1:-1]]
+        for s in starts[:: max(1, len(starts) // 3)][:3]:
+            wins.append((max(0, s - 12), min(N, s + 12)))
+    return wins
+
+
+def _channels(D: int) -> list[tuple[int, int]]:
+    return [(0, 8), (D // 2 - 4, D // 2 + 4), (D - 8, D)]
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_workload_full_size(cfg):
+    wl = inputs.WORKLOADS[cfg]
+    say(f"[workload {cfg}] {wl.name}: B={wl.B} T={wl.T} D={wl.D} W={wl.W} H={wl.H} R={wl.R} "
+        f"{wl.dtype} residual={wl.residual} varlen={wl.varlen}")
+    inp = inputs.make_inputs(wl)
+    cu = inp["cu_seqlens"]
+    tol = TOL[wl.dtype]
+    N, D = wl.N, wl.D
+    x64, g64 = to_f64(inp["x"]), to_f64(inp["dy"])
+    if wl.kind == "headwise":
+        y, dx, dw = run_headwise(inp, wl.residual)
+        w64 = to_f64(inp["w"])
+        G = D // wl.H
+        y, dx, dw = y.reshape(N, D), dx.reshape(N, D), dw.reshape(N, G, wl.W)
+        for lo, hi in _windows(N, cu) if cfg != 1 else [(0, N)]:
+            say(f"  rows [{lo},{hi})")
+            ry = oracle.headwise_fwd(x64, w64, cu_seqlens=cu, residual=wl.residual, rows=(lo, hi))
+            rdx, rdw = oracle.headwise_bwd(x64, w64, g64, cu_seqlens=cu, residual=wl.residual, rows=(lo, hi))
+            assert_close("y", y[lo:hi], ry, tol)
+            assert_close("dx", dx[lo:hi], rdx, tol)
+            assert_close("dw", dw[lo:hi], rdw, tol)
+    else:
+        W, R = wl.W, wl.R
+        y, dx, dz, dU = run_lowrank(inp, W, wl.residual)
+        z64, U64 = to_f64(inp["z"]), to_f64(inp["U"])
+        y, dx, dz = y.reshape(N, D), dx.reshape(N, D), dz.reshape(N, R)
+        for lo, hi in _windows(N, cu):
+            say(f"  rows [{lo},{hi})")
+            ry = oracle.lowrank_fwd(x64, z64, U64, W, cu_seqlens=cu, residual=wl.residual, rows=(lo, hi))
+            rdx, rdz, _ = oracle.lowrank_bwd(x64, z64, U64, g64, W, cu_seqlens=cu, residual=wl.residual,
+                                             rows=(lo, hi), channels=(0, 0))
+            assert_close("y", y[lo:hi], ry, tol)
+            assert_close("dx", dx[lo:hi], rdx, tol)
+            assert_close("dz", dz[lo:hi], rdz, tol)
+        dU3 = dU.reshape(R, D, W)
+        for c0, c1 in _channels(D):
+            say(f"  dU channels [{c0},{c1})")
+            _, _, rdU = oracle.lowrank_bwd(x64, z64, U64, g64, W, cu_seqlens=cu, residual=wl.residual,
+                                           rows=(0, 0), channels=(c0, c1))
+            assert_close("dU", dU3[:, c0:c1].reshape(R, (c1 - c0) * W), rdU, tol)
+
+
+def test_stream_argument_is_honoured():
+    """Calls on a side stream complete in order on that stream."""
+    wl, inp = inputs.small("headwise", 1, 256, 512, 4, H=8, dtype="bf16", residual=True, seed=9)
+    say(f"[stream] {wl.name}")
+    x, w = inp["x"].cuda(), inp["w"].cuda()
+    y1 = torch.empty_like(x)
+    y2 = torch.empty_like(x)
+    binding.dsc_headwise_fwd(x, w, y1, residual=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        binding.dsc_headwise_fwd(x, w, y2, residual=True, stream=s)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
