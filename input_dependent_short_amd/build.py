@@ -29,16 +29,32 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(out: str = LIB, verbose: bool = False, extra: list[str] | None = None) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    cmd = [hipcc, *FLAGS, *(extra or []), f"-I{os.path.join(ROOT, 'include')}", *sources(),
-           "-o", out + ".tmp"]
+def _run(cmd: list[str], verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with code {res.returncode}")
+        raise RuntimeError(f"hipcc failed with code {res.returncode}: {' '.join(cmd)}")
+
+
+def build(out: str = LIB, verbose: bool = False, extra: list[str] | None = None) -> str:
+    """Compile every HIP source (in parallel) and link libdsc.so."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    inc = f"-I{os.path.join(ROOT, 'include')}"
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    jobs = []
+    for src in sources():
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        jobs.append(([hipcc, *compile_flags, *(extra or []), inc, "-c", src, "-o", obj], obj))
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(lambda j: _run(j[0], verbose), jobs))
+    _run([hipcc, *FLAGS, *(extra or []), *[o for _, o in jobs], "-o", out + ".tmp"], verbose)
     os.replace(out + ".tmp", out)
     return out
 

@@ -185,7 +185,7 @@ __device__ __forceinline__ void fill_shift(Shifted<W> &xs, const uint32_t (&cur)
 template <int W, int RC, int PF>
 __global__ __launch_bounds__(kBlock) void lr_fwd_mfma(LrParams p, int64_t nslices, int64_t tok_per_wave) {
     const int lane = threadIdx.x & 63;
-    const int64_t wave = (int64_t)blockIdx.x * (kBlock / kWave) + (threadIdx.x >> 6);
+    const int64_t wave = (int64_t)blockIdx.x * (kBlock / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t tchunk = wave / nslices;
     const int64_t slice = wave - tchunk * nslices;
     const int64_t d0 = slice * 32;
@@ -273,6 +273,9 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_mfma(LrParams p, int64_t nslice
         }
     }
 
+    SeqCursor seqc;
+    seqc.init(p.seq, nbeg);
+
     uint32_t xq[PF][4];
     bf16x8 zq[PF][RC];
 #pragma unroll
@@ -313,9 +316,8 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_mfma(LrParams p, int64_t nslice
                 fill_shift<W, 1>(xs, xc, xprev);
 
                 // sequence masking: only when a boundary can touch this step
-                int64_t s0, e0;
-                p.seq.find(nstep, s0, e0);
-                const bool clean = (e0 >= nstep + 16) && (nstep - s0 >= W - 1);
+                seqc.advance(nstep);
+                const bool clean = (seqc.e >= nstep + 16) && (nstep - seqc.s >= W - 1);
                 if (!clean) {
                     int64_t s, e;
                     p.seq.find(n < p.N ? n : p.N - 1, s, e);
@@ -353,6 +355,428 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_mfma(LrParams p, int64_t nslice
             }
         }
     }
+}
+
+// Look-ahead shift inside a 16-lane row: lane i takes lane i+K of `cur`, and
+// lanes i >= 16-K take lane i+K-16 of `next` (the following 16 tokens).
+template <int K>
+__device__ __forceinline__ uint32_t shift_ahead_in_row(uint32_t cur, uint32_t next) {
+    const int rot = __builtin_amdgcn_mov_dpp((int)next, 0x120 + (16 - K), 0xf, 0xf, true);
+    return (uint32_t)__builtin_amdgcn_update_dpp(rot, (int)cur, 0x100 + K, 0xf, 0xf, false);
+}
+
+template <int W, int K>
+__device__ __forceinline__ void fill_ahead(Shifted<W> &gs, const uint32_t (&cur)[4], const uint32_t (&next)[4]) {
+    if constexpr (K < W) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gs.v[K][i] = shift_ahead_in_row<K>(cur[i], next[i]);
+        fill_ahead<W, K + 1>(gs, cur, next);
+    }
+}
+
+// Shift by a tap k (1 <= k < W, known after unrolling) of four packed registers.
+template <int W, int K = 1>
+__device__ __forceinline__ void shift_ahead4(int k, const uint32_t (&cur)[4], const uint32_t (&next)[4],
+                                             uint32_t (&out)[4]) {
+    if constexpr (K < W) {
+        if (k == K) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) out[i] = shift_ahead_in_row<K>(cur[i], next[i]);
+        } else {
+            shift_ahead4<W, K + 1>(k, cur, next, out);
+        }
+    }
+}
+
+template <int W, int K = 1>
+__device__ __forceinline__ void shift_back4(int k, const uint32_t (&cur)[4], const uint32_t (&prev)[4],
+                                            uint32_t (&out)[4]) {
+    if constexpr (K < W) {
+        if (k == K) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) out[i] = shift_in_row<K>(cur[i], prev[i]);
+        } else {
+            shift_back4<W, K + 1>(k, cur, prev, out);
+        }
+    }
+}
+
+__device__ __forceinline__ bf16x8 bf16x8_from_u32(const uint32_t (&v)[4]) {
+    uint4 q = make_uint4(v[0], v[1], v[2], v[3]);
+    return __builtin_bit_cast(bf16x8, q);
+}
+
+// Backward of the fused low-rank convolution, bf16.
+//
+// Block = 4 waves, one 32-channel slice each, walking the same token range
+// in steps of 16 tokens (pairs of steps = 32 tokens for the token
+// contraction of dU).  Per step and wave:
+//   * w of tokens n+k (k < W) on the matrix cores, B operand = z rows n+k
+//     read from an LDS ring of z rows (A = U_k^T kept in registers);
+//   * dx = rho*g + sum_k w_k * g shifted ahead by k (DPP with the next step);
+//   * dwc_k = g * x shifted back by k (DPP with the previous step), rounded
+//     to bf16 -- it is directly the B operand of dz^T = U_k * dwc_k, whose A
+//     operand (U_k, rank rows x channel K) is also kept in registers;
+//   * dwc_k is staged in LDS and re-read transposed (lane = channel,
+//     registers = tokens) as the A operand of dU_k^T += dwc_k^T * Z.
+// dz is summed over the block's 4 waves in LDS, then added to an fp32
+// accumulator with one atomic per (token, rank); dU stays in registers over
+// the whole token range and is added to the fp32 output with atomics at the
+// end.  Both accumulators are zeroed by the launcher first.
+template <int W, int RC>
+struct BwdLds {
+    static constexpr int RP = 32 * RC;           // padded rank
+    static constexpr int PW = 72;                // bytes per token row of dwc^T (32 ch + pad, 8-aligned)
+    static constexpr int PZ = 2 * RP + 8;        // bytes per z row
+    static constexpr int SZ = 16 * PZ + 32;      // bytes per z ring slot (16 rows)
+    static constexpr int PD = 4 * RP + 16;       // bytes per token row of dz partials
+    static constexpr int kDwc = W * 32 * PW;
+    static constexpr int kZ = 4 * SZ;
+    static constexpr int kDz = 2 * 32 * PD;      // double-buffered pair of steps
+    static constexpr int kLoop = kDwc + kZ + kDz;
+    static constexpr int kDuStage = RP * 32 * W * 4;   // dU tile staged for coalesced atomics
+    static constexpr int kWave = (((kLoop > kDuStage ? kLoop : kDuStage) + 15) / 16) * 16;
+    static constexpr int kBlock = 4 * kWave;
+};
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group,
+// lane i receives element (i & 3) of the 8-byte chunks addressed by lanes
+// i/4, 4 + i/4, 8 + i/4 and 12 + i/4.  Addressing lane i at row base + i/4,
+// column col0 + 4*(i & 3) of a row-major [row][col] bf16 array therefore
+// returns rows base .. base+3 of column col0 + i.
+__device__ __forceinline__ uint2 lds_read_tr(const unsigned char *addr) {
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(addr));
+    return __builtin_bit_cast(uint2, v);
+}
+
+template <int W, int RC>
+__global__ __launch_bounds__(kBlock, 1) void lr_bwd_mfma(LrParams p, int64_t nslices, int64_t tok_per_block) {
+    using L = BwdLds<W, RC>;
+    constexpr int RT = 2 * RC;  // 16-row rank tiles
+    __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBlock];
+
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t ngroups = (nslices + 3) / 4;
+    const int64_t tchunk = blockIdx.x / ngroups;
+    const int64_t group = blockIdx.x - tchunk * ngroups;
+    const int64_t d0 = (group * 4 + wid) * 32;
+    const int64_t nbeg = tchunk * tok_per_block;
+    const int64_t nend = min(nbeg + tok_per_block, p.N);
+    const int64_t npairs = (nend - nbeg + 31) / 32;
+
+    const int tok = lane & 15;
+    const int q = lane >> 4;
+    const int i16 = lane & 15;
+    const int64_t cbase = d0 + 8 * q;
+    const bool chan_ok = cbase < p.D;
+    const int R = p.R;
+    const int64_t N = p.N;
+    const int64_t DW = p.D * W;
+
+    const uint16_t *x = static_cast<const uint16_t *>(p.x);
+    const uint16_t *g = static_cast<const uint16_t *>(p.dy);
+    const uint16_t *z = static_cast<const uint16_t *>(p.z);
+    const uint16_t *U = static_cast<const uint16_t *>(p.U);
+    uint16_t *dx = static_cast<uint16_t *>(p.dx);
+
+    unsigned char *my = lds + wid * L::kWave;
+    unsigned char *dwcT = my;                       // [k][32 tokens][PW]
+    unsigned char *zring = my + L::kDwc;            // [4 slots][16 rows][PZ]
+    unsigned char *dzb = my + L::kDwc + L::kZ;      // [2][32 tokens][PD]
+
+    // ---- U operands, kept in registers for the whole walk
+    bf16x8 ua[W][2][RC];  // rows: channel d0 + 8(i>>2) + 4t + (i&3); K: rank 32c + 8(lane>>4) + e
+    bf16x8 ub[W][RT];     // rows: rank 16rt + (lane&15); K: channel d0 + 8(lane>>4) + e
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int64_t ch = d0 + 8 * (i16 >> 2) + 4 * t + (i16 & 3);
+#pragma unroll
+            for (int c = 0; c < RC; ++c)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int r = 32 * c + 8 * q + e;
+                    const uint16_t v = (r < R && ch < p.D) ? U[(int64_t)r * DW + ch * W + k] : (uint16_t)0;
+                    ua[k][t][c][e] = __builtin_bit_cast(__bf16, v);
+                }
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int r = 16 * rt + i16;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int64_t ch = d0 + 8 * q + e;
+                const uint16_t v = (r < R && ch < p.D) ? U[(int64_t)r * DW + ch * W + k] : (uint16_t)0;
+                ub[k][rt][e] = __builtin_bit_cast(__bf16, v);
+            }
+        }
+    }
+    floatx4 du[W][2][RT];
+#pragma unroll
+    for (int k = 0; k < W; ++k)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) du[k][ct][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    auto load_act = [&](const uint16_t *src, int64_t n, uint32_t (&dst)[4]) {
+        if (n >= 0 && n < N && chan_ok) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(src + n * p.D + cbase);
+            dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+        } else {
+            dst[0] = dst[1] = dst[2] = dst[3] = 0u;
+        }
+    };
+    const bool r_vec = (R % 8) == 0;
+    // z row n, rank 32c + 8q .. +7 for c < RC (zero outside [0,N) x [0,R))
+    auto load_z = [&](int64_t n, uint32_t (&dst)[RC][4]) {
+#pragma unroll
+        for (int c = 0; c < RC; ++c) {
+            const int r0 = 32 * c + 8 * q;
+            if (n < N && r0 < R) {
+                if (r_vec) {
+                    const uint4 v = *reinterpret_cast<const uint4 *>(z + n * R + r0);
+                    dst[c][0] = v.x; dst[c][1] = v.y; dst[c][2] = v.z; dst[c][3] = v.w;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t lo = (r0 + 2 * e < R) ? z[n * R + r0 + 2 * e] : 0u;
+                        const uint32_t hi = (r0 + 2 * e + 1 < R) ? z[n * R + r0 + 2 * e + 1] : 0u;
+                        dst[c][e] = lo | (hi << 16);
+                    }
+                }
+            } else {
+                dst[c][0] = dst[c][1] = dst[c][2] = dst[c][3] = 0u;
+            }
+        }
+    };
+    auto zslot = [&](int64_t step) { return zring + (int)(step & 3) * L::SZ; };
+    auto write_z = [&](int64_t step, const uint32_t (&v)[RC][4]) {
+        unsigned char *row = zslot(step) + tok * L::PZ;
+#pragma unroll
+        for (int c = 0; c < RC; ++c) {
+            uint2 *d = reinterpret_cast<uint2 *>(row + 2 * (32 * c + 8 * q));
+            d[0] = make_uint2(v[c][0], v[c][1]);
+            d[1] = make_uint2(v[c][2], v[c][3]);
+        }
+    };
+
+    // ---- prologue: x two steps ahead, dy three, z rows three (written to the
+    // LDS ring one step ahead of use)
+    uint32_t xprev[4], xc[4], xn[4], xn2[4], gc[4], gn[4], gn2[4], gn3[4];
+    uint32_t zr[RC][4], zr2[RC][4];
+    if (tok >= 16 - (W - 1)) load_act(x, nbeg - 16 + tok, xprev);
+    else xprev[0] = xprev[1] = xprev[2] = xprev[3] = 0u;
+    load_act(x, nbeg + tok, xc);
+    load_act(x, nbeg + 16 + tok, xn);
+    load_act(g, nbeg + tok, gc);
+    load_act(g, nbeg + 16 + tok, gn);
+    load_act(g, nbeg + 32 + tok, gn2);
+    load_z(nbeg + tok, zr);
+    write_z(0, zr);
+    load_z(nbeg + 16 + tok, zr);
+    load_z(nbeg + 32 + tok, zr2);
+
+    SeqCursor seqc;
+    seqc.init(p.seq, nbeg);
+
+    const int64_t nsteps = 2 * npairs;
+    int buf = 0;
+
+    for (int64_t s = 0; s < nsteps; ++s) {
+        const int ps = (int)(s & 1);
+        const int64_t nstep = nbeg + 16 * s;
+        const int64_t n = nstep + tok;
+
+        write_z(s + 1, zr);
+        __syncthreads();  // z rows of steps s, s+1 visible to the wave
+        load_act(x, n + 32, xn2);
+        load_act(g, n + 48, gn3);
+#pragma unroll
+        for (int c = 0; c < RC; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) zr[c][i] = zr2[c][i];
+        load_z(n + 48, zr2);
+
+        // sequence masks: taps k <= back (dwc) and k < ahead (dx) stay in n's sequence
+        int back = W - 1, ahead = W;
+        seqc.advance(nstep < N ? nstep : N - 1);
+        if (!((nstep - seqc.s >= W - 1) && (seqc.e >= nstep + 16 + W - 1))) {
+            int64_t sn, en;
+            p.seq.find(n < N ? n : N - 1, sn, en);
+            back = (int)min((int64_t)(W - 1), n - sn);
+            ahead = (int)min((int64_t)W, en - n);
+        }
+
+        // dx = rho*g + sum_k w[n+k] * g[n+k]; w of tokens n+k on the matrix cores
+        float acc[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] = p.rho * ((c & 1) ? bf16_hi(gc[c >> 1]) : bf16_lo(gc[c >> 1]));
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+            const int rr = tok + k;
+            const unsigned char *zrow = zslot(s + (rr >> 4)) + (rr & 15) * L::PZ;
+            bf16x8 zb[RC];
+#pragma unroll
+            for (int c = 0; c < RC; ++c) {
+                const uint2 *src = reinterpret_cast<const uint2 *>(zrow + 2 * (32 * c + 8 * q));
+                const uint2 a = src[0], b = src[1];
+                zb[c] = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+            }
+            uint32_t gk[4];
+            if (k == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) gk[i] = gc[i];
+            } else {
+                shift_ahead4<W>(k, gc, gn, gk);
+            }
+            const float keep = k < ahead ? 1.f : 0.f;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                floatx4 cw = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < RC; ++c)
+                    cw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua[k][t][c], zb[c], cw, 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int c = 4 * t + j;
+                    const float gv = (c & 1) ? bf16_hi(gk[c >> 1]) : bf16_lo(gk[c >> 1]);
+                    acc[c] = __builtin_fmaf(cw[j] * keep, gv, acc[c]);
+                }
+            }
+        }
+        if (n < nend && chan_ok) {
+            uint4 v;
+            v.x = pack_bf16x2(acc[0], acc[1]);
+            v.y = pack_bf16x2(acc[2], acc[3]);
+            v.z = pack_bf16x2(acc[4], acc[5]);
+            v.w = pack_bf16x2(acc[6], acc[7]);
+            *reinterpret_cast<uint4 *>(dx + n * p.D + cbase) = v;
+        }
+
+        // dwc_k = g * x[n-k] (bf16): dz^T partial on the matrix cores, dwc^T staged for dU
+        const bool own = n < nend;  // tokens outside this block's range contribute nothing
+        floatx4 cz[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) cz[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+            uint32_t xk[4];
+            if (k == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xk[i] = xc[i];
+            } else {
+                shift_back4<W>(k, xc, xprev, xk);
+            }
+            uint32_t dw[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t xv = (own && k <= back) ? xk[i] : 0u;
+                dw[i] = pack_bf16x2(bf16_lo(gc[i]) * bf16_lo(xv), bf16_hi(gc[i]) * bf16_hi(xv));
+            }
+            const bf16x8 b = bf16x8_from_u32(dw);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                cz[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ub[k][rt], b, cz[rt], 0, 0, 0);
+            uint2 *d = reinterpret_cast<uint2 *>(dwcT + k * 32 * L::PW + (16 * ps + tok) * L::PW + 16 * q);
+            d[0] = make_uint2(dw[0], dw[1]);
+            d[1] = make_uint2(dw[2], dw[3]);
+        }
+        // dz partials (rows r = 16rt + 4q + j, column = token) -> LDS for the block reduction
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            float4 *d = reinterpret_cast<float4 *>(dzb + buf * 32 * L::PD + (16 * ps + tok) * L::PD +
+                                                   4 * (16 * rt + 4 * q));
+            *d = make_float4(cz[rt][0], cz[rt][1], cz[rt][2], cz[rt][3]);
+        }
+
+        if (ps == 1) {
+            __syncthreads();
+            // dU_k^T[ch, r] += sum over the pair's 32 tokens of dwc_k^T[ch, tok] * z[tok, r].
+            // Operands re-read transposed from LDS: lane = channel / rank,
+            // registers = tokens 8q .. 8q+7 of the pair.
+            const int64_t s_pair = s - 1;
+            const int trow = 8 * q + (i16 >> 2);  // row addressed by this lane (first half)
+            const int tcol = 4 * (i16 & 3);        // column chunk addressed by this lane
+            bf16x8 zb[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                uint2 h[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int row = trow + 4 * hh;
+                    h[hh] = lds_read_tr(zslot(s_pair + (row >> 4)) + (row & 15) * L::PZ + 2 * (16 * rt + tcol));
+                }
+                zb[rt] = __builtin_bit_cast(bf16x8, make_uint4(h[0].x, h[0].y, h[1].x, h[1].y));
+            }
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    uint2 h[2];
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh)
+                        h[hh] = lds_read_tr(dwcT + k * 32 * L::PW + (trow + 4 * hh) * L::PW + 2 * (16 * ct + tcol));
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(h[0].x, h[0].y, h[1].x, h[1].y));
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+                        du[k][ct][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, zb[rt], du[k][ct][rt], 0, 0, 0);
+                }
+            }
+
+            // block-wide dz reduction for the pair, one atomic per (token, rank)
+            const int64_t npair0 = nbeg + 16 * s_pair;
+            for (int e = threadIdx.x; e < 32 * L::RP; e += kBlock) {
+                const int tl = e / L::RP, r = e - tl * L::RP;
+                const int64_t nn = npair0 + tl;
+                if (r < R && nn < nend) {
+                    float v = 0.f;
+#pragma unroll
+                    for (int w2 = 0; w2 < 4; ++w2)
+                        v += *reinterpret_cast<const float *>(lds + w2 * L::kWave + L::kDwc + L::kZ +
+                                                              buf * 32 * L::PD + tl * L::PD + 4 * r);
+                    atomicAdd(p.dzacc + nn * R + r, v);
+                }
+            }
+            buf ^= 1;
+        }
+
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            xprev[i] = xc[i];
+            xc[i] = xn[i];
+            xn[i] = xn2[i];
+            gc[i] = gn[i];
+            gn[i] = gn2[i];
+            gn2[i] = gn3[i];
+        }
+    }
+
+    // dU tile of this wave (rank x 32 channels x W taps) -> LDS in the memory
+    // order of dU, then added to the output with coalesced atomics (each wave
+    // instruction covers 64 consecutive floats of one rank row).
+    __syncthreads();  // every wave is done with the loop's LDS regions
+    float *dus = reinterpret_cast<float *>(my);
+#pragma unroll
+    for (int k = 0; k < W; ++k)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const int r = 16 * rt + i16;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dus[r * (32 * W) + (16 * ct + 4 * q + j) * W + k] = du[k][ct][rt][j];
+            }
+    __syncthreads();
+    const int64_t nvalid = (p.D - d0 < 32 ? p.D - d0 : 32) * W;  // channels of this slice inside D
+    for (int r = 0; r < R; ++r)
+        for (int idx = lane; idx < nvalid; idx += kWave)
+            atomicAdd(p.dU + (int64_t)r * DW + d0 * W + idx, dus[r * (32 * W) + idx]);
 }
 
 // ------------------------------------------------------------ small kernels
@@ -422,6 +846,41 @@ hipError_t mfma_fwd(const LrProblem &pr, hipStream_t st) {
     return hipGetLastError();
 }
 
+constexpr int64_t kTargetBwdBlocks = 512;
+
+template <int W, int RC>
+hipError_t mfma_bwd(const LrProblem &pr, hipStream_t st) {
+    LrParams p = make_params<BF16>(pr);
+    const int64_t nU = (int64_t)p.R * p.D * W;
+    const int64_t nz = p.N * p.R;
+    hipLaunchKernelGGL(fill_zero_f32, dim3((unsigned)nblocks(nU)), dim3(kBlock), 0, st, p.dU, nU);
+    hipLaunchKernelGGL(fill_zero_f32, dim3((unsigned)nblocks(nz)), dim3(kBlock), 0, st, p.dzacc, nz);
+    const int64_t nslices = (p.D + 31) / 32;
+    const int64_t ngroups = (nslices + 3) / 4;
+    int64_t tchunks = kTargetBwdBlocks / ngroups;
+    if (tchunks < 1) tchunks = 1;
+    int64_t tpb = (p.N + tchunks - 1) / tchunks;
+    tpb = ((tpb + 31) / 32) * 32;
+    tchunks = (p.N + tpb - 1) / tpb;
+    hipLaunchKernelGGL((lr_bwd_mfma<W, RC>), dim3((unsigned)(tchunks * ngroups)), dim3(kBlock), 0, st, p,
+                       nslices, tpb);
+    hipLaunchKernelGGL(cast_f32_bf16, dim3((unsigned)nblocks(nz)), dim3(kBlock), 0, st, p.dzacc,
+                       static_cast<uint16_t *>(p.dz), nz);
+    return hipGetLastError();
+}
+
+// The backward keeps W*RC*(two U operand sets + dU tiles) in registers; it is
+// instantiated while that fits (W*RC <= 8), other shapes use the generic kernel.
+template <int W>
+hipError_t mfma_bwd_rc(const LrProblem &pr, hipStream_t st) {
+    const int rc = (pr.R + 31) / 32;
+    if (rc == 1) return mfma_bwd<W, 1>(pr, st);
+    if constexpr (W <= 4) {
+        if (rc == 2) return mfma_bwd<W, 2>(pr, st);
+    }
+    return generic_bwd<BF16, W>(pr, st);
+}
+
 template <int W>
 hipError_t mfma_fwd_rc(const LrProblem &pr, hipStream_t st) {
     switch ((pr.R + 31) / 32) {
@@ -464,7 +923,7 @@ hipError_t lowrank_fwd(const LrProblem &p, hipStream_t s) {
 
 hipError_t lowrank_bwd(const LrProblem &p, hipStream_t s) {
     if (p.dtype == Dtype::BF16) {
-        DSC_W_SWITCH(p.W, (generic_bwd<BF16, Wc>(p, s)));
+        DSC_W_SWITCH(p.W, (mfma_bwd_rc<Wc>(p, s)));
     }
     DSC_W_SWITCH(p.W, (generic_bwd<F32, Wc>(p, s)));
 }

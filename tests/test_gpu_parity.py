@@ -52,9 +52,11 @@ LR_CASES = [
     ("bf16", 2, 31, 96, 3, 100, True, None),
     ("bf16", 1, 50, 128, 8, 1, False, (1, 9)),
     ("bf16", 1, 2, 32, 4, 16, False, None),
-    ("bf16", 3, 130, 512, 4, 32, False, None),
+    ("bf16", 3, 130, 2304, 4, 32, False, None),
     ("bf16", 1, 200, 128, 2, 128, True, (1, 50)),
-    ("bf16", 1, 130, 512, 4, 64, False, (1, 60)),
+    ("bf16", 1, 520, 6144, 4, 64, False, (1, 300)),
+    ("bf16", 2, 97, 200, 8, 20, True, (1, 60)),
+    ("bf16", 1, 64, 96, 2, 48, False, None),
 ]
 
 
