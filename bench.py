@@ -1,0 +1,393 @@
+#!/usr/bin/env python
+"""Benchmark of the dynamic short convolution hot path on one MI355X.
+
+One step = the whole hot path over one synthetic batch of the QKV workload
+at ~150M scale (B=8, T=2048, D=2304 = Q,K,V of width 768, W=4, bf16):
+  head-wise  (H=64, 36 filters per token, residual)  forward + backward,
+  low-rank   (R=32, filters generated on chip)       forward + backward,
+all through the C ABI of libdsc.so with inputs resident in HBM.
+
+Prints one JSON line: tokens/s of the step, achieved algorithmic HBM GB/s,
+the roofline of the dominant entry point (HIP events around each call on
+the stream it runs on), per-entry-point figures, the 2B-scale workloads
+(head-wise MLP D=8192 H=16 and low-rank varlen D=6144 R=64) timed the same
+way, and the fp64 CPU oracle timed on a bounded sample of the step's work.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
+METRIC = "dynamic-conv fwd+bwd tokens/s and achieved HBM GB/s (% of peak), 1 MI355X"
+
+
+def algorithmic_bytes(kind: str, direction: str, B, T, D, W, H=1, R=0, es=2) -> int:
+    """Each input read once, each output written once (the low-rank filters are never stored)."""
+    N = B * T
+    act = N * D * es
+    if kind == "headwise":
+        filt = N * (D // H) * W * es
+        return 2 * act + filt if direction == "fwd" else 3 * act + 2 * filt
+    zb, ub = N * R * es, R * D * W * es
+    if direction == "fwd":
+        return 2 * act + zb + ub
+    return 3 * act + 2 * zb + ub + R * D * W * 4  # dU is fp32
+
+
+class Case:
+    """Device tensors and the two entry-point calls of one workload."""
+
+    def __init__(self, wl, torch, binding, inputs):
+        self.wl = wl
+        inp = inputs.make_inputs(wl)
+        dev = "cuda"
+        self.x, self.dy = inp["x"].to(dev), inp["dy"].to(dev)
+        self.cu = None if inp["cu_seqlens"] is None else torch.from_numpy(inp["cu_seqlens"]).to(dev)
+        self.y, self.dx = torch.empty_like(self.x), torch.empty_like(self.x)
+        self.b = binding
+        if wl.kind == "headwise":
+            self.w = inp["w"].to(dev)
+            self.dw = torch.empty_like(self.w)
+        else:
+            self.z, self.U = inp["z"].to(dev), inp["U"].to(dev)
+            self.dz = torch.empty_like(self.z)
+            self.dU = torch.empty(self.U.shape, dtype=torch.float32, device=dev)
+            nws = binding.dsc_lowrank_bwd_workspace_size(self.x.dtype, wl.B, wl.T, wl.D, wl.W, wl.R)
+            self.ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+
+    def fwd(self):
+        wl = self.wl
+        if wl.kind == "headwise":
+            self.b.dsc_headwise_fwd(self.x, self.w, self.y, cu_seqlens=self.cu, residual=wl.residual)
+        else:
+            self.b.dsc_lowrank_fwd(self.x, self.z, self.U, self.y, W=wl.W, cu_seqlens=self.cu,
+                                   residual=wl.residual)
+
+    def bwd(self):
+        wl = self.wl
+        if wl.kind == "headwise":
+            self.b.dsc_headwise_bwd(self.x, self.w, self.dy, self.dx, self.dw, cu_seqlens=self.cu,
+                                    residual=wl.residual)
+        else:
+            self.b.dsc_lowrank_bwd(self.x, self.z, self.U, self.dy, self.dx, self.dz, self.dU, self.ws,
+                                   W=wl.W, cu_seqlens=self.cu, residual=wl.residual)
+
+    def bytes(self, direction):
+        wl = self.wl
+        return algorithmic_bytes(wl.kind, direction, wl.B, wl.T, wl.D, wl.W, wl.H, wl.R)
+
+    def flops(self, direction):
+        wl = self.wl
+        nd = wl.N * wl.D
+        if wl.kind == "headwise":
+            return (2 if direction == "fwd" else 4) * wl.W * nd
+        return (2 * wl.R * wl.W + 2 * wl.W) * nd * (1 if direction == "fwd" else 3)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "input_dependent_short_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(entry: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("entries", {}).get(entry, {}).get("bytes_per_launch")
+
+
+def cpu_baseline(wls, seconds: float):
+    """fp64 oracle on the first S tokens of row 0 of the step's workloads (both
+    variants, forward + backward), S grown until about `seconds` of CPU work."""
+    import oracle
+    from input_dependent_short_amd import inputs
+    from input_dependent_short_amd.inputs import to_f64
+
+    full = {wl.kind: inputs.make_inputs(wl) for wl in wls}
+    T = min(wl.T for wl in wls)
+    Bmax = min(wl.B for wl in wls)
+
+    def sample(d, S):
+        # S <= T: the first S tokens of row 0; beyond that whole rows (sequences)
+        out = {}
+        for n, v in d.items():
+            if n == "cu_seqlens":
+                continue
+            if n == "U":
+                out[n] = to_f64(v)
+            elif S <= T:
+                out[n] = to_f64(v[0:1, :S])
+            else:
+                out[n] = to_f64(v[0:S // T])
+        return out
+
+    def run(S):
+        a = {wl.kind: sample(full[wl.kind], S) for wl in wls}
+        t0 = time.perf_counter()
+        for wl in wls:
+            sl = a[wl.kind]
+            if wl.kind == "headwise":
+                oracle.headwise_fwd(sl["x"], sl["w"], residual=wl.residual)
+                oracle.headwise_bwd(sl["x"], sl["w"], sl["dy"], residual=wl.residual)
+            else:
+                oracle.lowrank_fwd(sl["x"], sl["z"], sl["U"], wl.W, residual=wl.residual)
+                oracle.lowrank_bwd(sl["x"], sl["z"], sl["U"], sl["dy"], wl.W, residual=wl.residual)
+        return time.perf_counter() - t0
+
+    def clamp(S):
+        S = max(64, min(S, Bmax * T))
+        return S if S <= T else (S // T) * T
+
+    S = 256
+    t = run(S)
+    while t < seconds / 8 and S < Bmax * T:
+        S = clamp(S * 4)
+        t = run(S)
+    if t < seconds * 0.7 and S < Bmax * T:
+        S = clamp(int(S * seconds / max(t, 1e-3)))
+        t = run(S)
+    desc = f"first {S} tokens of row 0" if S <= T else f"first {S // T} rows ({S} tokens)"
+    return {"value": S / t, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{desc} of the step's batch, head-wise and low-rank forward + backward "
+                      f"in fp64; {t:.1f} s of CPU time",
+            "host": platform.processor() or platform.machine()}
+
+
+COPY_BYTES = 1 << 30  # bytes read (and written) by the copy-kernel reference
+
+
+def copy_ceiling(torch, reps: int = 10) -> float:
+    """GB/s of a plain device copy (1 GiB read + 1 GiB written): the practical
+    streaming ceiling beside the nominal 8 TB/s, and the reference kernel of
+    known size that scales the HBM byte counters."""
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) * 1e-3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * COPY_BYTES / t / 1e9
+
+
+# kernels launched by each entry point (rocprofv3 kernel names contain these)
+ENTRY_KERNELS = {
+    "dsc_headwise_fwd": ["hw_fwd_kernel"],
+    "dsc_headwise_bwd": ["hw_bwd_kernel"],
+    "dsc_lowrank_fwd": ["lr_fwd_mfma"],
+    "dsc_lowrank_bwd": ["lr_bwd_mfma", "fill_zero_f32", "cast_f32_bf16"],
+}
+
+
+def _counter_rows(d: str):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, out_json: str) -> dict:
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch, from two rocprofv3
+    --pmc runs of this script) per entry point, scaled by what the same
+    counters read for the 1 GiB copy kernel; written to profiles/traffic.json."""
+    per = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        for r in _counter_rows(d):
+            if r.get("Counter_Name") != name:
+                continue
+            k = r["Kernel_Name"]
+            e = per.setdefault(k, {}).setdefault(name, [])
+            e.append(float(r["Counter_Value"]))
+    copy_k = [k for k in per if "copy" in k.lower() or "Copy" in k]
+    copy_k = max(copy_k, key=lambda k: sum(per[k].get("FETCH_SIZE", [0])) / max(1, len(per[k].get("FETCH_SIZE", [1]))))
+    cf = per[copy_k]
+    f_fetch = COPY_BYTES / (sum(cf["FETCH_SIZE"]) / len(cf["FETCH_SIZE"]) * 1024.0)
+    f_write = COPY_BYTES / (sum(cf["WRITE_SIZE"]) / len(cf["WRITE_SIZE"]) * 1024.0)
+    entries = {}
+    for entry, pats in ENTRY_KERNELS.items():
+        main_k = [k for k in per if pats[0] in k]
+        if not main_k:
+            continue
+        calls = len(per[main_k[0]]["FETCH_SIZE"])
+        fetch = write = 0.0
+        for k in per:
+            if any(pt in k for pt in pats):
+                fetch += sum(per[k].get("FETCH_SIZE", [])) * 1024.0 * f_fetch
+                write += sum(per[k].get("WRITE_SIZE", [])) * 1024.0 * f_write
+        entries[entry] = {"fetch_bytes_per_launch": fetch / calls, "write_bytes_per_launch": write / calls,
+                          "bytes_per_launch": (fetch + write) / calls, "launches": calls}
+    rec = {"kernel_source_hash": kernel_source_hash(), "copy_kernel": copy_k,
+           "fetch_scale": f_fetch, "write_scale": f_write, "entries": entries}
+    with open(out_json, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    return rec
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-large", action="store_true", help="skip the 2B-scale workloads")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs of this script into profiles/traffic.json")
+    args = ap.parse_args()
+
+    if args.summarize_counters:
+        rec = summarize_counters(*args.summarize_counters, os.path.join(ROOT, "profiles", "traffic.json"))
+        print(json.dumps(rec, indent=1))
+        return 0
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the dynamic short convolution is per-token local and this build runs on a single "
+              "MI355X.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from input_dependent_short_amd import binding, inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    binding.lib()  # fails loudly if the HIP library is not built
+
+    copy_gbps = copy_ceiling(torch)
+    cases = [Case(inputs.WORKLOADS[2], torch, binding, inputs), Case(inputs.WORKLOADS[3], torch, binding, inputs)]
+    calls = [(f"{c.wl.kind}_{d}", c, d) for c in cases for d in ("fwd", "bwd")]
+    names = {"headwise_fwd": "dsc_headwise_fwd", "headwise_bwd": "dsc_headwise_bwd",
+             "lowrank_fwd": "dsc_lowrank_fwd", "lowrank_bwd": "dsc_lowrank_bwd"}
+
+    def step(events=None):
+        for i, (_, c, d) in enumerate(calls):
+            if events is not None:
+                events[i][0].record()
+            (c.fwd if d == "fwd" else c.bwd)()
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(ev[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call = {}
+    for i, (key, c, d) in enumerate(calls):
+        ms = sorted(ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(K))
+        avg = sum(ms) / K
+        b = c.bytes(d)
+        per_call[key] = {"entry": names[key], "workload": c.wl.name, "avg_us": round(avg * 1e3, 2),
+                         "median_us": round(ms[K // 2] * 1e3, 2), "algorithmic_bytes": b,
+                         "GBps": round(b / (avg * 1e-3) / 1e9, 1),
+                         "frac_hbm_peak": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                         "TFLOPs": round(c.flops(d) / (avg * 1e-3) / 1e12, 2)}
+    ms_step = wall / K * 1e3
+    N = cases[0].wl.N
+    step_bytes = sum(c.bytes(d) for _, c, d in calls)
+    dom_key = max(per_call, key=lambda k: per_call[k]["avg_us"])
+    dom = per_call[dom_key]
+    traffic = measured_traffic(dom["entry"])
+
+    out = {
+        "metric": METRIC,
+        "value": round(N / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "QKV dynamic short conv at ~150M scale: head-wise (H=64, residual) and "
+                               "low-rank (R=32) forward+backward on one batch",
+                   "B": 8, "T": 2048, "D": 2304, "W": 4, "H": 64, "R": 32, "dtype": "bf16"},
+        "achieved_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "roofline": {"bound": "hbm", "kernel": dom["entry"], "achieved": dom["GBps"],
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": dom["frac_hbm_peak"],
+                     "traffic": traffic, "bytes_per_launch": dom["algorithmic_bytes"],
+                     "avg_launch_us": dom["avg_us"]},
+        "per_entry": per_call,
+        "copy_ceiling_GBps": round(copy_gbps, 1),
+    }
+
+    if not args.no_large:
+        large = {}
+        for cfg in (4, 5):
+            c = Case(inputs.WORKLOADS[cfg], torch, binding, inputs)
+            for _ in range(3):
+                c.fwd(); c.bwd()
+            torch.cuda.synchronize()
+            reps = max(5, K // 2)
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+                    torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for e in evs:
+                e[0].record(); c.fwd(); e[1].record(); c.bwd(); e[2].record()
+            torch.cuda.synchronize()
+            tf = sum(e[0].elapsed_time(e[1]) for e in evs) / reps * 1e-3
+            tb = sum(e[1].elapsed_time(e[2]) for e in evs) / reps * 1e-3
+            b = c.bytes("fwd") + c.bytes("bwd")
+            large[c.wl.name] = {"tokens_per_s": round(c.wl.N / (tf + tb), 1),
+                                "fwd_us": round(tf * 1e6, 1), "bwd_us": round(tb * 1e6, 1),
+                                "GBps": round(b / (tf + tb) / 1e9, 1),
+                                "frac_hbm_peak": round(b / (tf + tb) / 1e9 / PEAK_HBM_GBPS, 4)}
+            del c
+            torch.cuda.empty_cache()
+        out["workloads_2b"] = large
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline([cases[0].wl, cases[1].wl], args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -127,9 +127,9 @@ DSC_API dsc_status dsc_lowrank_fwd(void *stream, int dtype, int64_t B, int64_t T
                            const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, void *y);
 
 /*
- * Bytes of device workspace dsc_lowrank_bwd needs for these sizes and dtype
- * (fp32 accumulators of dz; 0 never happens for valid sizes).  Returns 0 for
- * invalid sizes.
+ * Bytes of device workspace dsc_lowrank_bwd needs for these sizes and dtype:
+ * an fp32 (B*T, R) accumulator of dz for DSC_BF16, nothing (0) for DSC_FP32,
+ * whose dz is accumulated in place.  Also returns 0 for invalid sizes.
  */
 DSC_API size_t dsc_lowrank_bwd_workspace_size(int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
                                       int32_t R);

@@ -43,6 +43,7 @@ def build(out_path: str = LIB_PATH, extra_flags: tuple[str, ...] = ()) -> str:
 def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     i64, i32, p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
     lib.oracle_abi_version.restype = ctypes.c_int
+    lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_headwise_fwd.argtypes = [i64, i64, i64, i32, i32, p, p, p, i32, i32, i64, i64, p]
     lib.oracle_headwise_bwd.argtypes = [i64, i64, i64, i32, i32, p, p, p, p, i32, i32, i64, i64, p, p]
     lib.oracle_lowrank_fwd.argtypes = [i64, i64, i64, i32, i32, p, p, p, p, i32, i32, i64, i64, p]
@@ -158,6 +159,11 @@ class Oracle:
         if rows is None:
             return dx.reshape(B, T, D), dz.reshape(B, T, R), dU
         return dx, dz, dU
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle uses."""
+    return int(load().oracle_num_threads())
 
 
 _default: Oracle | None = None

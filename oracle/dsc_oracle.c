@@ -42,10 +42,23 @@
  */
 #include <stdint.h>
 #include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORACLE_ABI_VERSION 1
 
 int oracle_abi_version(void) { return ORACLE_ABI_VERSION; }
+
+/* Threads an OpenMP loop of the oracle runs with. */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* First token of the segment of every flattened token n in [0, B*T).
  * Without cu_seqlens each of the B rows is one sequence; otherwise
