@@ -21,7 +21,8 @@
 //   * taps outside the token's sequence are masked per token, so packed
 //     sequences cost nothing when no boundary falls inside a tile;
 //   * the dw group sum over H channels is a per-thread sum over the chunk
-//     followed by a butterfly over the H/VEC lanes of the group;
+//     followed by a DPP butterfly over the H/VEC lanes of the group;
+//   * the forward keeps the next batch of loads in flight while computing;
 //   * fp32 accumulation, one round-to-nearest-even store per output.
 #include "dsc_kernels.h"
 
@@ -45,6 +46,70 @@ constexpr int kBlock = 256;
 template <int VEC, int GPT>
 __device__ __forceinline__ constexpr int grp(int c) {
     return GPT > 1 ? c / (VEC / GPT) : 0;
+}
+
+// Raw 16-byte vector of activations, widened to fp32 when used.
+template <class E>
+__device__ __forceinline__ uint4 load_raw(const typename E::store_t *p) {
+    return *reinterpret_cast<const uint4 *>(p);
+}
+
+template <class E>
+__device__ __forceinline__ float lane_elem(const uint4 &v, int c) {
+    const uint32_t w = c < (E::kVec / 4) ? v.x : c < 2 * (E::kVec / 4) ? v.y : c < 3 * (E::kVec / 4) ? v.z : v.w;
+    if constexpr (E::kVec == 4) {
+        return __uint_as_float(w);
+    } else {
+        return (c & 1) ? bf16_hi(w) : bf16_lo(w);
+    }
+}
+
+template <class E>
+__device__ __forceinline__ void unpack(const uint4 &v, float (&f)[E::kVec]) {
+#pragma unroll
+    for (int c = 0; c < E::kVec; ++c) f[c] = lane_elem<E>(v, c);
+}
+
+// Sum over aligned groups of `lanes` consecutive lanes (a power of two <= 64);
+// every lane of the group receives the total.  DPP inside 16-lane rows
+// (quad permutes, half-row and row mirrors), cross-lane shuffles beyond.
+__device__ __forceinline__ float dpp_add(float v, int ctrl_sel) {
+    int o;
+    switch (ctrl_sel) {
+        case 0: o = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, true); break;   // xor 1
+        case 1: o = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, true); break;   // xor 2
+        case 2: o = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xf, 0xf, true); break;  // half-row mirror
+        default: o = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xf, 0xf, true); break; // row mirror
+    }
+    return v + __int_as_float(o);
+}
+
+template <int NW>
+__device__ __forceinline__ void group_sum(float (&v)[NW], int lanes) {
+    if (lanes >= 2) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) v[i] = dpp_add(v[i], 0);
+    }
+    if (lanes >= 4) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) v[i] = dpp_add(v[i], 1);
+    }
+    if (lanes >= 8) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) v[i] = dpp_add(v[i], 2);
+    }
+    if (lanes >= 16) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) v[i] = dpp_add(v[i], 3);
+    }
+    if (lanes >= 32) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) v[i] += __shfl_xor(v[i], 16, kWave);
+    }
+    if (lanes >= 64) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) v[i] += __shfl_xor(v[i], 32, kWave);
+    }
 }
 
 template <class E, int W, int GPT, int TT, int U>
@@ -76,40 +141,44 @@ __global__ __launch_bounds__(kBlock) void hw_fwd_kernel(HwParams p) {
     for (int i = 0; i < W - 1; ++i) {
         const int64_t t = n0 - 1 - i;
         if (t >= s) {
-            Vec16<E>::load(x + t * p.D, ring[i]);
+            unpack<E>(load_raw<E>(x + t * p.D), ring[i]);
         } else {
 #pragma unroll
             for (int c = 0; c < VEC; ++c) ring[i][c] = 0.f;
         }
     }
 
-    for (int64_t nb = n0; nb < n1; nb += U) {
-        float xv[U][VEC];
-        float wv[U][NW];
+    // two batches of U tokens in flight: compute one while the next loads
+    uint4 xa[U], xb[U];
+    float wa[U][NW], wb[U][NW];
+    auto load_batch = [&](int64_t nb, uint4 (&xr)[U], float (&wr)[U][NW]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t n = nb + u;
             if (n < n1) {
-                Vec16<E>::load(x + n * p.D, xv[u]);
-                Span<E, NW>::template load<WALIGN>(w + n * p.G * W, wv[u]);
+                xr[u] = load_raw<E>(x + n * p.D);
+                Span<E, NW>::template load<WALIGN>(w + n * p.G * W, wr[u]);
             }
         }
+    };
+    auto compute_batch = [&](int64_t nb, const uint4 (&xr)[U], const float (&wr)[U][NW]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t n = nb + u;
             if (n < n1) {
                 if (n >= e) p.seq.find(n, s, e);
                 const int64_t nv = n - s;  // taps k <= nv lie inside the sequence
-                float acc[VEC];
+                float xv[VEC], acc[VEC];
+                unpack<E>(xr[u], xv);
 #pragma unroll
-                for (int c = 0; c < VEC; ++c) acc[c] = p.rho * xv[u][c];
+                for (int c = 0; c < VEC; ++c) acc[c] = p.rho * xv[c];
 #pragma unroll
                 for (int k = 0; k < W; ++k) {
                     const bool ok = k <= nv;
 #pragma unroll
                     for (int c = 0; c < VEC; ++c) {
-                        const float wk = ok ? wv[u][grp<VEC, GPT>(c) * W + k] : 0.f;
-                        const float xk = k == 0 ? xv[u][c] : ring[k - 1][c];
+                        const float wk = ok ? wr[u][grp<VEC, GPT>(c) * W + k] : 0.f;
+                        const float xk = k == 0 ? xv[c] : ring[k - 1][c];
                         acc[c] = __builtin_fmaf(wk, xk, acc[c]);
                     }
                 }
@@ -120,10 +189,19 @@ __global__ __launch_bounds__(kBlock) void hw_fwd_kernel(HwParams p) {
                     for (int c = 0; c < VEC; ++c) ring[i][c] = ring[i - 1][c];
                 if constexpr (W > 1) {
 #pragma unroll
-                    for (int c = 0; c < VEC; ++c) ring[0][c] = xv[u][c];
+                    for (int c = 0; c < VEC; ++c) ring[0][c] = xv[c];
                 }
             }
         }
+    };
+
+    load_batch(n0, xa, wa);
+    for (int64_t nb = n0; nb < n1; nb += 2 * U) {
+        if (nb + U < n1) load_batch(nb + U, xb, wb);
+        compute_batch(nb, xa, wa);
+        if (nb + U >= n1) break;
+        if (nb + 2 * U < n1) load_batch(nb + 2 * U, xa, wa);
+        compute_batch(nb + U, xb, wb);
     }
 }
 
@@ -138,7 +216,7 @@ __global__ __launch_bounds__(kBlock) void hw_bwd_kernel(HwParams p) {
     const int64_t item = xcd_block_id(blockIdx.x, gridDim.x) * kBlock + threadIdx.x;
     // Whole filter groups are active or inactive together (items is a
     // multiple of nchunks, which is a multiple of lanes), so exiting here never
-    // strands a lane that a group butterfly reads.
+    // strands a lane that a group reduction reads.
     if (item >= p.items) return;
     const int64_t tile = item / p.nchunks;
     const int64_t chunk = item - tile * p.nchunks;
@@ -157,50 +235,36 @@ __global__ __launch_bounds__(kBlock) void hw_bwd_kernel(HwParams p) {
     int64_t s, e;
     p.seq.find(n0, s, e);
 
-    float ring[W > 1 ? W - 1 : 1][VEC];  // ring[i] = x[m-1-i]
+    const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+    uint4 ring[W > 1 ? W - 1 : 1];  // ring[i] = x[m-1-i] (raw)
 #pragma unroll
     for (int i = 0; i < W - 1; ++i) {
         const int64_t t = n0 - 1 - i;
-        if (t >= s) {
-            Vec16<E>::load(x + t * p.D, ring[i]);
-        } else {
-#pragma unroll
-            for (int c = 0; c < VEC; ++c) ring[i][c] = 0.f;
-        }
+        ring[i] = t >= s ? load_raw<E>(x + t * p.D) : zero4;
     }
-    // window slot i holds token mb + i
-    float gw[WIN][VEC];
+    // look-ahead window: slot i holds token mb + i
+    uint4 gw[WIN];
     float ww[WIN][NW];
-#pragma unroll
-    for (int i = 0; i < W - 1; ++i) {
-        const int64_t t = n0 + i;
+    auto load_gw = [&](int64_t t, int slot) {
         if (t < p.N) {
-            Vec16<E>::load(g + t * p.D, gw[i]);
-            Span<E, NW>::template load<WALIGN>(w + t * p.G * W, ww[i]);
+            gw[slot] = load_raw<E>(g + t * p.D);
+            Span<E, NW>::template load<WALIGN>(w + t * p.G * W, ww[slot]);
         } else {
+            gw[slot] = zero4;
 #pragma unroll
-            for (int c = 0; c < VEC; ++c) gw[i][c] = 0.f;
-#pragma unroll
-            for (int c = 0; c < NW; ++c) ww[i][c] = 0.f;
+            for (int c = 0; c < NW; ++c) ww[slot][c] = 0.f;
         }
-    }
+    };
+#pragma unroll
+    for (int i = 0; i < W - 1; ++i) load_gw(n0 + i, i);
 
     for (int64_t mb = n0; mb < n1; mb += U) {
-        float xv[U][VEC];
+        uint4 xv[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t m = mb + u;
-            if (m < n1) Vec16<E>::load(x + m * p.D, xv[u]);
-            const int64_t t = mb + W - 1 + u;
-            if (t < p.N) {
-                Vec16<E>::load(g + t * p.D, gw[W - 1 + u]);
-                Span<E, NW>::template load<WALIGN>(w + t * p.G * W, ww[W - 1 + u]);
-            } else {
-#pragma unroll
-                for (int c = 0; c < VEC; ++c) gw[W - 1 + u][c] = 0.f;
-#pragma unroll
-                for (int c = 0; c < NW; ++c) ww[W - 1 + u][c] = 0.f;
-            }
+            xv[u] = m < n1 ? load_raw<E>(x + m * p.D) : zero4;
+            load_gw(mb + W - 1 + u, W - 1 + u);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -209,16 +273,18 @@ __global__ __launch_bounds__(kBlock) void hw_bwd_kernel(HwParams p) {
                 if (m >= e) p.seq.find(m, s, e);
                 const int64_t ahead = e - m;  // dx terms k < ahead stay in the sequence
                 const int64_t back = m - s;   // dw taps k <= back stay in the sequence
-                float acc[VEC];
+                float gm[VEC], acc[VEC];
+                unpack<E>(gw[u], gm);
 #pragma unroll
-                for (int c = 0; c < VEC; ++c) acc[c] = p.rho * gw[u][c];
+                for (int c = 0; c < VEC; ++c) acc[c] = p.rho * gm[c];
 #pragma unroll
                 for (int k = 0; k < W; ++k) {
                     const bool ok = k < ahead;
 #pragma unroll
                     for (int c = 0; c < VEC; ++c) {
                         const float wk = ok ? ww[u + k][grp<VEC, GPT>(c) * W + k] : 0.f;
-                        acc[c] = __builtin_fmaf(wk, gw[u + k][c], acc[c]);
+                        const float gk = k == 0 ? gm[c] : lane_elem<E>(gw[u + k], c);
+                        acc[c] = __builtin_fmaf(wk, gk, acc[c]);
                     }
                 }
                 Vec16<E>::store(dx + m * p.D, acc);
@@ -228,17 +294,13 @@ __global__ __launch_bounds__(kBlock) void hw_bwd_kernel(HwParams p) {
                 for (int i = 0; i < NW; ++i) part[i] = 0.f;
 #pragma unroll
                 for (int k = 0; k < W; ++k) {
+                    const uint4 &xr = k == 0 ? xv[u] : ring[k - 1];
 #pragma unroll
-                    for (int c = 0; c < VEC; ++c) {
-                        const float xk = k == 0 ? xv[u][c] : ring[k - 1][c];
+                    for (int c = 0; c < VEC; ++c)
                         part[grp<VEC, GPT>(c) * W + k] =
-                            __builtin_fmaf(gw[u][c], xk, part[grp<VEC, GPT>(c) * W + k]);
-                    }
+                            __builtin_fmaf(gm[c], lane_elem<E>(xr, c), part[grp<VEC, GPT>(c) * W + k]);
                 }
-                for (int off = 1; off < p.lanes; off <<= 1) {
-#pragma unroll
-                    for (int i = 0; i < NW; ++i) part[i] += __shfl_xor(part[i], off, kWave);
-                }
+                group_sum<NW>(part, p.lanes);
 #pragma unroll
                 for (int q = 0; q < GPT; ++q)
 #pragma unroll
@@ -247,28 +309,28 @@ __global__ __launch_bounds__(kBlock) void hw_bwd_kernel(HwParams p) {
                 if (leader) Span<E, NW>::template store<WALIGN>(dw + m * p.G * W, part);
 
 #pragma unroll
-                for (int i = W - 2; i > 0; --i)
-#pragma unroll
-                    for (int c = 0; c < VEC; ++c) ring[i][c] = ring[i - 1][c];
-                if constexpr (W > 1) {
-#pragma unroll
-                    for (int c = 0; c < VEC; ++c) ring[0][c] = xv[u][c];
-                }
+                for (int i = W - 2; i > 0; --i) ring[i] = ring[i - 1];
+                if constexpr (W > 1) ring[0] = xv[u];
             }
         }
         // slide the look-ahead window by U tokens
 #pragma unroll
         for (int i = 0; i < W - 1; ++i) {
-#pragma unroll
-            for (int c = 0; c < VEC; ++c) gw[i][c] = gw[U + i][c];
+            gw[i] = gw[U + i];
 #pragma unroll
             for (int c = 0; c < NW; ++c) ww[i][c] = ww[U + i][c];
         }
     }
 }
 
-constexpr int kTT = 32;  // tokens per thread tile
-constexpr int kU = 4;    // tokens per load batch
+#ifndef DSC_HW_TT
+#define DSC_HW_TT 32
+#endif
+#ifndef DSC_HW_U
+#define DSC_HW_U 4
+#endif
+constexpr int kTT = DSC_HW_TT;  // tokens per thread tile
+constexpr int kU = DSC_HW_U;    // tokens per load batch
 
 template <class E>
 HwParams make_params(const HwProblem &pr, int64_t &blocks) {
