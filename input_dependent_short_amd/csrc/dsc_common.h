@@ -169,6 +169,29 @@ struct Span {
     }
 };
 
+// ----------------------------------------------------------- buffer access
+
+// Raw buffer resource over [base, base + bytes): loads outside the range read
+// zero and stores outside it are dropped by the hardware, which replaces
+// per-lane bounds branches.  `bytes` is clamped to 32 bits; lanes that must
+// not touch memory use kNoOffset.
+constexpr uint32_t kBufferWord3 = 0x00020000u;  // gfx9-family raw buffer format
+constexpr uint32_t kNoOffset = 0xffffffffu;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const int64_t b = bytes < 0 ? 0 : (bytes > 0xffffffffll ? 0xffffffffll : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)(uint32_t)b, kBufferWord3);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v),
+                                           r, off, 0, 0);
+}
+
 // ----------------------------------------------------------- sequences
 
 // Sequence [start, end) on the flattened token axis that contains token n.
@@ -241,6 +264,64 @@ struct SeqCursor {
                 e = cu[idx + 1];
             }
         }
+    }
+};
+
+// Per-wave bit map of sequence starts over the tokens [base, base + 32*kWords),
+// kept in LDS and built once before a wave's token walk, so the walk itself
+// issues no memory loads besides its data stream (which keeps the compiler's
+// load counters exact and the prefetch in flight).  Bit i is set when token
+// base + i is the first token of a sequence, or is N (one past the end).
+template <int kWords>
+struct StartBits {
+    uint32_t *words;  // LDS, owned by one wave
+    int64_t base;
+
+    // All 64 lanes of the wave call this; the caller synchronises before use.
+    __device__ void build(uint32_t *lds_words, const SeqMap &m, int64_t N, int64_t first_token, int lane) {
+        words = lds_words;
+        base = first_token;
+        const int64_t hi = base + 32 * (int64_t)kWords;
+        // The wave's LDS operations complete in issue order, so the zeroing
+        // below is visible to the marking that follows and both to the
+        // caller's later reads.
+        for (int i = lane; i < kWords; i += kWave) words[i] = 0u;
+        auto mark = [&](int64_t t) {
+            if (t >= base && t < hi) {
+                const int64_t o = t - base;
+                atomicOr(&words[o >> 5], 1u << (o & 31));
+            }
+        };
+        if (m.cu == nullptr) {
+            const int64_t lo = base > 0 ? base : 0;
+            const int64_t first = ((lo + m.T - 1) / m.T) * m.T;
+            for (int64_t t = first + (int64_t)lane * m.T; t < hi && t <= N; t += (int64_t)kWave * m.T) mark(t);
+        } else {
+            int lo = 0, hi_i = m.n_seqs;  // first index with cu[i] >= base
+            if ((int64_t)m.cu[0] >= base) {
+                hi_i = 0;
+            } else {
+                while (hi_i - lo > 1) {
+                    const int mid = (lo + hi_i) >> 1;
+                    if ((int64_t)m.cu[mid] >= base) hi_i = mid;
+                    else lo = mid;
+                }
+            }
+            for (int j = hi_i + lane; j <= m.n_seqs; j += kWave) {
+                const int64_t t = m.cu[j];
+                if (t >= hi) break;
+                mark(t);
+            }
+        }
+    }
+
+    // 32 bits of the map starting at token t (base <= t, t + 32 <= base + 32*kWords).
+    __device__ __forceinline__ uint32_t window(int64_t t) const {
+        const int64_t o = t - base;
+        const int w = (int)(o >> 5), b = (int)(o & 31);
+        const uint32_t lo = words[w];
+        const uint32_t hi = b ? words[w + 1] : 0u;
+        return b ? (lo >> b) | (hi << (32 - b)) : lo;
     }
 };
 

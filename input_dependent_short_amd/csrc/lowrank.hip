@@ -40,6 +40,8 @@ struct LrParams {
 };
 
 constexpr int kBlock = 256;
+constexpr int kMaxTokPerWave = 4096;                          // token walk length cap
+constexpr int kSeqWords = (kMaxTokPerWave + 128) / 32 + 2;    // sequence-start bits per wave
 
 // ---------------------------------------------------------------- generic
 
@@ -182,7 +184,11 @@ __device__ __forceinline__ void fill_shift(Shifted<W> &xs, const uint32_t (&cur)
 // Wave tile: 16 tokens (one per lane column) x 32 channels (two 16-row MFMA
 // tiles).  Lane l: token l & 15, channel group q = l >> 4 owning channels
 // d0 + 8q .. d0 + 8q + 7.  MFMA tile t, row i <-> channel d0 + 8(i>>2) + 4t + (i&3).
-template <int W, int RC, int PF>
+// x, z and y move through raw buffer resources rebased every 16-token step
+// (scalar work only); each lane keeps one constant 32-bit offset, and tokens
+// past the wave's range fall outside the resource (loads read zero, stores
+// are dropped).  Loads run PF steps ahead in a register ring.
+template <int W, int RC, int PF, bool RVEC>
 __global__ __launch_bounds__(kBlock) void lr_fwd_mfma(LrParams p, int64_t nslices, int64_t tok_per_wave) {
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * (kBlock / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -192,25 +198,25 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_mfma(LrParams p, int64_t nslice
     const int64_t nbeg = tchunk * tok_per_wave;
     if (nbeg >= p.N) return;  // wave-uniform
     const int64_t nend = min(nbeg + tok_per_wave, p.N);
-    const int64_t nsteps = (nend - nbeg + 15) / 16;
+    const int nsteps = (int)((nend - nbeg + 15) / 16);
 
     const int tok = lane & 15;
     const int q = lane >> 4;
     const int64_t cbase = d0 + 8 * q;
     const bool chan_ok = cbase < p.D;  // D % 8 == 0: a lane's 8 channels are all in or out
     const int R = p.R;
-    const int64_t DW = p.D * W;
+    const int64_t D = p.D;
+    const int64_t DW = D * W;
 
-    const uint16_t *x = static_cast<const uint16_t *>(p.x);
-    const uint16_t *z = static_cast<const uint16_t *>(p.z);
     const uint16_t *U = static_cast<const uint16_t *>(p.U);
-    uint16_t *y = static_cast<uint16_t *>(p.y);
+    const uint16_t *xg = static_cast<const uint16_t *>(p.x);
+    const uint16_t *zg = static_cast<const uint16_t *>(p.z);
+    uint16_t *yg = static_cast<uint16_t *>(p.y);
 
     // A operands: U_k^T rows (channels) x K (rank), per tap k, tile t, K chunk c.
     bf16x8 ua[W][2][RC];
     {
         const int row = lane & 15;
-        const int kq = lane >> 4;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int64_t ch = d0 + 8 * (row >> 2) + 4 * t + (row & 3);
@@ -220,9 +226,9 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_mfma(LrParams p, int64_t nslice
                 for (int k = 0; k < W; ++k) {
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
-                        const int r = 32 * c + 8 * kq + i;
+                        const int r = 32 * c + 8 * q + i;
                         uint16_t v = 0;
-                        if (r < R && ch < p.D) v = U[(int64_t)r * DW + ch * W + k];
+                        if (r < R && ch < D) v = U[(int64_t)r * DW + ch * W + k];
                         ua[k][t][c][i] = __builtin_bit_cast(__bf16, v);
                     }
                 }
@@ -230,103 +236,106 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_mfma(LrParams p, int64_t nslice
         }
     }
 
-    auto load_x = [&](int64_t n, uint32_t (&dst)[4]) {
-        if (n < nend && chan_ok) {
-            uint4 v = *reinterpret_cast<const uint4 *>(x + n * p.D + cbase);
-            dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+    const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+    // per-lane byte offsets inside a step's 16 token rows
+    const uint32_t xoff = chan_ok ? (uint32_t)((tok * D + cbase) * 2) : kNoOffset;
+    uint32_t zoff[RC];
+#pragma unroll
+    for (int c = 0; c < RC; ++c) {
+        const int r0 = 32 * c + 8 * q;
+        zoff[c] = r0 < R ? (uint32_t)((tok * R + r0) * 2) : kNoOffset;
+    }
+
+    // prefetch cursor (wave-uniform): first token of the step being fetched
+    int64_t fpos = nbeg;
+    auto fetch = [&](uint4 &xd, uint4 (&zd)[RC]) {
+        const int64_t rows = nend - fpos;  // tokens of the range left from fpos
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(xg + fpos * D, rows * D * 2);
+        xd = buf_load16(rx, xoff);
+        if constexpr (RVEC) {
+            const __amdgpu_buffer_rsrc_t rz = make_rsrc(zg + fpos * R, rows * R * 2);
+#pragma unroll
+            for (int c = 0; c < RC; ++c) zd[c] = buf_load16(rz, zoff[c]);
         } else {
-            dst[0] = dst[1] = dst[2] = dst[3] = 0u;
-        }
-    };
-    // B operand: Z^T, K = rank 32c + 8q .. +7, column = token
-    const bool r_vec = (R % 8) == 0;
-    auto load_z = [&](int64_t n, bf16x8 (&dst)[RC]) {
+            const int64_t n = fpos + tok;
 #pragma unroll
-        for (int c = 0; c < RC; ++c) {
-            const int r0 = 32 * c + 8 * q;
-            if (n < nend && r0 < R) {
-                if (r_vec) {
-                    dst[c] = *reinterpret_cast<const bf16x8 *>(z + n * R + r0);
-                } else {
+            for (int c = 0; c < RC; ++c) {
+                const int r0 = 32 * c + 8 * q;
+                uint32_t h[4];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const uint16_t v = (r0 + i < R) ? z[n * R + r0 + i] : (uint16_t)0;
-                        dst[c][i] = __builtin_bit_cast(__bf16, v);
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t lo = (n < nend && r0 + 2 * e < R) ? zg[n * R + r0 + 2 * e] : 0u;
+                    const uint32_t hi = (n < nend && r0 + 2 * e + 1 < R) ? zg[n * R + r0 + 2 * e + 1] : 0u;
+                    h[e] = lo | (hi << 16);
                 }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) dst[c][i] = __builtin_bit_cast(__bf16, (uint16_t)0);
+                zd[c] = make_uint4(h[0], h[1], h[2], h[3]);
             }
         }
+        fpos += 16;
     };
 
-    // previous step's x for the taps that reach back across the step edge
-    uint32_t xprev[4];
+    __shared__ uint32_t seq_words[kBlock / kWave][kSeqWords];
+    StartBits<kSeqWords> starts;
+    starts.build(seq_words[threadIdx.x >> 6], p.seq, p.N, nbeg - 32, lane);
+
+    // Register ring of PF step slots.  Step s reads slot s % PF (its x and z)
+    // and slot (s-1) % PF (the previous x, for the taps that reach back across
+    // the step edge), then refills slot (s-1) % PF with step s + PF - 1: no
+    // value is copied between registers, so a load only has to land when its
+    // step is computed.
+    uint4 xq[PF];
+    uint4 zq[PF][RC];
+#pragma unroll
+    for (int i = 0; i < PF - 1; ++i) fetch(xq[i], zq[i]);
+    xq[PF - 1] = zero4;  // step -1: only its last W-1 tokens are read
     {
         const int64_t n = nbeg - 16 + tok;
-        if (n >= 0 && tok >= 16 - (W - 1) && chan_ok) {
-            uint4 v = *reinterpret_cast<const uint4 *>(x + n * p.D + cbase);
-            xprev[0] = v.x; xprev[1] = v.y; xprev[2] = v.z; xprev[3] = v.w;
-        } else {
-            xprev[0] = xprev[1] = xprev[2] = xprev[3] = 0u;
-        }
+        if (n >= 0 && tok >= 16 - (W - 1) && chan_ok)
+            xq[PF - 1] = *reinterpret_cast<const uint4 *>(xg + n * D + cbase);
     }
 
-    SeqCursor seqc;
-    seqc.init(p.seq, nbeg);
+    int64_t nstep = nbeg;
 
-    uint32_t xq[PF][4];
-    bf16x8 zq[PF][RC];
-#pragma unroll
-    for (int i = 0; i < PF; ++i) {
-        load_x(nbeg + 16 * i + tok, xq[i]);
-        load_z(nbeg + 16 * i + tok, zq[i]);
-    }
-
-    for (int64_t st = 0; st < nsteps; st += PF) {
+    for (int s0 = 0; s0 < nsteps; s0 += PF) {
 #pragma unroll
         for (int i = 0; i < PF; ++i) {
-            if (st + i < nsteps) {
-                const int64_t nstep = nbeg + 16 * (st + i);
-                const int64_t n = nstep + tok;
-                uint32_t xc[4] = {xq[i][0], xq[i][1], xq[i][2], xq[i][3]};
-                bf16x8 zc[RC];
-#pragma unroll
-                for (int c = 0; c < RC; ++c) zc[c] = zq[i][c];
-                if (st + i + PF < nsteps) {
-                    load_x(n + 16 * PF, xq[i]);
-                    load_z(n + 16 * PF, zq[i]);
-                }
-
+            constexpr int kPrevOff = PF - 1;
+            const int ip = (i + kPrevOff) % PF;
+            {  // steps past the range read zeros and store nothing (buffer bounds)
                 floatx4 acc[W][2];
 #pragma unroll
                 for (int k = 0; k < W; ++k)
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {
-                        acc[k][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+                        acc[k][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            ua[k][t][0], __builtin_bit_cast(bf16x8, zq[i][0]), floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-                        for (int c = 0; c < RC; ++c)
-                            acc[k][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua[k][t][c], zc[c], acc[k][t], 0, 0, 0);
+                        for (int c = 1; c < RC; ++c)
+                            acc[k][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                ua[k][t][c], __builtin_bit_cast(bf16x8, zq[i][c]), acc[k][t], 0, 0, 0);
                     }
 
+                const uint32_t xc[4] = {xq[i].x, xq[i].y, xq[i].z, xq[i].w};
+                const uint32_t xpv[4] = {xq[ip].x, xq[ip].y, xq[ip].z, xq[ip].w};
                 Shifted<W> xs;
 #pragma unroll
                 for (int i2 = 0; i2 < 4; ++i2) xs.v[0][i2] = xc[i2];
-                fill_shift<W, 1>(xs, xc, xprev);
+                fill_shift<W, 1>(xs, xc, xpv);
 
-                // sequence masking: only when a boundary can touch this step
-                seqc.advance(nstep);
-                const bool clean = (seqc.e >= nstep + 16) && (nstep - seqc.s >= W - 1);
-                if (!clean) {
-                    int64_t s, e;
-                    p.seq.find(n < p.N ? n : p.N - 1, s, e);
-                    const int64_t nv = n - s;
+                // sequence masking, only when a sequence starts inside the
+                // step's reach: bit j of win <-> token nstep - (W-1) + j
+                if constexpr (W > 1) {
+                    const uint32_t win = __builtin_amdgcn_readfirstlane(starts.window(nstep - (W - 1)));
+                    if (win & (((1u << (W + 14)) - 1u) << 1)) {
+                        // starts among tokens n-W+2 .. n (n = nstep + tok)
+                        const uint32_t sub = (win >> (tok + 1)) & ((1u << (W - 1)) - 1u);
+                        const int nv = sub ? (W - 2) - (31 - __builtin_clz(sub)) : W - 1;
 #pragma unroll
-                    for (int k = 1; k < W; ++k)
-                        if (k > nv)
+                        for (int k = 1; k < W; ++k)
+                            if (k > nv)
 #pragma unroll
-                            for (int i2 = 0; i2 < 4; ++i2) xs.v[k][i2] = 0u;
+                                for (int i2 = 0; i2 < 4; ++i2) xs.v[k][i2] = 0u;
+                    }
                 }
 
                 float out[8];
@@ -342,16 +351,15 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_mfma(LrParams p, int64_t nslice
                     }
                     out[c] = a;
                 }
-                if (n < nend && chan_ok) {
-                    uint4 v;
-                    v.x = pack_bf16x2(out[0], out[1]);
-                    v.y = pack_bf16x2(out[2], out[3]);
-                    v.z = pack_bf16x2(out[4], out[5]);
-                    v.w = pack_bf16x2(out[6], out[7]);
-                    *reinterpret_cast<uint4 *>(y + n * p.D + cbase) = v;
-                }
-#pragma unroll
-                for (int i2 = 0; i2 < 4; ++i2) xprev[i2] = xc[i2];
+                uint4 v;
+                v.x = pack_bf16x2(out[0], out[1]);
+                v.y = pack_bf16x2(out[2], out[3]);
+                v.z = pack_bf16x2(out[4], out[5]);
+                v.w = pack_bf16x2(out[6], out[7]);
+                buf_store16(make_rsrc(yg + nstep * D, (nend - nstep) * D * 2), xoff, v);
+
+                fetch(xq[ip], zq[ip]);  // step s0 + i + PF - 1
+                nstep += 16;
             }
         }
     }
@@ -412,17 +420,19 @@ __device__ __forceinline__ bf16x8 bf16x8_from_u32(const uint32_t (&v)[4]) {
 // in steps of 16 tokens (pairs of steps = 32 tokens for the token
 // contraction of dU).  Per step and wave:
 //   * w of tokens n+k (k < W) on the matrix cores, B operand = z rows n+k
-//     read from an LDS ring of z rows (A = U_k^T kept in registers);
+//     read from a wave-private LDS ring of z rows (A = U_k^T in registers);
 //   * dx = rho*g + sum_k w_k * g shifted ahead by k (DPP with the next step);
 //   * dwc_k = g * x shifted back by k (DPP with the previous step), rounded
 //     to bf16 -- it is directly the B operand of dz^T = U_k * dwc_k, whose A
 //     operand (U_k, rank rows x channel K) is also kept in registers;
 //   * dwc_k is staged in LDS and re-read transposed (lane = channel,
 //     registers = tokens) as the A operand of dU_k^T += dwc_k^T * Z.
-// dz is summed over the block's 4 waves in LDS, then added to an fp32
-// accumulator with one atomic per (token, rank); dU stays in registers over
-// the whole token range and is added to the fp32 output with atomics at the
-// end.  Both accumulators are zeroed by the launcher first.
+// x, dy and z stream through raw buffer resources rebased per step, into
+// register rings refilled P steps ahead without copies.  dz is summed over
+// the block's 4 waves in LDS and added to an fp32 accumulator with one atomic
+// per (token, rank); dU stays in registers over the whole token range and is
+// added to the fp32 output with coalesced atomics at the end.  Both
+// accumulators are zeroed by the launcher first.
 template <int W, int RC>
 struct BwdLds {
     static constexpr int RP = 32 * RC;           // padded rank
@@ -432,11 +442,17 @@ struct BwdLds {
     static constexpr int PD = 4 * RP + 16;       // bytes per token row of dz partials
     static constexpr int kDwc = W * 32 * PW;
     static constexpr int kZ = 4 * SZ;
-    static constexpr int kDz = 2 * 32 * PD;      // double-buffered pair of steps
+    // Two blocks per CU (R <= 32, W <= 4: registers and LDS fit) keep one
+    // buffer of dz partials per wave and pay a second barrier per pair;
+    // otherwise the buffer is doubled and the pairs alternate.
+    static constexpr int kBlocksPerCu = (RC == 1 && W <= 4) ? 2 : 1;
+    static constexpr int kDzBufs = kBlocksPerCu == 2 ? 1 : 2;
+    static constexpr int kDz = kDzBufs * 32 * PD;  // the wave's dz partials of kDzBufs pairs
     static constexpr int kLoop = kDwc + kZ + kDz;
     static constexpr int kDuStage = RP * 32 * W * 4;   // dU tile staged for coalesced atomics
     static constexpr int kWave = (((kLoop > kDuStage ? kLoop : kDuStage) + 15) / 16) * 16;
     static constexpr int kBlock = 4 * kWave;
+    static_assert(kBlocksPerCu == 1 || 2 * (kBlock + 4 * 4 * 140) <= 160 * 1024, "two blocks must fit the LDS");
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -452,11 +468,14 @@ __device__ __forceinline__ uint2 lds_read_tr(const unsigned char *addr) {
     return __builtin_bit_cast(uint2, v);
 }
 
-template <int W, int RC>
-__global__ __launch_bounds__(kBlock, 1) void lr_bwd_mfma(LrParams p, int64_t nslices, int64_t tok_per_block) {
+template <int W, int RC, int P, bool RVEC>
+__global__ __launch_bounds__(kBlock, (BwdLds<W, RC>::kBlocksPerCu)) void lr_bwd_mfma(LrParams p, int64_t nslices,
+                                                                                   int64_t tok_per_block) {
     using L = BwdLds<W, RC>;
     constexpr int RT = 2 * RC;  // 16-row rank tiles
+    static_assert(P % 2 == 0 && P >= 2, "ring holds whole pairs of steps");
     __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBlock];
+    __shared__ uint32_t seq_words[kBlock / kWave][kSeqWords];
 
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -466,7 +485,9 @@ __global__ __launch_bounds__(kBlock, 1) void lr_bwd_mfma(LrParams p, int64_t nsl
     const int64_t d0 = (group * 4 + wid) * 32;
     const int64_t nbeg = tchunk * tok_per_block;
     const int64_t nend = min(nbeg + tok_per_block, p.N);
-    const int64_t npairs = (nend - nbeg + 31) / 32;
+    // steps of this block: whole rings of P steps (steps past nend read zeros
+    // past N, store nothing past nend, and add nothing to dz or dU)
+    const int64_t nsteps = ((nend - nbeg + 16 * P - 1) / (16 * P)) * P;
 
     const int tok = lane & 15;
     const int q = lane >> 4;
@@ -475,18 +496,19 @@ __global__ __launch_bounds__(kBlock, 1) void lr_bwd_mfma(LrParams p, int64_t nsl
     const bool chan_ok = cbase < p.D;
     const int R = p.R;
     const int64_t N = p.N;
-    const int64_t DW = p.D * W;
+    const int64_t D = p.D;
+    const int64_t DW = D * W;
 
-    const uint16_t *x = static_cast<const uint16_t *>(p.x);
-    const uint16_t *g = static_cast<const uint16_t *>(p.dy);
-    const uint16_t *z = static_cast<const uint16_t *>(p.z);
+    const uint16_t *xg = static_cast<const uint16_t *>(p.x);
+    const uint16_t *gg = static_cast<const uint16_t *>(p.dy);
+    const uint16_t *zg = static_cast<const uint16_t *>(p.z);
     const uint16_t *U = static_cast<const uint16_t *>(p.U);
-    uint16_t *dx = static_cast<uint16_t *>(p.dx);
+    uint16_t *dxg = static_cast<uint16_t *>(p.dx);
 
     unsigned char *my = lds + wid * L::kWave;
     unsigned char *dwcT = my;                       // [k][32 tokens][PW]
     unsigned char *zring = my + L::kDwc;            // [4 slots][16 rows][PZ]
-    unsigned char *dzb = my + L::kDwc + L::kZ;      // [2][32 tokens][PD]
+    unsigned char *dzb = my + L::kDwc + L::kZ;      // [32 tokens][PD]
 
     // ---- U operands, kept in registers for the whole walk
     bf16x8 ua[W][2][RC];  // rows: channel d0 + 8(i>>2) + 4t + (i&3); K: rank 32c + 8(lane>>4) + e
@@ -501,7 +523,7 @@ __global__ __launch_bounds__(kBlock, 1) void lr_bwd_mfma(LrParams p, int64_t nsl
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int r = 32 * c + 8 * q + e;
-                    const uint16_t v = (r < R && ch < p.D) ? U[(int64_t)r * DW + ch * W + k] : (uint16_t)0;
+                    const uint16_t v = (r < R && ch < D) ? U[(int64_t)r * DW + ch * W + k] : (uint16_t)0;
                     ua[k][t][c][e] = __builtin_bit_cast(__bf16, v);
                 }
         }
@@ -511,7 +533,7 @@ __global__ __launch_bounds__(kBlock, 1) void lr_bwd_mfma(LrParams p, int64_t nsl
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int64_t ch = d0 + 8 * q + e;
-                const uint16_t v = (r < R && ch < p.D) ? U[(int64_t)r * DW + ch * W + k] : (uint16_t)0;
+                const uint16_t v = (r < R && ch < D) ? U[(int64_t)r * DW + ch * W + k] : (uint16_t)0;
                 ub[k][rt][e] = __builtin_bit_cast(__bf16, v);
             }
         }
@@ -524,236 +546,249 @@ __global__ __launch_bounds__(kBlock, 1) void lr_bwd_mfma(LrParams p, int64_t nsl
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) du[k][ct][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    auto load_act = [&](const uint16_t *src, int64_t n, uint32_t (&dst)[4]) {
-        if (n >= 0 && n < N && chan_ok) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(src + n * p.D + cbase);
-            dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
-        } else {
-            dst[0] = dst[1] = dst[2] = dst[3] = 0u;
-        }
+    StartBits<kSeqWords> starts;
+    starts.build(seq_words[wid], p.seq, N, nbeg - 32, lane);
+
+    // ---- streams: per-lane constant offsets inside a step's 16 token rows
+    const uint32_t xoff = chan_ok ? (uint32_t)((tok * D + cbase) * 2) : kNoOffset;
+    uint32_t zoff[RC];
+#pragma unroll
+    for (int c = 0; c < RC; ++c) {
+        const int r0 = 32 * c + 8 * q;
+        zoff[c] = r0 < R ? (uint32_t)((tok * R + r0) * 2) : kNoOffset;
+    }
+    const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+    auto fetch_act = [&](const uint16_t *src, int64_t step) {
+        const int64_t t0 = nbeg + 16 * step;
+        return buf_load16(make_rsrc(src + t0 * D, (N - t0) * D * 2), xoff);
     };
-    const bool r_vec = (R % 8) == 0;
-    // z row n, rank 32c + 8q .. +7 for c < RC (zero outside [0,N) x [0,R))
-    auto load_z = [&](int64_t n, uint32_t (&dst)[RC][4]) {
+    auto fetch_z = [&](int64_t step, uint4 (&dst)[RC]) {
+        const int64_t t0 = nbeg + 16 * step;
+        if constexpr (RVEC) {
+            const __amdgpu_buffer_rsrc_t rz = make_rsrc(zg + t0 * R, (N - t0) * R * 2);
 #pragma unroll
-        for (int c = 0; c < RC; ++c) {
-            const int r0 = 32 * c + 8 * q;
-            if (n < N && r0 < R) {
-                if (r_vec) {
-                    const uint4 v = *reinterpret_cast<const uint4 *>(z + n * R + r0);
-                    dst[c][0] = v.x; dst[c][1] = v.y; dst[c][2] = v.z; dst[c][3] = v.w;
-                } else {
+            for (int c = 0; c < RC; ++c) dst[c] = buf_load16(rz, zoff[c]);
+        } else {
+            const int64_t n = t0 + tok;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t lo = (r0 + 2 * e < R) ? z[n * R + r0 + 2 * e] : 0u;
-                        const uint32_t hi = (r0 + 2 * e + 1 < R) ? z[n * R + r0 + 2 * e + 1] : 0u;
-                        dst[c][e] = lo | (hi << 16);
-                    }
+            for (int c = 0; c < RC; ++c) {
+                const int r0 = 32 * c + 8 * q;
+                uint32_t h[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t lo = (n < N && r0 + 2 * e < R) ? zg[n * R + r0 + 2 * e] : 0u;
+                    const uint32_t hi = (n < N && r0 + 2 * e + 1 < R) ? zg[n * R + r0 + 2 * e + 1] : 0u;
+                    h[e] = lo | (hi << 16);
                 }
-            } else {
-                dst[c][0] = dst[c][1] = dst[c][2] = dst[c][3] = 0u;
+                dst[c] = make_uint4(h[0], h[1], h[2], h[3]);
             }
         }
     };
     auto zslot = [&](int64_t step) { return zring + (int)(step & 3) * L::SZ; };
-    auto write_z = [&](int64_t step, const uint32_t (&v)[RC][4]) {
+    auto write_z = [&](int64_t step, const uint4 (&v)[RC]) {
         unsigned char *row = zslot(step) + tok * L::PZ;
 #pragma unroll
         for (int c = 0; c < RC; ++c) {
             uint2 *d = reinterpret_cast<uint2 *>(row + 2 * (32 * c + 8 * q));
-            d[0] = make_uint2(v[c][0], v[c][1]);
-            d[1] = make_uint2(v[c][2], v[c][3]);
+            d[0] = make_uint2(v[c].x, v[c].y);
+            d[1] = make_uint2(v[c].z, v[c].w);
         }
     };
 
-    // ---- prologue: x two steps ahead, dy three, z rows three (written to the
-    // LDS ring one step ahead of use)
-    uint32_t xprev[4], xc[4], xn[4], xn2[4], gc[4], gn[4], gn2[4], gn3[4];
-    uint32_t zr[RC][4], zr2[RC][4];
-    if (tok >= 16 - (W - 1)) load_act(x, nbeg - 16 + tok, xprev);
-    else xprev[0] = xprev[1] = xprev[2] = xprev[3] = 0u;
-    load_act(x, nbeg + tok, xc);
-    load_act(x, nbeg + 16 + tok, xn);
-    load_act(g, nbeg + tok, gc);
-    load_act(g, nbeg + 16 + tok, gn);
-    load_act(g, nbeg + 32 + tok, gn2);
-    load_z(nbeg + tok, zr);
-    write_z(0, zr);
-    load_z(nbeg + 16 + tok, zr);
-    load_z(nbeg + 32 + tok, zr2);
+    // ---- register rings (slot = step mod P), refilled without copies:
+    //   x: step s reads slots s, s-1, then refills s-1 with step s+P-1
+    //   g: step s reads slots s, s+1, then refills s with step s+P
+    //   z: step s writes slot s+1 to the LDS ring, then refills it with step s+1+P
+    uint4 xr[P], gr[P];
+    uint4 zr[P][RC];
+#pragma unroll
+    for (int j = 0; j < P - 1; ++j) xr[j] = fetch_act(xg, j);
+    xr[P - 1] = zero4;  // step -1: only its last W-1 tokens are read
+    {
+        const int64_t n = nbeg - 16 + tok;
+        if (n >= 0 && tok >= 16 - (W - 1) && chan_ok)
+            xr[P - 1] = *reinterpret_cast<const uint4 *>(xg + n * D + cbase);
+    }
+#pragma unroll
+    for (int j = 0; j < P; ++j) gr[j] = fetch_act(gg, j);
+    {
+        uint4 z0[RC];
+        fetch_z(0, z0);
+        write_z(0, z0);
+    }
+    fetch_z(P, zr[0]);
+#pragma unroll
+    for (int j = 1; j < P; ++j) fetch_z(j, zr[j]);
 
-    SeqCursor seqc;
-    seqc.init(p.seq, nbeg);
-
-    const int64_t nsteps = 2 * npairs;
     int buf = 0;
+    for (int64_t s0 = 0; s0 < nsteps; s0 += P) {
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int cur = i, prv = (i + P - 1) % P, nxt = (i + 1) % P;
+            const int ps = i & 1;
+            const int64_t s = s0 + i;
+            const int64_t nstep = nbeg + 16 * s;
+            const int64_t n = nstep + tok;
 
-    for (int64_t s = 0; s < nsteps; ++s) {
-        const int ps = (int)(s & 1);
-        const int64_t nstep = nbeg + 16 * s;
-        const int64_t n = nstep + tok;
+            write_z(s + 1, zr[nxt]);  // the wave's own LDS ring; its LDS operations stay in order
+            fetch_z(s + 1 + P, zr[nxt]);
 
-        write_z(s + 1, zr);
-        __syncthreads();  // z rows of steps s, s+1 visible to the wave
-        load_act(x, n + 32, xn2);
-        load_act(g, n + 48, gn3);
-#pragma unroll
-        for (int c = 0; c < RC; ++c)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) zr[c][i] = zr2[c][i];
-        load_z(n + 48, zr2);
+            // sequence masks (branch-free): taps k <= back (dwc) and k < ahead (dx)
+            // stay in n's sequence; bit j of win <-> token nstep - (W-1) + j
+            int back = W - 1, ahead = W;
+            if constexpr (W > 1) {
+                const uint32_t win = __builtin_amdgcn_readfirstlane(starts.window(nstep - (W - 1)));
+                const uint32_t sb = (win >> (tok + 1)) & ((1u << (W - 1)) - 1u);  // starts in n-W+2 .. n
+                back = sb ? (W - 2) - (31 - __builtin_clz(sb)) : W - 1;
+                const uint32_t sa = (win >> (tok + W)) & ((1u << (W - 1)) - 1u);  // starts in n+1 .. n+W-1
+                ahead = sa ? 1 + __builtin_ctz(sa) : W;
+            }
 
-        // sequence masks: taps k <= back (dwc) and k < ahead (dx) stay in n's sequence
-        int back = W - 1, ahead = W;
-        seqc.advance(nstep < N ? nstep : N - 1);
-        if (!((nstep - seqc.s >= W - 1) && (seqc.e >= nstep + 16 + W - 1))) {
-            int64_t sn, en;
-            p.seq.find(n < N ? n : N - 1, sn, en);
-            back = (int)min((int64_t)(W - 1), n - sn);
-            ahead = (int)min((int64_t)W, en - n);
-        }
+            const uint32_t gc[4] = {gr[cur].x, gr[cur].y, gr[cur].z, gr[cur].w};
+            const uint32_t gn[4] = {gr[nxt].x, gr[nxt].y, gr[nxt].z, gr[nxt].w};
+            const uint32_t xc[4] = {xr[cur].x, xr[cur].y, xr[cur].z, xr[cur].w};
+            const uint32_t xp[4] = {xr[prv].x, xr[prv].y, xr[prv].z, xr[prv].w};
 
-        // dx = rho*g + sum_k w[n+k] * g[n+k]; w of tokens n+k on the matrix cores
-        float acc[8];
+            // dx = rho*g + sum_k w[n+k] * g[n+k]; w of tokens n+k on the matrix cores
+            float acc[8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] = p.rho * ((c & 1) ? bf16_hi(gc[c >> 1]) : bf16_lo(gc[c >> 1]));
-#pragma unroll
-        for (int k = 0; k < W; ++k) {
-            const int rr = tok + k;
-            const unsigned char *zrow = zslot(s + (rr >> 4)) + (rr & 15) * L::PZ;
-            bf16x8 zb[RC];
-#pragma unroll
-            for (int c = 0; c < RC; ++c) {
-                const uint2 *src = reinterpret_cast<const uint2 *>(zrow + 2 * (32 * c + 8 * q));
-                const uint2 a = src[0], b = src[1];
-                zb[c] = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
-            }
-            uint32_t gk[4];
-            if (k == 0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) gk[i] = gc[i];
-            } else {
-                shift_ahead4<W>(k, gc, gn, gk);
-            }
-            const float keep = k < ahead ? 1.f : 0.f;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                floatx4 cw = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int c = 0; c < RC; ++c)
-                    cw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua[k][t][c], zb[c], cw, 0, 0, 0);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int c = 4 * t + j;
-                    const float gv = (c & 1) ? bf16_hi(gk[c >> 1]) : bf16_lo(gk[c >> 1]);
-                    acc[c] = __builtin_fmaf(cw[j] * keep, gv, acc[c]);
-                }
-            }
-        }
-        if (n < nend && chan_ok) {
-            uint4 v;
-            v.x = pack_bf16x2(acc[0], acc[1]);
-            v.y = pack_bf16x2(acc[2], acc[3]);
-            v.z = pack_bf16x2(acc[4], acc[5]);
-            v.w = pack_bf16x2(acc[6], acc[7]);
-            *reinterpret_cast<uint4 *>(dx + n * p.D + cbase) = v;
-        }
-
-        // dwc_k = g * x[n-k] (bf16): dz^T partial on the matrix cores, dwc^T staged for dU
-        const bool own = n < nend;  // tokens outside this block's range contribute nothing
-        floatx4 cz[RT];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) cz[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < W; ++k) {
-            uint32_t xk[4];
-            if (k == 0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) xk[i] = xc[i];
-            } else {
-                shift_back4<W>(k, xc, xprev, xk);
-            }
-            uint32_t dw[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t xv = (own && k <= back) ? xk[i] : 0u;
-                dw[i] = pack_bf16x2(bf16_lo(gc[i]) * bf16_lo(xv), bf16_hi(gc[i]) * bf16_hi(xv));
-            }
-            const bf16x8 b = bf16x8_from_u32(dw);
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                cz[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ub[k][rt], b, cz[rt], 0, 0, 0);
-            uint2 *d = reinterpret_cast<uint2 *>(dwcT + k * 32 * L::PW + (16 * ps + tok) * L::PW + 16 * q);
-            d[0] = make_uint2(dw[0], dw[1]);
-            d[1] = make_uint2(dw[2], dw[3]);
-        }
-        // dz partials (rows r = 16rt + 4q + j, column = token) -> LDS for the block reduction
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            float4 *d = reinterpret_cast<float4 *>(dzb + buf * 32 * L::PD + (16 * ps + tok) * L::PD +
-                                                   4 * (16 * rt + 4 * q));
-            *d = make_float4(cz[rt][0], cz[rt][1], cz[rt][2], cz[rt][3]);
-        }
-
-        if (ps == 1) {
-            __syncthreads();
-            // dU_k^T[ch, r] += sum over the pair's 32 tokens of dwc_k^T[ch, tok] * z[tok, r].
-            // Operands re-read transposed from LDS: lane = channel / rank,
-            // registers = tokens 8q .. 8q+7 of the pair.
-            const int64_t s_pair = s - 1;
-            const int trow = 8 * q + (i16 >> 2);  // row addressed by this lane (first half)
-            const int tcol = 4 * (i16 & 3);        // column chunk addressed by this lane
-            bf16x8 zb[RT];
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                uint2 h[2];
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int row = trow + 4 * hh;
-                    h[hh] = lds_read_tr(zslot(s_pair + (row >> 4)) + (row & 15) * L::PZ + 2 * (16 * rt + tcol));
-                }
-                zb[rt] = __builtin_bit_cast(bf16x8, make_uint4(h[0].x, h[0].y, h[1].x, h[1].y));
-            }
+            for (int c = 0; c < 8; ++c) acc[c] = p.rho * ((c & 1) ? bf16_hi(gc[c >> 1]) : bf16_lo(gc[c >> 1]));
 #pragma unroll
             for (int k = 0; k < W; ++k) {
+                const int rr = tok + k;
+                const unsigned char *zrow = zslot(s + (rr >> 4)) + (rr & 15) * L::PZ;
+                bf16x8 zb[RC];
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
+                for (int c = 0; c < RC; ++c) {
+                    const uint2 *src = reinterpret_cast<const uint2 *>(zrow + 2 * (32 * c + 8 * q));
+                    const uint2 a = src[0], b = src[1];
+                    zb[c] = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+                }
+                uint32_t gk[4];
+                if (k == 0) {
+#pragma unroll
+                    for (int i2 = 0; i2 < 4; ++i2) gk[i2] = gc[i2];
+                } else {
+                    shift_ahead4<W>(k, gc, gn, gk);
+                }
+                const float keep = k < ahead ? 1.f : 0.f;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    floatx4 cw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua[k][t][0], zb[0], floatx4{0.f, 0.f, 0.f, 0.f},
+                                                                         0, 0, 0);
+#pragma unroll
+                    for (int c = 1; c < RC; ++c)
+                        cw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua[k][t][c], zb[c], cw, 0, 0, 0);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int c = 4 * t + j;
+                        const float gv = (c & 1) ? bf16_hi(gk[c >> 1]) : bf16_lo(gk[c >> 1]);
+                        acc[c] = __builtin_fmaf(cw[j] * keep, gv, acc[c]);
+                    }
+                }
+            }
+            {
+                uint4 v;
+                v.x = pack_bf16x2(acc[0], acc[1]);
+                v.y = pack_bf16x2(acc[2], acc[3]);
+                v.z = pack_bf16x2(acc[4], acc[5]);
+                v.w = pack_bf16x2(acc[6], acc[7]);
+                buf_store16(make_rsrc(dxg + nstep * D, (nend - nstep) * D * 2), xoff, v);
+            }
+
+            // dwc_k = g * x[n-k] (bf16): dz^T partial on the matrix cores, dwc^T staged for dU
+            const bool own = n < nend;  // tokens outside this block's range contribute nothing
+            floatx4 cz[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) cz[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                uint32_t xk[4];
+                if (k == 0) {
+#pragma unroll
+                    for (int i2 = 0; i2 < 4; ++i2) xk[i2] = xc[i2];
+                } else {
+                    shift_back4<W>(k, xc, xp, xk);
+                }
+                uint32_t dw[4];
+#pragma unroll
+                for (int i2 = 0; i2 < 4; ++i2) {
+                    const uint32_t xv = (own && k <= back) ? xk[i2] : 0u;
+                    dw[i2] = pack_bf16x2(bf16_lo(gc[i2]) * bf16_lo(xv), bf16_hi(gc[i2]) * bf16_hi(xv));
+                }
+                const bf16x8 b = bf16x8_from_u32(dw);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    cz[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ub[k][rt], b, cz[rt], 0, 0, 0);
+                uint2 *d = reinterpret_cast<uint2 *>(dwcT + k * 32 * L::PW + (16 * ps + tok) * L::PW + 16 * q);
+                d[0] = make_uint2(dw[0], dw[1]);
+                d[1] = make_uint2(dw[2], dw[3]);
+            }
+            // dz partials (rows r = 16rt + 4q + j, column = token) -> LDS for the block reduction
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                float4 *d = reinterpret_cast<float4 *>(dzb + (buf * 32 + 16 * ps + tok) * L::PD + 4 * (16 * rt + 4 * q));
+                *d = make_float4(cz[rt][0], cz[rt][1], cz[rt][2], cz[rt][3]);
+            }
+
+            // ring refills (issued after the step's reads of these slots)
+            xr[prv] = fetch_act(xg, s + P - 1);
+            gr[cur] = fetch_act(gg, s + P);
+
+            if (ps == 1) {
+                __syncthreads();  // the pair's dz partials from all four waves
+                // dU_k^T[ch, r] += sum over the pair's 32 tokens of dwc_k^T[ch, tok] * z[tok, r].
+                // Operands re-read transposed from LDS: lane = channel / rank,
+                // registers = tokens 8q .. 8q+7 of the pair.
+                const int64_t s_pair = s - 1;
+                const int trow = 8 * q + (i16 >> 2);  // row addressed by this lane (first half)
+                const int tcol = 4 * (i16 & 3);        // column chunk addressed by this lane
+                bf16x8 zb[RT];
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
                     uint2 h[2];
 #pragma unroll
-                    for (int hh = 0; hh < 2; ++hh)
-                        h[hh] = lds_read_tr(dwcT + k * 32 * L::PW + (trow + 4 * hh) * L::PW + 2 * (16 * ct + tcol));
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(h[0].x, h[0].y, h[1].x, h[1].y));
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int row = trow + 4 * hh;
+                        h[hh] = lds_read_tr(zslot(s_pair + (row >> 4)) + (row & 15) * L::PZ + 2 * (16 * rt + tcol));
+                    }
+                    zb[rt] = __builtin_bit_cast(bf16x8, make_uint4(h[0].x, h[0].y, h[1].x, h[1].y));
+                }
 #pragma unroll
-                    for (int rt = 0; rt < RT; ++rt)
-                        du[k][ct][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, zb[rt], du[k][ct][rt], 0, 0, 0);
+                for (int k = 0; k < W; ++k) {
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct) {
+                        uint2 h[2];
+#pragma unroll
+                        for (int hh = 0; hh < 2; ++hh)
+                            h[hh] = lds_read_tr(dwcT + k * 32 * L::PW + (trow + 4 * hh) * L::PW + 2 * (16 * ct + tcol));
+                        const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(h[0].x, h[0].y, h[1].x, h[1].y));
+#pragma unroll
+                        for (int rt = 0; rt < RT; ++rt)
+                            du[k][ct][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, zb[rt], du[k][ct][rt], 0, 0, 0);
+                    }
+                }
+
+                // block-wide dz reduction for the pair, one atomic per (token, rank)
+                const int64_t npair0 = nbeg + 16 * s_pair;
+                for (int e = threadIdx.x; e < 32 * L::RP; e += kBlock) {
+                    const int tl = e / L::RP, r = e - tl * L::RP;
+                    const int64_t nn = npair0 + tl;
+                    if (r < R && nn < nend) {
+                        float v = 0.f;
+#pragma unroll
+                        for (int w2 = 0; w2 < 4; ++w2)
+                            v += *reinterpret_cast<const float *>(lds + w2 * L::kWave + L::kDwc + L::kZ +
+                                                                  (buf * 32 + tl) * L::PD + 4 * r);
+                        atomicAdd(p.dzacc + nn * R + r, v);
+                    }
+                }
+                if constexpr (L::kDzBufs == 1) {
+                    __syncthreads();  // partials read before the next pair overwrites them
+                } else {
+                    buf ^= 1;         // the next pair writes the other buffer
                 }
             }
-
-            // block-wide dz reduction for the pair, one atomic per (token, rank)
-            const int64_t npair0 = nbeg + 16 * s_pair;
-            for (int e = threadIdx.x; e < 32 * L::RP; e += kBlock) {
-                const int tl = e / L::RP, r = e - tl * L::RP;
-                const int64_t nn = npair0 + tl;
-                if (r < R && nn < nend) {
-                    float v = 0.f;
-#pragma unroll
-                    for (int w2 = 0; w2 < 4; ++w2)
-                        v += *reinterpret_cast<const float *>(lds + w2 * L::kWave + L::kDwc + L::kZ +
-                                                              buf * 32 * L::PD + tl * L::PD + 4 * r);
-                    atomicAdd(p.dzacc + nn * R + r, v);
-                }
-            }
-            buf ^= 1;
-        }
-
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            xprev[i] = xc[i];
-            xc[i] = xn[i];
-            xn[i] = xn2[i];
-            gc[i] = gn[i];
-            gn[i] = gn2[i];
-            gn2[i] = gn3[i];
         }
     }
 
@@ -773,7 +808,7 @@ __global__ __launch_bounds__(kBlock, 1) void lr_bwd_mfma(LrParams p, int64_t nsl
                 for (int j = 0; j < 4; ++j) dus[r * (32 * W) + (16 * ct + 4 * q + j) * W + k] = du[k][ct][rt][j];
             }
     __syncthreads();
-    const int64_t nvalid = (p.D - d0 < 32 ? p.D - d0 : 32) * W;  // channels of this slice inside D
+    const int64_t nvalid = (D - d0 < 32 ? D - d0 : 32) * W;  // channels of this slice inside D
     for (int r = 0; r < R; ++r)
         for (int idx = lane; idx < nvalid; idx += kWave)
             atomicAdd(p.dU + (int64_t)r * DW + d0 * W + idx, dus[r * (32 * W) + idx]);
@@ -829,24 +864,42 @@ hipError_t generic_bwd(const LrProblem &pr, hipStream_t st) {
     return hipGetLastError();
 }
 
-constexpr int kPF = 4;
-constexpr int64_t kTargetWaves = 256 * 8;
+// Forward tuning per rank chunk count (measured on MI355X): the prefetch ring
+// depth in 16-token steps and the number of waves the grid aims for.
+template <int RC>
+struct FwdTune {
+    static constexpr int kPF = RC == 1 ? 8 : 6;
+    static constexpr int64_t kWaves = RC == 1 ? 2048 : 3072;
+};
 
 template <int W, int RC>
 hipError_t mfma_fwd(const LrProblem &pr, hipStream_t st) {
+    constexpr int PF = FwdTune<RC>::kPF;
     LrParams p = make_params<BF16>(pr);
     const int64_t nslices = (p.D + 31) / 32;
-    int64_t tpw = (p.N * nslices + kTargetWaves - 1) / kTargetWaves;
-    tpw = ((tpw + 15) / 16) * 16;
-    if (tpw < 16 * kPF) tpw = 16 * kPF;
+    int64_t tpw = (p.N * nslices + FwdTune<RC>::kWaves - 1) / FwdTune<RC>::kWaves;
+    tpw = ((tpw + 16 * PF - 1) / (16 * PF)) * (16 * PF);  // whole groups of PF steps
+    if (tpw > kMaxTokPerWave) tpw = (kMaxTokPerWave / (16 * PF)) * (16 * PF);
     const int64_t nchunks_t = (p.N + tpw - 1) / tpw;
     const int64_t waves = nchunks_t * nslices;
     const int64_t b = (waves + 3) / 4;
-    if (b) hipLaunchKernelGGL((lr_fwd_mfma<W, RC, kPF>), dim3((unsigned)b), dim3(kBlock), 0, st, p, nslices, tpw);
+    if (b) {
+        if (p.R % 8 == 0)
+            hipLaunchKernelGGL((lr_fwd_mfma<W, RC, PF, true>), dim3((unsigned)b), dim3(kBlock), 0, st, p, nslices, tpw);
+        else
+            hipLaunchKernelGGL((lr_fwd_mfma<W, RC, PF, false>), dim3((unsigned)b), dim3(kBlock), 0, st, p, nslices, tpw);
+    }
     return hipGetLastError();
 }
 
-constexpr int64_t kTargetBwdBlocks = 512;
+#ifndef DSC_LR_BWD_RING
+#define DSC_LR_BWD_RING 4
+#endif
+#ifndef DSC_LR_BWD_BLOCKS
+#define DSC_LR_BWD_BLOCKS 512
+#endif
+constexpr int kBwdRing = DSC_LR_BWD_RING;                   // backward prefetch ring depth (steps)
+constexpr int64_t kTargetBwdBlocks = DSC_LR_BWD_BLOCKS;     // backward grid size target
 
 template <int W, int RC>
 hipError_t mfma_bwd(const LrProblem &pr, hipStream_t st) {
@@ -860,10 +913,15 @@ hipError_t mfma_bwd(const LrProblem &pr, hipStream_t st) {
     int64_t tchunks = kTargetBwdBlocks / ngroups;
     if (tchunks < 1) tchunks = 1;
     int64_t tpb = (p.N + tchunks - 1) / tchunks;
-    tpb = ((tpb + 31) / 32) * 32;
+    tpb = ((tpb + 16 * kBwdRing - 1) / (16 * kBwdRing)) * (16 * kBwdRing);  // whole rings of steps
+    if (tpb > kMaxTokPerWave) tpb = kMaxTokPerWave;
     tchunks = (p.N + tpb - 1) / tpb;
-    hipLaunchKernelGGL((lr_bwd_mfma<W, RC>), dim3((unsigned)(tchunks * ngroups)), dim3(kBlock), 0, st, p,
-                       nslices, tpb);
+    if (p.R % 8 == 0)
+        hipLaunchKernelGGL((lr_bwd_mfma<W, RC, kBwdRing, true>), dim3((unsigned)(tchunks * ngroups)), dim3(kBlock),
+                           0, st, p, nslices, tpb);
+    else
+        hipLaunchKernelGGL((lr_bwd_mfma<W, RC, kBwdRing, false>), dim3((unsigned)(tchunks * ngroups)), dim3(kBlock),
+                           0, st, p, nslices, tpb);
     hipLaunchKernelGGL(cast_f32_bf16, dim3((unsigned)nblocks(nz)), dim3(kBlock), 0, st, p.dzacc,
                        static_cast<uint16_t *>(p.dz), nz);
     return hipGetLastError();
