@@ -171,15 +171,22 @@ struct Span {
 
 // ----------------------------------------------------------- buffer access
 
-// Raw buffer resource over [base, base + bytes): loads outside the range read
-// zero and stores outside it are dropped by the hardware, which replaces
-// per-lane bounds branches.  `bytes` is clamped to 32 bits; lanes that must
-// not touch memory use kNoOffset.
+// Raw buffer resources: loads outside a resource's range read zero and
+// stores outside it are dropped by the hardware, which replaces per-lane
+// bounds branches on the streaming paths.
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // gfx9-family raw buffer format
-constexpr uint32_t kNoOffset = 0xffffffffu;
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
-    const int64_t b = bytes < 0 ? 0 : (bytes > 0xffffffffll ? 0xffffffffll : bytes);
+// Streams with one resource per walk: a lane's offset is its place inside a
+// step plus the step's offset, both below 2^30 (the launchers cap the walk
+// length so that this holds).  Lanes with nothing to move start at kFar; the
+// resource size is clamped to kFar, so they stay out of range at every step
+// and no offset comes near the top of the 32-bit range.  Atomics never rely
+// on the range check: they are issued only by lanes whose offset is in range.
+constexpr uint32_t kFar = 0xc0000000u;
+constexpr int64_t kStreamSpan = 0x3fffffff;  // largest in-walk offset
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_stream(const void *base, int64_t bytes) {
+    const int64_t b = bytes < 0 ? 0 : (bytes > (int64_t)kFar ? (int64_t)kFar : bytes);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)(uint32_t)b, kBufferWord3);
 }
 

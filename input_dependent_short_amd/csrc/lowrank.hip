@@ -159,6 +159,92 @@ __global__ __launch_bounds__(kBlock) void lr_bwd_generic(LrParams p) {
 
 // ------------------------------------------------------------- bf16 MFMA
 
+// W consecutive bf16 values of U (the taps of one rank and channel) as raw
+// bits, with the widest accesses that the alignment allows: the offset
+// (r*D + ch)*W*2 is a multiple of the largest power of two dividing 2W
+// because D % 8 == 0.
+template <int W>
+__device__ __forceinline__ void load_taps(const uint16_t *p, uint16_t (&v)[W]) {
+    constexpr int PER = pow2_align(2 * W) / 2;  // elements per access
+#pragma unroll
+    for (int i = 0; i < W; i += PER) {
+        if constexpr (PER == 8) {
+            const uint4 q = *reinterpret_cast<const uint4 *>(p + i);
+            const uint32_t h[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[i + 2 * j] = (uint16_t)(h[j] & 0xffffu);
+                v[i + 2 * j + 1] = (uint16_t)(h[j] >> 16);
+            }
+        } else if constexpr (PER == 4) {
+            const uint2 q = *reinterpret_cast<const uint2 *>(p + i);
+            v[i] = (uint16_t)(q.x & 0xffffu); v[i + 1] = (uint16_t)(q.x >> 16);
+            v[i + 2] = (uint16_t)(q.y & 0xffffu); v[i + 3] = (uint16_t)(q.y >> 16);
+        } else if constexpr (PER == 2) {
+            const uint32_t q = *reinterpret_cast<const uint32_t *>(p + i);
+            v[i] = (uint16_t)(q & 0xffffu); v[i + 1] = (uint16_t)(q >> 16);
+        } else {
+            v[i] = p[i];
+        }
+    }
+}
+
+// A operand of w = z U for every tap k, kept in registers: rows are the
+// channels of a 32-channel slice (tile t, row i <-> channel
+// d0 + 8(i>>2) + 4t + (i&3)), K is rank 32c + 8(lane>>4) + e.  Zero outside R
+// and D.
+template <int W, int RC>
+__device__ __forceinline__ void load_u_rows(const uint16_t *U, int R, int64_t D, int64_t d0, int lane,
+                                            bf16x8 (&ua)[W][2][RC]) {
+    const int i16 = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int64_t ch = d0 + 8 * (i16 >> 2) + 4 * t + (i16 & 3);
+#pragma unroll
+        for (int c = 0; c < RC; ++c)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int r = 32 * c + 8 * q + e;
+                uint16_t v[W];
+#pragma unroll
+                for (int k = 0; k < W; ++k) v[k] = 0;
+                if (r < R && ch < D) load_taps<W>(U + ((int64_t)r * D + ch) * W, v);
+#pragma unroll
+                for (int k = 0; k < W; ++k) ua[k][t][c][e] = __builtin_bit_cast(__bf16, v[k]);
+            }
+    }
+}
+
+// A operand of dz^T = U_k dwc_k for every tap k: rows are ranks
+// 16rt + (lane&15), K is channel d0 + 8(lane>>4) + e.  A lane's 8 channels
+// and W taps are 8W consecutive values of U, 16-byte aligned.
+template <int W, int RT>
+__device__ __forceinline__ void load_u_cols(const uint16_t *U, int R, int64_t D, int64_t d0, int lane,
+                                            bf16x8 (&ub)[W][RT]) {
+    const int i16 = lane & 15, q = lane >> 4;
+    const int64_t ch0 = d0 + 8 * q;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int r = 16 * rt + i16;
+        uint32_t h[4 * W];
+#pragma unroll
+        for (int j = 0; j < 4 * W; ++j) h[j] = 0u;
+        if (r < R && ch0 < D) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(U + ((int64_t)r * D + ch0) * W);
+#pragma unroll
+            for (int j = 0; j < W; ++j) {
+                const uint4 v = src[j];
+                h[4 * j] = v.x; h[4 * j + 1] = v.y; h[4 * j + 2] = v.z; h[4 * j + 3] = v.w;
+            }
+        }
+#pragma unroll
+        for (int idx = 0; idx < 8 * W; ++idx) {  // element idx = channel e * W + tap k
+            const uint16_t v = (uint16_t)((idx & 1) ? (h[idx >> 1] >> 16) : (h[idx >> 1] & 0xffffu));
+            ub[idx % W][rt][idx / W] = __builtin_bit_cast(__bf16, v);
+        }
+    }
+}
+
 // DPP controls (row = 16 lanes): lane i of a row reads lane i-k (shr) or
 // lane (i-k) mod 16 (ror).
 template <int K>
@@ -184,10 +270,11 @@ __device__ __forceinline__ void fill_shift(Shifted<W> &xs, const uint32_t (&cur)
 // Wave tile: 16 tokens (one per lane column) x 32 channels (two 16-row MFMA
 // tiles).  Lane l: token l & 15, channel group q = l >> 4 owning channels
 // d0 + 8q .. d0 + 8q + 7.  MFMA tile t, row i <-> channel d0 + 8(i>>2) + 4t + (i&3).
-// x, z and y move through raw buffer resources rebased every 16-token step
-// (scalar work only); each lane keeps one constant 32-bit offset, and tokens
-// past the wave's range fall outside the resource (loads read zero, stores
-// are dropped).  Loads run PF steps ahead in a register ring.
+// x, z and y move through one raw buffer resource each over the wave's
+// token range; a lane's offset is its constant place in a step plus the
+// step's offset, and tokens past the range fall outside the resource (loads
+// read zero, stores are dropped).  Loads run PF steps ahead in a register
+// ring.
 template <int W, int RC, int PF, bool RVEC>
 __global__ __launch_bounds__(kBlock) void lr_fwd_mfma(LrParams p, int64_t nslices, int64_t tok_per_wave) {
     const int lane = threadIdx.x & 63;
@@ -215,47 +302,32 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_mfma(LrParams p, int64_t nslice
 
     // A operands: U_k^T rows (channels) x K (rank), per tap k, tile t, K chunk c.
     bf16x8 ua[W][2][RC];
-    {
-        const int row = lane & 15;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int64_t ch = d0 + 8 * (row >> 2) + 4 * t + (row & 3);
-#pragma unroll
-            for (int c = 0; c < RC; ++c) {
-#pragma unroll
-                for (int k = 0; k < W; ++k) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const int r = 32 * c + 8 * q + i;
-                        uint16_t v = 0;
-                        if (r < R && ch < D) v = U[(int64_t)r * DW + ch * W + k];
-                        ua[k][t][c][i] = __builtin_bit_cast(__bf16, v);
-                    }
-                }
-            }
-        }
-    }
+    load_u_rows<W, RC>(U, R, D, d0, lane, ua);
 
     const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
-    // per-lane byte offsets inside a step's 16 token rows
-    const uint32_t xoff = chan_ok ? (uint32_t)((tok * D + cbase) * 2) : kNoOffset;
+    // streams over the wave's rows [nbeg, nend): lane offset inside a step
+    // plus the step's offset
+    const uint32_t act_step = (uint32_t)(16 * D * 2);
+    const uint32_t z_step = (uint32_t)(16 * R * 2);
+    const uint32_t xoff = chan_ok ? (uint32_t)((tok * D + cbase) * 2) : kFar;
     uint32_t zoff[RC];
 #pragma unroll
     for (int c = 0; c < RC; ++c) {
         const int r0 = 32 * c + 8 * q;
-        zoff[c] = r0 < R ? (uint32_t)((tok * R + r0) * 2) : kNoOffset;
+        zoff[c] = r0 < R ? (uint32_t)((tok * R + r0) * 2) : kFar;
     }
+    const __amdgpu_buffer_rsrc_t rx = make_stream(xg + nbeg * D, (nend - nbeg) * D * 2);
+    const __amdgpu_buffer_rsrc_t rz = make_stream(zg + nbeg * R, (nend - nbeg) * R * 2);
+    const __amdgpu_buffer_rsrc_t ry = make_stream(yg + nbeg * D, (nend - nbeg) * D * 2);
 
-    // prefetch cursor (wave-uniform): first token of the step being fetched
+    // prefetch cursor (wave-uniform): the step being fetched
+    int fstep = 0;
     int64_t fpos = nbeg;
     auto fetch = [&](uint4 &xd, uint4 (&zd)[RC]) {
-        const int64_t rows = nend - fpos;  // tokens of the range left from fpos
-        const __amdgpu_buffer_rsrc_t rx = make_rsrc(xg + fpos * D, rows * D * 2);
-        xd = buf_load16(rx, xoff);
+        xd = buf_load16(rx, xoff + (uint32_t)fstep * act_step);
         if constexpr (RVEC) {
-            const __amdgpu_buffer_rsrc_t rz = make_rsrc(zg + fpos * R, rows * R * 2);
 #pragma unroll
-            for (int c = 0; c < RC; ++c) zd[c] = buf_load16(rz, zoff[c]);
+            for (int c = 0; c < RC; ++c) zd[c] = buf_load16(rz, zoff[c] + (uint32_t)fstep * z_step);
         } else {
             const int64_t n = fpos + tok;
 #pragma unroll
@@ -271,6 +343,7 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_mfma(LrParams p, int64_t nslice
                 zd[c] = make_uint4(h[0], h[1], h[2], h[3]);
             }
         }
+        fstep += 1;
         fpos += 16;
     };
 
@@ -356,7 +429,7 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_mfma(LrParams p, int64_t nslice
                 v.y = pack_bf16x2(out[2], out[3]);
                 v.z = pack_bf16x2(out[4], out[5]);
                 v.w = pack_bf16x2(out[6], out[7]);
-                buf_store16(make_rsrc(yg + nstep * D, (nend - nstep) * D * 2), xoff, v);
+                buf_store16(ry, xoff + (uint32_t)(s0 + i) * act_step, v);
 
                 fetch(xq[ip], zq[ip]);  // step s0 + i + PF - 1
                 nstep += 16;
@@ -427,8 +500,8 @@ __device__ __forceinline__ bf16x8 bf16x8_from_u32(const uint32_t (&v)[4]) {
 //     operand (U_k, rank rows x channel K) is also kept in registers;
 //   * dwc_k is staged in LDS and re-read transposed (lane = channel,
 //     registers = tokens) as the A operand of dU_k^T += dwc_k^T * Z.
-// x, dy and z stream through raw buffer resources rebased per step, into
-// register rings refilled P steps ahead without copies.  dz is summed over
+// x, dy and z stream through one buffer resource each (offset = lane place +
+// step offset), into register rings refilled P steps ahead without copies.  dz is summed over
 // the block's 4 waves in LDS and added to an fp32 accumulator with one atomic
 // per (token, rank); dU stays in registers over the whole token range and is
 // added to the fp32 output with coalesced atomics at the end.  Both
@@ -513,31 +586,8 @@ __global__ __launch_bounds__(kBlock, (BwdLds<W, RC>::kBlocksPerCu)) void lr_bwd_
     // ---- U operands, kept in registers for the whole walk
     bf16x8 ua[W][2][RC];  // rows: channel d0 + 8(i>>2) + 4t + (i&3); K: rank 32c + 8(lane>>4) + e
     bf16x8 ub[W][RT];     // rows: rank 16rt + (lane&15); K: channel d0 + 8(lane>>4) + e
-#pragma unroll
-    for (int k = 0; k < W; ++k) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int64_t ch = d0 + 8 * (i16 >> 2) + 4 * t + (i16 & 3);
-#pragma unroll
-            for (int c = 0; c < RC; ++c)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int r = 32 * c + 8 * q + e;
-                    const uint16_t v = (r < R && ch < D) ? U[(int64_t)r * DW + ch * W + k] : (uint16_t)0;
-                    ua[k][t][c][e] = __builtin_bit_cast(__bf16, v);
-                }
-        }
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const int r = 16 * rt + i16;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int64_t ch = d0 + 8 * q + e;
-                const uint16_t v = (r < R && ch < D) ? U[(int64_t)r * DW + ch * W + k] : (uint16_t)0;
-                ub[k][rt][e] = __builtin_bit_cast(__bf16, v);
-            }
-        }
-    }
+    load_u_rows<W, RC>(U, R, D, d0, lane, ua);
+    load_u_cols<W, RT>(U, R, D, d0, lane, ub);
     floatx4 du[W][2][RT];
 #pragma unroll
     for (int k = 0; k < W; ++k)
@@ -549,26 +599,31 @@ __global__ __launch_bounds__(kBlock, (BwdLds<W, RC>::kBlocksPerCu)) void lr_bwd_
     StartBits<kSeqWords> starts;
     starts.build(seq_words[wid], p.seq, N, nbeg - 32, lane);
 
-    // ---- streams: per-lane constant offsets inside a step's 16 token rows
-    const uint32_t xoff = chan_ok ? (uint32_t)((tok * D + cbase) * 2) : kNoOffset;
+    // ---- streams over the block's rows (x, dy and z up to N, dx up to nend):
+    // lane offset inside a step plus the step's offset
+    const uint32_t act_step = (uint32_t)(16 * D * 2);
+    const uint32_t z_step = (uint32_t)(16 * R * 2);
+    const uint32_t xoff = chan_ok ? (uint32_t)((tok * D + cbase) * 2) : kFar;
     uint32_t zoff[RC];
 #pragma unroll
     for (int c = 0; c < RC; ++c) {
         const int r0 = 32 * c + 8 * q;
-        zoff[c] = r0 < R ? (uint32_t)((tok * R + r0) * 2) : kNoOffset;
+        zoff[c] = r0 < R ? (uint32_t)((tok * R + r0) * 2) : kFar;
     }
+    const __amdgpu_buffer_rsrc_t rx = make_stream(xg + nbeg * D, (N - nbeg) * D * 2);
+    const __amdgpu_buffer_rsrc_t rg = make_stream(gg + nbeg * D, (N - nbeg) * D * 2);
+    const __amdgpu_buffer_rsrc_t rz = make_stream(zg + nbeg * R, (N - nbeg) * R * 2);
+    const __amdgpu_buffer_rsrc_t rdx = make_stream(dxg + nbeg * D, (nend - nbeg) * D * 2);
     const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
-    auto fetch_act = [&](const uint16_t *src, int64_t step) {
-        const int64_t t0 = nbeg + 16 * step;
-        return buf_load16(make_rsrc(src + t0 * D, (N - t0) * D * 2), xoff);
+    auto fetch_act = [&](__amdgpu_buffer_rsrc_t r, int64_t step) {
+        return buf_load16(r, xoff + (uint32_t)step * act_step);
     };
     auto fetch_z = [&](int64_t step, uint4 (&dst)[RC]) {
-        const int64_t t0 = nbeg + 16 * step;
         if constexpr (RVEC) {
-            const __amdgpu_buffer_rsrc_t rz = make_rsrc(zg + t0 * R, (N - t0) * R * 2);
 #pragma unroll
-            for (int c = 0; c < RC; ++c) dst[c] = buf_load16(rz, zoff[c]);
+            for (int c = 0; c < RC; ++c) dst[c] = buf_load16(rz, zoff[c] + (uint32_t)step * z_step);
         } else {
+            const int64_t t0 = nbeg + 16 * step;
             const int64_t n = t0 + tok;
 #pragma unroll
             for (int c = 0; c < RC; ++c) {
@@ -602,7 +657,7 @@ __global__ __launch_bounds__(kBlock, (BwdLds<W, RC>::kBlocksPerCu)) void lr_bwd_
     uint4 xr[P], gr[P];
     uint4 zr[P][RC];
 #pragma unroll
-    for (int j = 0; j < P - 1; ++j) xr[j] = fetch_act(xg, j);
+    for (int j = 0; j < P - 1; ++j) xr[j] = fetch_act(rx, j);
     xr[P - 1] = zero4;  // step -1: only its last W-1 tokens are read
     {
         const int64_t n = nbeg - 16 + tok;
@@ -610,7 +665,7 @@ __global__ __launch_bounds__(kBlock, (BwdLds<W, RC>::kBlocksPerCu)) void lr_bwd_
             xr[P - 1] = *reinterpret_cast<const uint4 *>(xg + n * D + cbase);
     }
 #pragma unroll
-    for (int j = 0; j < P; ++j) gr[j] = fetch_act(gg, j);
+    for (int j = 0; j < P; ++j) gr[j] = fetch_act(rg, j);
     {
         uint4 z0[RC];
         fetch_z(0, z0);
@@ -619,6 +674,10 @@ __global__ __launch_bounds__(kBlock, (BwdLds<W, RC>::kBlocksPerCu)) void lr_bwd_
     fetch_z(P, zr[0]);
 #pragma unroll
     for (int j = 1; j < P; ++j) fetch_z(j, zr[j]);
+
+    // dz atomics: rank of this lane and its element offset inside a pair
+    const int dz_rank = (int)threadIdx.x % L::RP;
+    const uint32_t dz_block_off = (uint32_t)(((int)threadIdx.x / L::RP) * R + dz_rank);
 
     int buf = 0;
     for (int64_t s0 = 0; s0 < nsteps; s0 += P) {
@@ -670,8 +729,9 @@ __global__ __launch_bounds__(kBlock, (BwdLds<W, RC>::kBlocksPerCu)) void lr_bwd_
                     for (int i2 = 0; i2 < 4; ++i2) gk[i2] = gc[i2];
                 } else {
                     shift_ahead4<W>(k, gc, gn, gk);
+#pragma unroll
+                    for (int i2 = 0; i2 < 4; ++i2) gk[i2] = k < ahead ? gk[i2] : 0u;  // m+k in m's sequence
                 }
-                const float keep = k < ahead ? 1.f : 0.f;
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     floatx4 cw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua[k][t][0], zb[0], floatx4{0.f, 0.f, 0.f, 0.f},
@@ -683,7 +743,7 @@ __global__ __launch_bounds__(kBlock, (BwdLds<W, RC>::kBlocksPerCu)) void lr_bwd_
                     for (int j = 0; j < 4; ++j) {
                         const int c = 4 * t + j;
                         const float gv = (c & 1) ? bf16_hi(gk[c >> 1]) : bf16_lo(gk[c >> 1]);
-                        acc[c] = __builtin_fmaf(cw[j] * keep, gv, acc[c]);
+                        acc[c] = __builtin_fmaf(cw[j], gv, acc[c]);
                     }
                 }
             }
@@ -693,7 +753,7 @@ __global__ __launch_bounds__(kBlock, (BwdLds<W, RC>::kBlocksPerCu)) void lr_bwd_
                 v.y = pack_bf16x2(acc[2], acc[3]);
                 v.z = pack_bf16x2(acc[4], acc[5]);
                 v.w = pack_bf16x2(acc[6], acc[7]);
-                buf_store16(make_rsrc(dxg + nstep * D, (nend - nstep) * D * 2), xoff, v);
+                buf_store16(rdx, xoff + (uint32_t)s * act_step, v);
             }
 
             // dwc_k = g * x[n-k] (bf16): dz^T partial on the matrix cores, dwc^T staged for dU
@@ -732,8 +792,8 @@ __global__ __launch_bounds__(kBlock, (BwdLds<W, RC>::kBlocksPerCu)) void lr_bwd_
             }
 
             // ring refills (issued after the step's reads of these slots)
-            xr[prv] = fetch_act(xg, s + P - 1);
-            gr[cur] = fetch_act(gg, s + P);
+            xr[prv] = fetch_act(rx, s + P - 1);
+            gr[cur] = fetch_act(rg, s + P);
 
             if (ps == 1) {
                 __syncthreads();  // the pair's dz partials from all four waves
@@ -769,24 +829,36 @@ __global__ __launch_bounds__(kBlock, (BwdLds<W, RC>::kBlocksPerCu)) void lr_bwd_
                     }
                 }
 
-                // block-wide dz reduction for the pair, one atomic per (token, rank)
+                // dz of the pair's 32 tokens: fp32 atomics into the accumulator, issued
+                // only by lanes of ranks below R and tokens inside the block's range,
+                // each at an in-range offset of a resource based at the pair's row
                 const int64_t npair0 = nbeg + 16 * s_pair;
-                for (int e = threadIdx.x; e < 32 * L::RP; e += kBlock) {
-                    const int tl = e / L::RP, r = e - tl * L::RP;
-                    const int64_t nn = npair0 + tl;
-                    if (r < R && nn < nend) {
-                        float v = 0.f;
+                const __amdgpu_buffer_rsrc_t rdz = make_stream(p.dzacc + npair0 * R, (nend - npair0) * R * 4);
+                {
+                    // block-wide: thread e sums (token e / RP, rank e % RP) over the four waves
+                    constexpr int kIt = 32 * L::RP / kBlock;
+                    float v[kIt];
 #pragma unroll
-                        for (int w2 = 0; w2 < 4; ++w2)
-                            v += *reinterpret_cast<const float *>(lds + w2 * L::kWave + L::kDwc + L::kZ +
-                                                                  (buf * 32 + tl) * L::PD + 4 * r);
-                        atomicAdd(p.dzacc + nn * R + r, v);
+                    for (int it = 0; it < kIt; ++it) {
+                        const int e = threadIdx.x + it * kBlock, tl = e / L::RP, r = e % L::RP;
+                        const unsigned char *src = lds + L::kDwc + L::kZ + (buf * 32 + tl) * L::PD + 4 * r;
+                        float a = 0.f;
+#pragma unroll
+                        for (int w2 = 0; w2 < 4; ++w2) a += *reinterpret_cast<const float *>(src + w2 * L::kWave);
+                        v[it] = a;
                     }
-                }
-                if constexpr (L::kDzBufs == 1) {
-                    __syncthreads();  // partials read before the next pair overwrites them
-                } else {
-                    buf ^= 1;         // the next pair writes the other buffer
+#pragma unroll
+                    for (int it = 0; it < kIt; ++it) {
+                        const int tl = (int)threadIdx.x / L::RP + it * (kBlock / L::RP);
+                        if (dz_rank < R && npair0 + tl < nend)
+                            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+                                v[it], rdz, 4 * (dz_block_off + (uint32_t)(it * (kBlock / L::RP) * R)), 0, 0);
+                    }
+                    if constexpr (L::kDzBufs == 1) {
+                        __syncthreads();  // partials read before the next pair overwrites them
+                    } else {
+                        buf ^= 1;         // the next pair writes the other buffer
+                    }
                 }
             }
         }
@@ -879,7 +951,11 @@ hipError_t mfma_fwd(const LrProblem &pr, hipStream_t st) {
     const int64_t nslices = (p.D + 31) / 32;
     int64_t tpw = (p.N * nslices + FwdTune<RC>::kWaves - 1) / FwdTune<RC>::kWaves;
     tpw = ((tpw + 16 * PF - 1) / (16 * PF)) * (16 * PF);  // whole groups of PF steps
-    if (tpw > kMaxTokPerWave) tpw = (kMaxTokPerWave / (16 * PF)) * (16 * PF);
+    // walk length cap: the LDS bitmap, and stream offsets below 2^30
+    const int64_t span = kStreamSpan / (2 * p.D) - 16 * (2 * PF + 2);
+    const int64_t cap = ((span < kMaxTokPerWave ? span : kMaxTokPerWave) / (16 * PF)) * (16 * PF);
+    if (cap < 16 * PF) return generic_fwd<BF16, W>(pr, st);
+    if (tpw > cap) tpw = cap;
     const int64_t nchunks_t = (p.N + tpw - 1) / tpw;
     const int64_t waves = nchunks_t * nslices;
     const int64_t b = (waves + 3) / 4;
@@ -904,6 +980,10 @@ constexpr int64_t kTargetBwdBlocks = DSC_LR_BWD_BLOCKS;     // backward grid siz
 template <int W, int RC>
 hipError_t mfma_bwd(const LrProblem &pr, hipStream_t st) {
     LrParams p = make_params<BF16>(pr);
+    // walk length cap: the LDS bitmap, and stream offsets below 2^30
+    const int64_t span = kStreamSpan / (2 * p.D) - 16 * (2 * kBwdRing + 2);
+    const int64_t cap = ((span < kMaxTokPerWave ? span : kMaxTokPerWave) / (16 * kBwdRing)) * (16 * kBwdRing);
+    if (cap < 16 * kBwdRing) return generic_bwd<BF16, W>(pr, st);
     const int64_t nU = (int64_t)p.R * p.D * W;
     const int64_t nz = p.N * p.R;
     hipLaunchKernelGGL(fill_zero_f32, dim3((unsigned)nblocks(nU)), dim3(kBlock), 0, st, p.dU, nU);
@@ -914,7 +994,7 @@ hipError_t mfma_bwd(const LrProblem &pr, hipStream_t st) {
     if (tchunks < 1) tchunks = 1;
     int64_t tpb = (p.N + tchunks - 1) / tchunks;
     tpb = ((tpb + 16 * kBwdRing - 1) / (16 * kBwdRing)) * (16 * kBwdRing);  // whole rings of steps
-    if (tpb > kMaxTokPerWave) tpb = kMaxTokPerWave;
+    if (tpb > cap) tpb = cap;
     tchunks = (p.N + tpb - 1) / tpb;
     if (p.R % 8 == 0)
         hipLaunchKernelGGL((lr_bwd_mfma<W, RC, kBwdRing, true>), dim3((unsigned)(tchunks * ngroups)), dim3(kBlock),
