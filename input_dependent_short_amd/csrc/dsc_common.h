@@ -169,6 +169,13 @@ struct Span {
     }
 };
 
+// Orders a wave's LDS writes before its later LDS reads at compile time.
+// Lanes that read what other lanes of the same wave wrote need it: without
+// it the compiler may move a read above a write whose address differs in
+// every single lane.  It emits no instruction (LDS operations of one wave
+// execute in issue order).
+__device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); }
+
 // ----------------------------------------------------------- buffer access
 
 // Raw buffer resources: loads outside a resource's range read zero and
@@ -284,15 +291,17 @@ struct StartBits {
     uint32_t *words;  // LDS, owned by one wave
     int64_t base;
 
-    // All 64 lanes of the wave call this; the caller synchronises before use.
+    // All 64 lanes of the wave call this; it ends with a wave LDS fence, so
+    // the wave can read the map right after.
     __device__ void build(uint32_t *lds_words, const SeqMap &m, int64_t N, int64_t first_token, int lane) {
         words = lds_words;
         base = first_token;
         const int64_t hi = base + 32 * (int64_t)kWords;
-        // The wave's LDS operations complete in issue order, so the zeroing
-        // below is visible to the marking that follows and both to the
-        // caller's later reads.
+        // The wave's LDS operations execute in issue order; the fences keep
+        // the compiler from reordering the zeroing, the marking by other
+        // lanes and the caller's reads.
         for (int i = lane; i < kWords; i += kWave) words[i] = 0u;
+        wave_lds_fence();
         auto mark = [&](int64_t t) {
             if (t >= base && t < hi) {
                 const int64_t o = t - base;
@@ -320,6 +329,7 @@ struct StartBits {
                 mark(t);
             }
         }
+        wave_lds_fence();  // the caller's window reads see every lane's marks
     }
 
     // 32 bits of the map starting at token t (base <= t, t + 32 <= base + 32*kWords).

@@ -23,6 +23,8 @@
 //
 // The generic kernels (any dtype; fp32 always uses them) evaluate the same
 // sums on the vector ALU; dz and dU are reduced with fp32 atomics.
+#include <atomic>
+
 #include "dsc_kernels.h"
 
 namespace dsc {
@@ -36,6 +38,7 @@ struct LrParams {
     int64_t N, D;
     int32_t R;
     float rho;
+    uint32_t rmask;  // all ones with the residual term, else zero
     int64_t nchunks;
 };
 
@@ -415,7 +418,7 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_mfma(LrParams p, int64_t nslice
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
                     const int t = c >> 2, j = c & 3;
-                    float a = p.rho * ((c & 1) ? bf16_hi(xc[c >> 1]) : bf16_lo(xc[c >> 1]));
+                    float a = __uint_as_float(((c & 1) ? (xc[c >> 1] & 0xffff0000u) : (xc[c >> 1] << 16)) & p.rmask);
 #pragma unroll
                     for (int k = 0; k < W; ++k) {
                         const uint32_t v = xs.v[k][c >> 1];
@@ -511,10 +514,11 @@ struct BwdLds {
     static constexpr int RP = 32 * RC;           // padded rank
     static constexpr int PW = 72;                // bytes per token row of dwc^T (32 ch + pad, 8-aligned)
     static constexpr int PZ = 2 * RP + 8;        // bytes per z row
-    static constexpr int SZ = 16 * PZ + 32;      // bytes per z ring slot (16 rows)
     static constexpr int PD = 4 * RP + 16;       // bytes per token row of dz partials
     static constexpr int kDwc = W * 32 * PW;
-    static constexpr int kZ = 4 * SZ;
+    // z ring: 4 steps of 16 rows, then a copy of the first step's rows, so
+    // that rows slot*16 + j (j < 32) are contiguous for every slot
+    static constexpr int kZ = 80 * PZ;
     // Two blocks per CU (R <= 32, W <= 4: registers and LDS fit) keep one
     // buffer of dz partials per wave and pay a second barrier per pair;
     // otherwise the buffer is doubled and the pairs alternate.
@@ -546,7 +550,7 @@ __global__ __launch_bounds__(kBlock, (BwdLds<W, RC>::kBlocksPerCu)) void lr_bwd_
                                                                                    int64_t tok_per_block) {
     using L = BwdLds<W, RC>;
     constexpr int RT = 2 * RC;  // 16-row rank tiles
-    static_assert(P % 2 == 0 && P >= 2, "ring holds whole pairs of steps");
+    static_assert(P % 4 == 0, "the register rings cover whole turns of the 4-slot z ring");
     __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBlock];
     __shared__ uint32_t seq_words[kBlock / kWave][kSeqWords];
 
@@ -580,7 +584,7 @@ __global__ __launch_bounds__(kBlock, (BwdLds<W, RC>::kBlocksPerCu)) void lr_bwd_
 
     unsigned char *my = lds + wid * L::kWave;
     unsigned char *dwcT = my;                       // [k][32 tokens][PW]
-    unsigned char *zring = my + L::kDwc;            // [4 slots][16 rows][PZ]
+    unsigned char *zring = my + L::kDwc;            // [64 + 16 rows][PZ]
     unsigned char *dzb = my + L::kDwc + L::kZ;      // [32 tokens][PD]
 
     // ---- U operands, kept in registers for the whole walk
@@ -639,14 +643,18 @@ __global__ __launch_bounds__(kBlock, (BwdLds<W, RC>::kBlocksPerCu)) void lr_bwd_
             }
         }
     };
-    auto zslot = [&](int64_t step) { return zring + (int)(step & 3) * L::SZ; };
-    auto write_z = [&](int64_t step, const uint4 (&v)[RC]) {
-        unsigned char *row = zslot(step) + tok * L::PZ;
+    // z rows of ring slot `slot` (= step mod 4, known after unrolling)
+    auto zrows = [&](int slot) { return zring + 16 * slot * L::PZ; };
+    auto write_z = [&](int slot, const uint4 (&v)[RC]) {
 #pragma unroll
-        for (int c = 0; c < RC; ++c) {
-            uint2 *d = reinterpret_cast<uint2 *>(row + 2 * (32 * c + 8 * q));
-            d[0] = make_uint2(v[c].x, v[c].y);
-            d[1] = make_uint2(v[c].z, v[c].w);
+        for (int copy = 0; copy < (slot == 0 ? 2 : 1); ++copy) {
+            unsigned char *row = zring + (16 * (slot + 4 * copy) + tok) * L::PZ;
+#pragma unroll
+            for (int c = 0; c < RC; ++c) {
+                uint2 *d = reinterpret_cast<uint2 *>(row + 2 * (32 * c + 8 * q));
+                d[0] = make_uint2(v[c].x, v[c].y);
+                d[1] = make_uint2(v[c].z, v[c].w);
+            }
         }
     };
 
@@ -689,7 +697,10 @@ __global__ __launch_bounds__(kBlock, (BwdLds<W, RC>::kBlocksPerCu)) void lr_bwd_
             const int64_t nstep = nbeg + 16 * s;
             const int64_t n = nstep + tok;
 
-            write_z(s + 1, zr[nxt]);  // the wave's own LDS ring; its LDS operations stay in order
+            write_z((i + 1) & 3, zr[nxt]);  // the wave's own LDS ring
+            // other lanes read these rows below: keep the compiler from moving
+            // the reads above the writes (the wave's LDS operations execute in order)
+            wave_lds_fence();
             fetch_z(s + 1 + P, zr[nxt]);
 
             // sequence masks (branch-free): taps k <= back (dwc) and k < ahead (dx)
@@ -711,11 +722,12 @@ __global__ __launch_bounds__(kBlock, (BwdLds<W, RC>::kBlocksPerCu)) void lr_bwd_
             // dx = rho*g + sum_k w[n+k] * g[n+k]; w of tokens n+k on the matrix cores
             float acc[8];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) acc[c] = p.rho * ((c & 1) ? bf16_hi(gc[c >> 1]) : bf16_lo(gc[c >> 1]));
+            for (int c = 0; c < 8; ++c)
+                acc[c] = __uint_as_float(((c & 1) ? (gc[c >> 1] & 0xffff0000u) : (gc[c >> 1] << 16)) & p.rmask);
 #pragma unroll
             for (int k = 0; k < W; ++k) {
                 const int rr = tok + k;
-                const unsigned char *zrow = zslot(s + (rr >> 4)) + (rr & 15) * L::PZ;
+                const unsigned char *zrow = zrows(i & 3) + rr * L::PZ;
                 bf16x8 zb[RC];
 #pragma unroll
                 for (int c = 0; c < RC; ++c) {
@@ -810,7 +822,7 @@ __global__ __launch_bounds__(kBlock, (BwdLds<W, RC>::kBlocksPerCu)) void lr_bwd_
 #pragma unroll
                     for (int hh = 0; hh < 2; ++hh) {
                         const int row = trow + 4 * hh;
-                        h[hh] = lds_read_tr(zslot(s_pair + (row >> 4)) + (row & 15) * L::PZ + 2 * (16 * rt + tcol));
+                        h[hh] = lds_read_tr(zrows((i - 1) & 3) + row * L::PZ + 2 * (16 * rt + tcol));
                     }
                     zb[rt] = __builtin_bit_cast(bf16x8, make_uint4(h[0].x, h[0].y, h[1].x, h[1].y));
                 }
@@ -909,6 +921,7 @@ LrParams make_params(const LrProblem &pr) {
     p.seq = SeqMap{pr.cu, pr.n_seqs, pr.T};
     p.N = pr.N; p.D = pr.D; p.R = pr.R;
     p.rho = pr.residual ? 1.f : 0.f;
+    p.rmask = pr.residual ? 0xffffffffu : 0u;
     p.nchunks = pr.D / E::kVec;
     return p;
 }
@@ -971,11 +984,40 @@ hipError_t mfma_fwd(const LrProblem &pr, hipStream_t st) {
 #ifndef DSC_LR_BWD_RING
 #define DSC_LR_BWD_RING 4
 #endif
-#ifndef DSC_LR_BWD_BLOCKS
-#define DSC_LR_BWD_BLOCKS 512
-#endif
-constexpr int kBwdRing = DSC_LR_BWD_RING;                   // backward prefetch ring depth (steps)
-constexpr int64_t kTargetBwdBlocks = DSC_LR_BWD_BLOCKS;     // backward grid size target
+constexpr int kBwdRing = DSC_LR_BWD_RING;  // backward prefetch ring depth (steps)
+constexpr int64_t kBlockFixedTokens = 256;  // a block's set-up and dU flush, in tokens of walk (measured)
+
+// Compute units of the current device (all devices of a process are taken
+// to be alike).
+int device_cus() {
+    static std::atomic<int> cus{0};
+    int n = cus.load(std::memory_order_relaxed);
+    if (n == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cus.store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Token range per backward block: whole rings of steps, at most `cap`.  The
+// grid runs in rounds of `slots` resident blocks, so the range that
+// minimises rounds x (range + fixed cost) is taken (the longest on ties).
+int64_t bwd_tokens_per_block(int64_t N, int64_t ngroups, int64_t slots, int64_t cap, int64_t unit) {
+    int64_t best = unit, best_cost = -1;
+    for (int64_t tpb = (cap / unit) * unit; tpb >= unit; tpb -= unit) {
+        const int64_t chunks = (N + tpb - 1) / tpb;
+        const int64_t rounds = (chunks * ngroups + slots - 1) / slots;
+        const int64_t cost = rounds * (tpb + kBlockFixedTokens);
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best = tpb;
+        }
+    }
+    return best;
+}
 
 template <int W, int RC>
 hipError_t mfma_bwd(const LrProblem &pr, hipStream_t st) {
@@ -990,12 +1032,9 @@ hipError_t mfma_bwd(const LrProblem &pr, hipStream_t st) {
     hipLaunchKernelGGL(fill_zero_f32, dim3((unsigned)nblocks(nz)), dim3(kBlock), 0, st, p.dzacc, nz);
     const int64_t nslices = (p.D + 31) / 32;
     const int64_t ngroups = (nslices + 3) / 4;
-    int64_t tchunks = kTargetBwdBlocks / ngroups;
-    if (tchunks < 1) tchunks = 1;
-    int64_t tpb = (p.N + tchunks - 1) / tchunks;
-    tpb = ((tpb + 16 * kBwdRing - 1) / (16 * kBwdRing)) * (16 * kBwdRing);  // whole rings of steps
-    if (tpb > cap) tpb = cap;
-    tchunks = (p.N + tpb - 1) / tpb;
+    const int64_t slots = (int64_t)device_cus() * BwdLds<W, RC>::kBlocksPerCu;
+    const int64_t tpb = bwd_tokens_per_block(p.N, ngroups, slots, cap, 16 * kBwdRing);
+    const int64_t tchunks = (p.N + tpb - 1) / tpb;
     if (p.R % 8 == 0)
         hipLaunchKernelGGL((lr_bwd_mfma<W, RC, kBwdRing, true>), dim3((unsigned)(tchunks * ngroups)), dim3(kBlock),
                            0, st, p, nslices, tpb);
