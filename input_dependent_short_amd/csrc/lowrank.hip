@@ -504,11 +504,12 @@ __device__ __forceinline__ bf16x8 bf16x8_from_u32(const uint32_t (&v)[4]) {
 //   * dwc_k is staged in LDS and re-read transposed (lane = channel,
 //     registers = tokens) as the A operand of dU_k^T += dwc_k^T * Z.
 // x, dy and z stream through one buffer resource each (offset = lane place +
-// step offset), into register rings refilled P steps ahead without copies.  dz is summed over
-// the block's 4 waves in LDS and added to an fp32 accumulator with one atomic
-// per (token, rank); dU stays in registers over the whole token range and is
-// added to the fp32 output with coalesced atomics at the end.  Both
-// accumulators are zeroed by the launcher first.
+// step offset), into register rings refilled P steps ahead without copies.
+// dz is summed over the block's 4 waves in LDS and added to an fp32
+// accumulator with one atomic per (token, rank), converted to bf16 by a
+// launch after the kernel.  dU stays in registers over the whole token range
+// and is added to the fp32 output with coalesced atomics at the end.  One
+// launch before the kernel zeroes dU and the accumulator.
 template <int W, int RC>
 struct BwdLds {
     static constexpr int RP = 32 * RC;           // padded rank
@@ -905,6 +906,25 @@ __global__ void fill_zero_f32(float *p, int64_t n) {
     if (i < n) p[i] = 0.f;
 }
 
+// Zeroes two 16-byte aligned arrays of 32-bit words in one launch; thread
+// i clears words 4i .. 4i+3 of the concatenation (vector store when whole).
+__device__ __forceinline__ void zero_words(uint32_t *p, int64_t n, int64_t unit) {
+    const int64_t i = 4 * unit;
+    if (i + 3 < n) {
+        *reinterpret_cast<uint4 *>(p + i) = make_uint4(0u, 0u, 0u, 0u);
+    } else {
+        for (int64_t j = i; j < n; ++j) p[j] = 0u;
+    }
+}
+
+__global__ void clear2(uint32_t *a, int64_t na, uint32_t *b, int64_t nb) {
+    int64_t u = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const int64_t ua = (na + 3) / 4, ub = (nb + 3) / 4;
+    if (u < ua) return zero_words(a, na, u);
+    u -= ua;
+    if (u < ub) zero_words(b, nb, u);
+}
+
 __global__ void cast_f32_bf16(const float *src, uint16_t *dst, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     if (i < n) dst[i] = to_bf16(src[i]);
@@ -1028,13 +1048,15 @@ hipError_t mfma_bwd(const LrProblem &pr, hipStream_t st) {
     if (cap < 16 * kBwdRing) return generic_bwd<BF16, W>(pr, st);
     const int64_t nU = (int64_t)p.R * p.D * W;
     const int64_t nz = p.N * p.R;
-    hipLaunchKernelGGL(fill_zero_f32, dim3((unsigned)nblocks(nU)), dim3(kBlock), 0, st, p.dU, nU);
-    hipLaunchKernelGGL(fill_zero_f32, dim3((unsigned)nblocks(nz)), dim3(kBlock), 0, st, p.dzacc, nz);
     const int64_t nslices = (p.D + 31) / 32;
     const int64_t ngroups = (nslices + 3) / 4;
     const int64_t slots = (int64_t)device_cus() * BwdLds<W, RC>::kBlocksPerCu;
     const int64_t tpb = bwd_tokens_per_block(p.N, ngroups, slots, cap, 16 * kBwdRing);
     const int64_t tchunks = (p.N + tpb - 1) / tpb;
+    // one launch clears dU and the dz accumulator
+    const int64_t units = (nU + 3) / 4 + (nz + 3) / 4;
+    hipLaunchKernelGGL(clear2, dim3((unsigned)nblocks(units)), dim3(kBlock), 0, st,
+                       reinterpret_cast<uint32_t *>(p.dU), nU, reinterpret_cast<uint32_t *>(p.dzacc), nz);
     if (p.R % 8 == 0)
         hipLaunchKernelGGL((lr_bwd_mfma<W, RC, kBwdRing, true>), dim3((unsigned)(tchunks * ngroups)), dim3(kBlock),
                            0, st, p, nslices, tpb);
