@@ -45,6 +45,9 @@ hipError_t headwise_bwd(const HwProblem &p, hipStream_t s);
 
 size_t lowrank_bwd_workspace(Dtype dt, int64_t N, int64_t D, int32_t W, int32_t R);
 hipError_t lowrank_fwd(const LrProblem &p, hipStream_t s);
+// Wide bf16 forward (R <= 64); sets *used to false when the shape is left to
+// the other kernels, which then run instead.
+hipError_t lowrank_fwd_wide(const LrProblem &p, hipStream_t s, bool *used);
 hipError_t lowrank_bwd(const LrProblem &p, hipStream_t s);
 
 }  // namespace dsc

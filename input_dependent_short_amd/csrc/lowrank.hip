@@ -23,28 +23,10 @@
 //
 // The generic kernels (any dtype; fp32 always uses them) evaluate the same
 // sums on the vector ALU; dz and dU are reduced with fp32 atomics.
-#include <atomic>
-
-#include "dsc_kernels.h"
+#include "lowrank_common.h"
 
 namespace dsc {
 namespace {
-
-struct LrParams {
-    const void *x, *z, *U, *dy;
-    void *y, *dx, *dz;
-    float *dU, *dzacc;
-    SeqMap seq;
-    int64_t N, D;
-    int32_t R;
-    float rho;
-    uint32_t rmask;  // all ones with the residual term, else zero
-    int64_t nchunks;
-};
-
-constexpr int kBlock = 256;
-constexpr int kMaxTokPerWave = 4096;                          // token walk length cap
-constexpr int kSeqWords = (kMaxTokPerWave + 128) / 32 + 2;    // sequence-start bits per wave
 
 // ---------------------------------------------------------------- generic
 
@@ -161,62 +143,6 @@ __global__ __launch_bounds__(kBlock) void lr_bwd_generic(LrParams p) {
 }
 
 // ------------------------------------------------------------- bf16 MFMA
-
-// W consecutive bf16 values of U (the taps of one rank and channel) as raw
-// bits, with the widest accesses that the alignment allows: the offset
-// (r*D + ch)*W*2 is a multiple of the largest power of two dividing 2W
-// because D % 8 == 0.
-template <int W>
-__device__ __forceinline__ void load_taps(const uint16_t *p, uint16_t (&v)[W]) {
-    constexpr int PER = pow2_align(2 * W) / 2;  // elements per access
-#pragma unroll
-    for (int i = 0; i < W; i += PER) {
-        if constexpr (PER == 8) {
-            const uint4 q = *reinterpret_cast<const uint4 *>(p + i);
-            const uint32_t h[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                v[i + 2 * j] = (uint16_t)(h[j] & 0xffffu);
-                v[i + 2 * j + 1] = (uint16_t)(h[j] >> 16);
-            }
-        } else if constexpr (PER == 4) {
-            const uint2 q = *reinterpret_cast<const uint2 *>(p + i);
-            v[i] = (uint16_t)(q.x & 0xffffu); v[i + 1] = (uint16_t)(q.x >> 16);
-            v[i + 2] = (uint16_t)(q.y & 0xffffu); v[i + 3] = (uint16_t)(q.y >> 16);
-        } else if constexpr (PER == 2) {
-            const uint32_t q = *reinterpret_cast<const uint32_t *>(p + i);
-            v[i] = (uint16_t)(q & 0xffffu); v[i + 1] = (uint16_t)(q >> 16);
-        } else {
-            v[i] = p[i];
-        }
-    }
-}
-
-// A operand of w = z U for every tap k, kept in registers: rows are the
-// channels of a 32-channel slice (tile t, row i <-> channel
-// d0 + 8(i>>2) + 4t + (i&3)), K is rank 32c + 8(lane>>4) + e.  Zero outside R
-// and D.
-template <int W, int RC>
-__device__ __forceinline__ void load_u_rows(const uint16_t *U, int R, int64_t D, int64_t d0, int lane,
-                                            bf16x8 (&ua)[W][2][RC]) {
-    const int i16 = lane & 15, q = lane >> 4;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int64_t ch = d0 + 8 * (i16 >> 2) + 4 * t + (i16 & 3);
-#pragma unroll
-        for (int c = 0; c < RC; ++c)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int r = 32 * c + 8 * q + e;
-                uint16_t v[W];
-#pragma unroll
-                for (int k = 0; k < W; ++k) v[k] = 0;
-                if (r < R && ch < D) load_taps<W>(U + ((int64_t)r * D + ch) * W, v);
-#pragma unroll
-                for (int k = 0; k < W; ++k) ua[k][t][c][e] = __builtin_bit_cast(__bf16, v[k]);
-            }
-    }
-}
 
 // A operand of dz^T = U_k dwc_k for every tap k: rows are ranks
 // 16rt + (lane&15), K is channel d0 + 8(lane>>4) + e.  A lane's 8 channels
@@ -930,22 +856,6 @@ __global__ void cast_f32_bf16(const float *src, uint16_t *dst, int64_t n) {
     if (i < n) dst[i] = to_bf16(src[i]);
 }
 
-int64_t nblocks(int64_t n) { return (n + kBlock - 1) / kBlock; }
-
-template <class E>
-LrParams make_params(const LrProblem &pr) {
-    LrParams p;
-    p.x = pr.x; p.z = pr.z; p.U = pr.U; p.dy = pr.dy;
-    p.y = pr.y; p.dx = pr.dx; p.dz = pr.dz;
-    p.dU = pr.dU; p.dzacc = pr.dz_acc;
-    p.seq = SeqMap{pr.cu, pr.n_seqs, pr.T};
-    p.N = pr.N; p.D = pr.D; p.R = pr.R;
-    p.rho = pr.residual ? 1.f : 0.f;
-    p.rmask = pr.residual ? 0xffffffffu : 0u;
-    p.nchunks = pr.D / E::kVec;
-    return p;
-}
-
 template <class E, int W>
 hipError_t generic_fwd(const LrProblem &pr, hipStream_t st) {
     LrParams p = make_params<E>(pr);
@@ -969,12 +879,17 @@ hipError_t generic_bwd(const LrProblem &pr, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Forward tuning per rank chunk count (measured on MI355X): the prefetch ring
-// depth in 16-token steps and the number of waves the grid aims for.
+#ifndef DSC_LR_FWD_WAVES
+#define DSC_LR_FWD_WAVES 3072
+#endif
+// Forward (R > 32) tuning, measured on MI355X: the prefetch ring depth in
+// 16-token steps and the number of waves the grid aims for.  These kernels
+// stay bandwidth-bound with a partly filled last round, so the grid is not
+// cut to one round of resident waves.
 template <int RC>
 struct FwdTune {
     static constexpr int kPF = RC == 1 ? 8 : 6;
-    static constexpr int64_t kWaves = RC == 1 ? 2048 : 3072;
+    static constexpr int64_t kWaves = DSC_LR_FWD_WAVES;
 };
 
 template <int W, int RC>
@@ -982,18 +897,16 @@ hipError_t mfma_fwd(const LrProblem &pr, hipStream_t st) {
     constexpr int PF = FwdTune<RC>::kPF;
     LrParams p = make_params<BF16>(pr);
     const int64_t nslices = (p.D + 31) / 32;
+    const int64_t cap = walk_cap(p.D, 16 * PF, 16 * (2 * PF + 2));
+    if (cap < 16 * PF) return generic_fwd<BF16, W>(pr, st);
     int64_t tpw = (p.N * nslices + FwdTune<RC>::kWaves - 1) / FwdTune<RC>::kWaves;
     tpw = ((tpw + 16 * PF - 1) / (16 * PF)) * (16 * PF);  // whole groups of PF steps
-    // walk length cap: the LDS bitmap, and stream offsets below 2^30
-    const int64_t span = kStreamSpan / (2 * p.D) - 16 * (2 * PF + 2);
-    const int64_t cap = ((span < kMaxTokPerWave ? span : kMaxTokPerWave) / (16 * PF)) * (16 * PF);
-    if (cap < 16 * PF) return generic_fwd<BF16, W>(pr, st);
     if (tpw > cap) tpw = cap;
-    const int64_t nchunks_t = (p.N + tpw - 1) / tpw;
-    const int64_t waves = nchunks_t * nslices;
+    const bool rvec = p.R % 8 == 0;
+    const int64_t waves = ((p.N + tpw - 1) / tpw) * nslices;
     const int64_t b = (waves + 3) / 4;
     if (b) {
-        if (p.R % 8 == 0)
+        if (rvec)
             hipLaunchKernelGGL((lr_fwd_mfma<W, RC, PF, true>), dim3((unsigned)b), dim3(kBlock), 0, st, p, nslices, tpw);
         else
             hipLaunchKernelGGL((lr_fwd_mfma<W, RC, PF, false>), dim3((unsigned)b), dim3(kBlock), 0, st, p, nslices, tpw);
@@ -1007,51 +920,19 @@ hipError_t mfma_fwd(const LrProblem &pr, hipStream_t st) {
 constexpr int kBwdRing = DSC_LR_BWD_RING;  // backward prefetch ring depth (steps)
 constexpr int64_t kBlockFixedTokens = 256;  // a block's set-up and dU flush, in tokens of walk (measured)
 
-// Compute units of the current device (all devices of a process are taken
-// to be alike).
-int device_cus() {
-    static std::atomic<int> cus{0};
-    int n = cus.load(std::memory_order_relaxed);
-    if (n == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cus.store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
-// Token range per backward block: whole rings of steps, at most `cap`.  The
-// grid runs in rounds of `slots` resident blocks, so the range that
-// minimises rounds x (range + fixed cost) is taken (the longest on ties).
-int64_t bwd_tokens_per_block(int64_t N, int64_t ngroups, int64_t slots, int64_t cap, int64_t unit) {
-    int64_t best = unit, best_cost = -1;
-    for (int64_t tpb = (cap / unit) * unit; tpb >= unit; tpb -= unit) {
-        const int64_t chunks = (N + tpb - 1) / tpb;
-        const int64_t rounds = (chunks * ngroups + slots - 1) / slots;
-        const int64_t cost = rounds * (tpb + kBlockFixedTokens);
-        if (best_cost < 0 || cost < best_cost) {
-            best_cost = cost;
-            best = tpb;
-        }
-    }
-    return best;
-}
-
 template <int W, int RC>
 hipError_t mfma_bwd(const LrProblem &pr, hipStream_t st) {
     LrParams p = make_params<BF16>(pr);
-    // walk length cap: the LDS bitmap, and stream offsets below 2^30
-    const int64_t span = kStreamSpan / (2 * p.D) - 16 * (2 * kBwdRing + 2);
-    const int64_t cap = ((span < kMaxTokPerWave ? span : kMaxTokPerWave) / (16 * kBwdRing)) * (16 * kBwdRing);
+    const int64_t cap = walk_cap(p.D, 16 * kBwdRing, 16 * (2 * kBwdRing + 2));
     if (cap < 16 * kBwdRing) return generic_bwd<BF16, W>(pr, st);
     const int64_t nU = (int64_t)p.R * p.D * W;
     const int64_t nz = p.N * p.R;
     const int64_t nslices = (p.D + 31) / 32;
     const int64_t ngroups = (nslices + 3) / 4;
-    const int64_t slots = (int64_t)device_cus() * BwdLds<W, RC>::kBlocksPerCu;
-    const int64_t tpb = bwd_tokens_per_block(p.N, ngroups, slots, cap, 16 * kBwdRing);
+    static const int bpc_vec = blocks_per_cu(reinterpret_cast<const void *>(&lr_bwd_mfma<W, RC, kBwdRing, true>));
+    static const int bpc_gather = blocks_per_cu(reinterpret_cast<const void *>(&lr_bwd_mfma<W, RC, kBwdRing, false>));
+    const int64_t slots = (int64_t)device_cus() * (p.R % 8 == 0 ? bpc_vec : bpc_gather);
+    const int64_t tpb = walk_length(p.N, ngroups, slots, cap, 16 * kBwdRing, kBlockFixedTokens);
     const int64_t tchunks = (p.N + tpb - 1) / tpb;
     // one launch clears dU and the dz accumulator
     const int64_t units = (nU + 3) / 4 + (nz + 3) / 4;
@@ -1115,6 +996,9 @@ size_t lowrank_bwd_workspace(Dtype dt, int64_t N, int64_t D, int32_t W, int32_t 
 
 hipError_t lowrank_fwd(const LrProblem &p, hipStream_t s) {
     if (p.dtype == Dtype::BF16) {
+        bool used = false;
+        const hipError_t e = lowrank_fwd_wide(p, s, &used);  // R <= 64 (lowrank_fwd.hip)
+        if (used) return e;
         DSC_W_SWITCH(p.W, mfma_fwd_rc<Wc>(p, s));
     }
     DSC_W_SWITCH(p.W, (generic_fwd<F32, Wc>(p, s)));
