@@ -436,7 +436,13 @@ __device__ __forceinline__ bf16x8 bf16x8_from_u32(const uint32_t (&v)[4]) {
 // launch after the kernel.  dU stays in registers over the whole token range
 // and is added to the fp32 output with coalesced atomics at the end.  One
 // launch before the kernel zeroes dU and the accumulator.
-template <int W, int RC>
+// H = 2 (R <= 32, W <= 4) doubles the block to 8 waves: two token halves
+// over the same 4 channel slices, 2 waves per SIMD as with two 4-wave
+// blocks, whose dU tiles are summed in LDS before the flush (half the dU
+// atomics).
+constexpr bool bwd_two_per_simd(int W, int RC) { return RC == 1 && W <= 4; }
+
+template <int W, int RC, int H>
 struct BwdLds {
     static constexpr int RP = 32 * RC;           // padded rank
     static constexpr int PW = 72;                // bytes per token row of dwc^T (32 ch + pad, 8-aligned)
@@ -446,17 +452,18 @@ struct BwdLds {
     // z ring: 4 steps of 16 rows, then a copy of the first step's rows, so
     // that rows slot*16 + j (j < 32) are contiguous for every slot
     static constexpr int kZ = 80 * PZ;
-    // Two blocks per CU (R <= 32, W <= 4: registers and LDS fit) keep one
-    // buffer of dz partials per wave and pay a second barrier per pair;
-    // otherwise the buffer is doubled and the pairs alternate.
-    static constexpr int kBlocksPerCu = (RC == 1 && W <= 4) ? 2 : 1;
-    static constexpr int kDzBufs = kBlocksPerCu == 2 ? 1 : 2;
+    // 8 waves per CU (R <= 32, W <= 4: registers and LDS fit) keep one buffer
+    // of dz partials per wave and pay a second barrier per pair; otherwise
+    // the buffer is doubled and the pairs alternate.
+    static constexpr bool kTwoPerSimd = bwd_two_per_simd(W, RC);
+    static constexpr int kBlocksPerCu = kTwoPerSimd ? 2 / H : 1;
+    static constexpr int kDzBufs = kTwoPerSimd ? 1 : 2;
     static constexpr int kDz = kDzBufs * 32 * PD;  // the wave's dz partials of kDzBufs pairs
     static constexpr int kLoop = kDwc + kZ + kDz;
     static constexpr int kDuStage = RP * 32 * W * 4;   // dU tile staged for coalesced atomics
     static constexpr int kWave = (((kLoop > kDuStage ? kLoop : kDuStage) + 15) / 16) * 16;
-    static constexpr int kBlock = 4 * kWave;
-    static_assert(kBlocksPerCu == 1 || 2 * (kBlock + 4 * 4 * 140) <= 160 * 1024, "two blocks must fit the LDS");
+    static constexpr int kBlock = 4 * H * kWave;
+    static_assert(kBlocksPerCu * (kBlock + 4 * H * 4 * kSeqWords) <= 160 * 1024, "the blocks of a CU must fit the LDS");
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -472,26 +479,31 @@ __device__ __forceinline__ uint2 lds_read_tr(const unsigned char *addr) {
     return __builtin_bit_cast(uint2, v);
 }
 
-template <int W, int RC, int P, bool RVEC>
-__global__ __launch_bounds__(kBlock, (BwdLds<W, RC>::kBlocksPerCu)) void lr_bwd_mfma(LrParams p, int64_t nslices,
-                                                                                   int64_t tok_per_block) {
-    using L = BwdLds<W, RC>;
+template <int W, int RC, int P, bool RVEC, int H>
+__global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void lr_bwd_mfma(LrParams p, int64_t nslices,
+                                                                                         int64_t tok_per_half) {
+    using L = BwdLds<W, RC, H>;
     constexpr int RT = 2 * RC;  // 16-row rank tiles
     static_assert(P % 4 == 0, "the register rings cover whole turns of the 4-slot z ring");
     __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBlock];
-    __shared__ uint32_t seq_words[kBlock / kWave][kSeqWords];
+    __shared__ uint32_t seq_words[4 * H][kSeqWords];
 
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int slice = wid & 3;  // channel slice of the block's group
+    const int half = wid >> 2;  // token half (H == 2)
     const int64_t ngroups = (nslices + 3) / 4;
     const int64_t tchunk = blockIdx.x / ngroups;
     const int64_t group = blockIdx.x - tchunk * ngroups;
-    const int64_t d0 = (group * 4 + wid) * 32;
-    const int64_t nbeg = tchunk * tok_per_block;
-    const int64_t nend = min(nbeg + tok_per_block, p.N);
-    // steps of this block: whole rings of P steps (steps past nend read zeros
+    const int64_t d0 = (group * 4 + slice) * 32;
+    const int64_t bbeg = tchunk * H * tok_per_half;  // the block's first token
+    const int64_t nbeg = bbeg + half * tok_per_half;
+    const int64_t nend = min(nbeg + tok_per_half, p.N);  // may be <= nbeg in the last block's second half
+    // steps of both halves: whole rings of P steps over the first half's
+    // range, so all waves meet the same barriers (steps past nend read zeros
     // past N, store nothing past nend, and add nothing to dz or dU)
-    const int64_t nsteps = ((nend - nbeg + 16 * P - 1) / (16 * P)) * P;
+    const int64_t len0 = min(tok_per_half, p.N - bbeg);
+    const int64_t nsteps = ((len0 + 16 * P - 1) / (16 * P)) * P;
 
     const int tok = lane & 15;
     const int q = lane >> 4;
@@ -596,7 +608,7 @@ __global__ __launch_bounds__(kBlock, (BwdLds<W, RC>::kBlocksPerCu)) void lr_bwd_
     xr[P - 1] = zero4;  // step -1: only its last W-1 tokens are read
     {
         const int64_t n = nbeg - 16 + tok;
-        if (n >= 0 && tok >= 16 - (W - 1) && chan_ok)
+        if (n >= 0 && n < N && tok >= 16 - (W - 1) && chan_ok)
             xr[P - 1] = *reinterpret_cast<const uint4 *>(xg + n * D + cbase);
     }
 #pragma unroll
@@ -611,8 +623,11 @@ __global__ __launch_bounds__(kBlock, (BwdLds<W, RC>::kBlocksPerCu)) void lr_bwd_
     for (int j = 1; j < P; ++j) fetch_z(j, zr[j]);
 
     // dz atomics: rank of this lane and its element offset inside a pair
-    const int dz_rank = (int)threadIdx.x % L::RP;
-    const uint32_t dz_block_off = (uint32_t)(((int)threadIdx.x / L::RP) * R + dz_rank);
+    // (each half reduces its own 4 waves with its own 256 threads)
+    const int hthread = (int)threadIdx.x & (kBlock - 1);
+    const int dz_rank = hthread % L::RP;
+    const uint32_t dz_block_off = (uint32_t)((hthread / L::RP) * R + dz_rank);
+    const unsigned char *dz_half = lds + 4 * half * L::kWave + L::kDwc + L::kZ;  // this half's first wave
 
     int buf = 0;
     for (int64_t s0 = 0; s0 < nsteps; s0 += P) {
@@ -774,13 +789,13 @@ __global__ __launch_bounds__(kBlock, (BwdLds<W, RC>::kBlocksPerCu)) void lr_bwd_
                 const int64_t npair0 = nbeg + 16 * s_pair;
                 const __amdgpu_buffer_rsrc_t rdz = make_stream(p.dzacc + npair0 * R, (nend - npair0) * R * 4);
                 {
-                    // block-wide: thread e sums (token e / RP, rank e % RP) over the four waves
+                    // per half: thread e sums (token e / RP, rank e % RP) over the half's four waves
                     constexpr int kIt = 32 * L::RP / kBlock;
                     float v[kIt];
 #pragma unroll
                     for (int it = 0; it < kIt; ++it) {
-                        const int e = threadIdx.x + it * kBlock, tl = e / L::RP, r = e % L::RP;
-                        const unsigned char *src = lds + L::kDwc + L::kZ + (buf * 32 + tl) * L::PD + 4 * r;
+                        const int e = hthread + it * kBlock, tl = e / L::RP, r = e % L::RP;
+                        const unsigned char *src = dz_half + (buf * 32 + tl) * L::PD + 4 * r;
                         float a = 0.f;
 #pragma unroll
                         for (int w2 = 0; w2 < 4; ++w2) a += *reinterpret_cast<const float *>(src + w2 * L::kWave);
@@ -788,7 +803,7 @@ __global__ __launch_bounds__(kBlock, (BwdLds<W, RC>::kBlocksPerCu)) void lr_bwd_
                     }
 #pragma unroll
                     for (int it = 0; it < kIt; ++it) {
-                        const int tl = (int)threadIdx.x / L::RP + it * (kBlock / L::RP);
+                        const int tl = hthread / L::RP + it * (kBlock / L::RP);
                         if (dz_rank < R && npair0 + tl < nend)
                             __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
                                 v[it], rdz, 4 * (dz_block_off + (uint32_t)(it * (kBlock / L::RP) * R)), 0, 0);
@@ -819,10 +834,16 @@ __global__ __launch_bounds__(kBlock, (BwdLds<W, RC>::kBlocksPerCu)) void lr_bwd_
                 for (int j = 0; j < 4; ++j) dus[r * (32 * W) + (16 * ct + 4 * q + j) * W + k] = du[k][ct][rt][j];
             }
     __syncthreads();
-    const int64_t nvalid = (D - d0 < 32 ? D - d0 : 32) * W;  // channels of this slice inside D
-    for (int r = 0; r < R; ++r)
-        for (int idx = lane; idx < nvalid; idx += kWave)
-            atomicAdd(p.dU + (int64_t)r * DW + d0 * W + idx, dus[r * (32 * W) + idx]);
+    if (half == 0) {  // wave-uniform; with H == 2 the second half's tile of the same slice is added here
+        const float *dus2 = reinterpret_cast<const float *>(my + 4 * L::kWave);
+        const int64_t nvalid = (D - d0 < 32 ? D - d0 : 32) * W;  // channels of this slice inside D
+        for (int r = 0; r < R; ++r)
+            for (int idx = lane; idx < nvalid; idx += kWave) {
+                float v = dus[r * (32 * W) + idx];
+                if constexpr (H == 2) v += dus2[r * (32 * W) + idx];
+                atomicAdd(p.dU + (int64_t)r * DW + d0 * W + idx, v);
+            }
+    }
 }
 
 // ------------------------------------------------------------ small kernels
@@ -929,21 +950,25 @@ hipError_t mfma_bwd(const LrProblem &pr, hipStream_t st) {
     const int64_t nz = p.N * p.R;
     const int64_t nslices = (p.D + 31) / 32;
     const int64_t ngroups = (nslices + 3) / 4;
-    static const int bpc_vec = blocks_per_cu(reinterpret_cast<const void *>(&lr_bwd_mfma<W, RC, kBwdRing, true>));
-    static const int bpc_gather = blocks_per_cu(reinterpret_cast<const void *>(&lr_bwd_mfma<W, RC, kBwdRing, false>));
+    constexpr int H = bwd_two_per_simd(W, RC) ? 2 : 1;  // token halves per block
+    static const int bpc_vec = blocks_per_cu(reinterpret_cast<const void *>(&lr_bwd_mfma<W, RC, kBwdRing, true, H>),
+                                             kBlock * H);
+    static const int bpc_gather = blocks_per_cu(reinterpret_cast<const void *>(&lr_bwd_mfma<W, RC, kBwdRing, false, H>),
+                                                kBlock * H);
     const int64_t slots = (int64_t)device_cus() * (p.R % 8 == 0 ? bpc_vec : bpc_gather);
-    const int64_t tpb = walk_length(p.N, ngroups, slots, cap, 16 * kBwdRing, kBlockFixedTokens);
-    const int64_t tchunks = (p.N + tpb - 1) / tpb;
+    const int64_t block_len = walk_length(p.N, ngroups, slots, H * cap, H * 16 * kBwdRing, H * kBlockFixedTokens);
+    const int64_t tph = block_len / H;  // tokens per half
+    const int64_t tchunks = (p.N + block_len - 1) / block_len;
     // one launch clears dU and the dz accumulator
     const int64_t units = (nU + 3) / 4 + (nz + 3) / 4;
     hipLaunchKernelGGL(clear2, dim3((unsigned)nblocks(units)), dim3(kBlock), 0, st,
                        reinterpret_cast<uint32_t *>(p.dU), nU, reinterpret_cast<uint32_t *>(p.dzacc), nz);
     if (p.R % 8 == 0)
-        hipLaunchKernelGGL((lr_bwd_mfma<W, RC, kBwdRing, true>), dim3((unsigned)(tchunks * ngroups)), dim3(kBlock),
-                           0, st, p, nslices, tpb);
+        hipLaunchKernelGGL((lr_bwd_mfma<W, RC, kBwdRing, true, H>), dim3((unsigned)(tchunks * ngroups)),
+                           dim3(kBlock * H), 0, st, p, nslices, tph);
     else
-        hipLaunchKernelGGL((lr_bwd_mfma<W, RC, kBwdRing, false>), dim3((unsigned)(tchunks * ngroups)), dim3(kBlock),
-                           0, st, p, nslices, tpb);
+        hipLaunchKernelGGL((lr_bwd_mfma<W, RC, kBwdRing, false, H>), dim3((unsigned)(tchunks * ngroups)),
+                           dim3(kBlock * H), 0, st, p, nslices, tph);
     hipLaunchKernelGGL(cast_f32_bf16, dim3((unsigned)nblocks(nz)), dim3(kBlock), 0, st, p.dzacc,
                        static_cast<uint16_t *>(p.dz), nz);
     return hipGetLastError();

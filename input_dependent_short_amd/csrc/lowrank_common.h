@@ -115,11 +115,11 @@ int device_cus() {
     return n;
 }
 
-// Workgroups of `kernel` (256 threads, static LDS only) resident per compute
-// unit, from the runtime's occupancy calculator.
-int blocks_per_cu(const void *kernel) {
+// Workgroups of `kernel` (`threads` per block, static LDS only) resident per
+// compute unit, from the runtime's occupancy calculator.
+int blocks_per_cu(const void *kernel, int threads = kBlock) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kBlock, 0) != hipSuccess || n < 1) n = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1) n = 1;
     return n;
 }
 
