@@ -57,6 +57,10 @@ LR_CASES = [
     ("bf16", 1, 520, 6144, 4, 64, False, (1, 300)),
     ("bf16", 2, 97, 200, 8, 20, True, (1, 60)),
     ("bf16", 1, 64, 96, 2, 48, False, None),
+    # wide forward with R in 33..64 gathered (R % 8 != 0), several token walks per channel pair
+    ("bf16", 1, 4100, 64, 3, 36, True, (1, 700)),
+    # backward blocks of two token halves, several blocks, partial last half, R % 8 != 0
+    ("bf16", 3, 1000, 128, 4, 20, True, (100, 900)),
 ]
 
 
