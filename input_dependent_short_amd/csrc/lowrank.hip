@@ -12,7 +12,12 @@
 //   dz[n,r]      = sum_{d,k} U[r,d*W+k] dwc[n,d,k]
 //   dU[r,d*W+k]  = sum_n z[n,r] dwc[n,d,k]
 //
-// bf16 forward: the R-wide contraction runs on the matrix cores
+// This file holds the backward kernels, the 32-channel forward kernel and the
+// dispatch.  The bf16 forward for R <= 64 runs the wide kernel of
+// lowrank_fwd.hip (64 channels per wave, whole-line loads and stores); the
+// 32-channel forward below serves R > 64 and very wide D.
+//
+// 32-channel bf16 forward: the R-wide contraction runs on the matrix cores
 // (v_mfma_f32_16x16x32_bf16), one product per tap, C_k = U_k^T (channels x R)
 // times Z^T (R x 16 tokens).  Every tap lands in the same accumulator layout
 // (lane = token, four channel rows per tile), so the convolution is lane-local:
