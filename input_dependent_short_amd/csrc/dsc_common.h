@@ -3,6 +3,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <stdint.h>
 
 namespace dsc {
@@ -351,6 +353,31 @@ __device__ __forceinline__ int64_t xcd_block_id(int64_t b, int64_t nblocks) {
     int64_t x = b % kXcd;
     int64_t start = x * q + (x < r ? x : r);
     return start + b / kXcd;
+}
+
+// ----------------------------------------------------------- launch sizing (host)
+
+// Compute units of the current device (all devices of a process are taken
+// to be alike).
+inline int device_cus() {
+    static std::atomic<int> cus{0};
+    int n = cus.load(std::memory_order_relaxed);
+    if (n == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cus.store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Workgroups of `kernel` (`threads` per block, static LDS only) resident per
+// compute unit, from the runtime's occupancy calculator.
+inline int blocks_per_cu(const void *kernel, int threads) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1) n = 1;
+    return n;
 }
 
 }  // namespace dsc

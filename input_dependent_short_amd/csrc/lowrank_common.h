@@ -100,29 +100,6 @@ LrParams make_params(const LrProblem &pr) {
 
 int64_t nblocks(int64_t n) { return (n + kBlock - 1) / kBlock; }
 
-// Compute units of the current device (all devices of a process are taken
-// to be alike).
-int device_cus() {
-    static std::atomic<int> cus{0};
-    int n = cus.load(std::memory_order_relaxed);
-    if (n == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cus.store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
-// Workgroups of `kernel` (`threads` per block, static LDS only) resident per
-// compute unit, from the runtime's occupancy calculator.
-int blocks_per_cu(const void *kernel, int threads = kBlock) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1) n = 1;
-    return n;
-}
-
 // Walk length of one work item (a wave of the forward, a block of the
 // backward): whole groups of `unit` tokens, at most `cap`.  ceil(N / len) *
 // `lanes` items run in rounds of `slots` resident items, so the length that

@@ -232,8 +232,8 @@ hipError_t mfma_fwd_wide(const LrProblem &pr, hipStream_t st) {
     const int64_t npairs = (p.D + 63) / 64;
     const int64_t cap = walk_cap(p.D, 16 * PF, 16 * (2 * PF + 2));
     if (cap < 16 * PF) return hipErrorNotSupported;  // the caller falls back
-    static const int bpc_vec = blocks_per_cu(reinterpret_cast<const void *>(&lr_fwd_wide<W, RC, PF, true>));
-    static const int bpc_gather = blocks_per_cu(reinterpret_cast<const void *>(&lr_fwd_wide<W, RC, PF, false>));
+    static const int bpc_vec = blocks_per_cu(reinterpret_cast<const void *>(&lr_fwd_wide<W, RC, PF, true>), kBlock);
+    static const int bpc_gather = blocks_per_cu(reinterpret_cast<const void *>(&lr_fwd_wide<W, RC, PF, false>), kBlock);
     const bool rvec = p.R % 8 == 0;
     const int64_t slots = (int64_t)device_cus() * (rvec ? bpc_vec : bpc_gather) * (kBlock / kWave);
     const int64_t tpw = walk_length(p.N, npairs, slots, cap, 16 * PF, kWaveFixedTokens);
