@@ -220,14 +220,17 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_wide(LrParams p, int64_t npairs
     }
 }
 
-#ifndef DSC_LR_FWD_WIDE_PF
-#define DSC_LR_FWD_WIDE_PF 4
+#ifndef DSC_LR_FWD_WIDE_PF2
+#define DSC_LR_FWD_WIDE_PF2 2
 #endif
-constexpr int kWidePF = DSC_LR_FWD_WIDE_PF;  // wide forward prefetch depth (steps, measured)
+// Prefetch depth in steps (measured on MI355X).  At R > 32 a depth of 2 keeps
+// the kernel within 256 VGPRs, i.e. 2 waves per SIMD.
+template <int RC>
+constexpr int wide_pf() { return RC == 1 ? 4 : DSC_LR_FWD_WIDE_PF2; }
 
 template <int W, int RC>
 hipError_t mfma_fwd_wide(const LrProblem &pr, hipStream_t st) {
-    constexpr int PF = kWidePF;
+    constexpr int PF = wide_pf<RC>();
     LrParams p = make_params<BF16>(pr);
     const int64_t npairs = (p.D + 63) / 64;
     const int64_t cap = walk_cap(p.D, 16 * PF, 16 * (2 * PF + 2));
