@@ -220,13 +220,16 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_wide(LrParams p, int64_t npairs
     }
 }
 
+#ifndef DSC_LR_FWD_WIDE_PF1
+#define DSC_LR_FWD_WIDE_PF1 4
+#endif
 #ifndef DSC_LR_FWD_WIDE_PF2
 #define DSC_LR_FWD_WIDE_PF2 2
 #endif
 // Prefetch depth in steps (measured on MI355X).  At R > 32 a depth of 2 keeps
 // the kernel within 256 VGPRs, i.e. 2 waves per SIMD.
 template <int RC>
-constexpr int wide_pf() { return RC == 1 ? 4 : DSC_LR_FWD_WIDE_PF2; }
+constexpr int wide_pf() { return RC == 1 ? DSC_LR_FWD_WIDE_PF1 : DSC_LR_FWD_WIDE_PF2; }
 
 template <int W, int RC>
 hipError_t mfma_fwd_wide(const LrProblem &pr, hipStream_t st) {
