@@ -235,54 +235,6 @@ struct SeqMap {
     }
 };
 
-// Wave-uniform walk over the sequences in increasing token order: one binary
-// search at the start, then each boundary crossing advances by one entry.
-// Call advance(n) with non-decreasing wave-uniform n; afterwards the sequence
-// [s, e) contains n.
-struct SeqCursor {
-    const int32_t *cu;
-    int64_t T;
-    int n_seqs;
-    int idx;
-    int64_t s, e;
-
-    __device__ __forceinline__ void init(const SeqMap &m, int64_t n) {
-        cu = m.cu;
-        T = m.T;
-        n_seqs = m.n_seqs;
-        idx = 0;
-        if (cu == nullptr) {
-            s = (n / T) * T;
-            e = s + T;
-            return;
-        }
-        int lo = 0, hi = m.n_seqs;
-        while (hi - lo > 1) {
-            int mid = (lo + hi) >> 1;
-            if ((int64_t)cu[mid] <= n) lo = mid;
-            else hi = mid;
-        }
-        idx = lo;
-        s = cu[lo];
-        e = cu[lo + 1];
-    }
-
-    // Stops at the last sequence: e never moves past the end of the offsets.
-    __device__ __forceinline__ void advance(int64_t n) {
-        while (n >= e) {
-            if (cu == nullptr) {
-                s = e;
-                e = s + T;
-            } else {
-                if (idx + 1 >= n_seqs) break;
-                ++idx;
-                s = e;
-                e = cu[idx + 1];
-            }
-        }
-    }
-};
-
 // Per-wave bit map of sequence starts over the tokens [base, base + 32*kWords),
 // kept in LDS and built once before a wave's token walk, so the walk itself
 // issues no memory loads besides its data stream (which keeps the compiler's
