@@ -31,7 +31,10 @@
  *               (fused multiply-add) and each output is rounded once, to
  *               nearest even, to its storage type.
  *   B, T, D     batch, tokens per row and channels; tensors named (B,T,D)
- *               are dense row-major with channels innermost.
+ *               are dense row-major with channels innermost.  B or T may
+ *               be 0 (an empty batch): the call then computes nothing
+ *               except that the low-rank backward zero-fills dU, and the
+ *               pointers of tensors without elements may be NULL.
  *   W           taps, 1..8.
  *   cu_seqlens  NULL with n_seqs == 0: each of the B rows is one sequence.
  *               Otherwise a DEVICE pointer to int32[n_seqs+1] strictly

@@ -55,7 +55,7 @@ size_t esize(int dtype) { return dtype == DSC_BF16 ? 2 : 4; }
 dsc_status check_common(int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
                         const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual) {
     if (dtype != DSC_FP32 && dtype != DSC_BF16) return fail(DSC_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
-    if (B < 1 || T < 1 || D < 1) return fail(DSC_ERR_SHAPE, "B, T, D must be >= 1 (got %lld, %lld, %lld)",
+    if (B < 0 || T < 0 || D < 1) return fail(DSC_ERR_SHAPE, "B, T must be >= 0 and D >= 1 (got %lld, %lld, %lld)",
                                              (long long)B, (long long)T, (long long)D);
     if (B > (int64_t)1 << 40 || T > (int64_t)1 << 40 || B * T > (int64_t)INT32_MAX)
         return fail(DSC_ERR_SHAPE, "B*T = %lld tokens exceeds 2^31-1", (long long)(B * T));
@@ -64,6 +64,7 @@ dsc_status check_common(int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
     const int vec = dtype == DSC_BF16 ? 8 : 4;
     if (D % vec) return fail(DSC_ERR_SHAPE, "D = %lld must be a multiple of %d for this dtype", (long long)D, vec);
     if (residual != 0 && residual != 1) return fail(DSC_ERR_SHAPE, "residual must be 0 or 1");
+    if (B * T == 0) return DSC_SUCCESS;  // empty batch: cu_seqlens is not read
     if ((cu_seqlens == nullptr) != (n_seqs == 0))
         return fail(DSC_ERR_SHAPE, "cu_seqlens and n_seqs disagree (NULL pointer iff n_seqs == 0)");
     if (n_seqs < 0 || n_seqs > B * T) return fail(DSC_ERR_SHAPE, "n_seqs = %d out of range", n_seqs);
@@ -90,10 +91,11 @@ dsc_status dsc_headwise_fwd(void *stream, int dtype, int64_t B, int64_t T, int64
                             int32_t H, const void *x, const void *w, const int32_t *cu_seqlens,
                             int32_t n_seqs, int32_t residual, void *y) {
     DSC_TRY(check_common(dtype, B, T, D, W, cu_seqlens, n_seqs, residual));
-    if (!x || !w || !y) return fail(DSC_ERR_NULL, "x, w and y are required");
     if (H < 1 || D % H) return fail(DSC_ERR_SHAPE, "H = %d must divide D = %lld", H, (long long)D);
     const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
     if (!dsc::headwise_supported(dt, D, H)) return fail(DSC_ERR_UNSUPPORTED, "H = %d not supported", H);
+    if (B * T == 0) return ok();  // empty batch: nothing to compute
+    if (!x || !w || !y) return fail(DSC_ERR_NULL, "x, w and y are required");
     if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
     const size_t es = esize(dtype), N = (size_t)(B * T);
     const Range in[] = {rng("x", x, N * D * es), rng("w", w, N * (D / H) * W * es),
@@ -109,10 +111,11 @@ dsc_status dsc_headwise_bwd(void *stream, int dtype, int64_t B, int64_t T, int64
                             const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual,
                             void *dx, void *dw) {
     DSC_TRY(check_common(dtype, B, T, D, W, cu_seqlens, n_seqs, residual));
-    if (!x || !w || !dy || !dx || !dw) return fail(DSC_ERR_NULL, "x, w, dy, dx and dw are required");
     if (H < 1 || D % H) return fail(DSC_ERR_SHAPE, "H = %d must divide D = %lld", H, (long long)D);
     const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
     if (!dsc::headwise_supported(dt, D, H)) return fail(DSC_ERR_UNSUPPORTED, "H = %d not supported", H);
+    if (B * T == 0) return ok();  // empty batch: dx and dw have no elements
+    if (!x || !w || !dy || !dx || !dw) return fail(DSC_ERR_NULL, "x, w, dy, dx and dw are required");
     if (!aligned16(x) || !aligned16(w) || !aligned16(dy) || !aligned16(dx) || !aligned16(dw))
         return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
     const size_t es = esize(dtype), N = (size_t)(B * T);
@@ -129,8 +132,9 @@ dsc_status dsc_lowrank_fwd(void *stream, int dtype, int64_t B, int64_t T, int64_
                            int32_t R, const void *x, const void *z, const void *U,
                            const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, void *y) {
     DSC_TRY(check_common(dtype, B, T, D, W, cu_seqlens, n_seqs, residual));
-    if (!x || !z || !U || !y) return fail(DSC_ERR_NULL, "x, z, U and y are required");
     if (R < 1 || R > 128) return fail(DSC_ERR_SHAPE, "R = %d must be in 1..128", R);
+    if (B * T == 0) return ok();  // empty batch: y has no elements
+    if (!x || !z || !U || !y) return fail(DSC_ERR_NULL, "x, z, U and y are required");
     if (!aligned16(x) || !aligned16(z) || !aligned16(U) || !aligned16(y))
         return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
     const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
@@ -154,9 +158,14 @@ dsc_status dsc_lowrank_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_
                            const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, void *dx,
                            void *dz, float *dU, void *workspace, size_t workspace_bytes) {
     DSC_TRY(check_common(dtype, B, T, D, W, cu_seqlens, n_seqs, residual));
+    if (R < 1 || R > 128) return fail(DSC_ERR_SHAPE, "R = %d must be in 1..128", R);
+    if (B * T == 0) {  // empty batch: dU is a sum over no tokens, zero; nothing else has elements
+        if (!dU) return fail(DSC_ERR_NULL, "dU is required");
+        if (!aligned16(dU)) return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+        return launched(dsc::lowrank_zero(dU, (int64_t)R * D * W, (hipStream_t)stream), "dsc_lowrank_bwd launch");
+    }
     if (!x || !z || !U || !dy || !dx || !dz || !dU)
         return fail(DSC_ERR_NULL, "x, z, U, dy, dx, dz and dU are required");
-    if (R < 1 || R > 128) return fail(DSC_ERR_SHAPE, "R = %d must be in 1..128", R);
     if (!aligned16(x) || !aligned16(z) || !aligned16(U) || !aligned16(dy) || !aligned16(dx) ||
         !aligned16(dz) || !aligned16(dU))
         return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");

@@ -49,5 +49,7 @@ hipError_t lowrank_fwd(const LrProblem &p, hipStream_t s);
 // the other kernels, which then run instead.
 hipError_t lowrank_fwd_wide(const LrProblem &p, hipStream_t s, bool *used);
 hipError_t lowrank_bwd(const LrProblem &p, hipStream_t s);
+// Zero-fills n fp32 values (16-byte aligned); the backward of an empty batch.
+hipError_t lowrank_zero(float *p, int64_t n, hipStream_t s);
 
 }  // namespace dsc

@@ -1034,6 +1034,13 @@ hipError_t lowrank_fwd(const LrProblem &p, hipStream_t s) {
     DSC_W_SWITCH(p.W, (generic_fwd<F32, Wc>(p, s)));
 }
 
+hipError_t lowrank_zero(float *p, int64_t n, hipStream_t s) {
+    const int64_t units = (n + 3) / 4;
+    if (units) hipLaunchKernelGGL(clear2, dim3((unsigned)nblocks(units)), dim3(kBlock), 0, s,
+                                  reinterpret_cast<uint32_t *>(p), n, static_cast<uint32_t *>(nullptr), (int64_t)0);
+    return hipGetLastError();
+}
+
 hipError_t lowrank_bwd(const LrProblem &p, hipStream_t s) {
     if (p.dtype == Dtype::BF16) {
         DSC_W_SWITCH(p.W, (mfma_bwd_rc<Wc>(p, s)));

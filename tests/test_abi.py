@@ -57,7 +57,8 @@ def test_headwise_fwd_validation(lib):
     assert hw_fwd(lib, H=7) == 2                  # H must divide D
     assert hw_fwd(lib, D=48, H=24) == 3           # 3 lanes per group: not built
     assert hw_fwd(lib, dtype=7) == 3
-    assert hw_fwd(lib, B=0) == 2
+    assert hw_fwd(lib, B=-1) == 2 and hw_fwd(lib, T=-3) == 2 and hw_fwd(lib, D=0) == 2
+    assert hw_fwd(lib, H=7, B=0) == 2             # shapes are checked for an empty batch too
     assert hw_fwd(lib, x=ctypes.c_void_p(A + 2)) == 4
     assert hw_fwd(lib, y=P(1)) == 5               # in place
     assert hw_fwd(lib, y=ctypes.c_void_p(A + 64)) == 5   # partial overlap with x
@@ -109,3 +110,15 @@ def test_binding_raises_with_message(lib):
     w = torch.zeros(1, 8, 60, 4, dtype=torch.bfloat16)
     with pytest.raises(binding.DscError, match="multiple of 8"):
         binding.dsc_headwise_fwd(x, w, x, stream=0)
+
+
+def test_empty_batch_is_a_no_op(lib):
+    # B or T = 0: nothing to compute and no HIP call, so NULL data pointers are
+    # accepted (the low-rank backward, which zero-fills dU, is covered on the GPU)
+    assert hw_fwd(lib, B=0, x=None, w=None, y=None) == 0
+    assert hw_fwd(lib, T=0, x=None, w=None, y=None) == 0
+    assert lib.dsc_headwise_bwd(S0, 1, 2, 0, 64, 4, 8, None, None, None, None, 0, 0, None, None) == 0
+    assert lib.dsc_lowrank_fwd(S0, 1, 0, 8, 64, 4, 16, None, None, None, None, 0, 1, None) == 0
+    assert lib.dsc_lowrank_fwd(S0, 1, 0, 8, 64, 4, 0, None, None, None, None, 0, 1, None) == 2  # R still checked
+    assert lib.dsc_lowrank_bwd(S0, 1, 0, 8, 64, 4, 16, None, None, None, None, None, 0, 0,
+                               None, None, None, None, 0) == 1   # dU is still required

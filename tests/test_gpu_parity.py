@@ -188,3 +188,27 @@ def test_stream_argument_is_honoured():
     s.synchronize()
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_empty_batch(dt):
+    """B*T = 0: every entry point succeeds; the low-rank dU (a sum over no tokens) is zero."""
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    B, D, W, H, R = 2, 64, 4, 8, 16
+    say(f"[empty] {dt} B={B} T=0 D={D}")
+    x = torch.empty((B, 0, D), dtype=dtype, device="cuda")
+    dy, y, dx = torch.empty_like(x), torch.empty_like(x), torch.empty_like(x)
+    w = torch.empty((B, 0, D // H, W), dtype=dtype, device="cuda")
+    dw = torch.empty_like(w)
+    z = torch.empty((B, 0, R), dtype=dtype, device="cuda")
+    dz = torch.empty_like(z)
+    U = torch.randn((R, D * W), device="cuda").to(dtype)
+    dU = torch.full((R, D * W), float("nan"), device="cuda")
+    binding.dsc_headwise_fwd(x, w, y)
+    binding.dsc_headwise_bwd(x, w, dy, dx, dw)
+    binding.dsc_lowrank_fwd(x, z, U, y, W=W)
+    assert binding.dsc_lowrank_bwd_workspace_size(dtype, B, 0, D, W, R) == 0
+    binding.dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, None, W=W)
+    torch.cuda.synchronize()
+    assert torch.equal(dU, torch.zeros_like(dU))
