@@ -465,7 +465,8 @@ struct BwdLds {
     static constexpr int kDzBufs = kTwoPerSimd ? 1 : 2;
     static constexpr int kDz = kDzBufs * 32 * PD;  // the wave's dz partials of kDzBufs pairs
     static constexpr int kLoop = kDwc + kZ + kDz;
-    static constexpr int kDuStage = RP * 32 * W * 4;   // dU tile staged for coalesced atomics
+    static constexpr int kDuPitch = 32 * W + 1;        // floats per rank row of the staged dU tile
+    static constexpr int kDuStage = RP * kDuPitch * 4; // dU tile staged for coalesced atomics
     static constexpr int kWave = (((kLoop > kDuStage ? kLoop : kDuStage) + 15) / 16) * 16;
     static constexpr int kBlock = 4 * H * kWave;
     static_assert(kBlocksPerCu * (kBlock + 4 * H * 4 * kSeqWords) <= 160 * 1024, "the blocks of a CU must fit the LDS");
@@ -666,11 +667,9 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
             const uint32_t xc[4] = {xr[cur].x, xr[cur].y, xr[cur].z, xr[cur].w};
             const uint32_t xp[4] = {xr[prv].x, xr[prv].y, xr[prv].z, xr[prv].w};
 
-            // dx = rho*g + sum_k w[n+k] * g[n+k]; w of tokens n+k on the matrix cores
+            // dx = rho*g + sum_k w[n+k] * g[n+k]; w of tokens n+k on the matrix cores,
+            // rho entering as the accumulator of tap 0: dx = (w_0 + rho) g + sum_{k>0} ...
             float acc[8];
-#pragma unroll
-            for (int c = 0; c < 8; ++c)
-                acc[c] = __uint_as_float(((c & 1) ? (gc[c >> 1] & 0xffff0000u) : (gc[c >> 1] << 16)) & p.rmask);
 #pragma unroll
             for (int k = 0; k < W; ++k) {
                 const int rr = tok + k;
@@ -693,7 +692,8 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
                 }
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    floatx4 cw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua[k][t][0], zb[0], floatx4{0.f, 0.f, 0.f, 0.f},
+                    const float c0 = k == 0 ? p.rho : 0.f;
+                    floatx4 cw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua[k][t][0], zb[0], floatx4{c0, c0, c0, c0},
                                                                          0, 0, 0);
 #pragma unroll
                     for (int c = 1; c < RC; ++c)
@@ -702,7 +702,7 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
                     for (int j = 0; j < 4; ++j) {
                         const int c = 4 * t + j;
                         const float gv = (c & 1) ? bf16_hi(gk[c >> 1]) : bf16_lo(gk[c >> 1]);
-                        acc[c] = __builtin_fmaf(cw[j], gv, acc[c]);
+                        acc[c] = k == 0 ? cw[j] * gv : __builtin_fmaf(cw[j], gv, acc[c]);
                     }
                 }
             }
@@ -824,9 +824,13 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
     }
 
     // dU tile of this wave (rank x 32 channels x W taps) -> LDS in the memory
-    // order of dU, then added to the output with coalesced atomics (each wave
-    // instruction covers 64 consecutive floats of one rank row).
+    // order of dU (odd row pitch, so a wave's staging writes spread over the
+    // banks), then added to the output with coalesced atomics: each wave
+    // instruction covers 64 consecutive floats of one rank row.  Every wave
+    // flushes ranks of its own slice; with H == 2 the two halves take
+    // alternate groups of 4 ranks and add both halves' tiles.
     __syncthreads();  // every wave is done with the loop's LDS regions
+    constexpr int kPitch = L::kDuPitch;
     float *dus = reinterpret_cast<float *>(my);
 #pragma unroll
     for (int k = 0; k < W; ++k)
@@ -836,18 +840,41 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
             for (int rt = 0; rt < RT; ++rt) {
                 const int r = 16 * rt + i16;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) dus[r * (32 * W) + (16 * ct + 4 * q + j) * W + k] = du[k][ct][rt][j];
+                for (int j = 0; j < 4; ++j) dus[r * kPitch + (16 * ct + 4 * q + j) * W + k] = du[k][ct][rt][j];
             }
     __syncthreads();
-    if (half == 0) {  // wave-uniform; with H == 2 the second half's tile of the same slice is added here
-        const float *dus2 = reinterpret_cast<const float *>(my + 4 * L::kWave);
-        const int64_t nvalid = (D - d0 < 32 ? D - d0 : 32) * W;  // channels of this slice inside D
-        for (int r = 0; r < R; ++r)
-            for (int idx = lane; idx < nvalid; idx += kWave) {
-                float v = dus[r * (32 * W) + idx];
-                if constexpr (H == 2) v += dus2[r * (32 * W) + idx];
-                atomicAdd(p.dU + (int64_t)r * DW + d0 * W + idx, v);
-            }
+    {
+        const float *t0 = reinterpret_cast<const float *>(lds + slice * L::kWave);
+        const float *t1 = reinterpret_cast<const float *>(lds + (4 + slice) * L::kWave);  // read only with H == 2
+        const int nvalid = (int)((D - d0 < 32 ? D - d0 : 32) * W);  // floats of this slice inside D
+        constexpr int kJ = (32 * W + kWave - 1) / kWave;
+        float *dst = p.dU + d0 * W;
+        // ranks rb .. rb+3 stay below RP (rb is a multiple of 4 below R <= RP, and
+        // RP is a multiple of 32): the tile reads are in bounds; ranks >= R are
+        // not added
+#pragma unroll 1
+        for (int rb = 4 * half; rb < R; rb += 4 * H) {
+            float v[4][kJ];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int j = 0; j < kJ; ++j) {
+                    const int idx = lane + kWave * j;
+                    float a = 0.f;
+                    if (idx < 32 * W) {
+                        a = t0[(rb + u) * kPitch + idx];
+                        if constexpr (H == 2) a += t1[(rb + u) * kPitch + idx];
+                    }
+                    v[u][j] = a;
+                }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int j = 0; j < kJ; ++j) {
+                    const int idx = lane + kWave * j;
+                    if (rb + u < R && idx < nvalid) atomicAdd(dst + (int64_t)(rb + u) * DW + idx, v[u][j]);
+                }
+        }
     }
 }
 
