@@ -485,6 +485,8 @@ __device__ __forceinline__ uint2 lds_read_tr(const unsigned char *addr) {
     return __builtin_bit_cast(uint2, v);
 }
 
+template <bool V> struct MaskTag { static constexpr bool value = V; };
+
 template <int W, int RC, int P, bool RVEC, int H>
 __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void lr_bwd_mfma(LrParams p, int64_t nslices,
                                                                                          int64_t tok_per_half) {
@@ -651,16 +653,22 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
             wave_lds_fence();
             fetch_z(s + 1 + P, zr[nxt]);
 
-            // sequence masks (branch-free): taps k <= back (dwc) and k < ahead (dx)
-            // stay in n's sequence; bit j of win <-> token nstep - (W-1) + j
+            // sequence masks: taps k <= back (dwc) and k < ahead (dx) stay in n's
+            // sequence; bit j of win <-> token nstep - (W-1) + j.  A step with no
+            // sequence start among its taps' tokens, inside the block's range, runs
+            // a copy of the step without the masks (the test is wave-uniform).
             int back = W - 1, ahead = W;
+            bool fast = nstep + 16 <= nend;
             if constexpr (W > 1) {
                 const uint32_t win = __builtin_amdgcn_readfirstlane(starts.window(nstep - (W - 1)));
+                fast = fast && ((win >> 1) & ((1u << (2 * W + 13)) - 1u)) == 0u;  // the bits sb, sa test below
                 const uint32_t sb = (win >> (tok + 1)) & ((1u << (W - 1)) - 1u);  // starts in n-W+2 .. n
                 back = sb ? (W - 2) - (31 - __builtin_clz(sb)) : W - 1;
                 const uint32_t sa = (win >> (tok + W)) & ((1u << (W - 1)) - 1u);  // starts in n+1 .. n+W-1
                 ahead = sa ? 1 + __builtin_ctz(sa) : W;
             }
+            auto body = [&](auto mask_tag) {
+            constexpr bool M = decltype(mask_tag)::value;  // apply the masks
 
             const uint32_t gc[4] = {gr[cur].x, gr[cur].y, gr[cur].z, gr[cur].w};
             const uint32_t gn[4] = {gr[nxt].x, gr[nxt].y, gr[nxt].z, gr[nxt].w};
@@ -688,7 +696,7 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
                 } else {
                     shift_ahead4<W>(k, gc, gn, gk);
 #pragma unroll
-                    for (int i2 = 0; i2 < 4; ++i2) gk[i2] = k < ahead ? gk[i2] : 0u;  // m+k in m's sequence
+                    for (int i2 = 0; i2 < 4; ++i2) gk[i2] = (!M || k < ahead) ? gk[i2] : 0u;  // m+k in m's sequence
                 }
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
@@ -732,7 +740,7 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
                 uint32_t dw[4];
 #pragma unroll
                 for (int i2 = 0; i2 < 4; ++i2) {
-                    const uint32_t xv = (own && k <= back) ? xk[i2] : 0u;
+                    const uint32_t xv = (!M || (own && k <= back)) ? xk[i2] : 0u;
                     dw[i2] = pack_bf16x2(bf16_lo(gc[i2]) * bf16_lo(xv), bf16_hi(gc[i2]) * bf16_hi(xv));
                 }
                 const bf16x8 b = bf16x8_from_u32(dw);
@@ -749,6 +757,8 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
                 float4 *d = reinterpret_cast<float4 *>(dzb + (buf * 32 + 16 * ps + tok) * L::PD + 4 * (16 * rt + 4 * q));
                 *d = make_float4(cz[rt][0], cz[rt][1], cz[rt][2], cz[rt][3]);
             }
+            };
+            if (fast) body(MaskTag<false>{}); else body(MaskTag<true>{});
 
             // ring refills (issued after the step's reads of these slots)
             xr[prv] = fetch_act(rx, s + P - 1);
