@@ -104,6 +104,40 @@ def test_lowrank_small(case):
     assert_close("dU", dU, rdU, tol)
 
 
+def _step_edge_cu(T: int) -> np.ndarray:
+    """Sequence starts at every offset around the kernels' 16-token steps
+    (first, second, third and last tokens of a step, and mid-step), with runs
+    of length-1 sequences across some step edges and a ragged end."""
+    offs = [0, 1, 2, 3, 7, 13, 14, 15]
+    starts = {0, T}
+    for j, m in enumerate(range(1, T // 16)):
+        starts.add(16 * m + offs[j % len(offs)])
+        if j % 5 == 0:
+            starts.update({16 * m - 1, 16 * m + 1})
+    return np.array(sorted(t for t in starts if 0 <= t <= T), dtype=np.int32)
+
+
+@pytest.mark.parametrize("W,R", [(4, 32), (4, 64), (3, 20), (8, 8), (2, 48)])
+def test_lowrank_sequence_starts_at_step_edges(W, R):
+    """Steps with a sequence start among their taps take the masked path, the
+    others the unmasked one; both must agree with the oracle everywhere."""
+    T = 709
+    wl, inp = inputs.small("lowrank", 1, T, 128, W, R=R, dtype="bf16", residual=True,
+                           seed=11 * W + R)
+    inp["cu_seqlens"] = _step_edge_cu(T)
+    say(f"[lowrank] {wl.name} step-edge starts={inp['cu_seqlens'].tolist()}")
+    y, dx, dz, dU = run_lowrank(inp, W, True)
+    cu = inp["cu_seqlens"]
+    x64, z64, U64, g64 = (to_f64(inp[k]) for k in ("x", "z", "U", "dy"))
+    ry = oracle.lowrank_fwd(x64, z64, U64, W, cu_seqlens=cu, residual=True)
+    rdx, rdz, rdU = oracle.lowrank_bwd(x64, z64, U64, g64, W, cu_seqlens=cu, residual=True)
+    tol = TOL["bf16"]
+    assert_close("y", y, ry, tol)
+    assert_close("dx", dx, rdx, tol)
+    assert_close("dz", dz, rdz, tol)
+    assert_close("dU", dU, rdU, tol)
+
+
 def test_headwise_repeat_is_bitwise_identical():
     wl, inp = inputs.small("headwise", 2, 300, 1024, 4, H=16, dtype="bf16", residual=True, seed=5)
     say(f"[headwise determinism] {wl.name}")
