@@ -49,8 +49,10 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_lowrank_fwd.argtypes = [i64, i64, i64, i32, i32, p, p, p, p, i32, i32, i64, i64, p]
     lib.oracle_lowrank_bwd.argtypes = [i64, i64, i64, i32, i32, p, p, p, p, p, i32, i32, i64, i64,
                                        p, p, i64, i64, p]
+    lib.oracle_static_fwd.argtypes = [i64, i64, i64, i32, p, p, p, i32, i32, i64, i64, p]
+    lib.oracle_static_bwd.argtypes = [i64, i64, i64, i32, p, p, p, p, i32, i32, i64, i64, p, p]
     for name in ("oracle_headwise_fwd", "oracle_headwise_bwd", "oracle_lowrank_fwd",
-                 "oracle_lowrank_bwd"):
+                 "oracle_lowrank_bwd", "oracle_static_fwd", "oracle_static_bwd"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -160,6 +162,35 @@ class Oracle:
             return dx.reshape(B, T, D), dz.reshape(B, T, R), dU
         return dx, dz, dU
 
+    def static_fwd(self, x, c, *, cu_seqlens=None, residual=False, rows=None):
+        """x (B,T,D), c (D,W) one filter per channel -> y (B,T,D) (or compact rows)."""
+        x, c = _f64(x), _f64(c)
+        B, T, D = x.shape
+        if c.ndim != 2 or c.shape[0] != D:
+            raise ValueError(f"c must be (D, W) with D={D}, got {c.shape}")
+        W = c.shape[1]
+        lo, hi = rows if rows is not None else (0, B * T)
+        cu, ns = _cu(cu_seqlens)
+        y = np.empty((hi - lo, D))
+        _check(self.lib.oracle_static_fwd(B, T, D, W, _ptr(x), _ptr(c), _ptr(cu), ns,
+                                          int(bool(residual)), lo, hi, _ptr(y)), "static_fwd")
+        return y.reshape(B, T, D) if rows is None else y
+
+    def static_bwd(self, x, c, dy, *, cu_seqlens=None, residual=False, rows=None):
+        """-> (dx, dc): dx over token rows, dc (D, W) summed over every token."""
+        x, c, dy = _f64(x), _f64(c), _f64(dy)
+        B, T, D = x.shape
+        if c.ndim != 2 or c.shape[0] != D:
+            raise ValueError(f"c must be (D, W) with D={D}, got {c.shape}")
+        W = c.shape[1]
+        lo, hi = rows if rows is not None else (0, B * T)
+        cu, ns = _cu(cu_seqlens)
+        dx = np.empty((hi - lo, D))
+        dc = np.empty((D, W))
+        _check(self.lib.oracle_static_bwd(B, T, D, W, _ptr(x), _ptr(c), _ptr(dy), _ptr(cu), ns,
+                                          int(bool(residual)), lo, hi, _ptr(dx), _ptr(dc)), "static_bwd")
+        return (dx.reshape(B, T, D) if rows is None else dx), dc
+
 
 def num_threads() -> int:
     """OpenMP threads the oracle uses."""
@@ -190,3 +221,11 @@ def lowrank_fwd(*a, **k):
 
 def lowrank_bwd(*a, **k):
     return default().lowrank_bwd(*a, **k)
+
+
+def static_fwd(*a, **k):
+    return default().static_fwd(*a, **k)
+
+
+def static_bwd(*a, **k):
+    return default().static_bwd(*a, **k)

@@ -19,6 +19,8 @@
  * and the authors' thread ("Custom Triton GPU kernels maintain wall-clock
  * training efficiency", digg.com): the static short convolution being
  * generalised is depthwise and causal, so x before a sequence start is zero.
+ * That static layer itself (one filter per channel, the same at every
+ * position) is the last pair of functions below.
  *
  * Readings where the pages are silent (each listed in the design notes):
  *   - tap k = 0 multiplies the current token x_t;
@@ -231,6 +233,69 @@ int oracle_lowrank_bwd(int64_t B, int64_t T, int64_t D, int32_t W, int32_t R,
                 if (n - k >= seg[n]) acc += z[n * R + r] * (g[n * D + d] * x[(n - k) * D + d]);
             dU[(int64_t)r * DWs + c] = acc;
         }
+    }
+    free(seg);
+    return 0;
+}
+
+/* ------------------------------------------------------------ static filter */
+
+/* The fixed-filter layer that the dynamic convolution generalises (authors'
+ * thread on digg.com: a depthwise causal convolution of small width, the
+ * same filter at every position), with tap k weighting lag k as above:
+ *   y[n,d] = rho*x[n,d] + sum_{k<W, n-k >= seg(n)} c[d,k] * x[n-k,d]
+ * c has layout (D, W), tap innermost.                                        */
+int oracle_static_fwd(int64_t B, int64_t T, int64_t D, int32_t W, const double *x, const double *c,
+                      const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual,
+                      int64_t n_lo, int64_t n_hi, double *y)
+{
+    if (check_common(B, T, D, W, cu_seqlens, n_seqs, n_lo, n_hi)) return -2;
+    int64_t *seg = segment_starts(B, T, cu_seqlens, n_seqs);
+    if (!seg) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = n_lo; n < n_hi; ++n) {
+        for (int64_t d = 0; d < D; ++d) {
+            double acc = residual ? x[n * D + d] : 0.0;
+            for (int32_t k = 0; k < W; ++k)
+                if (n - k >= seg[n]) acc += c[d * W + k] * x[(n - k) * D + d];
+            y[(n - n_lo) * D + d] = acc;
+        }
+    }
+    free(seg);
+    return 0;
+}
+
+/* Chain rule for L = <g, y>:
+ *   dx[m,d] = rho*g[m,d] + sum_{k: m+k < N, m >= seg(m+k)} c[d,k] * g[m+k,d]
+ *   dc[d,k] = sum over every token n of [n-k >= seg(n)] * g[n,d] * x[n-k,d]
+ * dx covers tokens [n_lo, n_hi); dc is (D, W) over all tokens.               */
+int oracle_static_bwd(int64_t B, int64_t T, int64_t D, int32_t W, const double *x, const double *c,
+                      const double *g, const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual,
+                      int64_t n_lo, int64_t n_hi, double *dx, double *dc)
+{
+    if (check_common(B, T, D, W, cu_seqlens, n_seqs, n_lo, n_hi)) return -2;
+    const int64_t N = B * T;
+    int64_t *seg = segment_starts(B, T, cu_seqlens, n_seqs);
+    if (!seg) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = n_lo; m < n_hi; ++m) {
+        for (int64_t d = 0; d < D; ++d) {
+            double acc = residual ? g[m * D + d] : 0.0;
+            for (int32_t k = 0; k < W; ++k) {
+                int64_t n = m + k;
+                if (n < N && m >= seg[n]) acc += c[d * W + k] * g[n * D + d];
+            }
+            dx[(m - n_lo) * D + d] = acc;
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < D * W; ++i) {
+        const int64_t d = i / W;
+        const int32_t k = (int32_t)(i % W);
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; ++n)
+            if (n - k >= seg[n]) acc += g[n * D + d] * x[(n - k) * D + d];
+        dc[i] = acc;
     }
     free(seg);
     return 0;

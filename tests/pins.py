@@ -6,7 +6,7 @@ disagrees with:
   - hand-worked examples of the defining formula (tests/golden),
   - the dense banded-matrix brute force (tests/bruteforce.py),
   - closed forms (impulse response, W = 1 scaling, static filters equal to
-    numpy.convolve, rank-1 low-rank),
+    numpy.convolve / numpy.correlate, rank-1 low-rank),
   - the adjoint identity and exact central finite differences of L = <g, y>,
   - structural identities (segment independence, locality / causality).
 The formula is the one in "Dynamic Short Convolutions Improve Transformers"
@@ -340,6 +340,82 @@ def pin_row_ranges_match_full(orc):
     _close(dxr, dx.reshape(B * T, D)[3:11], what="row range dx")
     _close(dzr, dz.reshape(B * T, R)[3:11], what="row range dz")
     _close(dUr, dU.reshape(R, D, W)[:, 1:3].reshape(R, 2 * W), what="channel range dU")
+
+
+# ------------------------------------------------------------ static filter
+# The fixed-filter layer the dynamic convolution generalises (authors' thread
+# on digg.com): one filter c[d, :] per channel, the same at every position.
+
+
+def pin_static_layer_is_numpy_convolve(orc):
+    """Per sequence and channel: y = rho*x + numpy.convolve(x, c[d])[:L], dx the same
+    with the sequence reversed, dc[d, k] the lag-k entry of numpy.correlate(g, x)."""
+    rng = _rng(14)
+    B, T, D, W = 2, 11, 5, 4
+    cu = [0, 1, 4, 11, 13, 22]
+    x = rng.standard_normal((B, T, D))
+    g = rng.standard_normal((B, T, D))
+    c = rng.standard_normal((D, W))
+    for res in (False, True):
+        y = orc.static_fwd(x, c, cu_seqlens=cu, residual=res).reshape(B * T, D)
+        dx, dc = orc.static_bwd(x, c, g, cu_seqlens=cu, residual=res)
+        dx = dx.reshape(B * T, D)
+        xf, gf = x.reshape(B * T, D), g.reshape(B * T, D)
+        want_dc = np.zeros((D, W))
+        for a, b in zip(cu[:-1], cu[1:]):
+            L = b - a
+            for d in range(D):
+                _close(y[a:b, d], res * xf[a:b, d] + np.convolve(xf[a:b, d], c[d])[:L], what="static y")
+                _close(dx[a:b, d], res * gf[a:b, d] + np.convolve(gf[a:b, d][::-1], c[d])[:L][::-1],
+                       what="static dx")
+                corr = np.correlate(gf[a:b, d], xf[a:b, d], mode="full")  # index L-1+k <-> lag k
+                for k in range(min(W, L)):
+                    want_dc[d, k] += corr[L - 1 + k]
+        _close(dc, want_dc, what="static dc")
+
+
+def pin_static_equals_constant_filter(orc):
+    """The static layer is the per-channel dynamic one with the same filter at every token."""
+    rng = _rng(15)
+    B, T, D, W = 2, 9, 6, 3
+    cu = [0, 5, 7, 18]
+    x = rng.standard_normal((B, T, D))
+    g = rng.standard_normal((B, T, D))
+    c = rng.standard_normal((D, W))
+    w = np.broadcast_to(c, (B, T, D, W)).copy()
+    _close(orc.static_fwd(x, c, cu_seqlens=cu, residual=True),
+           orc.headwise_fwd(x, w, cu_seqlens=cu, residual=True), what="static == constant dynamic y")
+    dx_s, dc = orc.static_bwd(x, c, g, cu_seqlens=cu, residual=True)
+    dx_h, dw = orc.headwise_bwd(x, w, g, cu_seqlens=cu, residual=True)
+    _close(dx_s, dx_h, what="static == constant dynamic dx")
+    _close(dc, dw.reshape(B * T, D, W).sum(0), what="dc == sum over tokens of the per-token dw")
+
+
+def pin_static_width_one_is_scaling(orc):
+    rng = _rng(16)
+    B, T, D = 2, 5, 3
+    x = rng.standard_normal((B, T, D))
+    g = rng.standard_normal((B, T, D))
+    c = rng.standard_normal((D, 1))
+    for res in (False, True):
+        _close(orc.static_fwd(x, c, residual=res), (res + c[:, 0]) * x, what="static W=1 y")
+        dx, dc = orc.static_bwd(x, c, g, residual=res)
+        _close(dx, (res + c[:, 0]) * g, what="static W=1 dx")
+        _close(dc[:, 0], (g * x).sum(axis=(0, 1)), what="static W=1 dc")
+
+
+def pin_finite_differences_static(orc):
+    rng = _rng(17)
+    B, T, D, W = 2, 5, 3, 4
+    cu = [0, 3, 4, 10]
+    x = rng.standard_normal((B, T, D))
+    g = rng.standard_normal((B, T, D))
+    c = rng.standard_normal((D, W))
+    for res in (False, True):
+        L = lambda: float(np.sum(g * orc.static_fwd(x, c, cu_seqlens=cu, residual=res)))
+        dx, dc = orc.static_bwd(x, c, g, cu_seqlens=cu, residual=res)
+        _close(dx, _fd_grad(L, x), tol=1e-8, what="FD static dx")
+        _close(dc, _fd_grad(L, c), tol=1e-8, what="FD static dc")
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

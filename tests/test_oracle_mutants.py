@@ -16,8 +16,8 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "dsc_oracle.c")
 
 # (name, exact source fragment, replacement, expected occurrences)
 MUTANTS = [
-    ("drop_residual_fwd", "double acc = residual ? x[n * D + d] : 0.0;", "double acc = 0.0;", 2),
-    ("drop_residual_dx", "double acc = residual ? g[m * D + d] : 0.0;", "double acc = 0.0;", 2),
+    ("drop_residual_fwd", "double acc = residual ? x[n * D + d] : 0.0;", "double acc = 0.0;", 3),
+    ("drop_residual_dx", "double acc = residual ? g[m * D + d] : 0.0;", "double acc = 0.0;", 3),
     ("unshifted_tap", "w[(n * G + d / H) * W + k] * x[(n - k) * D + d]",
      "w[(n * G + d / H) * W + k] * x[n * D + d]", 1),
     ("strict_segment_test", "if (n - k >= seg[n]) acc += w", "if (n - k > seg[n]) acc += w", 1),
@@ -38,6 +38,13 @@ MUTANTS = [
     ("dU_wrong_z", "acc += z[n * R + r] * (g[n * D + d]", "acc += z[n * R + (R - 1 - r)] * (g[n * D + d]", 1),
     ("dU_unshifted", "(g[n * D + d] * x[(n - k) * D + d]);", "(g[n * D + d] * x[n * D + d]);", 1),
     ("segment_from_row", "seg[n] = cu_seqlens[i];", "seg[n] = (n / T) * T;", 1),
+    ("static_unshifted", "acc += c[d * W + k] * x[(n - k) * D + d];", "acc += c[d * W + k] * x[n * D + d];", 1),
+    ("static_reversed_taps", "acc += c[d * W + k] * x[", "acc += c[d * W + (W - 1 - k)] * x[", 1),
+    ("static_no_mask", "if (n - k >= seg[n]) acc += c[", "if (n - k >= 0) acc += c[", 1),
+    ("static_dx_filter_lag", "acc += c[d * W + k] * g[n * D + d];", "acc += c[d * W + k] * g[m * D + d];", 1),
+    ("static_dx_no_mask", "if (n < N && m >= seg[n]) acc += c[", "if (n < N) acc += c[", 1),
+    ("static_dc_unshifted", "acc += g[n * D + d] * x[(n - k) * D + d];", "acc += g[n * D + d] * x[n * D + d];", 1),
+    ("static_dc_no_mask", "if (n - k >= seg[n]) acc += g[", "if (n - k >= 0) acc += g[", 1),
 ]
 
 
