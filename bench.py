@@ -11,7 +11,9 @@ Prints one JSON line: tokens/s of the step, achieved algorithmic HBM GB/s,
 the roofline of the dominant entry point (HIP events around each call on
 the stream it runs on), per-entry-point figures, the 2B-scale workloads
 (head-wise MLP D=8192 H=16 and low-rank varlen D=6144 R=64) timed the same
-way, and the fp64 CPU oracle timed on a bounded sample of the step's work.
+way, the static short convolution (one fixed filter per channel) at the two
+head-wise shapes beside the dynamic figures, and the fp64 CPU oracle timed on
+a bounded sample of the step's work.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -36,6 +38,8 @@ def algorithmic_bytes(kind: str, direction: str, B, T, D, W, H=1, R=0, es=2) -> 
     """Each input read once, each output written once (the low-rank filters are never stored)."""
     N = B * T
     act = N * D * es
+    if kind == "static":  # one (D, W) filter, read once; dc is fp32
+        return 2 * act + D * W * es if direction == "fwd" else 3 * act + D * W * es + D * W * 4
     if kind == "headwise":
         filt = N * (D // H) * W * es
         return 2 * act + filt if direction == "fwd" else 3 * act + 2 * filt
@@ -59,6 +63,9 @@ class Case:
         if wl.kind == "headwise":
             self.w = inp["w"].to(dev)
             self.dw = torch.empty_like(self.w)
+        elif wl.kind == "static":
+            self.c = inp["c"].to(dev)
+            self.dc = torch.empty(self.c.shape, dtype=torch.float32, device=dev)
         else:
             self.z, self.U = inp["z"].to(dev), inp["U"].to(dev)
             self.dz = torch.empty_like(self.z)
@@ -70,6 +77,8 @@ class Case:
         wl = self.wl
         if wl.kind == "headwise":
             self.b.dsc_headwise_fwd(self.x, self.w, self.y, cu_seqlens=self.cu, residual=wl.residual)
+        elif wl.kind == "static":
+            self.b.dsc_static_fwd(self.x, self.c, self.y, cu_seqlens=self.cu, residual=wl.residual)
         else:
             self.b.dsc_lowrank_fwd(self.x, self.z, self.U, self.y, W=wl.W, cu_seqlens=self.cu,
                                    residual=wl.residual)
@@ -79,6 +88,9 @@ class Case:
         if wl.kind == "headwise":
             self.b.dsc_headwise_bwd(self.x, self.w, self.dy, self.dx, self.dw, cu_seqlens=self.cu,
                                     residual=wl.residual)
+        elif wl.kind == "static":
+            self.b.dsc_static_bwd(self.x, self.c, self.dy, self.dx, self.dc, cu_seqlens=self.cu,
+                                  residual=wl.residual)
         else:
             self.b.dsc_lowrank_bwd(self.x, self.z, self.U, self.dy, self.dx, self.dz, self.dU, self.ws,
                                    W=wl.W, cu_seqlens=self.cu, residual=wl.residual)
@@ -90,7 +102,7 @@ class Case:
     def flops(self, direction):
         wl = self.wl
         nd = wl.N * wl.D
-        if wl.kind == "headwise":
+        if wl.kind in ("headwise", "static"):
             return (2 if direction == "fwd" else 4) * wl.W * nd
         return (2 * wl.R * wl.W + 2 * wl.W) * nd * (1 if direction == "fwd" else 3)
 
@@ -238,6 +250,8 @@ ENTRY_KERNELS = {
     "dsc_headwise_bwd": (["hw_bwd_kernel"], []),
     "dsc_lowrank_fwd": (["lr_fwd_wide", "lr_fwd_mfma", "lr_fwd_generic"], []),
     "dsc_lowrank_bwd": (["lr_bwd_mfma", "lr_bwd_generic"], ["clear2", "fill_zero_f32", "cast_f32_bf16"]),
+    "dsc_static_fwd": (["st_fwd_kernel"], []),
+    "dsc_static_bwd": (["st_bwd_kernel"], ["st_zero"]),
 }
 
 
@@ -406,29 +420,52 @@ def main() -> int:
         "copy_same_bytes_GBps": round(copy_rate(torch, dom["algorithmic_bytes"]), 1),
     }
 
+    def fwd_bwd_times(wl, reps):
+        """Average fwd and bwd seconds of one workload, HIP events around each call."""
+        c = Case(wl, torch, binding, inputs)
+        for _ in range(3):
+            c.fwd(); c.bwd()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+                torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e in evs:
+            e[0].record(); c.fwd(); e[1].record(); c.bwd(); e[2].record()
+        torch.cuda.synchronize()
+        tf = sum(e[0].elapsed_time(e[1]) for e in evs) / reps * 1e-3
+        tb = sum(e[1].elapsed_time(e[2]) for e in evs) / reps * 1e-3
+        b = c.bytes("fwd") + c.bytes("bwd")
+        del c
+        torch.cuda.empty_cache()
+        return tf, tb, b
+
     if not args.no_large:
         large = {}
         for cfg in (4, 5):
-            c = Case(inputs.WORKLOADS[cfg], torch, binding, inputs)
-            for _ in range(3):
-                c.fwd(); c.bwd()
-            torch.cuda.synchronize()
-            reps = max(5, K // 2)
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-                    torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-            for e in evs:
-                e[0].record(); c.fwd(); e[1].record(); c.bwd(); e[2].record()
-            torch.cuda.synchronize()
-            tf = sum(e[0].elapsed_time(e[1]) for e in evs) / reps * 1e-3
-            tb = sum(e[1].elapsed_time(e[2]) for e in evs) / reps * 1e-3
-            b = c.bytes("fwd") + c.bytes("bwd")
-            large[c.wl.name] = {"tokens_per_s": round(c.wl.N / (tf + tb), 1),
-                                "fwd_us": round(tf * 1e6, 1), "bwd_us": round(tb * 1e6, 1),
-                                "GBps": round(b / (tf + tb) / 1e9, 1),
-                                "frac_hbm_peak": round(b / (tf + tb) / 1e9 / PEAK_HBM_GBPS, 4)}
-            del c
-            torch.cuda.empty_cache()
+            wl = inputs.WORKLOADS[cfg]
+            tf, tb, b = fwd_bwd_times(wl, max(5, K // 2))
+            large[wl.name] = {"tokens_per_s": round(wl.N / (tf + tb), 1),
+                              "fwd_us": round(tf * 1e6, 1), "bwd_us": round(tb * 1e6, 1),
+                              "GBps": round(b / (tf + tb) / 1e9, 1),
+                              "frac_hbm_peak": round(b / (tf + tb) / 1e9 / PEAK_HBM_GBPS, 4)}
         out["workloads_2b"] = large
+
+        # The pages set the dynamic kernels' latency against optimised kernels of
+        # the static short convolution (one fixed filter per channel).  Our own
+        # static kernels at the two head-wise shapes, timed the same way, beside
+        # the dynamic head-wise figures above.
+        static = {}
+        for cfg, dyn in ((2, (per_call["headwise_fwd"]["avg_us"], per_call["headwise_bwd"]["avg_us"])),
+                         (4, (large["headwise-mlp-2b"]["fwd_us"], large["headwise-mlp-2b"]["bwd_us"]))):
+            hw = inputs.WORKLOADS[cfg]
+            wl = inputs.Workload(hw.name.replace("headwise", "static"), "static", hw.B, hw.T, hw.D, hw.W,
+                                 dtype=hw.dtype, residual=hw.residual, cfg=hw.cfg)
+            tf, tb, b = fwd_bwd_times(wl, max(5, K // 2))
+            static[wl.name] = {"fwd_us": round(tf * 1e6, 1), "bwd_us": round(tb * 1e6, 1),
+                               "GBps": round(b / (tf + tb) / 1e9, 1),
+                               "frac_hbm_peak": round(b / (tf + tb) / 1e9 / PEAK_HBM_GBPS, 4),
+                               "dynamic_headwise_fwd_us": dyn[0], "dynamic_headwise_bwd_us": dyn[1],
+                               "dynamic_over_static": round((dyn[0] + dyn[1]) / ((tf + tb) * 1e6), 3)}
+        out["static_vs_dynamic"] = static
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline([cases[0].wl, cases[1].wl], args.cpu_seconds)

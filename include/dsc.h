@@ -27,14 +27,15 @@
  *               Every call is asynchronous on that stream; device faults
  *               surface at the caller's next synchronisation.
  *   dtype       DSC_FP32 or DSC_BF16: the element type of every activation,
- *               filter and z/U tensor of the call.  Arithmetic is fp32
- *               (fused multiply-add) and each output is rounded once, to
- *               nearest even, to its storage type.
+ *               filter and z/U tensor of the call (dU and dc are always
+ *               fp32).  Arithmetic is fp32 (fused multiply-add) and each
+ *               output is rounded once, to nearest even, to its storage type.
  *   B, T, D     batch, tokens per row and channels; tensors named (B,T,D)
  *               are dense row-major with channels innermost.  B or T may
  *               be 0 (an empty batch): the call then computes nothing
- *               except that the low-rank backward zero-fills dU, and the
- *               pointers of tensors without elements may be NULL.
+ *               except that the low-rank and static backward zero-fill dU
+ *               and dc, and the pointers of tensors without elements may
+ *               be NULL.
  *   W           taps, 1..8.
  *   cu_seqlens  NULL with n_seqs == 0: each of the B rows is one sequence.
  *               Otherwise a DEVICE pointer to int32[n_seqs+1] strictly
@@ -155,6 +156,38 @@ DSC_API dsc_status dsc_lowrank_bwd(void *stream, int dtype, int64_t B, int64_t T
                            int32_t R, const void *x, const void *z, const void *U, const void *dy,
                            const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, void *dx,
                            void *dz, float *dU, void *workspace, size_t workspace_bytes);
+
+/*
+ * Static short convolution: the fixed-filter layer that the dynamic one
+ * generalises, with one filter per channel, the same at every position.
+ * The authors' thread on digg.com ("Custom Triton GPU kernels maintain
+ * wall-clock training efficiency") describes it as a depthwise causal
+ * convolution of small width.  The gist.science summaries (Performance) set
+ * the dynamic kernels' latency against optimised kernels of this layer
+ * (causal_conv1d):
+ *   y[n,d] = rho*x[n,d] + sum_{k<W, n-k in n's sequence} c[d,k] * x[n-k,d]
+ *
+ *   x (B,T,D) dtype, in.   c (D,W) dtype, in: tap k weights lag k, so
+ *   c[d,0] multiplies the current token (causal_conv1d's weight with its
+ *   taps in reverse order).   y (B,T,D) dtype, out.
+ *   D multiple of 8 (bf16) / 4 (fp32).
+ */
+DSC_API dsc_status dsc_static_fwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                          const void *x, const void *c, const int32_t *cu_seqlens, int32_t n_seqs,
+                          int32_t residual, void *y);
+
+/*
+ * Static short convolution, backward for L = <dy, y>:
+ *   dx[m,d] = rho*dy[m,d] + sum_{k<W, m+k in m's sequence} c[d,k] * dy[m+k,d]
+ *   dc[d,k] = sum over all tokens n of [n-k in n's sequence] dy[n,d] * x[n-k,d]
+ *
+ *   x, dy (B,T,D) in;  c (D,W) in;  dx (B,T,D) dtype out;  dc (D,W) fp32 out.
+ *   dc is a sum over every token accumulated with fp32 atomics: its last
+ *   bits may differ run to run.  An empty batch zero-fills dc.
+ */
+DSC_API dsc_status dsc_static_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                          const void *x, const void *c, const void *dy, const int32_t *cu_seqlens,
+                          int32_t n_seqs, int32_t residual, void *dx, float *dc);
 
 /* Static name of a status code. */
 DSC_API const char *dsc_status_string(int status);

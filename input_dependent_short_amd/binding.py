@@ -42,8 +42,10 @@ def lib() -> ctypes.CDLL:
         L.dsc_lowrank_bwd_workspace_size.restype = ctypes.c_size_t
         L.dsc_lowrank_bwd.argtypes = [p, i, i64, i64, i64, i32, i32, p, p, p, p, p, i32, i32, p, p, p,
                                       p, ctypes.c_size_t]
+        L.dsc_static_fwd.argtypes = [p, i, i64, i64, i64, i32, p, p, p, i32, i32, p]
+        L.dsc_static_bwd.argtypes = [p, i, i64, i64, i64, i32, p, p, p, p, i32, i32, p, p]
         for f in ("dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd",
-                  "dsc_abi_version"):
+                  "dsc_static_fwd", "dsc_static_bwd", "dsc_abi_version"):
             getattr(L, f).restype = ctypes.c_int
         L.dsc_status_string.argtypes = [i]
         L.dsc_status_string.restype = ctypes.c_char_p
@@ -128,6 +130,24 @@ def dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, workspace=None, *, W, cu_seqlens=No
     _check(lib().dsc_lowrank_bwd(_stream(stream), _dtype_code(x), B, T, D, W, R, _ptr(x), _ptr(z),
                                  _ptr(U), _ptr(dy), cu, ns, int(bool(residual)), _ptr(dx), _ptr(dz),
                                  _ptr(dU), _ptr(workspace), ws_bytes))
+
+
+def dsc_static_fwd(x, c, y, *, cu_seqlens=None, residual=False, stream=None) -> None:
+    """y = rho*x + static causal conv of x with one filter per channel, c (D, W)."""
+    B, T, D = x.shape
+    W = c.shape[1]
+    cu, ns = _seq(cu_seqlens)
+    _check(lib().dsc_static_fwd(_stream(stream), _dtype_code(x), B, T, D, W, _ptr(x), _ptr(c), cu, ns,
+                                int(bool(residual)), _ptr(y)))
+
+
+def dsc_static_bwd(x, c, dy, dx, dc, *, cu_seqlens=None, residual=False, stream=None) -> None:
+    """dx (B,T,D) and dc (D, W) fp32 of the static conv."""
+    B, T, D = x.shape
+    W = c.shape[1]
+    cu, ns = _seq(cu_seqlens)
+    _check(lib().dsc_static_bwd(_stream(stream), _dtype_code(x), B, T, D, W, _ptr(x), _ptr(c), _ptr(dy),
+                                cu, ns, int(bool(residual)), _ptr(dx), _ptr(dc)))
 
 
 def dsc_abi_version() -> int:

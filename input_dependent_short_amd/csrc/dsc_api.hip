@@ -189,6 +189,47 @@ dsc_status dsc_lowrank_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_
     return launched(dsc::lowrank_bwd(p, (hipStream_t)stream), "dsc_lowrank_bwd launch");
 }
 
+dsc_status dsc_static_fwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                          const void *x, const void *c, const int32_t *cu_seqlens, int32_t n_seqs,
+                          int32_t residual, void *y) {
+    DSC_TRY(check_common(dtype, B, T, D, W, cu_seqlens, n_seqs, residual));
+    if (B * T == 0) return ok();  // empty batch: y has no elements
+    if (!x || !c || !y) return fail(DSC_ERR_NULL, "x, c and y are required");
+    if (!aligned16(x) || !aligned16(c) || !aligned16(y)) return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    const size_t es = esize(dtype), N = (size_t)(B * T);
+    const Range in[] = {rng("x", x, N * D * es), rng("c", c, (size_t)D * W * es),
+                        rng("cu_seqlens", cu_seqlens, cu_seqlens ? 4u * (n_seqs + 1) : 0)};
+    const Range out[] = {rng("y", y, N * D * es)};
+    DSC_TRY(check_alias(in, 3, out, 1));
+    const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
+    dsc::StProblem p{dt, B * T, T, D, W, x, c, nullptr, y, nullptr, nullptr, cu_seqlens, n_seqs, residual};
+    return launched(dsc::static_fwd(p, (hipStream_t)stream), "dsc_static_fwd launch");
+}
+
+dsc_status dsc_static_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                          const void *x, const void *c, const void *dy, const int32_t *cu_seqlens,
+                          int32_t n_seqs, int32_t residual, void *dx, float *dc) {
+    DSC_TRY(check_common(dtype, B, T, D, W, cu_seqlens, n_seqs, residual));
+    if (B * T == 0) {  // empty batch: dc is a sum over no tokens, zero; dx has no elements
+        if (!dc) return fail(DSC_ERR_NULL, "dc is required");
+        if (!aligned16(dc)) return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+        dsc::StProblem p{dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32, 0, T, D, W, nullptr, nullptr,
+                         nullptr, nullptr, nullptr, dc, nullptr, 0, residual};
+        return launched(dsc::static_bwd(p, (hipStream_t)stream), "dsc_static_bwd launch");
+    }
+    if (!x || !c || !dy || !dx || !dc) return fail(DSC_ERR_NULL, "x, c, dy, dx and dc are required");
+    if (!aligned16(x) || !aligned16(c) || !aligned16(dy) || !aligned16(dx) || !aligned16(dc))
+        return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    const size_t es = esize(dtype), N = (size_t)(B * T);
+    const Range in[] = {rng("x", x, N * D * es), rng("c", c, (size_t)D * W * es), rng("dy", dy, N * D * es),
+                        rng("cu_seqlens", cu_seqlens, cu_seqlens ? 4u * (n_seqs + 1) : 0)};
+    const Range out[] = {rng("dx", dx, N * D * es), rng("dc", dc, (size_t)D * W * 4)};
+    DSC_TRY(check_alias(in, 4, out, 2));
+    const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
+    dsc::StProblem p{dt, B * T, T, D, W, x, c, dy, nullptr, dx, dc, cu_seqlens, n_seqs, residual};
+    return launched(dsc::static_bwd(p, (hipStream_t)stream), "dsc_static_bwd launch");
+}
+
 const char *dsc_status_string(int status) {
     switch (status) {
         case DSC_SUCCESS: return "DSC_SUCCESS";

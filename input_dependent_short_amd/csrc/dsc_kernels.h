@@ -37,6 +37,19 @@ struct LrProblem {
     int32_t residual;
 };
 
+// Static short convolution: one filter per channel, the same at every token.
+struct StProblem {
+    Dtype dtype;
+    int64_t N, T, D;
+    int32_t W;
+    const void *x, *c, *dy;
+    void *y, *dx;
+    float *dc;
+    const int32_t *cu;
+    int32_t n_seqs;
+    int32_t residual;
+};
+
 // Head-wise: whether this build has a kernel for (dtype, H).
 bool headwise_supported(Dtype dt, int64_t D, int32_t H);
 
@@ -49,6 +62,11 @@ hipError_t lowrank_fwd(const LrProblem &p, hipStream_t s);
 // the other kernels, which then run instead.
 hipError_t lowrank_fwd_wide(const LrProblem &p, hipStream_t s, bool *used);
 hipError_t lowrank_bwd(const LrProblem &p, hipStream_t s);
+hipError_t static_fwd(const StProblem &p, hipStream_t s);
+// Zero-fills dc, then runs the backward (dx and the fp32 sums of dc); with
+// N = 0 only the zero-fill runs.
+hipError_t static_bwd(const StProblem &p, hipStream_t s);
+
 // Zero-fills n fp32 values (16-byte aligned); the backward of an empty batch.
 hipError_t lowrank_zero(float *p, int64_t n, hipStream_t s);
 

@@ -25,7 +25,7 @@ DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16}
 class Workload:
     """One benchmark / parity configuration."""
     name: str
-    kind: str            # "headwise" or "lowrank"
+    kind: str            # "headwise", "lowrank" or "static" (one fixed filter per channel)
     B: int
     T: int
     D: int
@@ -101,9 +101,10 @@ def packed_cu_seqlens(B: int, T: int, lo: int, hi: int, seed: int) -> np.ndarray
 def make_inputs(wl: Workload, *, cfg: int | None = None, seglen_seed_slot: int = 4) -> dict:
     """All inputs of a workload as CPU tensors in the workload dtype.
 
-    Keys: x (B,T,D), dy (B,T,D), and w (B,T,D/H,W) for head-wise or z (B,T,R)
-    and U (R, D*W) for low-rank; cu_seqlens (int32 numpy or None).
-    Scales: x, dy, z ~ N(0,1); w ~ N(0, 1/W); U ~ N(0, 1/(R*W)).
+    Keys: x (B,T,D), dy (B,T,D), and w (B,T,D/H,W) for head-wise, z (B,T,R)
+    and U (R, D*W) for low-rank, or c (D,W) for static; cu_seqlens (int32
+    numpy or None).
+    Scales: x, dy, z ~ N(0,1); w, c ~ N(0, 1/W); U ~ N(0, 1/(R*W)).
     """
     c = wl.cfg if cfg is None else cfg
     B, T, D, W = wl.B, wl.T, wl.D, wl.W
@@ -112,6 +113,8 @@ def make_inputs(wl: Workload, *, cfg: int | None = None, seglen_seed_slot: int =
     if wl.kind == "headwise":
         G = D // wl.H
         out["w"] = _cast(_normal(seed_for(c, 1), (B, T, G, W), float(1.0 / np.sqrt(W))), wl.dtype)
+    elif wl.kind == "static":
+        out["c"] = _cast(_normal(seed_for(c, 1), (D, W), float(1.0 / np.sqrt(W))), wl.dtype)
     else:
         R = wl.R
         out["z"] = _cast(_normal(seed_for(c, 1), (B, T, R), 1.0), wl.dtype)

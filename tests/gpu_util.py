@@ -93,3 +93,19 @@ def assert_close(name: str, gpu: np.ndarray, ref: np.ndarray, tol: float) -> flo
     say(f"    {name:4s} normwise err {err:.3e} (tol {tol:.0e})")
     assert err <= tol, f"{name}: normwise error {err:.3e} > {tol:.0e}"
     return err
+
+
+def run_static(inp: dict, residual: bool, *, guard=True, repeat_bwd: int = 1):
+    """Static conv forward and backward on the GPU; returns numpy fp64 (y, dx, dc)."""
+    x, c, dy = dev(inp["x"]), dev(inp["c"]), dev(inp["dy"])
+    cu = None if inp["cu_seqlens"] is None else torch.from_numpy(inp["cu_seqlens"]).cuda()
+    y, dx = Guarded(x.shape, x.dtype), Guarded(x.shape, x.dtype)
+    dc = Guarded(c.shape, torch.float32)
+    binding.dsc_static_fwd(x, c, y.t, cu_seqlens=cu, residual=residual)
+    for _ in range(repeat_bwd):
+        binding.dsc_static_bwd(x, c, dy, dx.t, dc.t, cu_seqlens=cu, residual=residual)
+    torch.cuda.synchronize()
+    if guard:
+        for name, g in (("y", y), ("dx", dx), ("dc", dc)):
+            g.check_guards(name)
+    return y.host(), dx.host(), dc.host()

@@ -29,8 +29,8 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     syms = set(declared_symbols())
     for s in ("dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd",
-              "dsc_lowrank_bwd_workspace_size", "dsc_status_string", "dsc_last_error",
-              "dsc_abi_version"):
+              "dsc_lowrank_bwd_workspace_size", "dsc_static_fwd", "dsc_static_bwd",
+              "dsc_status_string", "dsc_last_error", "dsc_abi_version"):
         assert s in syms
 
 
@@ -103,6 +103,34 @@ def test_lowrank_validation(lib):
     assert lr_bwd(lib, dz=None) == 1
 
 
+def st_fwd(lib, dtype=1, B=1, T=8, D=64, W=4, x=P(1), c=P(2), cu=None, ns=0, res=0, y=P(3)):
+    return lib.dsc_static_fwd(S0, dtype, B, T, D, W, x, c, cu, ns, res, y)
+
+
+def st_bwd(lib, dtype=1, B=1, T=8, D=64, W=4, x=P(1), c=P(2), dy=P(3), cu=None, ns=0, res=0,
+           dx=P(4), dc=P(5)):
+    return lib.dsc_static_bwd(S0, dtype, B, T, D, W, x, c, dy, cu, ns, res, dx, dc)
+
+
+def test_static_validation(lib):
+    assert st_fwd(lib, W=0) == 2
+    assert st_fwd(lib, W=9) == 2
+    assert st_fwd(lib, D=60) == 2                     # bf16 needs D % 8 == 0
+    assert st_fwd(lib, dtype=0, D=62) == 2            # fp32 needs D % 4 == 0
+    assert st_fwd(lib, dtype=2) == 3
+    assert st_fwd(lib, res=2) == 2
+    assert st_fwd(lib, c=None) == 1
+    assert st_fwd(lib, c=ctypes.c_void_p(A * 2 + 8)) == 4
+    assert st_fwd(lib, y=P(1)) == 5                  # y = x in place
+    assert st_fwd(lib, y=ctypes.c_void_p(A * 2 + 16)) == 5   # y overlaps c (D*W*2 = 512 bytes)
+    assert st_fwd(lib, cu=P(6), ns=0) == 2            # cu_seqlens and n_seqs disagree
+    assert st_bwd(lib, dc=None) == 1
+    assert st_bwd(lib, dx=P(3)) == 5                  # dx aliases dy
+    assert st_bwd(lib, dc=P(2)) == 5                  # dc aliases c
+    assert st_bwd(lib, dc=ctypes.c_void_p(A * 5 + 4)) == 4
+    assert st_bwd(lib, W=9) == 2
+
+
 def test_binding_raises_with_message(lib):
     import torch
     from input_dependent_short_amd import binding
@@ -122,3 +150,5 @@ def test_empty_batch_is_a_no_op(lib):
     assert lib.dsc_lowrank_fwd(S0, 1, 0, 8, 64, 4, 0, None, None, None, None, 0, 1, None) == 2  # R still checked
     assert lib.dsc_lowrank_bwd(S0, 1, 0, 8, 64, 4, 16, None, None, None, None, None, 0, 0,
                                None, None, None, None, 0) == 1   # dU is still required
+    assert st_fwd(lib, B=0, x=None, c=None, y=None) == 0
+    assert st_bwd(lib, T=0, x=None, c=None, dy=None, dx=None, dc=None) == 1   # dc is still required
