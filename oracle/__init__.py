@@ -51,8 +51,12 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
                                        p, p, i64, i64, p]
     lib.oracle_static_fwd.argtypes = [i64, i64, i64, i32, p, p, p, i32, i32, i64, i64, p]
     lib.oracle_static_bwd.argtypes = [i64, i64, i64, i32, p, p, p, p, i32, i32, i64, i64, p, p]
+    lib.oracle_headwise_decode.argtypes = [i64, i64, i32, i32, p, p, p, i32, p]
+    lib.oracle_lowrank_decode.argtypes = [i64, i64, i32, i32, p, p, p, p, i32, p]
+    lib.oracle_state_from_prefill.argtypes = [i64, i64, i64, i32, p, p, i32, p]
     for name in ("oracle_headwise_fwd", "oracle_headwise_bwd", "oracle_lowrank_fwd",
-                 "oracle_lowrank_bwd", "oracle_static_fwd", "oracle_static_bwd"):
+                 "oracle_lowrank_bwd", "oracle_static_fwd", "oracle_static_bwd",
+                 "oracle_headwise_decode", "oracle_lowrank_decode", "oracle_state_from_prefill"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -191,6 +195,43 @@ class Oracle:
                                           int(bool(residual)), lo, hi, _ptr(dx), _ptr(dc)), "static_bwd")
         return (dx.reshape(B, T, D) if rows is None else dx), dc
 
+    def headwise_decode(self, x, w, state, *, residual=False):
+        """One token per sequence: x (B,D), w (B,D/H,W), state (B,W-1,D) -> (y (B,D), new state)."""
+        x, w = _f64(x), _f64(w)
+        st = _f64(state).copy()
+        B, D = x.shape
+        G, W = w.shape[1], w.shape[2]
+        if G < 1 or D % G or st.shape != (B, W - 1, D):
+            raise ValueError("bad decode shapes")
+        y = np.empty((B, D))
+        _check(self.lib.oracle_headwise_decode(B, D, W, D // G, _ptr(x), _ptr(w), _ptr(st),
+                                               int(bool(residual)), _ptr(y)), "headwise_decode")
+        return y, st
+
+    def lowrank_decode(self, x, z, U, state, W, *, residual=False):
+        """x (B,D), z (B,R), U (R, D*W), state (B,W-1,D) -> (y (B,D), new state)."""
+        x, z, U = _f64(x), _f64(z), _f64(U)
+        st = _f64(state).copy()
+        B, D = x.shape
+        R = z.shape[1]
+        if U.shape != (R, D * W) or st.shape != (B, W - 1, D):
+            raise ValueError("bad decode shapes")
+        y = np.empty((B, D))
+        _check(self.lib.oracle_lowrank_decode(B, D, W, R, _ptr(x), _ptr(z), _ptr(U), _ptr(st),
+                                              int(bool(residual)), _ptr(y)), "lowrank_decode")
+        return y, st
+
+    def state_from_prefill(self, x, W, *, cu_seqlens=None):
+        """x (B,T,D) prefill inputs -> state (S, W-1, D) of every sequence's last W-1 tokens."""
+        x = _f64(x)
+        B, T, D = x.shape
+        cu, ns = _cu(cu_seqlens)
+        S = ns if cu is not None else B
+        st = np.empty((S, W - 1, D))
+        _check(self.lib.oracle_state_from_prefill(B, T, D, W, _ptr(x), _ptr(cu), ns, _ptr(st)),
+               "state_from_prefill")
+        return st
+
 
 def num_threads() -> int:
     """OpenMP threads the oracle uses."""
@@ -229,3 +270,15 @@ def static_fwd(*a, **k):
 
 def static_bwd(*a, **k):
     return default().static_bwd(*a, **k)
+
+
+def headwise_decode(*a, **k):
+    return default().headwise_decode(*a, **k)
+
+
+def lowrank_decode(*a, **k):
+    return default().lowrank_decode(*a, **k)
+
+
+def state_from_prefill(*a, **k):
+    return default().state_from_prefill(*a, **k)

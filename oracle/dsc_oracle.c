@@ -300,3 +300,82 @@ int oracle_static_bwd(int64_t B, int64_t T, int64_t D, int32_t W, const double *
     free(seg);
     return 0;
 }
+
+/* ---------------------------------------------------------------- decoding */
+
+/* One token per sequence at inference (the pages' inference remark: decoding
+ * needs its own path).  Sequence b carries a state of its last W-1 inputs,
+ * state[b, i, d] = x of its token t-1-i (i = 0 the most recent), zero for
+ * positions before the sequence's first token.  For the new token x[b, d]:
+ *   y[b,d] = rho*x[b,d] + w[b,j,0]*x[b,d] + sum_{k=1}^{W-1} w[b,j,k]*state[b,k-1,d]
+ * with j = d/H (head-wise; w is (B, D/H, W)), which is the forward of the
+ * sequence evaluated at its newest token.  The state then shifts:
+ *   state'[b,0,d] = x[b,d],  state'[b,i,d] = state[b,i-1,d] (i >= 1).
+ * state (B, W-1, D) is read and overwritten; y is (B, D).                  */
+int oracle_headwise_decode(int64_t B, int64_t D, int32_t W, int32_t H, const double *x, const double *w,
+                           double *state, int32_t residual, double *y)
+{
+    if (B < 1 || D < 1 || W < 1 || H < 1 || D % H) return -2;
+    const int64_t G = D / H;
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t d = 0; d < D; ++d) {
+            double acc = residual ? x[b * D + d] : 0.0;
+            for (int32_t k = 0; k < W; ++k) {
+                double xv = k == 0 ? x[b * D + d] : state[(b * (W - 1) + (k - 1)) * D + d];
+                acc += w[(b * G + d / H) * W + k] * xv;
+            }
+            y[b * D + d] = acc;
+        }
+        for (int32_t i = W - 2; i >= 1; --i)
+            for (int64_t d = 0; d < D; ++d)
+                state[(b * (W - 1) + i) * D + d] = state[(b * (W - 1) + i - 1) * D + d];
+        if (W > 1)
+            for (int64_t d = 0; d < D; ++d) state[(b * (W - 1)) * D + d] = x[b * D + d];
+    }
+    return 0;
+}
+
+/* Low-rank decode: as above with w[b,d,k] = sum_r z[b,r] * U[r, d*W+k]; z is (B, R). */
+int oracle_lowrank_decode(int64_t B, int64_t D, int32_t W, int32_t R, const double *x, const double *z,
+                          const double *U, double *state, int32_t residual, double *y)
+{
+    if (B < 1 || D < 1 || W < 1 || R < 1) return -2;
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t d = 0; d < D; ++d) {
+            double acc = residual ? x[b * D + d] : 0.0;
+            for (int32_t k = 0; k < W; ++k) {
+                double wk = 0.0;
+                for (int32_t r = 0; r < R; ++r) wk += z[b * R + r] * U[(int64_t)r * D * W + d * W + k];
+                double xv = k == 0 ? x[b * D + d] : state[(b * (W - 1) + (k - 1)) * D + d];
+                acc += wk * xv;
+            }
+            y[b * D + d] = acc;
+        }
+        for (int32_t i = W - 2; i >= 1; --i)
+            for (int64_t d = 0; d < D; ++d)
+                state[(b * (W - 1) + i) * D + d] = state[(b * (W - 1) + i - 1) * D + d];
+        if (W > 1)
+            for (int64_t d = 0; d < D; ++d) state[(b * (W - 1)) * D + d] = x[b * D + d];
+    }
+    return 0;
+}
+
+/* State after a prefill of packed sequences: for sequence s = [cu[s], cu[s+1])
+ * of the flattened x (B*T, D) (rows of T tokens without cu_seqlens),
+ *   state[s, i, d] = x[cu[s+1]-1-i, d] if cu[s+1]-1-i >= cu[s], else 0.
+ * state is (n_seqs or B, W-1, D).                                           */
+int oracle_state_from_prefill(int64_t B, int64_t T, int64_t D, int32_t W, const double *x,
+                              const int32_t *cu_seqlens, int32_t n_seqs, double *state)
+{
+    if (check_common(B, T, D, W, cu_seqlens, n_seqs, 0, 0)) return -2;
+    const int64_t S = (cu_seqlens && n_seqs > 0) ? n_seqs : B;
+    for (int64_t sq = 0; sq < S; ++sq) {
+        const int64_t lo = (cu_seqlens && n_seqs > 0) ? cu_seqlens[sq] : sq * T;
+        const int64_t hi = (cu_seqlens && n_seqs > 0) ? cu_seqlens[sq + 1] : (sq + 1) * T;
+        for (int32_t i = 0; i < W - 1; ++i) {
+            const int64_t t = hi - 1 - i;
+            for (int64_t d = 0; d < D; ++d) state[(sq * (W - 1) + i) * D + d] = t >= lo ? x[t * D + d] : 0.0;
+        }
+    }
+    return 0;
+}

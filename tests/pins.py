@@ -418,4 +418,53 @@ def pin_finite_differences_static(orc):
         _close(dc, _fd_grad(L, c), tol=1e-8, what="FD static dc")
 
 
+# ---------------------------------------------------------------- decoding
+# One token per sequence with a rolling state of the last W-1 inputs: the
+# step is the forward evaluated at the sequence's newest token.
+
+
+def pin_decode_reproduces_forward(orc):
+    """Decoding a sequence token by token from a zero state gives the forward at
+    every position (head-wise and low-rank), and leaves the prefill state."""
+    rng = _rng(18)
+    B, T, D, W, H, R = 3, 9, 8, 4, 2, 3
+    x, w, _ = _hw_case(rng, B, T, D, W, H)
+    xl, z, U, _ = _lr_case(rng, B, T, D, W, R)
+    for res in (False, True):
+        y = orc.headwise_fwd(x, w, residual=res)
+        yl = orc.lowrank_fwd(xl, z, U, W, residual=res)
+        st = np.zeros((B, W - 1, D))
+        stl = np.zeros((B, W - 1, D))
+        for t in range(T):
+            yt, st = orc.headwise_decode(x[:, t], w[:, t], st, residual=res)
+            _close(yt, y[:, t], what=f"head-wise decode t={t}")
+            ylt, stl = orc.lowrank_decode(xl[:, t], z[:, t], U, stl, W, residual=res)
+            _close(ylt, yl[:, t], what=f"low-rank decode t={t}")
+        _close(st, orc.state_from_prefill(x, W), what="state after decoding == prefill state")
+        _close(stl, orc.state_from_prefill(xl, W), what="low-rank state == prefill state")
+
+
+def pin_prefill_handoff(orc):
+    """Packed prefill (sequences of 1..6 tokens, some shorter than W-1), state
+    from the prefill, then decode steps: the same outputs as the forward over
+    the whole sequences."""
+    rng = _rng(19)
+    D, W, H, steps = 4, 5, 1, 3
+    lens = [1, 6, 2, 4]
+    S = len(lens)
+    full = [rng.standard_normal((L + steps, D)) for L in lens]
+    wf = [rng.standard_normal((L + steps, D // H, W)) for L in lens]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    xp = np.concatenate([f[:L] for f, L in zip(full, lens)])[None]
+    st = orc.state_from_prefill(xp, W, cu_seqlens=cu)
+    assert st.shape == (S, W - 1, D)
+    for j in range(steps):
+        xt = np.stack([f[L + j] for f, L in zip(full, lens)])
+        wt = np.stack([g[L + j] for g, L in zip(wf, lens)])
+        yt, st = orc.headwise_decode(xt, wt, st, residual=True)
+        for s_, (f, g, L) in enumerate(zip(full, wf, lens)):
+            want = orc.headwise_fwd(f[None, :L + j + 1], g[None, :L + j + 1], residual=True)[0, -1]
+            _close(yt[s_], want, what=f"hand-off sequence {s_} step {j}")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

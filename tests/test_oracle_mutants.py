@@ -27,7 +27,7 @@ MUTANTS = [
     ("dx_tap_of_m", "acc += w[(n * G + d / H) * W + k] * g[n * D + d];",
      "acc += w[(m * G + d / H) * W + k] * g[n * D + d];", 1),
     ("dw_unshifted", "acc += g[m * D + d] * x[(m - k) * D + d];", "acc += g[m * D + d] * x[m * D + d];", 1),
-    ("U_transposed", "U[(int64_t)r * D * W + d * W + k];", "U[(int64_t)r * D * W + k * D + d];", 1),
+    ("U_transposed", "U[(int64_t)r * D * W + d * W + k];", "U[(int64_t)r * D * W + k * D + d];", 2),
     ("lowrank_fwd_no_shift", "lowrank_filter(D, W, R, z, U, n, d, k) * x[(n - k) * D + d]",
      "lowrank_filter(D, W, R, z, U, n, d, k) * x[n * D + d]", 1),
     ("lowrank_dx_filter_at_m", "lowrank_filter(D, W, R, z, U, n, d, k) * g[n * D + d]",
@@ -45,6 +45,13 @@ MUTANTS = [
     ("static_dx_no_mask", "if (n < N && m >= seg[n]) acc += c[", "if (n < N) acc += c[", 1),
     ("static_dc_unshifted", "acc += g[n * D + d] * x[(n - k) * D + d];", "acc += g[n * D + d] * x[n * D + d];", 1),
     ("static_dc_no_mask", "if (n - k >= seg[n]) acc += g[", "if (n - k >= 0) acc += g[", 1),
+    ("decode_state_slot", "state[(b * (W - 1) + (k - 1)) * D + d];", "state[(b * (W - 1) + (W - 1 - k)) * D + d];", 2),
+    ("decode_no_shift", "state[(b * (W - 1) + i) * D + d] = state[(b * (W - 1) + i - 1) * D + d];",
+     "state[(b * (W - 1) + i) * D + d] = state[(b * (W - 1) + i) * D + d];", 2),
+    ("decode_lowrank_U_transposed", "wk += z[b * R + r] * U[(int64_t)r * D * W + d * W + k];",
+     "wk += z[b * R + r] * U[(int64_t)r * D * W + k * D + d];", 1),
+    ("prefill_off_by_one", "const int64_t t = hi - 1 - i;", "const int64_t t = hi - i;", 1),
+    ("prefill_pads_with_first_token", "= t >= lo ? x[t * D + d] : 0.0;", "= t >= lo ? x[t * D + d] : x[lo * D + d];", 1),
 ]
 
 
