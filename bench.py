@@ -12,8 +12,9 @@ the roofline of the dominant entry point (HIP events around each call on
 the stream it runs on), per-entry-point figures, the 2B-scale workloads
 (head-wise MLP D=8192 H=16 and low-rank varlen D=6144 R=64) timed the same
 way, the static short convolution (one fixed filter per channel) at the two
-head-wise shapes beside the dynamic figures, and the fp64 CPU oracle timed on
-a bounded sample of the step's work.
+head-wise shapes beside the dynamic figures, one-token decoding steps for 64
+sequences, and the fp64 CPU oracle timed on a bounded sample of the step's
+work.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -252,6 +253,8 @@ ENTRY_KERNELS = {
     "dsc_lowrank_bwd": (["lr_bwd_mfma", "lr_bwd_generic"], ["clear2", "fill_zero_f32", "cast_f32_bf16"]),
     "dsc_static_fwd": (["st_fwd_kernel"], []),
     "dsc_static_bwd": (["st_bwd_kernel"], ["st_zero"]),
+    "dsc_headwise_decode": (["hw_decode_kernel"], []),
+    "dsc_lowrank_decode": (["lr_decode_kernel"], []),
 }
 
 
@@ -466,6 +469,64 @@ def main() -> int:
                                "dynamic_headwise_fwd_us": dyn[0], "dynamic_headwise_bwd_us": dyn[1],
                                "dynamic_over_static": round((dyn[0] + dyn[1]) / ((tf + tb) * 1e6), 3)}
         out["static_vs_dynamic"] = static
+
+        # decoding: one new token for each of 64 sequences per step, at the QKV
+        # ~150M width (inputs are rows of the step's seeded tensors); the state
+        # is updated in place step after step.  us_per_step is a HIP graph of
+        # the steps replayed (GPU time); us_per_step_eager launches each step
+        # from Python (host-bound at this size)
+        S_DEC, STEPS_DEC = 64, 200
+        hwc, lrc = cases[0], cases[1]
+        D, Wd = hwc.wl.D, hwc.wl.W
+        xd = hwc.x.view(-1, D)[:S_DEC].contiguous()
+        wd = hwc.w.view(-1, D // hwc.wl.H, Wd)[:S_DEC].contiguous()
+        zd = lrc.z.view(-1, lrc.wl.R)[:S_DEC].contiguous()
+        yd = torch.empty_like(xd)
+        state = torch.zeros(S_DEC, Wd - 1, D, dtype=xd.dtype, device="cuda")
+        es = xd.element_size()
+        act = S_DEC * D * es
+        dec_calls = {
+            "headwise-qkv-150m": (lambda: binding.dsc_headwise_decode(xd, wd, state, yd, residual=True),
+                                  2 * act + 2 * (Wd - 1) * act + wd.numel() * es),
+            "lowrank-qkv-150m": (lambda: binding.dsc_lowrank_decode(xd, zd, lrc.U, state, yd, W=Wd),
+                                 2 * act + 2 * (Wd - 1) * act + zd.numel() * es + lrc.U.numel() * es),
+        }
+        dec = {}
+        for name, (fn, nbytes) in dec_calls.items():
+            for _ in range(10):
+                fn()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(STEPS_DEC):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            t_eager = a.elapsed_time(b) * 1e-3 / STEPS_DEC
+            # the same steps captured once as a HIP graph and replayed: the GPU's
+            # own time per step, without the host's per-call launch work
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                fn()
+            torch.cuda.current_stream().wait_stream(side)
+            with torch.cuda.graph(g):
+                for _ in range(STEPS_DEC):
+                    fn()
+            g.replay()
+            torch.cuda.synchronize()
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) * 1e-3 / STEPS_DEC
+            dec[name] = {"sequences": S_DEC, "us_per_step": round(t * 1e6, 2),
+                         "us_per_step_eager": round(t_eager * 1e6, 2),
+                         "tokens_per_s": round(S_DEC / t, 1), "bytes_per_step": nbytes,
+                         "GBps": round(nbytes / t / 1e9, 1)}
+            del g
+        out["decode"] = dec
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline([cases[0].wl, cases[1].wl], args.cpu_seconds)

@@ -48,9 +48,10 @@
  *   pointers    DEVICE pointers, each 16-byte aligned.  The caller owns all
  *               memory; the library allocates nothing, keeps no state and
  *               is thread-safe.  Inputs are never written.  Every output is
- *               fully overwritten (nothing accumulates into it).  No output
- *               may overlap an input or another output (so y = x in place
- *               is rejected).
+ *               fully overwritten (nothing accumulates into it), except the
+ *               decoding state, which is updated in place.  No output may
+ *               overlap an input or another output (so y = x in place is
+ *               rejected).
  *
  * Errors: each entry point checks every host-checkable precondition first
  * and returns a status without making any HIP call when one fails; a failed
@@ -188,6 +189,45 @@ DSC_API dsc_status dsc_static_fwd(void *stream, int dtype, int64_t B, int64_t T,
 DSC_API dsc_status dsc_static_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
                           const void *x, const void *c, const void *dy, const int32_t *cu_seqlens,
                           int32_t n_seqs, int32_t residual, void *dx, float *dc);
+
+/*
+ * Decoding: one new token per sequence, B sequences, with a rolling state.
+ * The authors note that inference needs engineering of its own (gist.science
+ * technical summary, Significado y Reivindicaciones).  The step is the
+ * forward above evaluated at each sequence's newest token:
+ *   y[b,d] = rho*x[b,d] + w(b)_{d,0}*x[b,d] + sum_{k=1}^{W-1} w(b)_{d,k}*state[b,k-1,d]
+ * then the state shifts by one token:
+ *   state[b,0,d] <- x[b,d],  state[b,i,d] <- state[b,i-1,d] (i >= 1).
+ *
+ *   state (B, W-1, D) dtype, read and then overwritten in place (the one
+ *         in/out argument of the library): state[b,i,d] is the input of token
+ *         t-1-i of sequence b, zero before the sequence's first token.  A new
+ *         sequence starts from zeros; a prefill hands over its last W-1
+ *         inputs with dsc_state_from_prefill.  NULL when W = 1 (no slots).
+ *   x, y (B, D) dtype.  D multiple of 8 (bf16) / 4 (fp32).  B may be 0;
+ *         B*D < 2^31.
+ *   No argument may overlap another (state is not an alias of x or y).
+ */
+
+/* Head-wise decoding step: w (B, D/H, W), w(b)_{d,k} = w[b, d/H, k].
+ * H divides 8 (bf16) / 4 (fp32) or is a multiple of it; others return
+ * DSC_ERR_UNSUPPORTED. */
+DSC_API dsc_status dsc_headwise_decode(void *stream, int dtype, int64_t B, int64_t D, int32_t W, int32_t H,
+                               const void *x, const void *w, void *state, int32_t residual, void *y);
+
+/* Low-rank decoding step: z (B, R), U (R, D*W), w(b)_{d,k} = sum_r z[b,r] U[r, d*W+k]
+ * formed on chip.  1 <= R <= 128. */
+DSC_API dsc_status dsc_lowrank_decode(void *stream, int dtype, int64_t B, int64_t D, int32_t W, int32_t R,
+                              const void *x, const void *z, const void *U, void *state, int32_t residual,
+                              void *y);
+
+/* State after a prefill: for every sequence s of the (B,T,D) inputs x (rows,
+ * or the cu_seqlens sequences as above), state[s,i,d] = x of the sequence's
+ * token end-1-i, or 0 when the sequence has fewer than i+1 tokens.  state is
+ * (S, W-1, D) with S = n_seqs (or B without cu_seqlens); nothing is written
+ * when W = 1 or B*T = 0. */
+DSC_API dsc_status dsc_state_from_prefill(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                                  const void *x, const int32_t *cu_seqlens, int32_t n_seqs, void *state);
 
 /* Static name of a status code. */
 DSC_API const char *dsc_status_string(int status);

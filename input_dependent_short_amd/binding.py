@@ -44,8 +44,12 @@ def lib() -> ctypes.CDLL:
                                       p, ctypes.c_size_t]
         L.dsc_static_fwd.argtypes = [p, i, i64, i64, i64, i32, p, p, p, i32, i32, p]
         L.dsc_static_bwd.argtypes = [p, i, i64, i64, i64, i32, p, p, p, p, i32, i32, p, p]
+        L.dsc_headwise_decode.argtypes = [p, i, i64, i64, i32, i32, p, p, p, i32, p]
+        L.dsc_lowrank_decode.argtypes = [p, i, i64, i64, i32, i32, p, p, p, p, i32, p]
+        L.dsc_state_from_prefill.argtypes = [p, i, i64, i64, i64, i32, p, p, i32, p]
         for f in ("dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd",
-                  "dsc_static_fwd", "dsc_static_bwd", "dsc_abi_version"):
+                  "dsc_static_fwd", "dsc_static_bwd", "dsc_headwise_decode", "dsc_lowrank_decode",
+                  "dsc_state_from_prefill", "dsc_abi_version"):
             getattr(L, f).restype = ctypes.c_int
         L.dsc_status_string.argtypes = [i]
         L.dsc_status_string.restype = ctypes.c_char_p
@@ -148,6 +152,30 @@ def dsc_static_bwd(x, c, dy, dx, dc, *, cu_seqlens=None, residual=False, stream=
     cu, ns = _seq(cu_seqlens)
     _check(lib().dsc_static_bwd(_stream(stream), _dtype_code(x), B, T, D, W, _ptr(x), _ptr(c), _ptr(dy),
                                 cu, ns, int(bool(residual)), _ptr(dx), _ptr(dc)))
+
+
+def dsc_headwise_decode(x, w, state, y, *, residual=False, stream=None) -> None:
+    """One token per sequence: x (B,D), w (B,D/H,W), state (B,W-1,D) updated in place, y (B,D)."""
+    B, D = x.shape
+    G, W = w.shape[1], w.shape[2]
+    _check(lib().dsc_headwise_decode(_stream(stream), _dtype_code(x), B, D, W, D // G if G else 0, _ptr(x),
+                                     _ptr(w), _ptr(state), int(bool(residual)), _ptr(y)))
+
+
+def dsc_lowrank_decode(x, z, U, state, y, *, W, residual=False, stream=None) -> None:
+    """One token per sequence: x (B,D), z (B,R), U (R, D*W), state (B,W-1,D) updated in place."""
+    B, D = x.shape
+    R = z.shape[1]
+    _check(lib().dsc_lowrank_decode(_stream(stream), _dtype_code(x), B, D, W, R, _ptr(x), _ptr(z), _ptr(U),
+                                    _ptr(state), int(bool(residual)), _ptr(y)))
+
+
+def dsc_state_from_prefill(x, state, *, W, cu_seqlens=None, stream=None) -> None:
+    """state (S, W-1, D) <- the last W-1 inputs of every sequence of x (B,T,D)."""
+    B, T, D = x.shape
+    cu, ns = _seq(cu_seqlens)
+    _check(lib().dsc_state_from_prefill(_stream(stream), _dtype_code(x), B, T, D, W, _ptr(x), cu, ns,
+                                        _ptr(state)))
 
 
 def dsc_abi_version() -> int:

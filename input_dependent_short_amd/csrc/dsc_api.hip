@@ -230,6 +230,77 @@ dsc_status dsc_static_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_t
     return launched(dsc::static_bwd(p, (hipStream_t)stream), "dsc_static_bwd launch");
 }
 
+namespace {
+
+// Shared checks of the two decoding steps (B sequences, one token each).
+dsc_status check_decode(int dtype, int64_t B, int64_t D, int32_t W, int32_t residual) {
+    if (dtype != DSC_FP32 && dtype != DSC_BF16) return fail(DSC_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+    if (B < 0 || D < 1 || D > ((int64_t)1 << 24) || B * D >= ((int64_t)1 << 31))
+        return fail(DSC_ERR_SHAPE, "B >= 0, D in 1..2^24 and B*D < 2^31 required (got %lld, %lld)", (long long)B,
+                    (long long)D);
+    if (W < 1 || W > 8) return fail(DSC_ERR_SHAPE, "W must be in 1..8 (got %d)", W);
+    const int vec = dtype == DSC_BF16 ? 8 : 4;
+    if (D % vec) return fail(DSC_ERR_SHAPE, "D = %lld must be a multiple of %d for this dtype", (long long)D, vec);
+    if (residual != 0 && residual != 1) return fail(DSC_ERR_SHAPE, "residual must be 0 or 1");
+    return DSC_SUCCESS;
+}
+
+}  // namespace
+
+dsc_status dsc_headwise_decode(void *stream, int dtype, int64_t B, int64_t D, int32_t W, int32_t H,
+                               const void *x, const void *w, void *state, int32_t residual, void *y) {
+    DSC_TRY(check_decode(dtype, B, D, W, residual));
+    if (H < 1 || D % H) return fail(DSC_ERR_SHAPE, "H = %d must divide D = %lld", H, (long long)D);
+    const int vec = dtype == DSC_BF16 ? 8 : 4;
+    if (H < vec ? vec % H != 0 : H % vec != 0) return fail(DSC_ERR_UNSUPPORTED, "H = %d not supported", H);
+    if (B == 0) return ok();
+    if (!x || !w || !y || (W > 1 && !state)) return fail(DSC_ERR_NULL, "x, w, y and (W > 1) state are required");
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y) || !aligned16(state))
+        return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    const size_t es = esize(dtype), Bs = (size_t)B;
+    const Range in[] = {rng("x", x, Bs * D * es), rng("w", w, Bs * (D / H) * W * es)};
+    const Range out[] = {rng("y", y, Bs * D * es), rng("state", state, W > 1 ? Bs * (W - 1) * D * es : 0)};
+    DSC_TRY(check_alias(in, 2, out, 2));
+    const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
+    dsc::DecProblem p{dt, B, D, W, H, 0, false, x, w, nullptr, nullptr, state, y, residual};
+    return launched(dsc::decode_step(p, (hipStream_t)stream), "dsc_headwise_decode launch");
+}
+
+dsc_status dsc_lowrank_decode(void *stream, int dtype, int64_t B, int64_t D, int32_t W, int32_t R,
+                              const void *x, const void *z, const void *U, void *state, int32_t residual,
+                              void *y) {
+    DSC_TRY(check_decode(dtype, B, D, W, residual));
+    if (R < 1 || R > 128) return fail(DSC_ERR_SHAPE, "R = %d must be in 1..128", R);
+    if (B == 0) return ok();
+    if (!x || !z || !U || !y || (W > 1 && !state))
+        return fail(DSC_ERR_NULL, "x, z, U, y and (W > 1) state are required");
+    if (!aligned16(x) || !aligned16(z) || !aligned16(U) || !aligned16(y) || !aligned16(state))
+        return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    const size_t es = esize(dtype), Bs = (size_t)B;
+    const Range in[] = {rng("x", x, Bs * D * es), rng("z", z, Bs * R * es), rng("U", U, (size_t)R * D * W * es)};
+    const Range out[] = {rng("y", y, Bs * D * es), rng("state", state, W > 1 ? Bs * (W - 1) * D * es : 0)};
+    DSC_TRY(check_alias(in, 3, out, 2));
+    const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
+    dsc::DecProblem p{dt, B, D, W, 0, R, true, x, nullptr, z, U, state, y, residual};
+    return launched(dsc::decode_step(p, (hipStream_t)stream), "dsc_lowrank_decode launch");
+}
+
+dsc_status dsc_state_from_prefill(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                                  const void *x, const int32_t *cu_seqlens, int32_t n_seqs, void *state) {
+    DSC_TRY(check_common(dtype, B, T, D, W, cu_seqlens, n_seqs, 0));
+    if (B * T == 0 || W == 1) return ok();  // no sequences, or a state without slots
+    if (!x || !state) return fail(DSC_ERR_NULL, "x and state are required");
+    if (!aligned16(x) || !aligned16(state)) return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    const size_t es = esize(dtype), N = (size_t)(B * T);
+    const size_t nseq = cu_seqlens ? (size_t)n_seqs : (size_t)B;
+    const Range in[] = {rng("x", x, N * D * es), rng("cu_seqlens", cu_seqlens, cu_seqlens ? 4u * (n_seqs + 1) : 0)};
+    const Range out[] = {rng("state", state, nseq * (W - 1) * D * es)};
+    DSC_TRY(check_alias(in, 2, out, 1));
+    const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
+    return launched(dsc::state_from_prefill(dt, x, cu_seqlens, n_seqs, B, T, D, W, state, (hipStream_t)stream),
+                    "dsc_state_from_prefill launch");
+}
+
 const char *dsc_status_string(int status) {
     switch (status) {
         case DSC_SUCCESS: return "DSC_SUCCESS";

@@ -50,6 +50,17 @@ struct StProblem {
     int32_t residual;
 };
 
+// One decoding step (one token per sequence) with a rolling state.
+struct DecProblem {
+    Dtype dtype;
+    int64_t B, D;
+    int32_t W, H, R;
+    bool lowrank;
+    const void *x, *w, *z, *U;
+    void *state, *y;
+    int32_t residual;
+};
+
 // Head-wise: whether this build has a kernel for (dtype, H).
 bool headwise_supported(Dtype dt, int64_t D, int32_t H);
 
@@ -66,6 +77,11 @@ hipError_t static_fwd(const StProblem &p, hipStream_t s);
 // Zero-fills dc, then runs the backward (dx and the fp32 sums of dc); with
 // N = 0 only the zero-fill runs.
 hipError_t static_bwd(const StProblem &p, hipStream_t s);
+
+hipError_t decode_step(const DecProblem &p, hipStream_t s);
+// Last W-1 inputs of every sequence of a prefill into the state (S, W-1, D).
+hipError_t state_from_prefill(Dtype dt, const void *x, const int32_t *cu, int32_t n_seqs, int64_t B, int64_t T,
+                              int64_t D, int32_t W, void *state, hipStream_t s);
 
 // Zero-fills n fp32 values (16-byte aligned); the backward of an empty batch.
 hipError_t lowrank_zero(float *p, int64_t n, hipStream_t s);

@@ -30,6 +30,7 @@ def test_header_declares_the_entry_points():
     syms = set(declared_symbols())
     for s in ("dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd",
               "dsc_lowrank_bwd_workspace_size", "dsc_static_fwd", "dsc_static_bwd",
+              "dsc_headwise_decode", "dsc_lowrank_decode", "dsc_state_from_prefill",
               "dsc_status_string", "dsc_last_error", "dsc_abi_version"):
         assert s in syms
 
@@ -129,6 +130,29 @@ def test_static_validation(lib):
     assert st_bwd(lib, dc=P(2)) == 5                  # dc aliases c
     assert st_bwd(lib, dc=ctypes.c_void_p(A * 5 + 4)) == 4
     assert st_bwd(lib, W=9) == 2
+
+
+def test_decode_validation(lib):
+    hd = lambda dt=1, B=4, D=64, W=4, H=8, x=P(1), w=P(2), st=P(3), res=0, y=P(4): \
+        lib.dsc_headwise_decode(S0, dt, B, D, W, H, x, w, st, res, y)
+    ld = lambda dt=1, B=4, D=64, W=4, R=16, x=P(1), z=P(2), U=P(3), st=P(4), res=0, y=P(5): \
+        lib.dsc_lowrank_decode(S0, dt, B, D, W, R, x, z, U, st, res, y)
+    assert hd(W=0) == 2 and hd(W=9) == 2 and hd(D=60) == 2 and hd(H=3) == 2
+    assert hd(H=12, D=96) == 3                      # a chunk of 8 channels would span two filters
+    assert hd(st=None) == 1
+    assert hd(st=P(1)) == 5                         # state overlaps x
+    assert hd(y=P(3)) == 5                          # y overlaps the state
+    assert hd(x=ctypes.c_void_p(A + 8)) == 4
+    assert hd(B=-1) == 2
+    assert hd(B=0, x=None, w=None, st=None, y=None) == 0
+    assert ld(R=0) == 2 and ld(R=129) == 2
+    assert ld(U=None) == 1
+    assert ld(st=P(3)) == 5                         # state overlaps U
+    sp = lambda B=1, T=8, D=64, W=4, x=P(1), cu=None, ns=0, st=P(2): \
+        lib.dsc_state_from_prefill(S0, 1, B, T, D, W, x, cu, ns, st)
+    assert sp(W=9) == 2 and sp(st=None) == 1 and sp(st=P(1)) == 5
+    assert sp(W=1, st=None) == 0                    # no slots: nothing to write
+    assert sp(B=0, x=None, st=None) == 0
 
 
 def test_binding_raises_with_message(lib):
