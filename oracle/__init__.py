@@ -34,7 +34,7 @@ _lib = None
 def build(out_path: str = LIB_PATH, extra_flags: tuple[str, ...] = ()) -> str:
     """Compile the oracle with gcc (-O2, OpenMP).  Returns the library path."""
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", *extra_flags,
-           _SRC, "-o", out_path + ".tmp"]
+           _SRC, "-o", out_path + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(out_path + ".tmp", out_path)
     return out_path
@@ -54,9 +54,12 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_headwise_decode.argtypes = [i64, i64, i32, i32, p, p, p, i32, p]
     lib.oracle_lowrank_decode.argtypes = [i64, i64, i32, i32, p, p, p, p, i32, p]
     lib.oracle_state_from_prefill.argtypes = [i64, i64, i64, i32, p, p, i32, p]
+    lib.oracle_rope_table.argtypes = [i64, i32, ctypes.c_double, p]
+    lib.oracle_rope.argtypes = [i64, i64, i64, i64, i32, ctypes.c_double, p, i32, i32, i64, i64, p, p]
     for name in ("oracle_headwise_fwd", "oracle_headwise_bwd", "oracle_lowrank_fwd",
                  "oracle_lowrank_bwd", "oracle_static_fwd", "oracle_static_bwd",
-                 "oracle_headwise_decode", "oracle_lowrank_decode", "oracle_state_from_prefill"):
+                 "oracle_headwise_decode", "oracle_lowrank_decode", "oracle_state_from_prefill",
+                 "oracle_rope_table", "oracle_rope"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -232,6 +235,54 @@ class Oracle:
                "state_from_prefill")
         return st
 
+    # ------------------------------------------------------------------ RoPE
+    # The rotation follows "RoFormer: Enhanced Transformer with Rotary Position
+    # Embedding" (Su et al.), Section 3.4.2; the layer sits right before it on
+    # the query and key projections (pages: Methodology, placement).
+
+    def rope_table(self, max_pos, head_dim, base=10000.0):
+        """-> (max_pos, head_dim/2, 2): cos and sin of m * base^(-2i/head_dim)."""
+        t = np.empty((max_pos, head_dim // 2, 2))
+        _check(self.lib.oracle_rope_table(max_pos, head_dim, float(base), _ptr(t)), "rope_table")
+        return t
+
+    def rope(self, v, *, rot, head_dim, base=10000.0, cu_seqlens=None, inverse=False, rows=None,
+             shape=None):
+        """Rotate channels [0, rot) of every row (pairs 2i, 2i+1 of each head of
+        head_dim channels) by position-in-sequence times base^(-2i/head_dim).
+        v is (B,T,D), or with rows=(lo, hi) and shape=(B, T) the compact rows
+        (hi-lo, D).  inverse=True applies the transposed rotation."""
+        v = _f64(v)
+        if rows is None:
+            B, T, D = v.shape
+            lo, hi = 0, B * T
+        else:
+            (B, T), (lo, hi) = shape, rows
+            D = v.shape[-1]
+            if v.shape != (hi - lo, D):
+                raise ValueError(f"rows {rows} do not match {v.shape}")
+        cu, ns = _cu(cu_seqlens)
+        out = np.empty_like(v)
+        _check(self.lib.oracle_rope(B, T, D, int(rot), int(head_dim), float(base), _ptr(cu), ns,
+                                    int(bool(inverse)), lo, hi, _ptr(v), _ptr(out)), "rope")
+        return out
+
+    def headwise_rope_fwd(self, x, w, *, rot, head_dim, base=10000.0, cu_seqlens=None,
+                          residual=False, rows=None):
+        """RoPE(rho*x + conv(x)): the head-wise layer, then the rotation of its
+        first rot channels."""
+        y = self.headwise_fwd(x, w, cu_seqlens=cu_seqlens, residual=residual, rows=rows)
+        B, T, _ = np.shape(x)
+        return self.rope(y, rot=rot, head_dim=head_dim, base=base, cu_seqlens=cu_seqlens, rows=rows,
+                         shape=(B, T))
+
+    def headwise_rope_bwd(self, x, w, dy, *, rot, head_dim, base=10000.0, cu_seqlens=None,
+                          residual=False, rows=None):
+        """-> (dx, dw).  The rotation is orthogonal and comes last, so the
+        layer's output gradient is the transposed rotation of dy."""
+        ds = self.rope(dy, rot=rot, head_dim=head_dim, base=base, cu_seqlens=cu_seqlens, inverse=True)
+        return self.headwise_bwd(x, w, ds, cu_seqlens=cu_seqlens, residual=residual, rows=rows)
+
 
 def num_threads() -> int:
     """OpenMP threads the oracle uses."""
@@ -282,3 +333,19 @@ def lowrank_decode(*a, **k):
 
 def state_from_prefill(*a, **k):
     return default().state_from_prefill(*a, **k)
+
+
+def rope_table(*a, **k):
+    return default().rope_table(*a, **k)
+
+
+def rope(*a, **k):
+    return default().rope(*a, **k)
+
+
+def headwise_rope_fwd(*a, **k):
+    return default().headwise_rope_fwd(*a, **k)
+
+
+def headwise_rope_bwd(*a, **k):
+    return default().headwise_rope_bwd(*a, **k)

@@ -20,7 +20,9 @@
  * training efficiency", digg.com): the static short convolution being
  * generalised is depthwise and causal, so x before a sequence start is zero.
  * That static layer itself (one filter per channel, the same at every
- * position) is the last pair of functions below.
+ * position) is the next pair of functions below, followed by the decoding
+ * step and, last, the rotary position embedding that the placement puts
+ * right after the layer on the query and key projections.
  *
  * Readings where the pages are silent (each listed in the design notes):
  *   - tap k = 0 multiplies the current token x_t;
@@ -42,6 +44,7 @@
  * stored compactly (row n goes to row n - n_lo of the output); dU covers
  * channels [d_lo, d_hi) only, stored as (R, (d_hi-d_lo)*W).
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #ifdef _OPENMP
@@ -377,5 +380,65 @@ int oracle_state_from_prefill(int64_t B, int64_t T, int64_t D, int32_t W, const 
             for (int64_t d = 0; d < D; ++d) state[(sq * (W - 1) + i) * D + d] = t >= lo ? x[t * D + d] : 0.0;
         }
     }
+    return 0;
+}
+
+/* ------------------------------------------------------- rotary positions */
+/*
+ * The placement in the pages applies the layer (with its residual) to the
+ * query, key and value projections before the rotary position embedding
+ * (Methodology, placement).  The rotation itself is not defined there; it is
+ * taken from "RoFormer: Enhanced Transformer with Rotary Position Embedding"
+ * (Su et al.), Section 3.4.2, general form: a head vector of even dimension
+ * hd is split into hd/2 pairs of neighbouring channels (2i, 2i+1), and at
+ * position m pair i turns by the angle m * theta_i, theta_i = base^(-2i/hd).
+ * Readings: the rotated channels are the first `rot` channels of a row
+ * (query heads then key heads, hd channels each; rot a multiple of hd); the
+ * remaining channels (values) pass unchanged; the position m of a token is
+ * its index inside its own sequence (0 at each sequence start).
+ */
+
+/* table[(m*(hd/2) + i)*2 + 0] = cos(m * theta_i), table[... + 1] = sin(m * theta_i)
+ * for positions m < max_pos. */
+int oracle_rope_table(int64_t max_pos, int32_t hd, double base, double *table)
+{
+    if (max_pos < 0 || hd < 2 || hd % 2 || !(base > 0.0)) return -2;
+    for (int64_t m = 0; m < max_pos; ++m)
+        for (int32_t i = 0; i < hd / 2; ++i) {
+            const double ang = (double)m * pow(base, -2.0 * i / hd);
+            table[(m * (hd / 2) + i) * 2 + 0] = cos(ang);
+            table[(m * (hd / 2) + i) * 2 + 1] = sin(ang);
+        }
+    return 0;
+}
+
+/* Rows [n_lo, n_hi) of v (stored compactly, row n at n - n_lo) rotated into
+ * out.  inverse != 0 turns every pair by the opposite angle: the transpose of
+ * the rotation, which is what the chain rule applies to an output gradient. */
+int oracle_rope(int64_t B, int64_t T, int64_t D, int64_t rot, int32_t hd, double base,
+                const int32_t *cu_seqlens, int32_t n_seqs, int32_t inverse,
+                int64_t n_lo, int64_t n_hi, const double *v, double *out)
+{
+    if (check_common(B, T, D, 1, cu_seqlens, n_seqs, n_lo, n_hi)) return -2;
+    if (hd < 2 || hd % 2 || rot < 0 || rot > D || rot % hd || !(base > 0.0)) return -2;
+    int64_t *seg = segment_starts(B, T, cu_seqlens, n_seqs);
+    if (!seg) return -1;
+    const double sign = inverse ? -1.0 : 1.0;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = n_lo; n < n_hi; ++n) {
+        const double m = (double)(n - seg[n]);
+        const double *a = v + (n - n_lo) * D;
+        double *b = out + (n - n_lo) * D;
+        for (int64_t d = rot; d < D; ++d) b[d] = a[d];
+        for (int64_t h = 0; h < rot; h += hd)
+            for (int32_t i = 0; i < hd / 2; ++i) {
+                const double ang = sign * m * pow(base, -2.0 * i / hd);
+                const double c = cos(ang), s = sin(ang);
+                const double p = a[h + 2 * i], q = a[h + 2 * i + 1];
+                b[h + 2 * i] = p * c - q * s;
+                b[h + 2 * i + 1] = q * c + p * s;
+            }
+    }
+    free(seg);
     return 0;
 }

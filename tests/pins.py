@@ -467,4 +467,92 @@ def pin_prefill_handoff(orc):
             _close(yt[s_], want, what=f"hand-off sequence {s_} step {j}")
 
 
+# --------------------------------------------------------- rotary positions
+# The rotation that the placement puts right after the layer on queries and
+# keys is RoFormer's ("RoFormer: Enhanced Transformer with Rotary Position
+# Embedding", Su et al., Section 3.4.2): pair i = channels (2i, 2i+1) of a head
+# of hd channels turns by m * theta_i at position m, theta_i = base^(-2i/hd).
+
+# cos and sin of 1, 2 and 10 radians (standard tables, 17 significant digits)
+_COS1, _SIN1 = 0.54030230586813972, 0.84147098480789651
+_COS2, _SIN2 = -0.41614683654714239, 0.90929742682568170
+_COS10, _SIN10 = -0.83907152907645245, -0.54402111088936981
+
+
+def pin_rope_worked_values(orc):
+    """Unit vectors through the rotation at positions whose angles are whole
+    radians, and the cos / sin table at the same points."""
+    # head_dim 2: theta_0 = 1 for any base, so position m turns by m radians
+    for e, want in ((0, [[1, 0], [_COS1, _SIN1], [_COS2, _SIN2]]),
+                    (1, [[0, 1], [-_SIN1, _COS1], [-_SIN2, _COS2]])):
+        v = np.zeros((1, 3, 2))
+        v[0, :, e] = 1.0
+        _close(orc.rope(v, rot=2, head_dim=2, base=5.0)[0], want, what=f"head_dim 2, unit vector {e}")
+    # head_dim 4, base 100: theta_0 = 1 and theta_1 = 100^(-1/2) = 0.1, so at
+    # position 10 pair 0 turns by 10 rad and pair 1 by 1 rad.  Two rotated
+    # heads (channels 0..7), then one value channel that passes unchanged.
+    v = np.zeros((1, 11, 9))
+    v[0, :, 0] = 1.0  # head 0, pair 0
+    v[0, :, 6] = 1.0  # head 1, pair 1
+    v[0, :, 8] = 3.0
+    out = orc.rope(v, rot=8, head_dim=4, base=100.0)[0, 10]
+    _close(out, [_COS10, _SIN10, 0, 0, 0, 0, _COS1, _SIN1, 3.0], what="head_dim 4, base 100, position 10")
+    _close(orc.rope_table(3, 2, base=7.0)[:, 0], [[1, 0], [_COS1, _SIN1], [_COS2, _SIN2]], what="table, head_dim 2")
+    _close(orc.rope_table(11, 4, base=100.0)[10], [[_COS10, _SIN10], [_COS1, _SIN1]], what="table, head_dim 4")
+
+
+def pin_rope_relative_positions(orc):
+    """RoFormer's defining property: the inner product of a rotated query at
+    position m and a rotated key at position n depends on m - n only; and the
+    rotation keeps the norm of every head."""
+    rng = _rng(20)
+    hd, heads, T = 8, 2, 12
+    q, k = rng.standard_normal(heads * hd), rng.standard_normal(heads * hd)
+    v = np.tile(np.concatenate([q, k]), (1, T, 1))  # every token holds the same q and k
+    r = orc.rope(v, rot=2 * heads * hd, head_dim=hd, base=50.0)[0]
+    rq, rk = r[:, :heads * hd], r[:, heads * hd:]
+    for m, n in ((2, 0), (5, 7), (4, 4), (0, 9)):
+        for shift in (1, 2):
+            assert abs(rq[m] @ rk[n] - rq[m + shift] @ rk[n + shift]) <= 1e-12 * (abs(q) @ abs(k)), \
+                f"<q_m, k_n> changed under a common shift of m={m}, n={n}"
+    _close(rq[3] @ rk[3], q @ k, what="equal positions give the unrotated product")
+    _close(np.linalg.norm(r.reshape(T, -1, hd), axis=-1), np.linalg.norm(v[0].reshape(T, -1, hd), axis=-1),
+           what="head norms")
+
+
+def pin_rope_segments_inverse_passthrough(orc):
+    """Positions restart at every packed sequence (packed rows equal each
+    sequence rotated alone); channels from rot on pass unchanged; the inverse
+    undoes the rotation; compact row ranges match the full result."""
+    rng = _rng(21)
+    B, T, D, hd, rot = 2, 7, 20, 4, 12
+    cu = [0, 3, 7, 14]
+    x = rng.standard_normal((B, T, D))
+    r = orc.rope(x, rot=rot, head_dim=hd, base=9.0, cu_seqlens=cu)
+    flat, xf = r.reshape(B * T, D), x.reshape(B * T, D)
+    for a, b in zip(cu[:-1], cu[1:]):
+        _close(flat[a:b], orc.rope(xf[None, a:b], rot=rot, head_dim=hd, base=9.0)[0], what=f"segment [{a},{b})")
+    _close(r[..., rot:], x[..., rot:], what="channels past rot")
+    _close(orc.rope(r, rot=rot, head_dim=hd, base=9.0, cu_seqlens=cu, inverse=True), x, what="inverse")
+    part = orc.rope(xf[5:11], rot=rot, head_dim=hd, base=9.0, cu_seqlens=cu, rows=(5, 11), shape=(B, T))
+    _close(part, flat[5:11], what="row range")
+
+
+def pin_rope_layer_composition(orc):
+    """rot = 0 leaves the head-wise layer unchanged; the fused layer's
+    gradients equal exact central finite differences of L = <g, y>."""
+    rng = _rng(22)
+    B, T, D, W, H, hd = 2, 5, 8, 3, 2, 4
+    cu = [0, 3, 5, 10]
+    x, w, g = _hw_case(rng, B, T, D, W, H)
+    _close(orc.headwise_rope_fwd(x, w, rot=0, head_dim=hd, residual=True, cu_seqlens=cu),
+           orc.headwise_fwd(x, w, residual=True, cu_seqlens=cu), what="rot = 0")
+    for res in (False, True):
+        f = lambda: float(np.sum(g * orc.headwise_rope_fwd(x, w, rot=4, head_dim=hd, base=3.0, cu_seqlens=cu,
+                                                            residual=res)))
+        dx, dw = orc.headwise_rope_bwd(x, w, g, rot=4, head_dim=hd, base=3.0, cu_seqlens=cu, residual=res)
+        _close(dx, _fd_grad(f, x), tol=1e-8, what="FD dx (RoPE)")
+        _close(dw, _fd_grad(f, w), tol=1e-8, what="FD dw (RoPE)")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

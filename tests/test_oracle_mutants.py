@@ -52,6 +52,15 @@ MUTANTS = [
      "wk += z[b * R + r] * U[(int64_t)r * D * W + k * D + d];", 1),
     ("prefill_off_by_one", "const int64_t t = hi - 1 - i;", "const int64_t t = hi - i;", 1),
     ("prefill_pads_with_first_token", "= t >= lo ? x[t * D + d] : 0.0;", "= t >= lo ? x[t * D + d] : x[lo * D + d];", 1),
+    ("rope_sin_sign", "b[h + 2 * i + 1] = q * c + p * s;", "b[h + 2 * i + 1] = q * c - p * s;", 1),
+    ("rope_theta_exponent", "pow(base, -2.0 * i / hd)", "pow(base, -1.0 * i / hd)", 2),
+    ("rope_position_global", "const double m = (double)(n - seg[n]);", "const double m = (double)n;", 1),
+    ("rope_rotates_values", "for (int64_t h = 0; h < rot; h += hd)", "for (int64_t h = 0; h + hd <= D; h += hd)", 1),
+    ("rope_backward_not_inverted", "const double sign = inverse ? -1.0 : 1.0;", "const double sign = 1.0;", 1),
+    ("rope_half_split_pairs", "const double p = a[h + 2 * i], q = a[h + 2 * i + 1];",
+     "const double p = a[h + i], q = a[h + i + hd / 2];", 1),
+    ("rope_table_cos_sin_swapped", "table[(m * (hd / 2) + i) * 2 + 0] = cos(ang);",
+     "table[(m * (hd / 2) + i) * 2 + 0] = sin(ang);", 1),
 ]
 
 
@@ -62,7 +71,7 @@ def test_planted_mistake_is_caught(tmp_path, name, old, new, count):
     mutant = tmp_path / "mutant.c"
     mutant.write_text(src.replace(old, new))
     so = str(tmp_path / "libmutant.so")
-    subprocess.run(["gcc", "-O1", "-std=c11", "-fopenmp", "-fPIC", "-shared", str(mutant), "-o", so],
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fopenmp", "-fPIC", "-shared", str(mutant), "-o", so, "-lm"],
                    check=True)
     orc = oracle.Oracle(oracle.load(so))
     failed = []

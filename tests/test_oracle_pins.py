@@ -24,3 +24,9 @@ def test_oracle_rejects_bad_arguments(orc):
         orc.headwise_fwd(x, np.zeros((1, 4, 4, 2)), cu_seqlens=[0, 3, 2, 4])
     with pytest.raises(ValueError):
         orc.headwise_fwd(x, np.zeros((1, 4, 4, 2)), cu_seqlens=[0, 2, 5])
+    with pytest.raises(ValueError):
+        orc.rope(x, rot=3, head_dim=2)                     # rot not a multiple of head_dim
+    with pytest.raises(ValueError):
+        orc.rope(x, rot=4, head_dim=3)                     # odd head_dim
+    with pytest.raises(ValueError):
+        orc.rope(x, rot=6, head_dim=2)                     # rot > D
