@@ -255,6 +255,7 @@ ENTRY_KERNELS = {
     "dsc_static_bwd": (["st_bwd_kernel"], ["st_zero"]),
     "dsc_headwise_decode": (["hw_decode_kernel"], []),
     "dsc_lowrank_decode": (["lr_decode_kernel"], []),
+    "dsc_rope_table": (["rope_table_kernel"], []),
 }
 
 
@@ -527,6 +528,42 @@ def main() -> int:
                          "GBps": round(nbytes / t / 1e9, 1)}
             del g
         out["decode"] = dec
+
+        # The layer on the query / key / value projections feeds the rotary
+        # embedding of the queries and keys.  The fused calls rotate channels
+        # [0, 1536) (12 query and 12 key heads of 64) of the QKV ~150M
+        # workload on the fly; the layer alone is timed in the same loop.  A
+        # separate rotation pass would move rot*N elements in and out once
+        # more in each direction (unfused_extra_bytes per direction).
+        hd, rot = 64, 2 * 768
+        table = torch.empty(hwc.wl.T, hd // 2, 2, dtype=torch.float32, device="cuda")
+        binding.dsc_rope_table(table, base=10000.0)
+        kw = dict(rot=rot, head_dim=hd, table=table, residual=hwc.wl.residual)
+        calls = [lambda: binding.dsc_headwise_rope_fwd(hwc.x, hwc.w, hwc.y, **kw),
+                 lambda: binding.dsc_headwise_rope_bwd(hwc.x, hwc.w, hwc.dy, hwc.dx, hwc.dw, **kw),
+                 hwc.fwd, hwc.bwd]
+        for _ in range(3):
+            for f in calls:
+                f()
+        torch.cuda.synchronize()
+        reps = max(5, K // 2)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(reps)]
+        for e in evs:
+            e[0].record()
+            for i, f in enumerate(calls):
+                f()
+                e[i + 1].record()
+        torch.cuda.synchronize()
+        tr = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / reps * 1e-3 for i in range(len(calls))]
+        b = hwc.bytes("fwd") + hwc.bytes("bwd") + 2 * table.numel() * 4
+        out["rope_fused"] = {
+            "workload": f"{hwc.wl.name} + rotary embedding of channels [0, {rot}), heads of {hd}",
+            "fwd_us": round(tr[0] * 1e6, 1), "bwd_us": round(tr[1] * 1e6, 1),
+            "GBps": round(b / (tr[0] + tr[1]) / 1e9, 1),
+            "frac_hbm_peak": round(b / (tr[0] + tr[1]) / 1e9 / PEAK_HBM_GBPS, 4),
+            "layer_alone_fwd_us": round(tr[2] * 1e6, 1), "layer_alone_bwd_us": round(tr[3] * 1e6, 1),
+            "unfused_extra_bytes": 2 * rot * hwc.wl.N * hwc.x.element_size()}
+        del table
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline([cases[0].wl, cases[1].wl], args.cpu_seconds)

@@ -119,6 +119,59 @@ DSC_API dsc_status dsc_headwise_bwd(void *stream, int dtype, int64_t B, int64_t 
                             void *dx, void *dw);
 
 /*
+ * Rotary position table for the fused calls below.  The rotation is the one of
+ * "RoFormer: Enhanced Transformer with Rotary Position Embedding" (Su et al.),
+ * Section 3.4.2: pair i of a head (channels 2i, 2i+1) turns by m * theta_i at
+ * position m, theta_i = base^(-2i/head_dim).
+ *
+ *   table  (max_pos, head_dim/2, 2) fp32, out, 16-byte aligned:
+ *          table[m][i][0] = cos(m * theta_i), table[m][i][1] = sin(m * theta_i),
+ *          each computed in double precision and rounded once to fp32.
+ *   head_dim even, 2..65536; base > 0 (10000 is the usual value).
+ * The caller owns the table; it depends only on (max_pos, head_dim, base), so
+ * one table serves every call with those values.  max_pos = 0 does nothing.
+ */
+DSC_API dsc_status dsc_rope_table(void *stream, int64_t max_pos, int32_t head_dim, double base, float *table);
+
+/*
+ * Head-wise forward followed by the rotary embedding of the query and key
+ * channels.  The pages apply the layer (with its residual) to the Q, K and V
+ * projections right before the rotary embedding (Methodology, "placement");
+ * this call does both in one pass:
+ *   s[n,d] = the head-wise forward above (dsc_headwise_fwd),
+ *   y[n,h*hd+2i]   = s[n,h*hd+2i] * c - s[n,h*hd+2i+1] * sn      for h*hd < rot,
+ *   y[n,h*hd+2i+1] = s[n,h*hd+2i+1] * c + s[n,h*hd+2i] * sn
+ *   y[n,d] = s[n,d] for d >= rot,
+ * with (c, sn) = table[pos(n)][i] and pos(n) the index of token n inside its
+ * own sequence (0 at each sequence start; packed sequences restart).
+ *
+ *   rot       channels rotated, from channel 0 (query heads then key heads):
+ *             a multiple of head_dim in 0..D; rot = 0 is dsc_headwise_fwd.
+ *   head_dim  hd, even; a multiple of 8 (bf16) / 4 (fp32), else
+ *             DSC_ERR_UNSUPPORTED.
+ *   table     from dsc_rope_table with the same head_dim, in; read when
+ *             rot > 0.  max_pos must cover every position: max_pos >= T
+ *             without cu_seqlens, max_pos >= B*T with it.
+ *   Other arguments and rules as dsc_headwise_fwd.
+ */
+DSC_API dsc_status dsc_headwise_rope_fwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                                 int32_t H, const void *x, const void *w, const int32_t *cu_seqlens,
+                                 int32_t n_seqs, int32_t residual, int64_t rot, int32_t head_dim,
+                                 const float *table, int64_t max_pos, void *y);
+
+/*
+ * Backward of dsc_headwise_rope_fwd for L = <dy, y>.  The rotation is
+ * orthogonal, so the layer's output gradient is dy turned back by the same
+ * angles (ds = R^T dy, the transposed rotation); dx and dw are then those of
+ * dsc_headwise_bwd with ds in place of dy.  Shapes and rules as
+ * dsc_headwise_rope_fwd and dsc_headwise_bwd.
+ */
+DSC_API dsc_status dsc_headwise_rope_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                                 int32_t H, const void *x, const void *w, const void *dy,
+                                 const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, int64_t rot,
+                                 int32_t head_dim, const float *table, int64_t max_pos, void *dx, void *dw);
+
+/*
  * Low-rank forward (fused up-projection; Methodology, "parametrization (1)"
  * and Efficient training implementation, fused low-rank kernel):
  *   w[n,d,k] = sum_{r<R} z[n,r] * U[r, d*W+k]          (on chip only)

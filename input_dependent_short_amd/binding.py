@@ -47,9 +47,14 @@ def lib() -> ctypes.CDLL:
         L.dsc_headwise_decode.argtypes = [p, i, i64, i64, i32, i32, p, p, p, i32, p]
         L.dsc_lowrank_decode.argtypes = [p, i, i64, i64, i32, i32, p, p, p, p, i32, p]
         L.dsc_state_from_prefill.argtypes = [p, i, i64, i64, i64, i32, p, p, i32, p]
+        L.dsc_rope_table.argtypes = [p, i64, i32, ctypes.c_double, p]
+        L.dsc_headwise_rope_fwd.argtypes = [p, i, i64, i64, i64, i32, i32, p, p, p, i32, i32, i64, i32, p, i64, p]
+        L.dsc_headwise_rope_bwd.argtypes = [p, i, i64, i64, i64, i32, i32, p, p, p, p, i32, i32, i64, i32, p, i64,
+                                            p, p]
         for f in ("dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd",
                   "dsc_static_fwd", "dsc_static_bwd", "dsc_headwise_decode", "dsc_lowrank_decode",
-                  "dsc_state_from_prefill", "dsc_abi_version"):
+                  "dsc_state_from_prefill", "dsc_rope_table", "dsc_headwise_rope_fwd",
+                  "dsc_headwise_rope_bwd", "dsc_abi_version"):
             getattr(L, f).restype = ctypes.c_int
         L.dsc_status_string.argtypes = [i]
         L.dsc_status_string.restype = ctypes.c_char_p
@@ -109,6 +114,44 @@ def dsc_headwise_bwd(x, w, dy, dx, dw, *, cu_seqlens=None, residual=False, strea
     _check(lib().dsc_headwise_bwd(_stream(stream), _dtype_code(x), B, T, D, W, D // G if G else 0,
                                   _ptr(x), _ptr(w), _ptr(dy), cu, ns, int(bool(residual)),
                                   _ptr(dx), _ptr(dw)))
+
+
+def dsc_rope_table(table, *, base=10000.0, stream=None) -> None:
+    """Fill table (max_pos, head_dim/2, 2) fp32 with cos, sin of m * base^(-2i/head_dim)."""
+    if table.dtype != torch.float32 or table.dim() != 3 or table.shape[2] != 2:
+        raise ValueError("table must be fp32 (max_pos, head_dim/2, 2)")
+    _check(lib().dsc_rope_table(_stream(stream), table.shape[0], 2 * table.shape[1], float(base), _ptr(table)))
+
+
+def _table(table, head_dim):
+    if table is None:
+        return None, 0
+    if table.dtype != torch.float32 or table.dim() != 3 or table.shape[1:] != (head_dim // 2, 2):
+        raise ValueError(f"table must be fp32 (max_pos, {head_dim // 2}, 2)")
+    return _ptr(table), table.shape[0]
+
+
+def dsc_headwise_rope_fwd(x, w, y, *, rot, head_dim, table, cu_seqlens=None, residual=False,
+                          stream=None) -> None:
+    """y = rotary embedding (channels [0, rot), heads of head_dim) of the head-wise layer's output."""
+    B, T, D = x.shape
+    G, W = w.shape[2], w.shape[3]
+    cu, ns = _seq(cu_seqlens)
+    tp, max_pos = _table(table, head_dim)
+    _check(lib().dsc_headwise_rope_fwd(_stream(stream), _dtype_code(x), B, T, D, W, D // G if G else 0,
+                                       _ptr(x), _ptr(w), cu, ns, int(bool(residual)), int(rot), int(head_dim),
+                                       tp, max_pos, _ptr(y)))
+
+
+def dsc_headwise_rope_bwd(x, w, dy, dx, dw, *, rot, head_dim, table, cu_seqlens=None, residual=False,
+                          stream=None) -> None:
+    B, T, D = x.shape
+    G, W = w.shape[2], w.shape[3]
+    cu, ns = _seq(cu_seqlens)
+    tp, max_pos = _table(table, head_dim)
+    _check(lib().dsc_headwise_rope_bwd(_stream(stream), _dtype_code(x), B, T, D, W, D // G if G else 0,
+                                       _ptr(x), _ptr(w), _ptr(dy), cu, ns, int(bool(residual)), int(rot),
+                                       int(head_dim), tp, max_pos, _ptr(dx), _ptr(dw)))
 
 
 def dsc_lowrank_fwd(x, z, U, y, *, W, cu_seqlens=None, residual=False, stream=None) -> None:

@@ -128,6 +128,95 @@ dsc_status dsc_headwise_bwd(void *stream, int dtype, int64_t B, int64_t T, int64
     return launched(dsc::headwise_bwd(p, (hipStream_t)stream), "dsc_headwise_bwd launch");
 }
 
+dsc_status dsc_rope_table(void *stream, int64_t max_pos, int32_t head_dim, double base, float *table) {
+    if (max_pos < 0 || max_pos > INT32_MAX) return fail(DSC_ERR_SHAPE, "max_pos = %lld out of range", (long long)max_pos);
+    if (head_dim < 2 || head_dim % 2 || head_dim > (1 << 16))
+        return fail(DSC_ERR_SHAPE, "head_dim = %d must be even, in 2..65536", head_dim);
+    if (!(base > 0.0) || base > 1e300) return fail(DSC_ERR_SHAPE, "base must be positive and finite");
+    if (max_pos * (head_dim / 2) > (int64_t)INT32_MAX * 64) return fail(DSC_ERR_SHAPE, "table too large");
+    if (max_pos == 0) return ok();
+    if (!table) return fail(DSC_ERR_NULL, "table is required");
+    if (!aligned16(table)) return fail(DSC_ERR_ALIGNMENT, "table must be 16-byte aligned");
+    return launched(dsc::rope_table(max_pos, head_dim, base, table, (hipStream_t)stream), "dsc_rope_table launch");
+}
+
+namespace {
+
+// Rotation arguments of the fused head-wise + rotary calls.  A table row must
+// exist for every position a token can have: T without cu_seqlens, else the
+// whole packed batch B*T (a sequence can be that long).
+dsc_status check_rope(int dtype, int64_t B, int64_t T, int64_t D, const int32_t *cu_seqlens, int64_t rot,
+                      int32_t head_dim, const float *table, int64_t max_pos) {
+    if (head_dim < 2 || head_dim % 2 || head_dim > (1 << 16))
+        return fail(DSC_ERR_SHAPE, "head_dim = %d must be even, in 2..65536", head_dim);
+    const int vec = dtype == DSC_BF16 ? 8 : 4;
+    if (head_dim % vec)
+        return fail(DSC_ERR_UNSUPPORTED, "head_dim = %d must be a multiple of %d for this dtype", head_dim, vec);
+    if (rot < 0 || rot > D || rot % head_dim)
+        return fail(DSC_ERR_SHAPE, "rot = %lld must be a multiple of head_dim in 0..D", (long long)rot);
+    if (rot == 0 || B * T == 0) return DSC_SUCCESS;
+    const int64_t need = cu_seqlens ? B * T : T;
+    if (max_pos < need)
+        return fail(DSC_ERR_SHAPE, "max_pos = %lld: the table needs a row for each of %lld positions",
+                    (long long)max_pos, (long long)need);
+    if (max_pos > INT32_MAX / head_dim) return fail(DSC_ERR_SHAPE, "max_pos * head_dim exceeds 2^31-1");
+    if (!table) return fail(DSC_ERR_NULL, "table is required when rot > 0");
+    if (!aligned16(table)) return fail(DSC_ERR_ALIGNMENT, "table must be 16-byte aligned");
+    return DSC_SUCCESS;
+}
+
+}  // namespace
+
+dsc_status dsc_headwise_rope_fwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                                 int32_t H, const void *x, const void *w, const int32_t *cu_seqlens,
+                                 int32_t n_seqs, int32_t residual, int64_t rot, int32_t head_dim,
+                                 const float *table, int64_t max_pos, void *y) {
+    DSC_TRY(check_common(dtype, B, T, D, W, cu_seqlens, n_seqs, residual));
+    if (H < 1 || D % H) return fail(DSC_ERR_SHAPE, "H = %d must divide D = %lld", H, (long long)D);
+    const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
+    if (!dsc::headwise_supported(dt, D, H)) return fail(DSC_ERR_UNSUPPORTED, "H = %d not supported", H);
+    DSC_TRY(check_rope(dtype, B, T, D, cu_seqlens, rot, head_dim, table, max_pos));
+    if (B * T == 0) return ok();
+    if (!x || !w || !y) return fail(DSC_ERR_NULL, "x, w and y are required");
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    const size_t es = esize(dtype), N = (size_t)(B * T);
+    const Range in[] = {rng("x", x, N * D * es), rng("w", w, N * (D / H) * W * es),
+                        rng("cu_seqlens", cu_seqlens, cu_seqlens ? 4u * (n_seqs + 1) : 0),
+                        rng("table", table, rot ? (size_t)max_pos * head_dim * 4u : 0)};
+    const Range out[] = {rng("y", y, N * D * es)};
+    DSC_TRY(check_alias(in, 4, out, 1));
+    dsc::HwProblem p{dt, B * T, T, D, W, H, x, w, nullptr, y, nullptr, nullptr, cu_seqlens, n_seqs, residual,
+                     rot, head_dim, table, max_pos};
+    if (rot == 0) return launched(dsc::headwise_fwd(p, (hipStream_t)stream), "dsc_headwise_rope_fwd launch");
+    return launched(dsc::headwise_rope_fwd(p, (hipStream_t)stream), "dsc_headwise_rope_fwd launch");
+}
+
+dsc_status dsc_headwise_rope_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                                 int32_t H, const void *x, const void *w, const void *dy,
+                                 const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, int64_t rot,
+                                 int32_t head_dim, const float *table, int64_t max_pos, void *dx, void *dw) {
+    DSC_TRY(check_common(dtype, B, T, D, W, cu_seqlens, n_seqs, residual));
+    if (H < 1 || D % H) return fail(DSC_ERR_SHAPE, "H = %d must divide D = %lld", H, (long long)D);
+    const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
+    if (!dsc::headwise_supported(dt, D, H)) return fail(DSC_ERR_UNSUPPORTED, "H = %d not supported", H);
+    DSC_TRY(check_rope(dtype, B, T, D, cu_seqlens, rot, head_dim, table, max_pos));
+    if (B * T == 0) return ok();
+    if (!x || !w || !dy || !dx || !dw) return fail(DSC_ERR_NULL, "x, w, dy, dx and dw are required");
+    if (!aligned16(x) || !aligned16(w) || !aligned16(dy) || !aligned16(dx) || !aligned16(dw))
+        return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    const size_t es = esize(dtype), N = (size_t)(B * T);
+    const size_t wb = N * (D / H) * W * es;
+    const Range in[] = {rng("x", x, N * D * es), rng("w", w, wb), rng("dy", dy, N * D * es),
+                        rng("cu_seqlens", cu_seqlens, cu_seqlens ? 4u * (n_seqs + 1) : 0),
+                        rng("table", table, rot ? (size_t)max_pos * head_dim * 4u : 0)};
+    const Range out[] = {rng("dx", dx, N * D * es), rng("dw", dw, wb)};
+    DSC_TRY(check_alias(in, 5, out, 2));
+    dsc::HwProblem p{dt, B * T, T, D, W, H, x, w, dy, nullptr, dx, dw, cu_seqlens, n_seqs, residual,
+                     rot, head_dim, table, max_pos};
+    if (rot == 0) return launched(dsc::headwise_bwd(p, (hipStream_t)stream), "dsc_headwise_rope_bwd launch");
+    return launched(dsc::headwise_rope_bwd(p, (hipStream_t)stream), "dsc_headwise_rope_bwd launch");
+}
+
 dsc_status dsc_lowrank_fwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
                            int32_t R, const void *x, const void *z, const void *U,
                            const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, void *y) {

@@ -21,6 +21,12 @@ struct HwProblem {
     const int32_t *cu;
     int32_t n_seqs;
     int32_t residual;
+    // Rotary embedding after the layer (headwise_rope_* only): channels
+    // [0, rot) in heads of hd, cos / sin table (max_pos, hd/2, 2).
+    int64_t rot;
+    int32_t hd;
+    const float *rope;
+    int64_t max_pos;  // table rows
 };
 
 // Low-rank problem.
@@ -66,6 +72,11 @@ bool headwise_supported(Dtype dt, int64_t D, int32_t H);
 
 hipError_t headwise_fwd(const HwProblem &p, hipStream_t s);
 hipError_t headwise_bwd(const HwProblem &p, hipStream_t s);
+// The same layer followed by the rotary embedding of channels [0, p.rot).
+hipError_t headwise_rope_fwd(const HwProblem &p, hipStream_t s);
+hipError_t headwise_rope_bwd(const HwProblem &p, hipStream_t s);
+// table[(m*hd/2 + i)*2 + {0,1}] = {cos, sin}(m * base^(-2i/hd)), m < max_pos.
+hipError_t rope_table(int64_t max_pos, int32_t hd, double base, float *table, hipStream_t s);
 
 size_t lowrank_bwd_workspace(Dtype dt, int64_t N, int64_t D, int32_t W, int32_t R);
 hipError_t lowrank_fwd(const LrProblem &p, hipStream_t s);

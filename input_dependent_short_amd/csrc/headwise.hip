@@ -1,410 +1,12 @@
 // headwise.hip -- head-wise tied dynamic short convolution, forward and
-// backward, for gfx950.
-//
-// Operation ("Dynamic Short Convolutions Improve Transformers", gist.science
-// technical summary, Methodology: mechanism, parametrization (2) head-wise
-// tying, placement with residual):
-//   y[n,d] = rho*x[n,d] + sum_{k<W, n-k in seq(n)} w[n, d/H, k] * x[n-k, d]
-// Backward for L = <dy, y>:
-//   dx[m,d]   = rho*dy[m,d] + sum_{k<W, m+k in seq(m)} w[m+k, d/H, k] * dy[m+k, d]
-//   dw[n,j,k] = [n-k in seq(n)] * sum_{d in group j} dy[n,d] * x[n-k, d]
-//
-// Design (HBM-bound streaming, about 2 FLOP per byte):
-//   * one thread owns a 16-byte chunk of channels (8 bf16 / 4 fp32) and walks
-//     a tile of TT consecutive tokens, so x, w and dy are each read once from
-//     HBM and y, dx, dw written once; the W-1 token halo at each tile edge is
-//     re-read and mostly hits L2 (neighbouring tiles run on the same XCD);
-//   * the causal window is a register ring of the last W-1 inputs (forward)
-//     plus a W-1 token look-ahead of (dy, w) in the backward;
-//   * consecutive lanes own consecutive chunks of one token row, so every
-//     wave access is a contiguous run of 16-byte vectors;
-//   * taps outside the token's sequence are masked per token, so packed
-//     sequences cost nothing when no boundary falls inside a tile;
-//   * the dw group sum over H channels is a per-thread sum over the chunk
-//     followed by a DPP butterfly over the H/VEC lanes of the group;
-//   * the forward keeps the next batch of loads in flight while computing;
-//   * fp32 accumulation, one round-to-nearest-even store per output.
-#include "dsc_kernels.h"
+// backward, for gfx950 ("Dynamic Short Convolutions Improve Transformers",
+// gist.science technical summary, Methodology: mechanism, parametrization (2)
+// head-wise tying, placement with residual).  The kernels, their design and
+// the launch rules are in headwise_impl.h; this file instantiates the layer
+// alone.
+#include "headwise_impl.h"
 
 namespace dsc {
-namespace {
-
-struct HwParams {
-    const void *x, *w, *dy;
-    void *y, *dx, *dw;
-    SeqMap seq;
-    int64_t N, D, G;
-    int32_t H;
-    int32_t lanes;  // lanes sharing one filter group (H / VEC when H >= VEC)
-    float rho;
-    int64_t nchunks, items;
-};
-
-constexpr int kBlock = 256;
-
-// Group-local index of channel c of a chunk in the thread's filter span.
-template <int VEC, int GPT>
-__device__ __forceinline__ constexpr int grp(int c) {
-    return GPT > 1 ? c / (VEC / GPT) : 0;
-}
-
-// Raw 16-byte vector of activations, widened to fp32 when used.
-template <class E>
-__device__ __forceinline__ uint4 load_raw(const typename E::store_t *p) {
-    return *reinterpret_cast<const uint4 *>(p);
-}
-
-template <class E>
-__device__ __forceinline__ float lane_elem(const uint4 &v, int c) {
-    const uint32_t w = c < (E::kVec / 4) ? v.x : c < 2 * (E::kVec / 4) ? v.y : c < 3 * (E::kVec / 4) ? v.z : v.w;
-    if constexpr (E::kVec == 4) {
-        return __uint_as_float(w);
-    } else {
-        return (c & 1) ? bf16_hi(w) : bf16_lo(w);
-    }
-}
-
-template <class E>
-__device__ __forceinline__ void unpack(const uint4 &v, float (&f)[E::kVec]) {
-#pragma unroll
-    for (int c = 0; c < E::kVec; ++c) f[c] = lane_elem<E>(v, c);
-}
-
-// Sum over aligned groups of `lanes` consecutive lanes (a power of two <= 64);
-// every lane of the group receives the total.  DPP inside 16-lane rows
-// (quad permutes, half-row and row mirrors), cross-lane shuffles beyond.
-__device__ __forceinline__ float dpp_add(float v, int ctrl_sel) {
-    int o;
-    switch (ctrl_sel) {
-        case 0: o = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, true); break;   // xor 1
-        case 1: o = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, true); break;   // xor 2
-        case 2: o = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xf, 0xf, true); break;  // half-row mirror
-        default: o = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xf, 0xf, true); break; // row mirror
-    }
-    return v + __int_as_float(o);
-}
-
-template <int NW>
-__device__ __forceinline__ void group_sum(float (&v)[NW], int lanes) {
-    if (lanes >= 2) {
-#pragma unroll
-        for (int i = 0; i < NW; ++i) v[i] = dpp_add(v[i], 0);
-    }
-    if (lanes >= 4) {
-#pragma unroll
-        for (int i = 0; i < NW; ++i) v[i] = dpp_add(v[i], 1);
-    }
-    if (lanes >= 8) {
-#pragma unroll
-        for (int i = 0; i < NW; ++i) v[i] = dpp_add(v[i], 2);
-    }
-    if (lanes >= 16) {
-#pragma unroll
-        for (int i = 0; i < NW; ++i) v[i] = dpp_add(v[i], 3);
-    }
-    if (lanes >= 32) {
-#pragma unroll
-        for (int i = 0; i < NW; ++i) v[i] += __shfl_xor(v[i], 16, kWave);
-    }
-    if (lanes >= 64) {
-#pragma unroll
-        for (int i = 0; i < NW; ++i) v[i] += __shfl_xor(v[i], 32, kWave);
-    }
-}
-
-template <class E, int W, int GPT, int TT, int U>
-__global__ __launch_bounds__(kBlock) void hw_fwd_kernel(HwParams p) {
-    using S = typename E::store_t;
-    constexpr int VEC = E::kVec;
-    constexpr int NW = GPT * W;
-    constexpr int WALIGN = pow2_align(NW * (int)sizeof(S));
-
-    const int64_t item = xcd_block_id(blockIdx.x, gridDim.x) * kBlock + threadIdx.x;
-    if (item >= p.items) return;
-    const int64_t tile = item / p.nchunks;
-    const int64_t chunk = item - tile * p.nchunks;
-    const int64_t n0 = tile * TT;
-    const int64_t n1 = min(n0 + (int64_t)TT, p.N);
-    const int64_t d0 = chunk * VEC;
-    const int64_t jfirst = GPT > 1 ? chunk * GPT : d0 / p.H;
-
-    const S *x = static_cast<const S *>(p.x) + d0;
-    const S *w = static_cast<const S *>(p.w) + jfirst * W;
-    S *y = static_cast<S *>(p.y) + d0;
-
-    int64_t s, e;
-    p.seq.find(n0, s, e);
-
-    // ring[i] holds x[n-1-i]
-    float ring[W > 1 ? W - 1 : 1][VEC];
-#pragma unroll
-    for (int i = 0; i < W - 1; ++i) {
-        const int64_t t = n0 - 1 - i;
-        if (t >= s) {
-            unpack<E>(load_raw<E>(x + t * p.D), ring[i]);
-        } else {
-#pragma unroll
-            for (int c = 0; c < VEC; ++c) ring[i][c] = 0.f;
-        }
-    }
-
-    // two batches of U tokens in flight: compute one while the next loads
-    uint4 xa[U], xb[U];
-    float wa[U][NW], wb[U][NW];
-    auto load_batch = [&](int64_t nb, uint4 (&xr)[U], float (&wr)[U][NW]) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t n = nb + u;
-            if (n < n1) {
-                xr[u] = load_raw<E>(x + n * p.D);
-                Span<E, NW>::template load<WALIGN>(w + n * p.G * W, wr[u]);
-            }
-        }
-    };
-    auto compute_batch = [&](int64_t nb, const uint4 (&xr)[U], const float (&wr)[U][NW]) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t n = nb + u;
-            if (n < n1) {
-                if (n >= e) p.seq.find(n, s, e);
-                const int64_t nv = n - s;  // taps k <= nv lie inside the sequence
-                float xv[VEC], acc[VEC];
-                unpack<E>(xr[u], xv);
-#pragma unroll
-                for (int c = 0; c < VEC; ++c) acc[c] = p.rho * xv[c];
-#pragma unroll
-                for (int k = 0; k < W; ++k) {
-                    const bool ok = k <= nv;
-#pragma unroll
-                    for (int c = 0; c < VEC; ++c) {
-                        const float wk = ok ? wr[u][grp<VEC, GPT>(c) * W + k] : 0.f;
-                        const float xk = k == 0 ? xv[c] : ring[k - 1][c];
-                        acc[c] = __builtin_fmaf(wk, xk, acc[c]);
-                    }
-                }
-                Vec16<E>::store(y + n * p.D, acc);
-#pragma unroll
-                for (int i = W - 2; i > 0; --i)
-#pragma unroll
-                    for (int c = 0; c < VEC; ++c) ring[i][c] = ring[i - 1][c];
-                if constexpr (W > 1) {
-#pragma unroll
-                    for (int c = 0; c < VEC; ++c) ring[0][c] = xv[c];
-                }
-            }
-        }
-    };
-
-    load_batch(n0, xa, wa);
-    for (int64_t nb = n0; nb < n1; nb += 2 * U) {
-        if (nb + U < n1) load_batch(nb + U, xb, wb);
-        compute_batch(nb, xa, wa);
-        if (nb + U >= n1) break;
-        if (nb + 2 * U < n1) load_batch(nb + 2 * U, xa, wa);
-        compute_batch(nb + U, xb, wb);
-    }
-}
-
-template <class E, int W, int GPT, int TT, int U>
-__global__ __launch_bounds__(kBlock) void hw_bwd_kernel(HwParams p) {
-    using S = typename E::store_t;
-    constexpr int VEC = E::kVec;
-    constexpr int NW = GPT * W;
-    constexpr int WALIGN = pow2_align(NW * (int)sizeof(S));
-    constexpr int WIN = U + W - 1;  // look-ahead window of (dy, w)
-
-    const int64_t item = xcd_block_id(blockIdx.x, gridDim.x) * kBlock + threadIdx.x;
-    // Whole filter groups are active or inactive together (items is a
-    // multiple of nchunks, which is a multiple of lanes), so exiting here never
-    // strands a lane that a group reduction reads.
-    if (item >= p.items) return;
-    const int64_t tile = item / p.nchunks;
-    const int64_t chunk = item - tile * p.nchunks;
-    const int64_t n0 = tile * TT;
-    const int64_t n1 = min(n0 + (int64_t)TT, p.N);
-    const int64_t d0 = chunk * VEC;
-    const int64_t jfirst = GPT > 1 ? chunk * GPT : d0 / p.H;
-    const bool leader = (chunk & (p.lanes - 1)) == 0;
-
-    const S *x = static_cast<const S *>(p.x) + d0;
-    const S *g = static_cast<const S *>(p.dy) + d0;
-    const S *w = static_cast<const S *>(p.w) + jfirst * W;
-    S *dx = static_cast<S *>(p.dx) + d0;
-    S *dw = static_cast<S *>(p.dw) + jfirst * W;
-
-    int64_t s, e;
-    p.seq.find(n0, s, e);
-
-    const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
-    uint4 ring[W > 1 ? W - 1 : 1];  // ring[i] = x[m-1-i] (raw)
-#pragma unroll
-    for (int i = 0; i < W - 1; ++i) {
-        const int64_t t = n0 - 1 - i;
-        ring[i] = t >= s ? load_raw<E>(x + t * p.D) : zero4;
-    }
-    // look-ahead window: slot i holds token mb + i
-    uint4 gw[WIN];
-    float ww[WIN][NW];
-    auto load_gw = [&](int64_t t, int slot) {
-        if (t < p.N) {
-            gw[slot] = load_raw<E>(g + t * p.D);
-            Span<E, NW>::template load<WALIGN>(w + t * p.G * W, ww[slot]);
-        } else {
-            gw[slot] = zero4;
-#pragma unroll
-            for (int c = 0; c < NW; ++c) ww[slot][c] = 0.f;
-        }
-    };
-#pragma unroll
-    for (int i = 0; i < W - 1; ++i) load_gw(n0 + i, i);
-
-    for (int64_t mb = n0; mb < n1; mb += U) {
-        uint4 xv[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t m = mb + u;
-            xv[u] = m < n1 ? load_raw<E>(x + m * p.D) : zero4;
-            load_gw(mb + W - 1 + u, W - 1 + u);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t m = mb + u;
-            if (m < n1) {
-                if (m >= e) p.seq.find(m, s, e);
-                const int64_t ahead = e - m;  // dx terms k < ahead stay in the sequence
-                const int64_t back = m - s;   // dw taps k <= back stay in the sequence
-                float gm[VEC], acc[VEC];
-                unpack<E>(gw[u], gm);
-#pragma unroll
-                for (int c = 0; c < VEC; ++c) acc[c] = p.rho * gm[c];
-#pragma unroll
-                for (int k = 0; k < W; ++k) {
-                    const bool ok = k < ahead;
-#pragma unroll
-                    for (int c = 0; c < VEC; ++c) {
-                        const float wk = ok ? ww[u + k][grp<VEC, GPT>(c) * W + k] : 0.f;
-                        const float gk = k == 0 ? gm[c] : lane_elem<E>(gw[u + k], c);
-                        acc[c] = __builtin_fmaf(wk, gk, acc[c]);
-                    }
-                }
-                Vec16<E>::store(dx + m * p.D, acc);
-
-                float part[NW];
-#pragma unroll
-                for (int i = 0; i < NW; ++i) part[i] = 0.f;
-#pragma unroll
-                for (int k = 0; k < W; ++k) {
-                    const uint4 &xr = k == 0 ? xv[u] : ring[k - 1];
-#pragma unroll
-                    for (int c = 0; c < VEC; ++c)
-                        part[grp<VEC, GPT>(c) * W + k] =
-                            __builtin_fmaf(gm[c], lane_elem<E>(xr, c), part[grp<VEC, GPT>(c) * W + k]);
-                }
-                group_sum<NW>(part, p.lanes);
-#pragma unroll
-                for (int q = 0; q < GPT; ++q)
-#pragma unroll
-                    for (int k = 0; k < W; ++k)
-                        if (k > back) part[q * W + k] = 0.f;
-                if (leader) Span<E, NW>::template store<WALIGN>(dw + m * p.G * W, part);
-
-#pragma unroll
-                for (int i = W - 2; i > 0; --i) ring[i] = ring[i - 1];
-                if constexpr (W > 1) ring[0] = xv[u];
-            }
-        }
-        // slide the look-ahead window by U tokens
-#pragma unroll
-        for (int i = 0; i < W - 1; ++i) {
-            gw[i] = gw[U + i];
-#pragma unroll
-            for (int c = 0; c < NW; ++c) ww[i][c] = ww[U + i][c];
-        }
-    }
-}
-
-#ifndef DSC_HW_TT
-#define DSC_HW_TT 32
-#endif
-#ifndef DSC_HW_U
-#define DSC_HW_U 4
-#endif
-constexpr int kTT = DSC_HW_TT;  // tokens per thread tile
-constexpr int kU = DSC_HW_U;    // tokens per load batch
-
-template <class E>
-HwParams make_params(const HwProblem &pr, int64_t tt, int64_t &blocks) {
-    HwParams p;
-    p.x = pr.x; p.w = pr.w; p.dy = pr.dy;
-    p.y = pr.y; p.dx = pr.dx; p.dw = pr.dw;
-    p.seq = SeqMap{pr.cu, pr.n_seqs, pr.T};
-    p.N = pr.N; p.D = pr.D; p.G = pr.D / pr.H;
-    p.H = pr.H;
-    p.lanes = pr.H >= E::kVec ? pr.H / E::kVec : 1;
-    p.rho = pr.residual ? 1.f : 0.f;
-    p.nchunks = pr.D / E::kVec;
-    const int64_t ntiles = (pr.N + tt - 1) / tt;
-    p.items = ntiles * p.nchunks;
-    blocks = (p.items + kBlock - 1) / kBlock;
-    return p;
-}
-
-// The backward takes tiles of 2*kTT tokens when those still give at least
-// one whole round of resident waves (measured on MI355X: 7% faster at
-// B=4 T=4096 D=8192, much slower when the grid no longer fills the chip).
-template <class E, int W, int GPT>
-hipError_t launch_w(const HwProblem &pr, hipStream_t st, bool bwd) {
-    int64_t blocks;
-    if (bwd) {
-        static const int bpc = blocks_per_cu(reinterpret_cast<const void *>(&hw_bwd_kernel<E, W, GPT, 2 * kTT, kU>),
-                                             kBlock);
-        const int64_t waves_long = ((pr.N + 2 * kTT - 1) / (2 * kTT)) * (pr.D / E::kVec) / kWave;
-        if (waves_long >= (int64_t)device_cus() * bpc * (kBlock / kWave)) {
-            HwParams p = make_params<E>(pr, 2 * kTT, blocks);
-            if (blocks)
-                hipLaunchKernelGGL((hw_bwd_kernel<E, W, GPT, 2 * kTT, kU>), dim3((unsigned)blocks), dim3(kBlock), 0,
-                                   st, p);
-            return hipGetLastError();
-        }
-        HwParams p = make_params<E>(pr, kTT, blocks);
-        if (blocks) hipLaunchKernelGGL((hw_bwd_kernel<E, W, GPT, kTT, kU>), dim3((unsigned)blocks), dim3(kBlock), 0, st, p);
-        return hipGetLastError();
-    }
-    HwParams p = make_params<E>(pr, kTT, blocks);
-    if (blocks) hipLaunchKernelGGL((hw_fwd_kernel<E, W, GPT, kTT, kU>), dim3((unsigned)blocks), dim3(kBlock), 0, st, p);
-    return hipGetLastError();
-}
-
-template <class E, int GPT>
-hipError_t dispatch_w(const HwProblem &pr, hipStream_t st, bool bwd) {
-    switch (pr.W) {
-        case 1: return launch_w<E, 1, GPT>(pr, st, bwd);
-        case 2: return launch_w<E, 2, GPT>(pr, st, bwd);
-        case 3: return launch_w<E, 3, GPT>(pr, st, bwd);
-        case 4: return launch_w<E, 4, GPT>(pr, st, bwd);
-        case 5: return launch_w<E, 5, GPT>(pr, st, bwd);
-        case 6: return launch_w<E, 6, GPT>(pr, st, bwd);
-        case 7: return launch_w<E, 7, GPT>(pr, st, bwd);
-        case 8: return launch_w<E, 8, GPT>(pr, st, bwd);
-        default: return hipErrorInvalidValue;
-    }
-}
-
-template <class E>
-hipError_t dispatch(const HwProblem &pr, hipStream_t st, bool bwd) {
-    constexpr int VEC = E::kVec;
-    if (pr.H >= VEC) return dispatch_w<E, 1>(pr, st, bwd);
-    switch (VEC / pr.H) {
-        case 2: return dispatch_w<E, 2>(pr, st, bwd);
-        case 4: return dispatch_w<E, 4>(pr, st, bwd);
-        case 8:
-            if constexpr (VEC >= 8) return dispatch_w<E, 8>(pr, st, bwd);
-            return hipErrorInvalidValue;
-        default: return hipErrorInvalidValue;
-    }
-}
-
-}  // namespace
 
 bool headwise_supported(Dtype dt, int64_t D, int32_t H) {
     const int VEC = dt == Dtype::BF16 ? BF16::kVec : F32::kVec;
@@ -415,11 +17,11 @@ bool headwise_supported(Dtype dt, int64_t D, int32_t H) {
 }
 
 hipError_t headwise_fwd(const HwProblem &p, hipStream_t s) {
-    return p.dtype == Dtype::BF16 ? dispatch<BF16>(p, s, false) : dispatch<F32>(p, s, false);
+    return p.dtype == Dtype::BF16 ? dispatch<BF16, false>(p, s, false) : dispatch<F32, false>(p, s, false);
 }
 
 hipError_t headwise_bwd(const HwProblem &p, hipStream_t s) {
-    return p.dtype == Dtype::BF16 ? dispatch<BF16>(p, s, true) : dispatch<F32>(p, s, true);
+    return p.dtype == Dtype::BF16 ? dispatch<BF16, false>(p, s, true) : dispatch<F32, false>(p, s, true);
 }
 
 }  // namespace dsc

@@ -1,0 +1,602 @@
+// headwise_impl.h -- the head-wise kernels and their launchers, shared by
+// headwise.hip (the layer alone) and rope.hip (the layer followed by the
+// rotary position embedding of the query and key channels).  Internal to
+// libdsc.so; each including file instantiates one value of ROPE, so the two
+// sets of kernels compile in parallel.
+//
+// Operation ("Dynamic Short Convolutions Improve Transformers", gist.science
+// technical summary, Methodology: mechanism, parametrization (2) head-wise
+// tying, placement with residual):
+//   y[n,d] = rho*x[n,d] + sum_{k<W, n-k in seq(n)} w[n, d/H, k] * x[n-k, d]
+// Backward for L = <dy, y>:
+//   dx[m,d]   = rho*dy[m,d] + sum_{k<W, m+k in seq(m)} w[m+k, d/H, k] * dy[m+k, d]
+//   dw[n,j,k] = [n-k in seq(n)] * sum_{d in group j} dy[n,d] * x[n-k, d]
+// With ROPE, channels d < rot of y are then turned pair by pair (2i, 2i+1 of
+// each head of hd channels) by the angle pos(n) * theta_i, the rotary
+// embedding of "RoFormer: Enhanced Transformer with Rotary Position
+// Embedding" (Su et al., Section 3.4.2), pos(n) = n - start of n's sequence;
+// the backward first turns dy back (the transpose), then runs as above.
+//
+// Design (HBM-bound streaming, about 2 FLOP per byte):
+//   * one thread owns a 16-byte chunk of channels (8 bf16 / 4 fp32) and walks
+//     a tile of TT consecutive tokens, so x, w and dy are each read once from
+//     HBM and y, dx, dw written once; the W-1 token halo at each tile edge is
+//     re-read and mostly hits L2 (neighbouring tiles run on the same XCD);
+//   * the causal window is a register ring of the last W-1 inputs (forward)
+//     plus a W-1 token look-ahead of (dy, w) in the backward;
+//   * consecutive lanes own consecutive chunks of one token row, so every
+//     wave access is a contiguous run of 16-byte vectors;
+//   * taps outside the token's sequence are masked per token, so packed
+//     sequences cost nothing when no boundary falls inside a tile;
+//   * the dw group sum over H channels is a per-thread sum over the chunk
+//     followed by a DPP butterfly over the H/VEC lanes of the group;
+//   * the forward keeps the next batch of loads in flight while computing;
+//   * the rotation reads cos / sin from an fp32 table (position, pair); a
+//     16-byte chunk lies inside one head, so a thread's pairs are consecutive
+//     entries of one row.  Each thread reads row p0 (the position of its
+//     tile's first token) once.  bf16: the pair of cos / sin then turns by one
+//     step (row 1) per token, back to (1, 0) at a sequence start, with no
+//     memory access per token (the rounding drift over a tile, under 2e-5,
+//     is far below bf16 resolution).  fp32: a token at p0 + j also reads row
+//     j (rows j < TT + W are shared by every tile and stay in the L1 cache)
+//     and combines it with row p0 by angle addition (about 2 ulp); a
+//     sequence that starts inside the tile counts j from its own start;
+//   * fp32 accumulation, one round-to-nearest-even store per output.
+#pragma once
+
+#include "dsc_kernels.h"
+
+namespace dsc {
+namespace {
+
+
+struct HwParams {
+    const void *x, *w, *dy;
+    void *y, *dx, *dw;
+    SeqMap seq;
+    int64_t N, D, G;
+    int32_t H;
+    int32_t lanes;  // lanes sharing one filter group (H / VEC when H >= VEC)
+    float rho;
+    int64_t nchunks, items;
+    const float *rope;  // (npos, hd/2, 2) cos, sin; read only by the ROPE kernels
+    int32_t rot, hd;    // rotated channels [0, rot), head size
+    int32_t npos;       // table rows
+};
+
+constexpr int kBlock = 256;
+
+// Group-local index of channel c of a chunk in the thread's filter span.
+template <int VEC, int GPT>
+__device__ __forceinline__ constexpr int grp(int c) {
+    return GPT > 1 ? c / (VEC / GPT) : 0;
+}
+
+// Raw 16-byte vector of activations, widened to fp32 when used.
+template <class E>
+__device__ __forceinline__ uint4 load_raw(const typename E::store_t *p) {
+    return *reinterpret_cast<const uint4 *>(p);
+}
+
+template <class E>
+__device__ __forceinline__ float lane_elem(const uint4 &v, int c) {
+    const uint32_t w = c < (E::kVec / 4) ? v.x : c < 2 * (E::kVec / 4) ? v.y : c < 3 * (E::kVec / 4) ? v.z : v.w;
+    if constexpr (E::kVec == 4) {
+        return __uint_as_float(w);
+    } else {
+        return (c & 1) ? bf16_hi(w) : bf16_lo(w);
+    }
+}
+
+template <class E>
+__device__ __forceinline__ void unpack(const uint4 &v, float (&f)[E::kVec]) {
+#pragma unroll
+    for (int c = 0; c < E::kVec; ++c) f[c] = lane_elem<E>(v, c);
+}
+
+// Sum over aligned groups of `lanes` consecutive lanes (a power of two <= 64);
+// every lane of the group receives the total.  DPP inside 16-lane rows
+// (quad permutes, half-row and row mirrors), cross-lane shuffles beyond.
+__device__ __forceinline__ float dpp_add(float v, int ctrl_sel) {
+    int o;
+    switch (ctrl_sel) {
+        case 0: o = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, true); break;   // xor 1
+        case 1: o = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, true); break;   // xor 2
+        case 2: o = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xf, 0xf, true); break;  // half-row mirror
+        default: o = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xf, 0xf, true); break; // row mirror
+    }
+    return v + __int_as_float(o);
+}
+
+template <int NW>
+__device__ __forceinline__ void group_sum(float (&v)[NW], int lanes) {
+    if (lanes >= 2) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) v[i] = dpp_add(v[i], 0);
+    }
+    if (lanes >= 4) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) v[i] = dpp_add(v[i], 1);
+    }
+    if (lanes >= 8) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) v[i] = dpp_add(v[i], 2);
+    }
+    if (lanes >= 16) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) v[i] = dpp_add(v[i], 3);
+    }
+    if (lanes >= 32) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) v[i] += __shfl_xor(v[i], 16, kWave);
+    }
+    if (lanes >= 64) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) v[i] += __shfl_xor(v[i], 32, kWave);
+    }
+}
+
+// cos, sin of this thread's VEC/2 pairs at one position (VEC floats, 16-byte
+// aligned because a chunk starts at a multiple of VEC inside its head).
+template <int VEC>
+__device__ __forceinline__ void load_turn(const float *t, float (&cs)[VEC]) {
+#pragma unroll
+    for (int i = 0; i < VEC; i += 4) {
+        const float4 v = *reinterpret_cast<const float4 *>(t + i);
+        cs[i] = v.x; cs[i + 1] = v.y; cs[i + 2] = v.z; cs[i + 3] = v.w;
+    }
+}
+
+// cs <- an (x) cs pair by pair: cos and sin of the sum of the two angles.
+template <int VEC>
+__device__ __forceinline__ void compose(float (&cs)[VEC], const float (&an)[VEC]) {
+#pragma unroll
+    for (int j = 0; j < VEC / 2; ++j) {
+        const float c1 = an[2 * j], s1 = an[2 * j + 1], c2 = cs[2 * j], s2 = cs[2 * j + 1];
+        cs[2 * j] = c1 * c2 - s1 * s2;
+        cs[2 * j + 1] = s1 * c2 + c1 * s2;
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ void set_identity(float (&cs)[VEC]) {
+#pragma unroll
+    for (int j = 0; j < VEC / 2; ++j) {
+        cs[2 * j] = 1.f;
+        cs[2 * j + 1] = 0.f;
+    }
+}
+
+// Turns every pair (v[2j], v[2j+1]) by the angle whose cos, sin are
+// cs[2j], cs[2j+1]; INV turns by the opposite angle (the transpose).
+template <int VEC, bool INV>
+__device__ __forceinline__ void turn(float (&v)[VEC], const float (&cs)[VEC]) {
+#pragma unroll
+    for (int j = 0; j < VEC / 2; ++j) {
+        const float c = cs[2 * j], s = INV ? -cs[2 * j + 1] : cs[2 * j + 1];
+        const float a = v[2 * j], b = v[2 * j + 1];
+        v[2 * j] = a * c - b * s;
+        v[2 * j + 1] = b * c + a * s;
+    }
+}
+
+template <class E, int W, int GPT, int TT, int U, bool ROPE>
+__global__ __launch_bounds__(kBlock) void hw_fwd_kernel(HwParams p) {
+    using S = typename E::store_t;
+    constexpr int VEC = E::kVec;
+    constexpr int NW = GPT * W;
+    constexpr int WALIGN = pow2_align(NW * (int)sizeof(S));
+
+    const int64_t item = xcd_block_id(blockIdx.x, gridDim.x) * kBlock + threadIdx.x;
+    if (item >= p.items) return;
+    const int64_t tile = item / p.nchunks;
+    const int64_t chunk = item - tile * p.nchunks;
+    const int64_t n0 = tile * TT;
+    const int64_t n1 = min(n0 + (int64_t)TT, p.N);
+    const int64_t d0 = chunk * VEC;
+    const int64_t jfirst = GPT > 1 ? chunk * GPT : d0 / p.H;
+
+    const S *x = static_cast<const S *>(p.x) + d0;
+    const S *w = static_cast<const S *>(p.w) + jfirst * W;
+    S *y = static_cast<S *>(p.y) + d0;
+    // rotated chunks: this thread's pairs start at entry (d0 mod hd)/2 of a table row
+    const bool rotated = ROPE && d0 < p.rot;
+    const float *tab = ROPE ? p.rope + (int32_t)d0 % p.hd : nullptr;
+
+    int64_t s, e;
+    p.seq.find(n0, s, e);
+    // bf16 (REC): an is the cos / sin of the next token, stp one step;
+    // fp32: an is the cos / sin at the tile's first token
+    constexpr bool REC = ROPE && VEC == 8;
+    float an[VEC], stp[VEC];
+    if constexpr (ROPE) {
+        if (rotated) {
+            load_turn<VEC>(tab + (int32_t)(n0 - s) * p.hd, an);
+            if constexpr (REC) {
+                if (p.npos > 1) load_turn<VEC>(tab + p.hd, stp);
+                else set_identity<VEC>(stp);
+            }
+        }
+    }
+
+    // ring[i] holds x[n-1-i]
+    float ring[W > 1 ? W - 1 : 1][VEC];
+#pragma unroll
+    for (int i = 0; i < W - 1; ++i) {
+        const int64_t t = n0 - 1 - i;
+        if (t >= s) {
+            unpack<E>(load_raw<E>(x + t * p.D), ring[i]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) ring[i][c] = 0.f;
+        }
+    }
+
+    // two batches of U tokens in flight: compute one while the next loads
+    uint4 xa[U], xb[U];
+    float wa[U][NW], wb[U][NW];
+    auto load_batch = [&](int64_t nb, uint4 (&xr)[U], float (&wr)[U][NW]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t n = nb + u;
+            if (n < n1) {
+                xr[u] = load_raw<E>(x + n * p.D);
+                Span<E, NW>::template load<WALIGN>(w + n * p.G * W, wr[u]);
+            }
+        }
+    };
+    auto compute_batch = [&](int64_t nb, const uint4 (&xr)[U], const float (&wr)[U][NW]) {
+        // the batch's offset rows, all requested before the first is used;
+        // bit u of later: token u's sequence starts after n0 (no anchor)
+        float cs[U][VEC];
+        uint32_t later = 0;
+        if constexpr (ROPE && !REC) {
+            if (rotated) {
+                int64_t ts = s, te = e;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int64_t n = nb + u;
+                    if (n < n1) {
+                        if (n >= te) p.seq.find(n, ts, te);
+                        later |= (uint32_t)(ts > n0) << u;
+                        load_turn<VEC>(tab + (int32_t)(n - max(ts, n0)) * p.hd, cs[u]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t n = nb + u;
+            if (n < n1) {
+                if (n >= e) p.seq.find(n, s, e);
+                const int64_t nv = n - s;  // taps k <= nv lie inside the sequence
+                float xv[VEC], acc[VEC];
+                unpack<E>(xr[u], xv);
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) acc[c] = p.rho * xv[c];
+#pragma unroll
+                for (int k = 0; k < W; ++k) {
+                    const bool ok = k <= nv;
+#pragma unroll
+                    for (int c = 0; c < VEC; ++c) {
+                        const float wk = ok ? wr[u][grp<VEC, GPT>(c) * W + k] : 0.f;
+                        const float xk = k == 0 ? xv[c] : ring[k - 1][c];
+                        acc[c] = __builtin_fmaf(wk, xk, acc[c]);
+                    }
+                }
+                if constexpr (REC) {
+                    if (rotated) {
+                        if (nv == 0) set_identity<VEC>(an);
+                        turn<VEC, false>(acc, an);
+                        compose<VEC>(an, stp);
+                    }
+                } else if constexpr (ROPE) {
+                    if (rotated) {
+                        if (!((later >> u) & 1u)) compose<VEC>(cs[u], an);
+                        turn<VEC, false>(acc, cs[u]);
+                    }
+                }
+                Vec16<E>::store(y + n * p.D, acc);
+#pragma unroll
+                for (int i = W - 2; i > 0; --i)
+#pragma unroll
+                    for (int c = 0; c < VEC; ++c) ring[i][c] = ring[i - 1][c];
+                if constexpr (W > 1) {
+#pragma unroll
+                    for (int c = 0; c < VEC; ++c) ring[0][c] = xv[c];
+                }
+            }
+        }
+    };
+
+    load_batch(n0, xa, wa);
+    for (int64_t nb = n0; nb < n1; nb += 2 * U) {
+        if (nb + U < n1) load_batch(nb + U, xb, wb);
+        compute_batch(nb, xa, wa);
+        if (nb + U >= n1) break;
+        if (nb + 2 * U < n1) load_batch(nb + 2 * U, xa, wa);
+        compute_batch(nb + U, xb, wb);
+    }
+}
+
+template <class E, int W, int GPT, int TT, int U, bool ROPE>
+__global__ __launch_bounds__(kBlock) void hw_bwd_kernel(HwParams p) {
+    using S = typename E::store_t;
+    constexpr int VEC = E::kVec;
+    constexpr int NW = GPT * W;
+    constexpr int WALIGN = pow2_align(NW * (int)sizeof(S));
+    constexpr int WIN = U + W - 1;  // look-ahead window of (dy, w)
+
+    const int64_t item = xcd_block_id(blockIdx.x, gridDim.x) * kBlock + threadIdx.x;
+    // Whole filter groups are active or inactive together (items is a
+    // multiple of nchunks, which is a multiple of lanes), so exiting here never
+    // strands a lane that a group reduction reads.
+    if (item >= p.items) return;
+    const int64_t tile = item / p.nchunks;
+    const int64_t chunk = item - tile * p.nchunks;
+    const int64_t n0 = tile * TT;
+    const int64_t n1 = min(n0 + (int64_t)TT, p.N);
+    const int64_t d0 = chunk * VEC;
+    const int64_t jfirst = GPT > 1 ? chunk * GPT : d0 / p.H;
+    const bool leader = (chunk & (p.lanes - 1)) == 0;
+
+    const S *x = static_cast<const S *>(p.x) + d0;
+    const S *g = static_cast<const S *>(p.dy) + d0;
+    const S *w = static_cast<const S *>(p.w) + jfirst * W;
+    S *dx = static_cast<S *>(p.dx) + d0;
+    S *dw = static_cast<S *>(p.dw) + jfirst * W;
+    const bool rotated = ROPE && d0 < p.rot;
+    const float *tab = ROPE ? p.rope + (int32_t)d0 % p.hd : nullptr;
+
+    int64_t s, e;
+    p.seq.find(n0, s, e);
+    int64_t ls = s, le = e;  // sequence of the newest look-ahead token (ROPE)
+    // as in the forward: bf16 (REC) turns an by stp per look-ahead token
+    constexpr bool REC = ROPE && VEC == 8;
+    float an[VEC], stp[VEC];
+    if constexpr (ROPE) {
+        if (rotated) {
+            load_turn<VEC>(tab + (int32_t)(n0 - s) * p.hd, an);
+            if constexpr (REC) {
+                if (p.npos > 1) load_turn<VEC>(tab + p.hd, stp);
+                else set_identity<VEC>(stp);
+            }
+        }
+    }
+
+    const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+    uint4 ring[W > 1 ? W - 1 : 1];  // ring[i] = x[m-1-i] (raw)
+#pragma unroll
+    for (int i = 0; i < W - 1; ++i) {
+        const int64_t t = n0 - 1 - i;
+        ring[i] = t >= s ? load_raw<E>(x + t * p.D) : zero4;
+    }
+    // look-ahead window: slot i holds token mb + i
+    uint4 gw[WIN];
+    float ww[WIN][NW];
+    auto load_gw = [&](int64_t t, int slot) {
+        if (t < p.N) {
+            gw[slot] = load_raw<E>(g + t * p.D);
+            Span<E, NW>::template load<WALIGN>(w + t * p.G * W, ww[slot]);
+        } else {
+            gw[slot] = zero4;
+#pragma unroll
+            for (int c = 0; c < NW; ++c) ww[slot][c] = 0.f;
+        }
+    };
+    // ROPE: the window holds dy turned back, in fp32 (gf); cos / sin of a
+    // token are requested with its dy and applied when the slot is first used.
+    float gf[WIN][VEC];
+    // Look-ahead token t in stream order.  REC: returns whether t starts a
+    // sequence.  fp32: requests the offset row of t and returns whether t's
+    // sequence starts after n0 (no anchor then).
+    auto load_cs = [&](int64_t t, float (&cs)[VEC]) {
+        bool flag = false;
+        if (rotated && t < p.N) {
+            if (t >= le) p.seq.find(t, ls, le);
+            if constexpr (REC) {
+                flag = t == ls;
+            } else {
+                flag = ls > n0;
+                load_turn<VEC>(tab + (int32_t)(t - max(ls, n0)) * p.hd, cs);
+            }
+        }
+        return flag;
+    };
+    // dy of token t turned back, into the fp32 window (slots settle in stream order)
+    auto settle = [&](int64_t t, int slot, float (&cs)[VEC], bool flag) {
+        unpack<E>(gw[slot], gf[slot]);
+        if (rotated && t < p.N) {
+            if constexpr (REC) {
+                if (flag) set_identity<VEC>(an);
+                turn<VEC, true>(gf[slot], an);
+                compose<VEC>(an, stp);
+            } else {
+                if (!flag) compose<VEC>(cs, an);
+                turn<VEC, true>(gf[slot], cs);
+            }
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < W - 1; ++i) load_gw(n0 + i, i);
+    if constexpr (ROPE) {
+#pragma unroll
+        for (int i = 0; i < W - 1; ++i) {
+            float cs[VEC];
+            const bool lat = load_cs(n0 + i, cs);
+            settle(n0 + i, i, cs, lat);
+        }
+    }
+
+    for (int64_t mb = n0; mb < n1; mb += U) {
+        uint4 xv[U];
+        float cs[U][VEC];
+        uint32_t later = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t m = mb + u;
+            xv[u] = m < n1 ? load_raw<E>(x + m * p.D) : zero4;
+            load_gw(mb + W - 1 + u, W - 1 + u);
+            if constexpr (ROPE) later |= (uint32_t)load_cs(mb + W - 1 + u, cs[u]) << u;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t m = mb + u;
+            if (m < n1) {
+                if constexpr (ROPE) settle(mb + W - 1 + u, W - 1 + u, cs[u], (later >> u) & 1u);
+                if (m >= e) p.seq.find(m, s, e);
+                const int64_t ahead = e - m;  // dx terms k < ahead stay in the sequence
+                const int64_t back = m - s;   // dw taps k <= back stay in the sequence
+                float gm[VEC], acc[VEC];
+                if constexpr (ROPE) {
+#pragma unroll
+                    for (int c = 0; c < VEC; ++c) gm[c] = gf[u][c];
+                } else {
+                    unpack<E>(gw[u], gm);
+                }
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) acc[c] = p.rho * gm[c];
+#pragma unroll
+                for (int k = 0; k < W; ++k) {
+                    const bool ok = k < ahead;
+#pragma unroll
+                    for (int c = 0; c < VEC; ++c) {
+                        const float wk = ok ? ww[u + k][grp<VEC, GPT>(c) * W + k] : 0.f;
+                        float gk;
+                        if constexpr (ROPE) gk = gf[u + k][c];
+                        else gk = k == 0 ? gm[c] : lane_elem<E>(gw[u + k], c);
+                        acc[c] = __builtin_fmaf(wk, gk, acc[c]);
+                    }
+                }
+                Vec16<E>::store(dx + m * p.D, acc);
+
+                float part[NW];
+#pragma unroll
+                for (int i = 0; i < NW; ++i) part[i] = 0.f;
+#pragma unroll
+                for (int k = 0; k < W; ++k) {
+                    const uint4 &xr = k == 0 ? xv[u] : ring[k - 1];
+#pragma unroll
+                    for (int c = 0; c < VEC; ++c)
+                        part[grp<VEC, GPT>(c) * W + k] =
+                            __builtin_fmaf(gm[c], lane_elem<E>(xr, c), part[grp<VEC, GPT>(c) * W + k]);
+                }
+                group_sum<NW>(part, p.lanes);
+#pragma unroll
+                for (int q = 0; q < GPT; ++q)
+#pragma unroll
+                    for (int k = 0; k < W; ++k)
+                        if (k > back) part[q * W + k] = 0.f;
+                if (leader) Span<E, NW>::template store<WALIGN>(dw + m * p.G * W, part);
+
+#pragma unroll
+                for (int i = W - 2; i > 0; --i) ring[i] = ring[i - 1];
+                if constexpr (W > 1) ring[0] = xv[u];
+            }
+        }
+        // slide the look-ahead window by U tokens
+#pragma unroll
+        for (int i = 0; i < W - 1; ++i) {
+            if constexpr (ROPE) {
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) gf[i][c] = gf[U + i][c];
+            } else {
+                gw[i] = gw[U + i];
+            }
+#pragma unroll
+            for (int c = 0; c < NW; ++c) ww[i][c] = ww[U + i][c];
+        }
+    }
+}
+
+#ifndef DSC_HW_TT
+#define DSC_HW_TT 32
+#endif
+#ifndef DSC_HW_U
+#define DSC_HW_U 4
+#endif
+constexpr int kTT = DSC_HW_TT;  // tokens per thread tile
+constexpr int kU = DSC_HW_U;    // tokens per load batch
+
+template <class E>
+HwParams make_params(const HwProblem &pr, int64_t tt, int64_t &blocks) {
+    HwParams p;
+    p.x = pr.x; p.w = pr.w; p.dy = pr.dy;
+    p.y = pr.y; p.dx = pr.dx; p.dw = pr.dw;
+    p.seq = SeqMap{pr.cu, pr.n_seqs, pr.T};
+    p.N = pr.N; p.D = pr.D; p.G = pr.D / pr.H;
+    p.H = pr.H;
+    p.lanes = pr.H >= E::kVec ? pr.H / E::kVec : 1;
+    p.rho = pr.residual ? 1.f : 0.f;
+    p.nchunks = pr.D / E::kVec;
+    p.rope = pr.rope;
+    p.rot = (int32_t)pr.rot;
+    p.hd = pr.hd;
+    p.npos = (int32_t)pr.max_pos;
+    const int64_t ntiles = (pr.N + tt - 1) / tt;
+    p.items = ntiles * p.nchunks;
+    blocks = (p.items + kBlock - 1) / kBlock;
+    return p;
+}
+
+// The backward takes tiles of 2*kTT tokens when those still give at least
+// one whole round of resident waves (measured on MI355X: 7% faster at
+// B=4 T=4096 D=8192, much slower when the grid no longer fills the chip).
+template <class E, int W, int GPT, bool ROPE>
+hipError_t launch_w(const HwProblem &pr, hipStream_t st, bool bwd) {
+    constexpr int UB = kU;
+    int64_t blocks;
+    if (bwd) {
+        static const int bpc = blocks_per_cu(
+            reinterpret_cast<const void *>(&hw_bwd_kernel<E, W, GPT, 2 * kTT, UB, ROPE>), kBlock);
+        const int64_t waves_long = ((pr.N + 2 * kTT - 1) / (2 * kTT)) * (pr.D / E::kVec) / kWave;
+        if (waves_long >= (int64_t)device_cus() * bpc * (kBlock / kWave)) {
+            HwParams p = make_params<E>(pr, 2 * kTT, blocks);
+            if (blocks)
+                hipLaunchKernelGGL((hw_bwd_kernel<E, W, GPT, 2 * kTT, UB, ROPE>), dim3((unsigned)blocks),
+                                   dim3(kBlock), 0, st, p);
+            return hipGetLastError();
+        }
+        HwParams p = make_params<E>(pr, kTT, blocks);
+        if (blocks)
+            hipLaunchKernelGGL((hw_bwd_kernel<E, W, GPT, kTT, UB, ROPE>), dim3((unsigned)blocks), dim3(kBlock), 0,
+                               st, p);
+        return hipGetLastError();
+    }
+    HwParams p = make_params<E>(pr, kTT, blocks);
+    if (blocks)
+        hipLaunchKernelGGL((hw_fwd_kernel<E, W, GPT, kTT, kU, ROPE>), dim3((unsigned)blocks), dim3(kBlock), 0, st, p);
+    return hipGetLastError();
+}
+
+template <class E, int GPT, bool ROPE>
+hipError_t dispatch_w(const HwProblem &pr, hipStream_t st, bool bwd) {
+    switch (pr.W) {
+        case 1: return launch_w<E, 1, GPT, ROPE>(pr, st, bwd);
+        case 2: return launch_w<E, 2, GPT, ROPE>(pr, st, bwd);
+        case 3: return launch_w<E, 3, GPT, ROPE>(pr, st, bwd);
+        case 4: return launch_w<E, 4, GPT, ROPE>(pr, st, bwd);
+        case 5: return launch_w<E, 5, GPT, ROPE>(pr, st, bwd);
+        case 6: return launch_w<E, 6, GPT, ROPE>(pr, st, bwd);
+        case 7: return launch_w<E, 7, GPT, ROPE>(pr, st, bwd);
+        case 8: return launch_w<E, 8, GPT, ROPE>(pr, st, bwd);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <class E, bool ROPE>
+hipError_t dispatch(const HwProblem &pr, hipStream_t st, bool bwd) {
+    constexpr int VEC = E::kVec;
+    if (pr.H >= VEC) return dispatch_w<E, 1, ROPE>(pr, st, bwd);
+    switch (VEC / pr.H) {
+        case 2: return dispatch_w<E, 2, ROPE>(pr, st, bwd);
+        case 4: return dispatch_w<E, 4, ROPE>(pr, st, bwd);
+        case 8:
+            if constexpr (VEC >= 8) return dispatch_w<E, 8, ROPE>(pr, st, bwd);
+            return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+}  // namespace dsc

@@ -31,6 +31,7 @@ def test_header_declares_the_entry_points():
     for s in ("dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd",
               "dsc_lowrank_bwd_workspace_size", "dsc_static_fwd", "dsc_static_bwd",
               "dsc_headwise_decode", "dsc_lowrank_decode", "dsc_state_from_prefill",
+              "dsc_rope_table", "dsc_headwise_rope_fwd", "dsc_headwise_rope_bwd",
               "dsc_status_string", "dsc_last_error", "dsc_abi_version"):
         assert s in syms
 
@@ -153,6 +154,36 @@ def test_decode_validation(lib):
     assert sp(W=9) == 2 and sp(st=None) == 1 and sp(st=P(1)) == 5
     assert sp(W=1, st=None) == 0                    # no slots: nothing to write
     assert sp(B=0, x=None, st=None) == 0
+
+
+def test_rope_validation(lib):
+    # head-wise + rotary: B=2 T=8 D=128 bf16, rot = 64 (one query and one key head of 32)
+    def rf(dt=1, B=2, T=8, D=128, W=4, H=16, x=P(1), w=P(2), cu=None, ns=0, res=1, rot=64, hd=32,
+           tab=P(3), maxp=8, y=P(4)):
+        return lib.dsc_headwise_rope_fwd(S0, dt, B, T, D, W, H, x, w, cu, ns, res, rot, hd, tab, maxp, y)
+
+    def rb(rot=64, hd=32, tab=P(3), maxp=8, dx=P(5), dw=P(6)):
+        return lib.dsc_headwise_rope_bwd(S0, 1, 2, 8, 128, 4, 16, P(1), P(2), P(4), None, 0, 1, rot, hd, tab, maxp,
+                                         dx, dw)
+    assert rf(hd=31) == 2 and rf(hd=0) == 2          # odd / empty head
+    assert rf(hd=4) == 3                             # a bf16 chunk of 8 channels would span two heads
+    assert rf(dt=0, hd=4, rot=64, y=P(1)) == 5       # fp32 chunks are 4 channels: passes to the alias check
+    assert rf(rot=48) == 2 and rf(rot=160) == 2 and rf(rot=-32) == 2
+    assert rf(maxp=7) == 2                           # positions 0..T-1 need T rows
+    assert rf(cu=P(9), ns=3, maxp=8) == 2            # packed: a sequence may be B*T long
+    assert rf(tab=None) == 1
+    assert rf(tab=ctypes.c_void_p(A * 3 + 8)) == 4
+    assert rf(y=P(3)) == 5                           # y overlaps the table
+    assert rf(rot=0, tab=None, maxp=0, y=P(1)) == 5  # rot = 0 needs no table; aliasing still checked
+    assert rf(B=0, x=None, w=None, tab=None, y=None) == 0
+    assert rb(dx=P(3)) == 5 and rb(dw=None) == 1 and rb(maxp=2) == 2
+    assert lib.dsc_rope_table(S0, 8, 31, 10000.0, P(1)) == 2
+    assert lib.dsc_rope_table(S0, 8, 32, 0.0, P(1)) == 2
+    assert lib.dsc_rope_table(S0, 8, 32, float("nan"), P(1)) == 2
+    assert lib.dsc_rope_table(S0, -1, 32, 10000.0, P(1)) == 2
+    assert lib.dsc_rope_table(S0, 8, 32, 10000.0, None) == 1
+    assert lib.dsc_rope_table(S0, 8, 32, 10000.0, ctypes.c_void_p(A + 4)) == 4
+    assert lib.dsc_rope_table(S0, 0, 32, 10000.0, None) == 0
 
 
 def test_binding_raises_with_message(lib):

@@ -1,0 +1,142 @@
+"""GPU parity of the head-wise layer fused with the rotary position embedding
+of the query and key channels, and of its cos / sin table, through the C ABI
+against the fp64 oracle.
+
+The table is compared entry by entry with the oracle's double-precision table
+rounded to fp32 (at most one fp32 ulp apart: both sides take cos / sin in
+double precision and round once).  The fused layer's y, dx and dw are compared
+element by element at small shapes and on sampled token windows at the QKV
+~150M shape (B=8 T=2048 D=2304 W=4, heads of 64, query + key = 1536
+channels), with the normwise tolerance of the layer itself (1e-5 fp32, 2e-2
+bf16).
+"""
+from __future__ import annotations
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, Guarded, assert_close, say
+from input_dependent_short_amd import binding, inputs
+from input_dependent_short_amd.inputs import to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _table(max_pos: int, hd: int, base: float) -> torch.Tensor:
+    t = Guarded((max_pos, hd // 2, 2), torch.float32)
+    binding.dsc_rope_table(t.t, base=base)
+    torch.cuda.synchronize()
+    t.check_guards("table")
+    return t.t
+
+
+@pytest.mark.parametrize("max_pos,hd,base", [(2048, 64, 10000.0), (37, 8, 500.0), (16384, 128, 1e6), (5, 2, 3.0)])
+def test_rope_table(max_pos, hd, base):
+    say(f"[rope] table max_pos={max_pos} head_dim={hd} base={base}")
+    got = _table(max_pos, hd, base).cpu().numpy().astype(np.float64)
+    want = oracle.rope_table(max_pos, hd, base).astype(np.float32)
+    ulp = np.spacing(np.abs(want)).astype(np.float64)
+    diff = np.abs(got - want.astype(np.float64))
+    assert np.all(diff <= ulp), f"max difference {np.max(diff / ulp):.2f} fp32 ulp"
+
+
+def _run(inp, res, rot, hd, table):
+    x, w, dy = inp["x"].cuda(), inp["w"].cuda(), inp["dy"].cuda()
+    cu = None if inp["cu_seqlens"] is None else torch.from_numpy(inp["cu_seqlens"]).cuda()
+    y, dx, dw = Guarded(x.shape, x.dtype), Guarded(x.shape, x.dtype), Guarded(w.shape, w.dtype)
+    kw = dict(rot=rot, head_dim=hd, table=table, cu_seqlens=cu, residual=res)
+    binding.dsc_headwise_rope_fwd(x, w, y.t, **kw)
+    binding.dsc_headwise_rope_bwd(x, w, dy, dx.t, dw.t, **kw)
+    torch.cuda.synchronize()
+    for name, g in (("y", y), ("dx", dx), ("dw", dw)):
+        g.check_guards(name)
+    return y, dx, dw
+
+
+# (dtype, B, T, D, W, H, head_dim, rot, residual, segment-length range or None)
+RP_CASES = [
+    ("fp32", 2, 37, 96, 4, 4, 16, 64, True, None),
+    ("fp32", 1, 50, 64, 3, 1, 8, 32, False, (1, 9)),
+    ("fp32", 2, 33, 32, 1, 4, 4, 32, True, (1, 5)),      # W = 1, every channel rotated
+    ("bf16", 2, 100, 192, 4, 64, 64, 128, True, None),    # query, key, value heads of 64
+    ("bf16", 1, 300, 768, 4, 64, 64, 512, True, (1, 40)),
+    ("bf16", 3, 19, 48, 2, 8, 16, 32, False, None),
+    ("bf16", 1, 130, 256, 8, 16, 32, 256, True, (1, 40)),
+    ("bf16", 2, 66, 512, 7, 2, 64, 256, False, None),     # four filter groups per 16-byte chunk
+    ("bf16", 4, 65, 2304, 4, 64, 64, 1536, True, None),   # the QKV layout at a short length
+    ("bf16", 1, 1, 16, 3, 8, 8, 8, False, None),          # one token
+]
+
+
+def _ids(cases):
+    return [f"rope-{c[0]}-B{c[1]}T{c[2]}D{c[3]}W{c[4]}H{c[5]}-hd{c[6]}rot{c[7]}-res{int(c[8])}-"
+            f"{'varlen' if c[9] else 'rows'}" for c in cases]
+
+
+@pytest.mark.parametrize("case", RP_CASES, ids=_ids(RP_CASES))
+def test_headwise_rope_small(case):
+    dt, B, T, D, W, H, hd, rot, res, seg = case
+    wl, inp = inputs.small("headwise", B, T, D, W, H=H, dtype=dt, residual=res, varlen=seg is not None,
+                           seglen_range=seg or (1, 8), seed=zlib.crc32(repr(case).encode()) % 1000)
+    cu = inp["cu_seqlens"]
+    base = 10000.0 if hd >= 32 else 100.0
+    max_pos = B * T if cu is not None else T
+    say(f"[rope] {wl.name} hd={hd} rot={rot} residual={res} segments={cu}")
+    table = _table(max_pos, hd, base)
+    y, dx, dw = _run(inp, res, rot, hd, table)
+    x64, w64, g64 = (to_f64(inp[k]) for k in ("x", "w", "dy"))
+    kw = dict(rot=rot, head_dim=hd, base=base, cu_seqlens=cu, residual=res)
+    ry = oracle.headwise_rope_fwd(x64, w64, **kw)
+    rdx, rdw = oracle.headwise_rope_bwd(x64, w64, g64, **kw)
+    tol = TOL[dt]
+    assert_close("y", y.host(), ry, tol)
+    assert_close("dx", dx.host(), rdx, tol)
+    assert_close("dw", dw.host(), rdw, tol)
+    # the backward has no atomics: a second call gives the same bits
+    _, dx2, dw2 = _run(inp, res, rot, hd, table)
+    assert torch.equal(dx.t, dx2.t) and torch.equal(dw.t, dw2.t)
+
+
+def test_headwise_rope_qkv_150m_full_size():
+    wl = inputs.WORKLOADS[2]
+    inp = inputs.make_inputs(wl)
+    hd, rot = 64, 1536
+    say(f"[rope] {wl.name}: B={wl.B} T={wl.T} D={wl.D} W={wl.W} H={wl.H} head_dim={hd} rot={rot}")
+    table = _table(wl.T, hd, 10000.0)
+    y, dx, dw = _run(inp, True, rot, hd, table)
+    x64, w64, g64 = (to_f64(inp[k]) for k in ("x", "w", "dy"))
+    N, D, G = wl.N, wl.D, wl.D // wl.H
+    yf, dxf, dwf = y.host().reshape(N, D), dx.host().reshape(N, D), dw.host().reshape(N, G, wl.W)
+    kw = dict(rot=rot, head_dim=hd, base=10000.0, residual=True)
+    tol = TOL["bf16"]
+    for lo, hi in [(0, 40), (2040, 2060), (N // 2 - 7, N // 2 + 17), (N - 40, N)]:
+        assert_close("y", yf[lo:hi], oracle.headwise_rope_fwd(x64, w64, rows=(lo, hi), **kw), tol)
+        rdx, rdw = oracle.headwise_rope_bwd(x64, w64, g64, rows=(lo, hi), **kw)
+        assert_close("dx", dxf[lo:hi], rdx, tol)
+        assert_close("dw", dwf[lo:hi], rdw, tol)
+
+
+def test_headwise_rope_without_rotation_is_the_layer():
+    """rot = 0 (no table) gives the head-wise layer's outputs bit for bit."""
+    wl, inp = inputs.small("headwise", 2, 40, 256, 4, H=16, dtype="bf16", residual=True, seed=5)
+    x, w, dy = inp["x"].cuda(), inp["w"].cuda(), inp["dy"].cuda()
+    outs = [torch.empty_like(x) for _ in range(4)] + [torch.empty_like(w) for _ in range(2)]
+    binding.dsc_headwise_rope_fwd(x, w, outs[0], rot=0, head_dim=64, table=None, residual=True)
+    binding.dsc_headwise_fwd(x, w, outs[1], residual=True)
+    binding.dsc_headwise_rope_bwd(x, w, dy, outs[2], outs[4], rot=0, head_dim=64, table=None, residual=True)
+    binding.dsc_headwise_bwd(x, w, dy, outs[3], outs[5], residual=True)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[2], outs[3]) and torch.equal(outs[4], outs[5])
+
+
+def test_headwise_rope_empty_batch():
+    x = torch.empty(0, 16, 64, dtype=torch.bfloat16, device="cuda")
+    w = torch.empty(0, 16, 4, 4, dtype=torch.bfloat16, device="cuda")
+    binding.dsc_headwise_rope_fwd(x, w, torch.empty_like(x), rot=64, head_dim=16, table=None)
+    binding.dsc_headwise_rope_bwd(x, w, x, torch.empty_like(x), torch.empty_like(w), rot=64, head_dim=16,
+                                  table=None)
+    torch.cuda.synchronize()
