@@ -56,10 +56,11 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_state_from_prefill.argtypes = [i64, i64, i64, i32, p, p, i32, p]
     lib.oracle_rope_table.argtypes = [i64, i32, ctypes.c_double, p]
     lib.oracle_rope.argtypes = [i64, i64, i64, i64, i32, ctypes.c_double, p, i32, i32, i64, i64, p, p]
+    lib.oracle_rope_at.argtypes = [i64, i64, i64, i32, ctypes.c_double, p, p, p]
     for name in ("oracle_headwise_fwd", "oracle_headwise_bwd", "oracle_lowrank_fwd",
                  "oracle_lowrank_bwd", "oracle_static_fwd", "oracle_static_bwd",
                  "oracle_headwise_decode", "oracle_lowrank_decode", "oracle_state_from_prefill",
-                 "oracle_rope_table", "oracle_rope"):
+                 "oracle_rope_table", "oracle_rope", "oracle_rope_at"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -276,6 +277,24 @@ class Oracle:
         return self.rope(y, rot=rot, head_dim=head_dim, base=base, cu_seqlens=cu_seqlens, rows=rows,
                          shape=(B, T))
 
+    def rope_at(self, v, positions, *, rot, head_dim, base=10000.0):
+        """v (B, D): row b, the newest token of sequence b, rotated at position positions[b]."""
+        v = _f64(v)
+        pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int32))
+        B, D = v.shape
+        if pos.shape != (B,):
+            raise ValueError("one position per row")
+        out = np.empty_like(v)
+        _check(self.lib.oracle_rope_at(B, D, int(rot), int(head_dim), float(base), _ptr(pos), _ptr(v),
+                                       _ptr(out)), "rope_at")
+        return out
+
+    def headwise_rope_decode(self, x, w, state, positions, *, rot, head_dim, base=10000.0, residual=False):
+        """One decoding step of the head-wise layer, then the rotation of its
+        output at each sequence's position -> (y (B, D), new state)."""
+        y, st = self.headwise_decode(x, w, state, residual=residual)
+        return self.rope_at(y, positions, rot=rot, head_dim=head_dim, base=base), st
+
     def headwise_rope_bwd(self, x, w, dy, *, rot, head_dim, base=10000.0, cu_seqlens=None,
                           residual=False, rows=None):
         """-> (dx, dw).  The rotation is orthogonal and comes last, so the
@@ -349,3 +368,11 @@ def headwise_rope_fwd(*a, **k):
 
 def headwise_rope_bwd(*a, **k):
     return default().headwise_rope_bwd(*a, **k)
+
+
+def rope_at(*a, **k):
+    return default().rope_at(*a, **k)
+
+
+def headwise_rope_decode(*a, **k):
+    return default().headwise_rope_decode(*a, **k)

@@ -412,6 +412,23 @@ int oracle_rope_table(int64_t max_pos, int32_t hd, double base, double *table)
     return 0;
 }
 
+/* One row a of D channels turned into b at position m: channels [0, rot)
+ * in heads of hd, pair i of each head by the angle sign * m * theta_i; the
+ * other channels copied. */
+static void rotate_row(int64_t D, int64_t rot, int32_t hd, double base, double m, double sign,
+                       const double *a, double *b)
+{
+    for (int64_t d = rot; d < D; ++d) b[d] = a[d];
+    for (int64_t h = 0; h < rot; h += hd)
+        for (int32_t i = 0; i < hd / 2; ++i) {
+            const double ang = sign * m * pow(base, -2.0 * i / hd);
+            const double c = cos(ang), s = sin(ang);
+            const double p = a[h + 2 * i], q = a[h + 2 * i + 1];
+            b[h + 2 * i] = p * c - q * s;
+            b[h + 2 * i + 1] = q * c + p * s;
+        }
+}
+
 /* Rows [n_lo, n_hi) of v (stored compactly, row n at n - n_lo) rotated into
  * out.  inverse != 0 turns every pair by the opposite angle: the transpose of
  * the rotation, which is what the chain rule applies to an output gradient. */
@@ -427,18 +444,21 @@ int oracle_rope(int64_t B, int64_t T, int64_t D, int64_t rot, int32_t hd, double
 #pragma omp parallel for schedule(static)
     for (int64_t n = n_lo; n < n_hi; ++n) {
         const double m = (double)(n - seg[n]);
-        const double *a = v + (n - n_lo) * D;
-        double *b = out + (n - n_lo) * D;
-        for (int64_t d = rot; d < D; ++d) b[d] = a[d];
-        for (int64_t h = 0; h < rot; h += hd)
-            for (int32_t i = 0; i < hd / 2; ++i) {
-                const double ang = sign * m * pow(base, -2.0 * i / hd);
-                const double c = cos(ang), s = sin(ang);
-                const double p = a[h + 2 * i], q = a[h + 2 * i + 1];
-                b[h + 2 * i] = p * c - q * s;
-                b[h + 2 * i + 1] = q * c + p * s;
-            }
+        rotate_row(D, rot, hd, base, m, sign, v + (n - n_lo) * D, out + (n - n_lo) * D);
     }
     free(seg);
+    return 0;
+}
+
+/* Decoding: row b of v (B, D) is the newest token of sequence b, at position
+ * pos[b] inside it; the row is rotated at that position into out. */
+int oracle_rope_at(int64_t B, int64_t D, int64_t rot, int32_t hd, double base, const int32_t *pos,
+                   const double *v, double *out)
+{
+    if (B < 0 || D < 1 || hd < 2 || hd % 2 || rot < 0 || rot > D || rot % hd || !(base > 0.0)) return -2;
+    for (int64_t b = 0; b < B; ++b)
+        if (pos[b] < 0) return -2;
+    for (int64_t b = 0; b < B; ++b)
+        rotate_row(D, rot, hd, base, (double)pos[b], 1.0, v + b * D, out + b * D);
     return 0;
 }

@@ -555,4 +555,27 @@ def pin_rope_layer_composition(orc):
         _close(dw, _fd_grad(f, w), tol=1e-8, what="FD dw (RoPE)")
 
 
+def pin_rope_decode_reproduces_forward(orc):
+    """Decoding with the rotation at each token's position, after a packed
+    prefill of sequences of 1..6 tokens, gives the fused forward over the
+    whole sequences; positions restart per sequence."""
+    rng = _rng(23)
+    D, W, H, hd, rot, steps = 12, 3, 2, 4, 8, 3
+    lens = [1, 6, 2, 4]
+    full = [rng.standard_normal((L + steps, D)) for L in lens]
+    wf = [rng.standard_normal((L + steps, D // H, W)) for L in lens]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    xp = np.concatenate([f[:L] for f, L in zip(full, lens)])[None]
+    st = orc.state_from_prefill(xp, W, cu_seqlens=cu)
+    for j in range(steps):
+        xt = np.stack([f[L + j] for f, L in zip(full, lens)])
+        wt = np.stack([g[L + j] for g, L in zip(wf, lens)])
+        pos = np.array([L + j for L in lens])
+        yt, st = orc.headwise_rope_decode(xt, wt, st, pos, rot=rot, head_dim=hd, base=7.0, residual=True)
+        for s_, (f, g, L) in enumerate(zip(full, wf, lens)):
+            want = orc.headwise_rope_fwd(f[None, :L + j + 1], g[None, :L + j + 1], rot=rot, head_dim=hd,
+                                         base=7.0, residual=True)[0, -1]
+            _close(yt[s_], want, what=f"rotated decode, sequence {s_} step {j}")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -61,6 +61,8 @@ MUTANTS = [
      "const double p = a[h + i], q = a[h + i + hd / 2];", 1),
     ("rope_table_cos_sin_swapped", "table[(m * (hd / 2) + i) * 2 + 0] = cos(ang);",
      "table[(m * (hd / 2) + i) * 2 + 0] = sin(ang);", 1),
+    ("rope_decode_position_off_by_one", "rotate_row(D, rot, hd, base, (double)pos[b], 1.0,",
+     "rotate_row(D, rot, hd, base, (double)(pos[b] + 1), 1.0,", 1),
 ]
 
 
