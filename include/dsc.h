@@ -268,6 +268,28 @@ DSC_API dsc_status dsc_static_bwd(void *stream, int dtype, int64_t B, int64_t T,
 DSC_API dsc_status dsc_headwise_decode(void *stream, int dtype, int64_t B, int64_t D, int32_t W, int32_t H,
                                const void *x, const void *w, void *state, int32_t residual, void *y);
 
+/*
+ * One decoding step of the head-wise layer followed by the rotary embedding of
+ * the query and key channels: the serving form of dsc_headwise_rope_fwd.
+ * y is dsc_headwise_decode's output turned pair by pair (channels 2i, 2i+1 of
+ * each head of head_dim, channels < rot) by positions[b] * theta_i, with the
+ * cos / sin of table row positions[b]; the state update is that of
+ * dsc_headwise_decode.
+ *
+ *   positions  (B,) int32, in, device memory: the index of sequence b's new
+ *              token inside its sequence (after a prefill of L tokens, the
+ *              first step has position L).  A position outside [0, max_pos)
+ *              has no table row: that sequence's rotated channels of y are
+ *              set to NaN (the table is never read out of bounds).
+ *   rot, head_dim, table, max_pos  as dsc_headwise_rope_fwd (rot = 0 is
+ *              dsc_headwise_decode; head_dim is still required).
+ *   Other arguments and rules as dsc_headwise_decode.
+ */
+DSC_API dsc_status dsc_headwise_rope_decode(void *stream, int dtype, int64_t B, int64_t D, int32_t W, int32_t H,
+                                    const void *x, const void *w, void *state, int32_t residual, int64_t rot,
+                                    int32_t head_dim, const float *table, int64_t max_pos,
+                                    const int32_t *positions, void *y);
+
 /* Low-rank decoding step: z (B, R), U (R, D*W), w(b)_{d,k} = sum_r z[b,r] U[r, d*W+k]
  * formed on chip.  1 <= R <= 128. */
 DSC_API dsc_status dsc_lowrank_decode(void *stream, int dtype, int64_t B, int64_t D, int32_t W, int32_t R,

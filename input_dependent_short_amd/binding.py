@@ -48,13 +48,14 @@ def lib() -> ctypes.CDLL:
         L.dsc_lowrank_decode.argtypes = [p, i, i64, i64, i32, i32, p, p, p, p, i32, p]
         L.dsc_state_from_prefill.argtypes = [p, i, i64, i64, i64, i32, p, p, i32, p]
         L.dsc_rope_table.argtypes = [p, i64, i32, ctypes.c_double, p]
+        L.dsc_headwise_rope_decode.argtypes = [p, i, i64, i64, i32, i32, p, p, p, i32, i64, i32, p, i64, p, p]
         L.dsc_headwise_rope_fwd.argtypes = [p, i, i64, i64, i64, i32, i32, p, p, p, i32, i32, i64, i32, p, i64, p]
         L.dsc_headwise_rope_bwd.argtypes = [p, i, i64, i64, i64, i32, i32, p, p, p, p, i32, i32, i64, i32, p, i64,
                                             p, p]
         for f in ("dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd",
                   "dsc_static_fwd", "dsc_static_bwd", "dsc_headwise_decode", "dsc_lowrank_decode",
                   "dsc_state_from_prefill", "dsc_rope_table", "dsc_headwise_rope_fwd",
-                  "dsc_headwise_rope_bwd", "dsc_abi_version"):
+                  "dsc_headwise_rope_bwd", "dsc_headwise_rope_decode", "dsc_abi_version"):
             getattr(L, f).restype = ctypes.c_int
         L.dsc_status_string.argtypes = [i]
         L.dsc_status_string.restype = ctypes.c_char_p
@@ -152,6 +153,20 @@ def dsc_headwise_rope_bwd(x, w, dy, dx, dw, *, rot, head_dim, table, cu_seqlens=
     _check(lib().dsc_headwise_rope_bwd(_stream(stream), _dtype_code(x), B, T, D, W, D // G if G else 0,
                                        _ptr(x), _ptr(w), _ptr(dy), cu, ns, int(bool(residual)), int(rot),
                                        int(head_dim), tp, max_pos, _ptr(dx), _ptr(dw)))
+
+
+def dsc_headwise_rope_decode(x, w, state, y, positions, *, rot, head_dim, table, residual=False,
+                             stream=None) -> None:
+    """One decoding step (x (B,D), w (B,D/H,W), state (B,W-1,D) updated in place),
+    y rotated at positions (B,) int32 on the device."""
+    B, D = x.shape
+    G, W = w.shape[1], w.shape[2]
+    if positions.dtype != torch.int32:
+        raise TypeError("positions must be int32")
+    tp, max_pos = _table(table, head_dim)
+    _check(lib().dsc_headwise_rope_decode(_stream(stream), _dtype_code(x), B, D, W, D // G if G else 0, _ptr(x),
+                                          _ptr(w), _ptr(state), int(bool(residual)), int(rot), int(head_dim), tp,
+                                          max_pos, _ptr(positions), _ptr(y)))
 
 
 def dsc_lowrank_fwd(x, z, U, y, *, W, cu_seqlens=None, residual=False, stream=None) -> None:

@@ -36,6 +36,11 @@ struct DecParams {
     int32_t H, R;
     float rho;
     int64_t nchunks;
+    // rotary embedding of y (head-wise + rotation only): channels [0, rot) in
+    // heads of hd, table (npos, hd/2, 2), position pos[b] of sequence b's token
+    const float *rope;
+    const int32_t *pos;
+    int32_t rot, hd, npos;
 };
 
 template <int VEC, int GPT>
@@ -44,10 +49,12 @@ __device__ __forceinline__ constexpr int grp(int c) {
 }
 
 // y for one (sequence, chunk) from the input, the state slots and the
-// per-channel taps (tap 0 already includes rho); then the state shift.
-template <class E, int W>
+// per-channel taps (tap 0 already includes rho), turned by cs when ROT and
+// rotated; then the state shift.
+template <class E, int W, bool ROT = false>
 __device__ __forceinline__ void finish(const float (&xv)[E::kVec], const float (&wt)[E::kVec][W],
-                                       typename E::store_t *st, int64_t D, typename E::store_t *y) {
+                                       typename E::store_t *st, int64_t D, typename E::store_t *y,
+                                       bool rotated = false, const float (&cs)[E::kVec] = {}) {
     constexpr int VEC = E::kVec;
     float sv[W > 1 ? W - 1 : 1][VEC];
 #pragma unroll
@@ -60,6 +67,9 @@ __device__ __forceinline__ void finish(const float (&xv)[E::kVec], const float (
         for (int k = 1; k < W; ++k) a = __builtin_fmaf(wt[c][k], sv[k - 1][c], a);
         acc[c] = a;
     }
+    if constexpr (ROT) {
+        if (rotated) turn<VEC, false>(acc, cs);
+    }
     Vec16<E>::store(y, acc);
     if constexpr (W > 1) {
 #pragma unroll
@@ -69,7 +79,10 @@ __device__ __forceinline__ void finish(const float (&xv)[E::kVec], const float (
 }
 
 // Head-wise: thread = (sequence b, chunk), sequence fastest inside a chunk.
-template <class E, int W, int GPT>
+// ROPE: y of the first rot channels is then rotated at position pos[b]
+// (a table row read once); a position outside [0, npos) has no row, and the
+// sequence's rotated channels are set to NaN instead.
+template <class E, int W, int GPT, bool ROPE>
 __global__ __launch_bounds__(kBlock) void hw_decode_kernel(DecParams p) {
     using S = typename E::store_t;
     constexpr int VEC = E::kVec;
@@ -93,7 +106,20 @@ __global__ __launch_bounds__(kBlock) void hw_decode_kernel(DecParams p) {
 #pragma unroll
         for (int k = 0; k < W; ++k) wt[c][k] = wf[grp<VEC, GPT>(c) * W + k] + (k == 0 ? p.rho : 0.f);
     S *st = W > 1 ? static_cast<S *>(p.state) + b * (W - 1) * p.D + d0 : nullptr;  // no state when W = 1
-    finish<E, W>(xv, wt, st, p.D, static_cast<S *>(p.y) + b * p.D + d0);
+    float cs[VEC];
+    const bool rotated = ROPE && d0 < p.rot;
+    if constexpr (ROPE) {
+        if (rotated) {
+            const int32_t m = p.pos[b];
+            if (m >= 0 && m < p.npos) {
+                load_turn<VEC>(p.rope + m * p.hd + (int32_t)d0 % p.hd, cs);
+            } else {
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) cs[c] = __builtin_nanf("");
+            }
+        }
+    }
+    finish<E, W, ROPE>(xv, wt, st, p.D, static_cast<S *>(p.y) + b * p.D + d0, rotated, cs);
 }
 
 // Channels per low-rank decoding thread: one 16-byte run of U per rank
@@ -214,10 +240,41 @@ DecParams make_params(const DecProblem &pr) {
     p.G = pr.H > 0 ? pr.D / pr.H : 0;
     p.rho = pr.residual ? 1.f : 0.f;
     p.nchunks = pr.D / E::kVec;
+    p.rope = pr.rope;
+    p.pos = pr.pos;
+    p.rot = (int32_t)pr.rot;
+    p.hd = pr.hd;
+    p.npos = (int32_t)pr.max_pos;
     return p;
 }
 
 int64_t grid(int64_t items) { return (items + kBlock - 1) / kBlock; }
+
+template <class E, int W, bool ROPE>
+hipError_t launch_hw(const DecParams &p, int32_t H, int64_t blocks, hipStream_t st) {
+    constexpr int VEC = E::kVec;
+    if (H >= VEC) {
+        hipLaunchKernelGGL((hw_decode_kernel<E, W, 1, ROPE>), dim3((unsigned)blocks), dim3(kBlock), 0, st, p);
+    } else {
+        switch (VEC / H) {
+            case 2:
+                hipLaunchKernelGGL((hw_decode_kernel<E, W, 2, ROPE>), dim3((unsigned)blocks), dim3(kBlock), 0, st, p);
+                break;
+            case 4:
+                hipLaunchKernelGGL((hw_decode_kernel<E, W, 4, ROPE>), dim3((unsigned)blocks), dim3(kBlock), 0, st, p);
+                break;
+            case 8:
+                if constexpr (VEC >= 8) {
+                    hipLaunchKernelGGL((hw_decode_kernel<E, W, 8, ROPE>), dim3((unsigned)blocks), dim3(kBlock), 0,
+                                       st, p);
+                    break;
+                }
+                return hipErrorInvalidValue;
+            default: return hipErrorInvalidValue;
+        }
+    }
+    return hipGetLastError();
+}
 
 template <class E, int W>
 hipError_t launch_w(const DecProblem &pr, hipStream_t st) {
@@ -231,20 +288,10 @@ hipError_t launch_w(const DecProblem &pr, hipStream_t st) {
             hipLaunchKernelGGL((lr_decode_kernel<E, W, true>), dim3((unsigned)lr_blocks), dim3(kBlock), 0, st, p);
         else
             hipLaunchKernelGGL((lr_decode_kernel<E, W, false>), dim3((unsigned)lr_blocks), dim3(kBlock), 0, st, p);
-    } else if (pr.H >= VEC) {
-        hipLaunchKernelGGL((hw_decode_kernel<E, W, 1>), dim3((unsigned)blocks), dim3(kBlock), 0, st, p);
+    } else if (pr.rot > 0) {
+        return launch_hw<E, W, true>(p, pr.H, blocks, st);
     } else {
-        switch (VEC / pr.H) {
-            case 2: hipLaunchKernelGGL((hw_decode_kernel<E, W, 2>), dim3((unsigned)blocks), dim3(kBlock), 0, st, p); break;
-            case 4: hipLaunchKernelGGL((hw_decode_kernel<E, W, 4>), dim3((unsigned)blocks), dim3(kBlock), 0, st, p); break;
-            case 8:
-                if constexpr (VEC >= 8) {
-                    hipLaunchKernelGGL((hw_decode_kernel<E, W, 8>), dim3((unsigned)blocks), dim3(kBlock), 0, st, p);
-                    break;
-                }
-                return hipErrorInvalidValue;
-            default: return hipErrorInvalidValue;
-        }
+        return launch_hw<E, W, false>(p, pr.H, blocks, st);
     }
     return hipGetLastError();
 }

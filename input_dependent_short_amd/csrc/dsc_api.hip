@@ -336,23 +336,63 @@ dsc_status check_decode(int dtype, int64_t B, int64_t D, int32_t W, int32_t resi
 
 }  // namespace
 
-dsc_status dsc_headwise_decode(void *stream, int dtype, int64_t B, int64_t D, int32_t W, int32_t H,
-                               const void *x, const void *w, void *state, int32_t residual, void *y) {
+namespace {
+
+// The head-wise decoding step, with the rotation of y when rot > 0.
+dsc_status headwise_decode_call(void *stream, int dtype, int64_t B, int64_t D, int32_t W, int32_t H,
+                                const void *x, const void *w, void *state, int32_t residual, void *y, int64_t rot,
+                                int32_t head_dim, const float *table, int64_t max_pos, const int32_t *positions,
+                                const char *what) {
     DSC_TRY(check_decode(dtype, B, D, W, residual));
     if (H < 1 || D % H) return fail(DSC_ERR_SHAPE, "H = %d must divide D = %lld", H, (long long)D);
     const int vec = dtype == DSC_BF16 ? 8 : 4;
     if (H < vec ? vec % H != 0 : H % vec != 0) return fail(DSC_ERR_UNSUPPORTED, "H = %d not supported", H);
+    if (rot != 0 || head_dim != 0) {
+        if (head_dim < 2 || head_dim % 2 || head_dim > (1 << 16))
+            return fail(DSC_ERR_SHAPE, "head_dim = %d must be even, in 2..65536", head_dim);
+        if (head_dim % vec)
+            return fail(DSC_ERR_UNSUPPORTED, "head_dim = %d must be a multiple of %d for this dtype", head_dim, vec);
+        if (rot < 0 || rot > D || rot % head_dim)
+            return fail(DSC_ERR_SHAPE, "rot = %lld must be a multiple of head_dim in 0..D", (long long)rot);
+    }
     if (B == 0) return ok();
     if (!x || !w || !y || (W > 1 && !state)) return fail(DSC_ERR_NULL, "x, w, y and (W > 1) state are required");
     if (!aligned16(x) || !aligned16(w) || !aligned16(y) || !aligned16(state))
         return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    if (rot > 0) {
+        if (!table || !positions) return fail(DSC_ERR_NULL, "table and positions are required when rot > 0");
+        if (!aligned16(table) || ((uintptr_t)positions & 3u))
+            return fail(DSC_ERR_ALIGNMENT, "table must be 16-byte and positions 4-byte aligned");
+        if (max_pos < 1 || max_pos > INT32_MAX / head_dim)
+            return fail(DSC_ERR_SHAPE, "max_pos = %lld out of range", (long long)max_pos);
+    }
     const size_t es = esize(dtype), Bs = (size_t)B;
-    const Range in[] = {rng("x", x, Bs * D * es), rng("w", w, Bs * (D / H) * W * es)};
+    const Range in[] = {rng("x", x, Bs * D * es), rng("w", w, Bs * (D / H) * W * es),
+                        rng("table", table, rot > 0 ? (size_t)max_pos * head_dim * 4u : 0),
+                        rng("positions", positions, rot > 0 ? Bs * 4u : 0)};
     const Range out[] = {rng("y", y, Bs * D * es), rng("state", state, W > 1 ? Bs * (W - 1) * D * es : 0)};
-    DSC_TRY(check_alias(in, 2, out, 2));
+    DSC_TRY(check_alias(in, 4, out, 2));
     const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
-    dsc::DecProblem p{dt, B, D, W, H, 0, false, x, w, nullptr, nullptr, state, y, residual};
-    return launched(dsc::decode_step(p, (hipStream_t)stream), "dsc_headwise_decode launch");
+    dsc::DecProblem p{dt, B, D, W, H, 0, false, x, w, nullptr, nullptr, state, y, residual,
+                      rot, head_dim, table, max_pos, positions};
+    return launched(dsc::decode_step(p, (hipStream_t)stream), what);
+}
+
+}  // namespace
+
+dsc_status dsc_headwise_decode(void *stream, int dtype, int64_t B, int64_t D, int32_t W, int32_t H,
+                               const void *x, const void *w, void *state, int32_t residual, void *y) {
+    return headwise_decode_call(stream, dtype, B, D, W, H, x, w, state, residual, y, 0, 0, nullptr, 0, nullptr,
+                                "dsc_headwise_decode launch");
+}
+
+dsc_status dsc_headwise_rope_decode(void *stream, int dtype, int64_t B, int64_t D, int32_t W, int32_t H,
+                                    const void *x, const void *w, void *state, int32_t residual, int64_t rot,
+                                    int32_t head_dim, const float *table, int64_t max_pos,
+                                    const int32_t *positions, void *y) {
+    if (rot == 0 && head_dim == 0) return fail(DSC_ERR_SHAPE, "head_dim is required");
+    return headwise_decode_call(stream, dtype, B, D, W, H, x, w, state, residual, y, rot, head_dim, table, max_pos,
+                                positions, "dsc_headwise_rope_decode launch");
 }
 
 dsc_status dsc_lowrank_decode(void *stream, int dtype, int64_t B, int64_t D, int32_t W, int32_t R,

@@ -307,6 +307,55 @@ __device__ __forceinline__ int64_t xcd_block_id(int64_t b, int64_t nblocks) {
     return start + b / kXcd;
 }
 
+// ------------------------------------------------------- rotary embedding
+// Pair j of a chunk is (v[2j], v[2j+1]); a table row holds cos, sin of each
+// pair of a head in turn ("RoFormer: Enhanced Transformer with Rotary Position
+// Embedding", Su et al., Section 3.4.2).
+
+// cos, sin of a thread's VEC/2 pairs at one position (VEC floats, 16-byte
+// aligned because a chunk starts at a multiple of VEC inside its head).
+template <int VEC>
+__device__ __forceinline__ void load_turn(const float *t, float (&cs)[VEC]) {
+#pragma unroll
+    for (int i = 0; i < VEC; i += 4) {
+        const float4 v = *reinterpret_cast<const float4 *>(t + i);
+        cs[i] = v.x; cs[i + 1] = v.y; cs[i + 2] = v.z; cs[i + 3] = v.w;
+    }
+}
+
+// cs <- an (x) cs pair by pair: cos and sin of the sum of the two angles.
+template <int VEC>
+__device__ __forceinline__ void compose(float (&cs)[VEC], const float (&an)[VEC]) {
+#pragma unroll
+    for (int j = 0; j < VEC / 2; ++j) {
+        const float c1 = an[2 * j], s1 = an[2 * j + 1], c2 = cs[2 * j], s2 = cs[2 * j + 1];
+        cs[2 * j] = c1 * c2 - s1 * s2;
+        cs[2 * j + 1] = s1 * c2 + c1 * s2;
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ void set_identity(float (&cs)[VEC]) {
+#pragma unroll
+    for (int j = 0; j < VEC / 2; ++j) {
+        cs[2 * j] = 1.f;
+        cs[2 * j + 1] = 0.f;
+    }
+}
+
+// Turns every pair (v[2j], v[2j+1]) by the angle whose cos, sin are
+// cs[2j], cs[2j+1]; INV turns by the opposite angle (the transpose).
+template <int VEC, bool INV>
+__device__ __forceinline__ void turn(float (&v)[VEC], const float (&cs)[VEC]) {
+#pragma unroll
+    for (int j = 0; j < VEC / 2; ++j) {
+        const float c = cs[2 * j], s = INV ? -cs[2 * j + 1] : cs[2 * j + 1];
+        const float a = v[2 * j], b = v[2 * j + 1];
+        v[2 * j] = a * c - b * s;
+        v[2 * j + 1] = b * c + a * s;
+    }
+}
+
 // ----------------------------------------------------------- launch sizing (host)
 
 // Compute units of the current device (all devices of a process are taken

@@ -65,6 +65,13 @@ struct DecProblem {
     const void *x, *w, *z, *U;
     void *state, *y;
     int32_t residual;
+    // head-wise only: rotary embedding of y's channels [0, rot) at positions
+    // pos (B,), from the table (max_pos, hd/2, 2); rot = 0 for none
+    int64_t rot;
+    int32_t hd;
+    const float *rope;
+    int64_t max_pos;
+    const int32_t *pos;
 };
 
 // Head-wise: whether this build has a kernel for (dtype, H).

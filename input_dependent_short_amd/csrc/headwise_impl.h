@@ -136,50 +136,6 @@ __device__ __forceinline__ void group_sum(float (&v)[NW], int lanes) {
     }
 }
 
-// cos, sin of this thread's VEC/2 pairs at one position (VEC floats, 16-byte
-// aligned because a chunk starts at a multiple of VEC inside its head).
-template <int VEC>
-__device__ __forceinline__ void load_turn(const float *t, float (&cs)[VEC]) {
-#pragma unroll
-    for (int i = 0; i < VEC; i += 4) {
-        const float4 v = *reinterpret_cast<const float4 *>(t + i);
-        cs[i] = v.x; cs[i + 1] = v.y; cs[i + 2] = v.z; cs[i + 3] = v.w;
-    }
-}
-
-// cs <- an (x) cs pair by pair: cos and sin of the sum of the two angles.
-template <int VEC>
-__device__ __forceinline__ void compose(float (&cs)[VEC], const float (&an)[VEC]) {
-#pragma unroll
-    for (int j = 0; j < VEC / 2; ++j) {
-        const float c1 = an[2 * j], s1 = an[2 * j + 1], c2 = cs[2 * j], s2 = cs[2 * j + 1];
-        cs[2 * j] = c1 * c2 - s1 * s2;
-        cs[2 * j + 1] = s1 * c2 + c1 * s2;
-    }
-}
-
-template <int VEC>
-__device__ __forceinline__ void set_identity(float (&cs)[VEC]) {
-#pragma unroll
-    for (int j = 0; j < VEC / 2; ++j) {
-        cs[2 * j] = 1.f;
-        cs[2 * j + 1] = 0.f;
-    }
-}
-
-// Turns every pair (v[2j], v[2j+1]) by the angle whose cos, sin are
-// cs[2j], cs[2j+1]; INV turns by the opposite angle (the transpose).
-template <int VEC, bool INV>
-__device__ __forceinline__ void turn(float (&v)[VEC], const float (&cs)[VEC]) {
-#pragma unroll
-    for (int j = 0; j < VEC / 2; ++j) {
-        const float c = cs[2 * j], s = INV ? -cs[2 * j + 1] : cs[2 * j + 1];
-        const float a = v[2 * j], b = v[2 * j + 1];
-        v[2 * j] = a * c - b * s;
-        v[2 * j + 1] = b * c + a * s;
-    }
-}
-
 template <class E, int W, int GPT, int TT, int U, bool ROPE>
 __global__ __launch_bounds__(kBlock) void hw_fwd_kernel(HwParams p) {
     using S = typename E::store_t;

@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
     for s in ("dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd",
               "dsc_lowrank_bwd_workspace_size", "dsc_static_fwd", "dsc_static_bwd",
               "dsc_headwise_decode", "dsc_lowrank_decode", "dsc_state_from_prefill",
-              "dsc_rope_table", "dsc_headwise_rope_fwd", "dsc_headwise_rope_bwd",
+              "dsc_rope_table", "dsc_headwise_rope_fwd", "dsc_headwise_rope_bwd", "dsc_headwise_rope_decode",
               "dsc_status_string", "dsc_last_error", "dsc_abi_version"):
         assert s in syms
 
@@ -184,6 +184,17 @@ def test_rope_validation(lib):
     assert lib.dsc_rope_table(S0, 8, 32, 10000.0, None) == 1
     assert lib.dsc_rope_table(S0, 8, 32, 10000.0, ctypes.c_void_p(A + 4)) == 4
     assert lib.dsc_rope_table(S0, 0, 32, 10000.0, None) == 0
+    # rotated decoding step: B=4 sequences, D=128, heads of 32, rot = 64
+    def rd(B=4, hd=32, rot=64, tab=P(5), maxp=100, pos=P(6), y=P(4), st=P(3)):
+        return lib.dsc_headwise_rope_decode(S0, 1, B, 128, 4, 16, P(1), P(2), st, 1, rot, hd, tab, maxp, pos, y)
+    assert rd(hd=0, rot=0) == 2                      # head_dim is required
+    assert rd(hd=4) == 3 and rd(rot=48) == 2 and rd(hd=31) == 2
+    assert rd(pos=None) == 1 and rd(tab=None) == 1
+    assert rd(pos=ctypes.c_void_p(A * 6 + 2)) == 4 and rd(tab=ctypes.c_void_p(A * 5 + 8)) == 4
+    assert rd(maxp=0) == 2
+    assert rd(y=P(6)) == 5                           # y overlaps the positions
+    assert rd(st=P(5)) == 5                          # the state overlaps the table
+    assert rd(B=0) == 0
 
 
 def test_binding_raises_with_message(lib):

@@ -140,3 +140,101 @@ def test_headwise_rope_empty_batch():
     binding.dsc_headwise_rope_bwd(x, w, x, torch.empty_like(x), torch.empty_like(w), rot=64, head_dim=16,
                                   table=None)
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------ decoding
+
+# (dtype, B sequences, D, W, H, head_dim, rot)
+RD_CASES = [("bf16", 7, 2304, 4, 64, 64, 1536), ("bf16", 33, 256, 3, 2, 32, 128), ("fp32", 4, 96, 4, 1, 16, 64),
+            ("bf16", 5, 128, 1, 16, 8, 128)]
+
+
+@pytest.mark.parametrize("case", RD_CASES, ids=[f"rdec-{c[0]}-B{c[1]}D{c[2]}W{c[3]}H{c[4]}-hd{c[5]}rot{c[6]}"
+                                                for c in RD_CASES])
+def test_headwise_rope_decode_steps(case):
+    dt, B, D, W, H, hd, rot = case
+    rng = np.random.default_rng(B * 100 + D + hd)
+    tdt = inputs.DTYPES[dt]
+
+    def dev(a):
+        return torch.from_numpy(a.astype(np.float32)).to(tdt).cuda()
+
+    max_pos = 64
+    table = _table(max_pos, hd, 10000.0)
+    st0 = dev(rng.standard_normal((B, W - 1, D)))
+    state, ref_state = st0.clone(), to_f64(st0)
+    pos = rng.integers(0, max_pos - 5, size=B).astype(np.int32)
+    say(f"[rope decode] {dt} B={B} D={D} W={W} H={H} hd={hd} rot={rot}")
+    for t in range(5):
+        x = dev(rng.standard_normal((B, D)))
+        w = dev(rng.standard_normal((B, D // H, W)) / np.sqrt(W))
+        y = Guarded((B, D), tdt)
+        p = torch.from_numpy(pos + t).cuda()
+        binding.dsc_headwise_rope_decode(x, w, state, y.t, p, rot=rot, head_dim=hd, table=table,
+                                         residual=bool(t % 2))
+        torch.cuda.synchronize()
+        y.check_guards("y")
+        ry, ref_state = oracle.headwise_rope_decode(to_f64(x), to_f64(w), ref_state, pos + t, rot=rot, head_dim=hd,
+                                                    base=10000.0, residual=bool(t % 2))
+        assert_close("y", y.host(), ry, TOL[dt])
+        assert np.array_equal(to_f64(state), ref_state), f"state after step {t}"
+
+
+def test_prefill_then_rotated_decode():
+    """Packed prefill through the fused forward, the state it hands over, then
+    rotated decoding steps at positions len + j: every output equals the fused
+    forward over the whole extended sequence."""
+    D, W, H, hd, rot = 256, 4, 16, 32, 128
+    wl, inp = inputs.small("headwise", 1, 300, D, W, H=H, dtype="bf16", residual=True, varlen=True,
+                           seglen_range=(1, 40), seed=17)
+    cu = inp["cu_seqlens"]
+    S = len(cu) - 1
+    lens = np.diff(cu).astype(np.int32)
+    table = _table(400, hd, 10000.0)
+    x, w = inp["x"].cuda(), inp["w"].cuda()
+    cu_d = torch.from_numpy(cu).cuda()
+    say(f"[rope decode] prefill of {S} sequences, then 3 rotated steps")
+    y = torch.empty_like(x)
+    binding.dsc_headwise_rope_fwd(x, w, y, rot=rot, head_dim=hd, table=table, cu_seqlens=cu_d, residual=True)
+    state = torch.empty(S, W - 1, D, dtype=x.dtype, device="cuda")
+    binding.dsc_state_from_prefill(x, state, W=W, cu_seqlens=cu_d)
+    x64, w64 = to_f64(inp["x"]), to_f64(inp["w"])
+    assert_close("prefill y", to_f64(y), oracle.headwise_rope_fwd(x64, w64, rot=rot, head_dim=hd, cu_seqlens=cu,
+                                                                   residual=True), TOL["bf16"])
+    rng = np.random.default_rng(8)
+    seqs = [(x64[0, a:b], w64[0, a:b]) for a, b in zip(cu[:-1], cu[1:])]
+    for j in range(3):
+        xt = torch.from_numpy(rng.standard_normal((S, D)).astype(np.float32)).to(torch.bfloat16).cuda()
+        wt = torch.from_numpy((rng.standard_normal((S, D // H, W)) / 2).astype(np.float32)).to(torch.bfloat16).cuda()
+        yt = torch.empty_like(xt)
+        binding.dsc_headwise_rope_decode(xt, wt, state, yt, torch.from_numpy(lens + j).cuda(), rot=rot, head_dim=hd,
+                                         table=table, residual=True)
+        torch.cuda.synchronize()
+        xt64, wt64 = to_f64(xt), to_f64(wt)
+        seqs = [(np.vstack([sx, xt64[s][None]]), np.concatenate([sw, wt64[s][None]])) for s, (sx, sw) in enumerate(seqs)]
+        want = np.stack([oracle.headwise_rope_fwd(sx[None], sw[None], rot=rot, head_dim=hd, residual=True)[0, -1]
+                         for sx, sw in seqs])
+        assert_close("y", to_f64(yt), want, TOL["bf16"])
+
+
+def test_rotated_decode_position_outside_the_table():
+    """A position with no table row gives NaN in that sequence's rotated
+    channels only; the other channels, the other sequences and the state are
+    those of the plain step."""
+    B, D, W, H, hd, rot = 4, 128, 4, 16, 32, 64
+    g = torch.Generator().manual_seed(4)
+    x = torch.randn(B, D, generator=g).to(torch.bfloat16).cuda()
+    w = torch.randn(B, D // H, W, generator=g).to(torch.bfloat16).cuda()
+    st0 = torch.randn(B, W - 1, D, generator=g).to(torch.bfloat16).cuda()
+    table = _table(10, hd, 10000.0)
+    pos = torch.tensor([-1, 10, 3, 9], dtype=torch.int32).cuda()
+    s1, s2 = st0.clone(), st0.clone()
+    y1, y2 = torch.empty_like(x), torch.empty_like(x)
+    binding.dsc_headwise_rope_decode(x, w, s1, y1, pos, rot=rot, head_dim=hd, table=table)
+    binding.dsc_headwise_decode(x, w, s2, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    assert torch.isnan(y1[:2, :rot]).all() and not torch.isnan(y1[2:]).any()
+    assert torch.equal(y1[:, rot:], y2[:, rot:])
+    want = oracle.rope_at(to_f64(y2[2:]), [3, 9], rot=rot, head_dim=hd)
+    assert_close("in-range rows", to_f64(y1[2:]), want, TOL["bf16"])
