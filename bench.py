@@ -486,9 +486,18 @@ def main() -> int:
         state = torch.zeros(S_DEC, Wd - 1, D, dtype=xd.dtype, device="cuda")
         es = xd.element_size()
         act = S_DEC * D * es
+        # the rotated step: queries and keys (channels [0, 1536), heads of 64) at
+        # positions 1000 + b, cos / sin rows read once per (sequence, chunk)
+        dec_table = torch.empty(2048, 32, 2, dtype=torch.float32, device="cuda")
+        binding.dsc_rope_table(dec_table)
+        dec_pos = torch.arange(1000, 1000 + S_DEC, dtype=torch.int32, device="cuda")
         dec_calls = {
             "headwise-qkv-150m": (lambda: binding.dsc_headwise_decode(xd, wd, state, yd, residual=True),
                                   2 * act + 2 * (Wd - 1) * act + wd.numel() * es),
+            "headwise-rope-qkv-150m": (lambda: binding.dsc_headwise_rope_decode(
+                                           xd, wd, state, yd, dec_pos, rot=1536, head_dim=64, table=dec_table,
+                                           residual=True),
+                                       2 * act + 2 * (Wd - 1) * act + wd.numel() * es + S_DEC * 4),
             "lowrank-qkv-150m": (lambda: binding.dsc_lowrank_decode(xd, zd, lrc.U, state, yd, W=Wd),
                                  2 * act + 2 * (Wd - 1) * act + zd.numel() * es + lrc.U.numel() * es),
         }
