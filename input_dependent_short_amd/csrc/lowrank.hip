@@ -487,6 +487,12 @@ __device__ __forceinline__ uint2 lds_read_tr(const unsigned char *addr) {
 
 template <bool V> struct MaskTag { static constexpr bool value = V; };
 
+// Whether the backward's walk may end after any 32-token pair rather than
+// after a whole ring of prefetch steps.  Only the two-half, 16-byte z variant
+// takes it: in the other instances the early exit makes the compiler spill
+// (the R = 64 kernel ran twice as long), so they walk whole rings.
+constexpr bool bwd_exact_walk(int H, bool RVEC) { return H == 2 && RVEC; }
+
 template <int W, int RC, int P, bool RVEC, int H>
 __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void lr_bwd_mfma(LrParams p, int64_t nslices,
                                                                                          int64_t tok_per_half) {
@@ -507,11 +513,13 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
     const int64_t bbeg = tchunk * H * tok_per_half;  // the block's first token
     const int64_t nbeg = bbeg + half * tok_per_half;
     const int64_t nend = min(nbeg + tok_per_half, p.N);  // may be <= nbeg in the last block's second half
-    // steps of both halves: whole rings of P steps over the first half's
-    // range, so all waves meet the same barriers (steps past nend read zeros
-    // past N, store nothing past nend, and add nothing to dz or dU)
+    // steps of both halves, from the first half's range, so all waves meet the
+    // same barriers (steps past nend read zeros past N, store nothing past
+    // nend, and add nothing to dz or dU): whole 32-token pairs when the walk
+    // may end inside a ring (kExactWalk), else whole rings of P steps
+    constexpr bool kExactWalk = bwd_exact_walk(H, RVEC);
     const int64_t len0 = min(tok_per_half, p.N - bbeg);
-    const int64_t nsteps = ((len0 + 16 * P - 1) / (16 * P)) * P;
+    const int64_t nsteps = kExactWalk ? ((len0 + 31) / 32) * 2 : ((len0 + 16 * P - 1) / (16 * P)) * P;
 
     const int tok = lane & 15;
     const int q = lane >> 4;
@@ -830,6 +838,9 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
                     }
                 }
             }
+            if constexpr (kExactWalk) {
+                if (ps == 1 && s + 1 >= nsteps) break;  // the walk's last pair (block-uniform)
+            }
         }
     }
 
@@ -998,7 +1009,9 @@ hipError_t mfma_bwd(const LrProblem &pr, hipStream_t st) {
     static const int bpc_gather = blocks_per_cu(reinterpret_cast<const void *>(&lr_bwd_mfma<W, RC, kBwdRing, false, H>),
                                                 kBlock * H);
     const int64_t slots = (int64_t)device_cus() * (p.R % 8 == 0 ? bpc_vec : bpc_gather);
-    const int64_t block_len = walk_length(p.N, ngroups, slots, H * cap, H * 16 * kBwdRing, H * kBlockFixedTokens);
+    // walk unit: a 32-token pair per half where the walk may stop there, else a ring
+    const int64_t unit = bwd_exact_walk(H, p.R % 8 == 0) ? H * 32 : H * 16 * kBwdRing;
+    const int64_t block_len = walk_length(p.N, ngroups, slots, H * cap, unit, H * kBlockFixedTokens);
     const int64_t tph = block_len / H;  // tokens per half
     const int64_t tchunks = (p.N + block_len - 1) / block_len;
     // one launch clears dU and the dz accumulator
