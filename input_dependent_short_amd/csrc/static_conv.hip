@@ -214,16 +214,14 @@ __global__ __launch_bounds__(kBlock) void st_bwd_kernel(StParams p) {
 
         int64_t s, e;
         p.seq.find(n0, s, e);
-        float ring[RW][VEC];  // ring[i] = x[m-1-i], zero before m's sequence
+        // raw rows, widened where they are used: ring[i] = x[m-1-i], zero
+        // before m's sequence
+        uint4 ring[RW];
 #pragma unroll
         for (int i = 0; i < W - 1; ++i) {
             const int64_t t = n0 - 1 - i;
-            if (t >= s) {
-                load_vec<E>(x + t * p.D, ring[i]);
-            } else {
-#pragma unroll
-                for (int c = 0; c < VEC; ++c) ring[i][c] = 0.f;
-            }
+            ring[i] = make_uint4(0u, 0u, 0u, 0u);
+            if (t >= s) ring[i] = *reinterpret_cast<const uint4 *>(x + t * p.D);
         }
         // raw 16-byte rows, zero past the end (a branch, not a select between
         // addresses, so the load stays a global load)
@@ -251,9 +249,7 @@ __global__ __launch_bounds__(kBlock) void st_bwd_kernel(StParams p) {
                     if (m >= e) {  // m starts the next sequence
                         p.seq.find(m, s, e);
 #pragma unroll
-                        for (int i = 0; i < RW; ++i)
-#pragma unroll
-                            for (int c = 0; c < VEC; ++c) ring[i][c] = 0.f;
+                        for (int i = 0; i < RW; ++i) ring[i] = make_uint4(0u, 0u, 0u, 0u);
                     }
                     // dx: taps k with m+k in m's sequence (all of them unless m is
                     // among its sequence's last W-1 tokens)
@@ -284,11 +280,11 @@ __global__ __launch_bounds__(kBlock) void st_bwd_kernel(StParams p) {
                         const float gv = elem<E>(gw[u], c), xc = elem<E>(xv[u], c);
                         part[c][0] = __builtin_fmaf(gv, xc, part[c][0]);
 #pragma unroll
-                        for (int k = 1; k < W; ++k) part[c][k] = __builtin_fmaf(gv, ring[k - 1][c], part[c][k]);
-#pragma unroll
-                        for (int i = W - 2; i > 0; --i) ring[i][c] = ring[i - 1][c];
-                        if constexpr (W > 1) ring[0][c] = xc;
+                        for (int k = 1; k < W; ++k) part[c][k] = __builtin_fmaf(gv, elem<E>(ring[k - 1], c), part[c][k]);
                     }
+#pragma unroll
+                    for (int i = W - 2; i > 0; --i) ring[i] = ring[i - 1];
+                    if constexpr (W > 1) ring[0] = xv[u];
                 }
             }
 #pragma unroll
@@ -332,7 +328,9 @@ __global__ __launch_bounds__(kBlock) void st_zero(float *p, int64_t n) {
 #endif
 constexpr int kStTT = DSC_ST_TT;  // tokens per thread tile
 constexpr int kStU = 4;           // tokens per load batch (forward)
-constexpr int kStUb = 2;          // tokens per load batch (backward)
+// tokens per load batch (backward): 4, or 2 where the W*VEC dc partials of a
+// wider filter leave no room for the deeper batch
+constexpr int st_bwd_batch(int W) { return W <= 4 ? 4 : 2; }
 
 template <class E>
 StParams make_params(const StProblem &pr) {
@@ -372,7 +370,8 @@ hipError_t launch(const StProblem &pr, hipStream_t st, bool bwd) {
     hipLaunchKernelGGL(st_zero, dim3((unsigned)((nz + 4 * kBlock - 1) / (4 * kBlock))), dim3(kBlock), 0, st, pr.dc, nz);
     const int64_t tpb = kBlock / p.cb;
     const int64_t blocks = (p.ntiles + tpb - 1) / tpb * p.ncg;  // none for an empty batch
-    if (blocks) hipLaunchKernelGGL((st_bwd_kernel<E, W, kStTT, kStUb>), dim3((unsigned)blocks), dim3(kBlock), 0, st, p);
+    if (blocks)
+        hipLaunchKernelGGL((st_bwd_kernel<E, W, kStTT, st_bwd_batch(W)>), dim3((unsigned)blocks), dim3(kBlock), 0, st, p);
     return hipGetLastError();
 }
 
