@@ -89,6 +89,46 @@ __host__ __device__ constexpr int pow2_align(int n) {
 
 // Contiguous span of NE elements starting at an address aligned to ALIGN bytes:
 // loaded / stored with the widest aligned accesses.
+// NE elements kept as raw 32-bit words (bf16 pairs or fp32), widened on use.
+template <class E, int NE>
+struct RawSpan {
+    using S = typename E::store_t;
+    static constexpr int kBytes = NE * (int)sizeof(S);
+    static constexpr int kWords = (kBytes + 3) / 4;
+    template <int ALIGN>
+    __device__ __forceinline__ static void load(const S *p, uint32_t (&w)[kWords]) {
+        constexpr int A = ALIGN < kBytes ? ALIGN : pow2_align(kBytes);
+        if constexpr (A < 4) {  // 2-byte elements, 2-byte aligned
+            const uint16_t *h = reinterpret_cast<const uint16_t *>(p);
+#pragma unroll
+            for (int i = 0; i < kWords; ++i) {
+                const uint32_t lo = h[2 * i];
+                const uint32_t hi = 2 * i + 1 < NE ? (uint32_t)h[2 * i + 1] : 0u;
+                w[i] = lo | (hi << 16);
+            }
+            return;
+        }
+        constexpr int WPL = A >= 16 ? 4 : (A >= 4 ? A / 4 : 1);  // words per load
+#pragma unroll
+        for (int i = 0; i < kWords; i += WPL) {
+            const uint32_t *q = reinterpret_cast<const uint32_t *>(p) + i;
+            if constexpr (WPL == 4) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(q);
+                w[i] = v.x; w[i + 1] = v.y; w[i + 2] = v.z; w[i + 3] = v.w;
+            } else if constexpr (WPL == 2) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(q);
+                w[i] = v.x; w[i + 1] = v.y;
+            } else {
+                w[i] = *q;
+            }
+        }
+    }
+    __device__ __forceinline__ static float at(const uint32_t (&w)[kWords], int i) {
+        if constexpr (sizeof(S) == 4) return __uint_as_float(w[i]);
+        else return (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
+    }
+};
+
 template <class E, int NE>
 struct Span {
     using S = typename E::store_t;

@@ -189,19 +189,23 @@ __global__ __launch_bounds__(kBlock) void hw_fwd_kernel(HwParams p) {
     }
 
     // two batches of U tokens in flight: compute one while the next loads
+    // filters stay raw words until used: as fp32 the two batches' filters
+    // held 16 more registers (W = 4), which cost a wave per SIMD
+    using WS = RawSpan<E, NW>;
+    constexpr int NWW = WS::kWords;
     uint4 xa[U], xb[U];
-    float wa[U][NW], wb[U][NW];
-    auto load_batch = [&](int64_t nb, uint4 (&xr)[U], float (&wr)[U][NW]) {
+    uint32_t wa[U][NWW], wb[U][NWW];
+    auto load_batch = [&](int64_t nb, uint4 (&xr)[U], uint32_t (&wr)[U][NWW]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t n = nb + u;
             if (n < n1) {
                 xr[u] = load_raw<E>(x + n * p.D);
-                Span<E, NW>::template load<WALIGN>(w + n * p.G * W, wr[u]);
+                WS::template load<WALIGN>(w + n * p.G * W, wr[u]);
             }
         }
     };
-    auto compute_batch = [&](int64_t nb, const uint4 (&xr)[U], const float (&wr)[U][NW]) {
+    auto compute_batch = [&](int64_t nb, const uint4 (&xr)[U], const uint32_t (&wr)[U][NWW]) {
         // the batch's offset rows, all requested before the first is used;
         // bit u of later: token u's sequence starts after n0 (no anchor)
         float cs[U][VEC];
@@ -235,7 +239,7 @@ __global__ __launch_bounds__(kBlock) void hw_fwd_kernel(HwParams p) {
                     const bool ok = k <= nv;
 #pragma unroll
                     for (int c = 0; c < VEC; ++c) {
-                        const float wk = ok ? wr[u][grp<VEC, GPT>(c) * W + k] : 0.f;
+                        const float wk = ok ? WS::at(wr[u], grp<VEC, GPT>(c) * W + k) : 0.f;
                         const float xk = k == 0 ? xv[c] : ring[k - 1][c];
                         acc[c] = __builtin_fmaf(wk, xk, acc[c]);
                     }
@@ -328,16 +332,18 @@ __global__ __launch_bounds__(kBlock) void hw_bwd_kernel(HwParams p) {
         ring[i] = t >= s ? load_raw<E>(x + t * p.D) : zero4;
     }
     // look-ahead window: slot i holds token mb + i
+    using WS = RawSpan<E, NW>;  // filters as raw words, widened where used
+    constexpr int NWW = WS::kWords;
     uint4 gw[WIN];
-    float ww[WIN][NW];
+    uint32_t ww[WIN][NWW];
     auto load_gw = [&](int64_t t, int slot) {
         if (t < p.N) {
             gw[slot] = load_raw<E>(g + t * p.D);
-            Span<E, NW>::template load<WALIGN>(w + t * p.G * W, ww[slot]);
+            WS::template load<WALIGN>(w + t * p.G * W, ww[slot]);
         } else {
             gw[slot] = zero4;
 #pragma unroll
-            for (int c = 0; c < NW; ++c) ww[slot][c] = 0.f;
+            for (int c = 0; c < NWW; ++c) ww[slot][c] = 0u;
         }
     };
     // ROPE: the window holds dy turned back, in fp32 (gf); cos / sin of a
@@ -417,7 +423,7 @@ __global__ __launch_bounds__(kBlock) void hw_bwd_kernel(HwParams p) {
                     const bool ok = k < ahead;
 #pragma unroll
                     for (int c = 0; c < VEC; ++c) {
-                        const float wk = ok ? ww[u + k][grp<VEC, GPT>(c) * W + k] : 0.f;
+                        const float wk = ok ? WS::at(ww[u + k], grp<VEC, GPT>(c) * W + k) : 0.f;
                         float gk;
                         if constexpr (ROPE) gk = gf[u + k][c];
                         else gk = k == 0 ? gm[c] : lane_elem<E>(gw[u + k], c);
@@ -460,7 +466,7 @@ __global__ __launch_bounds__(kBlock) void hw_bwd_kernel(HwParams p) {
                 gw[i] = gw[U + i];
             }
 #pragma unroll
-            for (int c = 0; c < NW; ++c) ww[i][c] = ww[U + i][c];
+            for (int c = 0; c < NWW; ++c) ww[i][c] = ww[U + i][c];
         }
     }
 }
