@@ -69,6 +69,18 @@ __device__ __forceinline__ void load_taps(const typename E::store_t *c, float rh
     for (int i = 0; i < VEC; ++i) cf[i][0] += rho;
 }
 
+// Element c of a raw 16-byte vector, widened to fp32.
+template <class E>
+__device__ __forceinline__ float elem(const uint4 &v, int c) {
+    constexpr int PW = E::kVec / 4;  // elements per 32-bit word
+    const uint32_t w = c < PW ? v.x : c < 2 * PW ? v.y : c < 3 * PW ? v.z : v.w;
+    if constexpr (PW == 1) {
+        return __uint_as_float(w);
+    } else {
+        return (c & 1) ? bf16_hi(w) : bf16_lo(w);
+    }
+}
+
 // Forward: thread = (tile of TT tokens, chunk); batches of U tokens are
 // loaded one batch ahead of the arithmetic.
 template <class E, int W, int TT, int U>
@@ -92,25 +104,22 @@ __global__ __launch_bounds__(kBlock) void st_fwd_kernel(StParams p) {
 
     int64_t s, e;
     p.seq.find(n0, s, e);
-    float ring[RW][VEC];  // ring[i] = x[n-1-i], zero before n's sequence
+    // inputs stay raw 16-byte rows until used (widened per use)
+    uint4 ring[RW];  // ring[i] = x[n-1-i], zero before n's sequence
 #pragma unroll
     for (int i = 0; i < W - 1; ++i) {
         const int64_t t = n0 - 1 - i;
-        if (t >= s) {
-            load_vec<E>(x + t * p.D, ring[i]);
-        } else {
-#pragma unroll
-            for (int c = 0; c < VEC; ++c) ring[i][c] = 0.f;
-        }
+        ring[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (t >= s) ring[i] = *reinterpret_cast<const uint4 *>(x + t * p.D);
     }
 
-    float xa[U][VEC], xb[U][VEC];
-    auto load_batch = [&](int64_t nb, float (&xr)[U][VEC]) {
+    uint4 xa[U], xb[U];
+    auto load_batch = [&](int64_t nb, uint4 (&xr)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (nb + u < n1) load_vec<E>(x + (nb + u) * p.D, xr[u]);
+            if (nb + u < n1) xr[u] = *reinterpret_cast<const uint4 *>(x + (nb + u) * p.D);
     };
-    auto compute_batch = [&](int64_t nb, const float (&xr)[U][VEC]) {
+    auto compute_batch = [&](int64_t nb, const uint4 (&xr)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t n = nb + u;
@@ -118,27 +127,20 @@ __global__ __launch_bounds__(kBlock) void st_fwd_kernel(StParams p) {
                 if (n >= e) {  // n starts the next sequence: earlier inputs do not reach it
                     p.seq.find(n, s, e);
 #pragma unroll
-                    for (int i = 0; i < RW; ++i)
-#pragma unroll
-                        for (int c = 0; c < VEC; ++c) ring[i][c] = 0.f;
+                    for (int i = 0; i < RW; ++i) ring[i] = make_uint4(0u, 0u, 0u, 0u);
                 }
                 float acc[VEC];
 #pragma unroll
                 for (int c = 0; c < VEC; ++c) {
-                    float a = cf[c][0] * xr[u][c];
+                    float a = cf[c][0] * elem<E>(xr[u], c);
 #pragma unroll
-                    for (int k = 1; k < W; ++k) a = __builtin_fmaf(cf[c][k], ring[k - 1][c], a);
+                    for (int k = 1; k < W; ++k) a = __builtin_fmaf(cf[c][k], elem<E>(ring[k - 1], c), a);
                     acc[c] = a;
                 }
                 Vec16<E>::store(y + n * p.D, acc);
 #pragma unroll
-                for (int i = W - 2; i > 0; --i)
-#pragma unroll
-                    for (int c = 0; c < VEC; ++c) ring[i][c] = ring[i - 1][c];
-                if constexpr (W > 1) {
-#pragma unroll
-                    for (int c = 0; c < VEC; ++c) ring[0][c] = xr[u][c];
-                }
+                for (int i = W - 2; i > 0; --i) ring[i] = ring[i - 1];
+                if constexpr (W > 1) ring[0] = xr[u];
             }
         }
     };
@@ -153,17 +155,6 @@ __global__ __launch_bounds__(kBlock) void st_fwd_kernel(StParams p) {
     }
 }
 
-// Element c of a raw 16-byte vector, widened to fp32.
-template <class E>
-__device__ __forceinline__ float elem(const uint4 &v, int c) {
-    constexpr int PW = E::kVec / 4;  // elements per 32-bit word
-    const uint32_t w = c < PW ? v.x : c < 2 * PW ? v.y : c < 3 * PW ? v.z : v.w;
-    if constexpr (PW == 1) {
-        return __uint_as_float(w);
-    } else {
-        return (c & 1) ? bf16_hi(w) : bf16_lo(w);
-    }
-}
 
 constexpr int kRedFloats = 32 * (kBlock + kBlock / 8);  // LDS of the dc reduction, any chunks-per-block
 
