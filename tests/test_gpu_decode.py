@@ -54,7 +54,7 @@ def test_headwise_decode_steps(case):
 
 # (dtype, B sequences, D, W, R)
 LR_DEC = [("bf16", 1, 64, 4, 32), ("bf16", 8, 2304, 4, 32), ("bf16", 70, 512, 4, 64), ("bf16", 3, 128, 2, 5),
-          ("bf16", 2, 256, 8, 128), ("fp32", 4, 64, 4, 16), ("fp32", 1, 32, 1, 3)]
+          ("bf16", 2, 256, 8, 128), ("fp32", 4, 64, 4, 16), ("fp32", 1, 32, 1, 3), ("bf16", 5, 256, 3, 16)]
 
 
 @pytest.mark.parametrize("case", LR_DEC, ids=[f"lr-{c[0]}-B{c[1]}D{c[2]}W{c[3]}R{c[4]}" for c in LR_DEC])
