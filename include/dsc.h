@@ -35,7 +35,7 @@
  *               be 0 (an empty batch): the call then computes nothing
  *               except that the low-rank and static backward zero-fill dU
  *               and dc, and the pointers of tensors without elements may
- *               be NULL.
+ *               be NULL.  Decoding calls take B sequences of one token.
  *   W           taps, 1..8.
  *   cu_seqlens  NULL with n_seqs == 0: each of the B rows is one sequence.
  *               Otherwise a DEVICE pointer to int32[n_seqs+1] strictly
@@ -45,7 +45,8 @@
  *               The contents are not validated (a malformed array gives
  *               undefined results).
  *   residual    0 or 1 (rho above).
- *   pointers    DEVICE pointers, each 16-byte aligned.  The caller owns all
+ *   pointers    DEVICE pointers, each 16-byte aligned (the int32 arrays
+ *               cu_seqlens and positions: 4-byte).  The caller owns all
  *               memory; the library allocates nothing, keeps no state and
  *               is thread-safe.  Inputs are never written.  Every output is
  *               fully overwritten (nothing accumulates into it), except the
