@@ -435,13 +435,28 @@ __global__ __launch_bounds__(kBlock) void hw_bwd_kernel(HwParams p) {
                 float part[NW];
 #pragma unroll
                 for (int i = 0; i < NW; ++i) part[i] = 0.f;
+                // bf16 with filter groups of whole channel pairs: the dw partials are
+                // 2-term dot products of the packed dy and x words (fp32 sums, no
+                // widening); otherwise fp32 multiply-adds of the widened values
+                constexpr bool DOT = VEC == 8 && GPT <= 4 && !ROPE;
 #pragma unroll
                 for (int k = 0; k < W; ++k) {
                     const uint4 &xr = k == 0 ? xv[u] : ring[k - 1];
+                    if constexpr (DOT) {
+                        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+                        const uint32_t xw[4] = {xr.x, xr.y, xr.z, xr.w};
+                        const uint32_t gd[4] = {gw[u].x, gw[u].y, gw[u].z, gw[u].w};
 #pragma unroll
-                    for (int c = 0; c < VEC; ++c)
-                        part[grp<VEC, GPT>(c) * W + k] =
-                            __builtin_fmaf(gm[c], lane_elem<E>(xr, c), part[grp<VEC, GPT>(c) * W + k]);
+                        for (int j = 0; j < 4; ++j)
+                            part[grp<VEC, GPT>(2 * j) * W + k] = __builtin_amdgcn_fdot2_f32_bf16(
+                                __builtin_bit_cast(bf2, gd[j]), __builtin_bit_cast(bf2, xw[j]),
+                                part[grp<VEC, GPT>(2 * j) * W + k], false);
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < VEC; ++c)
+                            part[grp<VEC, GPT>(c) * W + k] =
+                                __builtin_fmaf(gm[c], lane_elem<E>(xr, c), part[grp<VEC, GPT>(c) * W + k]);
+                    }
                 }
                 group_sum<NW>(part, p.lanes);
 #pragma unroll
