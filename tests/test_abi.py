@@ -218,3 +218,15 @@ def test_empty_batch_is_a_no_op(lib):
                                None, None, None, None, 0) == 1   # dU is still required
     assert st_fwd(lib, B=0, x=None, c=None, y=None) == 0
     assert st_bwd(lib, T=0, x=None, c=None, dy=None, dx=None, dc=None) == 1   # dc is still required
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """No fallback: without libdsc.so every binding call raises."""
+    import torch
+    from input_dependent_short_amd import binding
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "absent" / "libdsc.so"))
+    monkeypatch.setattr(binding, "_lib", None)
+    x = torch.zeros(1, 8, 64, dtype=torch.bfloat16)
+    w = torch.zeros(1, 8, 8, 4, dtype=torch.bfloat16)
+    with pytest.raises(ImportError, match="not built"):
+        binding.dsc_headwise_fwd(x, w, x, stream=0)
