@@ -205,12 +205,46 @@ DSC_API size_t dsc_lowrank_bwd_workspace_size(int dtype, int64_t B, int64_t T, i
  *   workspace: device memory of at least dsc_lowrank_bwd_workspace_size()
  *   bytes, 16-byte aligned, contents undefined on entry and exit; it must not
  *   overlap any argument.  dz and dU are sums over many partial products
- *   accumulated with fp32 atomics: their last bits may differ run to run.
+ *   accumulated with fp32 atomics: their last bits may differ run to run
+ *   (dsc_lowrank_bwd_deterministic below gives reproducible ones).
  */
 DSC_API dsc_status dsc_lowrank_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
                            int32_t R, const void *x, const void *z, const void *U, const void *dy,
                            const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, void *dx,
                            void *dz, float *dU, void *workspace, size_t workspace_bytes);
+
+/*
+ * Bytes of device workspace dsc_lowrank_bwd_deterministic needs for these
+ * sizes and dtype (0 for invalid sizes, and where no workspace is needed).
+ * It depends on the sizes and dtype only, not on the device: for DSC_BF16
+ * shapes that the matrix-core kernel serves (R <= 32, or R <= 64 with W <= 4)
+ * it holds one fp32 (B*T, R) region of dz per block of 128 channels and one
+ * fp32 (R, D*W) region of dU per token chunk of the work split; otherwise 0.
+ * At B*T = 16384, D = 2304, W = 4, R = 32 that is about 55 MB.
+ */
+DSC_API size_t dsc_lowrank_bwd_deterministic_workspace_size(int dtype, int64_t B, int64_t T, int64_t D,
+                                                            int32_t W, int32_t R);
+
+/*
+ * The low-rank backward above with dz and dU summed in one fixed order, so
+ * that equal inputs give bitwise equal outputs on every call and on every
+ * device.  The same per-block partial sums as dsc_lowrank_bwd are formed;
+ * instead of fp32 atomics into one accumulator, each block's partials go to
+ * a workspace region of their own (each element written once) and a
+ * following launch adds the regions in ascending order (dz: channel blocks,
+ * dU: token chunks).  Where the generic kernels serve the shape (DSC_FP32,
+ * and the other bf16 shapes) one thread forms each dz and dU element,
+ * adding its terms in a fixed order.  dx is the same as dsc_lowrank_bwd's.
+ * Arguments, layouts and errors as for dsc_lowrank_bwd, with the workspace
+ * sized by dsc_lowrank_bwd_deterministic_workspace_size() (may be NULL when
+ * that is 0).  Costs extra HBM traffic: the partial regions are cleared,
+ * written and read back (about 110 MB more at the sizes above).
+ */
+DSC_API dsc_status dsc_lowrank_bwd_deterministic(void *stream, int dtype, int64_t B, int64_t T, int64_t D,
+                                                 int32_t W, int32_t R, const void *x, const void *z,
+                                                 const void *U, const void *dy, const int32_t *cu_seqlens,
+                                                 int32_t n_seqs, int32_t residual, void *dx, void *dz, float *dU,
+                                                 void *workspace, size_t workspace_bytes);
 
 /*
  * Static short convolution: the fixed-filter layer that the dynamic one

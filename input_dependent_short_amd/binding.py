@@ -42,6 +42,9 @@ def lib() -> ctypes.CDLL:
         L.dsc_lowrank_bwd_workspace_size.restype = ctypes.c_size_t
         L.dsc_lowrank_bwd.argtypes = [p, i, i64, i64, i64, i32, i32, p, p, p, p, p, i32, i32, p, p, p,
                                       p, ctypes.c_size_t]
+        L.dsc_lowrank_bwd_deterministic_workspace_size.argtypes = [i, i64, i64, i64, i32, i32]
+        L.dsc_lowrank_bwd_deterministic_workspace_size.restype = ctypes.c_size_t
+        L.dsc_lowrank_bwd_deterministic.argtypes = L.dsc_lowrank_bwd.argtypes
         L.dsc_static_fwd.argtypes = [p, i, i64, i64, i64, i32, p, p, p, i32, i32, p]
         L.dsc_static_bwd.argtypes = [p, i, i64, i64, i64, i32, p, p, p, p, i32, i32, p, p]
         L.dsc_headwise_decode.argtypes = [p, i, i64, i64, i32, i32, p, p, p, i32, p]
@@ -53,6 +56,7 @@ def lib() -> ctypes.CDLL:
         L.dsc_headwise_rope_bwd.argtypes = [p, i, i64, i64, i64, i32, i32, p, p, p, p, i32, i32, i64, i32, p, i64,
                                             p, p]
         for f in ("dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd",
+                  "dsc_lowrank_bwd_deterministic",
                   "dsc_static_fwd", "dsc_static_bwd", "dsc_headwise_decode", "dsc_lowrank_decode",
                   "dsc_state_from_prefill", "dsc_rope_table", "dsc_headwise_rope_fwd",
                   "dsc_headwise_rope_bwd", "dsc_headwise_rope_decode", "dsc_abi_version"):
@@ -192,6 +196,24 @@ def dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, workspace=None, *, W, cu_seqlens=No
     _check(lib().dsc_lowrank_bwd(_stream(stream), _dtype_code(x), B, T, D, W, R, _ptr(x), _ptr(z),
                                  _ptr(U), _ptr(dy), cu, ns, int(bool(residual)), _ptr(dx), _ptr(dz),
                                  _ptr(dU), _ptr(workspace), ws_bytes))
+
+
+def dsc_lowrank_bwd_deterministic_workspace_size(dtype: torch.dtype, B: int, T: int, D: int, W: int,
+                                                 R: int) -> int:
+    code = DSC_BF16 if dtype == torch.bfloat16 else DSC_FP32
+    return int(lib().dsc_lowrank_bwd_deterministic_workspace_size(code, B, T, D, W, R))
+
+
+def dsc_lowrank_bwd_deterministic(x, z, U, dy, dx, dz, dU, workspace=None, *, W, cu_seqlens=None,
+                                  residual=False, stream=None) -> None:
+    """dsc_lowrank_bwd with dz and dU summed in a fixed order (bitwise reproducible)."""
+    B, T, D = x.shape
+    R = z.shape[2]
+    cu, ns = _seq(cu_seqlens)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().dsc_lowrank_bwd_deterministic(_stream(stream), _dtype_code(x), B, T, D, W, R, _ptr(x), _ptr(z),
+                                               _ptr(U), _ptr(dy), cu, ns, int(bool(residual)), _ptr(dx),
+                                               _ptr(dz), _ptr(dU), _ptr(workspace), ws_bytes))
 
 
 def dsc_static_fwd(x, c, y, *, cu_seqlens=None, residual=False, stream=None) -> None:

@@ -242,16 +242,19 @@ size_t dsc_lowrank_bwd_workspace_size(int dtype, int64_t B, int64_t T, int64_t D
     return dsc::lowrank_bwd_workspace(dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32, B * T, D, W, R);
 }
 
-dsc_status dsc_lowrank_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
-                           int32_t R, const void *x, const void *z, const void *U, const void *dy,
-                           const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, void *dx,
-                           void *dz, float *dU, void *workspace, size_t workspace_bytes) {
+namespace {
+
+// Validation and launch shared by the two low-rank backward entry points.
+dsc_status lowrank_bwd_call(bool det, const char *name, void *stream, int dtype, int64_t B, int64_t T, int64_t D,
+                            int32_t W, int32_t R, const void *x, const void *z, const void *U, const void *dy,
+                            const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, void *dx, void *dz,
+                            float *dU, void *workspace, size_t workspace_bytes) {
     DSC_TRY(check_common(dtype, B, T, D, W, cu_seqlens, n_seqs, residual));
     if (R < 1 || R > 128) return fail(DSC_ERR_SHAPE, "R = %d must be in 1..128", R);
     if (B * T == 0) {  // empty batch: dU is a sum over no tokens, zero; nothing else has elements
         if (!dU) return fail(DSC_ERR_NULL, "dU is required");
         if (!aligned16(dU)) return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
-        return launched(dsc::lowrank_zero(dU, (int64_t)R * D * W, (hipStream_t)stream), "dsc_lowrank_bwd launch");
+        return launched(dsc::lowrank_zero(dU, (int64_t)R * D * W, (hipStream_t)stream), name);
     }
     if (!x || !z || !U || !dy || !dx || !dz || !dU)
         return fail(DSC_ERR_NULL, "x, z, U, dy, dx, dz and dU are required");
@@ -259,7 +262,8 @@ dsc_status dsc_lowrank_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_
         !aligned16(dz) || !aligned16(dU))
         return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
     const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
-    const size_t need = dsc::lowrank_bwd_workspace(dt, B * T, D, W, R);
+    const size_t need = det ? dsc::lowrank_bwd_det_workspace(dt, B * T, D, W, R)
+                            : dsc::lowrank_bwd_workspace(dt, B * T, D, W, R);
     if (need > 0) {
         if (!workspace || workspace_bytes < need)
             return fail(DSC_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need,
@@ -273,9 +277,34 @@ dsc_status dsc_lowrank_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_
     const Range out[] = {rng("dx", dx, N * D * es), rng("dz", dz, N * R * es),
                          rng("dU", dU, (size_t)R * D * W * 4), rng("workspace", workspace, need ? need : 0)};
     DSC_TRY(check_alias(in, 5, out, 4));
-    float *acc = need ? static_cast<float *>(workspace) : static_cast<float *>(dz);
+    float *acc = need ? static_cast<float *>(workspace) : det ? nullptr : static_cast<float *>(dz);
     dsc::LrProblem p{dt, B * T, T, D, W, R, x, z, U, dy, nullptr, dx, dz, dU, acc, cu_seqlens, n_seqs, residual};
-    return launched(dsc::lowrank_bwd(p, (hipStream_t)stream), "dsc_lowrank_bwd launch");
+    return launched(det ? dsc::lowrank_bwd_det(p, (hipStream_t)stream) : dsc::lowrank_bwd(p, (hipStream_t)stream),
+                    name);
+}
+
+}  // namespace
+
+dsc_status dsc_lowrank_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                           int32_t R, const void *x, const void *z, const void *U, const void *dy,
+                           const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, void *dx,
+                           void *dz, float *dU, void *workspace, size_t workspace_bytes) {
+    return lowrank_bwd_call(false, "dsc_lowrank_bwd launch", stream, dtype, B, T, D, W, R, x, z, U, dy, cu_seqlens,
+                            n_seqs, residual, dx, dz, dU, workspace, workspace_bytes);
+}
+
+size_t dsc_lowrank_bwd_deterministic_workspace_size(int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                                                    int32_t R) {
+    if (check_common(dtype, B, T, D, W, nullptr, 0, 0) != DSC_SUCCESS || R < 1 || R > 128) return 0;
+    return dsc::lowrank_bwd_det_workspace(dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32, B * T, D, W, R);
+}
+
+dsc_status dsc_lowrank_bwd_deterministic(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                                         int32_t R, const void *x, const void *z, const void *U, const void *dy,
+                                         const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, void *dx,
+                                         void *dz, float *dU, void *workspace, size_t workspace_bytes) {
+    return lowrank_bwd_call(true, "dsc_lowrank_bwd_deterministic launch", stream, dtype, B, T, D, W, R, x, z, U, dy,
+                            cu_seqlens, n_seqs, residual, dx, dz, dU, workspace, workspace_bytes);
 }
 
 dsc_status dsc_static_fwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,

@@ -91,6 +91,10 @@ hipError_t lowrank_fwd(const LrProblem &p, hipStream_t s);
 // the other kernels, which then run instead.
 hipError_t lowrank_fwd_wide(const LrProblem &p, hipStream_t s, bool *used);
 hipError_t lowrank_bwd(const LrProblem &p, hipStream_t s);
+// Reproducible backward: dz and dU summed in one fixed order (dz_acc = its
+// workspace of lowrank_bwd_det_workspace bytes, may be null when that is 0).
+size_t lowrank_bwd_det_workspace(Dtype dt, int64_t N, int64_t D, int32_t W, int32_t R);
+hipError_t lowrank_bwd_det(const LrProblem &p, hipStream_t s);
 hipError_t static_fwd(const StProblem &p, hipStream_t s);
 // Zero-fills dc, then runs the backward (dx and the fp32 sums of dc); with
 // N = 0 only the zero-fill runs.

@@ -76,7 +76,8 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_generic(LrParams p) {
     Vec16<E>::store(static_cast<S *>(p.y) + n * p.D + d0, acc);
 }
 
-template <class E, int W>
+// SUMS: also add this item's dz and dU terms with atomics (else dx only).
+template <class E, int W, bool SUMS = true>
 __global__ __launch_bounds__(kBlock) void lr_bwd_generic(LrParams p) {
     using S = typename E::store_t;
     constexpr int VEC = E::kVec;
@@ -119,6 +120,7 @@ __global__ __launch_bounds__(kBlock) void lr_bwd_generic(LrParams p) {
         }
     }
     Vec16<E>::store(static_cast<S *>(p.dx) + m * p.D + d0, acc);
+    if constexpr (!SUMS) return;
 
     // per-channel filter gradient of token m
     float dwc[VEC * W];
@@ -810,7 +812,8 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
                 // only by lanes of ranks below R and tokens inside the block's range,
                 // each at an in-range offset of a resource based at the pair's row
                 const int64_t npair0 = nbeg + 16 * s_pair;
-                const __amdgpu_buffer_rsrc_t rdz = make_stream(p.dzacc + npair0 * R, (nend - npair0) * R * 4);
+                const __amdgpu_buffer_rsrc_t rdz =
+                    make_stream(p.dzacc + group * p.dz_gstride + npair0 * R, (nend - npair0) * R * 4);
                 {
                     // per half: thread e sums (token e / RP, rank e % RP) over the half's four waves
                     constexpr int kIt = 32 * L::RP / kBlock;
@@ -869,7 +872,7 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
         const float *t1 = reinterpret_cast<const float *>(lds + (4 + slice) * L::kWave);  // read only with H == 2
         const int nvalid = (int)((D - d0 < 32 ? D - d0 : 32) * W);  // floats of this slice inside D
         constexpr int kJ = (32 * W + kWave - 1) / kWave;
-        float *dst = p.dU + d0 * W;
+        float *dst = p.dU + tchunk * p.du_cstride + d0 * W;
         // ranks rb .. rb+3 stay below RP (rb is a multiple of 4 below R <= RP, and
         // RP is a multiple of 32): the tile reads are in bounds; ranks >= R are
         // not added
@@ -930,6 +933,84 @@ __global__ void cast_f32_bf16(const float *src, uint16_t *dst, int64_t n) {
     if (i < n) dst[i] = to_bf16(src[i]);
 }
 
+// ------------------------------------------- deterministic split-K sums
+//
+// The reproducible backward (dsc_lowrank_bwd_deterministic) forms every sum
+// in one fixed order.  The matrix-core kernel then adds the dz of each
+// channel group and the dU of each token chunk into regions of their own,
+// zeroed first, that receive exactly one term per element (so each value is
+// exact); these kernels add the regions in ascending order.  The generic
+// kernels' atomics are replaced by one thread per dz or dU element.
+
+template <class T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) { return to_bf16(v); }
+
+// dst[i] = src[i] + src[stride + i] + ... + src[(nparts-1)*stride + i], in that order.
+template <class T>
+__global__ __launch_bounds__(kBlock) void sum_parts(const float *src, int64_t nparts, int64_t stride, T *dst,
+                                                    int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= n) return;
+    float a = 0.f;
+    for (int64_t j = 0; j < nparts; ++j) a += src[j * stride + i];
+    dst[i] = from_f32<T>(a);
+}
+
+// dz[n,r] = sum over channels d, then taps k (ascending) of U[r,d*W+k] * dwc[n,d,k].
+template <class E, int W>
+__global__ __launch_bounds__(kBlock) void lr_dz_direct(LrParams p) {
+    using S = typename E::store_t;
+    const int64_t item = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (item >= p.N * p.R) return;
+    const int64_t n = item / p.R;
+    const int64_t r = item - n * p.R;
+    const S *x = static_cast<const S *>(p.x);
+    const S *g = static_cast<const S *>(p.dy);
+    const S *U = static_cast<const S *>(p.U);
+    int64_t s, e;
+    p.seq.find(n, s, e);
+    const int kn = (int)(n - s + 1 < W ? n - s + 1 : W);  // taps whose token n-k is in n's sequence
+    float acc = 0.f;
+    for (int64_t d = 0; d < p.D; ++d) {
+        const float gv = load_elem<E>(g + n * p.D + d);
+        const S *u = U + (r * p.D + d) * W;
+        for (int k = 0; k < kn; ++k)
+            acc = __builtin_fmaf(load_elem<E>(u + k), gv * load_elem<E>(x + (n - k) * p.D + d), acc);
+    }
+    static_cast<S *>(p.dz)[item] = from_f32<S>(acc);
+}
+
+// dU[r,d*W+k] = sum over tokens n (ascending) of z[n,r] * dwc[n,d,k], in
+// partial sums of 256 tokens added in order.
+template <class E, int W>
+__global__ __launch_bounds__(kBlock) void lr_du_direct(LrParams p) {
+    using S = typename E::store_t;
+    const int64_t DW = p.D * W;
+    const int64_t item = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (item >= p.R * DW) return;
+    const int64_t r = item / DW;
+    const int64_t d = (item - r * DW) / W;
+    const int k = (int)(item - r * DW - d * W);
+    const S *x = static_cast<const S *>(p.x);
+    const S *g = static_cast<const S *>(p.dy);
+    const S *z = static_cast<const S *>(p.z);
+    float total = 0.f;
+    int64_t s = 0, e = 0;  // sequence of the current token: [s, e)
+    for (int64_t n0 = 0; n0 < p.N; n0 += 256) {
+        const int64_t n1 = n0 + 256 < p.N ? n0 + 256 : p.N;
+        float part = 0.f;
+        for (int64_t n = n0; n < n1; ++n) {
+            if (n >= e) p.seq.find(n, s, e);
+            if (n - k >= s)
+                part = __builtin_fmaf(load_elem<E>(z + n * p.R + r),
+                                      load_elem<E>(g + n * p.D + d) * load_elem<E>(x + (n - k) * p.D + d), part);
+        }
+        total += part;
+    }
+    p.dU[item] = total;
+}
+
 template <class E, int W>
 hipError_t generic_fwd(const LrProblem &pr, hipStream_t st) {
     LrParams p = make_params<E>(pr);
@@ -938,8 +1019,20 @@ hipError_t generic_fwd(const LrProblem &pr, hipStream_t st) {
     return hipGetLastError();
 }
 
+// dx, then dz and dU one thread per element (fixed order, no workspace).
 template <class E, int W>
-hipError_t generic_bwd(const LrProblem &pr, hipStream_t st) {
+hipError_t generic_bwd_det(const LrProblem &pr, hipStream_t st) {
+    LrParams p = make_params<E>(pr);
+    const int64_t b = nblocks(p.N * p.nchunks);
+    if (b) hipLaunchKernelGGL((lr_bwd_generic<E, W, false>), dim3((unsigned)b), dim3(kBlock), 0, st, p);
+    hipLaunchKernelGGL((lr_dz_direct<E, W>), dim3((unsigned)nblocks(p.N * p.R)), dim3(kBlock), 0, st, p);
+    hipLaunchKernelGGL((lr_du_direct<E, W>), dim3((unsigned)nblocks((int64_t)p.R * p.D * W)), dim3(kBlock), 0, st, p);
+    return hipGetLastError();
+}
+
+template <class E, int W>
+hipError_t generic_bwd(const LrProblem &pr, hipStream_t st, bool det = false) {
+    if (det) return generic_bwd_det<E, W>(pr, st);
     LrParams p = make_params<E>(pr);
     const int64_t nU = (int64_t)p.R * p.D * W;
     const int64_t nz = p.N * p.R;
@@ -994,51 +1087,91 @@ hipError_t mfma_fwd(const LrProblem &pr, hipStream_t st) {
 constexpr int kBwdRing = DSC_LR_BWD_RING;  // backward prefetch ring depth (steps)
 constexpr int64_t kBlockFixedTokens = 256;  // a block's set-up and dU flush, in tokens of walk (measured)
 
+// Work split of the matrix-core backward: H token halves per block, blocks
+// of 4 channel slices (ngroups across D) and token chunks of 2 * tph tokens.
+struct BwdPlan {
+    int64_t ngroups, tph, tchunks;
+};
+
+BwdPlan bwd_plan(int64_t N, int64_t D, int W, int R, int64_t slots) {
+    const int H = bwd_two_per_simd(W, (R + 31) / 32) ? 2 : 1;
+    const int64_t cap = walk_cap(D, 16 * kBwdRing, 16 * (2 * kBwdRing + 2));
+    const int64_t ngroups = ((D + 31) / 32 + 3) / 4;
+    // walk unit: a 32-token pair per half where the walk may stop there, else a ring
+    const int64_t unit = bwd_exact_walk(H, R % 8 == 0) ? H * 32 : H * 16 * kBwdRing;
+    const int64_t block_len = walk_length(N, ngroups, slots, H * cap, unit, H * kBlockFixedTokens);
+    return BwdPlan{ngroups, block_len / H, (N + block_len - 1) / block_len};
+}
+
+// Whether the bf16 backward of these sizes runs the matrix-core kernel: it
+// keeps W*RC*(two U operand sets + dU tiles) in registers and is instantiated
+// while that fits (W*RC <= 8); the walk cap must hold a ring.
+bool bwd_uses_mfma(Dtype dt, int64_t D, int W, int R) {
+    const int rc = (R + 31) / 32;
+    if (dt != Dtype::BF16 || W < 1 || W > 8 || !(rc == 1 || (rc == 2 && W <= 4))) return false;
+    return walk_cap(D, 16 * kBwdRing, 16 * (2 * kBwdRing + 2)) >= 16 * kBwdRing;
+}
+
+// The reproducible backward splits the work as the fast one would on a
+// 256-CU device with one block per CU (every instance's kBlocksPerCu), on
+// every device, so that its order of summation is the same everywhere.
+constexpr int64_t kDetSlots = 256;
+
+size_t det_dz_floats(const BwdPlan &pl, int64_t N, int R) { return (((size_t)pl.ngroups * N * R + 3) / 4) * 4; }
+
 template <int W, int RC>
-hipError_t mfma_bwd(const LrProblem &pr, hipStream_t st) {
+hipError_t mfma_bwd(const LrProblem &pr, hipStream_t st, bool det) {
     LrParams p = make_params<BF16>(pr);
-    const int64_t cap = walk_cap(p.D, 16 * kBwdRing, 16 * (2 * kBwdRing + 2));
-    if (cap < 16 * kBwdRing) return generic_bwd<BF16, W>(pr, st);
     const int64_t nU = (int64_t)p.R * p.D * W;
     const int64_t nz = p.N * p.R;
-    const int64_t nslices = (p.D + 31) / 32;
-    const int64_t ngroups = (nslices + 3) / 4;
     constexpr int H = bwd_two_per_simd(W, RC) ? 2 : 1;  // token halves per block
-    static const int bpc_vec = blocks_per_cu(reinterpret_cast<const void *>(&lr_bwd_mfma<W, RC, kBwdRing, true, H>),
-                                             kBlock * H);
-    static const int bpc_gather = blocks_per_cu(reinterpret_cast<const void *>(&lr_bwd_mfma<W, RC, kBwdRing, false, H>),
-                                                kBlock * H);
-    const int64_t slots = (int64_t)device_cus() * (p.R % 8 == 0 ? bpc_vec : bpc_gather);
-    // walk unit: a 32-token pair per half where the walk may stop there, else a ring
-    const int64_t unit = bwd_exact_walk(H, p.R % 8 == 0) ? H * 32 : H * 16 * kBwdRing;
-    const int64_t block_len = walk_length(p.N, ngroups, slots, H * cap, unit, H * kBlockFixedTokens);
-    const int64_t tph = block_len / H;  // tokens per half
-    const int64_t tchunks = (p.N + block_len - 1) / block_len;
-    // one launch clears dU and the dz accumulator
-    const int64_t units = (nU + 3) / 4 + (nz + 3) / 4;
+    int64_t slots = kDetSlots;
+    if (!det) {
+        static const int bpc_vec = blocks_per_cu(
+            reinterpret_cast<const void *>(&lr_bwd_mfma<W, RC, kBwdRing, true, H>), kBlock * H);
+        static const int bpc_gather = blocks_per_cu(
+            reinterpret_cast<const void *>(&lr_bwd_mfma<W, RC, kBwdRing, false, H>), kBlock * H);
+        slots = (int64_t)device_cus() * (p.R % 8 == 0 ? bpc_vec : bpc_gather);
+    }
+    const BwdPlan pl = bwd_plan(p.N, p.D, W, p.R, slots);
+    float *dz_sum = p.dzacc, *du_sum = p.dU;
+    int64_t nclear_dz = nz, nclear_du = nU;
+    if (det) {  // regions of their own: dz per channel group, dU per token chunk
+        p.dz_gstride = nz;
+        p.du_cstride = nU;
+        p.dU = p.dzacc + det_dz_floats(pl, p.N, p.R);
+        nclear_dz = pl.ngroups * nz;
+        nclear_du = pl.tchunks * nU;
+    }
+    // one launch clears dU and the dz accumulator (or their regions)
+    const int64_t units = (nclear_du + 3) / 4 + (nclear_dz + 3) / 4;
     hipLaunchKernelGGL(clear2, dim3((unsigned)nblocks(units)), dim3(kBlock), 0, st,
-                       reinterpret_cast<uint32_t *>(p.dU), nU, reinterpret_cast<uint32_t *>(p.dzacc), nz);
+                       reinterpret_cast<uint32_t *>(p.dU), nclear_du, reinterpret_cast<uint32_t *>(p.dzacc), nclear_dz);
+    const dim3 grid((unsigned)(pl.tchunks * pl.ngroups));
+    const int64_t nslices = (p.D + 31) / 32;
     if (p.R % 8 == 0)
-        hipLaunchKernelGGL((lr_bwd_mfma<W, RC, kBwdRing, true, H>), dim3((unsigned)(tchunks * ngroups)),
-                           dim3(kBlock * H), 0, st, p, nslices, tph);
+        hipLaunchKernelGGL((lr_bwd_mfma<W, RC, kBwdRing, true, H>), grid, dim3(kBlock * H), 0, st, p, nslices, pl.tph);
     else
-        hipLaunchKernelGGL((lr_bwd_mfma<W, RC, kBwdRing, false, H>), dim3((unsigned)(tchunks * ngroups)),
-                           dim3(kBlock * H), 0, st, p, nslices, tph);
-    hipLaunchKernelGGL(cast_f32_bf16, dim3((unsigned)nblocks(nz)), dim3(kBlock), 0, st, p.dzacc,
-                       static_cast<uint16_t *>(p.dz), nz);
+        hipLaunchKernelGGL((lr_bwd_mfma<W, RC, kBwdRing, false, H>), grid, dim3(kBlock * H), 0, st, p, nslices, pl.tph);
+    if (det) {
+        hipLaunchKernelGGL(sum_parts<uint16_t>, dim3((unsigned)nblocks(nz)), dim3(kBlock), 0, st, dz_sum,
+                           pl.ngroups, nz, static_cast<uint16_t *>(pr.dz), nz);
+        hipLaunchKernelGGL(sum_parts<float>, dim3((unsigned)nblocks(nU)), dim3(kBlock), 0, st, p.dU, pl.tchunks, nU,
+                           du_sum, nU);
+    } else {
+        hipLaunchKernelGGL(cast_f32_bf16, dim3((unsigned)nblocks(nz)), dim3(kBlock), 0, st, p.dzacc,
+                           static_cast<uint16_t *>(p.dz), nz);
+    }
     return hipGetLastError();
 }
 
-// The backward keeps W*RC*(two U operand sets + dU tiles) in registers; it is
-// instantiated while that fits (W*RC <= 8), other shapes use the generic kernel.
 template <int W>
-hipError_t mfma_bwd_rc(const LrProblem &pr, hipStream_t st) {
-    const int rc = (pr.R + 31) / 32;
-    if (rc == 1) return mfma_bwd<W, 1>(pr, st);
+hipError_t mfma_bwd_rc(const LrProblem &pr, hipStream_t st, bool det) {
+    if (!bwd_uses_mfma(Dtype::BF16, pr.D, W, pr.R)) return generic_bwd<BF16, W>(pr, st, det);
     if constexpr (W <= 4) {
-        if (rc == 2) return mfma_bwd<W, 2>(pr, st);
+        if ((pr.R + 31) / 32 == 2) return mfma_bwd<W, 2>(pr, st, det);
     }
-    return generic_bwd<BF16, W>(pr, st);
+    return mfma_bwd<W, 1>(pr, st, det);
 }
 
 template <int W>
@@ -1093,9 +1226,23 @@ hipError_t lowrank_zero(float *p, int64_t n, hipStream_t s) {
 
 hipError_t lowrank_bwd(const LrProblem &p, hipStream_t s) {
     if (p.dtype == Dtype::BF16) {
-        DSC_W_SWITCH(p.W, (mfma_bwd_rc<Wc>(p, s)));
+        DSC_W_SWITCH(p.W, (mfma_bwd_rc<Wc>(p, s, false)));
     }
     DSC_W_SWITCH(p.W, (generic_bwd<F32, Wc>(p, s)));
+}
+
+size_t lowrank_bwd_det_workspace(Dtype dt, int64_t N, int64_t D, int32_t W, int32_t R) {
+    if (!bwd_uses_mfma(dt, D, W, R)) return 0;
+    const BwdPlan pl = bwd_plan(N, D, W, R, kDetSlots);
+    const size_t bytes = (det_dz_floats(pl, N, R) + (size_t)pl.tchunks * R * D * W) * sizeof(float);
+    return (bytes + 255) & ~(size_t)255;
+}
+
+hipError_t lowrank_bwd_det(const LrProblem &p, hipStream_t s) {
+    if (p.dtype == Dtype::BF16) {
+        DSC_W_SWITCH(p.W, (mfma_bwd_rc<Wc>(p, s, true)));
+    }
+    DSC_W_SWITCH(p.W, (generic_bwd<F32, Wc>(p, s, true)));
 }
 
 }  // namespace dsc

@@ -20,6 +20,10 @@ struct LrParams {
     float rho;
     uint32_t rmask;  // all ones with the residual term, else zero
     int64_t nchunks;
+    // Backward partial sums: the matrix-core backward adds its dz of channel
+    // group g at dzacc + g*dz_gstride and its dU of token chunk c at
+    // dU + c*du_cstride.  Both are 0 when the partials share one accumulator.
+    int64_t dz_gstride, du_cstride;
 };
 
 constexpr int kBlock = 256;
@@ -95,6 +99,8 @@ LrParams make_params(const LrProblem &pr) {
     p.rho = pr.residual ? 1.f : 0.f;
     p.rmask = pr.residual ? 0xffffffffu : 0u;
     p.nchunks = pr.D / E::kVec;
+    p.dz_gstride = 0;
+    p.du_cstride = 0;
     return p;
 }
 

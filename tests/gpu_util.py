@@ -67,18 +67,22 @@ def run_headwise(inp: dict, residual: bool, *, guard=True):
     return y.host(), dx.host(), dw.host()
 
 
-def run_lowrank(inp: dict, W: int, residual: bool, *, guard=True, repeat_bwd: int = 1):
+def run_lowrank(inp: dict, W: int, residual: bool, *, guard=True, repeat_bwd: int = 1, deterministic=False):
     x, z, U, dy = dev(inp["x"]), dev(inp["z"]), dev(inp["U"]), dev(inp["dy"])
     B, T, D = x.shape
     R = z.shape[2]
     cu = None if inp["cu_seqlens"] is None else torch.from_numpy(inp["cu_seqlens"]).cuda()
     y, dx, dz = Guarded(x.shape, x.dtype), Guarded(x.shape, x.dtype), Guarded(z.shape, z.dtype)
     dU = Guarded(U.shape, torch.float32)
-    nws = binding.dsc_lowrank_bwd_workspace_size(x.dtype, B, T, D, W, R)
+    if deterministic:
+        size, bwd = binding.dsc_lowrank_bwd_deterministic_workspace_size, binding.dsc_lowrank_bwd_deterministic
+    else:
+        size, bwd = binding.dsc_lowrank_bwd_workspace_size, binding.dsc_lowrank_bwd
+    nws = size(x.dtype, B, T, D, W, R)
     ws = torch.full((max(nws, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda") if nws else None
     binding.dsc_lowrank_fwd(x, z, U, y.t, W=W, cu_seqlens=cu, residual=residual)
     for _ in range(repeat_bwd):
-        binding.dsc_lowrank_bwd(x, z, U, dy, dx.t, dz.t, dU.t, ws, W=W, cu_seqlens=cu, residual=residual)
+        bwd(x, z, U, dy, dx.t, dz.t, dU.t, ws, W=W, cu_seqlens=cu, residual=residual)
     torch.cuda.synchronize()
     if guard:
         for name, g in (("y", y), ("dx", dx), ("dz", dz), ("dU", dU)):

@@ -29,7 +29,8 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     syms = set(declared_symbols())
     for s in ("dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd",
-              "dsc_lowrank_bwd_workspace_size", "dsc_static_fwd", "dsc_static_bwd",
+              "dsc_lowrank_bwd_workspace_size", "dsc_lowrank_bwd_deterministic",
+              "dsc_lowrank_bwd_deterministic_workspace_size", "dsc_static_fwd", "dsc_static_bwd",
               "dsc_headwise_decode", "dsc_lowrank_decode", "dsc_state_from_prefill",
               "dsc_rope_table", "dsc_headwise_rope_fwd", "dsc_headwise_rope_bwd", "dsc_headwise_rope_decode",
               "dsc_status_string", "dsc_last_error", "dsc_abi_version"):
@@ -103,6 +104,34 @@ def test_lowrank_validation(lib):
     assert lr_bwd(lib, ws=P(1)) == 5              # workspace aliases x
     assert lr_bwd(lib, dU=P(5)) == 5
     assert lr_bwd(lib, dz=None) == 1
+
+
+def test_lowrank_deterministic_validation(lib):
+    G = lambda k: ctypes.c_void_p((1 << 30) * k)  # fake addresses 1 GiB apart: only the named overlaps
+    f = lambda ws=G(8), wsb=1 << 30, **k: lib.dsc_lowrank_bwd_deterministic(
+        S0, k.get("dtype", 1), 8, 2048, 2304, 4, 32, G(1), G(2), G(3), G(4), None, 0, 0, k.get("dx", G(5)),
+        k.get("dz", G(6)), k.get("dU", G(7)), ws, wsb)
+    size = lambda dtype, B, T, D, W, R: lib.dsc_lowrank_bwd_deterministic_workspace_size(dtype, B, T, D, W, R)
+    # 16384 tokens, D = 2304 (18 blocks of 128 channels), R = 32: one fp32 dz region
+    # per channel block, then one fp32 dU region (R x D*W) per token chunk; computed
+    # on the host alone (no device here), so it cannot depend on the device
+    need = size(1, 8, 2048, 2304, 4, 32)
+    dz_bytes = 18 * 16384 * 32 * 4
+    du_region = 32 * 2304 * 4 * 4
+    chunks, rest = divmod(need - dz_bytes, du_region)
+    assert need % 256 == 0 and rest < 256 and 1 <= chunks <= 16384 // 64
+    assert size(1, 4, 4096, 6144, 4, 64) >= 48 * 16384 * 64 * 4 + 64 * 6144 * 4 * 4
+    assert size(0, 1, 64, 64, 4, 16) == 0      # fp32: one thread per dz / dU element, no workspace
+    assert size(1, 1, 64, 64, 4, 96) == 0      # bf16 shapes of the generic kernels: none either
+    assert size(1, 1, 64, 64, 6, 40) == 0
+    assert size(1, 1, 8, 63, 4, 16) == 0       # invalid sizes
+    assert f(ws=None, wsb=0) == 6
+    assert f(wsb=need - 1) == 6
+    assert b"workspace of" in lib.dsc_last_error()
+    assert f(ws=G(1)) == 5                     # workspace aliases x
+    assert f(dz=G(5)) == 5                     # dz aliases dx
+    assert f(dU=None) == 1
+    assert f(dtype=0, ws=None, wsb=0, dU=G(4)) == 5   # fp32 needs no workspace; dU aliases dy
 
 
 def st_fwd(lib, dtype=1, B=1, T=8, D=64, W=4, x=P(1), c=P(2), cu=None, ns=0, res=0, y=P(3)):
