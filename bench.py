@@ -320,6 +320,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-large", action="store_true", help="skip the 2B-scale workloads")
+    ap.add_argument("--no-deterministic", action="store_true",
+                    help="skip the timing of the reproducible low-rank backward (whose kernel launches would "
+                         "otherwise mix with the fast backward's in a kernel trace)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs of this script into profiles/traffic.json")
     args = ap.parse_args()
@@ -573,6 +576,34 @@ def main() -> int:
             "layer_alone_fwd_us": round(tr[2] * 1e6, 1), "layer_alone_bwd_us": round(tr[3] * 1e6, 1),
             "unfused_extra_bytes": 2 * rot * hwc.wl.N * hwc.x.element_size()}
         del table
+
+        # The reproducible low-rank backward (dz and dU summed in a fixed order
+        # through per-block workspace regions) against the fast one, at the
+        # QKV ~150M low-rank size, alternating in the same loop.
+    if not args.no_large and not args.no_deterministic:
+        lw = lrc.wl
+        nws = binding.dsc_lowrank_bwd_deterministic_workspace_size(lrc.x.dtype, lw.B, lw.T, lw.D, lw.W, lw.R)
+        det_ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda")
+        calls = [lambda: binding.dsc_lowrank_bwd_deterministic(lrc.x, lrc.z, lrc.U, lrc.dy, lrc.dx, lrc.dz, lrc.dU,
+                                                               det_ws if nws else None, W=lw.W,
+                                                               cu_seqlens=lrc.cu, residual=lw.residual),
+                 lrc.bwd]
+        for _ in range(3):
+            for f in calls:
+                f()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(reps)]
+        for e in evs:
+            e[0].record()
+            for i, f in enumerate(calls):
+                f()
+                e[i + 1].record()
+        torch.cuda.synchronize()
+        td = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / reps * 1e-3 for i in range(len(calls))]
+        out["lowrank_bwd_deterministic"] = {
+            "workload": lw.name, "us": round(td[0] * 1e6, 1), "fast_us": round(td[1] * 1e6, 1),
+            "workspace_bytes": nws, "algorithmic_GBps": round(lrc.bytes("bwd") / td[0] / 1e9, 1)}
+        del det_ws
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline([cases[0].wl, cases[1].wl], args.cpu_seconds)

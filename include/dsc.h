@@ -237,8 +237,8 @@ DSC_API size_t dsc_lowrank_bwd_deterministic_workspace_size(int dtype, int64_t B
  * adding its terms in a fixed order.  dx is the same as dsc_lowrank_bwd's.
  * Arguments, layouts and errors as for dsc_lowrank_bwd, with the workspace
  * sized by dsc_lowrank_bwd_deterministic_workspace_size() (may be NULL when
- * that is 0).  Costs extra HBM traffic: the partial regions are cleared,
- * written and read back (about 110 MB more at the sizes above).
+ * that is 0).  Costs extra HBM traffic: the partial regions (about 54 MB
+ * at the sizes above) are cleared, written once and read back.
  */
 DSC_API dsc_status dsc_lowrank_bwd_deterministic(void *stream, int dtype, int64_t B, int64_t T, int64_t D,
                                                  int32_t W, int32_t R, const void *x, const void *z,
