@@ -1,6 +1,7 @@
 """Seeded synthetic inputs for the dynamic short convolution workloads.
 
 This module holds no arithmetic of the method: it only draws Gaussian
+(or, for tensors beyond what the host should hold, counter-based uniform)
 tensors, scales them, rounds them to the working dtype and builds packed
 sequence offsets.  Both the GPU parity tests and the fp64 oracle consume the
 same tensors it returns (the oracle receives the exact double value of every
@@ -132,6 +133,44 @@ def small(kind: str, B: int, T: int, D: int, W: int, *, H: int = 1, R: int = 0,
                   dtype=dtype, residual=residual, varlen=varlen, seglen_range=seglen_range,
                   cfg=1000 + seed)
     return wl, make_inputs(wl)
+
+
+# ---- counter-based inputs, for tensors too large to draw on the host
+#
+# Element i of a tensor drawn with seed s depends on (s, i) alone, so the host
+# can rebuild any window of a tensor that lives only on the GPU.  The counter
+# is mixed into 32 bits and passed through three rounds of xor-shift by 16 and
+# multiplication by 0x45d9f3b (a well-known 32-bit integer hash); the top 24
+# bits give a uniform value in [-1, 1), scaled by sqrt(3)*std so that its
+# variance is std^2 like the Gaussian draws above.  Every integer step stays
+# below 2^63 in int64 and the mapping to [-1, 1) is exact, so only the final
+# fp32 scaling and the cast round, identically on the CPU and the GPU.
+
+_M32 = 0xFFFFFFFF
+
+
+def counter_values(seed: int, index: torch.Tensor, std: float, dtype: str) -> torch.Tensor:
+    """Values of the elements at the flat positions ``index`` (int64, any device)."""
+    i = index.to(torch.int64)
+    x = (((i & _M32) * 0x2545F491) & _M32) + (((i >> 32) * 0x1B873593) & _M32)
+    x = (x + ((seed & _M32) * 0x27D4EB2F & _M32)) & _M32
+    for _ in range(3):
+        x = x ^ (x >> 16)
+        x = (x * 0x45D9F3B) & _M32
+    x = x ^ (x >> 16)
+    u = (x >> 8).to(torch.float32) * (2.0 ** -23) - 1.0
+    scale = torch.tensor(float(np.sqrt(3.0) * std), dtype=torch.float32, device=u.device)
+    return (u * scale).to(DTYPES[dtype])
+
+
+def counter_tensor(shape, seed: int, std: float, dtype: str, device, chunk: int = 1 << 26) -> torch.Tensor:
+    """A whole tensor of counter_values, filled chunk by chunk on ``device``."""
+    out = torch.empty(tuple(shape), dtype=DTYPES[dtype], device=device)
+    flat = out.view(-1)
+    for a in range(0, flat.numel(), chunk):
+        b = min(flat.numel(), a + chunk)
+        flat[a:b] = counter_values(seed, torch.arange(a, b, dtype=torch.int64, device=device), std, dtype)
+    return out
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:

@@ -1,0 +1,123 @@
+"""Tensors beyond 4 GiB (GPU): B=256 T=4096 D=2304 W=4, 1,048,576 tokens, so
+each bf16 activation holds 2.4e9 elements (4.8 GB) and its element and byte
+offsets pass 2^31 and 2^32.  Inputs are counter-based (their values depend on
+the element index alone) and are drawn on the GPU; the oracle sees host
+windows of them (tests/large_util.py, checked on the CPU against whole
+tensors): token windows at the start, across the 2^31-byte and 2^32-byte
+offsets, across a sequence start and at the end, and channel slices for the
+sums over every token (dU, dc)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import large_util as lu
+from gpu_util import TOL, assert_close, say
+from input_dependent_short_amd import binding, inputs
+from input_dependent_short_amd.inputs import to_f64
+
+pytestmark = pytest.mark.gpu
+
+B, T, D, W = 256, 4096, 2304, 4
+N = B * T
+DT = "bf16"
+ROWS = [(0, 16), (2**30 // D - 6, 2**30 // D + 10), (2**31 // D - 8, 2**31 // D + 8),
+        (228 * T - 8, 228 * T + 8), (N - 16, N)]
+CHANNELS = [(0, 8), (D - 8, D)]
+
+
+def _seeds(base: int) -> dict:
+    return {k: inputs.seed_for(base, i) for i, k in enumerate(("x", "w", "dy", "z", "U", "c"))}
+
+
+def _gpu(seed: int, std: float, shape) -> torch.Tensor:
+    return inputs.counter_tensor(shape, seed, std, DT, "cuda")
+
+
+def _nan(shape, dtype=torch.bfloat16) -> torch.Tensor:
+    return torch.full(shape, float("nan"), dtype=dtype, device="cuda")
+
+
+def _rows(t: torch.Tensor, lo: int, hi: int) -> np.ndarray:
+    return to_f64(t.view(N, -1)[lo:hi])
+
+
+def _free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def test_headwise_beyond_4gib():
+    H = 64
+    G = D // H
+    s = _seeds(901)
+    say(f"[large headwise] B={B} T={T} D={D} H={H}: {N * D * 2 / 1e9:.2f} GB per activation")
+    x, dy = _gpu(s["x"], 1.0, (B, T, D)), _gpu(s["dy"], 1.0, (B, T, D))
+    w = _gpu(s["w"], 1.0 / np.sqrt(W), (B, T, G, W))
+    y, dx, dw = _nan((B, T, D)), _nan((B, T, D)), _nan((B, T, G, W))
+    binding.dsc_headwise_fwd(x, w, y, residual=True)
+    binding.dsc_headwise_bwd(x, w, dy, dx, dw, residual=True)
+    torch.cuda.synchronize()
+    tol = TOL[DT]
+    for lo, hi in ROWS:
+        say(f"  rows [{lo},{hi})")
+        ry, rdx, rdw = lu.headwise_rows(s, N, T, D, G, W, lo, hi, True, DT)
+        assert_close("y", _rows(y, lo, hi), ry, tol)
+        assert_close("dx", _rows(dx, lo, hi), rdx, tol)
+        assert_close("dw", _rows(dw, lo, hi).reshape(hi - lo, G, W), rdw, tol)
+    del x, dy, w, y, dx, dw
+    _free()
+
+
+def test_lowrank_beyond_4gib():
+    R = 32
+    s = _seeds(902)
+    say(f"[large lowrank] B={B} T={T} D={D} R={R}")
+    x, dy = _gpu(s["x"], 1.0, (B, T, D)), _gpu(s["dy"], 1.0, (B, T, D))
+    z = _gpu(s["z"], 1.0, (B, T, R))
+    U = _gpu(s["U"], 1.0 / np.sqrt(R * W), (R, D * W))
+    y, dx, dz = _nan((B, T, D)), _nan((B, T, D)), _nan((B, T, R))
+    dU = _nan((R, D * W), torch.float32)
+    nws = binding.dsc_lowrank_bwd_workspace_size(x.dtype, B, T, D, W, R)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda")
+    binding.dsc_lowrank_fwd(x, z, U, y, W=W)
+    binding.dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, ws, W=W)
+    torch.cuda.synchronize()
+    tol = TOL[DT]
+    for lo, hi in ROWS:
+        say(f"  rows [{lo},{hi})")
+        ry, rdx, rdz = lu.lowrank_rows(s, N, T, D, R, W, lo, hi, False, DT)
+        assert_close("y", _rows(y, lo, hi), ry, tol)
+        assert_close("dx", _rows(dx, lo, hi), rdx, tol)
+        assert_close("dz", _rows(dz, lo, hi), rdz, tol)
+    dU3 = dU.cpu().double().numpy().reshape(R, D, W)
+    for c0, c1 in CHANNELS:
+        say(f"  dU channels [{c0},{c1})")
+        assert_close("dU", dU3[:, c0:c1].reshape(R, -1), lu.lowrank_dU(s, B, T, D, R, W, c0, c1, DT), tol)
+    del x, dy, z, U, y, dx, dz, dU, ws
+    _free()
+
+
+def test_static_beyond_4gib():
+    s = _seeds(903)
+    say(f"[large static] B={B} T={T} D={D}")
+    x, dy = _gpu(s["x"], 1.0, (B, T, D)), _gpu(s["dy"], 1.0, (B, T, D))
+    c = _gpu(s["c"], 1.0 / np.sqrt(W), (D, W))
+    y, dx = _nan((B, T, D)), _nan((B, T, D))
+    dc = _nan((D, W), torch.float32)
+    binding.dsc_static_fwd(x, c, y, residual=True)
+    binding.dsc_static_bwd(x, c, dy, dx, dc, residual=True)
+    torch.cuda.synchronize()
+    tol = TOL[DT]
+    for lo, hi in ROWS:
+        say(f"  rows [{lo},{hi})")
+        ry, rdx = lu.static_rows(s, N, T, D, W, lo, hi, True, DT)
+        assert_close("y", _rows(y, lo, hi), ry, tol)
+        assert_close("dx", _rows(dx, lo, hi), rdx, tol)
+    dcn = dc.cpu().double().numpy()
+    for c0, c1 in CHANNELS:
+        say(f"  dc channels [{c0},{c1})")
+        assert_close("dc", dcn[c0:c1], lu.static_dc(s, B, T, D, W, c0, c1, DT), tol)
+    del x, dy, c, y, dx, dc
+    _free()
