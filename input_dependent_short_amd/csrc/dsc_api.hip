@@ -57,8 +57,8 @@ dsc_status check_common(int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
     if (dtype != DSC_FP32 && dtype != DSC_BF16) return fail(DSC_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
     if (B < 0 || T < 0 || D < 1) return fail(DSC_ERR_SHAPE, "B, T must be >= 0 and D >= 1 (got %lld, %lld, %lld)",
                                              (long long)B, (long long)T, (long long)D);
-    if (B > (int64_t)1 << 40 || T > (int64_t)1 << 40 || B * T > (int64_t)INT32_MAX)
-        return fail(DSC_ERR_SHAPE, "B*T = %lld tokens exceeds 2^31-1", (long long)(B * T));
+    if (T > 0 && B > (int64_t)INT32_MAX / T)  // B*T > 2^31-1, tested without forming the product
+        return fail(DSC_ERR_SHAPE, "B*T tokens exceed 2^31-1 (B = %lld, T = %lld)", (long long)B, (long long)T);
     if (D > ((int64_t)1 << 24)) return fail(DSC_ERR_SHAPE, "D = %lld too large", (long long)D);
     if (W < 1 || W > 8) return fail(DSC_ERR_SHAPE, "W must be in 1..8 (got %d)", W);
     const int vec = dtype == DSC_BF16 ? 8 : 4;
@@ -353,7 +353,7 @@ namespace {
 // Shared checks of the two decoding steps (B sequences, one token each).
 dsc_status check_decode(int dtype, int64_t B, int64_t D, int32_t W, int32_t residual) {
     if (dtype != DSC_FP32 && dtype != DSC_BF16) return fail(DSC_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
-    if (B < 0 || D < 1 || D > ((int64_t)1 << 24) || B * D >= ((int64_t)1 << 31))
+    if (B < 0 || D < 1 || D > ((int64_t)1 << 24) || B > (int64_t)INT32_MAX / D)  // B*D < 2^31, no product formed
         return fail(DSC_ERR_SHAPE, "B >= 0, D in 1..2^24 and B*D < 2^31 required (got %lld, %lld)", (long long)B,
                     (long long)D);
     if (W < 1 || W > 8) return fail(DSC_ERR_SHAPE, "W must be in 1..8 (got %d)", W);
