@@ -1,12 +1,13 @@
 """The training entry points under HIP graph capture (GPU).
 
 Forward and backward of the head-wise, low-rank (with its zero-fill and cast
-launches), static and head-wise + rotary layers are captured once as a single
-graph.  The graph is replayed three times; between replays the same calls run
+launches, and the fixed-order backward with its summing launches), static and
+head-wise + rotary layers are captured once as a single graph.  The graph is replayed three times; between replays the same calls run
 eagerly on separate outputs, with synchronisation, and every replay is checked
 against them: bit for bit where no atomic sum is involved, and within 1e-6
 (fp32) or one bf16 rounding (bf16 dz) normwise for the sums accumulated with
-atomics (dz, dU, dc), whose order of addition varies from run to run.
+atomics (dz, dU, dc), whose order of addition varies from run to run.  The
+fixed-order backward's dz and dU are compared bit for bit.
 """
 from __future__ import annotations
 
@@ -28,6 +29,9 @@ def _outputs(t: dict) -> dict:
     o["lr_y"], o["lr_dx"], o["lr_dz"] = torch.empty_like(t["lx"]), torch.empty_like(t["lx"]), torch.empty_like(t["z"])
     o["lr_dU"] = torch.empty(t["U"].shape, dtype=torch.float32, device="cuda")
     o["lr_ws"] = torch.empty(t["ws_bytes"], dtype=torch.uint8, device="cuda")
+    o["ld_dx"], o["ld_dz"] = torch.empty_like(t["lx"]), torch.empty_like(t["z"])
+    o["ld_dU"] = torch.empty(t["U"].shape, dtype=torch.float32, device="cuda")
+    o["ld_ws"] = torch.empty(t["det_ws_bytes"], dtype=torch.uint8, device="cuda")
     o["st_y"], o["st_dx"] = torch.empty_like(t["sx"]), torch.empty_like(t["sx"])
     o["st_dc"] = torch.empty(t["c"].shape, dtype=torch.float32, device="cuda")
     return o
@@ -39,6 +43,8 @@ def _calls(t: dict, o: dict) -> None:
     b.dsc_headwise_bwd(t["hx"], t["hw"], t["hdy"], o["hw_dx"], o["hw_dw"], cu_seqlens=t["cu"], residual=True)
     b.dsc_lowrank_fwd(t["lx"], t["z"], t["U"], o["lr_y"], W=4)
     b.dsc_lowrank_bwd(t["lx"], t["z"], t["U"], t["ldy"], o["lr_dx"], o["lr_dz"], o["lr_dU"], o["lr_ws"], W=4)
+    b.dsc_lowrank_bwd_deterministic(t["lx"], t["z"], t["U"], t["ldy"], o["ld_dx"], o["ld_dz"], o["ld_dU"],
+                                    o["ld_ws"], W=4)
     b.dsc_static_fwd(t["sx"], t["c"], o["st_y"], residual=True)
     b.dsc_static_bwd(t["sx"], t["c"], t["sdy"], o["st_dx"], o["st_dc"], residual=True)
     kw = dict(rot=512, head_dim=64, table=t["table"], cu_seqlens=t["cu"], residual=True)
@@ -59,6 +65,8 @@ def test_training_entry_points_replayed_as_a_graph():
          "lx": li["x"].cuda(), "z": li["z"].cuda(), "U": li["U"].cuda(), "ldy": li["dy"].cuda(),
          "sx": si["x"].cuda(), "c": si["c"].cuda(), "sdy": si["dy"].cuda()}
     t["ws_bytes"] = max(16, binding.dsc_lowrank_bwd_workspace_size(torch.bfloat16, 2, 200, 256, 4, 32))
+    t["det_ws_bytes"] = max(16, binding.dsc_lowrank_bwd_deterministic_workspace_size(torch.bfloat16, 2, 200, 256, 4,
+                                                                                     32))
     t["table"] = torch.empty(2 * 300, 32, 2, dtype=torch.float32, device="cuda")
     binding.dsc_rope_table(t["table"])
     say("[graph] head-wise, low-rank, static and head-wise + rotary, forward and backward")
@@ -80,7 +88,7 @@ def test_training_entry_points_replayed_as_a_graph():
         _calls(t, oe)
         torch.cuda.synchronize()
         for k, a in og.items():
-            if k == "lr_ws":
+            if k in ("lr_ws", "ld_ws"):
                 continue
             b = oe[k]
             if k in ATOMIC:
