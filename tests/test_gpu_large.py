@@ -121,3 +121,52 @@ def test_static_beyond_4gib():
         assert_close("dc", dcn[c0:c1], lu.static_dc(s, B, T, D, W, c0, c1, DT), tol)
     del x, dy, c, y, dx, dc
     _free()
+
+
+def _seq_rows(seed: int, std: float, tail: tuple, lo: int, hi: int) -> np.ndarray:
+    return lu.rows_of(seed, std, DT, tail, lo, hi)
+
+
+@pytest.mark.parametrize("kind", ["headwise", "lowrank"])
+def test_decode_at_the_batch_limit(kind):
+    """One decoding step for the largest batch the ABI takes at D = 2304
+    (B*D < 2^31: 932,067 sequences): the (B, W-1, D) state holds 6.4e9 elements,
+    so its offsets pass 2^32.  Sequence windows at the start, across the 2^31-
+    byte offset of x and y, across the 2^31- and 2^32-element offsets of the
+    state, and at the end (x and y end just below 2^32 bytes); y and the
+    updated state against the oracle."""
+    import oracle
+    H, R = 64, 32
+    G = D // H
+    Bd = (2**31 - 1) // D
+    s = _seeds(904 if kind == "headwise" else 905)
+    say(f"[large decode {kind}] B={Bd} D={D} W={W}: state {Bd * (W - 1) * D * 2 / 1e9:.1f} GB")
+    x = _gpu(s["x"], 1.0, (Bd, D))
+    st = _gpu(s["c"], 1.0, (Bd, W - 1, D))
+    y = _nan((Bd, D))
+    if kind == "headwise":
+        w = _gpu(s["w"], 1.0 / np.sqrt(W), (Bd, G, W))
+        binding.dsc_headwise_decode(x, w, st, y, residual=True)
+    else:
+        z = _gpu(s["z"], 1.0, (Bd, R))
+        U = _gpu(s["U"], 1.0 / np.sqrt(R * W), (R, D * W))
+        binding.dsc_lowrank_decode(x, z, U, st, y, W=W)
+    torch.cuda.synchronize()
+    per = (W - 1) * D
+    wins = [(0, 8), (2**30 // D - 4, 2**30 // D + 4), (2**31 // per - 4, 2**31 // per + 4),
+            (2**32 // per - 4, 2**32 // per + 4), (Bd - 8, Bd)]
+    U64 = _seq_rows(s["U"], 1.0 / np.sqrt(R * W), (D * W,), 0, R) if kind == "lowrank" else None
+    tol = TOL[DT]
+    for lo, hi in wins:
+        say(f"  sequences [{lo},{hi})")
+        xw = _seq_rows(s["x"], 1.0, (D,), lo, hi)
+        sw = _seq_rows(s["c"], 1.0, (W - 1, D), lo, hi)
+        if kind == "headwise":
+            ry, rst = oracle.headwise_decode(xw, _seq_rows(s["w"], 1.0 / np.sqrt(W), (G, W), lo, hi), sw,
+                                             residual=True)
+        else:
+            ry, rst = oracle.lowrank_decode(xw, _seq_rows(s["z"], 1.0, (R,), lo, hi), U64, sw, W)
+        assert_close("y", to_f64(y[lo:hi]), ry, tol)
+        assert np.array_equal(to_f64(st[lo:hi]), rst), "state rows differ from the oracle's shift"
+    del x, st, y
+    _free()
