@@ -32,9 +32,11 @@ def channels_of(seed: int, std: float, dtype: str, N: int, D: int, c0: int, c1: 
     return to_f64(inputs.counter_values(seed, idx.reshape(-1), std, dtype)).reshape(N, c1 - c0)
 
 
-def window_cu(T: int, wlo: int, whi: int) -> np.ndarray:
-    """Sequence offsets of the window [wlo, whi) of a batch of rows of T tokens."""
-    starts = {0, whi - wlo} | {s - wlo for s in range((wlo // T + 1) * T, whi, T)}
+def window_cu(T: int, wlo: int, whi: int, cu=None) -> np.ndarray:
+    """Sequence offsets of the window [wlo, whi) of a batch of rows of T tokens
+    (each row one sequence), or of packed sequences with offsets ``cu``."""
+    inside = range((wlo // T + 1) * T, whi, T) if cu is None else [int(c) for c in cu if wlo < c < whi]
+    starts = {0, whi - wlo} | {s - wlo for s in inside}
     return np.array(sorted(starts), dtype=np.int32)
 
 
@@ -43,14 +45,14 @@ def window(N: int, W: int, lo: int, hi: int) -> tuple[int, int]:
 
 
 def headwise_rows(seeds: dict, N: int, T: int, D: int, G: int, W: int, lo: int, hi: int, residual: bool,
-                  dtype: str):
+                  dtype: str, cu=None):
     """Oracle (y, dx, dw) of rows [lo, hi) of a head-wise layer on counter inputs."""
     wlo, whi = window(N, W, lo, hi)
     L = whi - wlo
     x = rows_of(seeds["x"], 1.0, dtype, (D,), wlo, whi).reshape(1, L, D)
     w = rows_of(seeds["w"], 1.0 / np.sqrt(W), dtype, (G, W), wlo, whi).reshape(1, L, G, W)
     dy = rows_of(seeds["dy"], 1.0, dtype, (D,), wlo, whi).reshape(1, L, D)
-    cu, rows = window_cu(T, wlo, whi), (lo - wlo, hi - wlo)
+    cu, rows = window_cu(T, wlo, whi, cu), (lo - wlo, hi - wlo)
     y = oracle.headwise_fwd(x, w, cu_seqlens=cu, residual=residual, rows=rows)
     dx, dw = oracle.headwise_bwd(x, w, dy, cu_seqlens=cu, residual=residual, rows=rows)
     return y, dx, dw
@@ -61,7 +63,7 @@ def lowrank_U(seeds: dict, R: int, D: int, W: int, dtype: str) -> np.ndarray:
 
 
 def lowrank_rows(seeds: dict, N: int, T: int, D: int, R: int, W: int, lo: int, hi: int, residual: bool,
-                 dtype: str):
+                 dtype: str, cu=None):
     """Oracle (y, dx, dz) of rows [lo, hi) of a low-rank layer on counter inputs."""
     wlo, whi = window(N, W, lo, hi)
     L = whi - wlo
@@ -69,34 +71,36 @@ def lowrank_rows(seeds: dict, N: int, T: int, D: int, R: int, W: int, lo: int, h
     z = rows_of(seeds["z"], 1.0, dtype, (R,), wlo, whi).reshape(1, L, R)
     dy = rows_of(seeds["dy"], 1.0, dtype, (D,), wlo, whi).reshape(1, L, D)
     U = lowrank_U(seeds, R, D, W, dtype)
-    cu, rows = window_cu(T, wlo, whi), (lo - wlo, hi - wlo)
+    cu, rows = window_cu(T, wlo, whi, cu), (lo - wlo, hi - wlo)
     y = oracle.lowrank_fwd(x, z, U, W, cu_seqlens=cu, residual=residual, rows=rows)
     dx, dz, _ = oracle.lowrank_bwd(x, z, U, dy, W, cu_seqlens=cu, residual=residual, rows=rows, channels=(0, 0))
     return y, dx, dz
 
 
-def lowrank_dU(seeds: dict, B: int, T: int, D: int, R: int, W: int, c0: int, c1: int, dtype: str) -> np.ndarray:
+def lowrank_dU(seeds: dict, B: int, T: int, D: int, R: int, W: int, c0: int, c1: int, dtype: str,
+               cu=None) -> np.ndarray:
     """Oracle dU of channels [c0, c1), (R, (c1-c0)*W), summed over every token."""
     N, dc = B * T, c1 - c0
     x = channels_of(seeds["x"], 1.0, dtype, N, D, c0, c1).reshape(B, T, dc)
     dy = channels_of(seeds["dy"], 1.0, dtype, N, D, c0, c1).reshape(B, T, dc)
     z = rows_of(seeds["z"], 1.0, dtype, (R,), 0, N).reshape(B, T, R)
     U = lowrank_U(seeds, R, D, W, dtype).reshape(R, D, W)[:, c0:c1].reshape(R, dc * W)
-    return oracle.lowrank_bwd(x, z, U, dy, W, rows=(0, 0), channels=(0, dc))[2]
+    return oracle.lowrank_bwd(x, z, U, dy, W, cu_seqlens=cu, rows=(0, 0), channels=(0, dc))[2]
 
 
 def static_c(seeds: dict, D: int, W: int, dtype: str) -> np.ndarray:
     return rows_of(seeds["c"], 1.0 / np.sqrt(W), dtype, (W,), 0, D)
 
 
-def static_rows(seeds: dict, N: int, T: int, D: int, W: int, lo: int, hi: int, residual: bool, dtype: str):
+def static_rows(seeds: dict, N: int, T: int, D: int, W: int, lo: int, hi: int, residual: bool, dtype: str,
+                cu=None):
     """Oracle (y, dx) of rows [lo, hi) of the static layer on counter inputs."""
     wlo, whi = window(N, W, lo, hi)
     L = whi - wlo
     x = rows_of(seeds["x"], 1.0, dtype, (D,), wlo, whi).reshape(1, L, D)
     dy = rows_of(seeds["dy"], 1.0, dtype, (D,), wlo, whi).reshape(1, L, D)
     c = static_c(seeds, D, W, dtype)
-    cu, rows = window_cu(T, wlo, whi), (lo - wlo, hi - wlo)
+    cu, rows = window_cu(T, wlo, whi, cu), (lo - wlo, hi - wlo)
     y = oracle.static_fwd(x, c, cu_seqlens=cu, residual=residual, rows=rows)
     dx, _ = oracle.static_bwd(x, c, dy, cu_seqlens=cu, residual=residual, rows=rows)
     return y, dx

@@ -48,21 +48,36 @@ def _free():
     torch.cuda.empty_cache()
 
 
-def test_headwise_beyond_4gib():
+def _packed(seed: int):
+    """Packed sequences of 256..4096 tokens (the 2B varlen recipe), and extra
+    windows across the sequence starts nearest the 2^31- and 2^32-byte offsets."""
+    cu = inputs.packed_cu_seqlens(B, T, 256, 4096, seed)
+    extra = []
+    for n in (2**30 // D, 2**31 // D):
+        c = int(cu[np.searchsorted(cu, n)])
+        extra.append((c - 8, c + 8))
+    return cu, ROWS + extra
+
+
+@pytest.mark.parametrize("varlen", [False, True], ids=["rows", "packed"])
+def test_headwise_beyond_4gib(varlen):
     H = 64
     G = D // H
     s = _seeds(901)
-    say(f"[large headwise] B={B} T={T} D={D} H={H}: {N * D * 2 / 1e9:.2f} GB per activation")
+    cu_np, rows = _packed(906) if varlen else (None, ROWS)
+    cu = None if cu_np is None else torch.from_numpy(cu_np).cuda()
+    say(f"[large headwise] B={B} T={T} D={D} H={H}: {N * D * 2 / 1e9:.2f} GB per activation, "
+        f"{'packed' if varlen else 'rows'}")
     x, dy = _gpu(s["x"], 1.0, (B, T, D)), _gpu(s["dy"], 1.0, (B, T, D))
     w = _gpu(s["w"], 1.0 / np.sqrt(W), (B, T, G, W))
     y, dx, dw = _nan((B, T, D)), _nan((B, T, D)), _nan((B, T, G, W))
-    binding.dsc_headwise_fwd(x, w, y, residual=True)
-    binding.dsc_headwise_bwd(x, w, dy, dx, dw, residual=True)
+    binding.dsc_headwise_fwd(x, w, y, cu_seqlens=cu, residual=True)
+    binding.dsc_headwise_bwd(x, w, dy, dx, dw, cu_seqlens=cu, residual=True)
     torch.cuda.synchronize()
     tol = TOL[DT]
-    for lo, hi in ROWS:
+    for lo, hi in rows:
         say(f"  rows [{lo},{hi})")
-        ry, rdx, rdw = lu.headwise_rows(s, N, T, D, G, W, lo, hi, True, DT)
+        ry, rdx, rdw = lu.headwise_rows(s, N, T, D, G, W, lo, hi, True, DT, cu_np)
         assert_close("y", _rows(y, lo, hi), ry, tol)
         assert_close("dx", _rows(dx, lo, hi), rdx, tol)
         assert_close("dw", _rows(dw, lo, hi).reshape(hi - lo, G, W), rdw, tol)
@@ -70,10 +85,13 @@ def test_headwise_beyond_4gib():
     _free()
 
 
-def test_lowrank_beyond_4gib():
+@pytest.mark.parametrize("varlen", [False, True], ids=["rows", "packed"])
+def test_lowrank_beyond_4gib(varlen):
     R = 32
     s = _seeds(902)
-    say(f"[large lowrank] B={B} T={T} D={D} R={R}")
+    cu_np, rows = _packed(907) if varlen else (None, ROWS)
+    cu = None if cu_np is None else torch.from_numpy(cu_np).cuda()
+    say(f"[large lowrank] B={B} T={T} D={D} R={R}, {'packed' if varlen else 'rows'}")
     x, dy = _gpu(s["x"], 1.0, (B, T, D)), _gpu(s["dy"], 1.0, (B, T, D))
     z = _gpu(s["z"], 1.0, (B, T, R))
     U = _gpu(s["U"], 1.0 / np.sqrt(R * W), (R, D * W))
@@ -81,20 +99,20 @@ def test_lowrank_beyond_4gib():
     dU = _nan((R, D * W), torch.float32)
     nws = binding.dsc_lowrank_bwd_workspace_size(x.dtype, B, T, D, W, R)
     ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda")
-    binding.dsc_lowrank_fwd(x, z, U, y, W=W)
-    binding.dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, ws, W=W)
+    binding.dsc_lowrank_fwd(x, z, U, y, W=W, cu_seqlens=cu)
+    binding.dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, ws, W=W, cu_seqlens=cu)
     torch.cuda.synchronize()
     tol = TOL[DT]
-    for lo, hi in ROWS:
+    for lo, hi in rows:
         say(f"  rows [{lo},{hi})")
-        ry, rdx, rdz = lu.lowrank_rows(s, N, T, D, R, W, lo, hi, False, DT)
+        ry, rdx, rdz = lu.lowrank_rows(s, N, T, D, R, W, lo, hi, False, DT, cu_np)
         assert_close("y", _rows(y, lo, hi), ry, tol)
         assert_close("dx", _rows(dx, lo, hi), rdx, tol)
         assert_close("dz", _rows(dz, lo, hi), rdz, tol)
     dU3 = dU.cpu().double().numpy().reshape(R, D, W)
     for c0, c1 in CHANNELS:
         say(f"  dU channels [{c0},{c1})")
-        assert_close("dU", dU3[:, c0:c1].reshape(R, -1), lu.lowrank_dU(s, B, T, D, R, W, c0, c1, DT), tol)
+        assert_close("dU", dU3[:, c0:c1].reshape(R, -1), lu.lowrank_dU(s, B, T, D, R, W, c0, c1, DT, cu_np), tol)
     del x, dy, z, U, y, dx, dz, dU, ws
     _free()
 

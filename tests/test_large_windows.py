@@ -17,6 +17,7 @@ B, T, D, W, G, R = 3, 37, 16, 4, 4, 5
 N = B * T
 SEEDS = {"x": 11, "w": 12, "dy": 13, "z": 14, "U": 15, "c": 16}
 WINDOWS = [(0, 5), (10, 20), (T - 2, T + 3), (2 * T - 1, 2 * T + 1), (N - 4, N)]
+CU = np.array([0, 1, 9, 30, 37, 40, 41, 74, 100, N], dtype=np.int32)  # packed, crossing rows
 
 
 def full(key, std, tail):
@@ -41,32 +42,35 @@ def test_window_offsets():
 
 
 @pytest.mark.parametrize("residual", [False, True])
-def test_headwise_windows_match_the_whole_batch(residual):
+@pytest.mark.parametrize("packed", [False, True])
+def test_headwise_windows_match_the_whole_batch(residual, packed):
+    cu = CU if packed else None
     x = full("x", 1.0, (D,)).reshape(B, T, D)
     w = full("w", 1 / np.sqrt(W), (G, W)).reshape(B, T, G, W)
     dy = full("dy", 1.0, (D,)).reshape(B, T, D)
-    y = oracle.headwise_fwd(x, w, residual=residual).reshape(N, D)
-    dx, dw = oracle.headwise_bwd(x, w, dy, residual=residual)
+    y = oracle.headwise_fwd(x, w, cu_seqlens=cu, residual=residual).reshape(N, D)
+    dx, dw = oracle.headwise_bwd(x, w, dy, cu_seqlens=cu, residual=residual)
     dx, dw = dx.reshape(N, D), dw.reshape(N, G, W)
-    for lo, hi in WINDOWS:
-        wy, wdx, wdw = lu.headwise_rows(SEEDS, N, T, D, G, W, lo, hi, residual, "bf16")
+    for lo, hi in WINDOWS + [(5, 12), (36, 43)]:
+        wy, wdx, wdw = lu.headwise_rows(SEEDS, N, T, D, G, W, lo, hi, residual, "bf16", cu)
         assert np.array_equal(wy, y[lo:hi]) and np.array_equal(wdx, dx[lo:hi]) and np.array_equal(wdw, dw[lo:hi])
 
 
-def test_lowrank_windows_and_channel_slices_match_the_whole_batch():
+@pytest.mark.parametrize("cu", [None, CU], ids=["rows", "packed"])
+def test_lowrank_windows_and_channel_slices_match_the_whole_batch(cu):
     x = full("x", 1.0, (D,)).reshape(B, T, D)
     z = full("z", 1.0, (R,)).reshape(B, T, R)
     dy = full("dy", 1.0, (D,)).reshape(B, T, D)
     U = lu.lowrank_U(SEEDS, R, D, W, "bf16")
-    y = oracle.lowrank_fwd(x, z, U, W).reshape(N, D)
-    dx, dz, dU = oracle.lowrank_bwd(x, z, U, dy, W)
+    y = oracle.lowrank_fwd(x, z, U, W, cu_seqlens=cu).reshape(N, D)
+    dx, dz, dU = oracle.lowrank_bwd(x, z, U, dy, W, cu_seqlens=cu)
     dx, dz = dx.reshape(N, D), dz.reshape(N, R)
-    for lo, hi in WINDOWS:
-        wy, wdx, wdz = lu.lowrank_rows(SEEDS, N, T, D, R, W, lo, hi, False, "bf16")
+    for lo, hi in WINDOWS + [(5, 12), (36, 43)]:
+        wy, wdx, wdz = lu.lowrank_rows(SEEDS, N, T, D, R, W, lo, hi, False, "bf16", cu)
         assert np.array_equal(wy, y[lo:hi]) and np.array_equal(wdx, dx[lo:hi]) and np.allclose(wdz, dz[lo:hi],
                                                                                               rtol=1e-12, atol=1e-12)
     for c0, c1 in [(0, 3), (D - 5, D)]:
-        got = lu.lowrank_dU(SEEDS, B, T, D, R, W, c0, c1, "bf16")
+        got = lu.lowrank_dU(SEEDS, B, T, D, R, W, c0, c1, "bf16", cu)
         assert np.allclose(got, dU.reshape(R, D, W)[:, c0:c1].reshape(R, -1), rtol=1e-12, atol=1e-12)
 
 
