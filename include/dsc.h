@@ -272,11 +272,38 @@ DSC_API dsc_status dsc_static_fwd(void *stream, int dtype, int64_t B, int64_t T,
  *
  *   x, dy (B,T,D) in;  c (D,W) in;  dx (B,T,D) dtype out;  dc (D,W) fp32 out.
  *   dc is a sum over every token accumulated with fp32 atomics: its last
- *   bits may differ run to run.  An empty batch zero-fills dc.
+ *   bits may differ run to run (dsc_static_bwd_deterministic below gives
+ *   reproducible ones).  An empty batch zero-fills dc.
  */
 DSC_API dsc_status dsc_static_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
                           const void *x, const void *c, const void *dy, const int32_t *cu_seqlens,
                           int32_t n_seqs, int32_t residual, void *dx, float *dc);
+
+/*
+ * Bytes of device workspace dsc_static_bwd_deterministic needs: one fp32
+ * (D, W) region of dc per group of token tiles of the backward's work split,
+ * which depends on the sizes and dtype only (0 for an empty batch and for
+ * invalid sizes).  At B*T = 16384, D = 2304, W = 4 (bf16): 64 regions, 2.4 MB.
+ */
+DSC_API size_t dsc_static_bwd_deterministic_workspace_size(int dtype, int64_t B, int64_t T, int64_t D,
+                                                           int32_t W);
+
+/*
+ * The static backward above with dc summed in one fixed order, so that equal
+ * inputs give bitwise equal dc on every call and every device.  Each block
+ * of the backward adds its dc partial sums (already summed over its tiles in
+ * LDS) into a workspace region of its own group of token tiles, each element
+ * written once; a following launch adds the regions in ascending order.  dx
+ * is the same as dsc_static_bwd's.  Arguments, layouts and errors as for
+ * dsc_static_bwd, plus a workspace of at least
+ * dsc_static_bwd_deterministic_workspace_size() bytes, 16-byte aligned,
+ * contents undefined on entry and exit, overlapping no argument (may be NULL
+ * for an empty batch).
+ */
+DSC_API dsc_status dsc_static_bwd_deterministic(void *stream, int dtype, int64_t B, int64_t T, int64_t D,
+                                                int32_t W, const void *x, const void *c, const void *dy,
+                                                const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual,
+                                                void *dx, float *dc, void *workspace, size_t workspace_bytes);
 
 /*
  * Decoding: one new token per sequence, B sequences, with a rolling state.

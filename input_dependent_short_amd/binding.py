@@ -47,6 +47,10 @@ def lib() -> ctypes.CDLL:
         L.dsc_lowrank_bwd_deterministic.argtypes = L.dsc_lowrank_bwd.argtypes
         L.dsc_static_fwd.argtypes = [p, i, i64, i64, i64, i32, p, p, p, i32, i32, p]
         L.dsc_static_bwd.argtypes = [p, i, i64, i64, i64, i32, p, p, p, p, i32, i32, p, p]
+        L.dsc_static_bwd_deterministic_workspace_size.argtypes = [i, i64, i64, i64, i32]
+        L.dsc_static_bwd_deterministic_workspace_size.restype = ctypes.c_size_t
+        L.dsc_static_bwd_deterministic.argtypes = [p, i, i64, i64, i64, i32, p, p, p, p, i32, i32, p, p, p,
+                                                   ctypes.c_size_t]
         L.dsc_headwise_decode.argtypes = [p, i, i64, i64, i32, i32, p, p, p, i32, p]
         L.dsc_lowrank_decode.argtypes = [p, i, i64, i64, i32, i32, p, p, p, p, i32, p]
         L.dsc_state_from_prefill.argtypes = [p, i, i64, i64, i64, i32, p, p, i32, p]
@@ -56,7 +60,7 @@ def lib() -> ctypes.CDLL:
         L.dsc_headwise_rope_bwd.argtypes = [p, i, i64, i64, i64, i32, i32, p, p, p, p, i32, i32, i64, i32, p, i64,
                                             p, p]
         for f in ("dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd",
-                  "dsc_lowrank_bwd_deterministic",
+                  "dsc_lowrank_bwd_deterministic", "dsc_static_bwd_deterministic",
                   "dsc_static_fwd", "dsc_static_bwd", "dsc_headwise_decode", "dsc_lowrank_decode",
                   "dsc_state_from_prefill", "dsc_rope_table", "dsc_headwise_rope_fwd",
                   "dsc_headwise_rope_bwd", "dsc_headwise_rope_decode", "dsc_abi_version"):
@@ -232,6 +236,23 @@ def dsc_static_bwd(x, c, dy, dx, dc, *, cu_seqlens=None, residual=False, stream=
     cu, ns = _seq(cu_seqlens)
     _check(lib().dsc_static_bwd(_stream(stream), _dtype_code(x), B, T, D, W, _ptr(x), _ptr(c), _ptr(dy),
                                 cu, ns, int(bool(residual)), _ptr(dx), _ptr(dc)))
+
+
+def dsc_static_bwd_deterministic_workspace_size(dtype: torch.dtype, B: int, T: int, D: int, W: int) -> int:
+    code = DSC_BF16 if dtype == torch.bfloat16 else DSC_FP32
+    return int(lib().dsc_static_bwd_deterministic_workspace_size(code, B, T, D, W))
+
+
+def dsc_static_bwd_deterministic(x, c, dy, dx, dc, workspace=None, *, cu_seqlens=None, residual=False,
+                                 stream=None) -> None:
+    """dsc_static_bwd with dc summed in a fixed order (bitwise reproducible)."""
+    B, T, D = x.shape
+    W = c.shape[1]
+    cu, ns = _seq(cu_seqlens)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().dsc_static_bwd_deterministic(_stream(stream), _dtype_code(x), B, T, D, W, _ptr(x), _ptr(c),
+                                              _ptr(dy), cu, ns, int(bool(residual)), _ptr(dx), _ptr(dc),
+                                              _ptr(workspace), ws_bytes))
 
 
 def dsc_headwise_decode(x, w, state, y, *, residual=False, stream=None) -> None:

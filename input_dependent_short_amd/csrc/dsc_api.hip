@@ -324,28 +324,63 @@ dsc_status dsc_static_fwd(void *stream, int dtype, int64_t B, int64_t T, int64_t
     return launched(dsc::static_fwd(p, (hipStream_t)stream), "dsc_static_fwd launch");
 }
 
-dsc_status dsc_static_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
-                          const void *x, const void *c, const void *dy, const int32_t *cu_seqlens,
-                          int32_t n_seqs, int32_t residual, void *dx, float *dc) {
+namespace {
+
+// Validation and launch shared by the two static backward entry points.
+dsc_status static_bwd_call(bool det, const char *name, void *stream, int dtype, int64_t B, int64_t T, int64_t D,
+                           int32_t W, const void *x, const void *c, const void *dy, const int32_t *cu_seqlens,
+                           int32_t n_seqs, int32_t residual, void *dx, float *dc, void *workspace,
+                           size_t workspace_bytes) {
     DSC_TRY(check_common(dtype, B, T, D, W, cu_seqlens, n_seqs, residual));
+    const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
     if (B * T == 0) {  // empty batch: dc is a sum over no tokens, zero; dx has no elements
         if (!dc) return fail(DSC_ERR_NULL, "dc is required");
         if (!aligned16(dc)) return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
-        dsc::StProblem p{dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32, 0, T, D, W, nullptr, nullptr,
-                         nullptr, nullptr, nullptr, dc, nullptr, 0, residual};
-        return launched(dsc::static_bwd(p, (hipStream_t)stream), "dsc_static_bwd launch");
+        dsc::StProblem p{dt, 0, T, D, W, nullptr, nullptr, nullptr, nullptr, nullptr, dc, nullptr, 0, residual};
+        return launched(dsc::static_bwd(p, (hipStream_t)stream), name);
     }
     if (!x || !c || !dy || !dx || !dc) return fail(DSC_ERR_NULL, "x, c, dy, dx and dc are required");
     if (!aligned16(x) || !aligned16(c) || !aligned16(dy) || !aligned16(dx) || !aligned16(dc))
         return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    const size_t need = det ? dsc::static_bwd_det_workspace(dt, B * T, D, W) : 0;
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(DSC_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (!aligned16(workspace)) return fail(DSC_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+    }
     const size_t es = esize(dtype), N = (size_t)(B * T);
     const Range in[] = {rng("x", x, N * D * es), rng("c", c, (size_t)D * W * es), rng("dy", dy, N * D * es),
                         rng("cu_seqlens", cu_seqlens, cu_seqlens ? 4u * (n_seqs + 1) : 0)};
-    const Range out[] = {rng("dx", dx, N * D * es), rng("dc", dc, (size_t)D * W * 4)};
-    DSC_TRY(check_alias(in, 4, out, 2));
-    const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
+    const Range out[] = {rng("dx", dx, N * D * es), rng("dc", dc, (size_t)D * W * 4),
+                         rng("workspace", workspace, need)};
+    DSC_TRY(check_alias(in, 4, out, 3));
     dsc::StProblem p{dt, B * T, T, D, W, x, c, dy, nullptr, dx, dc, cu_seqlens, n_seqs, residual};
-    return launched(dsc::static_bwd(p, (hipStream_t)stream), "dsc_static_bwd launch");
+    const hipError_t e = det ? dsc::static_bwd_det(p, static_cast<float *>(workspace), (hipStream_t)stream)
+                             : dsc::static_bwd(p, (hipStream_t)stream);
+    return launched(e, name);
+}
+
+}  // namespace
+
+dsc_status dsc_static_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                          const void *x, const void *c, const void *dy, const int32_t *cu_seqlens,
+                          int32_t n_seqs, int32_t residual, void *dx, float *dc) {
+    return static_bwd_call(false, "dsc_static_bwd launch", stream, dtype, B, T, D, W, x, c, dy, cu_seqlens, n_seqs,
+                           residual, dx, dc, nullptr, 0);
+}
+
+size_t dsc_static_bwd_deterministic_workspace_size(int dtype, int64_t B, int64_t T, int64_t D, int32_t W) {
+    if (check_common(dtype, B, T, D, W, nullptr, 0, 0) != DSC_SUCCESS) return 0;
+    return dsc::static_bwd_det_workspace(dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32, B * T, D, W);
+}
+
+dsc_status dsc_static_bwd_deterministic(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                                        const void *x, const void *c, const void *dy, const int32_t *cu_seqlens,
+                                        int32_t n_seqs, int32_t residual, void *dx, float *dc, void *workspace,
+                                        size_t workspace_bytes) {
+    return static_bwd_call(true, "dsc_static_bwd_deterministic launch", stream, dtype, B, T, D, W, x, c, dy,
+                           cu_seqlens, n_seqs, residual, dx, dc, workspace, workspace_bytes);
 }
 
 namespace {

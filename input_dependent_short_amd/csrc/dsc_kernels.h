@@ -99,6 +99,10 @@ hipError_t static_fwd(const StProblem &p, hipStream_t s);
 // Zero-fills dc, then runs the backward (dx and the fp32 sums of dc); with
 // N = 0 only the zero-fill runs.
 hipError_t static_bwd(const StProblem &p, hipStream_t s);
+// Fixed-order backward: dc of each token-tile group in a region of ws (bytes
+// from static_bwd_det_workspace), the regions then added in order into dc.
+size_t static_bwd_det_workspace(Dtype dt, int64_t N, int64_t D, int32_t W);
+hipError_t static_bwd_det(const StProblem &p, float *ws, hipStream_t s);
 
 hipError_t decode_step(const DecProblem &p, hipStream_t s);
 // Last W-1 inputs of every sequence of a prefill into the state (S, W-1, D).

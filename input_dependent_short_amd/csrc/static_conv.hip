@@ -41,6 +41,7 @@ struct StParams {
     int64_t ntiles;   // token tiles
     int64_t ncg;      // backward: groups of cb chunks
     int32_t cb;       // backward: chunks per block (power of two, 8..64)
+    int64_t dc_stride;  // backward: dc of token-tile group q goes to dc + q*dc_stride (0: one sum)
 };
 
 constexpr int kBlock = 256;
@@ -299,9 +300,20 @@ __global__ __launch_bounds__(kBlock) void st_bwd_kernel(StParams p) {
             float v = 0.f;
             for (int t = 0; t < tpb; ++t) v += red[(t * EC + i) * pitch + cl];
             const int64_t ch = cg * cb + cl;
-            if (ch < p.nchunks) atomicAdd(p.dc + ch * NE + r0 + i, v);
+            if (ch < p.nchunks) atomicAdd(p.dc + tq * p.dc_stride + ch * NE + r0 + i, v);
         }
     }
+}
+
+// dst[i] = src[i] + src[stride + i] + ... + src[(nparts-1)*stride + i], in that
+// order: the fixed-order sum of the token-tile groups' dc regions.
+__global__ __launch_bounds__(kBlock) void st_sum_parts(const float *src, int64_t nparts, int64_t stride, float *dst,
+                                                       int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= n) return;
+    float a = 0.f;
+    for (int64_t j = 0; j < nparts; ++j) a += src[j * stride + i];
+    dst[i] = a;
 }
 
 // Zero-fills dc (n floats, 16-byte aligned) before the backward's atomics.
@@ -323,6 +335,15 @@ constexpr int kStU = 4;           // tokens per load batch (forward)
 // wider filter leave no room for the deeper batch
 constexpr int st_bwd_batch(int W) { return W <= 4 ? 4 : 2; }
 
+// Chunks per backward block: 64, or the largest of 32, 16, 8 that divides the
+// row when 64 does not (no idle lanes), else 64 with a ragged last group.
+int chunks_per_block(int64_t nchunks) {
+    if (nchunks % kWave == 0) return kWave;
+    for (int cb : {32, 16, 8})
+        if (nchunks % cb == 0) return cb;
+    return kWave;
+}
+
 template <class E>
 StParams make_params(const StProblem &pr) {
     StParams p;
@@ -334,49 +355,60 @@ StParams make_params(const StProblem &pr) {
     p.nchunks = pr.D / E::kVec;
     p.ntiles = (pr.N + kStTT - 1) / kStTT;
     p.items = p.ntiles * p.nchunks;
-    // chunks per backward block: 64, or the largest of 32, 16, 8 that divides
-    // the row when 64 does not (no idle lanes), else 64 with a ragged last group
-    p.cb = kWave;
-    if (p.nchunks % kWave != 0) {
-        for (int cb : {32, 16, 8}) {
-            if (p.nchunks % cb == 0) {
-                p.cb = cb;
-                break;
-            }
-        }
-    }
+    p.cb = chunks_per_block(p.nchunks);
     p.ncg = (p.nchunks + p.cb - 1) / p.cb;
+    p.dc_stride = 0;
     return p;
 }
 
+// Token-tile groups of the backward (blocks along the token axis): the
+// number of dc regions of the fixed-order backward.
+int64_t tile_groups(int64_t N, int64_t nchunks) {
+    const int64_t ntiles = (N + kStTT - 1) / kStTT;
+    const int64_t tpb = kBlock / chunks_per_block(nchunks);
+    return (ntiles + tpb - 1) / tpb;
+}
+
+// det_ws: the fixed-order backward's workspace (one dc region per token-tile
+// group, summed in order after the kernel), or null for the atomics into dc.
 template <class E, int W>
-hipError_t launch(const StProblem &pr, hipStream_t st, bool bwd) {
-    const StParams p = make_params<E>(pr);
+hipError_t launch(const StProblem &pr, hipStream_t st, bool bwd, float *det_ws = nullptr) {
+    StParams p = make_params<E>(pr);
     if (!bwd) {
         const int64_t blocks = (p.items + kBlock - 1) / kBlock;
         if (blocks) hipLaunchKernelGGL((st_fwd_kernel<E, W, kStTT, kStU>), dim3((unsigned)blocks), dim3(kBlock), 0, st, p);
         return hipGetLastError();
     }
     const int64_t nz = pr.D * pr.W;
-    hipLaunchKernelGGL(st_zero, dim3((unsigned)((nz + 4 * kBlock - 1) / (4 * kBlock))), dim3(kBlock), 0, st, pr.dc, nz);
+    const int64_t nq = tile_groups(pr.N, p.nchunks);
+    if (det_ws && nq > 0) {  // regions of their own, one per token-tile group
+        p.dc = det_ws;
+        p.dc_stride = nz;
+    }
+    const int64_t nclear = p.dc_stride ? nq * nz : nz;
+    hipLaunchKernelGGL(st_zero, dim3((unsigned)((nclear + 4 * kBlock - 1) / (4 * kBlock))), dim3(kBlock), 0, st, p.dc,
+                       nclear);
     const int64_t tpb = kBlock / p.cb;
     const int64_t blocks = (p.ntiles + tpb - 1) / tpb * p.ncg;  // none for an empty batch
     if (blocks)
         hipLaunchKernelGGL((st_bwd_kernel<E, W, kStTT, st_bwd_batch(W)>), dim3((unsigned)blocks), dim3(kBlock), 0, st, p);
+    if (p.dc_stride)
+        hipLaunchKernelGGL(st_sum_parts, dim3((unsigned)((nz + kBlock - 1) / kBlock)), dim3(kBlock), 0, st, p.dc, nq,
+                           nz, pr.dc, nz);
     return hipGetLastError();
 }
 
 template <class E>
-hipError_t dispatch(const StProblem &pr, hipStream_t st, bool bwd) {
+hipError_t dispatch(const StProblem &pr, hipStream_t st, bool bwd, float *det_ws = nullptr) {
     switch (pr.W) {
-        case 1: return launch<E, 1>(pr, st, bwd);
-        case 2: return launch<E, 2>(pr, st, bwd);
-        case 3: return launch<E, 3>(pr, st, bwd);
-        case 4: return launch<E, 4>(pr, st, bwd);
-        case 5: return launch<E, 5>(pr, st, bwd);
-        case 6: return launch<E, 6>(pr, st, bwd);
-        case 7: return launch<E, 7>(pr, st, bwd);
-        case 8: return launch<E, 8>(pr, st, bwd);
+        case 1: return launch<E, 1>(pr, st, bwd, det_ws);
+        case 2: return launch<E, 2>(pr, st, bwd, det_ws);
+        case 3: return launch<E, 3>(pr, st, bwd, det_ws);
+        case 4: return launch<E, 4>(pr, st, bwd, det_ws);
+        case 5: return launch<E, 5>(pr, st, bwd, det_ws);
+        case 6: return launch<E, 6>(pr, st, bwd, det_ws);
+        case 7: return launch<E, 7>(pr, st, bwd, det_ws);
+        case 8: return launch<E, 8>(pr, st, bwd, det_ws);
         default: return hipErrorInvalidValue;
     }
 }
@@ -389,6 +421,17 @@ hipError_t static_fwd(const StProblem &p, hipStream_t s) {
 
 hipError_t static_bwd(const StProblem &p, hipStream_t s) {
     return p.dtype == Dtype::BF16 ? dispatch<BF16>(p, s, true) : dispatch<F32>(p, s, true);
+}
+
+size_t static_bwd_det_workspace(Dtype dt, int64_t N, int64_t D, int32_t W) {
+    const int64_t nchunks = D / (dt == Dtype::BF16 ? BF16::kVec : F32::kVec);
+    if (N <= 0 || nchunks <= 0) return 0;
+    const size_t bytes = (size_t)tile_groups(N, nchunks) * (size_t)D * W * sizeof(float);
+    return (bytes + 255) & ~(size_t)255;
+}
+
+hipError_t static_bwd_det(const StProblem &p, float *ws, hipStream_t s) {
+    return p.dtype == Dtype::BF16 ? dispatch<BF16>(p, s, true, ws) : dispatch<F32>(p, s, true, ws);
 }
 
 }  // namespace dsc

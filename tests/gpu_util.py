@@ -99,15 +99,21 @@ def assert_close(name: str, gpu: np.ndarray, ref: np.ndarray, tol: float) -> flo
     return err
 
 
-def run_static(inp: dict, residual: bool, *, guard=True, repeat_bwd: int = 1):
+def run_static(inp: dict, residual: bool, *, guard=True, repeat_bwd: int = 1, deterministic=False):
     """Static conv forward and backward on the GPU; returns numpy fp64 (y, dx, dc)."""
     x, c, dy = dev(inp["x"]), dev(inp["c"]), dev(inp["dy"])
     cu = None if inp["cu_seqlens"] is None else torch.from_numpy(inp["cu_seqlens"]).cuda()
     y, dx = Guarded(x.shape, x.dtype), Guarded(x.shape, x.dtype)
     dc = Guarded(c.shape, torch.float32)
     binding.dsc_static_fwd(x, c, y.t, cu_seqlens=cu, residual=residual)
+    B, T, D = x.shape
+    nws = binding.dsc_static_bwd_deterministic_workspace_size(x.dtype, B, T, D, c.shape[1]) if deterministic else 0
+    ws = torch.full((max(nws, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda") if nws else None
     for _ in range(repeat_bwd):
-        binding.dsc_static_bwd(x, c, dy, dx.t, dc.t, cu_seqlens=cu, residual=residual)
+        if deterministic:
+            binding.dsc_static_bwd_deterministic(x, c, dy, dx.t, dc.t, ws, cu_seqlens=cu, residual=residual)
+        else:
+            binding.dsc_static_bwd(x, c, dy, dx.t, dc.t, cu_seqlens=cu, residual=residual)
     torch.cuda.synchronize()
     if guard:
         for name, g in (("y", y), ("dx", dx), ("dc", dc)):

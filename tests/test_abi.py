@@ -31,6 +31,7 @@ def test_header_declares_the_entry_points():
     for s in ("dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd",
               "dsc_lowrank_bwd_workspace_size", "dsc_lowrank_bwd_deterministic",
               "dsc_lowrank_bwd_deterministic_workspace_size", "dsc_static_fwd", "dsc_static_bwd",
+              "dsc_static_bwd_deterministic", "dsc_static_bwd_deterministic_workspace_size",
               "dsc_headwise_decode", "dsc_lowrank_decode", "dsc_state_from_prefill",
               "dsc_rope_table", "dsc_headwise_rope_fwd", "dsc_headwise_rope_bwd", "dsc_headwise_rope_decode",
               "dsc_status_string", "dsc_last_error", "dsc_abi_version"):
@@ -259,3 +260,21 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     w = torch.zeros(1, 8, 8, 4, dtype=torch.bfloat16)
     with pytest.raises(ImportError, match="not built"):
         binding.dsc_headwise_fwd(x, w, x, stream=0)
+
+
+def test_static_deterministic_validation(lib):
+    G = lambda k: ctypes.c_void_p((1 << 30) * k)
+    f = lambda ws=G(8), wsb=1 << 30, **k: lib.dsc_static_bwd_deterministic(
+        S0, 1, 8, 2048, 2304, 4, G(1), G(2), G(3), None, 0, 0, k.get("dx", G(4)), k.get("dc", G(5)), ws, wsb)
+    # D = 2304 bf16: 288 chunks of 8 channels, 32 per block (64 does not divide 288),
+    # so 8 token tiles of 32 per block; 16384 tokens = 512 tiles = 64 tile groups,
+    # each with one fp32 (D, W) region of dc
+    need = lib.dsc_static_bwd_deterministic_workspace_size(1, 8, 2048, 2304, 4)
+    assert need == 64 * 2304 * 4 * 4
+    assert lib.dsc_static_bwd_deterministic_workspace_size(1, 0, 2048, 2304, 4) == 0
+    assert lib.dsc_static_bwd_deterministic_workspace_size(1, 8, 2048, 2303, 4) == 0
+    assert f(ws=None, wsb=0) == 6
+    assert f(wsb=need - 1) == 6
+    assert f(ws=G(1)) == 5                     # workspace aliases x
+    assert f(dc=G(4)) == 5                     # dc aliases dx
+    assert f(dx=None) == 1

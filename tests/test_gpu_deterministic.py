@@ -1,4 +1,5 @@
-"""The reproducible low-rank backward, dsc_lowrank_bwd_deterministic (GPU).
+"""The reproducible backward passes, dsc_lowrank_bwd_deterministic and
+dsc_static_bwd_deterministic (GPU).
 
 Small shapes of every kernel family (matrix-core backward with two token
 halves, gathered z, two rank tiles and W = 8; the generic kernels in bf16 and
@@ -18,7 +19,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import TOL, assert_close, normwise_err, run_lowrank, say
+from gpu_util import TOL, assert_close, normwise_err, run_lowrank, run_static, say
 from input_dependent_short_amd import binding, inputs
 from input_dependent_short_amd.inputs import to_f64
 
@@ -114,3 +115,60 @@ def test_deterministic_full_size(cfg):
         _, _, rdU = oracle.lowrank_bwd(x64, z64, U64, g64, W, cu_seqlens=cu_np, residual=wl.residual,
                                        rows=(0, 0), channels=(c0, c1))
         assert_close("dU", dU3[:, c0:c1].reshape(R, (c1 - c0) * W), rdU, tol)
+
+
+# (dtype, B, T, D, W, residual, segment-length range or None)
+STATIC_CASES = [
+    ("bf16", 2, 300, 512, 4, True, None),
+    ("bf16", 1, 700, 2304, 3, False, (1, 200)),
+    ("bf16", 3, 45, 200, 8, True, None),      # 25 chunks: a ragged channel group
+    ("fp32", 2, 130, 96, 4, True, (1, 40)),
+    ("fp32", 1, 5, 16, 1, False, None),
+]
+
+
+@pytest.mark.parametrize("case", STATIC_CASES, ids=[f"{c[0]}-B{c[1]}T{c[2]}D{c[3]}W{c[4]}" for c in STATIC_CASES])
+def test_static_deterministic_small(case):
+    dt, B, T, D, W, res, seg = case
+    wl, inp = inputs.small("static", B, T, D, W, dtype=dt, residual=res, varlen=seg is not None,
+                           seglen_range=seg or (1, 8), seed=zlib.crc32(repr(case).encode()) % 1000)
+    say(f"[deterministic static] {wl.name} residual={res}")
+    first = run_static(inp, res, deterministic=True)
+    again = run_static(inp, res, deterministic=True, repeat_bwd=2)
+    for name, a, b in zip(("y", "dx", "dc"), first, again):
+        assert np.array_equal(a, b), f"{name} differs between two calls"
+    _, fdx, _ = run_static(inp, res)
+    assert np.array_equal(first[1], fdx), "dx differs from the fast backward's"
+    x64, c64, g64 = (to_f64(inp[k]) for k in ("x", "c", "dy"))
+    rdx, rdc = oracle.static_bwd(x64, c64, g64, cu_seqlens=inp["cu_seqlens"], residual=res)
+    tol = TOL[dt]
+    assert_close("dx", first[1], rdx, tol)
+    assert_close("dc", first[2], rdc, tol)
+
+
+@pytest.mark.parametrize("shape", [(8, 2048, 2304), (4, 4096, 8192)], ids=["qkv-150m", "mlp-2b"])
+def test_static_deterministic_full_size(shape):
+    B, T, D = shape
+    W = 4
+    wl, inp = inputs.small("static", B, T, D, W, dtype="bf16", residual=True, seed=77)
+    x, c, dy = (inp[k].cuda() for k in ("x", "c", "dy"))
+    nws = binding.dsc_static_bwd_deterministic_workspace_size(x.dtype, B, T, D, W)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    outs = []
+    for det in (True, True, False):
+        dx, dc = torch.empty_like(x), torch.empty(c.shape, dtype=torch.float32, device="cuda")
+        if det:
+            binding.dsc_static_bwd_deterministic(x, c, dy, dx, dc, ws, residual=True)
+        else:
+            binding.dsc_static_bwd(x, c, dy, dx, dc, residual=True)
+        torch.cuda.synchronize()
+        outs.append((dx, dc))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1]), "two calls differ"
+    assert torch.equal(outs[0][0], outs[2][0]), "dx differs from the fast backward's"
+    e = normwise_err(to_f64(outs[0][1]), to_f64(outs[2][1]))
+    say(f"[deterministic static] B={B} T={T} D={D}: dc against the fast backward {e:.2e}")
+    assert e <= 1e-6
+    c0, c1 = D - 8, D
+    x64, g64 = to_f64(inp["x"][:, :, c0:c1]), to_f64(inp["dy"][:, :, c0:c1])
+    _, rdc = oracle.static_bwd(x64, to_f64(inp["c"][c0:c1]), g64, residual=True, rows=(0, 0))
+    assert_close("dc", to_f64(outs[0][1][c0:c1]), rdc, TOL["bf16"])

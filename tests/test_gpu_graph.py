@@ -1,13 +1,13 @@
 """The training entry points under HIP graph capture (GPU).
 
 Forward and backward of the head-wise, low-rank (with its zero-fill and cast
-launches, and the fixed-order backward with its summing launches), static and
-head-wise + rotary layers are captured once as a single graph.  The graph is replayed three times; between replays the same calls run
+launches, and the fixed-order backward with its summing launches), static
+(also its fixed-order backward) and head-wise + rotary layers are captured once as a single graph.  The graph is replayed three times; between replays the same calls run
 eagerly on separate outputs, with synchronisation, and every replay is checked
 against them: bit for bit where no atomic sum is involved, and within 1e-6
 (fp32) or one bf16 rounding (bf16 dz) normwise for the sums accumulated with
 atomics (dz, dU, dc), whose order of addition varies from run to run.  The
-fixed-order backward's dz and dU are compared bit for bit.
+fixed-order backward passes' dz, dU and dc are compared bit for bit.
 """
 from __future__ import annotations
 
@@ -34,6 +34,9 @@ def _outputs(t: dict) -> dict:
     o["ld_ws"] = torch.empty(t["det_ws_bytes"], dtype=torch.uint8, device="cuda")
     o["st_y"], o["st_dx"] = torch.empty_like(t["sx"]), torch.empty_like(t["sx"])
     o["st_dc"] = torch.empty(t["c"].shape, dtype=torch.float32, device="cuda")
+    o["sd_dx"] = torch.empty_like(t["sx"])
+    o["sd_dc"] = torch.empty(t["c"].shape, dtype=torch.float32, device="cuda")
+    o["sd_ws"] = torch.empty(t["st_ws_bytes"], dtype=torch.uint8, device="cuda")
     return o
 
 
@@ -47,6 +50,7 @@ def _calls(t: dict, o: dict) -> None:
                                     o["ld_ws"], W=4)
     b.dsc_static_fwd(t["sx"], t["c"], o["st_y"], residual=True)
     b.dsc_static_bwd(t["sx"], t["c"], t["sdy"], o["st_dx"], o["st_dc"], residual=True)
+    b.dsc_static_bwd_deterministic(t["sx"], t["c"], t["sdy"], o["sd_dx"], o["sd_dc"], o["sd_ws"], residual=True)
     kw = dict(rot=512, head_dim=64, table=t["table"], cu_seqlens=t["cu"], residual=True)
     b.dsc_headwise_rope_fwd(t["hx"], t["hw"], o["rp_y"], **kw)
     b.dsc_headwise_rope_bwd(t["hx"], t["hw"], t["hdy"], o["rp_dx"], o["rp_dw"], **kw)
@@ -65,6 +69,7 @@ def test_training_entry_points_replayed_as_a_graph():
          "lx": li["x"].cuda(), "z": li["z"].cuda(), "U": li["U"].cuda(), "ldy": li["dy"].cuda(),
          "sx": si["x"].cuda(), "c": si["c"].cuda(), "sdy": si["dy"].cuda()}
     t["ws_bytes"] = max(16, binding.dsc_lowrank_bwd_workspace_size(torch.bfloat16, 2, 200, 256, 4, 32))
+    t["st_ws_bytes"] = max(16, binding.dsc_static_bwd_deterministic_workspace_size(torch.bfloat16, 2, 300, 512, 4))
     t["det_ws_bytes"] = max(16, binding.dsc_lowrank_bwd_deterministic_workspace_size(torch.bfloat16, 2, 200, 256, 4,
                                                                                      32))
     t["table"] = torch.empty(2 * 300, 32, 2, dtype=torch.float32, device="cuda")
@@ -88,7 +93,7 @@ def test_training_entry_points_replayed_as_a_graph():
         _calls(t, oe)
         torch.cuda.synchronize()
         for k, a in og.items():
-            if k in ("lr_ws", "ld_ws"):
+            if k in ("lr_ws", "ld_ws", "sd_ws"):
                 continue
             b = oe[k]
             if k in ATOMIC:
