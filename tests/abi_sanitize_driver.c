@@ -97,6 +97,14 @@ int main(void) {
     expect(dsc_static_bwd(0, DSC_BF16, 1, 0, 64, 4, NULL, NULL, NULL, NULL, 0, 0, NULL, NULL), DSC_ERR_NULL,
            "st empty needs dc");
 
+    const size_t sneed = dsc_static_bwd_deterministic_workspace_size(DSC_BF16, 8, 2048, 2304, 4);
+    if (sneed == 0) { fprintf(stderr, "static workspace size 0\n"); ++failures; }
+    expect((int)dsc_static_bwd_deterministic_workspace_size(DSC_BF16, big, big, 2304, 4), 0, "st det ws B*T");
+    expect(dsc_static_bwd_deterministic(0, DSC_BF16, 8, 2048, 2304, 4, P(1), P(2), P(3), NULL, 0, 0, P(4),
+                                        (float *)P(5), P(6), sneed - 1), DSC_ERR_WORKSPACE, "st det small workspace");
+    expect(dsc_static_bwd_deterministic(0, DSC_BF16, 8, 2048, 2304, 4, P(1), P(2), P(3), NULL, 0, 0, P(4),
+                                        (float *)P(5), P(3), sneed), DSC_ERR_ALIAS, "st det workspace alias");
+
     /* decoding */
     expect(dsc_headwise_decode(0, DSC_BF16, 4, 64, 4, 8, P(1), P(2), P(3), 0, P(3)), DSC_ERR_ALIAS, "dec alias");
     expect(dsc_headwise_decode(0, DSC_BF16, 4, 64, 4, 8, P(1), P(2), NULL, 0, P(4)), DSC_ERR_NULL, "dec state");
