@@ -605,6 +605,33 @@ def main() -> int:
             "workspace_bytes": nws, "algorithmic_GBps": round(lrc.bytes("bwd") / td[0] / 1e9, 1)}
         del det_ws
 
+        # The same for the static layer's dc, at the QKV ~150M head-wise shape.
+        hw2 = inputs.WORKLOADS[2]
+        swl = inputs.Workload(hw2.name.replace("headwise", "static"), "static", hw2.B, hw2.T, hw2.D, hw2.W,
+                              dtype=hw2.dtype, residual=hw2.residual, cfg=hw2.cfg)
+        sc = Case(swl, torch, binding, inputs)
+        nws = binding.dsc_static_bwd_deterministic_workspace_size(sc.x.dtype, swl.B, swl.T, swl.D, swl.W)
+        det_ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda")
+        calls = [lambda: binding.dsc_static_bwd_deterministic(sc.x, sc.c, sc.dy, sc.dx, sc.dc, det_ws,
+                                                              residual=swl.residual),
+                 sc.bwd]
+        for _ in range(3):
+            for f in calls:
+                f()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(reps)]
+        for e in evs:
+            e[0].record()
+            for i, f in enumerate(calls):
+                f()
+                e[i + 1].record()
+        torch.cuda.synchronize()
+        td = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / reps * 1e-3 for i in range(len(calls))]
+        out["static_bwd_deterministic"] = {
+            "workload": swl.name, "us": round(td[0] * 1e6, 1), "fast_us": round(td[1] * 1e6, 1),
+            "workspace_bytes": nws}
+        del det_ws, sc
+
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline([cases[0].wl, cases[1].wl], args.cpu_seconds)
     else:

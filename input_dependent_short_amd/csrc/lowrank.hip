@@ -953,6 +953,9 @@ __global__ __launch_bounds__(kBlock) void sum_parts(const float *src, int64_t np
     const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     if (i >= n) return;
     float a = 0.f;
+    // unrolled so that the loads of several regions are in flight together; the
+    // additions keep the ascending order
+#pragma unroll 16
     for (int64_t j = 0; j < nparts; ++j) a += src[j * stride + i];
     dst[i] = from_f32<T>(a);
 }

@@ -312,6 +312,9 @@ __global__ __launch_bounds__(kBlock) void st_sum_parts(const float *src, int64_t
     const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     if (i >= n) return;
     float a = 0.f;
+    // unrolled so that the loads of several regions are in flight together; the
+    // additions keep the ascending order
+#pragma unroll 16
     for (int64_t j = 0; j < nparts; ++j) a += src[j * stride + i];
     dst[i] = a;
 }
