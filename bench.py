@@ -1,22 +1,28 @@
 #!/usr/bin/env python
 """Benchmark of the dynamic short convolution hot path on one MI355X.
 
-One step = the whole hot path over one synthetic batch of the QKV workload
-at ~150M scale (B=8, T=2048, D=2304 = Q,K,V of width 768, W=4, bf16):
-  head-wise  (H=64, 36 filters per token, residual)  forward + backward,
-  low-rank   (R=32, filters generated on chip)       forward + backward,
+One step = the whole hot path over one synthetic batch of 16,384 tokens
+through the two dynamic-conv layers of a ~2B-parameter block:
+  MLP intermediate, head-wise  (B=4 T=4096 D=8192 W=4, H=16: 512 filters per
+                                token, residual)           forward + backward,
+  QKV, low-rank, packed seqs   (B=4 T=4096 D=6144 W=4, R=64: filters generated
+                                on chip; sequences of 256..4096 tokens)
+                                                           forward + backward,
 all through the C ABI of libdsc.so with inputs resident in HBM.
 
-Prints one JSON line: tokens/s of the step, achieved algorithmic HBM GB/s,
-the roofline of the dominant entry point (HIP events around each call on
-the stream it runs on), per-entry-point figures, the 2B-scale workloads
-(head-wise MLP D=8192 H=16 and low-rank varlen D=6144 R=64) timed the same
-way, the static short convolution (one fixed filter per channel) at the two
-head-wise shapes beside the dynamic figures, one-token decoding steps for 64
-sequences, and the fp64 CPU oracle timed on a bounded sample of the step's
-work.
+Prints one JSON line: tokens/s of the step (wall time of K steps bracketed by
+device synchronisation), achieved algorithmic HBM GB/s, per-entry-point
+figures (each call timed with HIP events on the stream it runs on, after a
+512 MiB write that evicts the last-level cache, median / min / mean over at
+least 50 calls), the roofline of the dominant entry point, the streaming
+ceiling measured with the library's own streaming kernel, and, as extras, the
+QKV ~150M step (head-wise H=64 and low-rank R=32 at B=8 T=2048 D=2304), the
+static short convolution beside the dynamic head-wise layer, decoding steps,
+the head-wise layer fused with the rotary embedding, the fixed-order
+backward passes, and the fp64 CPU oracle timed on a bounded sample of the
+step's work.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only]
 """
 from __future__ import annotations
 
@@ -131,8 +137,11 @@ def measured_traffic(entry: str):
 
 
 def cpu_baseline(wls, seconds: float):
-    """fp64 oracle on the first S tokens of row 0 of the step's workloads (both
-    variants, forward + backward), S grown until about `seconds` of CPU work."""
+    """fp64 oracle on the first S tokens of the step's workloads (both layers,
+    forward + backward; packed sequences cut at the sample's end), S grown
+    until about `seconds` of CPU work."""
+    import numpy as np
+
     import oracle
     from input_dependent_short_amd import inputs
     from input_dependent_short_amd.inputs import to_f64
@@ -142,12 +151,16 @@ def cpu_baseline(wls, seconds: float):
     Bmax = min(wl.B for wl in wls)
 
     def sample(d, S):
-        # S <= T: the first S tokens of row 0; beyond that whole rows (sequences)
+        # S <= T: the first S tokens of row 0; beyond that whole rows
         out = {}
         for n, v in d.items():
             if n == "cu_seqlens":
-                continue
-            if n == "U":
+                if v is not None:
+                    cu = [int(c) for c in v if c < S]
+                    out[n] = np.array(cu + [S], dtype=np.int32)
+                else:
+                    out[n] = None
+            elif n == "U":
                 out[n] = to_f64(v)
             elif S <= T:
                 out[n] = to_f64(v[0:1, :S])
@@ -160,19 +173,20 @@ def cpu_baseline(wls, seconds: float):
         t0 = time.perf_counter()
         for wl in wls:
             sl = a[wl.kind]
+            kw = dict(residual=wl.residual, cu_seqlens=sl["cu_seqlens"])
             if wl.kind == "headwise":
-                oracle.headwise_fwd(sl["x"], sl["w"], residual=wl.residual)
-                oracle.headwise_bwd(sl["x"], sl["w"], sl["dy"], residual=wl.residual)
+                oracle.headwise_fwd(sl["x"], sl["w"], **kw)
+                oracle.headwise_bwd(sl["x"], sl["w"], sl["dy"], **kw)
             else:
-                oracle.lowrank_fwd(sl["x"], sl["z"], sl["U"], wl.W, residual=wl.residual)
-                oracle.lowrank_bwd(sl["x"], sl["z"], sl["U"], sl["dy"], wl.W, residual=wl.residual)
+                oracle.lowrank_fwd(sl["x"], sl["z"], sl["U"], wl.W, **kw)
+                oracle.lowrank_bwd(sl["x"], sl["z"], sl["U"], sl["dy"], wl.W, **kw)
         return time.perf_counter() - t0
 
     def clamp(S):
         S = max(64, min(S, Bmax * T))
         return S if S <= T else (S // T) * T
 
-    S = 256
+    S = 64
     t = run(S)
     while t < seconds / 8 and S < Bmax * T:
         S = clamp(S * 4)
@@ -188,8 +202,8 @@ def cpu_baseline(wls, seconds: float):
     if passes > 1:
         desc += f", {passes} passes"
     return {"value": passes * S / t, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{desc} of the step's batch, head-wise and low-rank forward + backward "
-                      f"in fp64; {t:.1f} s of CPU time",
+            "sample": f"{desc} of the step's batch through both layers ({', '.join(wl.name for wl in wls)}), "
+                      f"forward + backward in fp64; {t:.1f} s of CPU time",
             "host": platform.processor() or platform.machine()}
 
 
@@ -312,19 +326,151 @@ def summarize_counters(fetch_dir: str, write_dir: str, out_json: str) -> dict:
     return rec
 
 
+def log(msg: str) -> None:
+    """Progress line on stderr (the JSON result is the only line on stdout)."""
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def timed_calls(torch, calls, iters, flush):
+    """Each call of `calls` (name -> fn) timed `iters` times with HIP events on
+    the current stream, each after a write of the flush buffer; returns
+    name -> sorted list of milliseconds."""
+    evs = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(iters)] for k in calls}
+    torch.cuda.synchronize()
+    for it in range(iters):
+        for k, fn in calls.items():
+            flush.fill_(it & 0xff)
+            a, b = evs[k][it]
+            a.record()
+            fn()
+            b.record()
+    torch.cuda.synchronize()
+    return {k: sorted(a.elapsed_time(b) for a, b in v) for k, v in evs.items()}
+
+
+def entry_figures(ms, nbytes, flops, entry, workload):
+    avg = sum(ms) / len(ms)
+    med, mn = ms[len(ms) // 2], ms[0]
+    return {"entry": entry, "workload": workload, "calls": len(ms), "avg_us": round(avg * 1e3, 2),
+            "median_us": round(med * 1e3, 2), "min_us": round(mn * 1e3, 2), "algorithmic_bytes": nbytes,
+            "GBps": round(nbytes / (avg * 1e-3) / 1e9, 1),
+            "GBps_median": round(nbytes / (med * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "TFLOPs": round(flops / (avg * 1e-3) / 1e12, 2)}
+
+
+ENTRY = {"headwise_fwd": "dsc_headwise_fwd", "headwise_bwd": "dsc_headwise_bwd",
+         "lowrank_fwd": "dsc_lowrank_fwd", "lowrank_bwd": "dsc_lowrank_bwd"}
+
+
+def step_calls(cases):
+    return {f"{c.wl.kind}_{d}": (c, d) for c in cases for d in ("fwd", "bwd")}
+
+
+def measure_step(torch, cases, K, warmup, iters, flush):
+    """Wall time of K steps (nothing but the entry-point calls inside), then
+    every call of the step timed on its own after a cache flush."""
+    calls = step_calls(cases)
+
+    def step():
+        for c, d in calls.values():
+            (c.fwd if d == "fwd" else c.bwd)()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = timed_calls(torch, {k: (c.fwd if d == "fwd" else c.bwd) for k, (c, d) in calls.items()}, iters, flush)
+    per = {k: entry_figures(ms[k], c.bytes(d), c.flops(d), ENTRY[k], c.wl.name) for k, (c, d) in calls.items()}
+    return wall / K * 1e3, per
+
+
+def stream_ceiling(torch, binding, mixes, reps, flush):
+    """Best rate of the library's streaming kernel (dsc_bench_stream) over a
+    few recipes, for each read / write byte mix: the practical ceiling of a
+    kernel moving those bytes, cache flushed before each launch."""
+    top = max(max(r, w) for r, w in mixes.values())
+    src = torch.empty(top, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(top, dtype=torch.uint8, device="cuda")
+    src.fill_(3)
+    recipes = [dict(unroll=u, load_nt=nt, store_nt=nt, chunked=ch) for u in (4, 8) for nt in (False, True)
+               for ch in (False, True)]
+    out = {}
+    for name, (rb, wb) in mixes.items():
+        best = None
+        for rcp in recipes:
+            fn = (lambda rb=rb, wb=wb, rcp=rcp: binding.dsc_bench_stream(src, rb, dst, wb, **rcp))
+            fn()
+            ms = timed_calls(torch, {"s": fn}, reps, flush)["s"]
+            gbps = (rb + wb) / (ms[len(ms) // 2] * 1e-3) / 1e9
+            if best is None or gbps > best[0]:
+                best = (gbps, rcp, ms)
+        gbps, rcp, ms = best
+        out[name] = {"read_bytes": rb, "write_bytes": wb, "GBps": round(gbps, 1),
+                     "median_us": round(ms[len(ms) // 2] * 1e3, 2), "min_us": round(ms[0] * 1e3, 2),
+                     "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4), "recipe": rcp}
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+def stream_sweep(torch, binding, inputs) -> int:
+    """Every recipe of dsc_bench_stream on the byte mixes of the MLP ~2B
+    head-wise layer (a 268 MB activation, its forward and backward mixes, pure
+    reads and writes, and a 1 GiB copy); prints the rate of each recipe."""
+    wl = inputs.WORKLOADS[4]
+    act = wl.N * wl.D * 2
+    filt = wl.N * (wl.D // wl.H) * wl.W * 2
+    mixes = {"copy_activation": (act, act), "copy_1GiB": (1 << 30, 1 << 30),
+             "headwise_fwd_mix": (act + filt, act), "headwise_bwd_mix": (2 * act + filt, act + filt),
+             "read_only": (3 * act + filt, 0), "write_only": (0, act + filt)}
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    top = max(max(r, w) for r, w in mixes.values())
+    src = torch.full((top,), 3, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(top, dtype=torch.uint8, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for name, (rb, wb) in mixes.items():
+        rows = []
+        for u in (1, 2, 4, 8):
+            for lnt, snt in ((False, False), (True, False), (False, True), (True, True)):
+                for ch in (False, True):
+                    for bl in (0, cus * 2, cus * 4, cus * 16, cus * 64):
+                        rcp = dict(unroll=u, load_nt=lnt, store_nt=snt, chunked=ch, blocks=bl)
+                        fn = (lambda rcp=rcp: binding.dsc_bench_stream(src, rb, dst, wb, **rcp))
+                        fn()
+                        ms = timed_calls(torch, {"s": fn}, 8, flush)["s"]
+                        rows.append((round((rb + wb) / (ms[len(ms) // 2] * 1e-3) / 1e9, 1), rcp))
+        rows.sort(key=lambda r: -r[0])
+        log(f"sweep {name}: best {rows[0]}")
+        print(json.dumps({"mix": name, "read_bytes": rb, "write_bytes": wb, "best": rows[:8],
+                          "worst": rows[-3:], "n": len(rows)}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
+    ap.add_argument("--iters", type=int, default=50, help="flushed calls timed per entry point (at least 50)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-large", action="store_true", help="skip the 2B-scale workloads")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the 2B step and its copy reference (for counter runs: every launch of an "
+                         "entry point's kernels then belongs to the headline workload)")
     ap.add_argument("--no-deterministic", action="store_true",
-                    help="skip the timing of the reproducible low-rank backward (whose kernel launches would "
+                    help="skip the timing of the fixed-order backward passes (whose kernel launches would "
                          "otherwise mix with the fast backward's in a kernel trace)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs of this script into profiles/traffic.json")
+    ap.add_argument("--stream-sweep", action="store_true",
+                    help="only sweep the streaming kernel's recipes (loads in flight, cache policies, order, "
+                         "grid size) over the byte mixes of the 2B head-wise layer; one JSON line per mix")
     args = ap.parse_args()
 
     if args.summarize_counters:
@@ -346,58 +492,26 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     binding.lib()  # fails loudly if the HIP library is not built
+    iters = max(50, args.iters)
+    if args.stream_sweep:
+        return stream_sweep(torch, binding, inputs)
+    # a 512 MiB write before every timed call evicts the inputs from the
+    # 256 MB last-level cache and the 4 MB L2 of each XCD
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
 
+    log("copy reference")
     copy_gbps = copy_ceiling(torch)
-    cases = [Case(inputs.WORKLOADS[2], torch, binding, inputs), Case(inputs.WORKLOADS[3], torch, binding, inputs)]
-    calls = [(f"{c.wl.kind}_{d}", c, d) for c in cases for d in ("fwd", "bwd")]
-    names = {"headwise_fwd": "dsc_headwise_fwd", "headwise_bwd": "dsc_headwise_bwd",
-             "lowrank_fwd": "dsc_lowrank_fwd", "lowrank_bwd": "dsc_lowrank_bwd"}
-
-    def step(events=None):
-        for i, (_, c, d) in enumerate(calls):
-            if events is not None:
-                events[i][0].record()
-            (c.fwd if d == "fwd" else c.bwd)()
-            if events is not None:
-                events[i][1].record()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
+    log("inputs of the 2B step")
+    cases = [Case(inputs.WORKLOADS[4], torch, binding, inputs), Case(inputs.WORKLOADS[5], torch, binding, inputs)]
     K = args.steps
-    # timed region 1: K whole steps, nothing but the entry-point calls inside
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(K):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # timed region 2: the same K steps with HIP events around every call (on
-    # the stream the kernels run on), for the per-entry durations; the event
-    # records themselves add host and queue work, so region 1 gives the step time
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
-          for _ in range(K)]
-    torch.cuda.synchronize()
-    for k in range(K):
-        step(ev[k])
-    torch.cuda.synchronize()
-    per_call = {}
-    for i, (key, c, d) in enumerate(calls):
-        ms = sorted(ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(K))
-        avg = sum(ms) / K
-        b = c.bytes(d)
-        per_call[key] = {"entry": names[key], "workload": c.wl.name, "avg_us": round(avg * 1e3, 2),
-                         "median_us": round(ms[K // 2] * 1e3, 2), "algorithmic_bytes": b,
-                         "GBps": round(b / (avg * 1e-3) / 1e9, 1),
-                         "frac_hbm_peak": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                         "TFLOPs": round(c.flops(d) / (avg * 1e-3) / 1e12, 2)}
-    ms_step = wall / K * 1e3
+    log("timing the 2B step")
+    ms_step, per_call = measure_step(torch, cases, K, args.warmup, iters, flush)
     N = cases[0].wl.N
-    step_bytes = sum(c.bytes(d) for _, c, d in calls)
+    step_bytes = sum(c.bytes(d) for c, d in step_calls(cases).values())
     dom_key = max(per_call, key=lambda k: per_call[k]["avg_us"])
     dom = per_call[dom_key]
     traffic = measured_traffic(dom["entry"])
+    hw4, lr5 = cases[0].wl, cases[1].wl
 
     out = {
         "metric": METRIC,
@@ -412,175 +526,197 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "QKV dynamic short conv at ~150M scale: head-wise (H=64, residual) and "
-                               "low-rank (R=32) forward+backward on one batch",
-                   "B": 8, "T": 2048, "D": 2304, "W": 4, "H": 64, "R": 32, "dtype": "bf16"},
+        "config": {"workload": "one batch of 16384 tokens through the two dynamic-conv layers of a ~2B block: "
+                               "MLP intermediate head-wise (H=16, residual) and QKV low-rank (R=64, packed "
+                               "sequences of 256..4096 tokens), forward+backward",
+                   "mlp_headwise": {"B": hw4.B, "T": hw4.T, "D": hw4.D, "W": hw4.W, "H": hw4.H},
+                   "qkv_lowrank": {"B": lr5.B, "T": lr5.T, "D": lr5.D, "W": lr5.W, "R": lr5.R,
+                                   "sequences": int(len(cases[1].cu) - 1)},
+                   "dtype": "bf16"},
         "achieved_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-        "roofline": {"bound": "hbm", "kernel": dom["entry"], "achieved": dom["GBps"],
-                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": dom["frac_hbm_peak"],
+        "roofline": {"bound": "hbm", "kernel": dom["entry"], "workload": dom["workload"],
+                     "achieved": dom["GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": dom["frac_hbm_peak"],
                      "traffic": traffic, "bytes_per_launch": dom["algorithmic_bytes"],
-                     "avg_launch_us": dom["avg_us"]},
+                     "avg_launch_us": dom["avg_us"], "median_launch_us": dom["median_us"],
+                     "min_launch_us": dom["min_us"]},
         "per_entry": per_call,
+        "fwd_bwd": {c.wl.name: {"fwd_bwd_us": round(per_call[f"{c.wl.kind}_fwd"]["avg_us"]
+                                                   + per_call[f"{c.wl.kind}_bwd"]["avg_us"], 1),
+                                "GBps": round((c.bytes("fwd") + c.bytes("bwd"))
+                                              / ((per_call[f"{c.wl.kind}_fwd"]["avg_us"]
+                                                  + per_call[f"{c.wl.kind}_bwd"]["avg_us"]) * 1e-6) / 1e9, 1)}
+                    for c in cases},
         "copy_ceiling_GBps": round(copy_gbps, 1),
-        # a device copy moving as many bytes as the dominant entry's algorithmic traffic
-        "copy_same_bytes_GBps": round(copy_rate(torch, dom["algorithmic_bytes"]), 1),
     }
+    for v in out["fwd_bwd"].values():
+        v["frac_hbm_peak"] = round(v["GBps"] / PEAK_HBM_GBPS, 4)
+    if args.headline_only:
+        print(json.dumps(out), flush=True)
+        return 0
 
-    def fwd_bwd_times(wl, reps):
-        """Average fwd and bwd seconds of one workload, HIP events around each call."""
-        c = Case(wl, torch, binding, inputs)
-        for _ in range(3):
-            c.fwd(); c.bwd()
-        torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-                torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for e in evs:
-            e[0].record(); c.fwd(); e[1].record(); c.bwd(); e[2].record()
-        torch.cuda.synchronize()
-        tf = sum(e[0].elapsed_time(e[1]) for e in evs) / reps * 1e-3
-        tb = sum(e[1].elapsed_time(e[2]) for e in evs) / reps * 1e-3
-        b = c.bytes("fwd") + c.bytes("bwd")
-        del c
+    # the practical ceiling of the same byte mixes (and of a plain copy) with
+    # the library's own streaming kernel, and of one device copy of the
+    # dominant entry's bytes
+    log("streaming ceiling")
+    c4 = cases[0]
+    out["stream_ceiling"] = stream_ceiling(torch, binding, {
+        "copy_activation": (c4.x.numel() * 2, c4.x.numel() * 2),
+        "headwise_fwd_mix": (c4.bytes("fwd") - c4.x.numel() * 2, c4.x.numel() * 2),
+        "headwise_bwd_mix": (c4.bytes("bwd") - c4.x.numel() * 2 - c4.w.numel() * 2,
+                             c4.x.numel() * 2 + c4.w.numel() * 2),
+        "read_only": (c4.bytes("bwd"), 0),
+        "write_only": (0, c4.x.numel() * 2)}, 10, flush)
+    out["copy_same_bytes_GBps"] = round(copy_rate(torch, dom["algorithmic_bytes"]), 1)
+    del cases, c4
+    torch.cuda.empty_cache()
+
+    # the QKV ~150M step (head-wise H=64 with residual, low-rank R=32) measured the same way
+    log("QKV ~150M step")
+    small = [Case(inputs.WORKLOADS[2], torch, binding, inputs), Case(inputs.WORKLOADS[3], torch, binding, inputs)]
+    ms_small, per_small = measure_step(torch, small, K, args.warmup, iters, flush)
+    small_bytes = sum(c.bytes(d) for c, d in step_calls(small).values())
+    out["qkv_150m_step"] = {"workload": "QKV dynamic short conv at ~150M scale: head-wise (H=64, residual) and "
+                                        "low-rank (R=32) forward+backward, B=8 T=2048 D=2304 W=4",
+                            "ms_per_step": round(ms_small, 4),
+                            "tokens_per_s": round(small[0].wl.N / (ms_small * 1e-3), 1),
+                            "GBps": round(small_bytes / (ms_small * 1e-3) / 1e9, 1),
+                            "per_entry": per_small}
+    hwc, lrc = small
+
+    # The pages set the dynamic kernels' latency against optimised kernels of
+    # the static short convolution (one fixed filter per channel).  Our own
+    # static kernels at the two head-wise shapes, timed the same way (flushed
+    # calls), beside the dynamic head-wise figures of this run.
+    log("static vs dynamic")
+    static = {}
+    for cfg, dyn in ((2, (per_small["headwise_fwd"]["avg_us"], per_small["headwise_bwd"]["avg_us"])),
+                     (4, (per_call["headwise_fwd"]["avg_us"], per_call["headwise_bwd"]["avg_us"]))):
+        hw = inputs.WORKLOADS[cfg]
+        wl = inputs.Workload(hw.name.replace("headwise", "static"), "static", hw.B, hw.T, hw.D, hw.W,
+                             dtype=hw.dtype, residual=hw.residual, cfg=hw.cfg)
+        sc = Case(wl, torch, binding, inputs)
+        ms = timed_calls(torch, {"fwd": sc.fwd, "bwd": sc.bwd}, iters, flush)
+        tf, tb = (sum(ms[k]) / len(ms[k]) * 1e-3 for k in ("fwd", "bwd"))
+        b = sc.bytes("fwd") + sc.bytes("bwd")
+        static[wl.name] = {"fwd_us": round(tf * 1e6, 1), "bwd_us": round(tb * 1e6, 1),
+                           "GBps": round(b / (tf + tb) / 1e9, 1),
+                           "frac_hbm_peak": round(b / (tf + tb) / 1e9 / PEAK_HBM_GBPS, 4),
+                           "dynamic_headwise_fwd_us": dyn[0], "dynamic_headwise_bwd_us": dyn[1],
+                           "dynamic_over_static": round((dyn[0] + dyn[1]) / ((tf + tb) * 1e6), 3)}
+        del sc
         torch.cuda.empty_cache()
-        return tf, tb, b
+    out["static_vs_dynamic"] = static
 
-    if not args.no_large:
-        large = {}
-        for cfg in (4, 5):
-            wl = inputs.WORKLOADS[cfg]
-            tf, tb, b = fwd_bwd_times(wl, max(5, K // 2))
-            large[wl.name] = {"tokens_per_s": round(wl.N / (tf + tb), 1),
-                              "fwd_us": round(tf * 1e6, 1), "bwd_us": round(tb * 1e6, 1),
-                              "GBps": round(b / (tf + tb) / 1e9, 1),
-                              "frac_hbm_peak": round(b / (tf + tb) / 1e9 / PEAK_HBM_GBPS, 4)}
-        out["workloads_2b"] = large
-
-        # The pages set the dynamic kernels' latency against optimised kernels of
-        # the static short convolution (one fixed filter per channel).  Our own
-        # static kernels at the two head-wise shapes, timed the same way, beside
-        # the dynamic head-wise figures above.
-        static = {}
-        for cfg, dyn in ((2, (per_call["headwise_fwd"]["avg_us"], per_call["headwise_bwd"]["avg_us"])),
-                         (4, (large["headwise-mlp-2b"]["fwd_us"], large["headwise-mlp-2b"]["bwd_us"]))):
-            hw = inputs.WORKLOADS[cfg]
-            wl = inputs.Workload(hw.name.replace("headwise", "static"), "static", hw.B, hw.T, hw.D, hw.W,
-                                 dtype=hw.dtype, residual=hw.residual, cfg=hw.cfg)
-            tf, tb, b = fwd_bwd_times(wl, max(5, K // 2))
-            static[wl.name] = {"fwd_us": round(tf * 1e6, 1), "bwd_us": round(tb * 1e6, 1),
-                               "GBps": round(b / (tf + tb) / 1e9, 1),
-                               "frac_hbm_peak": round(b / (tf + tb) / 1e9 / PEAK_HBM_GBPS, 4),
-                               "dynamic_headwise_fwd_us": dyn[0], "dynamic_headwise_bwd_us": dyn[1],
-                               "dynamic_over_static": round((dyn[0] + dyn[1]) / ((tf + tb) * 1e6), 3)}
-        out["static_vs_dynamic"] = static
-
-        # decoding: one new token for each of 64 sequences per step, at the QKV
-        # ~150M width (inputs are rows of the step's seeded tensors); the state
-        # is updated in place step after step.  us_per_step is a HIP graph of
-        # the steps replayed (GPU time); us_per_step_eager launches each step
-        # from Python (host-bound at this size)
-        S_DEC, STEPS_DEC = 64, 200
-        hwc, lrc = cases[0], cases[1]
-        D, Wd = hwc.wl.D, hwc.wl.W
-        xd = hwc.x.view(-1, D)[:S_DEC].contiguous()
-        wd = hwc.w.view(-1, D // hwc.wl.H, Wd)[:S_DEC].contiguous()
-        zd = lrc.z.view(-1, lrc.wl.R)[:S_DEC].contiguous()
-        yd = torch.empty_like(xd)
-        state = torch.zeros(S_DEC, Wd - 1, D, dtype=xd.dtype, device="cuda")
-        es = xd.element_size()
-        act = S_DEC * D * es
-        # the rotated step: queries and keys (channels [0, 1536), heads of 64) at
-        # positions 1000 + b, cos / sin rows read once per (sequence, chunk)
-        dec_table = torch.empty(2048, 32, 2, dtype=torch.float32, device="cuda")
-        binding.dsc_rope_table(dec_table)
-        dec_pos = torch.arange(1000, 1000 + S_DEC, dtype=torch.int32, device="cuda")
-        dec_calls = {
-            "headwise-qkv-150m": (lambda: binding.dsc_headwise_decode(xd, wd, state, yd, residual=True),
-                                  2 * act + 2 * (Wd - 1) * act + wd.numel() * es),
-            "headwise-rope-qkv-150m": (lambda: binding.dsc_headwise_rope_decode(
-                                           xd, wd, state, yd, dec_pos, rot=1536, head_dim=64, table=dec_table,
-                                           residual=True),
-                                       2 * act + 2 * (Wd - 1) * act + wd.numel() * es + S_DEC * 4),
-            "lowrank-qkv-150m": (lambda: binding.dsc_lowrank_decode(xd, zd, lrc.U, state, yd, W=Wd),
-                                 2 * act + 2 * (Wd - 1) * act + zd.numel() * es + lrc.U.numel() * es),
-        }
-        dec = {}
-        for name, (fn, nbytes) in dec_calls.items():
-            for _ in range(10):
-                fn()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            a.record()
+    # decoding: one new token for each of 64 sequences per step, at the QKV
+    # ~150M width (inputs are rows of the step's seeded tensors); the state
+    # is updated in place step after step.  us_per_step is a HIP graph of
+    # the steps replayed (GPU time); us_per_step_eager launches each step
+    # from Python (host-bound at this size)
+    log("decoding")
+    S_DEC, STEPS_DEC = 64, 200
+    D, Wd = hwc.wl.D, hwc.wl.W
+    xd = hwc.x.view(-1, D)[:S_DEC].contiguous()
+    wd = hwc.w.view(-1, D // hwc.wl.H, Wd)[:S_DEC].contiguous()
+    zd = lrc.z.view(-1, lrc.wl.R)[:S_DEC].contiguous()
+    yd = torch.empty_like(xd)
+    state = torch.zeros(S_DEC, Wd - 1, D, dtype=xd.dtype, device="cuda")
+    es = xd.element_size()
+    act = S_DEC * D * es
+    # the rotated step: queries and keys (channels [0, 1536), heads of 64) at
+    # positions 1000 + b, cos / sin rows read once per (sequence, chunk)
+    dec_table = torch.empty(2048, 32, 2, dtype=torch.float32, device="cuda")
+    binding.dsc_rope_table(dec_table)
+    dec_pos = torch.arange(1000, 1000 + S_DEC, dtype=torch.int32, device="cuda")
+    dec_calls = {
+        "headwise-qkv-150m": (lambda: binding.dsc_headwise_decode(xd, wd, state, yd, residual=True),
+                              2 * act + 2 * (Wd - 1) * act + wd.numel() * es),
+        "headwise-rope-qkv-150m": (lambda: binding.dsc_headwise_rope_decode(
+                                       xd, wd, state, yd, dec_pos, rot=1536, head_dim=64, table=dec_table,
+                                       residual=True),
+                                   2 * act + 2 * (Wd - 1) * act + wd.numel() * es + S_DEC * 4),
+        "lowrank-qkv-150m": (lambda: binding.dsc_lowrank_decode(xd, zd, lrc.U, state, yd, W=Wd),
+                             2 * act + 2 * (Wd - 1) * act + zd.numel() * es + lrc.U.numel() * es),
+    }
+    dec = {}
+    for name, (fn, nbytes) in dec_calls.items():
+        for _ in range(10):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(STEPS_DEC):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        t_eager = a.elapsed_time(b) * 1e-3 / STEPS_DEC
+        # the same steps captured once as a HIP graph and replayed: the GPU's
+        # own time per step, without the host's per-call launch work
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(g):
             for _ in range(STEPS_DEC):
                 fn()
-            b.record()
-            torch.cuda.synchronize()
-            t_eager = a.elapsed_time(b) * 1e-3 / STEPS_DEC
-            # the same steps captured once as a HIP graph and replayed: the GPU's
-            # own time per step, without the host's per-call launch work
-            g = torch.cuda.CUDAGraph()
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                fn()
-            torch.cuda.current_stream().wait_stream(side)
-            with torch.cuda.graph(g):
-                for _ in range(STEPS_DEC):
-                    fn()
-            g.replay()
-            torch.cuda.synchronize()
-            a.record()
-            g.replay()
-            b.record()
-            torch.cuda.synchronize()
-            t = a.elapsed_time(b) * 1e-3 / STEPS_DEC
-            dec[name] = {"sequences": S_DEC, "us_per_step": round(t * 1e6, 2),
-                         "us_per_step_eager": round(t_eager * 1e6, 2),
-                         "tokens_per_s": round(S_DEC / t, 1), "bytes_per_step": nbytes,
-                         "GBps": round(nbytes / t / 1e9, 1)}
-            del g
-        out["decode"] = dec
-
-        # The layer on the query / key / value projections feeds the rotary
-        # embedding of the queries and keys.  The fused calls rotate channels
-        # [0, 1536) (12 query and 12 key heads of 64) of the QKV ~150M
-        # workload on the fly; the layer alone is timed in the same loop.  A
-        # separate rotation pass would move rot*N elements in and out once
-        # more in each direction (unfused_extra_bytes per direction).
-        hd, rot = 64, 2 * 768
-        table = torch.empty(hwc.wl.T, hd // 2, 2, dtype=torch.float32, device="cuda")
-        binding.dsc_rope_table(table, base=10000.0)
-        kw = dict(rot=rot, head_dim=hd, table=table, residual=hwc.wl.residual)
-        calls = [lambda: binding.dsc_headwise_rope_fwd(hwc.x, hwc.w, hwc.y, **kw),
-                 lambda: binding.dsc_headwise_rope_bwd(hwc.x, hwc.w, hwc.dy, hwc.dx, hwc.dw, **kw),
-                 hwc.fwd, hwc.bwd]
-        for _ in range(3):
-            for f in calls:
-                f()
+        g.replay()
         torch.cuda.synchronize()
-        reps = max(5, K // 2)
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(reps)]
-        for e in evs:
-            e[0].record()
-            for i, f in enumerate(calls):
-                f()
-                e[i + 1].record()
+        a.record()
+        g.replay()
+        b.record()
         torch.cuda.synchronize()
-        tr = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / reps * 1e-3 for i in range(len(calls))]
-        b = hwc.bytes("fwd") + hwc.bytes("bwd") + 2 * table.numel() * 4
-        out["rope_fused"] = {
-            "workload": f"{hwc.wl.name} + rotary embedding of channels [0, {rot}), heads of {hd}",
-            "fwd_us": round(tr[0] * 1e6, 1), "bwd_us": round(tr[1] * 1e6, 1),
-            "GBps": round(b / (tr[0] + tr[1]) / 1e9, 1),
-            "frac_hbm_peak": round(b / (tr[0] + tr[1]) / 1e9 / PEAK_HBM_GBPS, 4),
-            "layer_alone_fwd_us": round(tr[2] * 1e6, 1), "layer_alone_bwd_us": round(tr[3] * 1e6, 1),
-            "unfused_extra_bytes": 2 * rot * hwc.wl.N * hwc.x.element_size()}
-        del table
+        t = a.elapsed_time(b) * 1e-3 / STEPS_DEC
+        dec[name] = {"sequences": S_DEC, "us_per_step": round(t * 1e6, 2),
+                     "us_per_step_eager": round(t_eager * 1e6, 2),
+                     "tokens_per_s": round(S_DEC / t, 1), "bytes_per_step": nbytes,
+                     "GBps": round(nbytes / t / 1e9, 1)}
+        del g
+    out["decode"] = dec
 
-        # The reproducible low-rank backward (dz and dU summed in a fixed order
-        # through per-block workspace regions) against the fast one, at the
-        # QKV ~150M low-rank size, alternating in the same loop.
-    if not args.no_large and not args.no_deterministic:
+    # The layer on the query / key / value projections feeds the rotary
+    # embedding of the queries and keys.  The fused calls rotate channels
+    # [0, 1536) (12 query and 12 key heads of 64) of the QKV ~150M
+    # workload on the fly; the layer alone is timed in the same loop.  A
+    # separate rotation pass would move rot*N elements in and out once
+    # more in each direction (unfused_extra_bytes per direction).
+    log("fused rotary embedding")
+    hd, rot = 64, 2 * 768
+    table = torch.empty(hwc.wl.T, hd // 2, 2, dtype=torch.float32, device="cuda")
+    binding.dsc_rope_table(table, base=10000.0)
+    kw = dict(rot=rot, head_dim=hd, table=table, residual=hwc.wl.residual)
+    calls = [lambda: binding.dsc_headwise_rope_fwd(hwc.x, hwc.w, hwc.y, **kw),
+             lambda: binding.dsc_headwise_rope_bwd(hwc.x, hwc.w, hwc.dy, hwc.dx, hwc.dw, **kw),
+             hwc.fwd, hwc.bwd]
+    for _ in range(3):
+        for f in calls:
+            f()
+    torch.cuda.synchronize()
+    reps = max(5, K // 2)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(reps)]
+    for e in evs:
+        e[0].record()
+        for i, f in enumerate(calls):
+            f()
+            e[i + 1].record()
+    torch.cuda.synchronize()
+    tr = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / reps * 1e-3 for i in range(len(calls))]
+    b = hwc.bytes("fwd") + hwc.bytes("bwd") + 2 * table.numel() * 4
+    out["rope_fused"] = {
+        "workload": f"{hwc.wl.name} + rotary embedding of channels [0, {rot}), heads of {hd}",
+        "fwd_us": round(tr[0] * 1e6, 1), "bwd_us": round(tr[1] * 1e6, 1),
+        "GBps": round(b / (tr[0] + tr[1]) / 1e9, 1),
+        "frac_hbm_peak": round(b / (tr[0] + tr[1]) / 1e9 / PEAK_HBM_GBPS, 4),
+        "layer_alone_fwd_us": round(tr[2] * 1e6, 1), "layer_alone_bwd_us": round(tr[3] * 1e6, 1),
+        "unfused_extra_bytes": 2 * rot * hwc.wl.N * hwc.x.element_size()}
+    del table
+
+    # The reproducible low-rank backward (dz and dU summed in a fixed order
+    # through per-block workspace regions) against the fast one, at the
+    # QKV ~150M low-rank size, alternating in the same loop.
+    if not args.no_deterministic:
+        log("fixed-order backward passes")
         lw = lrc.wl
         nws = binding.dsc_lowrank_bwd_deterministic_workspace_size(lrc.x.dtype, lw.B, lw.T, lw.D, lw.W, lw.R)
         det_ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda")
@@ -633,7 +769,8 @@ def main() -> int:
         del det_ws, sc
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline([cases[0].wl, cases[1].wl], args.cpu_seconds)
+        log("CPU oracle sample")
+        out["cpu_baseline"] = cpu_baseline([inputs.WORKLOADS[4], inputs.WORKLOADS[5]], args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
 

@@ -59,7 +59,8 @@ def lib() -> ctypes.CDLL:
         L.dsc_headwise_rope_fwd.argtypes = [p, i, i64, i64, i64, i32, i32, p, p, p, i32, i32, i64, i32, p, i64, p]
         L.dsc_headwise_rope_bwd.argtypes = [p, i, i64, i64, i64, i32, i32, p, p, p, p, i32, i32, i64, i32, p, i64,
                                             p, p]
-        for f in ("dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd",
+        L.dsc_bench_stream.argtypes = [p, p, i64, p, i64, i32, i32, i32, i32, i64]
+        for f in ("dsc_bench_stream", "dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd",
                   "dsc_lowrank_bwd_deterministic", "dsc_static_bwd_deterministic",
                   "dsc_static_fwd", "dsc_static_bwd", "dsc_headwise_decode", "dsc_lowrank_decode",
                   "dsc_state_from_prefill", "dsc_rope_table", "dsc_headwise_rope_fwd",
@@ -277,6 +278,15 @@ def dsc_state_from_prefill(x, state, *, W, cu_seqlens=None, stream=None) -> None
     cu, ns = _seq(cu_seqlens)
     _check(lib().dsc_state_from_prefill(_stream(stream), _dtype_code(x), B, T, D, W, _ptr(x), cu, ns,
                                         _ptr(state)))
+
+
+def dsc_bench_stream(src, read_bytes: int, dst, write_bytes: int, *, unroll=4, load_nt=False, store_nt=False,
+                     chunked=False, blocks=0, stream=None) -> None:
+    """Streaming measurement kernel (include/dsc_bench.h): reads read_bytes of
+    src and writes write_bytes of dst (raw device buffers, any dtype)."""
+    _check(lib().dsc_bench_stream(_stream(stream), _ptr(src), int(read_bytes), _ptr(dst), int(write_bytes),
+                                  int(unroll), int(bool(load_nt)), int(bool(store_nt)), int(bool(chunked)),
+                                  int(blocks)))
 
 
 def dsc_abi_version() -> int:

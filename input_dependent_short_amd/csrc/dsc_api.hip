@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include "../../include/dsc.h"
+#include "../../include/dsc_bench.h"
 #include "dsc_kernels.h"
 
 namespace {
@@ -492,6 +493,27 @@ dsc_status dsc_state_from_prefill(void *stream, int dtype, int64_t B, int64_t T,
     const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
     return launched(dsc::state_from_prefill(dt, x, cu_seqlens, n_seqs, B, T, D, W, state, (hipStream_t)stream),
                     "dsc_state_from_prefill launch");
+}
+
+dsc_status dsc_bench_stream(void *stream, const void *src, int64_t read_bytes, void *dst, int64_t write_bytes,
+                            int32_t unroll, int32_t load_nt, int32_t store_nt, int32_t chunked, int64_t blocks) {
+    const int64_t kMax = (int64_t)1 << 40;
+    if (read_bytes < 0 || write_bytes < 0 || read_bytes >= kMax || write_bytes >= kMax || read_bytes % 16 ||
+        write_bytes % 16)
+        return fail(DSC_ERR_SHAPE, "byte counts must be multiples of 16 in [0, 2^40)");
+    if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8)
+        return fail(DSC_ERR_SHAPE, "unroll must be 1, 2, 4 or 8 (got %d)", unroll);
+    if ((load_nt != 0 && load_nt != 1) || (store_nt != 0 && store_nt != 1) || (chunked != 0 && chunked != 1))
+        return fail(DSC_ERR_SHAPE, "load_nt, store_nt and chunked must be 0 or 1");
+    if (blocks < 0 || blocks > ((int64_t)1 << 30)) return fail(DSC_ERR_SHAPE, "blocks out of range");
+    if (!dst || (read_bytes && !src)) return fail(DSC_ERR_NULL, "dst (and src when reading) are required");
+    if (!aligned16(dst) || (src && !aligned16(src))) return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    const Range in[] = {rng("src", src, (size_t)read_bytes)};
+    const Range out[] = {rng("dst", dst, (size_t)(write_bytes > 16 ? write_bytes : 16))};
+    DSC_TRY(check_alias(in, 1, out, 1));
+    return launched(dsc::stream_probe(src, read_bytes, dst, write_bytes, unroll, load_nt == 1, store_nt == 1,
+                                      chunked == 1, blocks, (hipStream_t)stream),
+                    "dsc_bench_stream launch");
 }
 
 const char *dsc_status_string(int status) {

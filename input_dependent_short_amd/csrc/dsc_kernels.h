@@ -109,6 +109,12 @@ hipError_t decode_step(const DecProblem &p, hipStream_t s);
 hipError_t state_from_prefill(Dtype dt, const void *x, const int32_t *cu, int32_t n_seqs, int64_t B, int64_t T,
                               int64_t D, int32_t W, void *state, hipStream_t s);
 
+// Streaming measurement kernel (stream.hip): reads read_bytes and writes
+// write_bytes in 16-byte units; blocks <= 0 takes one round of resident
+// workgroups.
+hipError_t stream_probe(const void *src, int64_t read_bytes, void *dst, int64_t write_bytes, int unroll, bool lnt,
+                        bool snt, bool chunked, int64_t blocks, hipStream_t s);
+
 // Zero-fills n fp32 values (16-byte aligned); the backward of an empty batch.
 hipError_t lowrank_zero(float *p, int64_t n, hipStream_t s);
 

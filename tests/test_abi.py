@@ -4,13 +4,14 @@ Every call below fails validation, which the library performs before any HIP
 call, so no GPU is touched.
 """
 import ctypes
+import glob
 import os
 import re
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "dsc.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 @pytest.fixture(scope="module")
@@ -22,8 +23,11 @@ def lib():
 
 
 def declared_symbols():
-    text = open(HEADER).read()
-    return re.findall(r"DSC_API\s+[\w\s\*]+?\b(dsc_\w+)\s*\(", text)
+    """Every DSC_API function declared by a header under include/."""
+    syms = []
+    for h in HEADERS:
+        syms += re.findall(r"DSC_API\s+[\w\s\*]+?\b(dsc_\w+)\s*\(", open(h).read())
+    return syms
 
 
 def test_header_declares_the_entry_points():
@@ -278,3 +282,13 @@ def test_static_deterministic_validation(lib):
     assert f(ws=G(1)) == 5                     # workspace aliases x
     assert f(dc=G(4)) == 5                     # dc aliases dx
     assert f(dx=None) == 1
+
+
+def test_bench_stream_validation(lib):
+    st = lambda src=P(1), rb=1 << 20, dst=P(9), wb=1 << 20, u=4, ln=0, sn=0, ch=0, bl=0: lib.dsc_bench_stream(
+        S0, src, rb, dst, wb, u, ln, sn, ch, bl)
+    assert st(rb=10) == 2 and st(wb=-16) == 2 and st(rb=1 << 40) == 2
+    assert st(u=3) == 2 and st(ln=2) == 2 and st(ch=5) == 2 and st(bl=-1) == 2
+    assert st(dst=None) == 1 and st(src=None) == 1
+    assert st(src=ctypes.c_void_p(A + 8)) == 4
+    assert st(dst=P(1)) == 5                      # dst overlaps src

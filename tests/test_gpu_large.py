@@ -5,7 +5,8 @@ the element index alone) and are drawn on the GPU; the oracle sees host
 windows of them (tests/large_util.py, checked on the CPU against whole
 tensors): token windows at the start, across the 2^31-byte and 2^32-byte
 offsets, across a sequence start and at the end, and channel slices for the
-sums over every token (dU, dc)."""
+sums over every token (dU, dc).  Every output starts as NaN and is checked
+on the device to have been written in full."""
 from __future__ import annotations
 
 import numpy as np
@@ -43,6 +44,14 @@ def _rows(t: torch.Tensor, lo: int, hi: int) -> np.ndarray:
     return to_f64(t.view(N, -1)[lo:hi])
 
 
+def _written(**outs) -> None:
+    """Every element of each full-size output was written (checked on the device)."""
+    for name, t in outs.items():
+        bad = int(torch.isnan(t).sum().item())
+        say(f"  {name}: all {t.numel()} elements written" if not bad else f"  {name}: {bad} unwritten")
+        assert bad == 0, f"{name}: {bad} elements not written"
+
+
 def _free():
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -74,6 +83,7 @@ def test_headwise_beyond_4gib(varlen):
     binding.dsc_headwise_fwd(x, w, y, cu_seqlens=cu, residual=True)
     binding.dsc_headwise_bwd(x, w, dy, dx, dw, cu_seqlens=cu, residual=True)
     torch.cuda.synchronize()
+    _written(y=y, dx=dx, dw=dw)
     tol = TOL[DT]
     for lo, hi in rows:
         say(f"  rows [{lo},{hi})")
@@ -102,6 +112,7 @@ def test_lowrank_beyond_4gib(varlen):
     binding.dsc_lowrank_fwd(x, z, U, y, W=W, cu_seqlens=cu)
     binding.dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, ws, W=W, cu_seqlens=cu)
     torch.cuda.synchronize()
+    _written(y=y, dx=dx, dz=dz, dU=dU)
     tol = TOL[DT]
     for lo, hi in rows:
         say(f"  rows [{lo},{hi})")
@@ -127,6 +138,7 @@ def test_static_beyond_4gib():
     binding.dsc_static_fwd(x, c, y, residual=True)
     binding.dsc_static_bwd(x, c, dy, dx, dc, residual=True)
     torch.cuda.synchronize()
+    _written(y=y, dx=dx, dc=dc)
     tol = TOL[DT]
     for lo, hi in ROWS:
         say(f"  rows [{lo},{hi})")
@@ -170,6 +182,7 @@ def test_decode_at_the_batch_limit(kind):
         U = _gpu(s["U"], 1.0 / np.sqrt(R * W), (R, D * W))
         binding.dsc_lowrank_decode(x, z, U, st, y, W=W)
     torch.cuda.synchronize()
+    _written(y=y)
     per = (W - 1) * D
     wins = [(0, 8), (2**30 // D - 4, 2**30 // D + 4), (2**31 // per - 4, 2**31 // per + 4),
             (2**32 // per - 4, 2**32 // per + 4), (Bd - 8, Bd)]

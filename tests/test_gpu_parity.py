@@ -1,9 +1,11 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
-Small shapes are compared element by element over every output; the five
-workloads run at full size and are compared on sampled token windows (all
-channels) and sampled channel ranges (dU, all tokens), plus full-size
-invariants (every element written, guard bands intact).  Tolerance: normwise
+Small shapes are compared element by element over every output, for every
+tap count W in 1..8 on each kernel family.  The five workloads run at full
+size and every element of every output is compared with the oracle (the
+sums over all tokens, dU, channel block by channel block); before that,
+every output element is checked to have been written (outputs start as NaN)
+and the guard bands around each output to be intact.  Tolerance: normwise
 max-relative error max|gpu - ref| / max|ref| <= 1e-5 (fp32) or 2e-2 (bf16
 inputs, fp32 accumulation).
 """
@@ -39,6 +41,10 @@ HW_CASES = [
     ("bf16", 1, 3, 40, 8, 8, True, None),
     ("bf16", 4, 65, 2304, 4, 64, True, None),
     ("bf16", 2, 300, 8192, 4, 16, True, (1, 120)),
+    # W = 6 on each filter span: one filter per lane group, per chunk, and 4 per chunk
+    ("bf16", 2, 90, 256, 6, 16, True, (1, 30)),
+    ("bf16", 1, 70, 64, 6, 2, False, None),
+    ("fp32", 1, 50, 64, 6, 4, False, (1, 12)),
 ]
 
 # (dtype, B, T, D, W, R, residual, segment-length range or None)
@@ -61,6 +67,19 @@ LR_CASES = [
     ("bf16", 1, 4100, 64, 3, 36, True, (1, 700)),
     # backward blocks of two token halves, several blocks, partial last half, R % 8 != 0
     ("bf16", 3, 1000, 128, 4, 20, True, (100, 900)),
+    # W = 5, 6, 7 on every kernel family: wide forward + matrix-core backward
+    # (R <= 32, whole and gathered z rows, packed sequences), wide forward +
+    # vector backward (33 <= R <= 64), 32-channel matrix-core forward (R > 64),
+    # and fp32
+    ("bf16", 1, 150, 96, 5, 32, True, None),
+    ("bf16", 2, 90, 64, 6, 12, False, (1, 40)),
+    ("bf16", 1, 200, 128, 7, 24, True, (1, 60)),
+    ("bf16", 1, 70, 64, 5, 40, True, None),
+    ("bf16", 1, 60, 32, 6, 64, False, (1, 20)),
+    ("bf16", 1, 45, 48, 7, 100, True, (1, 15)),
+    ("fp32", 1, 40, 16, 5, 4, True, None),
+    ("fp32", 2, 30, 8, 6, 2, False, (1, 9)),
+    ("fp32", 1, 25, 12, 7, 6, True, None),
 ]
 
 
@@ -150,22 +169,21 @@ def test_headwise_repeat_is_bitwise_identical():
 # ------------------------------------------------------------ full workloads
 
 
-def _windows(N: int, cu) -> list[tuple[int, int]]:
-    """Sampled token windows: start, middle, end, and around segment starts."""
-    wins = [(0, 24), (N // 2 - 7, N // 2 + 17), (N - 24, N)]
-    if cu is not None:
-        starts = [int(s) for s in cu[1:-1]]
-        for s in starts[:: max(1, len(starts) // 3)][:3]:
-            wins.append((max(0, s - 12), min(N, s + 12)))
-    return wins
+def _written(name: str, a: np.ndarray) -> None:
+    """Every element of a full-size output was written (outputs start as NaN)."""
+    bad = int(np.isnan(a).sum())
+    say(f"    {name:4s} all {a.size} elements written" if not bad else f"    {name}: {bad} unwritten")
+    assert bad == 0, f"{name}: {bad} elements not written"
 
 
-def _channels(D: int) -> list[tuple[int, int]]:
-    return [(0, 8), (D // 2 - 4, D // 2 + 4), (D - 8, D)]
+def _row_chunks(N: int, parts: int) -> list[tuple[int, int]]:
+    step = (N + parts - 1) // parts
+    return [(lo, min(N, lo + step)) for lo in range(0, N, step)]
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_workload_full_size(cfg):
+    """Every element of every output of the workload against the oracle."""
     wl = inputs.WORKLOADS[cfg]
     say(f"[workload {cfg}] {wl.name}: B={wl.B} T={wl.T} D={wl.D} W={wl.W} H={wl.H} R={wl.R} "
         f"{wl.dtype} residual={wl.residual} varlen={wl.varlen}")
@@ -176,35 +194,45 @@ def test_workload_full_size(cfg):
     x64, g64 = to_f64(inp["x"]), to_f64(inp["dy"])
     if wl.kind == "headwise":
         y, dx, dw = run_headwise(inp, wl.residual)
+        for name, a in (("y", y), ("dx", dx), ("dw", dw)):
+            _written(name, a)
         w64 = to_f64(inp["w"])
-        G = D // wl.H
-        y, dx, dw = y.reshape(N, D), dx.reshape(N, D), dw.reshape(N, G, wl.W)
-        for lo, hi in _windows(N, cu) if cfg != 1 else [(0, N)]:
-            say(f"  rows [{lo},{hi})")
-            ry = oracle.headwise_fwd(x64, w64, cu_seqlens=cu, residual=wl.residual, rows=(lo, hi))
-            rdx, rdw = oracle.headwise_bwd(x64, w64, g64, cu_seqlens=cu, residual=wl.residual, rows=(lo, hi))
-            assert_close("y", y[lo:hi], ry, tol)
-            assert_close("dx", dx[lo:hi], rdx, tol)
-            assert_close("dw", dw[lo:hi], rdw, tol)
+        say("  oracle: all rows")
+        ry = oracle.headwise_fwd(x64, w64, cu_seqlens=cu, residual=wl.residual)
+        assert_close("y", y, ry, tol)
+        del ry
+        rdx, rdw = oracle.headwise_bwd(x64, w64, g64, cu_seqlens=cu, residual=wl.residual)
+        assert_close("dx", dx, rdx, tol)
+        assert_close("dw", dw, rdw, tol)
     else:
         W, R = wl.W, wl.R
         y, dx, dz, dU = run_lowrank(inp, W, wl.residual)
+        for name, a in (("y", y), ("dx", dx), ("dz", dz), ("dU", dU)):
+            _written(name, a)
         z64, U64 = to_f64(inp["z"]), to_f64(inp["U"])
         y, dx, dz = y.reshape(N, D), dx.reshape(N, D), dz.reshape(N, R)
-        for lo, hi in _windows(N, cu):
-            say(f"  rows [{lo},{hi})")
-            ry = oracle.lowrank_fwd(x64, z64, U64, W, cu_seqlens=cu, residual=wl.residual, rows=(lo, hi))
-            rdx, rdz, _ = oracle.lowrank_bwd(x64, z64, U64, g64, W, cu_seqlens=cu, residual=wl.residual,
-                                             rows=(lo, hi), channels=(0, 0))
-            assert_close("y", y[lo:hi], ry, tol)
-            assert_close("dx", dx[lo:hi], rdx, tol)
-            assert_close("dz", dz[lo:hi], rdz, tol)
-        dU3 = dU.reshape(R, D, W)
-        for c0, c1 in _channels(D):
-            say(f"  dU channels [{c0},{c1})")
-            _, _, rdU = oracle.lowrank_bwd(x64, z64, U64, g64, W, cu_seqlens=cu, residual=wl.residual,
-                                           rows=(0, 0), channels=(c0, c1))
-            assert_close("dU", dU3[:, c0:c1].reshape(R, (c1 - c0) * W), rdU, tol)
+        say("  oracle: all rows")
+        ry = oracle.lowrank_fwd(x64, z64, U64, W, cu_seqlens=cu, residual=wl.residual).reshape(N, D)
+        assert_close("y", y, ry, tol)
+        del ry
+        # the backward in row blocks (each compared against the whole
+        # tensor's scale), dU in channel blocks: every element in the end
+        rdx = np.empty((N, D))
+        rdz = np.empty((N, R))
+        for lo, hi in _row_chunks(N, 4):
+            say(f"  oracle: dx, dz rows [{lo},{hi})")
+            rdx[lo:hi], rdz[lo:hi], _ = oracle.lowrank_bwd(x64, z64, U64, g64, W, cu_seqlens=cu,
+                                                           residual=wl.residual, rows=(lo, hi), channels=(0, 0))
+        assert_close("dx", dx, rdx, tol)
+        assert_close("dz", dz, rdz, tol)
+        del rdx, rdz
+        rdU = np.empty((R, D, W))
+        for c0, c1 in _row_chunks(D, 4):
+            say(f"  oracle: dU channels [{c0},{c1})")
+            _, _, part = oracle.lowrank_bwd(x64, z64, U64, g64, W, cu_seqlens=cu, residual=wl.residual,
+                                            rows=(0, 0), channels=(c0, c1))
+            rdU[:, c0:c1] = part.reshape(R, c1 - c0, W)
+        assert_close("dU", dU.reshape(R, D, W), rdU, tol)
 
 
 def test_stream_argument_is_honoured():
