@@ -210,29 +210,27 @@ def cpu_baseline(wls, seconds: float):
 COPY_BYTES = 1 << 30  # bytes read (and written) by the copy-kernel reference
 
 
-def copy_rate(torch, nbytes: int, reps: int = 20) -> float:
-    """GB/s of one device copy that moves `nbytes` in all (half read, half
-    written), timed per launch like the entry points: the streaming rate a
-    single kernel of that size reaches, ramp and tail included.  A 512 MiB
-    write before every copy evicts the source from the 256 MB last-level
-    cache, which would otherwise serve a copy this small."""
+def copy_rate(torch, nbytes: int, flush, reps: int = 20) -> float:
+    """GB/s of one device copy (the runtime's) that moves `nbytes` in all
+    (half read, half written), timed per launch like the entry points: the
+    streaming rate a single kernel of that size reaches, ramp and tail
+    included, each copy after a cache flush."""
     half = nbytes // 2
     src = torch.empty(half, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in evs:
-        flush.fill_(1)
+        flush()
         a.record()
         dst.copy_(src)
         b.record()
     torch.cuda.synchronize()
     ts = sorted(a.elapsed_time(b) for a, b in evs)
     t = ts[len(ts) // 2] * 1e-3
-    del src, dst, flush
+    del src, dst
     torch.cuda.empty_cache()
     return 2 * half / t / 1e9
 
@@ -331,16 +329,33 @@ def log(msg: str) -> None:
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
+class Flush:
+    """Evicts the caches before a timed call: the library's streaming kernel
+    reads a 1 GiB buffer with the default cache policy, which replaces the
+    256 MB last-level cache and the 4 MB L2 of each XCD with clean lines (a
+    write would leave dirty lines whose write-back then runs during the timed
+    call)."""
+
+    def __init__(self, torch, binding, nbytes=1 << 30):
+        self.buf = torch.full((nbytes,), 1, dtype=torch.uint8, device="cuda")
+        self.sink = torch.empty(16, dtype=torch.uint8, device="cuda")
+        self.binding = binding
+        self.n = nbytes
+
+    def __call__(self):
+        self.binding.dsc_bench_stream(self.buf, self.n, self.sink, 0, unroll=8)
+
+
 def timed_calls(torch, calls, iters, flush):
     """Each call of `calls` (name -> fn) timed `iters` times with HIP events on
-    the current stream, each after a write of the flush buffer; returns
-    name -> sorted list of milliseconds."""
+    the current stream, each after a cache flush; returns name -> sorted list
+    of milliseconds."""
     evs = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(iters)] for k in calls}
     torch.cuda.synchronize()
     for it in range(iters):
         for k, fn in calls.items():
-            flush.fill_(it & 0xff)
+            flush()
             a, b = evs[k][it]
             a.record()
             fn()
@@ -398,8 +413,9 @@ def stream_ceiling(torch, binding, mixes, reps, flush):
     src = torch.empty(top, dtype=torch.uint8, device="cuda")
     dst = torch.empty(top, dtype=torch.uint8, device="cuda")
     src.fill_(3)
-    recipes = [dict(unroll=u, load_nt=nt, store_nt=nt, chunked=ch) for u in (4, 8) for nt in (False, True)
-               for ch in (False, True)]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    recipes = [dict(unroll=u, load_nt=nt, store_nt=nt, chunked=ch, blocks=bl) for u in (1, 4, 8)
+               for nt in (False, True) for ch in (False, True) for bl in (0, 4 * cus)]
     out = {}
     for name, (rb, wb) in mixes.items():
         best = None
@@ -429,7 +445,7 @@ def stream_sweep(torch, binding, inputs) -> int:
     mixes = {"copy_activation": (act, act), "copy_1GiB": (1 << 30, 1 << 30),
              "headwise_fwd_mix": (act + filt, act), "headwise_bwd_mix": (2 * act + filt, act + filt),
              "read_only": (3 * act + filt, 0), "write_only": (0, act + filt)}
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = Flush(torch, binding)
     top = max(max(r, w) for r, w in mixes.values())
     src = torch.full((top,), 3, dtype=torch.uint8, device="cuda")
     dst = torch.empty(top, dtype=torch.uint8, device="cuda")
@@ -495,9 +511,9 @@ def main() -> int:
     iters = max(50, args.iters)
     if args.stream_sweep:
         return stream_sweep(torch, binding, inputs)
-    # a 512 MiB write before every timed call evicts the inputs from the
+    # a 1 GiB read before every timed call evicts the inputs from the
     # 256 MB last-level cache and the 4 MB L2 of each XCD
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = Flush(torch, binding)
 
     log("copy reference")
     copy_gbps = copy_ceiling(torch)
@@ -567,7 +583,7 @@ def main() -> int:
                              c4.x.numel() * 2 + c4.w.numel() * 2),
         "read_only": (c4.bytes("bwd"), 0),
         "write_only": (0, c4.x.numel() * 2)}, 10, flush)
-    out["copy_same_bytes_GBps"] = round(copy_rate(torch, dom["algorithmic_bytes"]), 1)
+    out["copy_same_bytes_GBps"] = round(copy_rate(torch, dom["algorithmic_bytes"], flush), 1)
     del cases, c4
     torch.cuda.empty_cache()
 

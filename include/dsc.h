@@ -96,10 +96,13 @@ typedef enum dsc_status {
  *
  *   x  (B,T,D) dtype, in.      w  (B,T,D/H,W) dtype, in (tap innermost).
  *   y  (B,T,D) dtype, out.
- *   H  channels per shared filter: 1 <= H, D % H == 0.  This build supports
- *      H that divides 8 (bf16) / 4 (fp32), or H = 8*2^i (bf16) / 4*2^i (fp32)
- *      with H <= 64*8 (bf16) / 64*4 (fp32); other H return
- *      DSC_ERR_UNSUPPORTED.
+ *   H  channels per shared filter: any H >= 1 with D % H == 0 (the
+ *      pages' "H consecutive channels" has no other restriction).  Groups
+ *      that a 16-byte channel vector (8 bf16 / 4 fp32) holds whole, or that
+ *      cover at most 64 whole vectors, run the streaming kernels; every other
+ *      H (e.g. 3, 5, 6, 12, or H > 512 in bf16) runs kernels that read each
+ *      channel's filter by its group index, with the backward in two passes
+ *      (same results, slower).
  *   D  multiple of 8 (bf16) or 4 (fp32).
  */
 DSC_API dsc_status dsc_headwise_fwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
@@ -324,9 +327,8 @@ DSC_API dsc_status dsc_static_bwd_deterministic(void *stream, int dtype, int64_t
  *   No argument may overlap another (state is not an alias of x or y).
  */
 
-/* Head-wise decoding step: w (B, D/H, W), w(b)_{d,k} = w[b, d/H, k].
- * H divides 8 (bf16) / 4 (fp32) or is a multiple of it; others return
- * DSC_ERR_UNSUPPORTED. */
+/* Head-wise decoding step: w (B, D/H, W), w(b)_{d,k} = w[b, d/H, k], any H
+ * with D % H == 0. */
 DSC_API dsc_status dsc_headwise_decode(void *stream, int dtype, int64_t B, int64_t D, int32_t W, int32_t H,
                                const void *x, const void *w, void *state, int32_t residual, void *y);
 

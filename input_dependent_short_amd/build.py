@@ -46,13 +46,14 @@ def _run(cmd: list[str], verbose: bool) -> None:
         raise RuntimeError(f"hipcc failed with code {res.returncode}: {' '.join(cmd)}")
 
 
-def build(out: str = LIB, verbose: bool = False, extra: list[str] | None = None) -> str:
-    """Compile every HIP source (in parallel) and link libdsc.so."""
+def build(out: str = LIB, verbose: bool = False, extra: list[str] | None = None, objdir: str | None = None) -> str:
+    """Compile every HIP source (in parallel) and link libdsc.so (extra flags
+    and a separate object folder build variants of the library)."""
     from concurrent.futures import ThreadPoolExecutor
 
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     inc = f"-I{os.path.join(ROOT, 'include')}"
-    objdir = os.path.join(PKG, "_build")
+    objdir = objdir or os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
     compile_flags = [f for f in FLAGS if f != "-shared"]
     jobs = []

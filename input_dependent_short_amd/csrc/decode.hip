@@ -82,11 +82,12 @@ __device__ __forceinline__ void finish(const float (&xv)[E::kVec], const float (
 // ROPE: y of the first rot channels is then rotated at position pos[b]
 // (a table row read once); a position outside [0, npos) has no row, and the
 // sequence's rotated channels are set to NaN instead.
+// GPT = 0 serves any H: each channel reads the filter of its own group d/H.
 template <class E, int W, int GPT, bool ROPE>
 __global__ __launch_bounds__(kBlock) void hw_decode_kernel(DecParams p) {
     using S = typename E::store_t;
     constexpr int VEC = E::kVec;
-    constexpr int NW = GPT * W;
+    constexpr int NW = (GPT > 0 ? GPT : 1) * W;
     constexpr int WALIGN = pow2_align(NW * (int)sizeof(S));
     // 32-bit index arithmetic: the API limits a decoding batch to B*D < 2^31
     const uint32_t B = (uint32_t)p.B;
@@ -97,14 +98,25 @@ __global__ __launch_bounds__(kBlock) void hw_decode_kernel(DecParams p) {
     const int64_t d0 = (int64_t)chunk * VEC;
     const int64_t jfirst = GPT > 1 ? (int64_t)chunk * GPT : d0 / p.H;
 
-    float xv[VEC], wf[NW];
+    float xv[VEC];
     Vec16<E>::load(static_cast<const S *>(p.x) + b * p.D + d0, xv);
-    Span<E, NW>::template load<WALIGN>(static_cast<const S *>(p.w) + (b * p.G + jfirst) * W, wf);
     float wt[VEC][W];
+    if constexpr (GPT == 0) {
 #pragma unroll
-    for (int c = 0; c < VEC; ++c)
+        for (int c = 0; c < VEC; ++c) {
+            float wf[W];
+            Span<E, W>::template load<WALIGN>(static_cast<const S *>(p.w) + (b * p.G + (d0 + c) / p.H) * W, wf);
 #pragma unroll
-        for (int k = 0; k < W; ++k) wt[c][k] = wf[grp<VEC, GPT>(c) * W + k] + (k == 0 ? p.rho : 0.f);
+            for (int k = 0; k < W; ++k) wt[c][k] = wf[k] + (k == 0 ? p.rho : 0.f);
+        }
+    } else {
+        float wf[NW];
+        Span<E, NW>::template load<WALIGN>(static_cast<const S *>(p.w) + (b * p.G + jfirst) * W, wf);
+#pragma unroll
+        for (int c = 0; c < VEC; ++c)
+#pragma unroll
+            for (int k = 0; k < W; ++k) wt[c][k] = wf[grp<VEC, GPT>(c) * W + k] + (k == 0 ? p.rho : 0.f);
+    }
     S *st = W > 1 ? static_cast<S *>(p.state) + b * (W - 1) * p.D + d0 : nullptr;  // no state when W = 1
     float cs[VEC];
     const bool rotated = ROPE && d0 < p.rot;
@@ -253,7 +265,9 @@ int64_t grid(int64_t items) { return (items + kBlock - 1) / kBlock; }
 template <class E, int W, bool ROPE>
 hipError_t launch_hw(const DecParams &p, int32_t H, int64_t blocks, hipStream_t st) {
     constexpr int VEC = E::kVec;
-    if (H >= VEC) {
+    if (H >= VEC ? H % VEC != 0 : VEC % H != 0) {  // groups that do not align with 16-byte chunks
+        hipLaunchKernelGGL((hw_decode_kernel<E, W, 0, ROPE>), dim3((unsigned)blocks), dim3(kBlock), 0, st, p);
+    } else if (H >= VEC) {
         hipLaunchKernelGGL((hw_decode_kernel<E, W, 1, ROPE>), dim3((unsigned)blocks), dim3(kBlock), 0, st, p);
     } else {
         switch (VEC / H) {

@@ -94,7 +94,6 @@ dsc_status dsc_headwise_fwd(void *stream, int dtype, int64_t B, int64_t T, int64
     DSC_TRY(check_common(dtype, B, T, D, W, cu_seqlens, n_seqs, residual));
     if (H < 1 || D % H) return fail(DSC_ERR_SHAPE, "H = %d must divide D = %lld", H, (long long)D);
     const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
-    if (!dsc::headwise_supported(dt, D, H)) return fail(DSC_ERR_UNSUPPORTED, "H = %d not supported", H);
     if (B * T == 0) return ok();  // empty batch: nothing to compute
     if (!x || !w || !y) return fail(DSC_ERR_NULL, "x, w and y are required");
     if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
@@ -114,7 +113,6 @@ dsc_status dsc_headwise_bwd(void *stream, int dtype, int64_t B, int64_t T, int64
     DSC_TRY(check_common(dtype, B, T, D, W, cu_seqlens, n_seqs, residual));
     if (H < 1 || D % H) return fail(DSC_ERR_SHAPE, "H = %d must divide D = %lld", H, (long long)D);
     const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
-    if (!dsc::headwise_supported(dt, D, H)) return fail(DSC_ERR_UNSUPPORTED, "H = %d not supported", H);
     if (B * T == 0) return ok();  // empty batch: dx and dw have no elements
     if (!x || !w || !dy || !dx || !dw) return fail(DSC_ERR_NULL, "x, w, dy, dx and dw are required");
     if (!aligned16(x) || !aligned16(w) || !aligned16(dy) || !aligned16(dx) || !aligned16(dw))
@@ -175,7 +173,6 @@ dsc_status dsc_headwise_rope_fwd(void *stream, int dtype, int64_t B, int64_t T, 
     DSC_TRY(check_common(dtype, B, T, D, W, cu_seqlens, n_seqs, residual));
     if (H < 1 || D % H) return fail(DSC_ERR_SHAPE, "H = %d must divide D = %lld", H, (long long)D);
     const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
-    if (!dsc::headwise_supported(dt, D, H)) return fail(DSC_ERR_UNSUPPORTED, "H = %d not supported", H);
     DSC_TRY(check_rope(dtype, B, T, D, cu_seqlens, rot, head_dim, table, max_pos));
     if (B * T == 0) return ok();
     if (!x || !w || !y) return fail(DSC_ERR_NULL, "x, w and y are required");
@@ -199,7 +196,6 @@ dsc_status dsc_headwise_rope_bwd(void *stream, int dtype, int64_t B, int64_t T, 
     DSC_TRY(check_common(dtype, B, T, D, W, cu_seqlens, n_seqs, residual));
     if (H < 1 || D % H) return fail(DSC_ERR_SHAPE, "H = %d must divide D = %lld", H, (long long)D);
     const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
-    if (!dsc::headwise_supported(dt, D, H)) return fail(DSC_ERR_UNSUPPORTED, "H = %d not supported", H);
     DSC_TRY(check_rope(dtype, B, T, D, cu_seqlens, rot, head_dim, table, max_pos));
     if (B * T == 0) return ok();
     if (!x || !w || !dy || !dx || !dw) return fail(DSC_ERR_NULL, "x, w, dy, dx and dw are required");
@@ -276,7 +272,8 @@ dsc_status lowrank_bwd_call(bool det, const char *name, void *stream, int dtype,
                         rng("dy", dy, N * D * es),
                         rng("cu_seqlens", cu_seqlens, cu_seqlens ? 4u * (n_seqs + 1) : 0)};
     const Range out[] = {rng("dx", dx, N * D * es), rng("dz", dz, N * R * es),
-                         rng("dU", dU, (size_t)R * D * W * 4), rng("workspace", workspace, need ? need : 0)};
+                         rng("dU", dU, (size_t)R * D * W * 4),
+                         rng("workspace", workspace, need ? need : 0)};
     DSC_TRY(check_alias(in, 5, out, 4));
     float *acc = need ? static_cast<float *>(workspace) : det ? nullptr : static_cast<float *>(dz);
     dsc::LrProblem p{dt, B * T, T, D, W, R, x, z, U, dy, nullptr, dx, dz, dU, acc, cu_seqlens, n_seqs, residual};
@@ -411,7 +408,6 @@ dsc_status headwise_decode_call(void *stream, int dtype, int64_t B, int64_t D, i
     DSC_TRY(check_decode(dtype, B, D, W, residual));
     if (H < 1 || D % H) return fail(DSC_ERR_SHAPE, "H = %d must divide D = %lld", H, (long long)D);
     const int vec = dtype == DSC_BF16 ? 8 : 4;
-    if (H < vec ? vec % H != 0 : H % vec != 0) return fail(DSC_ERR_UNSUPPORTED, "H = %d not supported", H);
     if (rot != 0 || head_dim != 0) {
         if (head_dim < 2 || head_dim % 2 || head_dim > (1 << 16))
             return fail(DSC_ERR_SHAPE, "head_dim = %d must be even, in 2..65536", head_dim);

@@ -74,8 +74,11 @@ struct DecProblem {
     const int32_t *pos;
 };
 
-// Head-wise: whether this build has a kernel for (dtype, H).
-bool headwise_supported(Dtype dt, int64_t D, int32_t H);
+// Head-wise: whether the kernels of headwise_impl.h serve (dtype, H); every
+// other H with D % H == 0 runs the kernels of headwise_any.hip.
+bool headwise_fast(Dtype dt, int32_t H);
+// The layer (rope false) or the layer with the rotary embedding for any H.
+hipError_t headwise_any(const HwProblem &p, hipStream_t s, bool bwd, bool rope);
 
 hipError_t headwise_fwd(const HwProblem &p, hipStream_t s);
 hipError_t headwise_bwd(const HwProblem &p, hipStream_t s);

@@ -8,19 +8,22 @@
 
 namespace dsc {
 
-bool headwise_supported(Dtype dt, int64_t D, int32_t H) {
+// A chunk holds whole groups (H divides VEC), or a group spans H / VEC
+// chunks on at most 64 lanes (rounded up to a power of two in the backward).
+bool headwise_fast(Dtype dt, int32_t H) {
     const int VEC = dt == Dtype::BF16 ? BF16::kVec : F32::kVec;
-    if (H < 1 || D % H) return false;
+    if (H < 1) return false;
     if (H < VEC) return VEC % H == 0;
-    const int lanes = H / VEC;
-    return H % VEC == 0 && (lanes & (lanes - 1)) == 0 && lanes <= kWave;
+    return H % VEC == 0 && H / VEC <= kWave;
 }
 
 hipError_t headwise_fwd(const HwProblem &p, hipStream_t s) {
+    if (!headwise_fast(p.dtype, p.H)) return headwise_any(p, s, false, false);
     return p.dtype == Dtype::BF16 ? dispatch<BF16, false>(p, s, false) : dispatch<F32, false>(p, s, false);
 }
 
 hipError_t headwise_bwd(const HwProblem &p, hipStream_t s) {
+    if (!headwise_fast(p.dtype, p.H)) return headwise_any(p, s, true, false);
     return p.dtype == Dtype::BF16 ? dispatch<BF16, false>(p, s, true) : dispatch<F32, false>(p, s, true);
 }
 

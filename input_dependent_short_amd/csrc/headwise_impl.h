@@ -56,9 +56,14 @@ struct HwParams {
     SeqMap seq;
     int64_t N, D, G;
     int32_t H;
-    int32_t lanes;  // lanes sharing one filter group (H / VEC when H >= VEC)
+    // Backward lane groups: a filter group of H >= VEC channels spans L =
+    // H / VEC chunks and takes `lanes` (L rounded up to a power of two)
+    // consecutive lanes, of which the first L are active; with H < VEC a
+    // chunk holds whole groups and L = lanes = 1.
+    int32_t lanes, L;
     float rho;
     int64_t nchunks, items;
+    int64_t slots;  // backward lanes per token tile: (nchunks / L) * lanes
     const float *rope;  // (npos, hd/2, 2) cos, sin; read only by the ROPE kernels
     int32_t rot, hd;    // rotated channels [0, rot), head size
     int32_t npos;       // table rows
@@ -72,10 +77,18 @@ __device__ __forceinline__ constexpr int grp(int c) {
     return GPT > 1 ? c / (VEC / GPT) : 0;
 }
 
+// Cache policy of the streams each thread reads or writes once (x, w and
+// dy rows of its own tile; y, dx and dw): nontemporal.  The halo rows before
+// a tile, which the neighbouring tile also reads, keep the default policy.
+#ifndef DSC_HW_NT
+#define DSC_HW_NT 1
+#endif
+constexpr bool kNT = DSC_HW_NT != 0;
+
 // Raw 16-byte vector of activations, widened to fp32 when used.
-template <class E>
+template <class E, bool NT = false>
 __device__ __forceinline__ uint4 load_raw(const typename E::store_t *p) {
-    return *reinterpret_cast<const uint4 *>(p);
+    return ld_u4<NT>(p);
 }
 
 template <class E>
@@ -200,8 +213,8 @@ __global__ __launch_bounds__(kBlock) void hw_fwd_kernel(HwParams p) {
         for (int u = 0; u < U; ++u) {
             const int64_t n = nb + u;
             if (n < n1) {
-                xr[u] = load_raw<E>(x + n * p.D);
-                WS::template load<WALIGN>(w + n * p.G * W, wr[u]);
+                xr[u] = load_raw<E, kNT>(x + n * p.D);
+                WS::template load<WALIGN, kNT>(w + n * p.G * W, wr[u]);
             }
         }
     };
@@ -256,7 +269,7 @@ __global__ __launch_bounds__(kBlock) void hw_fwd_kernel(HwParams p) {
                         turn<VEC, false>(acc, cs[u]);
                     }
                 }
-                Vec16<E>::store(y + n * p.D, acc);
+                Vec16<E>::template store<kNT>(y + n * p.D, acc);
 #pragma unroll
                 for (int i = W - 2; i > 0; --i)
 #pragma unroll
@@ -289,16 +302,22 @@ __global__ __launch_bounds__(kBlock) void hw_bwd_kernel(HwParams p) {
 
     const int64_t item = xcd_block_id(blockIdx.x, gridDim.x) * kBlock + threadIdx.x;
     // Whole filter groups are active or inactive together (items is a
-    // multiple of nchunks, which is a multiple of lanes), so exiting here never
+    // multiple of slots, which is a multiple of lanes), so exiting here never
     // strands a lane that a group reduction reads.
     if (item >= p.items) return;
-    const int64_t tile = item / p.nchunks;
-    const int64_t chunk = item - tile * p.nchunks;
+    const int64_t tile = item / p.slots;
+    const int64_t slot = item - tile * p.slots;
+    // lane li of filter group gi; padding lanes (li >= L) repeat the group's
+    // last chunk, store nothing and add zeros to the group sum
+    const int64_t gi = slot / p.lanes;
+    const int li = (int)(slot - gi * p.lanes);
+    const bool active = li < p.L;
+    const int64_t chunk = gi * p.L + (active ? li : p.L - 1);
     const int64_t n0 = tile * TT;
     const int64_t n1 = min(n0 + (int64_t)TT, p.N);
     const int64_t d0 = chunk * VEC;
     const int64_t jfirst = GPT > 1 ? chunk * GPT : d0 / p.H;
-    const bool leader = (chunk & (p.lanes - 1)) == 0;
+    const bool leader = li == 0;
 
     const S *x = static_cast<const S *>(p.x) + d0;
     const S *g = static_cast<const S *>(p.dy) + d0;
@@ -338,8 +357,8 @@ __global__ __launch_bounds__(kBlock) void hw_bwd_kernel(HwParams p) {
     uint32_t ww[WIN][NWW];
     auto load_gw = [&](int64_t t, int slot) {
         if (t < p.N) {
-            gw[slot] = load_raw<E>(g + t * p.D);
-            WS::template load<WALIGN>(w + t * p.G * W, ww[slot]);
+            gw[slot] = load_raw<E, kNT>(g + t * p.D);
+            WS::template load<WALIGN, kNT>(w + t * p.G * W, ww[slot]);
         } else {
             gw[slot] = zero4;
 #pragma unroll
@@ -397,7 +416,7 @@ __global__ __launch_bounds__(kBlock) void hw_bwd_kernel(HwParams p) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t m = mb + u;
-            xv[u] = m < n1 ? load_raw<E>(x + m * p.D) : zero4;
+            xv[u] = m < n1 ? load_raw<E, kNT>(x + m * p.D) : zero4;
             load_gw(mb + W - 1 + u, W - 1 + u);
             if constexpr (ROPE) later |= (uint32_t)load_cs(mb + W - 1 + u, cs[u]) << u;
         }
@@ -430,7 +449,7 @@ __global__ __launch_bounds__(kBlock) void hw_bwd_kernel(HwParams p) {
                         acc[c] = __builtin_fmaf(wk, gk, acc[c]);
                     }
                 }
-                Vec16<E>::store(dx + m * p.D, acc);
+                if (active) Vec16<E>::template store<kNT>(dx + m * p.D, acc);
 
                 float part[NW];
 #pragma unroll
@@ -458,13 +477,17 @@ __global__ __launch_bounds__(kBlock) void hw_bwd_kernel(HwParams p) {
                                 __builtin_fmaf(gm[c], lane_elem<E>(xr, c), part[grp<VEC, GPT>(c) * W + k]);
                     }
                 }
+                if (!active) {
+#pragma unroll
+                    for (int i = 0; i < NW; ++i) part[i] = 0.f;
+                }
                 group_sum<NW>(part, p.lanes);
 #pragma unroll
                 for (int q = 0; q < GPT; ++q)
 #pragma unroll
                     for (int k = 0; k < W; ++k)
                         if (k > back) part[q * W + k] = 0.f;
-                if (leader) Span<E, NW>::template store<WALIGN>(dw + m * p.G * W, part);
+                if (leader) Span<E, NW>::template store<WALIGN, kNT>(dw + m * p.G * W, part);
 
 #pragma unroll
                 for (int i = W - 2; i > 0; --i) ring[i] = ring[i - 1];
@@ -496,22 +519,25 @@ constexpr int kTT = DSC_HW_TT;  // tokens per thread tile
 constexpr int kU = DSC_HW_U;    // tokens per load batch
 
 template <class E>
-HwParams make_params(const HwProblem &pr, int64_t tt, int64_t &blocks) {
+HwParams make_params(const HwProblem &pr, int64_t tt, bool bwd, int64_t &blocks) {
     HwParams p;
     p.x = pr.x; p.w = pr.w; p.dy = pr.dy;
     p.y = pr.y; p.dx = pr.dx; p.dw = pr.dw;
     p.seq = SeqMap{pr.cu, pr.n_seqs, pr.T};
     p.N = pr.N; p.D = pr.D; p.G = pr.D / pr.H;
     p.H = pr.H;
-    p.lanes = pr.H >= E::kVec ? pr.H / E::kVec : 1;
+    p.L = pr.H >= E::kVec ? pr.H / E::kVec : 1;
+    p.lanes = 1;
+    while (p.lanes < p.L) p.lanes *= 2;
     p.rho = pr.residual ? 1.f : 0.f;
     p.nchunks = pr.D / E::kVec;
+    p.slots = p.nchunks / p.L * p.lanes;
     p.rope = pr.rope;
     p.rot = (int32_t)pr.rot;
     p.hd = pr.hd;
     p.npos = (int32_t)pr.max_pos;
     const int64_t ntiles = (pr.N + tt - 1) / tt;
-    p.items = ntiles * p.nchunks;
+    p.items = ntiles * (bwd ? p.slots : p.nchunks);
     blocks = (p.items + kBlock - 1) / kBlock;
     return p;
 }
@@ -526,21 +552,21 @@ hipError_t launch_w(const HwProblem &pr, hipStream_t st, bool bwd) {
     if (bwd) {
         static const int bpc = blocks_per_cu(
             reinterpret_cast<const void *>(&hw_bwd_kernel<E, W, GPT, 2 * kTT, UB, ROPE>), kBlock);
-        const int64_t waves_long = ((pr.N + 2 * kTT - 1) / (2 * kTT)) * (pr.D / E::kVec) / kWave;
+        HwParams p = make_params<E>(pr, 2 * kTT, true, blocks);
+        const int64_t waves_long = p.items / kWave;
         if (waves_long >= (int64_t)device_cus() * bpc * (kBlock / kWave)) {
-            HwParams p = make_params<E>(pr, 2 * kTT, blocks);
             if (blocks)
                 hipLaunchKernelGGL((hw_bwd_kernel<E, W, GPT, 2 * kTT, UB, ROPE>), dim3((unsigned)blocks),
                                    dim3(kBlock), 0, st, p);
             return hipGetLastError();
         }
-        HwParams p = make_params<E>(pr, kTT, blocks);
+        p = make_params<E>(pr, kTT, true, blocks);
         if (blocks)
             hipLaunchKernelGGL((hw_bwd_kernel<E, W, GPT, kTT, UB, ROPE>), dim3((unsigned)blocks), dim3(kBlock), 0,
                                st, p);
         return hipGetLastError();
     }
-    HwParams p = make_params<E>(pr, kTT, blocks);
+    HwParams p = make_params<E>(pr, kTT, false, blocks);
     if (blocks)
         hipLaunchKernelGGL((hw_fwd_kernel<E, W, GPT, kTT, kU, ROPE>), dim3((unsigned)blocks), dim3(kBlock), 0, st, p);
     return hipGetLastError();

@@ -31,10 +31,12 @@ __global__ __launch_bounds__(256) void rope_table_kernel(float2 *table, int64_t 
 }  // namespace
 
 hipError_t headwise_rope_fwd(const HwProblem &p, hipStream_t s) {
+    if (!headwise_fast(p.dtype, p.H)) return headwise_any(p, s, false, true);
     return p.dtype == Dtype::BF16 ? dispatch<BF16, true>(p, s, false) : dispatch<F32, true>(p, s, false);
 }
 
 hipError_t headwise_rope_bwd(const HwProblem &p, hipStream_t s) {
+    if (!headwise_fast(p.dtype, p.H)) return headwise_any(p, s, true, true);
     return p.dtype == Dtype::BF16 ? dispatch<BF16, true>(p, s, true) : dispatch<F32, true>(p, s, true);
 }
 

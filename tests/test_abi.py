@@ -63,7 +63,8 @@ def test_headwise_fwd_validation(lib):
     assert hw_fwd(lib, W=0) == 2 and hw_fwd(lib, W=9) == 2
     assert hw_fwd(lib, D=60) == 2                 # bf16 needs D % 8 == 0
     assert hw_fwd(lib, H=7) == 2                  # H must divide D
-    assert hw_fwd(lib, D=48, H=24) == 3           # 3 lanes per group: not built
+    assert hw_fwd(lib, D=48, H=24, y=P(1)) == 5   # any H dividing D passes the shape checks
+    assert hw_fwd(lib, D=48, H=3, y=P(1)) == 5 and hw_fwd(lib, D=48, H=48, y=P(1)) == 5
     assert hw_fwd(lib, dtype=7) == 3
     assert hw_fwd(lib, B=-1) == 2 and hw_fwd(lib, T=-3) == 2 and hw_fwd(lib, D=0) == 2
     assert hw_fwd(lib, H=7, B=0) == 2             # shapes are checked for an empty batch too
@@ -173,7 +174,7 @@ def test_decode_validation(lib):
     ld = lambda dt=1, B=4, D=64, W=4, R=16, x=P(1), z=P(2), U=P(3), st=P(4), res=0, y=P(5): \
         lib.dsc_lowrank_decode(S0, dt, B, D, W, R, x, z, U, st, res, y)
     assert hd(W=0) == 2 and hd(W=9) == 2 and hd(D=60) == 2 and hd(H=3) == 2
-    assert hd(H=12, D=96) == 3                      # a chunk of 8 channels would span two filters
+    assert hd(H=12, D=96, y=P(1)) == 5              # groups across 16-byte chunks pass the shape checks
     assert hd(st=None) == 1
     assert hd(st=P(1)) == 5                         # state overlaps x
     assert hd(y=P(3)) == 5                          # y overlaps the state

@@ -29,7 +29,10 @@ def _tensor(a: np.ndarray, dt: str) -> torch.Tensor:
 
 # (dtype, B sequences, D, W, H)
 HW_DEC = [("bf16", 1, 64, 4, 64), ("bf16", 7, 2304, 4, 64), ("bf16", 33, 256, 3, 2), ("bf16", 5, 128, 8, 16),
-          ("bf16", 3, 64, 1, 8), ("fp32", 4, 96, 4, 1), ("fp32", 2, 32, 6, 8)]
+          ("bf16", 3, 64, 1, 8), ("fp32", 4, 96, 4, 1), ("fp32", 2, 32, 6, 8),
+          # any H with D % H == 0, groups across 16-byte chunks or of several chunks
+          ("bf16", 6, 96, 4, 3), ("bf16", 3, 96, 4, 6), ("bf16", 4, 192, 4, 24), ("bf16", 2, 480, 3, 48),
+          ("bf16", 5, 768, 4, 96), ("fp32", 3, 60, 5, 3)]
 
 
 @pytest.mark.parametrize("case", HW_DEC, ids=[f"hw-{c[0]}-B{c[1]}D{c[2]}W{c[3]}H{c[4]}" for c in HW_DEC])

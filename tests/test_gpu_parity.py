@@ -45,6 +45,22 @@ HW_CASES = [
     ("bf16", 2, 90, 256, 6, 16, True, (1, 30)),
     ("bf16", 1, 70, 64, 6, 2, False, None),
     ("fp32", 1, 50, 64, 6, 4, False, (1, 12)),
+    # any H with D % H == 0: groups of 3, 5, 6 and 12 channels across the
+    # 16-byte chunks, and groups wider than 64 chunks (per-channel group
+    # index); groups of 3, 5, 6 and 12 chunks (lane groups padded to a power
+    # of two in the backward)
+    ("bf16", 2, 90, 48, 4, 3, True, (1, 30)),
+    ("bf16", 1, 50, 40, 8, 5, False, (1, 12)),
+    ("bf16", 1, 70, 96, 4, 6, False, None),
+    ("bf16", 1, 30, 96, 4, 12, True, None),
+    ("bf16", 1, 20, 2048, 4, 1024, True, (1, 9)),
+    ("bf16", 2, 100, 192, 4, 24, True, (1, 40)),
+    ("bf16", 1, 40, 1200, 5, 40, True, None),
+    ("bf16", 1, 80, 480, 3, 48, True, None),
+    ("bf16", 2, 64, 768, 4, 96, False, (1, 50)),
+    ("fp32", 1, 50, 60, 4, 3, True, (1, 20)),
+    ("fp32", 1, 40, 96, 6, 12, False, None),
+    ("fp32", 1, 30, 40, 4, 10, True, None),
 ]
 
 # (dtype, B, T, D, W, R, residual, segment-length range or None)

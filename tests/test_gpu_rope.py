@@ -69,6 +69,13 @@ RP_CASES = [
     ("bf16", 2, 66, 512, 7, 2, 64, 256, False, None),     # four filter groups per 16-byte chunk
     ("bf16", 4, 65, 2304, 4, 64, 64, 1536, True, None),   # the QKV layout at a short length
     ("bf16", 1, 1, 16, 3, 8, 8, 8, False, None),          # one token
+    # any H: groups across 16-byte chunks (3, 6), lane groups padded to a power of two (24, 48, 96)
+    ("bf16", 2, 60, 96, 4, 3, 16, 64, True, (1, 20)),
+    ("bf16", 1, 70, 192, 4, 6, 32, 128, False, None),
+    ("bf16", 2, 50, 192, 4, 24, 32, 128, True, (1, 30)),
+    ("bf16", 1, 90, 384, 4, 48, 64, 256, True, None),
+    ("bf16", 1, 40, 768, 3, 96, 64, 512, False, (1, 25)),
+    ("fp32", 1, 30, 48, 4, 3, 8, 32, True, None),
 ]
 
 
