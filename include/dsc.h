@@ -217,6 +217,27 @@ DSC_API dsc_status dsc_lowrank_bwd(void *stream, int dtype, int64_t B, int64_t T
                            void *dz, float *dU, void *workspace, size_t workspace_bytes);
 
 /*
+ * The low-rank backward above for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that
+ * forbid allocation): no workspace argument; the fp32 dz accumulator lives
+ * in a scratch array built into the library, one per device, held by the
+ * process until it ends.  Nothing is allocated by the call.
+ *   Limit: B*T*R <= 4,194,304 (16 MiB of fp32); larger sizes return
+ *   DSC_ERR_WORKSPACE before any HIP call.  (DSC_FP32 needs no scratch.)
+ *   The scratch of the device current at the call is used: the stream must
+ *   belong to that device.  Calls that overlap in time on one device race
+ *   on its scratch; serialise them (one stream, or events).  The scratch is
+ *   cleared by a kernel of the call before use and keeps the last call's
+ *   contents afterwards.
+ * Other arguments, results and errors as dsc_lowrank_bwd (dz and dU are
+ * summed with fp32 atomics).
+ */
+DSC_API dsc_status dsc_lowrank_bwd_noalloc(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                                           int32_t R, const void *x, const void *z, const void *U,
+                                           const void *dy, const int32_t *cu_seqlens, int32_t n_seqs,
+                                           int32_t residual, void *dx, void *dz, float *dU);
+
+/*
  * Bytes of device workspace dsc_lowrank_bwd_deterministic needs for these
  * sizes and dtype (0 for invalid sizes, and where no workspace is needed).
  * It depends on the sizes and dtype only, not on the device: for DSC_BF16

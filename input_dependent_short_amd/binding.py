@@ -45,6 +45,7 @@ def lib() -> ctypes.CDLL:
         L.dsc_lowrank_bwd_deterministic_workspace_size.argtypes = [i, i64, i64, i64, i32, i32]
         L.dsc_lowrank_bwd_deterministic_workspace_size.restype = ctypes.c_size_t
         L.dsc_lowrank_bwd_deterministic.argtypes = L.dsc_lowrank_bwd.argtypes
+        L.dsc_lowrank_bwd_noalloc.argtypes = [p, i, i64, i64, i64, i32, i32, p, p, p, p, p, i32, i32, p, p, p]
         L.dsc_static_fwd.argtypes = [p, i, i64, i64, i64, i32, p, p, p, i32, i32, p]
         L.dsc_static_bwd.argtypes = [p, i, i64, i64, i64, i32, p, p, p, p, i32, i32, p, p]
         L.dsc_static_bwd_deterministic_workspace_size.argtypes = [i, i64, i64, i64, i32]
@@ -60,7 +61,7 @@ def lib() -> ctypes.CDLL:
         L.dsc_headwise_rope_bwd.argtypes = [p, i, i64, i64, i64, i32, i32, p, p, p, p, i32, i32, i64, i32, p, i64,
                                             p, p]
         L.dsc_bench_stream.argtypes = [p, p, i64, p, i64, i32, i32, i32, i32, i64]
-        for f in ("dsc_bench_stream", "dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd",
+        for f in ("dsc_bench_stream", "dsc_lowrank_bwd_noalloc", "dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd",
                   "dsc_lowrank_bwd_deterministic", "dsc_static_bwd_deterministic",
                   "dsc_static_fwd", "dsc_static_bwd", "dsc_headwise_decode", "dsc_lowrank_decode",
                   "dsc_state_from_prefill", "dsc_rope_table", "dsc_headwise_rope_fwd",
@@ -201,6 +202,17 @@ def dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, workspace=None, *, W, cu_seqlens=No
     _check(lib().dsc_lowrank_bwd(_stream(stream), _dtype_code(x), B, T, D, W, R, _ptr(x), _ptr(z),
                                  _ptr(U), _ptr(dy), cu, ns, int(bool(residual)), _ptr(dx), _ptr(dz),
                                  _ptr(dU), _ptr(workspace), ws_bytes))
+
+
+def dsc_lowrank_bwd_noalloc(x, z, U, dy, dx, dz, dU, *, W, cu_seqlens=None, residual=False,
+                            stream=None) -> None:
+    """dsc_lowrank_bwd without a workspace (the library's built-in device scratch; B*T*R <= 4,194,304)."""
+    B, T, D = x.shape
+    R = z.shape[2]
+    cu, ns = _seq(cu_seqlens)
+    _check(lib().dsc_lowrank_bwd_noalloc(_stream(stream), _dtype_code(x), B, T, D, W, R, _ptr(x), _ptr(z),
+                                         _ptr(U), _ptr(dy), cu, ns, int(bool(residual)), _ptr(dx), _ptr(dz),
+                                         _ptr(dU)))
 
 
 def dsc_lowrank_bwd_deterministic_workspace_size(dtype: torch.dtype, B: int, T: int, D: int, W: int,

@@ -242,10 +242,12 @@ size_t dsc_lowrank_bwd_workspace_size(int dtype, int64_t B, int64_t T, int64_t D
 namespace {
 
 // Validation and launch shared by the two low-rank backward entry points.
+// noalloc: no workspace argument; the accumulator is the device's built-in
+// scratch, whose address is taken only after every other check passed.
 dsc_status lowrank_bwd_call(bool det, const char *name, void *stream, int dtype, int64_t B, int64_t T, int64_t D,
                             int32_t W, int32_t R, const void *x, const void *z, const void *U, const void *dy,
                             const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, void *dx, void *dz,
-                            float *dU, void *workspace, size_t workspace_bytes) {
+                            float *dU, void *workspace, size_t workspace_bytes, bool noalloc = false) {
     DSC_TRY(check_common(dtype, B, T, D, W, cu_seqlens, n_seqs, residual));
     if (R < 1 || R > 128) return fail(DSC_ERR_SHAPE, "R = %d must be in 1..128", R);
     if (B * T == 0) {  // empty batch: dU is a sum over no tokens, zero; nothing else has elements
@@ -261,7 +263,13 @@ dsc_status lowrank_bwd_call(bool det, const char *name, void *stream, int dtype,
     const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
     const size_t need = det ? dsc::lowrank_bwd_det_workspace(dt, B * T, D, W, R)
                             : dsc::lowrank_bwd_workspace(dt, B * T, D, W, R);
-    if (need > 0) {
+    if (noalloc) {
+        if (need > (size_t)dsc::kNoallocScratchFloats * sizeof(float))
+            return fail(DSC_ERR_WORKSPACE,
+                        "B*T*R = %lld exceeds the built-in scratch of %lld fp32 values (use dsc_lowrank_bwd "
+                        "with a workspace)",
+                        (long long)(B * T * R), (long long)dsc::kNoallocScratchFloats);
+    } else if (need > 0) {
         if (!workspace || workspace_bytes < need)
             return fail(DSC_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need,
                         workspace ? workspace_bytes : (size_t)0);
@@ -273,8 +281,14 @@ dsc_status lowrank_bwd_call(bool det, const char *name, void *stream, int dtype,
                         rng("cu_seqlens", cu_seqlens, cu_seqlens ? 4u * (n_seqs + 1) : 0)};
     const Range out[] = {rng("dx", dx, N * D * es), rng("dz", dz, N * R * es),
                          rng("dU", dU, (size_t)R * D * W * 4),
-                         rng("workspace", workspace, need ? need : 0)};
+                         rng("workspace", workspace, need && !noalloc ? need : 0)};
     DSC_TRY(check_alias(in, 5, out, 4));
+    if (noalloc && need > 0) {
+        float *scratch = nullptr;
+        const hipError_t e = dsc::noalloc_scratch(&scratch);
+        if (e != hipSuccess) return fail(DSC_ERR_HIP, "%s: scratch address: %s", name, hipGetErrorString(e));
+        workspace = scratch;
+    }
     float *acc = need ? static_cast<float *>(workspace) : det ? nullptr : static_cast<float *>(dz);
     dsc::LrProblem p{dt, B * T, T, D, W, R, x, z, U, dy, nullptr, dx, dz, dU, acc, cu_seqlens, n_seqs, residual};
     return launched(det ? dsc::lowrank_bwd_det(p, (hipStream_t)stream) : dsc::lowrank_bwd(p, (hipStream_t)stream),
@@ -289,6 +303,14 @@ dsc_status dsc_lowrank_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_
                            void *dz, float *dU, void *workspace, size_t workspace_bytes) {
     return lowrank_bwd_call(false, "dsc_lowrank_bwd launch", stream, dtype, B, T, D, W, R, x, z, U, dy, cu_seqlens,
                             n_seqs, residual, dx, dz, dU, workspace, workspace_bytes);
+}
+
+dsc_status dsc_lowrank_bwd_noalloc(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                                   int32_t R, const void *x, const void *z, const void *U, const void *dy,
+                                   const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, void *dx,
+                                   void *dz, float *dU) {
+    return lowrank_bwd_call(false, "dsc_lowrank_bwd_noalloc launch", stream, dtype, B, T, D, W, R, x, z, U, dy,
+                            cu_seqlens, n_seqs, residual, dx, dz, dU, nullptr, 0, true);
 }
 
 size_t dsc_lowrank_bwd_deterministic_workspace_size(int dtype, int64_t B, int64_t T, int64_t D, int32_t W,

@@ -112,6 +112,12 @@ hipError_t decode_step(const DecProblem &p, hipStream_t s);
 hipError_t state_from_prefill(Dtype dt, const void *x, const int32_t *cu, int32_t n_seqs, int64_t B, int64_t T,
                               int64_t D, int32_t W, void *state, hipStream_t s);
 
+// Allocation-free low-rank backward: the device address of this device's
+// file-scope scratch (kNoallocScratchFloats fp32 values), taken once per
+// device (noalloc.hip).
+constexpr int64_t kNoallocScratchFloats = (int64_t)4 << 20;  // 16 MiB: B*T*R <= 4,194,304
+hipError_t noalloc_scratch(float **out);
+
 // Streaming measurement kernel (stream.hip): reads read_bytes and writes
 // write_bytes in 16-byte units; blocks <= 0 takes one round of resident
 // workgroups.

@@ -91,6 +91,14 @@ int main(void) {
                DSC_ERR_NULL, "lr bwd empty needs dU");
     }
 
+    /* the allocation-free backward: its scratch limit and the usual checks, before any HIP call */
+    expect(dsc_lowrank_bwd_noalloc(0, DSC_BF16, 4, 16385, 64, 4, 64, P(1), P(2), P(3), P(4), NULL, 0, 0, P(5), P(6),
+                                   (float *)P(7)), DSC_ERR_WORKSPACE, "noalloc limit");
+    expect(dsc_lowrank_bwd_noalloc(0, DSC_BF16, huge, 2, 64, 4, 64, P(1), P(2), P(3), P(4), NULL, 0, 0, P(5), P(6),
+                                   (float *)P(7)), DSC_ERR_SHAPE, "noalloc B max");
+    expect(dsc_lowrank_bwd_noalloc(0, DSC_BF16, 1, 8, 64, 4, 16, P(1), P(2), P(3), P(4), NULL, 0, 0, P(1), P(6),
+                                   (float *)P(7)), DSC_ERR_ALIAS, "noalloc alias");
+
     /* static layer */
     expect(dsc_static_fwd(0, DSC_BF16, 1, 8, 64, 9, P(1), P(2), NULL, 0, 0, P(3)), DSC_ERR_SHAPE, "st W");
     expect(dsc_static_bwd(0, DSC_BF16, 1, 8, 64, 4, P(1), P(2), P(3), NULL, 0, 0, P(4), (float *)P(4)),

@@ -293,3 +293,17 @@ def test_bench_stream_validation(lib):
     assert st(dst=None) == 1 and st(src=None) == 1
     assert st(src=ctypes.c_void_p(A + 8)) == 4
     assert st(dst=P(1)) == 5                      # dst overlaps src
+
+
+def test_lowrank_bwd_noalloc_validation(lib):
+    """The allocation-free backward checks everything, including its scratch
+    limit (B*T*R <= 4,194,304), before any HIP call."""
+    def call(B=1, T=8, D=64, R=16, x=P(1), dU=P(7)):
+        return lib.dsc_lowrank_bwd_noalloc(S0, 1, B, T, D, 4, R, x, P(2), P(3), P(4), None, 0, 0,
+                                           P(5), P(6), dU)
+    assert call(x=None) == 1
+    assert call(dU=ctypes.c_void_p(A * 7 + 4)) == 4
+    assert call(R=0) == 2 and call(R=129) == 2
+    assert call(T=(4 << 20) // 64 + 1, R=64) == 6     # one token past the scratch
+    assert call(B=2, T=1 << 20, R=4) == 6
+    assert b"built-in scratch" in lib.dsc_last_error()
