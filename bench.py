@@ -473,7 +473,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--iters", type=int, default=50, help="flushed calls timed per entry point (at least 50)")
+    ap.add_argument("--iters", type=int, default=50,
+                    help="flushed calls timed per entry point (the default run uses at least 50; fewer only with "
+                         "--headline-only, for profiler passes)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
@@ -508,7 +510,7 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     binding.lib()  # fails loudly if the HIP library is not built
-    iters = max(50, args.iters)
+    iters = args.iters if args.headline_only else max(50, args.iters)
     if args.stream_sweep:
         return stream_sweep(torch, binding, inputs)
     # a 1 GiB read before every timed call evicts the inputs from the
