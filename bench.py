@@ -468,6 +468,42 @@ def stream_sweep(torch, binding, inputs) -> int:
     return 0
 
 
+def summarize_sq(dirs, kernels=("hw_fwd_kernel", "hw_bwd_kernel", "lr_fwd_wide", "lr_fwd_mfma", "lr_bwd_mfma",
+                                 "lr_dz_", "lr_bwd_generic", "st_fwd_kernel", "st_bwd_kernel")) -> str:
+    """Markdown table of the SQ counters (rocprofv3 --pmc passes of this
+    script, one directory each) of the convolution kernels, averaged per
+    dispatch: instructions per wave, vector-ALU and matrix-core busy fractions
+    per SIMD, LDS bank conflicts per active LDS cycle."""
+    import collections
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for d in dirs:
+        for r in _counter_rows(d):
+            k = r["Kernel_Name"]
+            if any(p in k for p in kernels):
+                vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                vals[k]["VGPR"] = [float(r["VGPR_Count"])]
+                vals[k]["AGPR"] = [float(r.get("Accum_VGPR_Count") or 0)]
+    avg = lambda k, c: (sum(vals[k][c]) / len(vals[k][c])) if vals[k].get(c) else float("nan")
+    out = ["| kernel | waves | VGPR + AGPR | VALU / wave | MFMA / wave | LDS / wave | SALU / wave | "
+           "VMEM rd / wave | VMEM wr / wave | VALU busy | matrix cores busy | waiting / wave cycles | "
+           "LDS conflict / LDS active |", "|" + "---|" * 13]
+    for k in sorted(vals):
+        w = avg(k, "SQ_WAVES")
+        cyc = avg(k, "GRBM_GUI_ACTIVE") / 8.0  # the counter sums the 8 XCDs
+        simds = 1024.0
+        name = k.replace("void ", "").replace("dsc::(anonymous namespace)::", "").replace("dsc::", "")
+        name = name[:name.index(">") + 1] if ">" in name else name.split("(")[0]
+        out.append(f"| `{name}` | {w:.0f} | {avg(k, 'VGPR'):.0f} + {avg(k, 'AGPR'):.0f} | "
+                   f"{avg(k, 'SQ_INSTS_VALU') / w:.0f} | {avg(k, 'SQ_INSTS_MFMA') / w:.0f} | "
+                   f"{avg(k, 'SQ_INSTS_LDS') / w:.0f} | {avg(k, 'SQ_INSTS_SALU') / w:.0f} | "
+                   f"{avg(k, 'SQ_INSTS_VMEM_RD') / w:.0f} | {avg(k, 'SQ_INSTS_VMEM_WR') / w:.0f} | "
+                   f"{avg(k, 'SQ_ACTIVE_INST_VALU') * 4 / simds / cyc:.0%} | "
+                   f"{avg(k, 'SQ_VALU_MFMA_BUSY_CYCLES') / simds / cyc:.0%} | "
+                   f"{avg(k, 'SQ_WAIT_INST_ANY') / max(avg(k, 'SQ_WAVE_CYCLES'), 1):.0%} | "
+                   f"{avg(k, 'SQ_LDS_BANK_CONFLICT') / max(avg(k, 'SQ_ACTIVE_INST_LDS'), 1):.2f} |")
+    return "\n".join(out)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -486,11 +522,16 @@ def main() -> int:
                          "otherwise mix with the fast backward's in a kernel trace)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs of this script into profiles/traffic.json")
+    ap.add_argument("--summarize-sq", nargs="+", metavar="DIR",
+                    help="print a markdown table of the SQ counters from rocprofv3 --pmc passes of this script")
     ap.add_argument("--stream-sweep", action="store_true",
                     help="only sweep the streaming kernel's recipes (loads in flight, cache policies, order, "
                          "grid size) over the byte mixes of the 2B head-wise layer; one JSON line per mix")
     args = ap.parse_args()
 
+    if args.summarize_sq:
+        print(summarize_sq(args.summarize_sq))
+        return 0
     if args.summarize_counters:
         rec = summarize_counters(*args.summarize_counters, os.path.join(ROOT, "profiles", "traffic.json"))
         print(json.dumps(rec, indent=1))

@@ -262,7 +262,7 @@ dsc_status lowrank_bwd_call(bool det, const char *name, void *stream, int dtype,
         return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
     const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
     const size_t need = det ? dsc::lowrank_bwd_det_workspace(dt, B * T, D, W, R)
-                            : dsc::lowrank_bwd_workspace(dt, B * T, D, W, R);
+                            : dsc::lowrank_bwd_workspace(dt, B * T, D, W, R, !noalloc);
     if (noalloc) {
         if (need > (size_t)dsc::kNoallocScratchFloats * sizeof(float))
             return fail(DSC_ERR_WORKSPACE,
@@ -291,7 +291,8 @@ dsc_status lowrank_bwd_call(bool det, const char *name, void *stream, int dtype,
     }
     float *acc = need ? static_cast<float *>(workspace) : det ? nullptr : static_cast<float *>(dz);
     dsc::LrProblem p{dt, B * T, T, D, W, R, x, z, U, dy, nullptr, dx, dz, dU, acc, cu_seqlens, n_seqs, residual};
-    return launched(det ? dsc::lowrank_bwd_det(p, (hipStream_t)stream) : dsc::lowrank_bwd(p, (hipStream_t)stream),
+    return launched(det ? dsc::lowrank_bwd_det(p, (hipStream_t)stream)
+                        : dsc::lowrank_bwd(p, (hipStream_t)stream, !noalloc),
                     name);
 }
 

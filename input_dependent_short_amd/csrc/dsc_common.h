@@ -279,13 +279,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_stream(const void *base, 
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)(uint32_t)b, kBufferWord3);
 }
 
+// NT: the nontemporal (streaming) cache policy, for streams read or written
+// once per launch in whole cache lines.
+template <bool NT = false>
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, NT ? 2 : 0));
 }
 
+template <bool NT = false>
 __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v),
-                                           r, off, 0, 0);
+                                           r, off, 0, NT ? 2 : 0);
 }
 
 // ----------------------------------------------------------- sequences

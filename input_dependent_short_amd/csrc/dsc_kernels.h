@@ -88,12 +88,27 @@ hipError_t headwise_rope_bwd(const HwProblem &p, hipStream_t s);
 // table[(m*hd/2 + i)*2 + {0,1}] = {cos, sin}(m * base^(-2i/hd)), m < max_pos.
 hipError_t rope_table(int64_t max_pos, int32_t hd, double base, float *table, hipStream_t s);
 
-size_t lowrank_bwd_workspace(Dtype dt, int64_t N, int64_t D, int32_t W, int32_t R);
+// split_ok false keeps dz inside the matrix-core backward (workspace: one
+// fp32 (N, R) accumulator), as the allocation-free entry point needs.
+size_t lowrank_bwd_workspace(Dtype dt, int64_t N, int64_t D, int32_t W, int32_t R, bool split_ok = true);
+
+// dz of the low-rank backward as its own launches (lowrank_dz.hip): a
+// tap-major copy of U (ut_elems bf16) and fp32 partial sums, one (N, R)
+// region per split of the channels (S of them, cper channels each), added in
+// ascending order afterwards.  The split depends on the sizes only.
+struct LrDzPlan {
+    int64_t ntb, cper;
+    int32_t S;
+    int64_t ut_elems, part_floats;
+};
+LrDzPlan lowrank_dz_plan(int64_t N, int64_t D, int32_t W, int32_t R);
+bool lowrank_dz_supported(int32_t W, int32_t R);
+hipError_t lowrank_dz_partials(const LrProblem &pr, const LrDzPlan &pl, uint16_t *Ut, float *parts, hipStream_t st);
 hipError_t lowrank_fwd(const LrProblem &p, hipStream_t s);
 // Wide bf16 forward (R <= 64); sets *used to false when the shape is left to
 // the other kernels, which then run instead.
 hipError_t lowrank_fwd_wide(const LrProblem &p, hipStream_t s, bool *used);
-hipError_t lowrank_bwd(const LrProblem &p, hipStream_t s);
+hipError_t lowrank_bwd(const LrProblem &p, hipStream_t s, bool split_ok = true);
 // Reproducible backward: dz and dU summed in one fixed order (dz_acc = its
 // workspace of lowrank_bwd_det_workspace bytes, may be null when that is 0).
 size_t lowrank_bwd_det_workspace(Dtype dt, int64_t N, int64_t D, int32_t W, int32_t R);

@@ -63,7 +63,8 @@ struct HwParams {
     int32_t lanes, L;
     float rho;
     int64_t nchunks, items;
-    int64_t slots;  // backward lanes per token tile: (nchunks / L) * lanes
+    int64_t slots;    // backward lanes per token tile: (nchunks / L) * lanes
+    int64_t lblocks;  // logical workgroups of kBlock work items
     const float *rope;  // (npos, hd/2, 2) cos, sin; read only by the ROPE kernels
     int32_t rot, hd;    // rotated channels [0, rot), head size
     int32_t npos;       // table rows
@@ -81,9 +82,13 @@ __device__ __forceinline__ constexpr int grp(int c) {
 // dy rows of its own tile; y, dx and dw): nontemporal.  The halo rows before
 // a tile, which the neighbouring tile also reads, keep the default policy.
 #ifndef DSC_HW_NT
-#define DSC_HW_NT 1
+#define DSC_HW_NT 13  // bits: 1 x loads, 2 filter loads, 4 y / dx stores, 8 dy loads, 16 dw stores
 #endif
-constexpr bool kNT = DSC_HW_NT != 0;
+constexpr bool kNT = (DSC_HW_NT & 1) != 0;
+constexpr bool kNTW = (DSC_HW_NT & 2) != 0;
+constexpr bool kNTS = (DSC_HW_NT & 4) != 0;
+constexpr bool kNTG = (DSC_HW_NT & 8) != 0;
+constexpr bool kNTD = (DSC_HW_NT & 16) != 0;
 
 // Raw 16-byte vector of activations, widened to fp32 when used.
 template <class E, bool NT = false>
@@ -149,15 +154,14 @@ __device__ __forceinline__ void group_sum(float (&v)[NW], int lanes) {
     }
 }
 
+// One work item (a 16-byte channel chunk of one token tile) of the forward.
 template <class E, int W, int GPT, int TT, int U, bool ROPE>
-__global__ __launch_bounds__(kBlock) void hw_fwd_kernel(HwParams p) {
+__device__ __forceinline__ void hw_fwd_item(const HwParams &p, int64_t item) {
     using S = typename E::store_t;
     constexpr int VEC = E::kVec;
     constexpr int NW = GPT * W;
     constexpr int WALIGN = pow2_align(NW * (int)sizeof(S));
 
-    const int64_t item = xcd_block_id(blockIdx.x, gridDim.x) * kBlock + threadIdx.x;
-    if (item >= p.items) return;
     const int64_t tile = item / p.nchunks;
     const int64_t chunk = item - tile * p.nchunks;
     const int64_t n0 = tile * TT;
@@ -214,7 +218,7 @@ __global__ __launch_bounds__(kBlock) void hw_fwd_kernel(HwParams p) {
             const int64_t n = nb + u;
             if (n < n1) {
                 xr[u] = load_raw<E, kNT>(x + n * p.D);
-                WS::template load<WALIGN, kNT>(w + n * p.G * W, wr[u]);
+                WS::template load<WALIGN, kNTW>(w + n * p.G * W, wr[u]);
             }
         }
     };
@@ -269,7 +273,7 @@ __global__ __launch_bounds__(kBlock) void hw_fwd_kernel(HwParams p) {
                         turn<VEC, false>(acc, cs[u]);
                     }
                 }
-                Vec16<E>::template store<kNT>(y + n * p.D, acc);
+                Vec16<E>::template store<kNTS>(y + n * p.D, acc);
 #pragma unroll
                 for (int i = W - 2; i > 0; --i)
 #pragma unroll
@@ -292,19 +296,28 @@ __global__ __launch_bounds__(kBlock) void hw_fwd_kernel(HwParams p) {
     }
 }
 
+// Workgroups of kBlock threads walk the logical blocks lb = blockIdx.x,
+// blockIdx.x + gridDim.x, ... (one each when the grid covers them all; a
+// grid of one round of resident workgroups otherwise), logical blocks
+// remapped so that neighbouring tiles run on the same XCD (the grid is a
+// multiple of 8 workgroups when it walks).
 template <class E, int W, int GPT, int TT, int U, bool ROPE>
-__global__ __launch_bounds__(kBlock) void hw_bwd_kernel(HwParams p) {
+__global__ __launch_bounds__(kBlock) void hw_fwd_kernel(HwParams p) {
+    for (int64_t lb = blockIdx.x; lb < p.lblocks; lb += gridDim.x) {
+        const int64_t item = xcd_block_id(lb, p.lblocks) * kBlock + threadIdx.x;
+        if (item < p.items) hw_fwd_item<E, W, GPT, TT, U, ROPE>(p, item);
+    }
+}
+
+// One work item of the backward.
+template <class E, int W, int GPT, int TT, int U, bool ROPE>
+__device__ __forceinline__ void hw_bwd_item(const HwParams &p, int64_t item) {
     using S = typename E::store_t;
     constexpr int VEC = E::kVec;
     constexpr int NW = GPT * W;
     constexpr int WALIGN = pow2_align(NW * (int)sizeof(S));
     constexpr int WIN = U + W - 1;  // look-ahead window of (dy, w)
 
-    const int64_t item = xcd_block_id(blockIdx.x, gridDim.x) * kBlock + threadIdx.x;
-    // Whole filter groups are active or inactive together (items is a
-    // multiple of slots, which is a multiple of lanes), so exiting here never
-    // strands a lane that a group reduction reads.
-    if (item >= p.items) return;
     const int64_t tile = item / p.slots;
     const int64_t slot = item - tile * p.slots;
     // lane li of filter group gi; padding lanes (li >= L) repeat the group's
@@ -357,8 +370,8 @@ __global__ __launch_bounds__(kBlock) void hw_bwd_kernel(HwParams p) {
     uint32_t ww[WIN][NWW];
     auto load_gw = [&](int64_t t, int slot) {
         if (t < p.N) {
-            gw[slot] = load_raw<E, kNT>(g + t * p.D);
-            WS::template load<WALIGN, kNT>(w + t * p.G * W, ww[slot]);
+            gw[slot] = load_raw<E, kNTG>(g + t * p.D);
+            WS::template load<WALIGN, kNTW>(w + t * p.G * W, ww[slot]);
         } else {
             gw[slot] = zero4;
 #pragma unroll
@@ -449,7 +462,7 @@ __global__ __launch_bounds__(kBlock) void hw_bwd_kernel(HwParams p) {
                         acc[c] = __builtin_fmaf(wk, gk, acc[c]);
                     }
                 }
-                if (active) Vec16<E>::template store<kNT>(dx + m * p.D, acc);
+                if (active) Vec16<E>::template store<kNTS>(dx + m * p.D, acc);
 
                 float part[NW];
 #pragma unroll
@@ -487,7 +500,7 @@ __global__ __launch_bounds__(kBlock) void hw_bwd_kernel(HwParams p) {
 #pragma unroll
                     for (int k = 0; k < W; ++k)
                         if (k > back) part[q * W + k] = 0.f;
-                if (leader) Span<E, NW>::template store<WALIGN, kNT>(dw + m * p.G * W, part);
+                if (leader) Span<E, NW>::template store<WALIGN, kNTD>(dw + m * p.G * W, part);
 
 #pragma unroll
                 for (int i = W - 2; i > 0; --i) ring[i] = ring[i - 1];
@@ -506,6 +519,17 @@ __global__ __launch_bounds__(kBlock) void hw_bwd_kernel(HwParams p) {
 #pragma unroll
             for (int c = 0; c < NWW; ++c) ww[i][c] = ww[U + i][c];
         }
+    }
+}
+
+template <class E, int W, int GPT, int TT, int U, bool ROPE>
+__global__ __launch_bounds__(kBlock) void hw_bwd_kernel(HwParams p) {
+    for (int64_t lb = blockIdx.x; lb < p.lblocks; lb += gridDim.x) {
+        const int64_t item = xcd_block_id(lb, p.lblocks) * kBlock + threadIdx.x;
+        // Whole filter groups are in or out of range together (items is a
+        // multiple of slots, which is a multiple of lanes), so skipping here
+        // never strands a lane that a group reduction reads.
+        if (item < p.items) hw_bwd_item<E, W, GPT, TT, U, ROPE>(p, item);
     }
 }
 
@@ -538,13 +562,28 @@ HwParams make_params(const HwProblem &pr, int64_t tt, bool bwd, int64_t &blocks)
     p.npos = (int32_t)pr.max_pos;
     const int64_t ntiles = (pr.N + tt - 1) / tt;
     p.items = ntiles * (bwd ? p.slots : p.nchunks);
-    blocks = (p.items + kBlock - 1) / kBlock;
+    p.lblocks = (p.items + kBlock - 1) / kBlock;
+    blocks = p.lblocks;
     return p;
 }
 
 // The backward takes tiles of 2*kTT tokens when those still give at least
 // one whole round of resident waves (measured on MI355X: 7% faster at
 // B=4 T=4096 D=8192, much slower when the grid no longer fills the chip).
+#ifndef DSC_HW_PERSIST
+#define DSC_HW_PERSIST 1
+#endif
+// Grid of a launch over `lblocks` logical workgroups: all of them, or (when
+// they need more than one round of resident workgroups) one round, a
+// multiple of 8, whose workgroups then walk the logical blocks.  One round
+// avoids the ramp between rounds.
+inline int64_t hw_grid(int64_t lblocks, int bpc) {
+    if (!DSC_HW_PERSIST) return lblocks;
+    int64_t round = (int64_t)device_cus() * bpc;
+    round -= round % 8;
+    return (round >= 8 && lblocks > round) ? round : lblocks;
+}
+
 template <class E, int W, int GPT, bool ROPE>
 hipError_t launch_w(const HwProblem &pr, hipStream_t st, bool bwd) {
     constexpr int UB = kU;
@@ -556,19 +595,24 @@ hipError_t launch_w(const HwProblem &pr, hipStream_t st, bool bwd) {
         const int64_t waves_long = p.items / kWave;
         if (waves_long >= (int64_t)device_cus() * bpc * (kBlock / kWave)) {
             if (blocks)
-                hipLaunchKernelGGL((hw_bwd_kernel<E, W, GPT, 2 * kTT, UB, ROPE>), dim3((unsigned)blocks),
+                hipLaunchKernelGGL((hw_bwd_kernel<E, W, GPT, 2 * kTT, UB, ROPE>), dim3((unsigned)hw_grid(blocks, bpc)),
                                    dim3(kBlock), 0, st, p);
             return hipGetLastError();
         }
+        static const int bpc_short = blocks_per_cu(
+            reinterpret_cast<const void *>(&hw_bwd_kernel<E, W, GPT, kTT, UB, ROPE>), kBlock);
         p = make_params<E>(pr, kTT, true, blocks);
         if (blocks)
-            hipLaunchKernelGGL((hw_bwd_kernel<E, W, GPT, kTT, UB, ROPE>), dim3((unsigned)blocks), dim3(kBlock), 0,
-                               st, p);
+            hipLaunchKernelGGL((hw_bwd_kernel<E, W, GPT, kTT, UB, ROPE>), dim3((unsigned)hw_grid(blocks, bpc_short)),
+                               dim3(kBlock), 0, st, p);
         return hipGetLastError();
     }
+    static const int bpc_fwd = blocks_per_cu(
+        reinterpret_cast<const void *>(&hw_fwd_kernel<E, W, GPT, kTT, kU, ROPE>), kBlock);
     HwParams p = make_params<E>(pr, kTT, false, blocks);
     if (blocks)
-        hipLaunchKernelGGL((hw_fwd_kernel<E, W, GPT, kTT, kU, ROPE>), dim3((unsigned)blocks), dim3(kBlock), 0, st, p);
+        hipLaunchKernelGGL((hw_fwd_kernel<E, W, GPT, kTT, kU, ROPE>), dim3((unsigned)hw_grid(blocks, bpc_fwd)),
+                           dim3(kBlock), 0, st, p);
     return hipGetLastError();
 }
 

@@ -181,13 +181,6 @@ __device__ __forceinline__ void load_u_cols(const uint16_t *U, int R, int64_t D,
     }
 }
 
-// DPP controls (row = 16 lanes): lane i of a row reads lane i-k (shr) or
-// lane (i-k) mod 16 (ror).
-template <int K>
-__device__ __forceinline__ uint32_t shift_in_row(uint32_t cur, uint32_t prev) {
-    const int rot = __builtin_amdgcn_mov_dpp((int)prev, 0x120 + K, 0xf, 0xf, true);
-    return (uint32_t)__builtin_amdgcn_update_dpp(rot, (int)cur, 0x110 + K, 0xf, 0xf, false);
-}
 
 template <int W>
 struct Shifted {
@@ -405,18 +398,6 @@ __device__ __forceinline__ void shift_ahead4(int k, const uint32_t (&cur)[4], co
     }
 }
 
-template <int W, int K = 1>
-__device__ __forceinline__ void shift_back4(int k, const uint32_t (&cur)[4], const uint32_t (&prev)[4],
-                                            uint32_t (&out)[4]) {
-    if constexpr (K < W) {
-        if (k == K) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) out[i] = shift_in_row<K>(cur[i], prev[i]);
-        } else {
-            shift_back4<W, K + 1>(k, cur, prev, out);
-        }
-    }
-}
 
 __device__ __forceinline__ bf16x8 bf16x8_from_u32(const uint32_t (&v)[4]) {
     uint4 q = make_uint4(v[0], v[1], v[2], v[3]);
@@ -495,7 +476,10 @@ template <bool V> struct MaskTag { static constexpr bool value = V; };
 // (the R = 64 kernel ran twice as long), so they walk whole rings.
 constexpr bool bwd_exact_walk(int H, bool RVEC) { return H == 2 && RVEC; }
 
-template <int W, int RC, int P, bool RVEC, int H>
+// DZ false: dx and dU only (dz is then computed by the kernels of
+// lowrank_dz.hip); the dz products, their LDS exchange and its barriers and
+// atomics are left out.
+template <int W, int RC, int P, bool RVEC, int H, bool DZ = true>
 __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void lr_bwd_mfma(LrParams p, int64_t nslices,
                                                                                          int64_t tok_per_half) {
     using L = BwdLds<W, RC, H>;
@@ -546,9 +530,9 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
 
     // ---- U operands, kept in registers for the whole walk
     bf16x8 ua[W][2][RC];  // rows: channel d0 + 8(i>>2) + 4t + (i&3); K: rank 32c + 8(lane>>4) + e
-    bf16x8 ub[W][RT];     // rows: rank 16rt + (lane&15); K: channel d0 + 8(lane>>4) + e
+    bf16x8 ub[DZ ? W : 1][DZ ? RT : 1];  // rows: rank 16rt + (lane&15); K: channel d0 + 8(lane>>4) + e
     load_u_rows<W, RC>(U, R, D, d0, lane, ua);
-    load_u_cols<W, RT>(U, R, D, d0, lane, ub);
+    if constexpr (DZ) load_u_cols<W, RT>(U, R, D, d0, lane, ub);
     floatx4 du[W][2][RT];
 #pragma unroll
     for (int k = 0; k < W; ++k)
@@ -576,9 +560,8 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
     const __amdgpu_buffer_rsrc_t rz = make_stream(zg + nbeg * R, (N - nbeg) * R * 2);
     const __amdgpu_buffer_rsrc_t rdx = make_stream(dxg + nbeg * D, (nend - nbeg) * D * 2);
     const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
-    auto fetch_act = [&](__amdgpu_buffer_rsrc_t r, int64_t step) {
-        return buf_load16(r, xoff + (uint32_t)step * act_step);
-    };
+    auto fetch_x = [&](int64_t step) { return buf_load16<kLrNtX>(rx, xoff + (uint32_t)step * act_step); };
+    auto fetch_g = [&](int64_t step) { return buf_load16<kLrNtG>(rg, xoff + (uint32_t)step * act_step); };
     auto fetch_z = [&](int64_t step, uint4 (&dst)[RC]) {
         if constexpr (RVEC) {
 #pragma unroll
@@ -622,7 +605,7 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
     uint4 xr[P], gr[P];
     uint4 zr[P][RC];
 #pragma unroll
-    for (int j = 0; j < P - 1; ++j) xr[j] = fetch_act(rx, j);
+    for (int j = 0; j < P - 1; ++j) xr[j] = fetch_x(j);
     xr[P - 1] = zero4;  // step -1: only its last W-1 tokens are read
     {
         const int64_t n = nbeg - 16 + tok;
@@ -630,7 +613,7 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
             xr[P - 1] = *reinterpret_cast<const uint4 *>(xg + n * D + cbase);
     }
 #pragma unroll
-    for (int j = 0; j < P; ++j) gr[j] = fetch_act(rg, j);
+    for (int j = 0; j < P; ++j) gr[j] = fetch_g(j);
     {
         uint4 z0[RC];
         fetch_z(0, z0);
@@ -730,7 +713,7 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
                 v.y = pack_bf16x2(acc[2], acc[3]);
                 v.z = pack_bf16x2(acc[4], acc[5]);
                 v.w = pack_bf16x2(acc[6], acc[7]);
-                buf_store16(rdx, xoff + (uint32_t)s * act_step, v);
+                buf_store16<kLrNtDx>(rdx, xoff + (uint32_t)s * act_step, v);
             }
 
             // dwc_k = g * x[n-k] (bf16): dz^T partial on the matrix cores, dwc^T staged for dU
@@ -754,28 +737,37 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
                     dw[i2] = pack_bf16x2(bf16_lo(gc[i2]) * bf16_lo(xv), bf16_hi(gc[i2]) * bf16_hi(xv));
                 }
                 const bf16x8 b = bf16x8_from_u32(dw);
+                if constexpr (DZ) {
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
-                    cz[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ub[k][rt], b, cz[rt], 0, 0, 0);
+                    for (int rt = 0; rt < RT; ++rt)
+                        cz[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ub[k][rt], b, cz[rt], 0, 0, 0);
+                }
                 uint2 *d = reinterpret_cast<uint2 *>(dwcT + k * 32 * L::PW + (16 * ps + tok) * L::PW + 16 * q);
                 d[0] = make_uint2(dw[0], dw[1]);
                 d[1] = make_uint2(dw[2], dw[3]);
             }
             // dz partials (rows r = 16rt + 4q + j, column = token) -> LDS for the block reduction
+            if constexpr (DZ) {
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                float4 *d = reinterpret_cast<float4 *>(dzb + (buf * 32 + 16 * ps + tok) * L::PD + 4 * (16 * rt + 4 * q));
-                *d = make_float4(cz[rt][0], cz[rt][1], cz[rt][2], cz[rt][3]);
+                for (int rt = 0; rt < RT; ++rt) {
+                    float4 *d =
+                        reinterpret_cast<float4 *>(dzb + (buf * 32 + 16 * ps + tok) * L::PD + 4 * (16 * rt + 4 * q));
+                    *d = make_float4(cz[rt][0], cz[rt][1], cz[rt][2], cz[rt][3]);
+                }
             }
             };
             if (fast) body(MaskTag<false>{}); else body(MaskTag<true>{});
 
             // ring refills (issued after the step's reads of these slots)
-            xr[prv] = fetch_act(rx, s + P - 1);
-            gr[cur] = fetch_act(rg, s + P);
+            xr[prv] = fetch_x(s + P - 1);
+            gr[cur] = fetch_g(s + P);
 
             if (ps == 1) {
-                __syncthreads();  // the pair's dz partials from all four waves
+                if constexpr (DZ) {
+                    __syncthreads();  // the pair's dz partials from all four waves
+                } else {
+                    wave_lds_fence();  // the pair's dwc^T rows written by the wave's other lanes
+                }
                 // dU_k^T[ch, r] += sum over the pair's 32 tokens of dwc_k^T[ch, tok] * z[tok, r].
                 // Operands re-read transposed from LDS: lane = channel / rank,
                 // registers = tokens 8q .. 8q+7 of the pair.
@@ -811,6 +803,7 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
                 // dz of the pair's 32 tokens: fp32 atomics into the accumulator, issued
                 // only by lanes of ranks below R and tokens inside the block's range,
                 // each at an in-range offset of a resource based at the pair's row
+                if constexpr (DZ) {
                 const int64_t npair0 = nbeg + 16 * s_pair;
                 const __amdgpu_buffer_rsrc_t rdz =
                     make_stream(p.dzacc + group * p.dz_gstride + npair0 * R, (nend - npair0) * R * 4);
@@ -839,6 +832,7 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
                     } else {
                         buf ^= 1;         // the next pair writes the other buffer
                     }
+                }
                 }
             }
             if constexpr (kExactWalk) {
@@ -1168,9 +1162,72 @@ hipError_t mfma_bwd(const LrProblem &pr, hipStream_t st, bool det) {
     return hipGetLastError();
 }
 
+// Which bf16 shapes compute dz in launches of their own (split backward):
+// the matrix-core backward then runs without dz, so its blocks exchange
+// nothing and add no dz atomics.
+#ifndef DSC_LR_SPLIT
+#define DSC_LR_SPLIT 0
+#endif
+bool bwd_split(Dtype dt, int64_t D, int W, int R) {
+    if (!bwd_uses_mfma(dt, D, W, R) || !lowrank_dz_supported(W, R)) return false;
+    if (DSC_LR_SPLIT == 2) return true;
+    return DSC_LR_SPLIT == 1 && (R + 31) / 32 == 2;
+}
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+size_t split_workspace(int64_t N, int64_t D, int W, int R) {
+    const LrDzPlan pl = lowrank_dz_plan(N, D, W, R);
+    return align256((size_t)pl.ut_elems * 2) + align256((size_t)pl.part_floats * 4);
+}
+
+// dx and dU from the matrix-core kernel without dz; dz from the kernels of
+// lowrank_dz.hip into the workspace ([tap-major U][partials per channel
+// split]), then the partials added in order and rounded to bf16.
+template <int W, int RC>
+hipError_t split_bwd(const LrProblem &pr, hipStream_t st) {
+    LrParams p = make_params<BF16>(pr);
+    const int64_t nU = (int64_t)p.R * p.D * W;
+    const int64_t nz = p.N * p.R;
+    constexpr int H = bwd_two_per_simd(W, RC) ? 2 : 1;
+    static const int bpc_vec = blocks_per_cu(
+        reinterpret_cast<const void *>(&lr_bwd_mfma<W, RC, kBwdRing, true, H, false>), kBlock * H);
+    static const int bpc_gather = blocks_per_cu(
+        reinterpret_cast<const void *>(&lr_bwd_mfma<W, RC, kBwdRing, false, H, false>), kBlock * H);
+    const int64_t slots = (int64_t)device_cus() * (p.R % 8 == 0 ? bpc_vec : bpc_gather);
+    const BwdPlan pl = bwd_plan(p.N, p.D, W, p.R, slots);
+    const LrDzPlan dzp = lowrank_dz_plan(p.N, p.D, W, p.R);
+    unsigned char *ws = reinterpret_cast<unsigned char *>(pr.dz_acc);
+    uint16_t *Ut = reinterpret_cast<uint16_t *>(ws);
+    float *parts = reinterpret_cast<float *>(ws + align256((size_t)dzp.ut_elems * 2));
+    hipLaunchKernelGGL(clear2, dim3((unsigned)nblocks((nU + 3) / 4)), dim3(kBlock), 0, st,
+                       reinterpret_cast<uint32_t *>(p.dU), nU, static_cast<uint32_t *>(nullptr), (int64_t)0);
+    const dim3 grid((unsigned)(pl.tchunks * pl.ngroups));
+    const int64_t nslices = (p.D + 31) / 32;
+    if (p.R % 8 == 0)
+        hipLaunchKernelGGL((lr_bwd_mfma<W, RC, kBwdRing, true, H, false>), grid, dim3(kBlock * H), 0, st, p, nslices,
+                           pl.tph);
+    else
+        hipLaunchKernelGGL((lr_bwd_mfma<W, RC, kBwdRing, false, H, false>), grid, dim3(kBlock * H), 0, st, p,
+                           nslices, pl.tph);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = lowrank_dz_partials(pr, dzp, Ut, parts, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sum_parts<uint16_t>, dim3((unsigned)nblocks(nz)), dim3(kBlock), 0, st, parts,
+                       (int64_t)dzp.S, nz, static_cast<uint16_t *>(pr.dz), nz);
+    return hipGetLastError();
+}
+
 template <int W>
-hipError_t mfma_bwd_rc(const LrProblem &pr, hipStream_t st, bool det) {
+hipError_t mfma_bwd_rc(const LrProblem &pr, hipStream_t st, bool det, bool split_ok = true) {
     if (!bwd_uses_mfma(Dtype::BF16, pr.D, W, pr.R)) return generic_bwd<BF16, W>(pr, st, det);
+    if (!det && split_ok && bwd_split(Dtype::BF16, pr.D, W, pr.R)) {
+        if constexpr (W <= 4) {
+            if ((pr.R + 31) / 32 == 2) return split_bwd<W, 2>(pr, st);
+        }
+        return split_bwd<W, 1>(pr, st);
+    }
     if constexpr (W <= 4) {
         if ((pr.R + 31) / 32 == 2) return mfma_bwd<W, 2>(pr, st, det);
     }
@@ -1203,9 +1260,9 @@ hipError_t mfma_fwd_rc(const LrProblem &pr, hipStream_t st) {
 
 }  // namespace
 
-size_t lowrank_bwd_workspace(Dtype dt, int64_t N, int64_t D, int32_t W, int32_t R) {
-    (void)D; (void)W;
+size_t lowrank_bwd_workspace(Dtype dt, int64_t N, int64_t D, int32_t W, int32_t R, bool split_ok) {
     if (dt == Dtype::F32) return 0;
+    if (split_ok && bwd_split(dt, D, W, R)) return split_workspace(N, D, W, R);
     const size_t bytes = (size_t)N * (size_t)R * sizeof(float);
     return (bytes + 255) & ~(size_t)255;
 }
@@ -1227,9 +1284,9 @@ hipError_t lowrank_zero(float *p, int64_t n, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t lowrank_bwd(const LrProblem &p, hipStream_t s) {
+hipError_t lowrank_bwd(const LrProblem &p, hipStream_t s, bool split_ok) {
     if (p.dtype == Dtype::BF16) {
-        DSC_W_SWITCH(p.W, (mfma_bwd_rc<Wc>(p, s, false)));
+        DSC_W_SWITCH(p.W, (mfma_bwd_rc<Wc>(p, s, false, split_ok)));
     }
     DSC_W_SWITCH(p.W, (generic_bwd<F32, Wc>(p, s)));
 }

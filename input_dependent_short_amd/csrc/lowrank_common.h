@@ -27,8 +27,44 @@ struct LrParams {
 };
 
 constexpr int kBlock = 256;
+
+// Cache policy of the low-rank kernels' activation streams: bit 1 x loads,
+// 2 y stores (forward), 4 dy loads, 8 dx stores (backward); set bits take
+// the nontemporal policy.
+#ifndef DSC_LR_NT
+#define DSC_LR_NT 13
+#endif
+constexpr bool kLrNtX = (DSC_LR_NT & 1) != 0;
+constexpr bool kLrNtY = (DSC_LR_NT & 2) != 0;
+constexpr bool kLrNtG = (DSC_LR_NT & 4) != 0;
+constexpr bool kLrNtDx = (DSC_LR_NT & 8) != 0;
 constexpr int kMaxTokPerWave = 4096;                          // token walk length cap
 constexpr int kSeqWords = (kMaxTokPerWave + 128) / 32 + 2;    // sequence-start bits per wave
+
+// DPP controls (row = 16 lanes): lane i of a row reads lane i-k (shr) or
+// lane (i-k) mod 16 (ror).  With lane = token inside a 16-token step, this
+// moves the values of token t-K to token t, the first K tokens taking the
+// last K of the previous step (prev).
+template <int K>
+__device__ __forceinline__ uint32_t shift_in_row(uint32_t cur, uint32_t prev) {
+    const int rot = __builtin_amdgcn_mov_dpp((int)prev, 0x120 + K, 0xf, 0xf, true);
+    return (uint32_t)__builtin_amdgcn_update_dpp(rot, (int)cur, 0x110 + K, 0xf, 0xf, false);
+}
+
+// Shift back by a tap k (1 <= k < W, known after unrolling) of four packed
+// registers: out = cur moved k tokens later, the first k taken from prev.
+template <int W, int K = 1>
+__device__ __forceinline__ void shift_back4(int k, const uint32_t (&cur)[4], const uint32_t (&prev)[4],
+                                            uint32_t (&out)[4]) {
+    if constexpr (K < W) {
+        if (k == K) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) out[i] = shift_in_row<K>(cur[i], prev[i]);
+        } else {
+            shift_back4<W, K + 1>(k, cur, prev, out);
+        }
+    }
+}
 
 // ---------------------------------------------------------------- U operands
 

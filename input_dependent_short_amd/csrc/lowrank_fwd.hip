@@ -85,8 +85,8 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_wide(LrParams p, int64_t npairs
     const __amdgpu_buffer_rsrc_t ry = make_stream(yg + nbeg * D, (nend - nbeg) * D * 2);
 
     auto fetch_x = [&](int step, uint4 (&xd)[2]) {
-        xd[0] = buf_load16(rx, roff + (uint32_t)step * act_step);
-        xd[1] = buf_load16(rx, roff + half_step + (uint32_t)step * act_step);
+        xd[0] = buf_load16<kLrNtX>(rx, roff + (uint32_t)step * act_step);
+        xd[1] = buf_load16<kLrNtX>(rx, roff + half_step + (uint32_t)step * act_step);
     };
     auto fetch_z = [&](int step, uint4 (&zd)[RC]) {
         if constexpr (RVEC) {
@@ -213,8 +213,8 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_wide(LrParams p, int64_t npairs
             {
                 const uint4 y0 = *reinterpret_cast<const uint4 *>(yl + swz(rl, cl));
                 const uint4 y1 = *reinterpret_cast<const uint4 *>(yl + swz(8 + rl, cl));
-                buf_store16(ry, roff + (uint32_t)s * act_step, y0);
-                buf_store16(ry, roff + half_step + (uint32_t)s * act_step, y1);
+                buf_store16<kLrNtY>(ry, roff + (uint32_t)s * act_step, y0);
+                buf_store16<kLrNtY>(ry, roff + half_step + (uint32_t)s * act_step, y1);
             }
         }
     }
