@@ -302,6 +302,25 @@ class Oracle:
         ds = self.rope(dy, rot=rot, head_dim=head_dim, base=base, cu_seqlens=cu_seqlens, inverse=True)
         return self.headwise_bwd(x, w, ds, cu_seqlens=cu_seqlens, residual=residual, rows=rows)
 
+    def lowrank_rope_fwd(self, x, z, U, W, *, rot, head_dim, base=10000.0, cu_seqlens=None,
+                         residual=False, rows=None):
+        """RoPE(rho*x + conv(x)) with the low-rank filters z U: the low-rank
+        layer on the query, key and value projections (ES summary,
+        Metodología: placement right before the rotary embedding), then the
+        rotation of its first rot channels."""
+        y = self.lowrank_fwd(x, z, U, W, cu_seqlens=cu_seqlens, residual=residual, rows=rows)
+        B, T, _ = np.shape(x)
+        return self.rope(y, rot=rot, head_dim=head_dim, base=base, cu_seqlens=cu_seqlens, rows=rows,
+                         shape=(B, T))
+
+    def lowrank_rope_bwd(self, x, z, U, dy, W, *, rot, head_dim, base=10000.0, cu_seqlens=None,
+                         residual=False, rows=None, channels=None):
+        """-> (dx, dz, dU): the low-rank layer's backward on the transposed
+        rotation of dy (the rotation is orthogonal and comes last)."""
+        ds = self.rope(dy, rot=rot, head_dim=head_dim, base=base, cu_seqlens=cu_seqlens, inverse=True)
+        return self.lowrank_bwd(x, z, U, ds, W, cu_seqlens=cu_seqlens, residual=residual, rows=rows,
+                                channels=channels)
+
 
 def num_threads() -> int:
     """OpenMP threads the oracle uses."""
@@ -364,6 +383,14 @@ def rope(*a, **k):
 
 def headwise_rope_fwd(*a, **k):
     return default().headwise_rope_fwd(*a, **k)
+
+
+def lowrank_rope_fwd(*a, **k):
+    return default().lowrank_rope_fwd(*a, **k)
+
+
+def lowrank_rope_bwd(*a, **k):
+    return default().lowrank_rope_bwd(*a, **k)
 
 
 def headwise_rope_bwd(*a, **k):

@@ -555,6 +555,33 @@ def pin_rope_layer_composition(orc):
         _close(dw, _fd_grad(f, w), tol=1e-8, what="FD dw (RoPE)")
 
 
+def pin_rope_lowrank_layer_composition(orc):
+    """The low-rank layer followed by the rotation: rot = 0 leaves the layer
+    unchanged, the rotated output is the layer's output turned pair by pair
+    (checked against the rotation alone on the layer's output rows), and the
+    fused gradients dx, dz, dU equal exact central finite differences of
+    L = <g, y> (L is linear in x, in z and in U)."""
+    rng = _rng(24)
+    B, T, D, W, R, hd = 2, 5, 8, 3, 2, 4
+    cu = [0, 2, 5, 10]
+    x, z, U, g = _lr_case(rng, B, T, D, W, R)
+    _close(orc.lowrank_rope_fwd(x, z, U, W, rot=0, head_dim=hd, residual=True, cu_seqlens=cu),
+           orc.lowrank_fwd(x, z, U, W, residual=True, cu_seqlens=cu), what="rot = 0")
+    # value channels [rot, D) pass unchanged; query / key channels keep their norm per pair
+    y0 = orc.lowrank_fwd(x, z, U, W, cu_seqlens=cu)
+    y1 = orc.lowrank_rope_fwd(x, z, U, W, rot=4, head_dim=hd, base=3.0, cu_seqlens=cu)
+    _close(y1[..., 4:], y0[..., 4:], what="channels past rot")
+    _close(np.hypot(y1[..., 0:4:2], y1[..., 1:4:2]), np.hypot(y0[..., 0:4:2], y0[..., 1:4:2]), what="pair norms")
+    for res in (False, True):
+        f = lambda: float(np.sum(g * orc.lowrank_rope_fwd(x, z, U, W, rot=4, head_dim=hd, base=3.0, cu_seqlens=cu,
+                                                           residual=res)))
+        dx, dz, dU = orc.lowrank_rope_bwd(x, z, U, g, W, rot=4, head_dim=hd, base=3.0, cu_seqlens=cu,
+                                          residual=res)
+        _close(dx, _fd_grad(f, x), tol=1e-8, what="FD dx (low-rank, RoPE)")
+        _close(dz, _fd_grad(f, z), tol=1e-8, what="FD dz (low-rank, RoPE)")
+        _close(dU, _fd_grad(f, U), tol=1e-8, what="FD dU (low-rank, RoPE)")
+
+
 def pin_rope_decode_reproduces_forward(orc):
     """Decoding with the rotation at each token's position, after a packed
     prefill of sequences of 1..6 tokens, gives the fused forward over the
