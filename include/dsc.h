@@ -217,6 +217,41 @@ DSC_API dsc_status dsc_lowrank_bwd(void *stream, int dtype, int64_t B, int64_t T
                            void *dz, float *dU, void *workspace, size_t workspace_bytes);
 
 /*
+ * Low-rank forward followed by the rotary embedding of the query and key
+ * channels: the fused low-rank layer of the Q, K and V projections right
+ * before the rotary embedding (Methodology, "placement"; the rotation of
+ * RoFormer, Section 3.4.2) in one pass:
+ *   s[n,d] = the low-rank forward above (dsc_lowrank_fwd),
+ *   y[n,d] = s[n,d] turned pair by pair at token n's position inside its own
+ *            sequence for d < rot, exactly as dsc_headwise_rope_fwd turns it;
+ *   y[n,d] = s[n,d] for d >= rot.
+ * The rotation acts on the fp32 result before its one rounding to the dtype.
+ *   rot, head_dim, table, max_pos  as dsc_headwise_rope_fwd (rot = 0 is
+ *   dsc_lowrank_fwd).  Other arguments and rules as dsc_lowrank_fwd.
+ */
+DSC_API dsc_status dsc_lowrank_rope_fwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                                        int32_t R, const void *x, const void *z, const void *U,
+                                        const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, int64_t rot,
+                                        int32_t head_dim, const float *table, int64_t max_pos, void *y);
+
+/*
+ * Backward of dsc_lowrank_rope_fwd for L = <dy, y>: the layer's output
+ * gradient is dy turned back (ds = R^T dy, the transposed rotation), and dx,
+ * dz and dU are those of dsc_lowrank_bwd with ds in place of dy.  For DSC_BF16
+ * shapes served by the matrix-core backward, ds is formed on chip and rounded
+ * to bf16 before it enters the products (like every matrix-core operand);
+ * elsewhere it stays fp32.  The workspace that dsc_lowrank_bwd_workspace_size
+ * reports suffices.  rot = 0 is dsc_lowrank_bwd.  Other arguments, results
+ * and errors as dsc_lowrank_rope_fwd and dsc_lowrank_bwd (dz and dU summed
+ * with fp32 atomics).
+ */
+DSC_API dsc_status dsc_lowrank_rope_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                                        int32_t R, const void *x, const void *z, const void *U, const void *dy,
+                                        const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, int64_t rot,
+                                        int32_t head_dim, const float *table, int64_t max_pos, void *dx,
+                                        void *dz, float *dU, void *workspace, size_t workspace_bytes);
+
+/*
  * The low-rank backward above for callers that cannot allocate device
  * memory (code under stream capture, tight serving loops, harnesses that
  * forbid allocation): no workspace argument; the fp32 dz accumulator lives

@@ -60,12 +60,16 @@ def lib() -> ctypes.CDLL:
         L.dsc_headwise_rope_fwd.argtypes = [p, i, i64, i64, i64, i32, i32, p, p, p, i32, i32, i64, i32, p, i64, p]
         L.dsc_headwise_rope_bwd.argtypes = [p, i, i64, i64, i64, i32, i32, p, p, p, p, i32, i32, i64, i32, p, i64,
                                             p, p]
+        L.dsc_lowrank_rope_fwd.argtypes = [p, i, i64, i64, i64, i32, i32, p, p, p, p, i32, i32, i64, i32, p, i64, p]
+        L.dsc_lowrank_rope_bwd.argtypes = [p, i, i64, i64, i64, i32, i32, p, p, p, p, p, i32, i32, i64, i32, p, i64,
+                                           p, p, p, p, ctypes.c_size_t]
         L.dsc_bench_stream.argtypes = [p, p, i64, p, i64, i32, i32, i32, i32, i64]
         for f in ("dsc_bench_stream", "dsc_lowrank_bwd_noalloc", "dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd",
                   "dsc_lowrank_bwd_deterministic", "dsc_static_bwd_deterministic",
                   "dsc_static_fwd", "dsc_static_bwd", "dsc_headwise_decode", "dsc_lowrank_decode",
                   "dsc_state_from_prefill", "dsc_rope_table", "dsc_headwise_rope_fwd",
-                  "dsc_headwise_rope_bwd", "dsc_headwise_rope_decode", "dsc_abi_version"):
+                  "dsc_headwise_rope_bwd", "dsc_headwise_rope_decode", "dsc_lowrank_rope_fwd",
+                  "dsc_lowrank_rope_bwd", "dsc_abi_version"):
             getattr(L, f).restype = ctypes.c_int
         L.dsc_status_string.argtypes = [i]
         L.dsc_status_string.restype = ctypes.c_char_p
@@ -186,6 +190,30 @@ def dsc_lowrank_fwd(x, z, U, y, *, W, cu_seqlens=None, residual=False, stream=No
     cu, ns = _seq(cu_seqlens)
     _check(lib().dsc_lowrank_fwd(_stream(stream), _dtype_code(x), B, T, D, W, R, _ptr(x), _ptr(z),
                                  _ptr(U), cu, ns, int(bool(residual)), _ptr(y)))
+
+
+def dsc_lowrank_rope_fwd(x, z, U, y, *, W, rot, head_dim, table, cu_seqlens=None, residual=False,
+                         stream=None) -> None:
+    """y = rotary embedding (channels [0, rot), heads of head_dim) of the low-rank layer's output."""
+    B, T, D = x.shape
+    R = z.shape[2]
+    cu, ns = _seq(cu_seqlens)
+    tp, max_pos = _table(table, head_dim)
+    _check(lib().dsc_lowrank_rope_fwd(_stream(stream), _dtype_code(x), B, T, D, W, R, _ptr(x), _ptr(z),
+                                      _ptr(U), cu, ns, int(bool(residual)), int(rot), int(head_dim), tp, max_pos,
+                                      _ptr(y)))
+
+
+def dsc_lowrank_rope_bwd(x, z, U, dy, dx, dz, dU, workspace=None, *, W, rot, head_dim, table, cu_seqlens=None,
+                         residual=False, stream=None) -> None:
+    B, T, D = x.shape
+    R = z.shape[2]
+    cu, ns = _seq(cu_seqlens)
+    tp, max_pos = _table(table, head_dim)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().dsc_lowrank_rope_bwd(_stream(stream), _dtype_code(x), B, T, D, W, R, _ptr(x), _ptr(z),
+                                      _ptr(U), _ptr(dy), cu, ns, int(bool(residual)), int(rot), int(head_dim), tp,
+                                      max_pos, _ptr(dx), _ptr(dz), _ptr(dU), _ptr(workspace), ws_bytes))
 
 
 def dsc_lowrank_bwd_workspace_size(dtype: torch.dtype, B: int, T: int, D: int, W: int, R: int) -> int:

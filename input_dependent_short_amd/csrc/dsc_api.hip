@@ -234,6 +234,29 @@ dsc_status dsc_lowrank_fwd(void *stream, int dtype, int64_t B, int64_t T, int64_
     return launched(dsc::lowrank_fwd(p, (hipStream_t)stream), "dsc_lowrank_fwd launch");
 }
 
+dsc_status dsc_lowrank_rope_fwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                                int32_t R, const void *x, const void *z, const void *U,
+                                const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, int64_t rot,
+                                int32_t head_dim, const float *table, int64_t max_pos, void *y) {
+    DSC_TRY(check_common(dtype, B, T, D, W, cu_seqlens, n_seqs, residual));
+    if (R < 1 || R > 128) return fail(DSC_ERR_SHAPE, "R = %d must be in 1..128", R);
+    DSC_TRY(check_rope(dtype, B, T, D, cu_seqlens, rot, head_dim, table, max_pos));
+    if (B * T == 0) return ok();
+    if (!x || !z || !U || !y) return fail(DSC_ERR_NULL, "x, z, U and y are required");
+    if (!aligned16(x) || !aligned16(z) || !aligned16(U) || !aligned16(y))
+        return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
+    const size_t es = esize(dtype), N = (size_t)(B * T);
+    const Range in[] = {rng("x", x, N * D * es), rng("z", z, N * R * es), rng("U", U, (size_t)R * D * W * es),
+                        rng("cu_seqlens", cu_seqlens, cu_seqlens ? 4u * (n_seqs + 1) : 0),
+                        rng("table", table, rot ? (size_t)max_pos * head_dim * 4u : 0)};
+    const Range out[] = {rng("y", y, N * D * es)};
+    DSC_TRY(check_alias(in, 5, out, 1));
+    dsc::LrProblem p{dt, B * T, T, D, W, R, x, z, U, nullptr, y, nullptr, nullptr, nullptr, nullptr,
+                     cu_seqlens, n_seqs, residual, rot, head_dim, table, max_pos};
+    return launched(dsc::lowrank_rope_fwd(p, (hipStream_t)stream), "dsc_lowrank_rope_fwd launch");
+}
+
 size_t dsc_lowrank_bwd_workspace_size(int dtype, int64_t B, int64_t T, int64_t D, int32_t W, int32_t R) {
     if (check_common(dtype, B, T, D, W, nullptr, 0, 0) != DSC_SUCCESS || R < 1 || R > 128) return 0;
     return dsc::lowrank_bwd_workspace(dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32, B * T, D, W, R);
@@ -241,15 +264,27 @@ size_t dsc_lowrank_bwd_workspace_size(int dtype, int64_t B, int64_t T, int64_t D
 
 namespace {
 
-// Validation and launch shared by the two low-rank backward entry points.
+// The rotary embedding that follows the layer (dsc_lowrank_rope_bwd).
+struct RopeArgs {
+    int64_t rot;
+    int32_t head_dim;
+    const float *table;
+    int64_t max_pos;
+};
+
+// Validation and launch shared by the low-rank backward entry points.
 // noalloc: no workspace argument; the accumulator is the device's built-in
 // scratch, whose address is taken only after every other check passed.
+// rope: the layer followed by the rotary embedding (the fused backward, never
+// the split one, so its workspace is at most dsc_lowrank_bwd_workspace_size).
 dsc_status lowrank_bwd_call(bool det, const char *name, void *stream, int dtype, int64_t B, int64_t T, int64_t D,
                             int32_t W, int32_t R, const void *x, const void *z, const void *U, const void *dy,
                             const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, void *dx, void *dz,
-                            float *dU, void *workspace, size_t workspace_bytes, bool noalloc = false) {
+                            float *dU, void *workspace, size_t workspace_bytes, bool noalloc = false,
+                            const RopeArgs *rope = nullptr) {
     DSC_TRY(check_common(dtype, B, T, D, W, cu_seqlens, n_seqs, residual));
     if (R < 1 || R > 128) return fail(DSC_ERR_SHAPE, "R = %d must be in 1..128", R);
+    if (rope) DSC_TRY(check_rope(dtype, B, T, D, cu_seqlens, rope->rot, rope->head_dim, rope->table, rope->max_pos));
     if (B * T == 0) {  // empty batch: dU is a sum over no tokens, zero; nothing else has elements
         if (!dU) return fail(DSC_ERR_NULL, "dU is required");
         if (!aligned16(dU)) return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
@@ -262,7 +297,7 @@ dsc_status lowrank_bwd_call(bool det, const char *name, void *stream, int dtype,
         return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
     const dsc::Dtype dt = dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32;
     const size_t need = det ? dsc::lowrank_bwd_det_workspace(dt, B * T, D, W, R)
-                            : dsc::lowrank_bwd_workspace(dt, B * T, D, W, R, !noalloc);
+                            : dsc::lowrank_bwd_workspace(dt, B * T, D, W, R, !noalloc && !rope);
     if (noalloc) {
         if (need > (size_t)dsc::kNoallocScratchFloats * sizeof(float))
             return fail(DSC_ERR_WORKSPACE,
@@ -278,11 +313,13 @@ dsc_status lowrank_bwd_call(bool det, const char *name, void *stream, int dtype,
     const size_t es = esize(dtype), N = (size_t)(B * T);
     const Range in[] = {rng("x", x, N * D * es), rng("z", z, N * R * es), rng("U", U, (size_t)R * D * W * es),
                         rng("dy", dy, N * D * es),
-                        rng("cu_seqlens", cu_seqlens, cu_seqlens ? 4u * (n_seqs + 1) : 0)};
+                        rng("cu_seqlens", cu_seqlens, cu_seqlens ? 4u * (n_seqs + 1) : 0),
+                        rng("table", rope ? rope->table : nullptr,
+                            rope && rope->rot ? (size_t)rope->max_pos * rope->head_dim * 4u : 0)};
     const Range out[] = {rng("dx", dx, N * D * es), rng("dz", dz, N * R * es),
                          rng("dU", dU, (size_t)R * D * W * 4),
                          rng("workspace", workspace, need && !noalloc ? need : 0)};
-    DSC_TRY(check_alias(in, 5, out, 4));
+    DSC_TRY(check_alias(in, 6, out, 4));
     if (noalloc && need > 0) {
         float *scratch = nullptr;
         const hipError_t e = dsc::noalloc_scratch(&scratch);
@@ -291,6 +328,13 @@ dsc_status lowrank_bwd_call(bool det, const char *name, void *stream, int dtype,
     }
     float *acc = need ? static_cast<float *>(workspace) : det ? nullptr : static_cast<float *>(dz);
     dsc::LrProblem p{dt, B * T, T, D, W, R, x, z, U, dy, nullptr, dx, dz, dU, acc, cu_seqlens, n_seqs, residual};
+    if (rope) {
+        p.rot = rope->rot;
+        p.hd = rope->head_dim;
+        p.rope = rope->table;
+        p.max_pos = rope->max_pos;
+        return launched(dsc::lowrank_rope_bwd(p, (hipStream_t)stream), name);
+    }
     return launched(det ? dsc::lowrank_bwd_det(p, (hipStream_t)stream)
                         : dsc::lowrank_bwd(p, (hipStream_t)stream, !noalloc),
                     name);
@@ -304,6 +348,16 @@ dsc_status dsc_lowrank_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_
                            void *dz, float *dU, void *workspace, size_t workspace_bytes) {
     return lowrank_bwd_call(false, "dsc_lowrank_bwd launch", stream, dtype, B, T, D, W, R, x, z, U, dy, cu_seqlens,
                             n_seqs, residual, dx, dz, dU, workspace, workspace_bytes);
+}
+
+dsc_status dsc_lowrank_rope_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                                int32_t R, const void *x, const void *z, const void *U, const void *dy,
+                                const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, int64_t rot,
+                                int32_t head_dim, const float *table, int64_t max_pos, void *dx, void *dz,
+                                float *dU, void *workspace, size_t workspace_bytes) {
+    const RopeArgs rope{rot, head_dim, table, max_pos};
+    return lowrank_bwd_call(false, "dsc_lowrank_rope_bwd launch", stream, dtype, B, T, D, W, R, x, z, U, dy,
+                            cu_seqlens, n_seqs, residual, dx, dz, dU, workspace, workspace_bytes, false, &rope);
 }
 
 dsc_status dsc_lowrank_bwd_noalloc(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,

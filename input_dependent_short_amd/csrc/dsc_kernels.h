@@ -41,6 +41,12 @@ struct LrProblem {
     const int32_t *cu;
     int32_t n_seqs;
     int32_t residual;
+    // Rotary embedding after the layer (lowrank_rope_* only): channels
+    // [0, rot) in heads of hd, cos / sin table (max_pos, hd/2, 2).
+    int64_t rot = 0;
+    int32_t hd = 0;
+    const float *rope = nullptr;
+    int64_t max_pos = 0;
 };
 
 // Static short convolution: one filter per channel, the same at every token.
@@ -109,6 +115,11 @@ hipError_t lowrank_fwd(const LrProblem &p, hipStream_t s);
 // the other kernels, which then run instead.
 hipError_t lowrank_fwd_wide(const LrProblem &p, hipStream_t s, bool *used);
 hipError_t lowrank_bwd(const LrProblem &p, hipStream_t s, bool split_ok = true);
+// The low-rank layer followed by the rotary embedding of channels [0, p.rot)
+// (the backward turns dy back first); the backward's workspace is that of
+// lowrank_bwd_workspace(..., split_ok = false).
+hipError_t lowrank_rope_fwd(const LrProblem &p, hipStream_t s);
+hipError_t lowrank_rope_bwd(const LrProblem &p, hipStream_t s);
 // Reproducible backward: dz and dU summed in one fixed order (dz_acc = its
 // workspace of lowrank_bwd_det_workspace bytes, may be null when that is 0).
 size_t lowrank_bwd_det_workspace(Dtype dt, int64_t N, int64_t D, int32_t W, int32_t R);

@@ -35,8 +35,9 @@ namespace {
 
 // ---------------------------------------------------------------- generic
 
-// One thread per (token, 16-byte channel chunk).
-template <class E, int W>
+// One thread per (token, 16-byte channel chunk).  ROPE: channels below p.rot
+// of the result are then turned at the token's position in its sequence.
+template <class E, int W, bool ROPE = false>
 __global__ __launch_bounds__(kBlock) void lr_fwd_generic(LrParams p) {
     using S = typename E::store_t;
     constexpr int VEC = E::kVec;
@@ -73,11 +74,20 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_generic(LrParams p) {
             for (int c = 0; c < VEC; ++c) acc[c] = __builtin_fmaf(wv[c * W + k], xk[c], acc[c]);
         }
     }
+    if constexpr (ROPE) {
+        if (d0 < p.rot) {
+            float cs[VEC];
+            rope_cs<VEC>(p, n - s, d0, cs);
+            turn<VEC, false>(acc, cs);
+        }
+    }
     Vec16<E>::store(static_cast<S *>(p.y) + n * p.D + d0, acc);
 }
 
 // SUMS: also add this item's dz and dU terms with atomics (else dx only).
-template <class E, int W, bool SUMS = true>
+// ROPE: dy's channels below p.rot are turned back first (each token at its
+// own position), in fp32.
+template <class E, int W, bool SUMS = true, bool ROPE = false>
 __global__ __launch_bounds__(kBlock) void lr_bwd_generic(LrParams p) {
     using S = typename E::store_t;
     constexpr int VEC = E::kVec;
@@ -93,10 +103,20 @@ __global__ __launch_bounds__(kBlock) void lr_bwd_generic(LrParams p) {
     const int64_t DW = p.D * W;
     int64_t s, e;
     p.seq.find(m, s, e);
+    auto turn_back = [&](float (&v)[VEC], int64_t t) {
+        if constexpr (ROPE) {
+            if (d0 < p.rot) {
+                float cs[VEC];
+                rope_cs<VEC>(p, t - s, d0, cs);
+                turn<VEC, true>(v, cs);
+            }
+        }
+    };
 
     // dx: filters of the W tokens m..m+W-1 that read x[m]
     float gm[VEC], acc[VEC];
     Vec16<E>::load(g + m * p.D + d0, gm);
+    turn_back(gm, m);
 #pragma unroll
     for (int c = 0; c < VEC; ++c) acc[c] = p.rho * gm[c];
 #pragma unroll
@@ -115,6 +135,7 @@ __global__ __launch_bounds__(kBlock) void lr_bwd_generic(LrParams p) {
             }
             float gt[VEC];
             Vec16<E>::load(g + t * p.D + d0, gt);
+            turn_back(gt, t);
 #pragma unroll
             for (int c = 0; c < VEC; ++c) acc[c] = __builtin_fmaf(wk[c], gt[c], acc[c]);
         }
@@ -478,8 +499,11 @@ constexpr bool bwd_exact_walk(int H, bool RVEC) { return H == 2 && RVEC; }
 
 // DZ false: dx and dU only (dz is then computed by the kernels of
 // lowrank_dz.hip); the dz products, their LDS exchange and its barriers and
-// atomics are left out.
-template <int W, int RC, int P, bool RVEC, int H, bool DZ = true>
+// atomics are left out.  ROPE: the layer is followed by the rotary embedding
+// of channels below p.rot, so dy is first turned back (the transposed
+// rotation, at each token's position in its sequence) as it enters the
+// look-ahead ring, and rounded to bf16 like the other matrix-core operands.
+template <int W, int RC, int P, bool RVEC, int H, bool DZ = true, bool ROPE = false>
 __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void lr_bwd_mfma(LrParams p, int64_t nslices,
                                                                                          int64_t tok_per_half) {
     using L = BwdLds<W, RC, H>;
@@ -543,6 +567,12 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
 
     StartBits<kSeqWords> starts;
     starts.build(seq_words[wid], p.seq, N, nbeg - 32, lane);
+    SeqPos sp{0};
+    if constexpr (ROPE) {
+        int64_t s_, e_;
+        p.seq.find(nbeg < N ? nbeg : N - 1, s_, e_);
+        sp.start = s_;
+    }
 
     // ---- streams over the block's rows (x, dy and z up to N, dx up to nend):
     // lane offset inside a step plus the step's offset
@@ -614,6 +644,26 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
     }
 #pragma unroll
     for (int j = 0; j < P; ++j) gr[j] = fetch_g(j);
+    // dy of the 16 tokens from nstep turned back at their positions (steps in order)
+    auto turn_g = [&](uint4 &v, int64_t nstep) {
+        if constexpr (ROPE) {
+            const int64_t pos = sp.pos_and_advance(starts, nstep, tok);
+            if (chan_ok && cbase < p.rot) {
+                float f[8], cs[8];
+                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int i2 = 0; i2 < 4; ++i2) {
+                    f[2 * i2] = bf16_lo(w4[i2]);
+                    f[2 * i2 + 1] = bf16_hi(w4[i2]);
+                }
+                rope_cs<8>(p, pos, cbase, cs);
+                turn<8, true>(f, cs);
+                v = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                               pack_bf16x2(f[6], f[7]));
+            }
+        }
+    };
+    turn_g(gr[0], nbeg);
     {
         uint4 z0[RC];
         fetch_z(0, z0);
@@ -640,6 +690,7 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
             const int64_t nstep = nbeg + 16 * s;
             const int64_t n = nstep + tok;
 
+            turn_g(gr[nxt], nstep + 16);     // the next step's dy, used from this step on
             write_z((i + 1) & 3, zr[nxt]);  // the wave's own LDS ring
             // other lanes read these rows below: keep the compiler from moving
             // the reads above the writes (the wave's LDS operations execute in order)
@@ -1008,11 +1059,11 @@ __global__ __launch_bounds__(kBlock) void lr_du_direct(LrParams p) {
     p.dU[item] = total;
 }
 
-template <class E, int W>
+template <class E, int W, bool ROPE = false>
 hipError_t generic_fwd(const LrProblem &pr, hipStream_t st) {
     LrParams p = make_params<E>(pr);
     const int64_t b = nblocks(p.N * p.nchunks);
-    if (b) hipLaunchKernelGGL((lr_fwd_generic<E, W>), dim3((unsigned)b), dim3(kBlock), 0, st, p);
+    if (b) hipLaunchKernelGGL((lr_fwd_generic<E, W, ROPE>), dim3((unsigned)b), dim3(kBlock), 0, st, p);
     return hipGetLastError();
 }
 
@@ -1027,16 +1078,18 @@ hipError_t generic_bwd_det(const LrProblem &pr, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <class E, int W>
+template <class E, int W, bool ROPE = false>
 hipError_t generic_bwd(const LrProblem &pr, hipStream_t st, bool det = false) {
-    if (det) return generic_bwd_det<E, W>(pr, st);
+    if constexpr (!ROPE) {
+        if (det) return generic_bwd_det<E, W>(pr, st);
+    }
     LrParams p = make_params<E>(pr);
     const int64_t nU = (int64_t)p.R * p.D * W;
     const int64_t nz = p.N * p.R;
     hipLaunchKernelGGL(fill_zero_f32, dim3((unsigned)nblocks(nU)), dim3(kBlock), 0, st, p.dU, nU);
     hipLaunchKernelGGL(fill_zero_f32, dim3((unsigned)nblocks(nz)), dim3(kBlock), 0, st, p.dzacc, nz);
     const int64_t b = nblocks(p.N * p.nchunks);
-    if (b) hipLaunchKernelGGL((lr_bwd_generic<E, W>), dim3((unsigned)b), dim3(kBlock), 0, st, p);
+    if (b) hipLaunchKernelGGL((lr_bwd_generic<E, W, true, ROPE>), dim3((unsigned)b), dim3(kBlock), 0, st, p);
     if constexpr (sizeof(typename E::store_t) == 2)
         hipLaunchKernelGGL(cast_f32_bf16, dim3((unsigned)nblocks(nz)), dim3(kBlock), 0, st, p.dzacc,
                            static_cast<uint16_t *>(p.dz), nz);
@@ -1116,7 +1169,7 @@ constexpr int64_t kDetSlots = 256;
 
 size_t det_dz_floats(const BwdPlan &pl, int64_t N, int R) { return (((size_t)pl.ngroups * N * R + 3) / 4) * 4; }
 
-template <int W, int RC>
+template <int W, int RC, bool ROPE = false>
 hipError_t mfma_bwd(const LrProblem &pr, hipStream_t st, bool det) {
     LrParams p = make_params<BF16>(pr);
     const int64_t nU = (int64_t)p.R * p.D * W;
@@ -1125,9 +1178,9 @@ hipError_t mfma_bwd(const LrProblem &pr, hipStream_t st, bool det) {
     int64_t slots = kDetSlots;
     if (!det) {
         static const int bpc_vec = blocks_per_cu(
-            reinterpret_cast<const void *>(&lr_bwd_mfma<W, RC, kBwdRing, true, H>), kBlock * H);
+            reinterpret_cast<const void *>(&lr_bwd_mfma<W, RC, kBwdRing, true, H, true, ROPE>), kBlock * H);
         static const int bpc_gather = blocks_per_cu(
-            reinterpret_cast<const void *>(&lr_bwd_mfma<W, RC, kBwdRing, false, H>), kBlock * H);
+            reinterpret_cast<const void *>(&lr_bwd_mfma<W, RC, kBwdRing, false, H, true, ROPE>), kBlock * H);
         slots = (int64_t)device_cus() * (p.R % 8 == 0 ? bpc_vec : bpc_gather);
     }
     const BwdPlan pl = bwd_plan(p.N, p.D, W, p.R, slots);
@@ -1147,9 +1200,11 @@ hipError_t mfma_bwd(const LrProblem &pr, hipStream_t st, bool det) {
     const dim3 grid((unsigned)(pl.tchunks * pl.ngroups));
     const int64_t nslices = (p.D + 31) / 32;
     if (p.R % 8 == 0)
-        hipLaunchKernelGGL((lr_bwd_mfma<W, RC, kBwdRing, true, H>), grid, dim3(kBlock * H), 0, st, p, nslices, pl.tph);
+        hipLaunchKernelGGL((lr_bwd_mfma<W, RC, kBwdRing, true, H, true, ROPE>), grid, dim3(kBlock * H), 0, st, p,
+                           nslices, pl.tph);
     else
-        hipLaunchKernelGGL((lr_bwd_mfma<W, RC, kBwdRing, false, H>), grid, dim3(kBlock * H), 0, st, p, nslices, pl.tph);
+        hipLaunchKernelGGL((lr_bwd_mfma<W, RC, kBwdRing, false, H, true, ROPE>), grid, dim3(kBlock * H), 0, st, p,
+                           nslices, pl.tph);
     if (det) {
         hipLaunchKernelGGL(sum_parts<uint16_t>, dim3((unsigned)nblocks(nz)), dim3(kBlock), 0, st, dz_sum,
                            pl.ngroups, nz, static_cast<uint16_t *>(pr.dz), nz);
@@ -1245,6 +1300,30 @@ hipError_t mfma_fwd_rc(const LrProblem &pr, hipStream_t st) {
     }
 }
 
+// The layer followed by the rotary embedding: the wide forward (R <= 64) or
+// the generic one; the fused matrix-core backward (dz in the same kernel, no
+// split) where it runs, else the generic one.
+template <int W>
+hipError_t rope_fwd_w(const LrProblem &pr, hipStream_t st) {
+    if (pr.dtype == Dtype::BF16) {
+        bool used = false;
+        const hipError_t e = lowrank_fwd_wide(pr, st, &used);
+        if (used) return e;
+        return generic_fwd<BF16, W, true>(pr, st);
+    }
+    return generic_fwd<F32, W, true>(pr, st);
+}
+
+template <int W>
+hipError_t rope_bwd_w(const LrProblem &pr, hipStream_t st) {
+    if (pr.dtype == Dtype::F32) return generic_bwd<F32, W, true>(pr, st);
+    if (!bwd_uses_mfma(Dtype::BF16, pr.D, W, pr.R)) return generic_bwd<BF16, W, true>(pr, st);
+    if constexpr (W <= 4) {
+        if ((pr.R + 31) / 32 == 2) return mfma_bwd<W, 2, true>(pr, st, false);
+    }
+    return mfma_bwd<W, 1, true>(pr, st, false);
+}
+
 #define DSC_W_SWITCH(W_, CALL)             \
     switch (W_) {                          \
         case 1: { constexpr int Wc = 1; return CALL; } \
@@ -1296,6 +1375,16 @@ size_t lowrank_bwd_det_workspace(Dtype dt, int64_t N, int64_t D, int32_t W, int3
     const BwdPlan pl = bwd_plan(N, D, W, R, kDetSlots);
     const size_t bytes = (det_dz_floats(pl, N, R) + (size_t)pl.tchunks * R * D * W) * sizeof(float);
     return (bytes + 255) & ~(size_t)255;
+}
+
+hipError_t lowrank_rope_fwd(const LrProblem &p, hipStream_t s) {
+    if (p.rot <= 0) return lowrank_fwd(p, s);
+    DSC_W_SWITCH(p.W, rope_fwd_w<Wc>(p, s));
+}
+
+hipError_t lowrank_rope_bwd(const LrProblem &p, hipStream_t s) {
+    if (p.rot <= 0) return lowrank_bwd(p, s, false);
+    DSC_W_SWITCH(p.W, rope_bwd_w<Wc>(p, s));
 }
 
 hipError_t lowrank_bwd_det(const LrProblem &p, hipStream_t s) {

@@ -24,6 +24,10 @@ struct LrParams {
     // group g at dzacc + g*dz_gstride and its dU of token chunk c at
     // dU + c*du_cstride.  Both are 0 when the partials share one accumulator.
     int64_t dz_gstride, du_cstride;
+    // rotary embedding (ROPE kernels only): channels [0, rot), heads of hd,
+    // table (npos, hd/2, 2) of cos, sin
+    const float *rope;
+    int32_t rot, hd, npos;
 };
 
 constexpr int kBlock = 256;
@@ -64,6 +68,33 @@ __device__ __forceinline__ void shift_back4(int k, const uint32_t (&cur)[4], con
             shift_back4<W, K + 1>(k, cur, prev, out);
         }
     }
+}
+
+// Position of a lane's token inside its sequence, for a walk in 16-token
+// steps taken in order.  `start` is the first token of the sequence in
+// effect before the step (wave-uniform); the step's own starts come from the
+// walk's bitmap.  pos_and_advance returns the lane's position at step
+// token nstep + tok and moves `start` past the step.
+struct SeqPos {
+    int64_t start;
+    template <int kWords>
+    __device__ __forceinline__ int64_t pos_and_advance(const StartBits<kWords> &bits, int64_t nstep, int tok) {
+        const uint32_t w16 = __builtin_amdgcn_readfirstlane(bits.window(nstep)) & 0xffffu;
+        const uint32_t m = w16 & ((2u << tok) - 1u);  // starts among tokens nstep .. nstep + tok
+        const int64_t s = m ? nstep + (31 - __builtin_clz(m)) : start;
+        if (w16) start = nstep + (31 - __builtin_clz(w16));
+        return nstep + tok - s;
+    }
+};
+
+// cos, sin of the VEC/2 pairs of VEC channels starting at channel ch (< rot,
+// a multiple of VEC, so all in one head) of a token at position pos (clamped
+// into the table: positions past it belong to tokens past the walk, whose
+// values are never stored).
+template <int VEC>
+__device__ __forceinline__ void rope_cs(const LrParams &p, int64_t pos, int64_t ch, float (&cs)[VEC]) {
+    const int64_t m = pos < 0 ? 0 : (pos >= p.npos ? p.npos - 1 : pos);
+    load_turn<VEC>(p.rope + m * p.hd + (int32_t)(ch % p.hd), cs);
 }
 
 // ---------------------------------------------------------------- U operands
@@ -137,6 +168,10 @@ LrParams make_params(const LrProblem &pr) {
     p.nchunks = pr.D / E::kVec;
     p.dz_gstride = 0;
     p.du_cstride = 0;
+    p.rope = pr.rope;
+    p.rot = (int32_t)pr.rot;
+    p.hd = pr.hd;
+    p.npos = (int32_t)pr.max_pos;
     return p;
 }
 

@@ -35,7 +35,11 @@ struct FwdWideLds {
 // and 8 chunks of one row both spread over distinct banks.
 __device__ __forceinline__ int swz(int r, int c) { return r * FwdWideLds::kRow + 16 * (c ^ ((r >> 1) & 7)); }
 
-template <int W, int RC, int PF, bool RVEC>
+// ROPE: the output's channels below p.rot are then turned pair by pair at
+// the token's position in its sequence ("RoFormer: Enhanced Transformer with
+// Rotary Position Embedding", Su et al., Section 3.4.2), on the fp32 result
+// before it is rounded.
+template <int W, int RC, int PF, bool RVEC, bool ROPE = false>
 __global__ __launch_bounds__(kBlock) void lr_fwd_wide(LrParams p, int64_t npairs, int64_t tok_per_wave) {
     using L = FwdWideLds;
     static_assert(PF % 2 == 0, "x ring slots alternate with the step parity");
@@ -123,6 +127,12 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_wide(LrParams p, int64_t npairs
 
     StartBits<kSeqWords> starts;
     starts.build(seq_words[wid], p.seq, p.N, nbeg - 32, lane);
+    SeqPos sp{0};
+    if constexpr (ROPE) {
+        int64_t s_, e_;
+        p.seq.find(nbeg < p.N ? nbeg : p.N - 1, s_, e_);
+        sp.start = s_;
+    }
 
     // the previous step's tail (tokens nbeg-7 .. nbeg-1) into slot 1 and the mirror
     {
@@ -156,6 +166,8 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_wide(LrParams p, int64_t npairs
             uint32_t win = 0;
             if constexpr (W > 1) win = __builtin_amdgcn_readfirstlane(starts.window(nbeg + 16 * (int64_t)s - (W - 1)));
             const bool masked = (win & (((1u << (W + 14)) - 1u) << 1)) != 0u;  // wave-uniform
+            int64_t pos = 0;
+            if constexpr (ROPE) pos = sp.pos_and_advance(starts, nbeg + 16 * (int64_t)s, tok);
 
 #pragma unroll
             for (int sl = 0; sl < 2; ++sl) {
@@ -201,6 +213,14 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_wide(LrParams p, int64_t npairs
                     }
                     out[c] = a;
                 }
+                if constexpr (ROPE) {
+                    const int64_t ch0 = c0 + 32 * sl + 8 * q;  // the lane's 8 channels: 4 pairs of one head
+                    if (ch0 < p.rot) {
+                        float cs[8];
+                        rope_cs<8>(p, pos, ch0, cs);
+                        turn<8, false>(out, cs);
+                    }
+                }
                 uint4 yv;
                 yv.x = pack_bf16x2(out[0], out[1]);
                 yv.y = pack_bf16x2(out[2], out[3]);
@@ -231,15 +251,17 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_wide(LrParams p, int64_t npairs
 template <int RC>
 constexpr int wide_pf() { return RC == 1 ? DSC_LR_FWD_WIDE_PF1 : DSC_LR_FWD_WIDE_PF2; }
 
-template <int W, int RC>
+template <int W, int RC, bool ROPE>
 hipError_t mfma_fwd_wide(const LrProblem &pr, hipStream_t st) {
     constexpr int PF = wide_pf<RC>();
     LrParams p = make_params<BF16>(pr);
     const int64_t npairs = (p.D + 63) / 64;
     const int64_t cap = walk_cap(p.D, 16 * PF, 16 * (2 * PF + 2));
     if (cap < 16 * PF) return hipErrorNotSupported;  // the caller falls back
-    static const int bpc_vec = blocks_per_cu(reinterpret_cast<const void *>(&lr_fwd_wide<W, RC, PF, true>), kBlock);
-    static const int bpc_gather = blocks_per_cu(reinterpret_cast<const void *>(&lr_fwd_wide<W, RC, PF, false>), kBlock);
+    static const int bpc_vec =
+        blocks_per_cu(reinterpret_cast<const void *>(&lr_fwd_wide<W, RC, PF, true, ROPE>), kBlock);
+    static const int bpc_gather =
+        blocks_per_cu(reinterpret_cast<const void *>(&lr_fwd_wide<W, RC, PF, false, ROPE>), kBlock);
     const bool rvec = p.R % 8 == 0;
     const int64_t slots = (int64_t)device_cus() * (rvec ? bpc_vec : bpc_gather) * (kBlock / kWave);
     const int64_t tpw = walk_length(p.N, npairs, slots, cap, 16 * PF, kWaveFixedTokens);
@@ -247,9 +269,11 @@ hipError_t mfma_fwd_wide(const LrProblem &pr, hipStream_t st) {
     const int64_t b = (waves + 3) / 4;
     if (b) {
         if (rvec)
-            hipLaunchKernelGGL((lr_fwd_wide<W, RC, PF, true>), dim3((unsigned)b), dim3(kBlock), 0, st, p, npairs, tpw);
+            hipLaunchKernelGGL((lr_fwd_wide<W, RC, PF, true, ROPE>), dim3((unsigned)b), dim3(kBlock), 0, st, p, npairs,
+                               tpw);
         else
-            hipLaunchKernelGGL((lr_fwd_wide<W, RC, PF, false>), dim3((unsigned)b), dim3(kBlock), 0, st, p, npairs, tpw);
+            hipLaunchKernelGGL((lr_fwd_wide<W, RC, PF, false, ROPE>), dim3((unsigned)b), dim3(kBlock), 0, st, p,
+                               npairs, tpw);
     }
     return hipGetLastError();
 }
@@ -257,9 +281,10 @@ hipError_t mfma_fwd_wide(const LrProblem &pr, hipStream_t st) {
 template <int W>
 hipError_t wide_rc(const LrProblem &pr, hipStream_t st, bool *used) {
     hipError_t e = hipErrorNotSupported;
+    const bool rope = pr.rot > 0;
     switch ((pr.R + 31) / 32) {
-        case 1: e = mfma_fwd_wide<W, 1>(pr, st); break;
-        case 2: e = mfma_fwd_wide<W, 2>(pr, st); break;
+        case 1: e = rope ? mfma_fwd_wide<W, 1, true>(pr, st) : mfma_fwd_wide<W, 1, false>(pr, st); break;
+        case 2: e = rope ? mfma_fwd_wide<W, 2, true>(pr, st) : mfma_fwd_wide<W, 2, false>(pr, st); break;
         default: break;
     }
     *used = e != hipErrorNotSupported;

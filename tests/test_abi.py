@@ -38,6 +38,7 @@ def test_header_declares_the_entry_points():
               "dsc_static_bwd_deterministic", "dsc_static_bwd_deterministic_workspace_size",
               "dsc_headwise_decode", "dsc_lowrank_decode", "dsc_state_from_prefill",
               "dsc_rope_table", "dsc_headwise_rope_fwd", "dsc_headwise_rope_bwd", "dsc_headwise_rope_decode",
+              "dsc_lowrank_rope_fwd", "dsc_lowrank_rope_bwd",
               "dsc_status_string", "dsc_last_error", "dsc_abi_version"):
         assert s in syms
 
@@ -230,6 +231,32 @@ def test_rope_validation(lib):
     assert rd(y=P(6)) == 5                           # y overlaps the positions
     assert rd(st=P(5)) == 5                          # the state overlaps the table
     assert rd(B=0) == 0
+
+
+def test_lowrank_rope_validation(lib):
+    # low-rank + rotary: B=2 T=8 D=128 W=4 R=16 bf16, rot = 64 (heads of 32)
+    def lf(dt=1, B=2, T=8, D=128, W=4, R=16, x=P(1), z=P(2), U=P(3), cu=None, ns=0, res=0, rot=64, hd=32,
+           tab=P(4), maxp=8, y=P(5)):
+        return lib.dsc_lowrank_rope_fwd(S0, dt, B, T, D, W, R, x, z, U, cu, ns, res, rot, hd, tab, maxp, y)
+
+    def lb(dt=1, R=16, rot=64, hd=32, tab=P(4), maxp=8, dx=P(6), dz=P(7), dU=P(8), ws=P(9), wsb=1 << 20):
+        return lib.dsc_lowrank_rope_bwd(S0, dt, 2, 8, 128, 4, R, P(1), P(2), P(3), P(5), None, 0, 0, rot, hd, tab,
+                                         maxp, dx, dz, dU, ws, wsb)
+    assert lf(R=0) == 2 and lf(R=129) == 2
+    assert lf(hd=31) == 2 and lf(hd=4) == 3          # a bf16 chunk of 8 channels would span two heads
+    assert lf(rot=48) == 2 and lf(rot=160) == 2
+    assert lf(maxp=7) == 2                           # positions 0..T-1 need T rows
+    assert lf(cu=P(10), ns=3, maxp=8) == 2           # packed: a sequence may be B*T long
+    assert lf(tab=None) == 1
+    assert lf(tab=ctypes.c_void_p(A * 4 + 8)) == 4
+    assert lf(y=P(4)) == 5                           # y overlaps the table
+    assert lf(rot=0, tab=None, maxp=0, y=P(1)) == 5  # rot = 0 needs no table; aliasing still checked
+    assert lf(B=0, x=None, z=None, U=None, tab=None, y=None) == 0
+    assert lb(dx=P(4)) == 5 and lb(dz=None) == 1 and lb(maxp=2) == 2
+    assert lb(ws=None, wsb=0) == 6                   # bf16 needs the dz accumulator
+    assert lb(wsb=16) == 6
+    assert lb(ws=P(4)) == 5                          # the workspace overlaps the table
+    assert lb(dt=0, ws=None, wsb=0, dx=P(1)) == 5    # fp32 needs no workspace: on to the alias check
 
 
 def test_binding_raises_with_message(lib):

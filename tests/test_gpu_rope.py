@@ -1,6 +1,6 @@
-"""GPU parity of the head-wise layer fused with the rotary position embedding
-of the query and key channels, and of its cos / sin table, through the C ABI
-against the fp64 oracle.
+"""GPU parity of the head-wise and low-rank layers fused with the rotary
+position embedding of the query and key channels, and of its cos / sin table,
+through the C ABI against the fp64 oracle.
 
 The table is compared entry by entry with the oracle's double-precision table
 rounded to fp32 (at most one fp32 ulp apart: both sides take cos / sin in
@@ -8,7 +8,9 @@ double precision and round once).  The fused layer's y, dx and dw are compared
 element by element at small shapes and on sampled token windows at the QKV
 ~150M shape (B=8 T=2048 D=2304 W=4, heads of 64, query + key = 1536
 channels), with the normwise tolerance of the layer itself (1e-5 fp32, 2e-2
-bf16).
+bf16).  The low-rank layer's y, dx, dz and dU are compared the same way at
+small shapes (every kernel family) and at the QKV ~150M (R = 32, heads of 64)
+and QKV ~2B (R = 64, packed sequences, heads of 128) workloads.
 """
 from __future__ import annotations
 
@@ -147,6 +149,167 @@ def test_headwise_rope_empty_batch():
     binding.dsc_headwise_rope_bwd(x, w, x, torch.empty_like(x), torch.empty_like(w), rot=64, head_dim=16,
                                   table=None)
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------ low-rank layer
+
+
+def _run_lr(inp, W, res, rot, hd, table):
+    x, z, U, dy = (inp[k].cuda() for k in ("x", "z", "U", "dy"))
+    B, T, D = x.shape
+    R = z.shape[2]
+    cu = None if inp["cu_seqlens"] is None else torch.from_numpy(inp["cu_seqlens"]).cuda()
+    y, dx, dz = Guarded(x.shape, x.dtype), Guarded(x.shape, x.dtype), Guarded(z.shape, z.dtype)
+    dU = Guarded(U.shape, torch.float32)
+    nws = binding.dsc_lowrank_bwd_workspace_size(x.dtype, B, T, D, W, R)
+    ws = torch.full((max(nws, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda") if nws else None
+    kw = dict(W=W, rot=rot, head_dim=hd, table=table, cu_seqlens=cu, residual=res)
+    binding.dsc_lowrank_rope_fwd(x, z, U, y.t, **kw)
+    binding.dsc_lowrank_rope_bwd(x, z, U, dy, dx.t, dz.t, dU.t, ws, **kw)
+    torch.cuda.synchronize()
+    for name, g in (("y", y), ("dx", dx), ("dz", dz), ("dU", dU)):
+        g.check_guards(name)
+    return y, dx, dz, dU
+
+
+# (dtype, B, T, D, W, R, head_dim, rot, residual, segment-length range or None)
+LRP_CASES = [
+    ("fp32", 2, 37, 64, 4, 8, 16, 32, True, None),
+    ("fp32", 1, 50, 48, 3, 5, 8, 48, False, (1, 9)),       # every channel rotated
+    ("bf16", 2, 100, 192, 4, 32, 64, 128, True, None),     # query, key, value heads of 64
+    ("bf16", 1, 300, 768, 4, 64, 64, 512, False, (1, 40)),  # R = 64: two rank tiles
+    ("bf16", 1, 200, 128, 3, 20, 32, 128, True, (1, 30)),  # z rows gathered (R % 8 != 0)
+    ("bf16", 1, 60, 64, 4, 100, 16, 32, False, None),      # R > 64: vector-ALU kernels
+    ("bf16", 1, 90, 128, 6, 48, 32, 64, True, (1, 20)),    # wide forward, vector-ALU backward
+    ("bf16", 1, 130, 256, 8, 8, 32, 256, True, (1, 40)),
+    ("bf16", 2, 65, 2304, 4, 32, 64, 1536, False, None),   # the QKV ~150M layout at a short length
+    ("bf16", 1, 400, 6144, 4, 64, 128, 4096, False, (1, 150)),  # the QKV ~2B layout, packed
+    ("bf16", 1, 1, 16, 3, 4, 8, 8, False, None),           # one token
+    # several token walks per channel pair, walks starting inside a sequence
+    ("bf16", 1, 4100, 64, 3, 36, 16, 64, True, (1, 700)),
+    ("bf16", 3, 1000, 128, 4, 20, 32, 128, True, (100, 900)),
+    ("bf16", 2, 1500, 256, 4, 32, 64, 192, False, None),
+]
+
+
+def _lr_ids(cases):
+    return [f"lrope-{c[0]}-B{c[1]}T{c[2]}D{c[3]}W{c[4]}R{c[5]}-hd{c[6]}rot{c[7]}-res{int(c[8])}-"
+            f"{'varlen' if c[9] else 'rows'}" for c in cases]
+
+
+def _check_lr(wl, inp, W, res, rot, hd, base, dt):
+    cu = inp["cu_seqlens"]
+    B, T = inp["x"].shape[:2]
+    table = _table(B * T if cu is not None else T, hd, base)
+    y, dx, dz, dU = _run_lr(inp, W, res, rot, hd, table)
+    x64, z64, U64, g64 = (to_f64(inp[k]) for k in ("x", "z", "U", "dy"))
+    kw = dict(rot=rot, head_dim=hd, base=base, cu_seqlens=cu, residual=res)
+    ry = oracle.lowrank_rope_fwd(x64, z64, U64, W, **kw)
+    rdx, rdz, rdU = oracle.lowrank_rope_bwd(x64, z64, U64, g64, W, **kw)
+    tol = TOL[dt]
+    assert_close("y", y.host(), ry, tol)
+    assert_close("dx", dx.host(), rdx, tol)
+    assert_close("dz", dz.host(), rdz, tol)
+    assert_close("dU", dU.host(), rdU, tol)
+
+
+@pytest.mark.parametrize("case", LRP_CASES, ids=_lr_ids(LRP_CASES))
+def test_lowrank_rope_small(case):
+    dt, B, T, D, W, R, hd, rot, res, seg = case
+    wl, inp = inputs.small("lowrank", B, T, D, W, R=R, dtype=dt, residual=res, varlen=seg is not None,
+                           seglen_range=seg or (1, 8), seed=zlib.crc32(repr(case).encode()) % 1000)
+    base = 10000.0 if hd >= 32 else 100.0
+    say(f"[lowrank rope] {wl.name} hd={hd} rot={rot} residual={res} segments={inp['cu_seqlens']}")
+    _check_lr(wl, inp, W, res, rot, hd, base, dt)
+
+
+def test_lowrank_rope_sequence_starts_at_step_edges():
+    """Sequence starts at every offset around the 16-token steps: the
+    position of each token restarts exactly at its sequence's first token."""
+    T = 709
+    starts = {0, T}
+    offs = [0, 1, 2, 3, 7, 13, 14, 15]
+    for j, m in enumerate(range(1, T // 16)):
+        starts.add(16 * m + offs[j % len(offs)])
+        if j % 5 == 0:
+            starts.update({16 * m - 1, 16 * m + 1})
+    wl, inp = inputs.small("lowrank", 1, T, 128, 4, R=32, dtype="bf16", residual=True, seed=23)
+    inp["cu_seqlens"] = np.array(sorted(starts), dtype=np.int32)
+    say(f"[lowrank rope] {wl.name} step-edge starts")
+    _check_lr(wl, inp, 4, True, 64, 32, 10000.0, "bf16")
+
+
+def test_lowrank_rope_without_rotation_is_the_layer():
+    """rot = 0 (no table) gives the low-rank layer's outputs: y bit for bit,
+    dx bit for bit, dz and dU up to the order of their fp32 atomic sums."""
+    wl, inp = inputs.small("lowrank", 2, 70, 256, 4, R=32, dtype="bf16", residual=True, seed=6)
+    x, z, U, dy = (inp[k].cuda() for k in ("x", "z", "U", "dy"))
+    B, T, D = x.shape
+    ws = torch.empty(binding.dsc_lowrank_bwd_workspace_size(x.dtype, B, T, D, 4, 32) // 4, device="cuda")
+    y1, y2, dx1, dx2 = (torch.empty_like(x) for _ in range(4))
+    dz1, dz2 = torch.empty_like(z), torch.empty_like(z)
+    dU1, dU2 = (torch.empty(U.shape, dtype=torch.float32, device="cuda") for _ in range(2))
+    binding.dsc_lowrank_rope_fwd(x, z, U, y1, W=4, rot=0, head_dim=64, table=None, residual=True)
+    binding.dsc_lowrank_fwd(x, z, U, y2, W=4, residual=True)
+    binding.dsc_lowrank_rope_bwd(x, z, U, dy, dx1, dz1, dU1, ws, W=4, rot=0, head_dim=64, table=None, residual=True)
+    binding.dsc_lowrank_bwd(x, z, U, dy, dx2, dz2, dU2, ws, W=4, residual=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(dx1, dx2)
+    assert torch.allclose(dz1.float(), dz2.float(), rtol=1e-2, atol=1e-2)
+    assert torch.allclose(dU1, dU2, rtol=1e-4, atol=1e-4)
+
+
+def test_lowrank_rope_empty_batch():
+    x = torch.empty(0, 16, 64, dtype=torch.bfloat16, device="cuda")
+    z = torch.empty(0, 16, 8, dtype=torch.bfloat16, device="cuda")
+    U = torch.randn(8, 64 * 4, device="cuda").to(torch.bfloat16)
+    dU = torch.full((8, 256), float("nan"), device="cuda")
+    binding.dsc_lowrank_rope_fwd(x, z, U, torch.empty_like(x), W=4, rot=64, head_dim=16, table=None)
+    binding.dsc_lowrank_rope_bwd(x, z, U, x, torch.empty_like(x), torch.empty_like(z), dU, None, W=4, rot=64,
+                                 head_dim=16, table=None)
+    torch.cuda.synchronize()
+    assert torch.equal(dU, torch.zeros_like(dU))  # a sum over no tokens
+
+
+# (workload, head_dim, rot): the query and key channels of the QKV projections
+LR_FULL = [(3, 64, 1536), (5, 128, 4096)]
+
+
+@pytest.mark.parametrize("cfg,hd,rot", LR_FULL, ids=[f"cfg{c[0]}" for c in LR_FULL])
+def test_lowrank_rope_full_size(cfg, hd, rot):
+    """The low-rank workloads with the rotation of their query and key
+    channels: every output element written, and token windows (sequence
+    starts, walk boundaries, the ends) and channel blocks across the rotated
+    and plain channels against the oracle."""
+    wl = inputs.WORKLOADS[cfg]
+    inp = inputs.make_inputs(wl)
+    cu = inp["cu_seqlens"]
+    N, D, W, R = wl.N, wl.D, wl.W, wl.R
+    say(f"[lowrank rope] {wl.name}: B={wl.B} T={wl.T} D={D} W={W} R={R} head_dim={hd} rot={rot}")
+    table = _table(N if cu is not None else wl.T, hd, 10000.0)
+    y, dx, dz, dU = _run_lr(inp, W, wl.residual, rot, hd, table)
+    for name, g in (("y", y), ("dx", dx), ("dz", dz), ("dU", dU)):
+        assert not torch.isnan(g.t).any().item(), f"{name}: unwritten elements"
+    x64, z64, U64, g64 = (to_f64(inp[k]) for k in ("x", "z", "U", "dy"))
+    kw = dict(rot=rot, head_dim=hd, base=10000.0, cu_seqlens=cu, residual=wl.residual)
+    tol = TOL[wl.dtype]
+    wins = [(0, 40), (4090, 4110), (N // 2 - 7, N // 2 + 17), (N - 40, N)]
+    if cu is not None:
+        s = int(cu[len(cu) // 2])
+        wins.append((max(0, s - 20), min(N, s + 20)))
+    for lo, hi in wins:
+        say(f"  rows [{lo},{hi})")
+        yr = to_f64(y.t.reshape(N, D)[lo:hi])
+        assert_close("y", yr, oracle.lowrank_rope_fwd(x64, z64, U64, W, rows=(lo, hi), **kw).reshape(hi - lo, D),
+                     tol)
+        rdx, rdz, _ = oracle.lowrank_rope_bwd(x64, z64, U64, g64, W, rows=(lo, hi), channels=(0, 0), **kw)
+        assert_close("dx", to_f64(dx.t.reshape(N, D)[lo:hi]), rdx.reshape(hi - lo, D), tol)
+        assert_close("dz", to_f64(dz.t.reshape(N, R)[lo:hi]), rdz.reshape(hi - lo, R), tol)
+    dUf = to_f64(dU.t).reshape(R, D, W)
+    for c0, c1 in [(0, 64), (rot - 64, rot + 64), (D - 64, D)]:
+        say(f"  dU channels [{c0},{c1})")
+        _, _, part = oracle.lowrank_rope_bwd(x64, z64, U64, g64, W, rows=(0, 0), channels=(c0, c1), **kw)
+        assert_close("dU", dUf[:, c0:c1], part.reshape(R, c1 - c0, W), tol)
 
 
 # ------------------------------------------------------------ decoding
