@@ -13,12 +13,12 @@ all through the C ABI of libdsc.so with inputs resident in HBM.
 Prints one JSON line: tokens/s of the step (wall time of K steps bracketed by
 device synchronisation), achieved algorithmic HBM GB/s, per-entry-point
 figures (each call timed with HIP events on the stream it runs on, after a
-512 MiB write that evicts the last-level cache, median / min / mean over at
+1 GiB read that evicts the last-level cache, median / min / mean over at
 least 50 calls), the roofline of the dominant entry point, the streaming
 ceiling measured with the library's own streaming kernel, and, as extras, the
 QKV ~150M step (head-wise H=64 and low-rank R=32 at B=8 T=2048 D=2304), the
 static short convolution beside the dynamic head-wise layer, decoding steps,
-the head-wise layer fused with the rotary embedding, the fixed-order
+the head-wise and low-rank layers fused with the rotary embedding, the fixed-order
 backward passes, and the fp64 CPU oracle timed on a bounded sample of the
 step's work.
 
@@ -422,6 +422,23 @@ def measure_step(torch, cases, K, warmup, iters, flush):
     return wall / K * 1e3, per, pairs
 
 
+def interleaved_s(torch, calls, reps):
+    """Seconds per call of each of `calls`, run in turn in one loop (after 3
+    untimed rounds), from events between consecutive calls."""
+    for _ in range(3):
+        for f in calls:
+            f()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(reps)]
+    for e in evs:
+        e[0].record()
+        for i, f in enumerate(calls):
+            f()
+            e[i + 1].record()
+    torch.cuda.synchronize()
+    return [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / reps * 1e-3 for i in range(len(calls))]
+
+
 def steady_us(torch, fn, reps):
     """Microseconds per call of `fn` launched `reps` times back to back
     (HIP events around the batch): the steady state, where every call also
@@ -760,38 +777,35 @@ def main() -> int:
     # The layer on the query / key / value projections feeds the rotary
     # embedding of the queries and keys.  The fused calls rotate channels
     # [0, 1536) (12 query and 12 key heads of 64) of the QKV ~150M
-    # workload on the fly; the layer alone is timed in the same loop.  A
+    # workloads on the fly; the layer alone is timed in the same loop.  A
     # separate rotation pass would move rot*N elements in and out once
     # more in each direction (unfused_extra_bytes per direction).
     log("fused rotary embedding")
     hd, rot = 64, 2 * 768
     table = torch.empty(hwc.wl.T, hd // 2, 2, dtype=torch.float32, device="cuda")
     binding.dsc_rope_table(table, base=10000.0)
-    kw = dict(rot=rot, head_dim=hd, table=table, residual=hwc.wl.residual)
-    calls = [lambda: binding.dsc_headwise_rope_fwd(hwc.x, hwc.w, hwc.y, **kw),
-             lambda: binding.dsc_headwise_rope_bwd(hwc.x, hwc.w, hwc.dy, hwc.dx, hwc.dw, **kw),
-             hwc.fwd, hwc.bwd]
-    for _ in range(3):
-        for f in calls:
-            f()
-    torch.cuda.synchronize()
     reps = max(5, K // 2)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(reps)]
-    for e in evs:
-        e[0].record()
-        for i, f in enumerate(calls):
-            f()
-            e[i + 1].record()
-    torch.cuda.synchronize()
-    tr = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / reps * 1e-3 for i in range(len(calls))]
-    b = hwc.bytes("fwd") + hwc.bytes("bwd") + 2 * table.numel() * 4
-    out["rope_fused"] = {
-        "workload": f"{hwc.wl.name} + rotary embedding of channels [0, {rot}), heads of {hd}",
-        "fwd_us": round(tr[0] * 1e6, 1), "bwd_us": round(tr[1] * 1e6, 1),
-        "GBps": round(b / (tr[0] + tr[1]) / 1e9, 1),
-        "frac_hbm_peak": round(b / (tr[0] + tr[1]) / 1e9 / PEAK_HBM_GBPS, 4),
-        "layer_alone_fwd_us": round(tr[2] * 1e6, 1), "layer_alone_bwd_us": round(tr[3] * 1e6, 1),
-        "unfused_extra_bytes": 2 * rot * hwc.wl.N * hwc.x.element_size()}
+    rope = {}
+    kw = dict(rot=rot, head_dim=hd, table=table, residual=hwc.wl.residual)
+    lkw = dict(W=lrc.wl.W, rot=rot, head_dim=hd, table=table, residual=lrc.wl.residual)
+    for name, c, calls in (
+            ("headwise", hwc, [lambda: binding.dsc_headwise_rope_fwd(hwc.x, hwc.w, hwc.y, **kw),
+                               lambda: binding.dsc_headwise_rope_bwd(hwc.x, hwc.w, hwc.dy, hwc.dx, hwc.dw, **kw),
+                               hwc.fwd, hwc.bwd]),
+            ("lowrank", lrc, [lambda: binding.dsc_lowrank_rope_fwd(lrc.x, lrc.z, lrc.U, lrc.y, **lkw),
+                              lambda: binding.dsc_lowrank_rope_bwd(lrc.x, lrc.z, lrc.U, lrc.dy, lrc.dx, lrc.dz,
+                                                                   lrc.dU, lrc.ws, **lkw),
+                              lrc.fwd, lrc.bwd])):
+        tr = interleaved_s(torch, calls, reps)
+        b = c.bytes("fwd") + c.bytes("bwd") + 2 * table.numel() * 4
+        rope[name] = {
+            "workload": f"{c.wl.name} + rotary embedding of channels [0, {rot}), heads of {hd}",
+            "fwd_us": round(tr[0] * 1e6, 1), "bwd_us": round(tr[1] * 1e6, 1),
+            "GBps": round(b / (tr[0] + tr[1]) / 1e9, 1),
+            "frac_hbm_peak": round(b / (tr[0] + tr[1]) / 1e9 / PEAK_HBM_GBPS, 4),
+            "layer_alone_fwd_us": round(tr[2] * 1e6, 1), "layer_alone_bwd_us": round(tr[3] * 1e6, 1),
+            "unfused_extra_bytes": 2 * rot * c.wl.N * c.x.element_size()}
+    out["rope_fused"] = rope
     del table
 
     # The reproducible low-rank backward (dz and dU summed in a fixed order
@@ -806,18 +820,7 @@ def main() -> int:
                                                                det_ws if nws else None, W=lw.W,
                                                                cu_seqlens=lrc.cu, residual=lw.residual),
                  lrc.bwd]
-        for _ in range(3):
-            for f in calls:
-                f()
-        torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(reps)]
-        for e in evs:
-            e[0].record()
-            for i, f in enumerate(calls):
-                f()
-                e[i + 1].record()
-        torch.cuda.synchronize()
-        td = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / reps * 1e-3 for i in range(len(calls))]
+        td = interleaved_s(torch, calls, reps)
         out["lowrank_bwd_deterministic"] = {
             "workload": lw.name, "us": round(td[0] * 1e6, 1), "fast_us": round(td[1] * 1e6, 1),
             "workspace_bytes": nws, "algorithmic_GBps": round(lrc.bytes("bwd") / td[0] / 1e9, 1)}
@@ -833,18 +836,7 @@ def main() -> int:
         calls = [lambda: binding.dsc_static_bwd_deterministic(sc.x, sc.c, sc.dy, sc.dx, sc.dc, det_ws,
                                                               residual=swl.residual),
                  sc.bwd]
-        for _ in range(3):
-            for f in calls:
-                f()
-        torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(reps)]
-        for e in evs:
-            e[0].record()
-            for i, f in enumerate(calls):
-                f()
-                e[i + 1].record()
-        torch.cuda.synchronize()
-        td = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / reps * 1e-3 for i in range(len(calls))]
+        td = interleaved_s(torch, calls, reps)
         out["static_bwd_deterministic"] = {
             "workload": swl.name, "us": round(td[0] * 1e6, 1), "fast_us": round(td[1] * 1e6, 1),
             "workspace_bytes": nws}

@@ -57,10 +57,14 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_rope_table.argtypes = [i64, i32, ctypes.c_double, p]
     lib.oracle_rope.argtypes = [i64, i64, i64, i64, i32, ctypes.c_double, p, i32, i32, i64, i64, p, p]
     lib.oracle_rope_at.argtypes = [i64, i64, i64, i32, ctypes.c_double, p, p, p]
+    lib.oracle_generate.argtypes = [i64, i64, i64, p, p, i64, i64, p]
+    lib.oracle_generate_bwd_h.argtypes = [i64, i64, p, p, i64, p]
+    lib.oracle_generate_bwd_v.argtypes = [i64, i64, i64, p, p, i64, i64, p]
     for name in ("oracle_headwise_fwd", "oracle_headwise_bwd", "oracle_lowrank_fwd",
                  "oracle_lowrank_bwd", "oracle_static_fwd", "oracle_static_bwd",
                  "oracle_headwise_decode", "oracle_lowrank_decode", "oracle_state_from_prefill",
-                 "oracle_rope_table", "oracle_rope", "oracle_rope_at"):
+                 "oracle_rope_table", "oracle_rope", "oracle_rope_at", "oracle_generate",
+                 "oracle_generate_bwd_h", "oracle_generate_bwd_v"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -302,6 +306,73 @@ class Oracle:
         ds = self.rope(dy, rot=rot, head_dim=head_dim, base=base, cu_seqlens=cu_seqlens, inverse=True)
         return self.headwise_bwd(x, w, ds, cu_seqlens=cu_seqlens, residual=residual, rows=rows)
 
+    def generate(self, h, V, *, rows=None):
+        """w = h V^T: h (N, K) hidden states, V (C, K) the generator's weight ->
+        (rows, C) for token rows [lo, hi) (default all)."""
+        h, V = _f64(h), _f64(V)
+        h = h.reshape(-1, h.shape[-1])
+        N, K = h.shape
+        C = V.shape[0]
+        if V.shape != (C, K):
+            raise ValueError(f"V must be (C, {K}), got {V.shape}")
+        lo, hi = rows if rows is not None else (0, N)
+        w = np.empty((hi - lo, C))
+        _check(self.lib.oracle_generate(N, K, C, _ptr(h), _ptr(V), lo, hi, _ptr(w)), "generate")
+        return w
+
+    def headwise_gen_fwd(self, h, V, x, *, W, cu_seqlens=None, residual=False, rows=None):
+        """The head-wise layer whose filters come from the hidden state:
+        w[n, g, k] = sum_j h[n, j] V[g*W + k, j] (Methodology, parametrization:
+        a learned linear map of the current hidden state), then y as
+        headwise_fwd.  h (B,T,K), V (G*W, K), x (B,T,D) -> y (or compact rows)."""
+        x = _f64(x)
+        B, T, D = x.shape
+        N = B * T
+        G = _f64(V).shape[0] // W
+        lo, hi = rows if rows is not None else (0, N)
+        w = np.zeros((N, G * W))
+        w[lo:hi] = self.generate(h, V, rows=(lo, hi))  # y of row n reads w of row n only
+        return self.headwise_fwd(x, w.reshape(B, T, G, W), cu_seqlens=cu_seqlens, residual=residual, rows=rows)
+
+    def headwise_gen_bwd(self, h, V, x, dy, *, W, cu_seqlens=None, residual=False, rows=None, groups=None):
+        """-> (dx, dh, dV) for L = <dy, y>: dx, dh over token rows [lo, hi)
+        (default all), dV (rows g*W + k for groups [g_lo, g_hi), K) summed
+        over every token (default all groups).  dw is the head-wise layer's
+        filter gradient; dh = dw V and dV = dw^T h are the chain rule of the
+        linear map."""
+        h, V, x, dy = _f64(h), _f64(V), _f64(x), _f64(dy)
+        B, T, D = x.shape
+        N = B * T
+        K = h.shape[-1]
+        C = V.shape[0]
+        G = C // W
+        H = D // G
+        lo, hi = rows if rows is not None else (0, N)
+        glo, ghi = groups if groups is not None else (0, G)
+        # dx of rows [lo, hi) reads the filters of rows up to hi + W - 2
+        w = np.zeros((N, C))
+        whi = min(N, hi + W - 1)
+        if hi > lo:
+            w[lo:whi] = self.generate(h, V, rows=(lo, whi))
+        dx, dw = self.headwise_bwd(x, w.reshape(B, T, G, W), dy, cu_seqlens=cu_seqlens, residual=residual,
+                                   rows=(lo, hi))
+        dh = np.empty((hi - lo, K))
+        _check(self.lib.oracle_generate_bwd_h(K, C, _ptr(np.ascontiguousarray(dw.reshape(hi - lo, C))), _ptr(V),
+                                              hi - lo, _ptr(dh)), "generate_bwd_h")
+        # dV of groups [glo, ghi): the filter gradient of those groups' channels
+        # over every token (it does not depend on w)
+        dV = np.empty(((ghi - glo) * W, K))
+        if ghi > glo:
+            xs = np.ascontiguousarray(x[..., glo * H:ghi * H])
+            gs = np.ascontiguousarray(dy[..., glo * H:ghi * H])
+            _, dws = self.headwise_bwd(xs, np.zeros((B, T, ghi - glo, W)), gs, cu_seqlens=cu_seqlens)
+            dws = np.ascontiguousarray(dws.reshape(N, (ghi - glo) * W))
+            _check(self.lib.oracle_generate_bwd_v(N, K, (ghi - glo) * W, _ptr(dws), _ptr(h.reshape(N, K)), 0,
+                                                  (ghi - glo) * W, _ptr(dV)), "generate_bwd_v")
+        if rows is None:
+            return dx.reshape(B, T, D), dh.reshape(B, T, K), dV
+        return dx, dh, dV
+
     def lowrank_rope_fwd(self, x, z, U, W, *, rot, head_dim, base=10000.0, cu_seqlens=None,
                          residual=False, rows=None):
         """RoPE(rho*x + conv(x)) with the low-rank filters z U: the low-rank
@@ -383,6 +454,18 @@ def rope(*a, **k):
 
 def headwise_rope_fwd(*a, **k):
     return default().headwise_rope_fwd(*a, **k)
+
+
+def generate(*a, **k):
+    return default().generate(*a, **k)
+
+
+def headwise_gen_fwd(*a, **k):
+    return default().headwise_gen_fwd(*a, **k)
+
+
+def headwise_gen_bwd(*a, **k):
+    return default().headwise_gen_bwd(*a, **k)
 
 
 def lowrank_rope_fwd(*a, **k):

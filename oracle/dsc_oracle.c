@@ -304,6 +304,60 @@ int oracle_static_bwd(int64_t B, int64_t T, int64_t D, int32_t W, const double *
     return 0;
 }
 
+/* ---------------------------------------------------------- filter generator */
+
+/* The head-wise filters as a learned linear map of the current hidden state
+ * ("Dynamic Short Convolutions Improve Transformers", gist.science technical
+ * summary, Methodology: parametrization), written as a linear layer with
+ * weight V (C, K): for rows n in [n_lo, n_hi) of h (N, K),
+ *   w[n, c] = sum_{j<K} h[n, j] * V[c, j],   c = g*W + k  (C = G*W).
+ * w is stored compactly (row n at n - n_lo).                                */
+int oracle_generate(int64_t N, int64_t K, int64_t C, const double *h, const double *V, int64_t n_lo,
+                    int64_t n_hi, double *w)
+{
+    if (N < 0 || K < 1 || C < 1 || n_lo < 0 || n_hi > N || n_lo > n_hi) return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = n_lo; n < n_hi; ++n)
+        for (int64_t c = 0; c < C; ++c) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < K; ++j) acc += h[n * K + j] * V[c * K + j];
+            w[(n - n_lo) * C + c] = acc;
+        }
+    return 0;
+}
+
+/* Chain rule of the map for L = <dw, w>:
+ *   dh[n, j] = sum_{c<C} dw[n, c] * V[c, j]   for rows [n_lo, n_hi) (dw and dh
+ *              stored compactly, row n at n - n_lo),
+ *   dV[c, j] = sum_{n<N} dw[n, c] * h[n, j]   for c in [c_lo, c_hi) (dw (N, C)
+ *              over every row; dV row c at c - c_lo).                       */
+int oracle_generate_bwd_h(int64_t K, int64_t C, const double *dw, const double *V, int64_t rows, double *dh)
+{
+    if (K < 1 || C < 1 || rows < 0) return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < rows; ++n)
+        for (int64_t j = 0; j < K; ++j) {
+            double acc = 0.0;
+            for (int64_t c = 0; c < C; ++c) acc += dw[n * C + c] * V[c * K + j];
+            dh[n * K + j] = acc;
+        }
+    return 0;
+}
+
+int oracle_generate_bwd_v(int64_t N, int64_t K, int64_t C, const double *dw, const double *h, int64_t c_lo,
+                          int64_t c_hi, double *dV)
+{
+    if (N < 0 || K < 1 || C < 1 || c_lo < 0 || c_hi > C || c_lo > c_hi) return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t c = c_lo; c < c_hi; ++c)
+        for (int64_t j = 0; j < K; ++j) {
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) acc += dw[n * C + c] * h[n * K + j];
+            dV[(c - c_lo) * K + j] = acc;
+        }
+    return 0;
+}
+
 /* ---------------------------------------------------------------- decoding */
 
 /* One token per sequence at inference (the pages' inference remark: decoding

@@ -605,4 +605,99 @@ def pin_rope_decode_reproduces_forward(orc):
             _close(yt[s_], want, what=f"rotated decode, sequence {s_} step {j}")
 
 
+# ------------------------------------------------------- filter generator
+
+
+def _gen_case(rng, B, T, D, W, H, K):
+    h = rng.standard_normal((B, T, K))
+    V = rng.standard_normal(((D // H) * W, K))
+    x = rng.standard_normal((B, T, D))
+    g = rng.standard_normal((B, T, D))
+    return h, V, x, g
+
+
+def pin_generator_bruteforce(orc):
+    """The generated filters and the layer on them, by direct loops over
+    every index (the map w[n, g*W + k] = sum_j h[n, j] V[g*W + k, j], then
+    the convolution with the per-sequence causal mask); the map alone also
+    against numpy's matrix product."""
+    rng = _rng(30)
+    B, T, D, W, H, K = 2, 5, 6, 3, 2, 4
+    cu = [0, 2, 5, 7, 10]
+    h, V, x, _ = _gen_case(rng, B, T, D, W, H, K)
+    hf, xf = h.reshape(-1, K), x.reshape(-1, D)
+    _close(orc.generate(h, V), hf @ V.T, what="generator == h V^T")
+    seg = np.zeros(B * T, dtype=int)
+    for s0, s1 in zip(cu[:-1], cu[1:]):
+        seg[s0:s1] = s0
+    for res in (False, True):
+        want = np.zeros((B * T, D))
+        for n in range(B * T):
+            for d in range(D):
+                acc = xf[n, d] if res else 0.0
+                for k in range(W):
+                    if n - k >= seg[n]:
+                        wk = sum(hf[n, j] * V[(d // H) * W + k, j] for j in range(K))
+                        acc += wk * xf[n - k, d]
+                want[n, d] = acc
+        got = orc.headwise_gen_fwd(h, V, x, W=W, cu_seqlens=cu, residual=res)
+        _close(got.reshape(-1, D), want, what=f"generated layer, residual={res}")
+
+
+def pin_generator_finite_differences(orc):
+    """dx, dh, dV of L = <g, y> equal exact central differences (L is linear
+    in each of h, V and x separately)."""
+    rng = _rng(31)
+    B, T, D, W, H, K = 2, 4, 4, 3, 2, 3
+    cu = [0, 3, 4, 8]
+    h, V, x, g = _gen_case(rng, B, T, D, W, H, K)
+    for res in (False, True):
+        f = lambda: float(np.sum(g * orc.headwise_gen_fwd(h, V, x, W=W, cu_seqlens=cu, residual=res)))
+        dx, dh, dV = orc.headwise_gen_bwd(h, V, x, g, W=W, cu_seqlens=cu, residual=res)
+        _close(dx, _fd_grad(f, x), tol=1e-8, what="FD dx (generated)")
+        _close(dh, _fd_grad(f, h), tol=1e-8, what="FD dh")
+        _close(dV, _fd_grad(f, V), tol=1e-8, what="FD dV")
+
+
+def pin_generator_constant_state_is_static(orc):
+    """A hidden state that is the same unit vector e_0 at every token makes
+    the filter the same at every token, w = V[:, 0]: the layer is then the
+    static short convolution with c[d, k] = V[(d/H)*W + k, 0], dV[:, 0] is
+    the static filter gradient summed over each group's channels, and dV is
+    zero in every other column."""
+    rng = _rng(32)
+    B, T, D, W, H, K = 2, 7, 6, 4, 3, 3
+    cu = [0, 5, 9, 14]
+    _, V, x, g = _gen_case(rng, B, T, D, W, H, K)
+    h = np.zeros((B, T, K))
+    h[..., 0] = 1.0
+    c = np.repeat(V[:, 0].reshape(D // H, W), H, axis=0)
+    _close(orc.headwise_gen_fwd(h, V, x, W=W, cu_seqlens=cu, residual=True),
+           orc.static_fwd(x, c, cu_seqlens=cu, residual=True), what="constant state == static layer")
+    dx, dh, dV = orc.headwise_gen_bwd(h, V, x, g, W=W, cu_seqlens=cu, residual=True)
+    sdx, sdc = orc.static_bwd(x, c, g, cu_seqlens=cu, residual=True)
+    _close(dx, sdx, what="constant state dx == static dx")
+    _close(dV[:, 0], sdc.reshape(D // H, H, W).sum(1).reshape(-1), what="dV column 0 == grouped static dc")
+    _close(dV[:, 1:], np.zeros_like(dV[:, 1:]), what="dV of unused state columns")
+
+
+def pin_generator_rows_and_groups_match_full(orc):
+    rng = _rng(33)
+    B, T, D, W, H, K = 2, 9, 8, 3, 2, 5
+    cu = [0, 4, 9, 10, 18]
+    h, V, x, g = _gen_case(rng, B, T, D, W, H, K)
+    N = B * T
+    y = orc.headwise_gen_fwd(h, V, x, W=W, cu_seqlens=cu, residual=True).reshape(N, D)
+    dx, dh, dV = orc.headwise_gen_bwd(h, V, x, g, W=W, cu_seqlens=cu, residual=True)
+    dx, dh = dx.reshape(N, D), dh.reshape(N, K)
+    for lo, hi in [(0, 3), (5, 12), (N - 2, N), (7, 7)]:
+        _close(orc.headwise_gen_fwd(h, V, x, W=W, cu_seqlens=cu, residual=True, rows=(lo, hi)), y[lo:hi],
+               what=f"y rows {lo}:{hi}")
+        rdx, rdh, rdV = orc.headwise_gen_bwd(h, V, x, g, W=W, cu_seqlens=cu, residual=True, rows=(lo, hi),
+                                             groups=(1, 3))
+        _close(rdx, dx[lo:hi], what=f"dx rows {lo}:{hi}")
+        _close(rdh, dh[lo:hi], what=f"dh rows {lo}:{hi}")
+        _close(rdV, dV[W:3 * W], what="dV groups 1:3")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -61,6 +61,11 @@ MUTANTS = [
      "const double p = a[h + i], q = a[h + i + hd / 2];", 1),
     ("rope_table_cos_sin_swapped", "table[(m * (hd / 2) + i) * 2 + 0] = cos(ang);",
      "table[(m * (hd / 2) + i) * 2 + 0] = sin(ang);", 1),
+    ("generate_V_transposed", "acc += h[n * K + j] * V[c * K + j];", "acc += h[n * K + j] * V[j * C + c];", 1),
+    ("generate_dh_reversed", "acc += dw[n * C + c] * V[c * K + j];", "acc += dw[n * C + c] * V[c * K + (K - 1 - j)];",
+     1),
+    ("generate_dV_wrong_row", "acc += dw[n * C + c] * h[n * K + j];",
+     "acc += dw[n * C + c] * h[(N - 1 - n) * K + j];", 1),
     ("rope_decode_position_off_by_one", "rotate_row(D, rot, hd, base, (double)pos[b], 1.0,",
      "rotate_row(D, rot, hd, base, (double)(pos[b] + 1), 1.0,", 1),
 ]
