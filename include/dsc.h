@@ -176,6 +176,57 @@ DSC_API dsc_status dsc_headwise_rope_bwd(void *stream, int dtype, int64_t B, int
                                  int32_t head_dim, const float *table, int64_t max_pos, void *dx, void *dw);
 
 /*
+ * Head-wise layer whose filters are generated on chip from the hidden state.
+ * The pages generate the filter of token t by a learned linear map of the
+ * current hidden state (Methodology, "parametrization"); with head-wise tying
+ * the map yields one W-tap filter per group of H channels:
+ *   w[n, g*W + k] = sum_{j<K} h[n, j] * V[g*W + k, j]        (on chip only)
+ *   y[n, d]       = the head-wise forward (dsc_headwise_fwd) with these w.
+ * The map runs on the matrix cores (bf16 products, fp32 sums) and its result
+ * feeds the convolution in the same kernel; w is never written to memory.
+ *
+ *   h  (B,T,K) in: the hidden state of each token (the layer's own input x,
+ *      or another tensor of any width K, e.g. the block's input);
+ *   V  (G*W, K) in: the map's weight, row g*W + k producing tap k of group g
+ *      (the layout of a linear layer's weight, out x in), G = D/H;
+ *   x  (B,T,D) in;  y (B,T,D) out.
+ *   DSC_BF16 only (DSC_ERR_UNSUPPORTED otherwise); K a multiple of 8 and
+ *   G*W a multiple of 8 (else DSC_ERR_UNSUPPORTED), K <= 2^20; any H
+ *   dividing D.  h may be the same buffer as x.  Other arguments and rules
+ *   as dsc_headwise_fwd.
+ */
+DSC_API dsc_status dsc_headwise_gen_fwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                                        int32_t H, int64_t K, const void *h, const void *V, const void *x,
+                                        const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, void *y);
+
+/*
+ * Bytes of device workspace dsc_headwise_gen_bwd needs: the filter gradient
+ * dw (B*T, G*W) in bf16, rounded up to 256.  0 for invalid sizes.
+ */
+DSC_API size_t dsc_headwise_gen_bwd_workspace_size(int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                                                   int32_t H, int64_t K);
+
+/*
+ * Backward of dsc_headwise_gen_fwd for L = <dy, y>:
+ *   dx = the head-wise dx (dsc_headwise_bwd) with the generated w,
+ *   dw[n, g*W+k] = sum_{d in group g, n-k in n's sequence} dy[n,d] * x[n-k,d],
+ *   dh[n, j] = sum_c dw[n, c] * V[c, j],    dV[c, j] = sum_n dw[n, c] * h[n, j].
+ * w is generated again on chip (not stored by the forward); dw is rounded to
+ * bf16 once, in the workspace, and both products read it there.
+ *   dx (B,T,D) bf16 out;  dh (B,T,K) bf16 out;  dV (G*W, K) fp32 out (zero
+ *   for an empty batch).  When h is x, the caller adds dh to dx.
+ *   workspace: at least dsc_headwise_gen_bwd_workspace_size() bytes, 16-byte
+ *   aligned, contents undefined on entry and exit, overlapping no argument.
+ * dx, dh and dV are deterministic (no atomics).  Other rules as
+ * dsc_headwise_gen_fwd.
+ */
+DSC_API dsc_status dsc_headwise_gen_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
+                                        int32_t H, int64_t K, const void *h, const void *V, const void *x,
+                                        const void *dy, const int32_t *cu_seqlens, int32_t n_seqs,
+                                        int32_t residual, void *dx, void *dh, float *dV, void *workspace,
+                                        size_t workspace_bytes);
+
+/*
  * Low-rank forward (fused up-projection; Methodology, "parametrization (1)"
  * and Efficient training implementation, fused low-rank kernel):
  *   w[n,d,k] = sum_{r<R} z[n,r] * U[r, d*W+k]          (on chip only)

@@ -63,13 +63,18 @@ def lib() -> ctypes.CDLL:
         L.dsc_lowrank_rope_fwd.argtypes = [p, i, i64, i64, i64, i32, i32, p, p, p, p, i32, i32, i64, i32, p, i64, p]
         L.dsc_lowrank_rope_bwd.argtypes = [p, i, i64, i64, i64, i32, i32, p, p, p, p, p, i32, i32, i64, i32, p, i64,
                                            p, p, p, p, ctypes.c_size_t]
+        L.dsc_headwise_gen_fwd.argtypes = [p, i, i64, i64, i64, i32, i32, i64, p, p, p, p, i32, i32, p]
+        L.dsc_headwise_gen_bwd_workspace_size.argtypes = [i, i64, i64, i64, i32, i32, i64]
+        L.dsc_headwise_gen_bwd_workspace_size.restype = ctypes.c_size_t
+        L.dsc_headwise_gen_bwd.argtypes = [p, i, i64, i64, i64, i32, i32, i64, p, p, p, p, p, i32, i32, p, p, p,
+                                           p, ctypes.c_size_t]
         L.dsc_bench_stream.argtypes = [p, p, i64, p, i64, i32, i32, i32, i32, i64]
         for f in ("dsc_bench_stream", "dsc_lowrank_bwd_noalloc", "dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd",
                   "dsc_lowrank_bwd_deterministic", "dsc_static_bwd_deterministic",
                   "dsc_static_fwd", "dsc_static_bwd", "dsc_headwise_decode", "dsc_lowrank_decode",
                   "dsc_state_from_prefill", "dsc_rope_table", "dsc_headwise_rope_fwd",
                   "dsc_headwise_rope_bwd", "dsc_headwise_rope_decode", "dsc_lowrank_rope_fwd",
-                  "dsc_lowrank_rope_bwd", "dsc_abi_version"):
+                  "dsc_lowrank_rope_bwd", "dsc_headwise_gen_fwd", "dsc_headwise_gen_bwd", "dsc_abi_version"):
             getattr(L, f).restype = ctypes.c_int
         L.dsc_status_string.argtypes = [i]
         L.dsc_status_string.restype = ctypes.c_char_p
@@ -181,6 +186,33 @@ def dsc_headwise_rope_decode(x, w, state, y, positions, *, rot, head_dim, table,
     _check(lib().dsc_headwise_rope_decode(_stream(stream), _dtype_code(x), B, D, W, D // G if G else 0, _ptr(x),
                                           _ptr(w), _ptr(state), int(bool(residual)), int(rot), int(head_dim), tp,
                                           max_pos, _ptr(positions), _ptr(y)))
+
+
+def dsc_headwise_gen_fwd(h, V, x, y, *, W, cu_seqlens=None, residual=False, stream=None) -> None:
+    """y = head-wise layer on x with filters w = h V^T generated on chip (V is (G*W, K))."""
+    B, T, D = x.shape
+    K = h.shape[2]
+    G = V.shape[0] // W if W else 0
+    cu, ns = _seq(cu_seqlens)
+    _check(lib().dsc_headwise_gen_fwd(_stream(stream), _dtype_code(x), B, T, D, W, D // G if G else 0, K,
+                                      _ptr(h), _ptr(V), _ptr(x), cu, ns, int(bool(residual)), _ptr(y)))
+
+
+def dsc_headwise_gen_bwd_workspace_size(dtype: torch.dtype, B: int, T: int, D: int, W: int, H: int, K: int) -> int:
+    code = DSC_BF16 if dtype == torch.bfloat16 else DSC_FP32
+    return int(lib().dsc_headwise_gen_bwd_workspace_size(code, B, T, D, W, H, K))
+
+
+def dsc_headwise_gen_bwd(h, V, x, dy, dx, dh, dV, workspace=None, *, W, cu_seqlens=None, residual=False,
+                         stream=None) -> None:
+    B, T, D = x.shape
+    K = h.shape[2]
+    G = V.shape[0] // W if W else 0
+    cu, ns = _seq(cu_seqlens)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().dsc_headwise_gen_bwd(_stream(stream), _dtype_code(x), B, T, D, W, D // G if G else 0, K,
+                                      _ptr(h), _ptr(V), _ptr(x), _ptr(dy), cu, ns, int(bool(residual)), _ptr(dx),
+                                      _ptr(dh), _ptr(dV), _ptr(workspace), ws_bytes))
 
 
 def dsc_lowrank_fwd(x, z, U, y, *, W, cu_seqlens=None, residual=False, stream=None) -> None:

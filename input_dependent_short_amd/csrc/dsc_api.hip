@@ -257,6 +257,81 @@ dsc_status dsc_lowrank_rope_fwd(void *stream, int dtype, int64_t B, int64_t T, i
     return launched(dsc::lowrank_rope_fwd(p, (hipStream_t)stream), "dsc_lowrank_rope_fwd launch");
 }
 
+namespace {
+
+// Shape rules of the generated head-wise layer (both directions).
+dsc_status check_gen(int dtype, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H, int64_t K,
+                     const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual) {
+    DSC_TRY(check_common(dtype, B, T, D, W, cu_seqlens, n_seqs, residual));
+    if (H < 1 || D % H) return fail(DSC_ERR_SHAPE, "H = %d must divide D = %lld", H, (long long)D);
+    if (K < 1 || K > (1 << 20)) return fail(DSC_ERR_SHAPE, "K = %lld must be in 1..2^20", (long long)K);
+    if (dtype != DSC_BF16) return fail(DSC_ERR_UNSUPPORTED, "the generated layer is implemented for DSC_BF16 only");
+    if (K % 8) return fail(DSC_ERR_UNSUPPORTED, "K = %lld must be a multiple of 8", (long long)K);
+    if ((D / H) * W % 8)
+        return fail(DSC_ERR_UNSUPPORTED, "(D/H)*W = %lld must be a multiple of 8", (long long)((D / H) * W));
+    return DSC_SUCCESS;
+}
+
+size_t gen_workspace(int64_t N, int64_t D, int32_t W, int32_t H) {
+    return ((size_t)N * (size_t)((D / H) * W) * 2 + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+dsc_status dsc_headwise_gen_fwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H,
+                                int64_t K, const void *h, const void *V, const void *x, const int32_t *cu_seqlens,
+                                int32_t n_seqs, int32_t residual, void *y) {
+    DSC_TRY(check_gen(dtype, B, T, D, W, H, K, cu_seqlens, n_seqs, residual));
+    if (B * T == 0) return ok();
+    if (!h || !V || !x || !y) return fail(DSC_ERR_NULL, "h, V, x and y are required");
+    if (!aligned16(h) || !aligned16(V) || !aligned16(x) || !aligned16(y))
+        return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    const size_t N = (size_t)(B * T), GW = (size_t)((D / H) * W);
+    const Range in[] = {rng("h", h, N * K * 2), rng("V", V, GW * K * 2), rng("x", x, N * D * 2),
+                        rng("cu_seqlens", cu_seqlens, cu_seqlens ? 4u * (n_seqs + 1) : 0)};
+    const Range out[] = {rng("y", y, N * D * 2)};
+    DSC_TRY(check_alias(in, 4, out, 1));
+    dsc::GenProblem p{B * T, T, D, W, H, K, h, V, x, nullptr, y, nullptr, nullptr, nullptr, nullptr,
+                      cu_seqlens, n_seqs, residual};
+    return launched(dsc::headwise_gen_fwd(p, (hipStream_t)stream), "dsc_headwise_gen_fwd launch");
+}
+
+size_t dsc_headwise_gen_bwd_workspace_size(int dtype, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H,
+                                           int64_t K) {
+    if (check_gen(dtype, B, T, D, W, H, K, nullptr, 0, 0) != DSC_SUCCESS) return 0;
+    return gen_workspace(B * T, D, W, H);
+}
+
+dsc_status dsc_headwise_gen_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H,
+                                int64_t K, const void *h, const void *V, const void *x, const void *dy,
+                                const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, void *dx, void *dh,
+                                float *dV, void *workspace, size_t workspace_bytes) {
+    DSC_TRY(check_gen(dtype, B, T, D, W, H, K, cu_seqlens, n_seqs, residual));
+    const size_t GW = (size_t)((D / H) * W);
+    if (B * T == 0) {  // dV is a sum over no tokens: zero
+        if (!dV) return fail(DSC_ERR_NULL, "dV is required");
+        if (!aligned16(dV)) return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+        return launched(dsc::lowrank_zero(dV, (int64_t)(GW * K), (hipStream_t)stream), "dsc_headwise_gen_bwd launch");
+    }
+    if (!h || !V || !x || !dy || !dx || !dh || !dV) return fail(DSC_ERR_NULL, "h, V, x, dy, dx, dh and dV are required");
+    if (!aligned16(h) || !aligned16(V) || !aligned16(x) || !aligned16(dy) || !aligned16(dx) || !aligned16(dh) ||
+        !aligned16(dV))
+        return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    const size_t N = (size_t)(B * T), need = gen_workspace(B * T, D, W, H);
+    if (!workspace || workspace_bytes < need)
+        return fail(DSC_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(DSC_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+    const Range in[] = {rng("h", h, N * K * 2), rng("V", V, GW * K * 2), rng("x", x, N * D * 2),
+                        rng("dy", dy, N * D * 2), rng("cu_seqlens", cu_seqlens, cu_seqlens ? 4u * (n_seqs + 1) : 0)};
+    const Range out[] = {rng("dx", dx, N * D * 2), rng("dh", dh, N * K * 2), rng("dV", dV, GW * K * 4),
+                         rng("workspace", workspace, need)};
+    DSC_TRY(check_alias(in, 5, out, 4));
+    dsc::GenProblem p{B * T, T, D, W, H, K, h, V, x, dy, nullptr, dx, dh, dV, workspace, cu_seqlens, n_seqs,
+                      residual};
+    return launched(dsc::headwise_gen_bwd(p, (hipStream_t)stream), "dsc_headwise_gen_bwd launch");
+}
+
 size_t dsc_lowrank_bwd_workspace_size(int dtype, int64_t B, int64_t T, int64_t D, int32_t W, int32_t R) {
     if (check_common(dtype, B, T, D, W, nullptr, 0, 0) != DSC_SUCCESS || R < 1 || R > 128) return 0;
     return dsc::lowrank_bwd_workspace(dtype == DSC_BF16 ? dsc::Dtype::BF16 : dsc::Dtype::F32, B * T, D, W, R);

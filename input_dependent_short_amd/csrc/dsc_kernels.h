@@ -49,6 +49,23 @@ struct LrProblem {
     int64_t max_pos = 0;
 };
 
+// Head-wise layer whose filters are generated on chip from the hidden state
+// (generator.hip): w[n, g*W + k] = sum_j h[n, j] V[g*W + k, j], bf16 only.
+struct GenProblem {
+    int64_t N, T, D;
+    int32_t W, H;
+    int64_t K;  // hidden width
+    const void *h, *V, *x, *dy;
+    void *y, *dx, *dh;
+    float *dV;
+    void *dw;  // backward workspace: the filter gradient (N, G*W) bf16
+    const int32_t *cu;
+    int32_t n_seqs;
+    int32_t residual;
+};
+hipError_t headwise_gen_fwd(const GenProblem &p, hipStream_t s);
+hipError_t headwise_gen_bwd(const GenProblem &p, hipStream_t s);
+
 // Static short convolution: one filter per channel, the same at every token.
 struct StProblem {
     Dtype dtype;

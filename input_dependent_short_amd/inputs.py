@@ -64,7 +64,8 @@ WORKLOADS = {
 
 
 def seed_for(cfg: int, slot: int) -> int:
-    """Seed of input slot (0 x, 1 w or z, 2 U, 3 dy, 4 segment lengths) of a workload."""
+    """Seed of input slot (0 x, 1 w or z, 2 U, 3 dy, 4 segment lengths, 5 hidden
+    state h, 6 generator weight V) of a workload."""
     return SEED_BASE + 10 * cfg + slot
 
 
@@ -133,6 +134,21 @@ def small(kind: str, B: int, T: int, D: int, W: int, *, H: int = 1, R: int = 0,
                   dtype=dtype, residual=residual, varlen=varlen, seglen_range=seglen_range,
                   cfg=1000 + seed)
     return wl, make_inputs(wl)
+
+
+def generator_inputs(wl: Workload, K: int, *, cfg: int | None = None) -> dict:
+    """Inputs of the head-wise layer whose filters come from a hidden state:
+    those of make_inputs (x, dy, cu_seqlens; the drawn w is dropped) plus the
+    hidden state h (B,T,K) ~ N(0,1) and the generator's weight V (G*W, K) ~
+    N(0, 1/(K*W)), so that the generated filters h V^T have the variance 1/W
+    of the directly drawn ones."""
+    c = wl.cfg if cfg is None else cfg
+    out = make_inputs(wl, cfg=cfg)
+    out.pop("w", None)
+    G = wl.D // wl.H
+    out["h"] = _cast(_normal(seed_for(c, 5), (wl.B, wl.T, K), 1.0), wl.dtype)
+    out["V"] = _cast(_normal(seed_for(c, 6), (G * wl.W, K), float(1.0 / np.sqrt(K * wl.W))), wl.dtype)
+    return out
 
 
 # ---- counter-based inputs, for tensors too large to draw on the host

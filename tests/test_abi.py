@@ -38,7 +38,8 @@ def test_header_declares_the_entry_points():
               "dsc_static_bwd_deterministic", "dsc_static_bwd_deterministic_workspace_size",
               "dsc_headwise_decode", "dsc_lowrank_decode", "dsc_state_from_prefill",
               "dsc_rope_table", "dsc_headwise_rope_fwd", "dsc_headwise_rope_bwd", "dsc_headwise_rope_decode",
-              "dsc_lowrank_rope_fwd", "dsc_lowrank_rope_bwd",
+              "dsc_lowrank_rope_fwd", "dsc_lowrank_rope_bwd", "dsc_headwise_gen_fwd", "dsc_headwise_gen_bwd",
+              "dsc_headwise_gen_bwd_workspace_size",
               "dsc_status_string", "dsc_last_error", "dsc_abi_version"):
         assert s in syms
 
@@ -257,6 +258,32 @@ def test_lowrank_rope_validation(lib):
     assert lb(wsb=16) == 6
     assert lb(ws=P(4)) == 5                          # the workspace overlaps the table
     assert lb(dt=0, ws=None, wsb=0, dx=P(1)) == 5    # fp32 needs no workspace: on to the alias check
+
+
+def test_generator_validation(lib):
+    # generated head-wise layer: B=2 T=8 D=128 W=4 H=16 (G=8, G*W=32), hidden width K=64, bf16
+    def gf(dt=1, B=2, T=8, D=128, W=4, H=16, K=64, h=P(1), V=P(2), x=P(3), cu=None, ns=0, res=1, y=P(4)):
+        return lib.dsc_headwise_gen_fwd(S0, dt, B, T, D, W, H, K, h, V, x, cu, ns, res, y)
+
+    def gb(dt=1, K=64, dy=P(5), dx=P(6), dh=P(7), dV=P(8), ws=P(9), wsb=1 << 20, h=P(1)):
+        return lib.dsc_headwise_gen_bwd(S0, dt, 2, 8, 128, 4, 16, K, h, P(2), P(3), dy, None, 0, 1, dx, dh, dV,
+                                        ws, wsb)
+    size = lambda dt=1, K=64, H=16, W=4: lib.dsc_headwise_gen_bwd_workspace_size(dt, 2, 8, 128, W, H, K)
+    assert gf(dt=0) == 3                             # bf16 only
+    assert gf(H=48) == 2 and gf(H=0) == 2            # H must divide D
+    assert gf(K=0) == 2 and gf(K=12) == 3            # K a multiple of 8
+    assert gf(W=3, H=64) == 3                        # G*W = 6 is not a multiple of 8
+    assert gf(W=9) == 2
+    assert gf(h=None) == 1 and gf(y=ctypes.c_void_p(A * 4 + 2)) == 4
+    assert gf(y=P(3)) == 5 and gf(y=P(1)) == 5       # y overlaps x / h
+    assert gf(B=0, h=None, V=None, x=None, y=None) == 0
+    assert size() == 1024                            # dw (16 tokens, 32 taps) in bf16
+    assert gf(h=P(3), y=P(3)) == 5                   # h may be x; y may not
+    assert size(dt=0) == 0 and size(K=12) == 0
+    assert gb(ws=None, wsb=0) == 6 and gb(wsb=100) == 6
+    assert gb(dh=P(1)) == 5                          # dh overlaps h
+    assert gb(dV=None) == 1 and gb(dx=ctypes.c_void_p(A * 6 + 8)) == 4
+    assert gb(ws=P(5)) == 5                          # the workspace overlaps dy
 
 
 def test_binding_raises_with_message(lib):
