@@ -18,7 +18,8 @@ least 50 calls), the roofline of the dominant entry point, the streaming
 ceiling measured with the library's own streaming kernel, and, as extras, the
 QKV ~150M step (head-wise H=64 and low-rank R=32 at B=8 T=2048 D=2304), the
 static short convolution beside the dynamic head-wise layer, decoding steps,
-the head-wise and low-rank layers fused with the rotary embedding, the fixed-order
+the head-wise and low-rank layers fused with the rotary embedding, the
+head-wise layer with filters generated on chip from a hidden state, the fixed-order
 backward passes, and the fp64 CPU oracle timed on a bounded sample of the
 step's work.
 
@@ -807,6 +808,60 @@ def main() -> int:
             "unfused_extra_bytes": 2 * rot * c.wl.N * c.x.element_size()}
     out["rope_fused"] = rope
     del table
+
+    # The head-wise layer with its filters generated from a hidden state of
+    # width 2048 (the ~2B block's), at the MLP ~2B shape: the fused calls (w
+    # formed on chip, never stored) against the same product written to
+    # memory by this library's matrix-core GEMM (dsc_generate_filters), then
+    # read by the head-wise layer, and against the ROCm GEMM (torch.matmul) in
+    # that role; the backward the same way (library: w, then dx and dw, then
+    # dh and dV).  Back to back, in one loop.
+    log("generated filters")
+    gwl, Kg = inputs.WORKLOADS[4], 2048
+    ginp = inputs.generator_inputs(gwl, Kg)
+    gx, gdy, gV, gh = (ginp[k].to("cuda") for k in ("x", "dy", "V", "h"))
+    del ginp
+    Ng, Gg, Wg = gwl.N, gwl.D // gwl.H, gwl.W
+    gy, gdx = torch.empty_like(gx), torch.empty_like(gx)
+    gdh = torch.empty_like(gh)
+    gdV = torch.empty(gV.shape, dtype=torch.float32, device="cuda")
+    gw_ = torch.empty(gwl.B, gwl.T, Gg, Wg, dtype=torch.bfloat16, device="cuda")
+    gdw = torch.empty_like(gw_)
+    gws = torch.empty(binding.dsc_headwise_gen_bwd_workspace_size(gx.dtype, gwl.B, gwl.T, gwl.D, Wg, gwl.H, Kg),
+                      dtype=torch.uint8, device="cuda")
+    hf, wf, dwf = gh.view(Ng, Kg), gw_.view(Ng, Gg * Wg), gdw.view(Ng, Gg * Wg)
+    res = gwl.residual
+
+    def lib_bwd():
+        torch.matmul(hf, gV.t(), out=wf)
+        binding.dsc_headwise_bwd(gx, gw_, gdy, gdx, gdw, residual=res)
+        torch.matmul(dwf, gV, out=gdh.view(Ng, Kg))
+        gdV.copy_(torch.matmul(dwf.t(), hf))
+
+    gcalls = {
+        "fused_fwd": lambda: binding.dsc_headwise_gen_fwd(gh, gV, gx, gy, W=Wg, residual=res),
+        "fused_bwd": lambda: binding.dsc_headwise_gen_bwd(gh, gV, gx, gdy, gdx, gdh, gdV, gws, W=Wg, residual=res),
+        "own_gemm_w": lambda: binding.dsc_generate_filters(hf, gV, wf),
+        "headwise_fwd": lambda: binding.dsc_headwise_fwd(gx, gw_, gy, residual=res),
+        "library_gemm_w": lambda: torch.matmul(hf, gV.t(), out=wf),
+        "library_path_bwd": lib_bwd,
+    }
+    gt = dict(zip(gcalls, interleaved_s(torch, list(gcalls.values()), reps)))
+    us = {k: round(v * 1e6, 1) for k, v in gt.items()}
+    gflop = 2.0 * Ng * Kg * Gg * Wg
+    out["generator_fused"] = {
+        "workload": f"{gwl.name} with w = h V^T generated from a hidden state of width {Kg} "
+                    f"(B={gwl.B} T={gwl.T} D={gwl.D} W={Wg} H={gwl.H}, V ({Gg * Wg}, {Kg}))",
+        "fused_fwd_us": us["fused_fwd"], "fused_bwd_us": us["fused_bwd"],
+        "unfused_own_gemm_fwd_us": round(us["own_gemm_w"] + us["headwise_fwd"], 1),
+        "unfused_library_gemm_fwd_us": round(us["library_gemm_w"] + us["headwise_fwd"], 1),
+        "unfused_library_bwd_us": us["library_path_bwd"],
+        "own_gemm_TFLOPs": round(gflop / gt["own_gemm_w"] / 1e12, 1),
+        "library_gemm_TFLOPs": round(gflop / gt["library_gemm_w"] / 1e12, 1),
+        "w_round_trip_bytes": 2 * Ng * Gg * Wg * 2,
+        "per_call_us": us}
+    del gx, gdy, gV, gh, gy, gdx, gdh, gdV, gw_, gdw, gws, hf, wf, dwf
+    torch.cuda.empty_cache()
 
     # The reproducible low-rank backward (dz and dU summed in a fixed order
     # through per-block workspace regions) against the fast one, at the

@@ -200,8 +200,24 @@ DSC_API dsc_status dsc_headwise_gen_fwd(void *stream, int dtype, int64_t B, int6
                                         const int32_t *cu_seqlens, int32_t n_seqs, int32_t residual, void *y);
 
 /*
- * Bytes of device workspace dsc_headwise_gen_bwd needs: the filter gradient
- * dw (B*T, G*W) in bf16, rounded up to 256.  0 for invalid sizes.
+ * The filter generator alone: w[n, c] = sum_{j<K} h[n, j] * V[c, j] for the
+ * N rows of h, i.e. the filters that dsc_headwise_gen_fwd forms on chip,
+ * written out (w (N, C) bf16 is the (B,T,G,W) filter tensor of
+ * dsc_headwise_fwd when C = G*W).  Same matrix-core product and rounding as
+ * the fused layer (bf16 operands, fp32 sums, one rounding to bf16).
+ *   h (N, K) in;  V (C, K) in;  w (N, C) out.  DSC_BF16 only; K and C
+ *   multiples of 8 (else DSC_ERR_UNSUPPORTED); K <= 2^20, C <= 2^24.
+ */
+DSC_API dsc_status dsc_generate_filters(void *stream, int dtype, int64_t N, int64_t K, int64_t C, const void *h,
+                                        const void *V, void *w);
+
+/*
+ * Bytes of device workspace dsc_headwise_gen_bwd needs (0 for invalid
+ * sizes): the filter gradient dw (B*T, G*W) in bf16, transposed bf16 copies
+ * of V, dw and h (the two products read every operand along its reduced
+ * dimension), and, when the sum over tokens of dV is split to fill the
+ * device, the fp32 partial sums of each split (added in a fixed order).  It
+ * depends on the sizes only.
  */
 DSC_API size_t dsc_headwise_gen_bwd_workspace_size(int dtype, int64_t B, int64_t T, int64_t D, int32_t W,
                                                    int32_t H, int64_t K);
@@ -212,7 +228,7 @@ DSC_API size_t dsc_headwise_gen_bwd_workspace_size(int dtype, int64_t B, int64_t
  *   dw[n, g*W+k] = sum_{d in group g, n-k in n's sequence} dy[n,d] * x[n-k,d],
  *   dh[n, j] = sum_c dw[n, c] * V[c, j],    dV[c, j] = sum_n dw[n, c] * h[n, j].
  * w is generated again on chip (not stored by the forward); dw is rounded to
- * bf16 once, in the workspace, and both products read it there.
+ * bf16 once, in the workspace, and both products read it from there.
  *   dx (B,T,D) bf16 out;  dh (B,T,K) bf16 out;  dV (G*W, K) fp32 out (zero
  *   for an empty batch).  When h is x, the caller adds dh to dx.
  *   workspace: at least dsc_headwise_gen_bwd_workspace_size() bytes, 16-byte

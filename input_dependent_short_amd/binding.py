@@ -68,13 +68,15 @@ def lib() -> ctypes.CDLL:
         L.dsc_headwise_gen_bwd_workspace_size.restype = ctypes.c_size_t
         L.dsc_headwise_gen_bwd.argtypes = [p, i, i64, i64, i64, i32, i32, i64, p, p, p, p, p, i32, i32, p, p, p,
                                            p, ctypes.c_size_t]
+        L.dsc_generate_filters.argtypes = [p, i, i64, i64, i64, p, p, p]
         L.dsc_bench_stream.argtypes = [p, p, i64, p, i64, i32, i32, i32, i32, i64]
         for f in ("dsc_bench_stream", "dsc_lowrank_bwd_noalloc", "dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd",
                   "dsc_lowrank_bwd_deterministic", "dsc_static_bwd_deterministic",
                   "dsc_static_fwd", "dsc_static_bwd", "dsc_headwise_decode", "dsc_lowrank_decode",
                   "dsc_state_from_prefill", "dsc_rope_table", "dsc_headwise_rope_fwd",
                   "dsc_headwise_rope_bwd", "dsc_headwise_rope_decode", "dsc_lowrank_rope_fwd",
-                  "dsc_lowrank_rope_bwd", "dsc_headwise_gen_fwd", "dsc_headwise_gen_bwd", "dsc_abi_version"):
+                  "dsc_lowrank_rope_bwd", "dsc_headwise_gen_fwd", "dsc_headwise_gen_bwd", "dsc_generate_filters",
+                  "dsc_abi_version"):
             getattr(L, f).restype = ctypes.c_int
         L.dsc_status_string.argtypes = [i]
         L.dsc_status_string.restype = ctypes.c_char_p
@@ -196,6 +198,14 @@ def dsc_headwise_gen_fwd(h, V, x, y, *, W, cu_seqlens=None, residual=False, stre
     cu, ns = _seq(cu_seqlens)
     _check(lib().dsc_headwise_gen_fwd(_stream(stream), _dtype_code(x), B, T, D, W, D // G if G else 0, K,
                                       _ptr(h), _ptr(V), _ptr(x), cu, ns, int(bool(residual)), _ptr(y)))
+
+
+def dsc_generate_filters(h, V, w, stream=None) -> None:
+    """w (N, C) = h (N, K) V (C, K)^T on the matrix cores (bf16)."""
+    K = h.shape[-1]
+    N = h.numel() // K if K else 0
+    C = V.shape[0]
+    _check(lib().dsc_generate_filters(_stream(stream), _dtype_code(h), N, K, C, _ptr(h), _ptr(V), _ptr(w)))
 
 
 def dsc_headwise_gen_bwd_workspace_size(dtype: torch.dtype, B: int, T: int, D: int, W: int, H: int, K: int) -> int:

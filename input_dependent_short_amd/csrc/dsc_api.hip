@@ -272,9 +272,6 @@ dsc_status check_gen(int dtype, int64_t B, int64_t T, int64_t D, int32_t W, int3
     return DSC_SUCCESS;
 }
 
-size_t gen_workspace(int64_t N, int64_t D, int32_t W, int32_t H) {
-    return ((size_t)N * (size_t)((D / H) * W) * 2 + 255) & ~(size_t)255;
-}
 
 }  // namespace
 
@@ -296,10 +293,29 @@ dsc_status dsc_headwise_gen_fwd(void *stream, int dtype, int64_t B, int64_t T, i
     return launched(dsc::headwise_gen_fwd(p, (hipStream_t)stream), "dsc_headwise_gen_fwd launch");
 }
 
+dsc_status dsc_generate_filters(void *stream, int dtype, int64_t N, int64_t K, int64_t C, const void *h,
+                                const void *V, void *w) {
+    if (dtype != DSC_BF16 && dtype != DSC_FP32) return fail(DSC_ERR_SHAPE, "dtype %d is not DSC_FP32 or DSC_BF16", dtype);
+    if (N < 0 || K < 1 || K > (1 << 20) || C < 1 || C > (1 << 24))
+        return fail(DSC_ERR_SHAPE, "N = %lld, K = %lld, C = %lld out of range", (long long)N, (long long)K,
+                    (long long)C);
+    if (dtype != DSC_BF16) return fail(DSC_ERR_UNSUPPORTED, "the filter generator is implemented for DSC_BF16 only");
+    if (K % 8 || C % 8) return fail(DSC_ERR_UNSUPPORTED, "K and C must be multiples of 8");
+    if (N == 0) return ok();
+    if (!h || !V || !w) return fail(DSC_ERR_NULL, "h, V and w are required");
+    if (!aligned16(h) || !aligned16(V) || !aligned16(w)) return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    const Range in[] = {rng("h", h, (size_t)N * K * 2), rng("V", V, (size_t)C * K * 2)};
+    const Range out[] = {rng("w", w, (size_t)N * C * 2)};
+    DSC_TRY(check_alias(in, 2, out, 1));
+    return launched(dsc::generate_filters(static_cast<const uint16_t *>(h), static_cast<const uint16_t *>(V), N, K, C,
+                                          static_cast<uint16_t *>(w), (hipStream_t)stream),
+                    "dsc_generate_filters launch");
+}
+
 size_t dsc_headwise_gen_bwd_workspace_size(int dtype, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H,
                                            int64_t K) {
     if (check_gen(dtype, B, T, D, W, H, K, nullptr, 0, 0) != DSC_SUCCESS) return 0;
-    return gen_workspace(B * T, D, W, H);
+    return dsc::headwise_gen_bwd_workspace(B * T, D, W, H, K);
 }
 
 dsc_status dsc_headwise_gen_bwd(void *stream, int dtype, int64_t B, int64_t T, int64_t D, int32_t W, int32_t H,
@@ -317,7 +333,7 @@ dsc_status dsc_headwise_gen_bwd(void *stream, int dtype, int64_t B, int64_t T, i
     if (!aligned16(h) || !aligned16(V) || !aligned16(x) || !aligned16(dy) || !aligned16(dx) || !aligned16(dh) ||
         !aligned16(dV))
         return fail(DSC_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
-    const size_t N = (size_t)(B * T), need = gen_workspace(B * T, D, W, H);
+    const size_t N = (size_t)(B * T), need = dsc::headwise_gen_bwd_workspace(B * T, D, W, H, K);
     if (!workspace || workspace_bytes < need)
         return fail(DSC_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need,
                     workspace ? workspace_bytes : (size_t)0);

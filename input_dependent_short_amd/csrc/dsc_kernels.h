@@ -58,13 +58,20 @@ struct GenProblem {
     const void *h, *V, *x, *dy;
     void *y, *dx, *dh;
     float *dV;
-    void *dw;  // backward workspace: the filter gradient (N, G*W) bf16
+    void *dw;  // backward workspace (headwise_gen_bwd_workspace bytes), the filter gradient first
     const int32_t *cu;
     int32_t n_seqs;
     int32_t residual;
 };
 hipError_t headwise_gen_fwd(const GenProblem &p, hipStream_t s);
+// Workspace bytes of headwise_gen_bwd (p.dw points at it): the filter
+// gradient, the transposed operands of dh and dV, and dV's split partials.
+size_t headwise_gen_bwd_workspace(int64_t N, int64_t D, int32_t W, int32_t H, int64_t K);
 hipError_t headwise_gen_bwd(const GenProblem &p, hipStream_t s);
+// w (N x C) = h (N x K) . V (C x K)^T in bf16 (fp32 sums), on the same
+// matrix-core GEMM as the fused layer.
+hipError_t generate_filters(const uint16_t *h, const uint16_t *V, int64_t N, int64_t K, int64_t C, uint16_t *w,
+                            hipStream_t s);
 
 // Static short convolution: one filter per channel, the same at every token.
 struct StProblem {

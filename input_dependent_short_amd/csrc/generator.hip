@@ -20,150 +20,178 @@
 // forms dx and the filter gradient dw of the tile's tokens in the epilogue,
 // and writes dw once (bf16) for the two products dh = dw V and dV = dw^T h,
 // which the same GEMM core runs with plain epilogues.
+#include <algorithm>
+
 #include "dsc_common.h"
 #include "dsc_kernels.h"
 
 namespace dsc {
 namespace {
 
-constexpr int kGBlock = 256;   // 4 waves; wave v owns tile rows [32v, 32v + 32)
-constexpr int kBM = 128;       // tile rows (GEMM M)
-constexpr int kBK = 64;        // K per LDS stage
-constexpr int kLdk = kBK + 8;  // LDS row stride (bf16) of the operand tiles: 144 B, conflict-free 16-byte row reads
+constexpr int kGBlock = 256;  // 4 waves
+constexpr int kBM = 128;      // tile rows (GEMM M)
 
 // Groups per tile: BN = TG*W columns of w (a multiple of 16 for any W <= 8).
 constexpr int gen_tg(int W) { return W <= 4 ? 32 : 16; }
 
-// Global -> register -> LDS staging of one operand tile of BR rows (rows of A
-// or columns of B) by kBK k, stored K-contiguous in LDS ([BR][kLdk] bf16).
-// KC: element (r, k) sits at p[r*ld + k] (k contiguous, K % 8 == 0); else at
-// p[k*ld + r] (r contiguous, rows % 8 == 0): a thread then reads 8 rows at 4
-// consecutive k and transposes them in registers.  Out-of-range elements are
-// zero.
-template <int BR, bool KC>
-struct TileLoader {
-    static constexpr int kUnits = KC ? BR * (kBK / 8) : (BR / 8) * (kBK / 4);
-    static constexpr int kPer = (kUnits + kGBlock - 1) / kGBlock;
-    static constexpr int kRegs = KC ? kPer : 4 * kPer;
-    uint4 v[kRegs];
+// ------------------------------------------- matrix-core GEMM, direct loads
+//
+// The products whose operands are both K-contiguous (the generator h V^T and
+// dh = dw V^T... with V transposed) run a four-stage pipeline: each stage is
+// a kDBK = 32 slice of K, loaded by buffer_load ... lds straight from memory
+// into LDS (no registers), three stages ahead of the matrix cores.  A stage
+// holds the A tile (kBM rows) then the B tile (BN <= 128 rows), rows of 64
+// bytes whose four 16-byte chunks are placed at chunk ^ chunk_swz(row), chunk_swz(r) =
+// ((r >> 1) ^ (r >> 2)) & 3, so that the 16 rows a fragment read touches fall
+// on distinct banks whether the LDS serves 16 lanes over 64 banks or 8 lanes
+// over 32 banks per cycle (measured: the plain (r >> 2) placement left four
+// conflict cycles per LDS instruction cycle).  Each
+// stage is an LDS array of its own, so the compiler can tell which load a
+// fragment read waits for; a stage is refilled only after a barrier that all
+// waves pass once they are done reading it.  Out-of-range rows lie past the
+// buffer resource and out-of-range k take the offset kFar: both read as zero.
 
-    __device__ __forceinline__ void load(const uint16_t *p, int64_t ld, int64_t rows, int64_t K, int64_t r0,
-                                         int64_t k0, int tid) {
-        const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int u = tid + i * kGBlock;
-            if constexpr (KC) {
-                const int64_t gr = r0 + (u >> 3), gk = k0 + (u & 7) * 8;
-                v[i] = (u < kUnits && gr < rows && gk < K) ? *reinterpret_cast<const uint4 *>(p + gr * ld + gk)
-                                                           : zero;
-            } else {
-                const int64_t gr = r0 + (u % (BR / 8)) * 8, gk = k0 + (u / (BR / 8)) * 4;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    v[4 * i + j] = (u < kUnits && gr < rows && gk + j < K)
-                                       ? *reinterpret_cast<const uint4 *>(p + (gk + j) * ld + gr)
-                                       : zero;
-            }
-        }
-    }
+constexpr int kDBK = 32;
+__device__ __forceinline__ int chunk_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+constexpr int kDStage = 16384;  // bytes per stage: A 128 x 64 B, B up to 128 x 64 B
+typedef __attribute__((address_space(3))) void lds_void;
 
-    __device__ __forceinline__ void store(uint16_t *lds, int tid) const {
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int u = tid + i * kGBlock;
-            if (u >= kUnits) break;
-            if constexpr (KC) {
-                *reinterpret_cast<uint4 *>(lds + (u >> 3) * kLdk + (u & 7) * 8) = v[i];
-            } else {
-                const int rc = (u % (BR / 8)) * 8, kq = (u / (BR / 8)) * 4;
-                const uint32_t w[4][4] = {{v[4 * i].x, v[4 * i].y, v[4 * i].z, v[4 * i].w},
-                                          {v[4 * i + 1].x, v[4 * i + 1].y, v[4 * i + 1].z, v[4 * i + 1].w},
-                                          {v[4 * i + 2].x, v[4 * i + 2].y, v[4 * i + 2].z, v[4 * i + 2].w},
-                                          {v[4 * i + 3].x, v[4 * i + 3].y, v[4 * i + 3].z, v[4 * i + 3].w}};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    // element e (row rc + e) of the four k rows
-                    auto el = [&](int j) { return (w[j][e >> 1] >> (16 * (e & 1))) & 0xffffu; };
-                    *reinterpret_cast<uint2 *>(lds + (rc + e) * kLdk + kq) =
-                        make_uint2(el(0) | (el(1) << 16), el(2) | (el(3) << 16));
-                }
-            }
-        }
-    }
+// The four stage arrays of a block.
+struct Stages {
+    unsigned char *s[4];
 };
 
-// C[kBM x BN] tile = A[m0 .., :] . B[n0 .., :]^T over the whole K, fp32 in
-// registers: acc[mf][nf][j] is C[32v + 16mf + 4(lane>>4) + j][16nf + (lane&15)]
-// for wave v.  `lds` holds two stages of both operand tiles.  Ends with a
-// barrier, after which the LDS may be reused.
-template <int BN, bool AKC, bool BKC>
-__device__ __forceinline__ void gemm_tile(const uint16_t *A, int64_t lda, int64_t M, const uint16_t *B,
-                                          int64_t ldb, int64_t Nc, int64_t K, int64_t m0, int64_t n0,
-                                          uint16_t *lds, floatx4 (&acc)[2][BN / 16]) {
-    constexpr int NF = BN / 16;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint16_t *As[2] = {lds, lds + kBM * kLdk};
-    uint16_t *Bs[2] = {lds + 2 * kBM * kLdk, lds + 2 * kBM * kLdk + BN * kLdk};
+// Wave layout of a kBM x BN tile: WM x WN waves, each MF x NF fragments of 16 x 16.
+template <int BN>
+struct DLayout {
+    static constexpr int WN = (BN / 2) % 16 == 0 ? 2 : 1, WM = 4 / WN;
+    static constexpr int MF = kBM / WM / 16, NF = BN / WN / 16;
+};
+
+// Direct loads of one operand tile (BR rows, kDBK k from k0) into dst.  A
+// wave instruction fills 64 consecutive 16-byte slots; the BR/16 of them are
+// spread over the 4 waves, and a wave with no instruction left repeats the
+// last one (same bytes to the same place), so every wave issues the same
+// count per tile.
+template <int BR>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, int64_t ld, int64_t k0, int64_t K,
+                                         unsigned char *dst, int wave, int lane) {
+    constexpr int kInst = BR / 16, kPer = (kInst + 3) / 4;
 #pragma unroll
-    for (int mf = 0; mf < 2; ++mf)
-#pragma unroll
-        for (int nf = 0; nf < NF; ++nf) acc[mf][nf] = floatx4{0.f, 0.f, 0.f, 0.f};
-    TileLoader<kBM, AKC> la;
-    TileLoader<BN, BKC> lb;
-    const int64_t nk = (K + kBK - 1) / kBK;
-    la.load(A, lda, M, K, m0, 0, tid);
-    lb.load(B, ldb, Nc, K, n0, 0, tid);
-    la.store(As[0], tid);
-    lb.store(Bs[0], tid);
-    __syncthreads();
-    const int arow = 32 * wave + (lane & 15), kofs = 8 * (lane >> 4);
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        const int cur = (int)(kt & 1);
-        if (kt + 1 < nk) {
-            la.load(A, lda, M, K, m0, (kt + 1) * kBK, tid);
-            lb.load(B, ldb, Nc, K, n0, (kt + 1) * kBK, tid);
-        }
-#pragma unroll
-        for (int kk = 0; kk < kBK; kk += 32) {
-            bf16x8 a[2], b[NF];
-#pragma unroll
-            for (int mf = 0; mf < 2; ++mf)
-                a[mf] = *reinterpret_cast<const bf16x8 *>(As[cur] + (arow + 16 * mf) * kLdk + kk + kofs);
-#pragma unroll
-            for (int nf = 0; nf < NF; ++nf)
-                b[nf] = *reinterpret_cast<const bf16x8 *>(Bs[cur] + (16 * nf + (lane & 15)) * kLdk + kk + kofs);
-#pragma unroll
-            for (int mf = 0; mf < 2; ++mf)
-#pragma unroll
-                for (int nf = 0; nf < NF; ++nf)
-                    acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mf], b[nf], acc[mf][nf], 0, 0, 0);
-        }
-        if (kt + 1 < nk) {
-            la.store(As[cur ^ 1], tid);
-            lb.store(Bs[cur ^ 1], tid);
-        }
-        __syncthreads();
+    for (int j = 0; j < kPer; ++j) {
+        const int i = wave + 4 * j < kInst ? wave + 4 * j : kInst - 1;
+        const int slot = 64 * i + lane;
+        const int row = slot >> 2, logical = (slot & 3) ^ chunk_swz(row);
+        const int64_t kk = k0 + 8 * logical;
+        // k past K: bit 31 set, past every tile's resource (a tile spans < 2^31 bytes); arithmetic rather
+        // than a select, which the compiler would turn into a branch around the load
+        const uint32_t off = (uint32_t)(((int64_t)row * ld + kk) * 2) | ((uint32_t)(kk >= K) << 31);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + 1024 * i), 16, off, 0, 0, 0);
     }
 }
 
-template <int BN>
-constexpr int gemm_lds_bytes() {
-    return 2 * (kBM + BN) * kLdk * 2;
+template <int BR>
+constexpr int dma_per_wave() {
+    return (BR / 16 + 3) / 4;
 }
 
-// The accumulators into an fp32 LDS tile [kBM][BN + 4].
+// C[kBM x BN] = A[m0 .., :] . B[n0 .., :]^T (both K-contiguous, K % 8 == 0),
+// fp32: acc[mf][nf][j] = C[RM*wm + 16mf + 4(lane>>4) + j][RN*wn + 16nf + (lane&15)]
+// with RM = kBM/WM, RN = BN/WN, (wm, wn) = (wave / WN, wave % WN).  Ends with
+// every load landed and a barrier: the stages may then be reused.
 template <int BN>
-__device__ __forceinline__ void park(const floatx4 (&acc)[2][BN / 16], float *Cs) {
-    constexpr int ld = BN + 4;
+__device__ __forceinline__ void dma_gemm(const uint16_t *A, int64_t lda, int64_t M, const uint16_t *B, int64_t ldb,
+                                         int64_t Nc, int64_t K, int64_t m0, int64_t n0, const Stages &S,
+                                         floatx4 (&acc)[DLayout<BN>::MF][DLayout<BN>::NF]) {
+    using L = DLayout<BN>;
+    constexpr int kPerTile = dma_per_wave<kBM>() + dma_per_wave<BN>();
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / L::WN, wn = wave % L::WN;
+    const int64_t mr = min((int64_t)kBM, M - m0), nr = min((int64_t)BN, Nc - n0);
+    const __amdgpu_buffer_rsrc_t ra = make_stream(A + m0 * lda, mr > 0 ? mr * lda * 2 : 0);
+    const __amdgpu_buffer_rsrc_t rb = make_stream(B + n0 * ldb, nr > 0 ? nr * ldb * 2 : 0);
+#pragma unroll
+    for (int mf = 0; mf < L::MF; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < L::NF; ++nf) acc[mf][nf] = floatx4{0.f, 0.f, 0.f, 0.f};
+    auto issue = [&](int64_t t, unsigned char *st) {
+        dma_tile<kBM>(ra, lda, t * kDBK, K, st, wave, lane);
+        dma_tile<BN>(rb, ldb, t * kDBK, K, st + 8192, wave, lane);
+    };
+    // fragment rows: A rows RM*wm + 16mf + (lane&15), B rows RN*wn + 16nf + (lane&15); chunk lane>>4
+    const int c = lane >> 4;
+    int aoff[L::MF], boff[L::NF];
+#pragma unroll
+    for (int mf = 0; mf < L::MF; ++mf) {
+        const int r = (kBM / L::WM) * wm + 16 * mf + (lane & 15);
+        aoff[mf] = r * 64 + 16 * (c ^ chunk_swz(r));
+    }
+#pragma unroll
+    for (int nf = 0; nf < L::NF; ++nf) {
+        const int r = (BN / L::WN) * wn + 16 * nf + (lane & 15);
+        boff[nf] = 8192 + r * 64 + 16 * (c ^ chunk_swz(r));
+    }
+    auto compute = [&](const unsigned char *st) {
+        bf16x8 a[L::MF], b[L::NF];
+#pragma unroll
+        for (int mf = 0; mf < L::MF; ++mf) a[mf] = *reinterpret_cast<const bf16x8 *>(st + aoff[mf]);
+#pragma unroll
+        for (int nf = 0; nf < L::NF; ++nf) b[nf] = *reinterpret_cast<const bf16x8 *>(st + boff[nf]);
+#pragma unroll
+        for (int mf = 0; mf < L::MF; ++mf)
+#pragma unroll
+            for (int nf = 0; nf < L::NF; ++nf)
+                acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mf], b[nf], acc[mf][nf], 0, 0, 0);
+    };
+    // tile t waits until only the loads of tiles t+1, t+2 are in flight, then
+    // a barrier makes every wave's loads of tile t visible (and ends every
+    // wave's reads of the stage that tile t+3 refills)
+    auto step = [&](int64_t t, unsigned char *cur, unsigned char *refill) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPerTile) : "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue(t + 3, refill);
+        compute(cur);
+    };
+    const int64_t nk = (K + kDBK - 1) / kDBK;
+    issue(0, S.s[0]);
+    issue(1, S.s[1]);
+    issue(2, S.s[2]);
+    // whole rounds of four tiles: tiles past nk read as zero and add nothing
+    for (int64_t t = 0; t < nk; t += 4) {
+        step(t, S.s[0], S.s[3]);
+        step(t + 1, S.s[1], S.s[0]);
+        step(t + 2, S.s[2], S.s[1]);
+        step(t + 3, S.s[3], S.s[2]);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+}
+
+// The fp32 result tile of dma_gemm parked in the four stages: row r in stage
+// r / 32 at (r % 32) * BN floats (kBM * BN * 4 <= 4 * kDStage).
+struct CsView {
+    unsigned char *s[4];
+    int bn;
+    __device__ __forceinline__ const float *row(int r) const {
+        return reinterpret_cast<const float *>(s[r >> 5]) + (r & 31) * bn;
+    }
+    __device__ __forceinline__ float *wrow(int r) const { return reinterpret_cast<float *>(s[r >> 5]) + (r & 31) * bn; }
+};
+
+template <int BN>
+__device__ __forceinline__ void dma_park(const floatx4 (&acc)[DLayout<BN>::MF][DLayout<BN>::NF], const CsView &cs) {
+    using L = DLayout<BN>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / L::WN, wn = wave % L::WN;
 #pragma unroll
-    for (int mf = 0; mf < 2; ++mf)
+    for (int mf = 0; mf < L::MF; ++mf)
 #pragma unroll
-        for (int nf = 0; nf < BN / 16; ++nf)
+        for (int nf = 0; nf < L::NF; ++nf)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                Cs[(32 * wave + 16 * mf + 4 * (lane >> 4) + j) * ld + 16 * nf + (lane & 15)] = acc[mf][nf][j];
+                cs.wrow((kBM / L::WM) * wm + 16 * mf + 4 * (lane >> 4) + j)[(BN / L::WN) * wn + 16 * nf + (lane & 15)] =
+                    acc[mf][nf][j];
 }
 
 struct GenParams {
@@ -193,13 +221,64 @@ __device__ __forceinline__ void store8(uint16_t *p, const float (&v)[8]) {
 
 __device__ __forceinline__ float ld_bf16(const uint16_t *p) { return __uint_as_float((uint32_t)*p << 16); }
 
+constexpr int kSeg = 16;  // tokens one thread walks in the epilogues
+
+// Row n of x (clamped into [0, N)) as raw bf16 bits, 8 channels from c.
+__device__ __forceinline__ uint4 row8(const uint16_t *base, int64_t n, int64_t N, int64_t D, int64_t c) {
+    const int64_t r = n < 0 ? 0 : (n >= N ? N - 1 : n);
+    return *reinterpret_cast<const uint4 *>(base + r * D + c);
+}
+
+__device__ __forceinline__ float elem8(const uint4 &v, int e) {
+    const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+    return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+// y of tokens n0 + t0 .. + kSeg - 1 (those below N) for channels c .. c+7.
+// UNI: the 8 channels share one group (H % 8 == 0): one filter read per tap.
+template <int W, bool UNI>
+__device__ __forceinline__ void fwd_walk(const GenParams &p, const CsView &cs, const int64_t *seq_start,
+                                         int64_t n0, int t0, int64_t c, int64_t g0) {
+    constexpr int NR = kSeg + W - 1;
+    uint4 xr[NR];  // rows n0 + t0 - (W-1) + i
+#pragma unroll
+    for (int i = 0; i < NR; ++i) xr[i] = row8(p.x, n0 + t0 - (W - 1) + i, p.N, p.D, c);
+    int col[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) col[e] = (int)((c + (UNI ? 0 : e)) / p.H - g0) * W;
+#pragma unroll
+    for (int j = 0; j < kSeg; ++j) {
+        const int t = t0 + j;
+        const int64_t n = n0 + t;
+        if (n >= p.N) break;
+        const int64_t s = seq_start[t];
+        const float *wrow = cs.row(t);
+        float out[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] = p.rho * elem8(xr[j + W - 1], e);
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+            const bool in = n - k >= s;
+            if constexpr (UNI) {
+                const float wk = in ? wrow[col[0] + k] : 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) out[e] = __builtin_fmaf(wk, elem8(xr[j + W - 1 - k], e), out[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    out[e] = __builtin_fmaf(in ? wrow[col[e] + k] : 0.f, elem8(xr[j + W - 1 - k], e), out[e]);
+            }
+        }
+        store8(p.y + n * p.D + c, out);
+    }
+}
+
 // Forward: block = (token tile, group tile), walked so that the group tiles
 // of one token tile (which share its rows of h) run on one XCD.
 template <int W>
-__global__ __launch_bounds__(kGBlock) void gen_fwd_kernel(GenParams p) {
-    constexpr int TG = gen_tg(W), BN = TG * W, LDC = BN + 4;
-    constexpr int kLds = gemm_lds_bytes<BN>() > kBM * LDC * 4 ? gemm_lds_bytes<BN>() : kBM * LDC * 4;
-    __shared__ __align__(16) unsigned char lds[kLds];
+__global__ __launch_bounds__(kGBlock, 2) void gen_fwd_kernel(GenParams p) {
+    constexpr int TG = gen_tg(W), BN = TG * W;
+    __shared__ __align__(16) unsigned char st0[kDStage], st1[kDStage], st2[kDStage], st3[kDStage];
     __shared__ int64_t seq_start[kBM];
     const int64_t lb = xcd_block_id(blockIdx.x, (int64_t)gridDim.x);
     const int64_t tn = lb / p.ntiles_g, tg = lb - tn * p.ntiles_g;
@@ -210,55 +289,99 @@ __global__ __launch_bounds__(kGBlock) void gen_fwd_kernel(GenParams p) {
         p.seq.find(n0 + tid, s, e);
         seq_start[tid] = s;
     }
-    floatx4 acc[2][BN / 16];
-    gemm_tile<BN, true, true>(p.h, p.K, p.N, p.V, p.K, p.G * W, p.K, n0, g0 * W,
-                              reinterpret_cast<uint16_t *>(lds), acc);
-    float *Cs = reinterpret_cast<float *>(lds);
-    park<BN>(acc, Cs);
+    const Stages S{{st0, st1, st2, st3}};
+    floatx4 acc[DLayout<BN>::MF][DLayout<BN>::NF];
+    dma_gemm<BN>(p.h, p.K, p.N, p.V, p.K, p.G * W, p.K, n0, g0 * W, S, acc);
+    const CsView cs{{st0, st1, st2, st3}, BN};
+    dma_park<BN>(acc, cs);
     __syncthreads();
 
     // y of the tile's tokens over the channels of groups [g0, g0 + gcount):
-    // one (token, 8-channel chunk) per item, consecutive threads along a row
+    // a thread walks kSeg consecutive tokens of one 8-channel chunk, with the
+    // kSeg + W - 1 rows of x it reads loaded up front (no load depends on a
+    // branch); consecutive threads take consecutive chunks of the same rows
     const int64_t gcount = min((int64_t)TG, p.G - g0);
     const int64_t c0 = g0 * p.H;
     const int nchunks = (int)(gcount * p.H / 8);
-    const int64_t D = p.D;
-    for (int it = tid; it < kBM * nchunks; it += kGBlock) {
-        const int t = it / nchunks, q = it - t * nchunks;
-        const int64_t n = n0 + t;
-        if (n >= p.N) break;  // items are in token order
-        const int64_t c = c0 + 8 * q;
-        int col[8];  // the column of tap 0 of each channel's group in the tile
+    const bool uniform = p.H % 8 == 0;  // a chunk's 8 channels share one group
+    for (int it = tid; it < nchunks * (kBM / kSeg); it += kGBlock) {
+        const int sg = it / nchunks, q = it - sg * nchunks;
+        if (n0 + kSeg * sg >= p.N) break;  // items are in segment order
+        if (uniform) fwd_walk<W, true>(p, cs, seq_start, n0, kSeg * sg, c0 + 8 * q, g0);
+        else fwd_walk<W, false>(p, cs, seq_start, n0, kSeg * sg, c0 + 8 * q, g0);
+    }
+}
+
+// dx and dw of tokens n0 + t0 .. + kSeg - 1 (those below N and inside the
+// tile's kStep outputs) for channels c .. c+7 of group g (column gl of the
+// tile), H % 8 == 0.  The group's cpg = H/8 chunks sit on cpg consecutive
+// lanes (a power of two, aligned), which sum dw with butterfly shuffles; the
+// first of them stores it.  All rows are loaded before they are used.
+template <int W>
+__device__ __forceinline__ void bwd_walk(const GenParams &p, const CsView &cs, const int64_t *seq_start,
+                                         const int64_t *seq_end, int64_t n0, int t0, int kStep, int64_t c, int gl,
+                                         int64_t g, int cpg, bool lead) {
+    constexpr int NR = kSeg + W - 1;
+    const int64_t N = p.N, D = p.D;
+    uint4 gr[NR];  // dy rows n0 + t0 + i
 #pragma unroll
-        for (int e = 0; e < 8; ++e) col[e] = (int)((c + e) / p.H - g0) * W;
-        const float *wrow = Cs + t * LDC;
-        float xv[8], out[8];
-        load8(p.x + n * D + c, xv);
+    for (int i = 0; i < NR; ++i) gr[i] = row8(p.dy, n0 + t0 + i, N, D, c);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) out[e] = __builtin_fmaf(wrow[col[e]], xv[e], p.rho * xv[e]);
-        const int64_t s = seq_start[t];
+    for (int j = 0; j < kSeg; ++j) {
+        const int t = t0 + j;
+        const int64_t m = n0 + t;
+        if (t >= kStep || m >= N) break;
+        const int64_t e_ = seq_end[t];
+        float out[8];
 #pragma unroll
-        for (int k = 1; k < W; ++k) {
-            if (n - k < s) break;
-            float xk[8];
-            load8(p.x + (n - k) * D + c, xk);
+        for (int e = 0; e < 8; ++e) out[e] = p.rho * elem8(gr[j], e);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) out[e] = __builtin_fmaf(wrow[col[e] + k], xk[e], out[e]);
+        for (int k = 0; k < W; ++k) {
+            const float wk = m + k < e_ ? cs.row(t + k)[gl * W + k] : 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) out[e] = __builtin_fmaf(wk, elem8(gr[j + k], e), out[e]);
         }
-        store8(p.y + n * D + c, out);
+        store8(p.dx + m * D + c, out);
+    }
+    uint4 xr[NR];  // x rows n0 + t0 - (W-1) + i
+#pragma unroll
+    for (int i = 0; i < NR; ++i) xr[i] = row8(p.x, n0 + t0 - (W - 1) + i, N, D, c);
+    const int64_t GW = p.G * W;
+#pragma unroll
+    for (int j = 0; j < kSeg; ++j) {
+        const int t = t0 + j;
+        const int64_t m = n0 + t;
+        if (t >= kStep || m >= N) break;
+        const int64_t s_ = seq_start[t];
+        float dws[W];
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+            float v = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v = __builtin_fmaf(elem8(gr[j], e), elem8(xr[j + W - 1 - k], e), v);
+            dws[k] = m - k >= s_ ? v : 0.f;
+        }
+        for (int off = 1; off < cpg; off <<= 1)
+#pragma unroll
+            for (int k = 0; k < W; ++k) dws[k] += __shfl_xor(dws[k], off);
+        if (lead) {
+            uint16_t *dst = p.dw + m * GW + g * W;
+#pragma unroll
+            for (int k = 0; k < W; ++k) dst[k] = to_bf16(dws[k]);
+        }
     }
 }
 
 // Backward, w recomputed: tile rows [n0, n0 + kBM) with n0 = tile * kStep;
-// dx and dw of tokens [n0, n0 + kStep).  One (token, group) per item, so a
-// group's filter gradient is summed in registers; VEC = 8 channels per load
-// when H % 8 == 0, else one.
-template <int W, int VEC>
-__global__ __launch_bounds__(kGBlock) void gen_bwd_kernel(GenParams p) {
-    constexpr int TG = gen_tg(W), BN = TG * W, LDC = BN + 4;
+// dx and dw of tokens [n0, n0 + kStep).  MODE 2 (H % 8 == 0, H/8 a power of
+// two up to 64): segment walks per 8-channel chunk (bwd_walk).  Otherwise one
+// (token, group) per item, so a group's filter gradient is summed in
+// registers, with 8 channels per load (MODE 1, H % 8 == 0) or one (MODE 0).
+template <int W, int MODE>
+__global__ __launch_bounds__(kGBlock, 2) void gen_bwd_kernel(GenParams p) {
+    constexpr int TG = gen_tg(W), BN = TG * W;
     constexpr int kStep = kBM - (W - 1);
-    constexpr int kLds = gemm_lds_bytes<BN>() > kBM * LDC * 4 ? gemm_lds_bytes<BN>() : kBM * LDC * 4;
-    __shared__ __align__(16) unsigned char lds[kLds];
+    __shared__ __align__(16) unsigned char st0[kDStage], st1[kDStage], st2[kDStage], st3[kDStage];
     __shared__ int64_t seq_start[kBM], seq_end[kBM];
     const int64_t lb = xcd_block_id(blockIdx.x, (int64_t)gridDim.x);
     const int64_t tn = lb / p.ntiles_g, tg = lb - tn * p.ntiles_g;
@@ -270,16 +393,28 @@ __global__ __launch_bounds__(kGBlock) void gen_bwd_kernel(GenParams p) {
         seq_start[tid] = s;
         seq_end[tid] = e;
     }
-    floatx4 acc[2][BN / 16];
-    gemm_tile<BN, true, true>(p.h, p.K, p.N, p.V, p.K, p.G * W, p.K, n0, g0 * W,
-                              reinterpret_cast<uint16_t *>(lds), acc);
-    float *Cs = reinterpret_cast<float *>(lds);
-    park<BN>(acc, Cs);
+    const Stages S{{st0, st1, st2, st3}};
+    floatx4 acc[DLayout<BN>::MF][DLayout<BN>::NF];
+    dma_gemm<BN>(p.h, p.K, p.N, p.V, p.K, p.G * W, p.K, n0, g0 * W, S, acc);
+    const CsView cs{{st0, st1, st2, st3}, BN};
+    dma_park<BN>(acc, cs);
     __syncthreads();
 
     const int gcount = (int)min((int64_t)TG, p.G - g0);
     const int64_t D = p.D, GW = p.G * W;
     const int H = p.H;
+    if constexpr (MODE == 2) {
+        const int cpg = H / 8, nchunks = gcount * cpg;
+        for (int it = tid; it < nchunks * (kBM / kSeg); it += kGBlock) {
+            const int sg = it / nchunks, q = it - sg * nchunks;
+            if (kSeg * sg >= kStep || n0 + kSeg * sg >= p.N) break;  // items are in segment order
+            const int gl = q / cpg;
+            bwd_walk<W>(p, cs, seq_start, seq_end, n0, kSeg * sg, kStep, g0 * H + 8 * q, gl, g0 + gl, cpg,
+                        (q & (cpg - 1)) == 0);
+        }
+        return;
+    }
+    constexpr int VEC = MODE == 1 ? 8 : 1;
     for (int it = tid; it < kStep * gcount; it += kGBlock) {
         const int t = it / gcount, gl = it - t * gcount;
         const int64_t m = n0 + t;
@@ -289,7 +424,7 @@ __global__ __launch_bounds__(kGBlock) void gen_bwd_kernel(GenParams p) {
         const int ahead = (int)min((int64_t)W, e - m), back = (int)min((int64_t)W, m - s + 1);
         float wk[W];
 #pragma unroll
-        for (int k = 0; k < W; ++k) wk[k] = k < ahead ? Cs[(t + k) * LDC + gl * W + k] : 0.f;
+        for (int k = 0; k < W; ++k) wk[k] = k < ahead ? cs.row(t + k)[gl * W + k] : 0.f;
         float dws[W];
 #pragma unroll
         for (int k = 0; k < W; ++k) dws[k] = 0.f;
@@ -328,33 +463,87 @@ __global__ __launch_bounds__(kGBlock) void gen_bwd_kernel(GenParams p) {
     }
 }
 
-// Plain product C (M x Nc) = A . B^T with an fp32 or bf16 store.
-template <bool AKC, bool BKC, class OUT>
-__global__ __launch_bounds__(kGBlock) void gemm_kernel(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
-                                                       int64_t M, int64_t Nc, int64_t K, OUT *C, int64_t ldc,
-                                                       int64_t ntiles_n) {
+// Plain product C (M x Nc) = A . B^T (both K-contiguous) over k in
+// [ks * kc, min(K, (ks + 1) * kc)) for split ks = blockIdx / tiles, stored as
+// OUT at C + ks * split_stride (the partial sums of a split-K product, or
+// the product itself with one split).
+template <class OUT>
+__global__ __launch_bounds__(kGBlock, 2) void dma_gemm_kernel(const uint16_t *A, int64_t lda, const uint16_t *B,
+                                                              int64_t ldb, int64_t M, int64_t Nc, int64_t K, int64_t kc,
+                                                              OUT *C, int64_t ldc, int64_t split_stride,
+                                                              int64_t ntiles_n, int64_t ntiles) {
     constexpr int BN = 128;
-    __shared__ __align__(16) unsigned char lds[gemm_lds_bytes<BN>()];
+    using L = DLayout<BN>;
+    __shared__ __align__(16) unsigned char st0[kDStage], st1[kDStage], st2[kDStage], st3[kDStage];
     const int64_t lb = xcd_block_id(blockIdx.x, (int64_t)gridDim.x);
-    const int64_t tm = lb / ntiles_n, tn = lb - tm * ntiles_n;
-    const int64_t m0 = tm * kBM, n0 = tn * BN;
-    floatx4 acc[2][BN / 16];
-    gemm_tile<BN, AKC, BKC>(A, lda, M, B, ldb, Nc, K, m0, n0, reinterpret_cast<uint16_t *>(lds), acc);
+    const int64_t ks = lb / ntiles, tile = lb - ks * ntiles;
+    const int64_t tm = tile / ntiles_n, tn = tile - tm * ntiles_n;
+    const int64_t m0 = tm * kBM, n0 = tn * BN, kb = ks * kc;
+    const Stages S{{st0, st1, st2, st3}};
+    floatx4 acc[L::MF][L::NF];
+    dma_gemm<BN>(A + kb, lda, M, B + kb, ldb, Nc, min(kc, K - kb), m0, n0, S, acc);
+    OUT *Cs = C + ks * split_stride;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / L::WN, wn = wave % L::WN;
 #pragma unroll
-    for (int mf = 0; mf < 2; ++mf)
+    for (int mf = 0; mf < L::MF; ++mf)
 #pragma unroll
-        for (int nf = 0; nf < BN / 16; ++nf) {
-            const int64_t col = n0 + 16 * nf + (lane & 15);
+        for (int nf = 0; nf < L::NF; ++nf) {
+            const int64_t col = n0 + (BN / L::WN) * wn + 16 * nf + (lane & 15);
             if (col >= Nc) continue;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int64_t row = m0 + 32 * wave + 16 * mf + 4 * (lane >> 4) + j;
+                const int64_t row = m0 + (kBM / L::WM) * wm + 16 * mf + 4 * (lane >> 4) + j;
                 if (row >= M) continue;
-                if constexpr (sizeof(OUT) == 4) C[row * ldc + col] = acc[mf][nf][j];
-                else C[row * ldc + col] = to_bf16(acc[mf][nf][j]);
+                if constexpr (sizeof(OUT) == 4) Cs[row * ldc + col] = acc[mf][nf][j];
+                else Cs[row * ldc + col] = to_bf16(acc[mf][nf][j]);
             }
         }
+}
+
+// dst[c][r] = src[r][c] for r < rows, 0 for rows <= r < ldd (src rows x cols,
+// dst cols x ldd; cols and ldd multiples of 4).  64 x 64 tiles through LDS,
+// 8-byte accesses.
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t *src, int64_t rows, int64_t cols,
+                                                        uint16_t *dst, int64_t ldd) {
+    __shared__ uint16_t tile[64][68];
+    const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+    const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t r = r0 + ty + 16 * i, c = c0 + 4 * tx;
+        uint2 v = make_uint2(0u, 0u);
+        if (r < rows && c < cols) v = *reinterpret_cast<const uint2 *>(src + r * cols + c);
+        tile[ty + 16 * i][4 * tx] = (uint16_t)(v.x & 0xffffu);
+        tile[ty + 16 * i][4 * tx + 1] = (uint16_t)(v.x >> 16);
+        tile[ty + 16 * i][4 * tx + 2] = (uint16_t)(v.y & 0xffffu);
+        tile[ty + 16 * i][4 * tx + 3] = (uint16_t)(v.y >> 16);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t c = c0 + ty + 16 * i, r = r0 + 4 * tx;
+        if (c >= cols || r >= ldd) continue;
+        const int cl = ty + 16 * i;
+        const uint2 v = make_uint2((uint32_t)tile[4 * tx][cl] | ((uint32_t)tile[4 * tx + 1][cl] << 16),
+                                   (uint32_t)tile[4 * tx + 2][cl] | ((uint32_t)tile[4 * tx + 3][cl] << 16));
+        *reinterpret_cast<uint2 *>(dst + c * ldd + r) = v;
+    }
+}
+
+hipError_t transpose(const uint16_t *src, int64_t rows, int64_t cols, uint16_t *dst, int64_t ldd, hipStream_t st) {
+    const dim3 grid((unsigned)((ldd + 63) / 64), (unsigned)((cols + 63) / 64));
+    hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, st, src, rows, cols, dst, ldd);
+    return hipGetLastError();
+}
+
+// dst[i] = sum over s < nparts of src[s * n + i], in order of s.
+__global__ __launch_bounds__(256) void sum_splits(const float *src, int64_t nparts, int64_t n, float *dst) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float acc = 0.f;
+    for (int64_t s = 0; s < nparts; ++s) acc += src[s * n + i];
+    dst[i] = acc;
 }
 
 GenParams make_gen(const GenProblem &pr, int64_t tiles_n, int64_t tiles_g) {
@@ -388,28 +577,81 @@ hipError_t gen_fwd_w(const GenProblem &pr, hipStream_t st) {
     return hipGetLastError();
 }
 
+// The backward's workspace: dw (N x GW), V^T (K x GW), dw^T (GW x Np), h^T
+// (K x Np) in bf16, with Np = N rounded up to 32 (zero columns past N), and
+// the fp32 partial sums of dV when its K = Np reduction is split.
+struct GenBwdPlan {
+    int64_t GW, Np, splits, kc;
+    size_t off_vt, off_dwt, off_ht, off_parts, bytes;
+};
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+GenBwdPlan gen_bwd_plan(int64_t N, int64_t D, int32_t W, int32_t H, int64_t K) {
+    GenBwdPlan pl;
+    pl.GW = (D / H) * W;
+    pl.Np = (N + 31) / 32 * 32;
+    // dV has ceil(GW/128) * ceil(K/128) output tiles; split its token sum
+    // until about 512 blocks run (splits of at least 1024 tokens, at most 32)
+    const int64_t tiles = ((pl.GW + 127) / 128) * ((K + 127) / 128);
+    int64_t sp = tiles < 512 ? (512 + tiles - 1) / tiles : 1;
+    sp = std::min<int64_t>(std::min<int64_t>(sp, 32), std::max<int64_t>(1, pl.Np / 1024));
+    pl.kc = ((pl.Np + sp - 1) / sp + 31) / 32 * 32;
+    pl.splits = (pl.Np + pl.kc - 1) / pl.kc;
+    size_t o = align256((size_t)N * pl.GW * 2);
+    pl.off_vt = o;
+    o += align256((size_t)K * pl.GW * 2);
+    pl.off_dwt = o;
+    o += align256((size_t)pl.GW * pl.Np * 2);
+    pl.off_ht = o;
+    o += align256((size_t)K * pl.Np * 2);
+    pl.off_parts = o;
+    if (pl.splits > 1) o += align256((size_t)pl.splits * pl.GW * K * 4);
+    pl.bytes = o;
+    return pl;
+}
+
 template <int W>
 hipError_t gen_bwd_w(const GenProblem &pr, hipStream_t st) {
     constexpr int TG = gen_tg(W);
     constexpr int kStep = kBM - (W - 1);
     const int64_t G = pr.D / pr.H, GW = G * W;
     const int64_t tn = (pr.N + kStep - 1) / kStep, tg = (G + TG - 1) / TG;
+    const GenBwdPlan pl = gen_bwd_plan(pr.N, pr.D, pr.W, pr.H, pr.K);
+    unsigned char *ws = static_cast<unsigned char *>(pr.dw);
+    uint16_t *Vt = reinterpret_cast<uint16_t *>(ws + pl.off_vt);
+    uint16_t *dwT = reinterpret_cast<uint16_t *>(ws + pl.off_dwt);
+    uint16_t *hT = reinterpret_cast<uint16_t *>(ws + pl.off_ht);
+    float *parts = reinterpret_cast<float *>(ws + pl.off_parts);
     const GenParams p = make_gen(pr, tn, tg);
-    if (pr.H % 8 == 0)
-        hipLaunchKernelGGL((gen_bwd_kernel<W, 8>), dim3((unsigned)(tn * tg)), dim3(kGBlock), 0, st, p);
-    else
+    const int cpg = pr.H / 8;
+    if (pr.H % 8 == 0 && cpg <= 64 && (cpg & (cpg - 1)) == 0)
+        hipLaunchKernelGGL((gen_bwd_kernel<W, 2>), dim3((unsigned)(tn * tg)), dim3(kGBlock), 0, st, p);
+    else if (pr.H % 8 == 0)
         hipLaunchKernelGGL((gen_bwd_kernel<W, 1>), dim3((unsigned)(tn * tg)), dim3(kGBlock), 0, st, p);
-    // dh (N x K) = dw (N x GW, k contiguous) . V (GW x K, read as K-major columns)
+    else
+        hipLaunchKernelGGL((gen_bwd_kernel<W, 0>), dim3((unsigned)(tn * tg)), dim3(kGBlock), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // dh (N x K) = dw (N x GW) . (V^T)^T, both with GW contiguous
+    if ((e = transpose(p.V, GW, pr.K, Vt, GW, st)) != hipSuccess) return e;
     {
         const int64_t tm = (pr.N + kBM - 1) / kBM, tk = (pr.K + 127) / 128;
-        hipLaunchKernelGGL((gemm_kernel<true, false, uint16_t>), dim3((unsigned)(tm * tk)), dim3(kGBlock), 0, st,
-                           p.dw, GW, p.V, pr.K, pr.N, pr.K, GW, static_cast<uint16_t *>(pr.dh), pr.K, tk);
+        hipLaunchKernelGGL((dma_gemm_kernel<uint16_t>), dim3((unsigned)(tm * tk)), dim3(kGBlock), 0, st, p.dw, GW, Vt,
+                           GW, pr.N, pr.K, GW, GW, static_cast<uint16_t *>(pr.dh), pr.K, (int64_t)0, tk, tm * tk);
     }
-    // dV (GW x K) = dw^T (rows contiguous along GW) . h (rows contiguous along K), summed over the N tokens
+    // dV (GW x K) = dw^T . (h^T)^T over the Np (zero-padded) tokens, in splits
+    // of kc tokens summed in order afterwards
+    if ((e = transpose(p.dw, pr.N, GW, dwT, pl.Np, st)) != hipSuccess) return e;
+    if ((e = transpose(p.h, pr.N, pr.K, hT, pl.Np, st)) != hipSuccess) return e;
     {
         const int64_t tm = (GW + kBM - 1) / kBM, tk = (pr.K + 127) / 128;
-        hipLaunchKernelGGL((gemm_kernel<false, false, float>), dim3((unsigned)(tm * tk)), dim3(kGBlock), 0, st,
-                           p.dw, GW, p.h, pr.K, GW, pr.K, pr.N, pr.dV, pr.K, tk);
+        float *out = pl.splits > 1 ? parts : pr.dV;
+        hipLaunchKernelGGL((dma_gemm_kernel<float>), dim3((unsigned)(tm * tk * pl.splits)), dim3(kGBlock), 0, st, dwT,
+                           pl.Np, hT, pl.Np, GW, pr.K, pl.Np, pl.kc, out, pr.K, GW * pr.K, tk, tm * tk);
+        if (pl.splits > 1)
+            hipLaunchKernelGGL(sum_splits, dim3((unsigned)((GW * pr.K + 255) / 256)), dim3(256), 0, st, parts,
+                               pl.splits, GW * pr.K, pr.dV);
     }
     return hipGetLastError();
 }
@@ -428,6 +670,18 @@ hipError_t gen_bwd_w(const GenProblem &pr, hipStream_t st) {
     }
 
 }  // namespace
+
+hipError_t generate_filters(const uint16_t *h, const uint16_t *V, int64_t N, int64_t K, int64_t C, uint16_t *w,
+                            hipStream_t st) {
+    const int64_t tm = (N + kBM - 1) / kBM, tc = (C + 127) / 128;
+    hipLaunchKernelGGL((dma_gemm_kernel<uint16_t>), dim3((unsigned)(tm * tc)), dim3(kGBlock), 0, st, h, K, V, K, N, C,
+                       K, K, w, C, (int64_t)0, tc, tm * tc);
+    return hipGetLastError();
+}
+
+size_t headwise_gen_bwd_workspace(int64_t N, int64_t D, int32_t W, int32_t H, int64_t K) {
+    return gen_bwd_plan(N, D, W, H, K).bytes;
+}
 
 hipError_t headwise_gen_fwd(const GenProblem &p, hipStream_t s) { DSC_GEN_W_SWITCH(p.W, gen_fwd_w<Wc>(p, s)); }
 

@@ -39,7 +39,7 @@ def test_header_declares_the_entry_points():
               "dsc_headwise_decode", "dsc_lowrank_decode", "dsc_state_from_prefill",
               "dsc_rope_table", "dsc_headwise_rope_fwd", "dsc_headwise_rope_bwd", "dsc_headwise_rope_decode",
               "dsc_lowrank_rope_fwd", "dsc_lowrank_rope_bwd", "dsc_headwise_gen_fwd", "dsc_headwise_gen_bwd",
-              "dsc_headwise_gen_bwd_workspace_size",
+              "dsc_headwise_gen_bwd_workspace_size", "dsc_generate_filters",
               "dsc_status_string", "dsc_last_error", "dsc_abi_version"):
         assert s in syms
 
@@ -277,13 +277,18 @@ def test_generator_validation(lib):
     assert gf(h=None) == 1 and gf(y=ctypes.c_void_p(A * 4 + 2)) == 4
     assert gf(y=P(3)) == 5 and gf(y=P(1)) == 5       # y overlaps x / h
     assert gf(B=0, h=None, V=None, x=None, y=None) == 0
-    assert size() == 1024                            # dw (16 tokens, 32 taps) in bf16
+    # dw (16 x 32), V^T (64 x 32), dw^T (32 x 32: tokens padded to 32), h^T (64 x 32), all bf16
+    assert size() == 2 * (16 * 32 + 64 * 32 + 32 * 32 + 64 * 32)
     assert gf(h=P(3), y=P(3)) == 5                   # h may be x; y may not
     assert size(dt=0) == 0 and size(K=12) == 0
     assert gb(ws=None, wsb=0) == 6 and gb(wsb=100) == 6
     assert gb(dh=P(1)) == 5                          # dh overlaps h
     assert gb(dV=None) == 1 and gb(dx=ctypes.c_void_p(A * 6 + 8)) == 4
     assert gb(ws=P(5)) == 5                          # the workspace overlaps dy
+    gen = lambda dt=1, N=16, K=64, C=32, h=P(1), V=P(2), w=P(3): lib.dsc_generate_filters(S0, dt, N, K, C, h, V, w)
+    assert gen(dt=0) == 3 and gen(dt=7) == 2 and gen(K=12) == 3 and gen(C=20) == 3 and gen(K=0) == 2
+    assert gen(w=None) == 1 and gen(w=P(1)) == 5 and gen(h=ctypes.c_void_p(A + 4)) == 4
+    assert gen(N=0, h=None, V=None, w=None) == 0
 
 
 def test_binding_raises_with_message(lib):

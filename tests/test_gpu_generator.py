@@ -123,6 +123,21 @@ def test_generated_headwise_constant_state_is_the_layer():
     assert_close("dx", dx.host(), to_f64(dx2), 2e-3)
 
 
+@pytest.mark.parametrize("N,K,C", [(300, 64, 48), (4096, 2048, 2048), (1, 8, 8), (1000, 40, 200)])
+def test_generate_filters(N, K, C):
+    """The generator alone (w written out) against the oracle's map; the
+    fused forward on those filters equals the head-wise layer run on them."""
+    g = torch.Generator().manual_seed(N + K + C)
+    h = torch.randn(N, K, generator=g).to(torch.bfloat16)
+    V = (torch.randn(C, K, generator=g) / np.sqrt(K)).to(torch.bfloat16)
+    w = Guarded((N, C), torch.bfloat16)
+    binding.dsc_generate_filters(h.cuda(), V.cuda(), w.t)
+    torch.cuda.synchronize()
+    w.check_guards("w")
+    say(f"[generator] filters N={N} K={K} C={C}")
+    assert_close("w", w.host(), oracle.generate(to_f64(h), to_f64(V)), TOL["bf16"])
+
+
 def test_generated_headwise_empty_batch():
     x = torch.empty(0, 16, 64, dtype=torch.bfloat16, device="cuda")
     h = torch.empty(0, 16, 32, dtype=torch.bfloat16, device="cuda")
