@@ -473,7 +473,9 @@ struct BwdLds {
     static constexpr int kDuStage = RP * kDuPitch * 4; // dU tile staged for coalesced atomics
     static constexpr int kWave = (((kLoop > kDuStage ? kLoop : kDuStage) + 15) / 16) * 16;
     static constexpr int kBlock = 4 * H * kWave;
-    static_assert(kBlocksPerCu * (kBlock + 4 * H * 4 * kSeqWords) <= 160 * 1024, "the blocks of a CU must fit the LDS");
+    // (with the sequence-start maps and, for the RoPE instances, 128 bytes per wave of rotation constants)
+    static_assert(kBlocksPerCu * (kBlock + 4 * H * 4 * kSeqWords + 4 * H * 128) <= 160 * 1024,
+                  "the blocks of a CU must fit the LDS");
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -511,6 +513,10 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
     static_assert(P % 4 == 0, "the register rings cover whole turns of the 4-slot z ring");
     __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBlock];
     __shared__ uint32_t seq_words[4 * H][kSeqWords];
+    // ROPE with one token half (kCarry below): each wave's turn by 16
+    // positions for its 4 chunks of 8 channels
+    constexpr bool kCarry = ROPE && H == 1;
+    __shared__ __align__(16) float rope_r16[kCarry ? 4 : 1][kCarry ? 32 : 1];
 
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -644,22 +650,50 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
     }
 #pragma unroll
     for (int j = 0; j < P; ++j) gr[j] = fetch_g(j);
-    // dy of the 16 tokens from nstep turned back at their positions (steps in order)
+    // dy of the 16 tokens from nstep turned back at their positions (steps in
+    // order).  With two token halves (8 waves, registers at the limit) cos,
+    // sin are read from the table at each step; with one (kCarry) they are
+    // carried from step to step (RopeCarry), the turn by 16 positions read
+    // from the wave's LDS copy, which measured faster there (no table load in
+    // steady state) but spills registers in the two-half instances.
+    RopeCarry rc;
+    if constexpr (kCarry) {
+        if (tok == 0) {
+            float t16[8];
+            rope_cs<8>(p, 16, cbase, t16);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) rope_r16[wid][8 * q + e] = t16[e];
+        }
+        wave_lds_fence();
+    }
     auto turn_g = [&](uint4 &v, int64_t nstep) {
         if constexpr (ROPE) {
             const int64_t pos = sp.pos_and_advance(starts, nstep, tok);
-            if (chan_ok && cbase < p.rot) {
-                float f[8], cs[8];
-                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int i2 = 0; i2 < 4; ++i2) {
-                    f[2 * i2] = bf16_lo(w4[i2]);
-                    f[2 * i2 + 1] = bf16_hi(w4[i2]);
+            float cs[8];
+            if constexpr (kCarry) {
+                if (nstep == nbeg) {
+                    rc.start(p, pos, cbase);
+                } else {
+                    float r16[8];
+                    const float4 a = *reinterpret_cast<const float4 *>(&rope_r16[wid][8 * q]);
+                    const float4 b = *reinterpret_cast<const float4 *>(&rope_r16[wid][8 * q + 4]);
+                    r16[0] = a.x; r16[1] = a.y; r16[2] = a.z; r16[3] = a.w;
+                    r16[4] = b.x; r16[5] = b.y; r16[6] = b.z; r16[7] = b.w;
+                    rc.advance(p, pos, cbase, r16, rope_restart(starts, nstep));
                 }
-                rope_cs<8>(p, pos, cbase, cs);
-                turn<8, true>(f, cs);
-                v = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
-                               pack_bf16x2(f[6], f[7]));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) cs[e] = rc.c[e];
+            }
+            if (chan_ok && cbase < p.rot) {
+                if constexpr (!kCarry) rope_cs<8>(p, pos, cbase, cs);
+                uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int i2 = 0; i2 < 4; ++i2) {  // pair i2 = the two halves of word i2, turned back
+                    const float a = bf16_lo(w4[i2]), b = bf16_hi(w4[i2]);
+                    const float c = cs[2 * i2], sn = cs[2 * i2 + 1];
+                    w4[i2] = pack_bf16x2(a * c + b * sn, b * c - a * sn);
+                }
+                v = make_uint4(w4[0], w4[1], w4[2], w4[3]);
             }
         }
     };

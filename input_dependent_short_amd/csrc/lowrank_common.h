@@ -87,14 +87,53 @@ struct SeqPos {
     }
 };
 
-// cos, sin of the VEC/2 pairs of VEC channels starting at channel ch (< rot,
-// a multiple of VEC, so all in one head) of a token at position pos (clamped
-// into the table: positions past it belong to tokens past the walk, whose
-// values are never stored).
+// cos, sin of the VEC/2 pairs of VEC channels starting at channel ch (a
+// multiple of VEC, so all in one head) of a token at position pos.  Any
+// channel reads the entry of its place in its head, so callers may load for
+// channels past rot and skip the turn; pos is clamped into the table
+// (positions past it belong to tokens past the walk, whose values are never
+// stored).
 template <int VEC>
 __device__ __forceinline__ void rope_cs(const LrParams &p, int64_t pos, int64_t ch, float (&cs)[VEC]) {
     const int64_t m = pos < 0 ? 0 : (pos >= p.npos ? p.npos - 1 : pos);
     load_turn<VEC>(p.rope + m * p.hd + (int32_t)(ch % p.hd), cs);
+}
+
+// cos, sin of a lane's 4 pairs (8 channels from ch) at its token's position,
+// carried along a walk of 16-token steps: a token 16 or more positions into
+// its sequence turns the value its lane held one step earlier (the token 16
+// before, same sequence) by 16 positions, angle addition with table row 16.
+// Tokens within 16 of their sequence start, and the walk's first step, read
+// the table; steps with none of those (the test is wave-uniform) issue no
+// memory load, so the streams' prefetch depth stays intact.  Each turn adds
+// about one fp32 rounding: over a 4096-token walk well under bf16 resolution.
+struct RopeCarry {
+    float c[8];
+    __device__ __forceinline__ void start(const LrParams &p, int64_t pos, int64_t ch) { rope_cs<8>(p, pos, ch, c); }
+    // r16: cos, sin of 16 positions for the lane's 4 pairs (table row 16);
+    // restart: some token of the step is within 16 of its sequence start (a
+    // wave-uniform flag from the start bitmap).  In such a step every lane
+    // loads (position clamped) and a select consumes the load inside the
+    // branch, so the wait for it stays there: a load whose value lived on past
+    // the branch would make every step wait for it, and with it for the
+    // streams' prefetched loads.
+    __device__ __forceinline__ void advance(const LrParams &p, int64_t pos, int64_t ch, const float (&r16)[8],
+                                            bool restart) {
+        compose<8>(c, r16);
+        if (restart) {
+            float t[8];
+            rope_cs<8>(p, pos < 16 ? pos : 0, ch, t);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) c[e] = pos < 16 ? t[e] : c[e];
+        }
+    }
+};
+
+// Whether a step of 16 tokens from nstep has a token within 16 positions of
+// its sequence start: a start among tokens nstep - 15 .. nstep + 15.
+template <int kWords>
+__device__ __forceinline__ bool rope_restart(const StartBits<kWords> &bits, int64_t nstep) {
+    return (__builtin_amdgcn_readfirstlane(bits.window(nstep - 15)) & 0x7fffffffu) != 0u;
 }
 
 // ---------------------------------------------------------------- U operands

@@ -128,6 +128,8 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_wide(LrParams p, int64_t npairs
     StartBits<kSeqWords> starts;
     starts.build(seq_words[wid], p.seq, p.N, nbeg - 32, lane);
     SeqPos sp{0};
+    RopeCarry rc[ROPE ? 2 : 1];   // the lane's two 8-channel chunks (one per slice)
+    float r16[ROPE ? 2 : 1][8];   // their turn by 16 positions (table row 16)
     if constexpr (ROPE) {
         int64_t s_, e_;
         p.seq.find(nbeg < p.N ? nbeg : p.N - 1, s_, e_);
@@ -166,8 +168,19 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_wide(LrParams p, int64_t npairs
             uint32_t win = 0;
             if constexpr (W > 1) win = __builtin_amdgcn_readfirstlane(starts.window(nbeg + 16 * (int64_t)s - (W - 1)));
             const bool masked = (win & (((1u << (W + 14)) - 1u) << 1)) != 0u;  // wave-uniform
-            int64_t pos = 0;
-            if constexpr (ROPE) pos = sp.pos_and_advance(starts, nbeg + 16 * (int64_t)s, tok);
+            if constexpr (ROPE) {
+                const int64_t pos = sp.pos_and_advance(starts, nbeg + 16 * (int64_t)s, tok);
+#pragma unroll
+                for (int sl = 0; sl < 2; ++sl) {
+                    if (s == 0) {
+                        rc[sl].start(p, pos, c0 + 32 * sl + 8 * q);
+                        rope_cs<8>(p, 16, c0 + 32 * sl + 8 * q, r16[sl]);
+                    } else {
+                        rc[sl].advance(p, pos, c0 + 32 * sl + 8 * q, r16[sl],
+                                       rope_restart(starts, nbeg + 16 * (int64_t)s));
+                    }
+                }
+            }
 
 #pragma unroll
             for (int sl = 0; sl < 2; ++sl) {
@@ -214,12 +227,8 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_wide(LrParams p, int64_t npairs
                     out[c] = a;
                 }
                 if constexpr (ROPE) {
-                    const int64_t ch0 = c0 + 32 * sl + 8 * q;  // the lane's 8 channels: 4 pairs of one head
-                    if (ch0 < p.rot) {
-                        float cs[8];
-                        rope_cs<8>(p, pos, ch0, cs);
-                        turn<8, false>(out, cs);
-                    }
+                    // the lane's 8 channels: 4 pairs of one head
+                    if (c0 + 32 * sl + 8 * q < p.rot) turn<8, false>(out, rc[sl].c);
                 }
                 uint4 yv;
                 yv.x = pack_bf16x2(out[0], out[1]);
