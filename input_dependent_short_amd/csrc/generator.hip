@@ -28,11 +28,15 @@
 namespace dsc {
 namespace {
 
-constexpr int kGBlock = 256;  // 4 waves
-constexpr int kBM = 128;      // tile rows (GEMM M)
 
 // Groups per tile: BN = TG*W columns of w (a multiple of 16 for any W <= 8).
 constexpr int gen_tg(int W) { return W <= 4 ? 32 : 16; }
+// Token rows per tile of the fused kernels (4 waves).  Tiles of 256 rows on
+// 8 waves (one block per CU, 6 stages) measured slower, for the fused and the
+// plain products alike (MLP ~2B, K = 2048: forward 323 against 277 us,
+// backward 931 against 815 us), so every kernel takes 128 rows.
+constexpr int gen_bm(int) { return 128; }
+constexpr int gen_threads(int W) { return 2 * gen_bm(W); }  // 64 threads per 32 rows
 
 // ------------------------------------------- matrix-core GEMM, direct loads
 //
@@ -40,7 +44,7 @@ constexpr int gen_tg(int W) { return W <= 4 ? 32 : 16; }
 // dh = dw V^T... with V transposed) run a four-stage pipeline: each stage is
 // a kDBK = 32 slice of K, loaded by buffer_load ... lds straight from memory
 // into LDS (no registers), three stages ahead of the matrix cores.  A stage
-// holds the A tile (kBM rows) then the B tile (BN <= 128 rows), rows of 64
+// holds the A tile (BM rows) then the B tile (BN <= 128 rows), rows of 64
 // bytes whose four 16-byte chunks are placed at chunk ^ chunk_swz(row), chunk_swz(r) =
 // ((r >> 1) ^ (r >> 2)) & 3, so that the 16 rows a fragment read touches fall
 // on distinct banks whether the LDS serves 16 lanes over 64 banks or 8 lanes
@@ -53,33 +57,51 @@ constexpr int gen_tg(int W) { return W <= 4 ? 32 : 16; }
 
 constexpr int kDBK = 32;
 __device__ __forceinline__ int chunk_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
-constexpr int kDStage = 16384;  // bytes per stage: A 128 x 64 B, B up to 128 x 64 B
 typedef __attribute__((address_space(3))) void lds_void;
 
-// The four stage arrays of a block.
-struct Stages {
-    unsigned char *s[4];
+template <int BR, int NW>
+constexpr int dma_per_wave() {
+    return (BR / 16 + NW - 1) / NW;
+}
+
+// Tile configuration: BM rows of A by BN rows of B (the columns of C) on
+// BM / 32 waves (4 or 8), NST stages of kStage bytes (A tile, then B tile);
+// the fp32 result tile is parked RPS rows per stage.  WM x WN waves, each
+// MF x NF fragments of 16 x 16.  The 256-row tiles (8 waves, 6 stages) keep
+// about 1.7 times the bytes of the 128-row ones in flight per CU and load a
+// quarter fewer operand bytes per product.
+template <int BM, int BN>
+struct DCfg {
+    static constexpr int NW = BM / 32;
+    static constexpr int kThreads = 64 * NW;
+    static constexpr int NST = BM == 256 ? 6 : 4;
+    static constexpr int kA = BM * 64, kB = BN * 64;
+    static constexpr int kStage = BM == 256 ? 24576 : 16384;
+    static constexpr int RPS = 32;  // result rows per stage (a shift in the epilogues)
+    static constexpr int WN = (BN / 2) % 16 == 0 ? 2 : 1, WM = NW / WN;
+    static constexpr int MF = BM / WM / 16, NF = BN / WN / 16;
+    static constexpr int kPerTile = dma_per_wave<BM, NW>() + dma_per_wave<BN, NW>();
+    static_assert(kA + kB <= kStage && RPS * BN * 4 <= kStage && 4 * RPS >= BM && MF >= 1 && NF >= 1,
+                  "tile configuration");
 };
 
-// Wave layout of a kBM x BN tile: WM x WN waves, each MF x NF fragments of 16 x 16.
-template <int BN>
-struct DLayout {
-    static constexpr int WN = (BN / 2) % 16 == 0 ? 2 : 1, WM = 4 / WN;
-    static constexpr int MF = kBM / WM / 16, NF = BN / WN / 16;
+// The stage arrays of a block (NST of them used).
+struct Stages {
+    unsigned char *s[6];
 };
 
 // Direct loads of one operand tile (BR rows, kDBK k from k0) into dst.  A
 // wave instruction fills 64 consecutive 16-byte slots; the BR/16 of them are
-// spread over the 4 waves, and a wave with no instruction left repeats the
+// spread over the NW waves, and a wave with no instruction left repeats the
 // last one (same bytes to the same place), so every wave issues the same
 // count per tile.
-template <int BR>
+template <int BR, int NW>
 __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, int64_t ld, int64_t k0, int64_t K,
                                          unsigned char *dst, int wave, int lane) {
-    constexpr int kInst = BR / 16, kPer = (kInst + 3) / 4;
+    constexpr int kInst = BR / 16, kPer = dma_per_wave<BR, NW>();
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-        const int i = wave + 4 * j < kInst ? wave + 4 * j : kInst - 1;
+        const int i = wave + NW * j < kInst ? wave + NW * j : kInst - 1;
         const int slot = 64 * i + lane;
         const int row = slot >> 2, logical = (slot & 3) ^ chunk_swz(row);
         const int64_t kk = k0 + 8 * logical;
@@ -90,109 +112,125 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, int64_t ld, 
     }
 }
 
-template <int BR>
-constexpr int dma_per_wave() {
-    return (BR / 16 + 3) / 4;
-}
-
-// C[kBM x BN] = A[m0 .., :] . B[n0 .., :]^T (both K-contiguous, K % 8 == 0),
+// C[BM x BN] = A[m0 .., :] . B[n0 .., :]^T (both K-contiguous, K % 8 == 0),
 // fp32: acc[mf][nf][j] = C[RM*wm + 16mf + 4(lane>>4) + j][RN*wn + 16nf + (lane&15)]
-// with RM = kBM/WM, RN = BN/WN, (wm, wn) = (wave / WN, wave % WN).  Ends with
+// with RM = BM/WM, RN = BN/WN, (wm, wn) = (wave / WN, wave % WN).  Ends with
 // every load landed and a barrier: the stages may then be reused.
-template <int BN>
+template <int BM, int BN>
 __device__ __forceinline__ void dma_gemm(const uint16_t *A, int64_t lda, int64_t M, const uint16_t *B, int64_t ldb,
                                          int64_t Nc, int64_t K, int64_t m0, int64_t n0, const Stages &S,
-                                         floatx4 (&acc)[DLayout<BN>::MF][DLayout<BN>::NF]) {
-    using L = DLayout<BN>;
-    constexpr int kPerTile = dma_per_wave<kBM>() + dma_per_wave<BN>();
+                                         floatx4 (&acc)[DCfg<BM, BN>::MF][DCfg<BM, BN>::NF]) {
+    using C = DCfg<BM, BN>;
+    constexpr int NST = C::NST;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / L::WN, wn = wave % L::WN;
-    const int64_t mr = min((int64_t)kBM, M - m0), nr = min((int64_t)BN, Nc - n0);
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int64_t mr = min((int64_t)BM, M - m0), nr = min((int64_t)BN, Nc - n0);
     const __amdgpu_buffer_rsrc_t ra = make_stream(A + m0 * lda, mr > 0 ? mr * lda * 2 : 0);
     const __amdgpu_buffer_rsrc_t rb = make_stream(B + n0 * ldb, nr > 0 ? nr * ldb * 2 : 0);
 #pragma unroll
-    for (int mf = 0; mf < L::MF; ++mf)
+    for (int mf = 0; mf < C::MF; ++mf)
 #pragma unroll
-        for (int nf = 0; nf < L::NF; ++nf) acc[mf][nf] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int nf = 0; nf < C::NF; ++nf) acc[mf][nf] = floatx4{0.f, 0.f, 0.f, 0.f};
     auto issue = [&](int64_t t, unsigned char *st) {
-        dma_tile<kBM>(ra, lda, t * kDBK, K, st, wave, lane);
-        dma_tile<BN>(rb, ldb, t * kDBK, K, st + 8192, wave, lane);
+        dma_tile<BM, C::NW>(ra, lda, t * kDBK, K, st, wave, lane);
+        dma_tile<BN, C::NW>(rb, ldb, t * kDBK, K, st + C::kA, wave, lane);
     };
     // fragment rows: A rows RM*wm + 16mf + (lane&15), B rows RN*wn + 16nf + (lane&15); chunk lane>>4
     const int c = lane >> 4;
-    int aoff[L::MF], boff[L::NF];
+    int aoff[C::MF], boff[C::NF];
 #pragma unroll
-    for (int mf = 0; mf < L::MF; ++mf) {
-        const int r = (kBM / L::WM) * wm + 16 * mf + (lane & 15);
+    for (int mf = 0; mf < C::MF; ++mf) {
+        const int r = (BM / C::WM) * wm + 16 * mf + (lane & 15);
         aoff[mf] = r * 64 + 16 * (c ^ chunk_swz(r));
     }
 #pragma unroll
-    for (int nf = 0; nf < L::NF; ++nf) {
-        const int r = (BN / L::WN) * wn + 16 * nf + (lane & 15);
-        boff[nf] = 8192 + r * 64 + 16 * (c ^ chunk_swz(r));
+    for (int nf = 0; nf < C::NF; ++nf) {
+        const int r = (BN / C::WN) * wn + 16 * nf + (lane & 15);
+        boff[nf] = C::kA + r * 64 + 16 * (c ^ chunk_swz(r));
     }
     auto compute = [&](const unsigned char *st) {
-        bf16x8 a[L::MF], b[L::NF];
+        bf16x8 a[C::MF], b[C::NF];
 #pragma unroll
-        for (int mf = 0; mf < L::MF; ++mf) a[mf] = *reinterpret_cast<const bf16x8 *>(st + aoff[mf]);
+        for (int mf = 0; mf < C::MF; ++mf) a[mf] = *reinterpret_cast<const bf16x8 *>(st + aoff[mf]);
 #pragma unroll
-        for (int nf = 0; nf < L::NF; ++nf) b[nf] = *reinterpret_cast<const bf16x8 *>(st + boff[nf]);
+        for (int nf = 0; nf < C::NF; ++nf) b[nf] = *reinterpret_cast<const bf16x8 *>(st + boff[nf]);
 #pragma unroll
-        for (int mf = 0; mf < L::MF; ++mf)
+        for (int mf = 0; mf < C::MF; ++mf)
 #pragma unroll
-            for (int nf = 0; nf < L::NF; ++nf)
+            for (int nf = 0; nf < C::NF; ++nf)
                 acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mf], b[nf], acc[mf][nf], 0, 0, 0);
     };
-    // tile t waits until only the loads of tiles t+1, t+2 are in flight, then
-    // a barrier makes every wave's loads of tile t visible (and ends every
-    // wave's reads of the stage that tile t+3 refills)
+    // tile t waits until only the loads of tiles t+1 .. t+NST-2 are in flight,
+    // then a barrier makes every wave's loads of tile t visible (and ends every
+    // wave's reads of the stage that tile t+NST-1 refills)
     auto step = [&](int64_t t, unsigned char *cur, unsigned char *refill) {
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPerTile) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 2) * C::kPerTile) : "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        issue(t + 3, refill);
+        issue(t + NST - 1, refill);
         compute(cur);
     };
     const int64_t nk = (K + kDBK - 1) / kDBK;
-    issue(0, S.s[0]);
-    issue(1, S.s[1]);
-    issue(2, S.s[2]);
-    // whole rounds of four tiles: tiles past nk read as zero and add nothing
-    for (int64_t t = 0; t < nk; t += 4) {
-        step(t, S.s[0], S.s[3]);
-        step(t + 1, S.s[1], S.s[0]);
-        step(t + 2, S.s[2], S.s[1]);
-        step(t + 3, S.s[3], S.s[2]);
+#pragma unroll
+    for (int j = 0; j < NST - 1; ++j) issue(j, S.s[j]);
+    // whole rounds of NST tiles: tiles past nk read as zero and add nothing
+    for (int64_t t = 0; t < nk; t += NST) {
+#pragma unroll
+        for (int j = 0; j < NST; ++j) step(t + j, S.s[j], S.s[(j + NST - 1) % NST]);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 }
 
-// The fp32 result tile of dma_gemm parked in the four stages: row r in stage
-// r / 32 at (r % 32) * BN floats (kBM * BN * 4 <= 4 * kDStage).
+// The fp32 result tile of dma_gemm parked in the first four stages: row r
+// in stage r / 32 at (r % 32) * bn floats.  The stage is picked by selects
+// (an array indexed by r would be kept in memory, LDS or scratch, per thread).
 struct CsView {
-    unsigned char *s[4];
+    unsigned char *s0, *s1, *s2, *s3;
     int bn;
-    __device__ __forceinline__ const float *row(int r) const {
-        return reinterpret_cast<const float *>(s[r >> 5]) + (r & 31) * bn;
+    __device__ __forceinline__ float *wrow(int r) const {
+        unsigned char *b = r < 64 ? (r < 32 ? s0 : s1) : (r < 96 ? s2 : s3);
+        return reinterpret_cast<float *>(b) + (r & 31) * bn;
     }
-    __device__ __forceinline__ float *wrow(int r) const { return reinterpret_cast<float *>(s[r >> 5]) + (r & 31) * bn; }
+    __device__ __forceinline__ const float *row(int r) const { return wrow(r); }
 };
 
-template <int BN>
-__device__ __forceinline__ void dma_park(const floatx4 (&acc)[DLayout<BN>::MF][DLayout<BN>::NF], const CsView &cs) {
-    using L = DLayout<BN>;
+template <int BM, int BN>
+__device__ __forceinline__ void dma_park(const floatx4 (&acc)[DCfg<BM, BN>::MF][DCfg<BM, BN>::NF], const CsView &cs) {
+    using C = DCfg<BM, BN>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave / L::WN, wn = wave % L::WN;
+    const int wm = wave / C::WN, wn = wave % C::WN;
 #pragma unroll
-    for (int mf = 0; mf < L::MF; ++mf)
+    for (int mf = 0; mf < C::MF; ++mf)
 #pragma unroll
-        for (int nf = 0; nf < L::NF; ++nf)
+        for (int nf = 0; nf < C::NF; ++nf)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                cs.wrow((kBM / L::WM) * wm + 16 * mf + 4 * (lane >> 4) + j)[(BN / L::WN) * wn + 16 * nf + (lane & 15)] =
+                cs.wrow((BM / C::WM) * wm + 16 * mf + 4 * (lane >> 4) + j)[(BN / C::WN) * wn + 16 * nf + (lane & 15)] =
                     acc[mf][nf][j];
 }
+
+// Element by element: an aggregate initializer made only of LDS addresses
+// would be emitted as a constant in global memory, which cannot hold them.
+__device__ __forceinline__ void set_stages(Stages &S, CsView &cs, unsigned char *a, unsigned char *b,
+                                           unsigned char *c, unsigned char *d, unsigned char *e, unsigned char *f,
+                                           int bn) {
+    S.s[0] = cs.s0 = a;
+    S.s[1] = cs.s1 = b;
+    S.s[2] = cs.s2 = c;
+    S.s[3] = cs.s3 = d;
+    S.s[4] = e;
+    S.s[5] = f;
+    cs.bn = bn;
+}
+
+// The stage arrays of a kernel with tile configuration C (NST of them sized).
+#define DSC_GEN_STAGES(C)                                                                         \
+    __shared__ __align__(16) unsigned char st0[C::kStage], st1[C::kStage], st2[C::kStage],      \
+        st3[C::kStage], st4[C::NST > 4 ? C::kStage : 16], st5[C::NST > 5 ? C::kStage : 16];      \
+    Stages S;                                                                                      \
+    CsView cs;                                                                                     \
+    set_stages(S, cs, st0, st1, st2, st3, st4, st5, C::kB / 64)
 
 struct GenParams {
     const uint16_t *h, *V, *x, *dy;
@@ -276,24 +314,25 @@ __device__ __forceinline__ void fwd_walk(const GenParams &p, const CsView &cs, c
 // Forward: block = (token tile, group tile), walked so that the group tiles
 // of one token tile (which share its rows of h) run on one XCD.
 template <int W>
-__global__ __launch_bounds__(kGBlock, 2) void gen_fwd_kernel(GenParams p) {
-    constexpr int TG = gen_tg(W), BN = TG * W;
-    __shared__ __align__(16) unsigned char st0[kDStage], st1[kDStage], st2[kDStage], st3[kDStage];
-    __shared__ int64_t seq_start[kBM];
+__global__ __launch_bounds__(gen_threads(W), 512 / gen_threads(W))
+void gen_fwd_kernel(GenParams p) {
+    constexpr int TG = gen_tg(W), BN = TG * W, BM = gen_bm(W);
+    using C = DCfg<BM, BN>;
+    static_assert(C::kThreads == gen_threads(W), "block size");
+    DSC_GEN_STAGES(C);
+    __shared__ int64_t seq_start[BM];
     const int64_t lb = xcd_block_id(blockIdx.x, (int64_t)gridDim.x);
     const int64_t tn = lb / p.ntiles_g, tg = lb - tn * p.ntiles_g;
-    const int64_t n0 = tn * kBM, g0 = tg * TG;
+    const int64_t n0 = tn * BM, g0 = tg * TG;
     const int tid = threadIdx.x;
-    if (tid < kBM && n0 + tid < p.N) {
+    if (tid < BM && n0 + tid < p.N) {
         int64_t s, e;
         p.seq.find(n0 + tid, s, e);
         seq_start[tid] = s;
     }
-    const Stages S{{st0, st1, st2, st3}};
-    floatx4 acc[DLayout<BN>::MF][DLayout<BN>::NF];
-    dma_gemm<BN>(p.h, p.K, p.N, p.V, p.K, p.G * W, p.K, n0, g0 * W, S, acc);
-    const CsView cs{{st0, st1, st2, st3}, BN};
-    dma_park<BN>(acc, cs);
+    floatx4 acc[C::MF][C::NF];
+    dma_gemm<BM, BN>(p.h, p.K, p.N, p.V, p.K, p.G * W, p.K, n0, g0 * W, S, acc);
+    dma_park<BM, BN>(acc, cs);
     __syncthreads();
 
     // y of the tile's tokens over the channels of groups [g0, g0 + gcount):
@@ -304,7 +343,7 @@ __global__ __launch_bounds__(kGBlock, 2) void gen_fwd_kernel(GenParams p) {
     const int64_t c0 = g0 * p.H;
     const int nchunks = (int)(gcount * p.H / 8);
     const bool uniform = p.H % 8 == 0;  // a chunk's 8 channels share one group
-    for (int it = tid; it < nchunks * (kBM / kSeg); it += kGBlock) {
+    for (int it = tid; it < nchunks * (BM / kSeg); it += C::kThreads) {
         const int sg = it / nchunks, q = it - sg * nchunks;
         if (n0 + kSeg * sg >= p.N) break;  // items are in segment order
         if (uniform) fwd_walk<W, true>(p, cs, seq_start, n0, kSeg * sg, c0 + 8 * q, g0);
@@ -372,17 +411,19 @@ __device__ __forceinline__ void bwd_walk(const GenParams &p, const CsView &cs, c
     }
 }
 
-// Backward, w recomputed: tile rows [n0, n0 + kBM) with n0 = tile * kStep;
+// Backward, w recomputed: tile rows [n0, n0 + BM) with n0 = tile * kStep;
 // dx and dw of tokens [n0, n0 + kStep).  MODE 2 (H % 8 == 0, H/8 a power of
 // two up to 64): segment walks per 8-channel chunk (bwd_walk).  Otherwise one
 // (token, group) per item, so a group's filter gradient is summed in
 // registers, with 8 channels per load (MODE 1, H % 8 == 0) or one (MODE 0).
 template <int W, int MODE>
-__global__ __launch_bounds__(kGBlock, 2) void gen_bwd_kernel(GenParams p) {
-    constexpr int TG = gen_tg(W), BN = TG * W;
-    constexpr int kStep = kBM - (W - 1);
-    __shared__ __align__(16) unsigned char st0[kDStage], st1[kDStage], st2[kDStage], st3[kDStage];
-    __shared__ int64_t seq_start[kBM], seq_end[kBM];
+__global__ __launch_bounds__(gen_threads(W), 512 / gen_threads(W))
+void gen_bwd_kernel(GenParams p) {
+    constexpr int TG = gen_tg(W), BN = TG * W, BM = gen_bm(W);
+    using C = DCfg<BM, BN>;
+    constexpr int kStep = BM - (W - 1);
+    DSC_GEN_STAGES(C);
+    __shared__ int64_t seq_start[BM], seq_end[BM];
     const int64_t lb = xcd_block_id(blockIdx.x, (int64_t)gridDim.x);
     const int64_t tn = lb / p.ntiles_g, tg = lb - tn * p.ntiles_g;
     const int64_t n0 = tn * kStep, g0 = tg * TG;
@@ -393,11 +434,9 @@ __global__ __launch_bounds__(kGBlock, 2) void gen_bwd_kernel(GenParams p) {
         seq_start[tid] = s;
         seq_end[tid] = e;
     }
-    const Stages S{{st0, st1, st2, st3}};
-    floatx4 acc[DLayout<BN>::MF][DLayout<BN>::NF];
-    dma_gemm<BN>(p.h, p.K, p.N, p.V, p.K, p.G * W, p.K, n0, g0 * W, S, acc);
-    const CsView cs{{st0, st1, st2, st3}, BN};
-    dma_park<BN>(acc, cs);
+    floatx4 acc[C::MF][C::NF];
+    dma_gemm<BM, BN>(p.h, p.K, p.N, p.V, p.K, p.G * W, p.K, n0, g0 * W, S, acc);
+    dma_park<BM, BN>(acc, cs);
     __syncthreads();
 
     const int gcount = (int)min((int64_t)TG, p.G - g0);
@@ -405,7 +444,7 @@ __global__ __launch_bounds__(kGBlock, 2) void gen_bwd_kernel(GenParams p) {
     const int H = p.H;
     if constexpr (MODE == 2) {
         const int cpg = H / 8, nchunks = gcount * cpg;
-        for (int it = tid; it < nchunks * (kBM / kSeg); it += kGBlock) {
+        for (int it = tid; it < nchunks * (BM / kSeg); it += C::kThreads) {
             const int sg = it / nchunks, q = it - sg * nchunks;
             if (kSeg * sg >= kStep || n0 + kSeg * sg >= p.N) break;  // items are in segment order
             const int gl = q / cpg;
@@ -415,7 +454,7 @@ __global__ __launch_bounds__(kGBlock, 2) void gen_bwd_kernel(GenParams p) {
         return;
     }
     constexpr int VEC = MODE == 1 ? 8 : 1;
-    for (int it = tid; it < kStep * gcount; it += kGBlock) {
+    for (int it = tid; it < kStep * gcount; it += C::kThreads) {
         const int t = it / gcount, gl = it - t * gcount;
         const int64_t m = n0 + t;
         if (m >= p.N) break;
@@ -467,21 +506,25 @@ __global__ __launch_bounds__(kGBlock, 2) void gen_bwd_kernel(GenParams p) {
 // [ks * kc, min(K, (ks + 1) * kc)) for split ks = blockIdx / tiles, stored as
 // OUT at C + ks * split_stride (the partial sums of a split-K product, or
 // the product itself with one split).
+constexpr int kPBM = 128, kPBN = 128;  // tile of the plain products
+using PlainCfg = DCfg<kPBM, kPBN>;
+
 template <class OUT>
-__global__ __launch_bounds__(kGBlock, 2) void dma_gemm_kernel(const uint16_t *A, int64_t lda, const uint16_t *B,
-                                                              int64_t ldb, int64_t M, int64_t Nc, int64_t K, int64_t kc,
-                                                              OUT *C, int64_t ldc, int64_t split_stride,
-                                                              int64_t ntiles_n, int64_t ntiles) {
-    constexpr int BN = 128;
-    using L = DLayout<BN>;
-    __shared__ __align__(16) unsigned char st0[kDStage], st1[kDStage], st2[kDStage], st3[kDStage];
+__global__ __launch_bounds__(PlainCfg::kThreads, 2) void dma_gemm_kernel(const uint16_t *A, int64_t lda,
+                                                                         const uint16_t *B, int64_t ldb, int64_t M,
+                                                                         int64_t Nc, int64_t K, int64_t kc, OUT *C,
+                                                                         int64_t ldc, int64_t split_stride,
+                                                                         int64_t ntiles_n, int64_t ntiles) {
+    constexpr int BM = kPBM, BN = kPBN;
+    using L = PlainCfg;
+    DSC_GEN_STAGES(L);
+    (void)cs;
     const int64_t lb = xcd_block_id(blockIdx.x, (int64_t)gridDim.x);
     const int64_t ks = lb / ntiles, tile = lb - ks * ntiles;
     const int64_t tm = tile / ntiles_n, tn = tile - tm * ntiles_n;
-    const int64_t m0 = tm * kBM, n0 = tn * BN, kb = ks * kc;
-    const Stages S{{st0, st1, st2, st3}};
+    const int64_t m0 = tm * BM, n0 = tn * BN, kb = ks * kc;
     floatx4 acc[L::MF][L::NF];
-    dma_gemm<BN>(A + kb, lda, M, B + kb, ldb, Nc, min(kc, K - kb), m0, n0, S, acc);
+    dma_gemm<BM, BN>(A + kb, lda, M, B + kb, ldb, Nc, min(kc, K - kb), m0, n0, S, acc);
     OUT *Cs = C + ks * split_stride;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / L::WN, wn = wave % L::WN;
@@ -493,7 +536,7 @@ __global__ __launch_bounds__(kGBlock, 2) void dma_gemm_kernel(const uint16_t *A,
             if (col >= Nc) continue;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int64_t row = m0 + (kBM / L::WM) * wm + 16 * mf + 4 * (lane >> 4) + j;
+                const int64_t row = m0 + (BM / L::WM) * wm + 16 * mf + 4 * (lane >> 4) + j;
                 if (row >= M) continue;
                 if constexpr (sizeof(OUT) == 4) Cs[row * ldc + col] = acc[mf][nf][j];
                 else Cs[row * ldc + col] = to_bf16(acc[mf][nf][j]);
@@ -569,11 +612,11 @@ GenParams make_gen(const GenProblem &pr, int64_t tiles_n, int64_t tiles_g) {
 
 template <int W>
 hipError_t gen_fwd_w(const GenProblem &pr, hipStream_t st) {
-    constexpr int TG = gen_tg(W);
+    constexpr int TG = gen_tg(W), BM = gen_bm(W);
     const int64_t G = pr.D / pr.H;
-    const int64_t tn = (pr.N + kBM - 1) / kBM, tg = (G + TG - 1) / TG;
+    const int64_t tn = (pr.N + BM - 1) / BM, tg = (G + TG - 1) / TG;
     const GenParams p = make_gen(pr, tn, tg);
-    hipLaunchKernelGGL((gen_fwd_kernel<W>), dim3((unsigned)(tn * tg)), dim3(kGBlock), 0, st, p);
+    hipLaunchKernelGGL((gen_fwd_kernel<W>), dim3((unsigned)(tn * tg)), dim3(DCfg<BM, TG * W>::kThreads), 0, st, p);
     return hipGetLastError();
 }
 
@@ -613,8 +656,9 @@ GenBwdPlan gen_bwd_plan(int64_t N, int64_t D, int32_t W, int32_t H, int64_t K) {
 
 template <int W>
 hipError_t gen_bwd_w(const GenProblem &pr, hipStream_t st) {
-    constexpr int TG = gen_tg(W);
-    constexpr int kStep = kBM - (W - 1);
+    constexpr int TG = gen_tg(W), BM = gen_bm(W);
+    constexpr int kStep = BM - (W - 1);
+    constexpr int kThr = DCfg<BM, TG * W>::kThreads;
     const int64_t G = pr.D / pr.H, GW = G * W;
     const int64_t tn = (pr.N + kStep - 1) / kStep, tg = (G + TG - 1) / TG;
     const GenBwdPlan pl = gen_bwd_plan(pr.N, pr.D, pr.W, pr.H, pr.K);
@@ -626,18 +670,18 @@ hipError_t gen_bwd_w(const GenProblem &pr, hipStream_t st) {
     const GenParams p = make_gen(pr, tn, tg);
     const int cpg = pr.H / 8;
     if (pr.H % 8 == 0 && cpg <= 64 && (cpg & (cpg - 1)) == 0)
-        hipLaunchKernelGGL((gen_bwd_kernel<W, 2>), dim3((unsigned)(tn * tg)), dim3(kGBlock), 0, st, p);
+        hipLaunchKernelGGL((gen_bwd_kernel<W, 2>), dim3((unsigned)(tn * tg)), dim3(kThr), 0, st, p);
     else if (pr.H % 8 == 0)
-        hipLaunchKernelGGL((gen_bwd_kernel<W, 1>), dim3((unsigned)(tn * tg)), dim3(kGBlock), 0, st, p);
+        hipLaunchKernelGGL((gen_bwd_kernel<W, 1>), dim3((unsigned)(tn * tg)), dim3(kThr), 0, st, p);
     else
-        hipLaunchKernelGGL((gen_bwd_kernel<W, 0>), dim3((unsigned)(tn * tg)), dim3(kGBlock), 0, st, p);
+        hipLaunchKernelGGL((gen_bwd_kernel<W, 0>), dim3((unsigned)(tn * tg)), dim3(kThr), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // dh (N x K) = dw (N x GW) . (V^T)^T, both with GW contiguous
     if ((e = transpose(p.V, GW, pr.K, Vt, GW, st)) != hipSuccess) return e;
     {
-        const int64_t tm = (pr.N + kBM - 1) / kBM, tk = (pr.K + 127) / 128;
-        hipLaunchKernelGGL((dma_gemm_kernel<uint16_t>), dim3((unsigned)(tm * tk)), dim3(kGBlock), 0, st, p.dw, GW, Vt,
+        const int64_t tm = (pr.N + kPBM - 1) / kPBM, tk = (pr.K + kPBN - 1) / kPBN;
+        hipLaunchKernelGGL((dma_gemm_kernel<uint16_t>), dim3((unsigned)(tm * tk)), dim3(PlainCfg::kThreads), 0, st, p.dw, GW, Vt,
                            GW, pr.N, pr.K, GW, GW, static_cast<uint16_t *>(pr.dh), pr.K, (int64_t)0, tk, tm * tk);
     }
     // dV (GW x K) = dw^T . (h^T)^T over the Np (zero-padded) tokens, in splits
@@ -645,9 +689,9 @@ hipError_t gen_bwd_w(const GenProblem &pr, hipStream_t st) {
     if ((e = transpose(p.dw, pr.N, GW, dwT, pl.Np, st)) != hipSuccess) return e;
     if ((e = transpose(p.h, pr.N, pr.K, hT, pl.Np, st)) != hipSuccess) return e;
     {
-        const int64_t tm = (GW + kBM - 1) / kBM, tk = (pr.K + 127) / 128;
+        const int64_t tm = (GW + kPBM - 1) / kPBM, tk = (pr.K + kPBN - 1) / kPBN;
         float *out = pl.splits > 1 ? parts : pr.dV;
-        hipLaunchKernelGGL((dma_gemm_kernel<float>), dim3((unsigned)(tm * tk * pl.splits)), dim3(kGBlock), 0, st, dwT,
+        hipLaunchKernelGGL((dma_gemm_kernel<float>), dim3((unsigned)(tm * tk * pl.splits)), dim3(PlainCfg::kThreads), 0, st, dwT,
                            pl.Np, hT, pl.Np, GW, pr.K, pl.Np, pl.kc, out, pr.K, GW * pr.K, tk, tm * tk);
         if (pl.splits > 1)
             hipLaunchKernelGGL(sum_splits, dim3((unsigned)((GW * pr.K + 255) / 256)), dim3(256), 0, st, parts,
@@ -673,8 +717,8 @@ hipError_t gen_bwd_w(const GenProblem &pr, hipStream_t st) {
 
 hipError_t generate_filters(const uint16_t *h, const uint16_t *V, int64_t N, int64_t K, int64_t C, uint16_t *w,
                             hipStream_t st) {
-    const int64_t tm = (N + kBM - 1) / kBM, tc = (C + 127) / 128;
-    hipLaunchKernelGGL((dma_gemm_kernel<uint16_t>), dim3((unsigned)(tm * tc)), dim3(kGBlock), 0, st, h, K, V, K, N, C,
+    const int64_t tm = (N + kPBM - 1) / kPBM, tc = (C + kPBN - 1) / kPBN;
+    hipLaunchKernelGGL((dma_gemm_kernel<uint16_t>), dim3((unsigned)(tm * tc)), dim3(PlainCfg::kThreads), 0, st, h, K, V, K, N, C,
                        K, K, w, C, (int64_t)0, tc, tm * tc);
     return hipGetLastError();
 }
