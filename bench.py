@@ -515,7 +515,7 @@ def stream_sweep(torch, binding, inputs) -> int:
 
 
 def summarize_sq(dirs, kernels=("hw_fwd_kernel", "hw_bwd_kernel", "lr_fwd_wide", "lr_fwd_mfma", "lr_bwd_mfma",
-                                 "lr_dz_", "lr_bwd_generic", "st_fwd_kernel", "st_bwd_kernel")) -> str:
+                                 "lr_bwd_taps", "lr_dz_", "lr_bwd_generic", "st_fwd_kernel", "st_bwd_kernel")) -> str:
     """Markdown table of the SQ counters (rocprofv3 --pmc passes of this
     script, one directory each) of the convolution kernels, averaged per
     dispatch: instructions per wave, vector-ALU and matrix-core busy fractions

@@ -258,6 +258,28 @@ struct Span {
 // execute in issue order).
 __device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); }
 
+// All ones when ok, else zero, hidden from the optimizer: a load whose
+// value is masked by it stays unconditional (a select on the loaded value
+// would be turned into a branch around the load, and a loop of such loads
+// then waits for each one in turn).
+__device__ __forceinline__ uint32_t keep_mask(bool ok) {
+    uint32_t m = ok ? 0xffffffffu : 0u;
+    asm volatile("" : "+v"(m));
+    return m;
+}
+
+// Workgroup barrier for waves that exchange data through LDS only: the
+// wave's LDS operations complete before it (lgkmcnt 0) and no LDS access
+// moves across it.  __syncthreads also waits for every global load and store
+// the wave has in flight (vmcnt 0), which drains a prefetch ring and waits
+// for store acknowledgements at every barrier; this one leaves them in
+// flight.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ----------------------------------------------------------- buffer access
 
 // Raw buffer resources: loads outside a resource's range read zero and

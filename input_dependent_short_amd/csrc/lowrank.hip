@@ -184,15 +184,15 @@ __device__ __forceinline__ void load_u_cols(const uint16_t *U, int R, int64_t D,
     for (int rt = 0; rt < RT; ++rt) {
         const int r = 16 * rt + i16;
         uint32_t h[4 * W];
+        // loads from U's start when out of range, zeroed by a mask (no branch per load)
+        const bool ok = r < R && ch0 < D;
+        const uint32_t m = keep_mask(ok);
+        const uint4 *src = reinterpret_cast<const uint4 *>(U + (ok ? ((int64_t)r * D + ch0) * W : 0));
 #pragma unroll
-        for (int j = 0; j < 4 * W; ++j) h[j] = 0u;
-        if (r < R && ch0 < D) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(U + ((int64_t)r * D + ch0) * W);
-#pragma unroll
-            for (int j = 0; j < W; ++j) {
-                const uint4 v = src[j];
-                h[4 * j] = v.x; h[4 * j + 1] = v.y; h[4 * j + 2] = v.z; h[4 * j + 3] = v.w;
-            }
+        for (int j = 0; j < W; ++j) {
+            const uint4 v = src[j];
+            h[4 * j] = v.x & m; h[4 * j + 1] = v.y & m;
+            h[4 * j + 2] = v.z & m; h[4 * j + 3] = v.w & m;
         }
 #pragma unroll
         for (int idx = 0; idx < 8 * W; ++idx) {  // element idx = channel e * W + tap k
@@ -390,11 +390,6 @@ __global__ __launch_bounds__(kBlock) void lr_fwd_mfma(LrParams p, int64_t nslice
 
 // Look-ahead shift inside a 16-lane row: lane i takes lane i+K of `cur`, and
 // lanes i >= 16-K take lane i+K-16 of `next` (the following 16 tokens).
-template <int K>
-__device__ __forceinline__ uint32_t shift_ahead_in_row(uint32_t cur, uint32_t next) {
-    const int rot = __builtin_amdgcn_mov_dpp((int)next, 0x120 + (16 - K), 0xf, 0xf, true);
-    return (uint32_t)__builtin_amdgcn_update_dpp(rot, (int)cur, 0x100 + K, 0xf, 0xf, false);
-}
 
 template <int W, int K>
 __device__ __forceinline__ void fill_ahead(Shifted<W> &gs, const uint32_t (&cur)[4], const uint32_t (&next)[4]) {
@@ -405,25 +400,8 @@ __device__ __forceinline__ void fill_ahead(Shifted<W> &gs, const uint32_t (&cur)
     }
 }
 
-// Shift by a tap k (1 <= k < W, known after unrolling) of four packed registers.
-template <int W, int K = 1>
-__device__ __forceinline__ void shift_ahead4(int k, const uint32_t (&cur)[4], const uint32_t (&next)[4],
-                                             uint32_t (&out)[4]) {
-    if constexpr (K < W) {
-        if (k == K) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) out[i] = shift_ahead_in_row<K>(cur[i], next[i]);
-        } else {
-            shift_ahead4<W, K + 1>(k, cur, next, out);
-        }
-    }
-}
 
 
-__device__ __forceinline__ bf16x8 bf16x8_from_u32(const uint32_t (&v)[4]) {
-    uint4 q = make_uint4(v[0], v[1], v[2], v[3]);
-    return __builtin_bit_cast(bf16x8, q);
-}
 
 // Backward of the fused low-rank convolution, bf16.
 //
@@ -478,20 +456,7 @@ struct BwdLds {
                   "the blocks of a CU must fit the LDS");
 };
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-// Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group,
-// lane i receives element (i & 3) of the 8-byte chunks addressed by lanes
-// i/4, 4 + i/4, 8 + i/4 and 12 + i/4.  Addressing lane i at row base + i/4,
-// column col0 + 4*(i & 3) of a row-major [row][col] bf16 array therefore
-// returns rows base .. base+3 of column col0 + i.
-__device__ __forceinline__ uint2 lds_read_tr(const unsigned char *addr) {
-    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(addr));
-    return __builtin_bit_cast(uint2, v);
-}
-
-template <bool V> struct MaskTag { static constexpr bool value = V; };
 
 // Whether the backward's walk may end after any 32-token pair rather than
 // after a whole ring of prefetch steps.  Only the two-half, 16-byte z variant
@@ -849,7 +814,7 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
 
             if (ps == 1) {
                 if constexpr (DZ) {
-                    __syncthreads();  // the pair's dz partials from all four waves
+                    lds_barrier();  // the pair's dz partials from all four waves
                 } else {
                     wave_lds_fence();  // the pair's dwc^T rows written by the wave's other lanes
                 }
@@ -913,7 +878,7 @@ __global__ __launch_bounds__(kBlock * H, (BwdLds<W, RC, H>::kBlocksPerCu)) void 
                                 v[it], rdz, 4 * (dz_block_off + (uint32_t)(it * (kBlock / L::RP) * R)), 0, 0);
                     }
                     if constexpr (L::kDzBufs == 1) {
-                        __syncthreads();  // partials read before the next pair overwrites them
+                        lds_barrier();  // partials read before the next pair overwrites them
                     } else {
                         buf ^= 1;         // the next pair writes the other buffer
                     }
@@ -1196,10 +1161,6 @@ bool bwd_uses_mfma(Dtype dt, int64_t D, int W, int R) {
     return walk_cap(D, 16 * kBwdRing, 16 * (2 * kBwdRing + 2)) >= 16 * kBwdRing;
 }
 
-// The reproducible backward splits the work as the fast one would on a
-// 256-CU device with one block per CU (every instance's kBlocksPerCu), on
-// every device, so that its order of summation is the same everywhere.
-constexpr int64_t kDetSlots = 256;
 
 size_t det_dz_floats(const BwdPlan &pl, int64_t N, int R) { return (((size_t)pl.ngroups * N * R + 3) / 4) * 4; }
 
@@ -1254,6 +1215,12 @@ hipError_t mfma_bwd(const LrProblem &pr, hipStream_t st, bool det) {
 // Which bf16 shapes compute dz in launches of their own (split backward):
 // the matrix-core backward then runs without dz, so its blocks exchange
 // nothing and add no dz atomics.
+// Whether ranks 33..64 at W = 2..4 take the backward with the taps of a
+// slice split over two waves (lowrank_taps.hip).
+#ifndef DSC_LR_TAPS
+#define DSC_LR_TAPS 1
+#endif
+
 #ifndef DSC_LR_SPLIT
 #define DSC_LR_SPLIT 0
 #endif
@@ -1318,7 +1285,11 @@ hipError_t mfma_bwd_rc(const LrProblem &pr, hipStream_t st, bool det, bool split
         return split_bwd<W, 1>(pr, st);
     }
     if constexpr (W <= 4) {
-        if ((pr.R + 31) / 32 == 2) return mfma_bwd<W, 2>(pr, st, det);
+        if ((pr.R + 31) / 32 == 2) {
+            if (DSC_LR_TAPS && lowrank_bwd_taps_supported(Dtype::BF16, pr.D, W, pr.R))
+                return lowrank_bwd_taps(pr, st, det);
+            return mfma_bwd<W, 2>(pr, st, det);
+        }
     }
     return mfma_bwd<W, 1>(pr, st, det);
 }
@@ -1397,6 +1368,30 @@ hipError_t lowrank_zero(float *p, int64_t n, hipStream_t s) {
     return hipGetLastError();
 }
 
+hipError_t lowrank_zero2(float *a, int64_t na, float *b, int64_t nb, hipStream_t s) {
+    const int64_t units = (na + 3) / 4 + (nb + 3) / 4;
+    if (units) hipLaunchKernelGGL(clear2, dim3((unsigned)nblocks(units)), dim3(kBlock), 0, s,
+                                  reinterpret_cast<uint32_t *>(a), na, reinterpret_cast<uint32_t *>(b), nb);
+    return hipGetLastError();
+}
+
+hipError_t lowrank_sum_parts(const float *src, int64_t nparts, int64_t stride, float *dst_f32, uint16_t *dst_bf16,
+                             int64_t n, hipStream_t s) {
+    if (!n) return hipSuccess;
+    if (dst_bf16)
+        hipLaunchKernelGGL(sum_parts<uint16_t>, dim3((unsigned)nblocks(n)), dim3(kBlock), 0, s, src, nparts, stride,
+                           dst_bf16, n);
+    else
+        hipLaunchKernelGGL(sum_parts<float>, dim3((unsigned)nblocks(n)), dim3(kBlock), 0, s, src, nparts, stride,
+                           dst_f32, n);
+    return hipGetLastError();
+}
+
+hipError_t lowrank_round_bf16(const float *src, uint16_t *dst, int64_t n, hipStream_t s) {
+    if (n) hipLaunchKernelGGL(cast_f32_bf16, dim3((unsigned)nblocks(n)), dim3(kBlock), 0, s, src, dst, n);
+    return hipGetLastError();
+}
+
 hipError_t lowrank_bwd(const LrProblem &p, hipStream_t s, bool split_ok) {
     if (p.dtype == Dtype::BF16) {
         DSC_W_SWITCH(p.W, (mfma_bwd_rc<Wc>(p, s, false, split_ok)));
@@ -1406,6 +1401,7 @@ hipError_t lowrank_bwd(const LrProblem &p, hipStream_t s, bool split_ok) {
 
 size_t lowrank_bwd_det_workspace(Dtype dt, int64_t N, int64_t D, int32_t W, int32_t R) {
     if (!bwd_uses_mfma(dt, D, W, R)) return 0;
+    if (DSC_LR_TAPS && lowrank_bwd_taps_supported(dt, D, W, R)) return lowrank_bwd_taps_det_workspace(N, D, W, R);
     const BwdPlan pl = bwd_plan(N, D, W, R, kDetSlots);
     const size_t bytes = (det_dz_floats(pl, N, R) + (size_t)pl.tchunks * R * D * W) * sizeof(float);
     return (bytes + 255) & ~(size_t)255;

@@ -70,6 +70,49 @@ __device__ __forceinline__ void shift_back4(int k, const uint32_t (&cur)[4], con
     }
 }
 
+// Shift ahead by K tokens: token t takes the value of token t+K, the last K
+// of the row taken from the next step (next).
+template <int K>
+__device__ __forceinline__ uint32_t shift_ahead_in_row(uint32_t cur, uint32_t next) {
+    const int rot = __builtin_amdgcn_mov_dpp((int)next, 0x120 + (16 - K), 0xf, 0xf, true);
+    return (uint32_t)__builtin_amdgcn_update_dpp(rot, (int)cur, 0x100 + K, 0xf, 0xf, false);
+}
+
+// Shift by a tap k (1 <= k < W, known after unrolling) of four packed registers.
+template <int W, int K = 1>
+__device__ __forceinline__ void shift_ahead4(int k, const uint32_t (&cur)[4], const uint32_t (&next)[4],
+                                             uint32_t (&out)[4]) {
+    if constexpr (K < W) {
+        if (k == K) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) out[i] = shift_ahead_in_row<K>(cur[i], next[i]);
+        } else {
+            shift_ahead4<W, K + 1>(k, cur, next, out);
+        }
+    }
+}
+
+__device__ __forceinline__ bf16x8 bf16x8_from_u32(const uint32_t (&v)[4]) {
+    uint4 q = make_uint4(v[0], v[1], v[2], v[3]);
+    return __builtin_bit_cast(bf16x8, q);
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group,
+// lane i receives element (i & 3) of the 8-byte chunks addressed by lanes
+// i/4, 4 + i/4, 8 + i/4 and 12 + i/4.  Addressing lane i at row base + i/4,
+// column col0 + 4*(i & 3) of a row-major [row][col] bf16 array therefore
+// returns rows base .. base+3 of column col0 + i.
+__device__ __forceinline__ uint2 lds_read_tr(const unsigned char *addr) {
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(addr));
+    return __builtin_bit_cast(uint2, v);
+}
+
+// Compile-time switch of a step body between its masked and unmasked copies.
+template <bool V> struct MaskTag { static constexpr bool value = V; };
+
 // Position of a lane's token inside its sequence, for a walk in 16-token
 // steps taken in order.  `start` is the first token of the sequence in
 // effect before the step (wave-uniform); the step's own starts come from the
@@ -185,11 +228,13 @@ __device__ __forceinline__ void load_u_rows(const uint16_t *U, int R, int64_t D,
             for (int e = 0; e < 8; ++e) {
                 const int r = 32 * c + 8 * q + e;
                 uint16_t v[W];
+                // every lane loads (from U's start when out of range) and zeroes by a
+                // mask: a branch per element would wait for each load in turn
+                const bool ok = r < R && ch < D;
+                const uint16_t m = (uint16_t)keep_mask(ok);
+                load_taps<W>(U + (ok ? ((int64_t)r * D + ch) * W : 0), v);
 #pragma unroll
-                for (int k = 0; k < W; ++k) v[k] = 0;
-                if (r < R && ch < D) load_taps<W>(U + ((int64_t)r * D + ch) * W, v);
-#pragma unroll
-                for (int k = 0; k < W; ++k) ua[k][t][c][e] = __builtin_bit_cast(__bf16, v[k]);
+                for (int k = 0; k < W; ++k) ua[k][t][c][e] = __builtin_bit_cast(__bf16, (uint16_t)(v[k] & m));
             }
     }
 }
@@ -240,6 +285,11 @@ int64_t walk_cap(int64_t D, int64_t unit, int64_t overrun) {
     const int64_t span = kStreamSpan / (2 * D) - overrun;
     return ((span < kMaxTokPerWave ? span : kMaxTokPerWave) / unit) * unit;
 }
+
+// The reproducible backward splits the work as the fast one would on a
+// 256-CU device with one block per CU, on every device, so that its order
+// of summation is the same everywhere.
+constexpr int64_t kDetSlots = 256;
 
 constexpr int64_t kWaveFixedTokens = 64;  // a forward wave's set-up, in tokens of walk
 

@@ -81,6 +81,13 @@ LR_CASES = [
     ("bf16", 1, 64, 96, 2, 48, False, None),
     # wide forward with R in 33..64 gathered (R % 8 != 0), several token walks per channel pair
     ("bf16", 1, 4100, 64, 3, 36, True, (1, 700)),
+    # backward with the taps of a slice over two waves (33 <= R <= 64, W = 2..4):
+    # gathered z rows (R % 4 != 0), a partial last slice, packed sequences,
+    # several token chunks per channel group
+    ("bf16", 1, 300, 96, 4, 45, True, (1, 80)),
+    ("bf16", 2, 150, 64, 3, 63, False, None),
+    ("bf16", 1, 700, 256, 2, 33, True, (1, 120)),
+    ("bf16", 2, 333, 136, 4, 40, False, (1, 50)),
     # backward blocks of two token halves, several blocks, partial last half, R % 8 != 0
     ("bf16", 3, 1000, 128, 4, 20, True, (100, 900)),
     # W = 5, 6, 7 on every kernel family: wide forward + matrix-core backward
