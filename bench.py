@@ -263,7 +263,7 @@ ENTRY_KERNELS = {
     "dsc_headwise_fwd": (["hw_fwd_kernel"], []),
     "dsc_headwise_bwd": (["hw_bwd_kernel"], []),
     "dsc_lowrank_fwd": (["lr_fwd_wide", "lr_fwd_mfma", "lr_fwd_generic"], []),
-    "dsc_lowrank_bwd": (["lr_bwd_mfma", "lr_bwd_generic"], ["clear2", "fill_zero_f32", "cast_f32_bf16"]),
+    "dsc_lowrank_bwd": (["lr_bwd_taps", "lr_bwd_mfma", "lr_bwd_generic"], ["clear2", "fill_zero_f32", "cast_f32_bf16"]),
     "dsc_static_fwd": (["st_fwd_kernel"], []),
     "dsc_static_bwd": (["st_bwd_kernel"], ["st_zero"]),
     "dsc_headwise_decode": (["hw_decode_kernel"], []),
