@@ -24,12 +24,14 @@
 //     with dy shifted ahead by k (DPP row moves, filled from the next step);
 //   * dwc of its taps (x shifted back by k), which is directly the B operand
 //     of dz^T += U_k dwc_k, and stages dwc^T in LDS for dU.
-// Per 32-token pair the block meets two barriers: between them the first
-// wave of a slice adds the second wave's part of dx (exchanged through LDS)
-// and stores dx, every wave adds the pair's dU of its taps on the matrix
-// cores (operands re-read transposed from LDS), and the dz partials of the
-// 8 waves are summed in LDS and added to an fp32 accumulator with one atomic
-// per (token, rank).  The z ring (8 slots of 16 rows and a copy of slot 0,
+// Per 32-token pair the block meets two barriers (LDS only: loads and
+// stores in flight stay in flight).  Between them the first wave of a slice
+// adds the second wave's part of dx (exchanged through LDS) into the block's
+// dx tile, which all threads store at the next pair's start as whole rows of
+// the block's 128 channels.  Every wave also adds the pair's dU of its taps on
+// the matrix cores (operands re-read transposed from LDS), and the dz
+// partials of the 8 waves are summed in LDS and added to an fp32 accumulator
+// with one atomic per (token, rank).  The z ring (8 slots of 16 rows and a copy of slot 0,
 // so that every step's rows and the W-1 after them are contiguous) is
 // written two pairs ahead by all threads of the block.  dU stays in
 // registers over the whole range and is added with coalesced atomics at the
