@@ -284,14 +284,56 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
                     const uint32_t sa = (win >> (tok + W)) & ((1u << (W - 1)) - 1u);  // starts in n+1 .. n+W-1
                     ahead = sa ? 1 + __builtin_ctz(sa) : W;
                 }
-                auto body = [&](auto mask_tag) {
+                // Each step forms dwc first (it is the last reader of x's previous
+                // step), then issues the x refill, then forms the wave's part of dx (the
+                // last reader of dy's current step) and issues the dy refill, so that
+                // each load is in flight while the other half of the step runs.
+                const unsigned char *zst = zring + 16 * (zs0 + i) * L::PZ;  // rows of step s
+                auto dwc_part = [&](auto mask_tag) {
+                    constexpr bool M = decltype(mask_tag)::value;
+                    const uint32_t gc[4] = {gr[cur].x, gr[cur].y, gr[cur].z, gr[cur].w};
+                    const uint32_t xc[4] = {xr[cur].x, xr[cur].y, xr[cur].z, xr[cur].w};
+                    const uint32_t xp[4] = {xr[prv].x, xr[prv].y, xr[prv].z, xr[prv].w};
+                    // dwc of the wave's taps: dz^T partial on the matrix cores, dwc^T staged for dU
+                    const bool own = n < nend;  // tokens outside this block's range contribute nothing
+                    floatx4 cz[RT];
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) cz[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int j = 0; j < NK; ++j) {
+                        const int k = K0 + j;
+                        uint32_t xk[4];
+                        if (k == 0) {
+#pragma unroll
+                            for (int i2 = 0; i2 < 4; ++i2) xk[i2] = xc[i2];
+                        } else {
+                            shift_back4<W>(k, xc, xp, xk);
+                        }
+                        uint32_t dw[4];
+#pragma unroll
+                        for (int i2 = 0; i2 < 4; ++i2) {
+                            const uint32_t xv = (!M || (own && k <= back)) ? xk[i2] : 0u;
+                            dw[i2] = pack_bf16x2(bf16_lo(gc[i2]) * bf16_lo(xv), bf16_hi(gc[i2]) * bf16_hi(xv));
+                        }
+                        const bf16x8 b = bf16x8_from_u32(dw);
+#pragma unroll
+                        for (int rt = 0; rt < RT; ++rt)
+                            cz[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ub[j][rt], b, cz[rt], 0, 0, 0);
+                        uint2 *d = reinterpret_cast<uint2 *>(dwcT + j * 32 * L::PW + (16 * ps + tok) * L::PW + 16 * q);
+                        d[0] = make_uint2(dw[0], dw[1]);
+                        d[1] = make_uint2(dw[2], dw[3]);
+                    }
+                    // dz partials (rows r = 16rt + 4q + jj, column = token) for the block's sum
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) {
+                        float4 *d = reinterpret_cast<float4 *>(dzb + (16 * ps + tok) * L::PD + 4 * (16 * rt + 4 * q));
+                        *d = make_float4(cz[rt][0], cz[rt][1], cz[rt][2], cz[rt][3]);
+                    }
+                };
+                auto dx_part = [&](auto mask_tag) {
                     constexpr bool M = decltype(mask_tag)::value;
                     const uint32_t gc[4] = {gr[cur].x, gr[cur].y, gr[cur].z, gr[cur].w};
                     const uint32_t gn[4] = {gr[nxt].x, gr[nxt].y, gr[nxt].z, gr[nxt].w};
-                    const uint32_t xc[4] = {xr[cur].x, xr[cur].y, xr[cur].z, xr[cur].w};
-                    const uint32_t xp[4] = {xr[prv].x, xr[prv].y, xr[prv].z, xr[prv].w};
-                    const unsigned char *zst = zring + 16 * (zs0 + i) * L::PZ;  // rows of step s
-
                     // the wave's part of dx: sum over its taps of w[n+k] dy[n+k] (rho
                     // entering as the accumulator of tap 0's product)
                     float acc[8];
@@ -338,47 +380,11 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
                         for (int c = 0; c < 8; ++c) accp[ps][c] = acc[c];
                     }
 
-                    // dwc of the wave's taps: dz^T partial on the matrix cores, dwc^T staged for dU
-                    const bool own = n < nend;  // tokens outside this block's range contribute nothing
-                    floatx4 cz[RT];
-#pragma unroll
-                    for (int rt = 0; rt < RT; ++rt) cz[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int j = 0; j < NK; ++j) {
-                        const int k = K0 + j;
-                        uint32_t xk[4];
-                        if (k == 0) {
-#pragma unroll
-                            for (int i2 = 0; i2 < 4; ++i2) xk[i2] = xc[i2];
-                        } else {
-                            shift_back4<W>(k, xc, xp, xk);
-                        }
-                        uint32_t dw[4];
-#pragma unroll
-                        for (int i2 = 0; i2 < 4; ++i2) {
-                            const uint32_t xv = (!M || (own && k <= back)) ? xk[i2] : 0u;
-                            dw[i2] = pack_bf16x2(bf16_lo(gc[i2]) * bf16_lo(xv), bf16_hi(gc[i2]) * bf16_hi(xv));
-                        }
-                        const bf16x8 b = bf16x8_from_u32(dw);
-#pragma unroll
-                        for (int rt = 0; rt < RT; ++rt)
-                            cz[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ub[j][rt], b, cz[rt], 0, 0, 0);
-                        uint2 *d = reinterpret_cast<uint2 *>(dwcT + j * 32 * L::PW + (16 * ps + tok) * L::PW + 16 * q);
-                        d[0] = make_uint2(dw[0], dw[1]);
-                        d[1] = make_uint2(dw[2], dw[3]);
-                    }
-                    // dz partials (rows r = 16rt + 4q + jj, column = token) for the block's sum
-#pragma unroll
-                    for (int rt = 0; rt < RT; ++rt) {
-                        float4 *d = reinterpret_cast<float4 *>(dzb + (16 * ps + tok) * L::PD + 4 * (16 * rt + 4 * q));
-                        *d = make_float4(cz[rt][0], cz[rt][1], cz[rt][2], cz[rt][3]);
-                    }
                 };
-                if (fast) body(MaskTag<false>{}); else body(MaskTag<true>{});
-
-                // ring refills (issued after the step's reads of these slots)
-                xr[prv] = fetch_x(s + P - 1);
-                gr[cur] = fetch_g(s + P);
+                if (fast) dwc_part(MaskTag<false>{}); else dwc_part(MaskTag<true>{});
+                xr[prv] = fetch_x(s + P - 1);  // x of step s-1 is no longer read
+                if (fast) dx_part(MaskTag<false>{}); else dx_part(MaskTag<true>{});
+                gr[cur] = fetch_g(s + P);      // dy of step s is no longer read
 
                 if (ps == 1) {
                     lds_barrier();  // the pair's dx parts, dz partials and dwc^T rows of every wave
