@@ -13,27 +13,31 @@
 //   dU[r,d*W+k] = sum_n z[n,r] dwc[n,d,k]
 //
 // Design.  A block of 8 waves owns 4 slices of 32 channels and a token range
-// walked in 16-token steps; the two waves of a slice take the taps [0, KH)
-// and [KH, W).  Each wave keeps the U operands of its own taps only (both
-// matrix-core layouts) and the dU tiles of its own taps, half of what one
-// wave holding every tap needs, so that two waves fit per SIMD and one
-// wave's matrix-core products overlap the other's vector work.  Per step a
-// wave forms
-//   * w of its taps for tokens n+k on the matrix cores (U_k^T z, the z rows
-//     read from one LDS ring shared by the block) and its taps' part of dx
-//     with dy shifted ahead by k (DPP row moves, filled from the next step);
+// walked in 16-token steps.  The two waves of a slice split its work two
+// ways: for dx by channels (wave HF takes channels 4HF..4HF+3 of every
+// 8-channel chunk, over every tap), for dz and dU by taps (the first wave
+// takes the taps [0, KH), the second [KH, W)).  Each wave keeps the U
+// operands of dx for its channels and of dz for its taps, and the dU tiles of
+// its taps, half of what one wave doing all of the slice needs, so that two
+// waves fit per SIMD and one wave's matrix-core products overlap the other's
+// vector work.  Per step a wave forms
 //   * dwc of its taps (x shifted back by k), which is directly the B operand
-//     of dz^T += U_k dwc_k, and stages dwc^T in LDS for dU.
-// Per 32-token pair the block meets two barriers (LDS only: loads and
-// stores in flight stay in flight).  Between them the first wave of a slice
-// adds the second wave's part of dx (exchanged through LDS) into the block's
-// dx tile, which all threads store at the next pair's start as whole rows of
-// the block's 128 channels.  Every wave also adds the pair's dU of its taps on
-// the matrix cores (operands re-read transposed from LDS), and the dz
-// partials of the 8 waves are summed in LDS and added to an fp32 accumulator
-// with one atomic per (token, rank).  The z ring (8 slots of 16 rows and a copy of slot 0,
-// so that every step's rows and the W-1 after them are contiguous) is
-// written two pairs ahead by all threads of the block.  dU stays in
+//     of dz^T += U_k dwc_k, and stages dwc^T in LDS for dU;
+//   * w of every tap for its channels and tokens n+k on the matrix cores
+//     (U_k^T z, the z rows read from one LDS ring shared by the block) and dx
+//     of its channels with dy shifted ahead by k (DPP row moves, filled from
+//     the next step), written as bf16 into the pair's dx tile in LDS.
+// The x refill is issued between the two parts and the dy refill after them,
+// so each load is in flight while half a step runs.  Per 32-token pair the
+// block meets two barriers (LDS only: loads and stores in flight stay in
+// flight).  At the next pair's start all threads store the pair's dx tile as
+// whole rows of the block's 128 channels (two tiles, pairs alternate).
+// Between the barriers every wave adds the pair's dU of its taps on the
+// matrix cores (operands re-read transposed from LDS), and the dz partials of
+// the 8 waves are summed in LDS and added to an fp32 accumulator with one
+// atomic per (token, rank).  The z ring (8 slots of 16 rows and a copy of
+// slot 0, so that every step's rows and the W-1 after them are contiguous)
+// is written two pairs ahead by all threads of the block.  dU stays in
 // registers over the whole range and is added with coalesced atomics at the
 // end, as in the one-wave-per-slice kernel of lowrank.hip.
 #include "lowrank_common.h"
@@ -60,14 +64,11 @@ struct TapLds {
     static constexpr int kDwcWave = KH * 32 * PW;
     static constexpr int PD = 4 * RP + 16;  // bytes per token row of dz partials
     static constexpr int kDzWave = 32 * PD;
-    static constexpr int PX = 4 * 36;       // bytes per token row of the dx exchange (32 floats + pad)
-    static constexpr int kDxSlice = 32 * PX;
     static constexpr int oDwc = kZ;
     static constexpr int oDz = oDwc + kTapWaves * kDwcWave;
-    static constexpr int oDx = oDz + kTapWaves * kDzWave;
-    static constexpr int oDxt = oDx + 4 * kDxSlice;
-    static constexpr int kDxt = 32 * 256;        // the pair's dx rows of the block's 128 channels (bf16)
-    static constexpr int kLoop = oDxt + kDxt;
+    static constexpr int oDxt = oDz + kTapWaves * kDzWave;
+    static constexpr int kDxt = 32 * 256;        // a pair's dx rows of the block's 128 channels (bf16)
+    static constexpr int kLoop = oDxt + 2 * kDxt;  // two tiles: pairs alternate
     static constexpr int kDuPitch = 32 * W + 1;  // floats per rank row of a slice's staged dU tile
     static constexpr int kDuSlice = RP * kDuPitch * 4;
     static constexpr int kBytes = kLoop > 4 * kDuSlice ? kLoop : 4 * kDuSlice;
@@ -116,9 +117,10 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
     unsigned char *zring = lds;
     unsigned char *dwcT = lds + L::oDwc + wid * L::kDwcWave;  // [tap slot][32 tokens][PW]
     unsigned char *dzb = lds + L::oDz + wid * L::kDzWave;     // [32 tokens][PD]
-    unsigned char *dxx = lds + L::oDx + slice * L::kDxSlice;  // [32 tokens][PX]
     // dx of a pair, [32 tokens][16 chunks of 8 channels], chunk c of row r at
-    // position c ^ (r & 15) (16 rows at one chunk hit distinct banks)
+    // position c ^ (r & 15) (16 rows at one chunk hit distinct banks); pair p
+    // writes tile p % 2 during its steps, and the block stores it at the start
+    // of pair p + 1
     unsigned char *dxt = lds + L::oDxt;
 
     StartBits<kSeqWords> starts;
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
         dxt_off = ch < D ? (uint32_t)((row * D + ch) * 2) : kFar;
     }
     auto store_dx = [&](int64_t first_step) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(dxt + 16 * tid);
+        const uint4 v = *reinterpret_cast<const uint4 *>(dxt + ((first_step >> 1) & 1) * L::kDxt + 16 * tid);
         buf_store16<kLrNtDx>(rdx, dxt_off + (uint32_t)first_step * act_step, v);
     };
 
@@ -202,14 +204,15 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
         constexpr int K0 = HF * KH;                  // first tap of this wave
         constexpr int NK = HF == 0 ? KH : W - KH;    // taps K0 .. K0+NK-1
 
-        // U operands of the wave's taps, kept in registers for the whole walk:
-        //   ua: rows channel d0 + 8(i>>2) + 4t + (i&3), K rank 32c + 8(lane>>4) + e
-        //   ub: rows rank 16rt + (lane&15), K channel d0 + 8(lane>>4) + e
-        bf16x8 ua[NK][2][2];
+        // U operands kept in registers for the whole walk:
+        //   ua (dx, every tap, the wave's channel half HF of the slice): rows
+        //     channel d0 + 8(i>>2) + 4HF + (i&3), K rank 32c + 8(lane>>4) + e
+        //   ub (dz, the wave's taps): rows rank 16rt + (lane&15), K channel
+        //     d0 + 8(lane>>4) + e
+        bf16x8 ua[W][2];
         bf16x8 ub[NK][RT];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int64_t ch = d0 + 8 * (i16 >> 2) + 4 * t + (i16 & 3);
+        {
+            const int64_t ch = d0 + 8 * (i16 >> 2) + 4 * HF + (i16 & 3);
 #pragma unroll
             for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -220,7 +223,7 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
                     const uint16_t m = (uint16_t)keep_mask(ok);
                     load_taps<W>(U + (ok ? ((int64_t)r * D + ch) * W : 0), v);
 #pragma unroll
-                    for (int j = 0; j < NK; ++j) ua[j][t][c][e] = __builtin_bit_cast(__bf16, (uint16_t)(v[K0 + j] & m));
+                    for (int k = 0; k < W; ++k) ua[k][c][e] = __builtin_bit_cast(__bf16, (uint16_t)(v[k] & m));
                 }
         }
 #pragma unroll
@@ -252,7 +255,6 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
             for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) du[j][ct][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        float accp[2][8];  // first wave: its part of dx for the pair's two steps
 
         for (int64_t s0 = 0; s0 < nsteps; s0 += P) {
             const int zs0 = (int)(s0 & 7);  // ring slot of step s0 (0 or 4)
@@ -264,6 +266,7 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
                 const int64_t nstep = nbeg + 16 * s;
                 const int64_t n = nstep + tok;
 
+                unsigned char *dxtp = dxt + ((s >> 1) & 1) * L::kDxt;  // this pair's dx tile
                 if (ps == 0) {  // z rows two pairs ahead into the ring, the next pair fetched
                     write_zp(s / 2 + 2, zpf);
                     zpf = fetch_zp(s / 2 + 3);
@@ -334,12 +337,12 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
                     constexpr bool M = decltype(mask_tag)::value;
                     const uint32_t gc[4] = {gr[cur].x, gr[cur].y, gr[cur].z, gr[cur].w};
                     const uint32_t gn[4] = {gr[nxt].x, gr[nxt].y, gr[nxt].z, gr[nxt].w};
-                    // the wave's part of dx: sum over its taps of w[n+k] dy[n+k] (rho
-                    // entering as the accumulator of tap 0's product)
-                    float acc[8];
+                    // dx of the wave's 4 channels of every 8-channel chunk: the sum over
+                    // every tap of w[n+k] dy[n+k] (rho entering as the accumulator of tap
+                    // 0's product), into the pair's dx tile
+                    float acc[4];
 #pragma unroll
-                    for (int j = 0; j < NK; ++j) {
-                        const int k = K0 + j;
+                    for (int k = 0; k < W; ++k) {
                         const unsigned char *zrow_k = zst + (tok + k) * L::PZ;
                         bf16x8 zb[2];
 #pragma unroll
@@ -348,38 +351,28 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
                             const uint2 a = src[0], b = src[1];
                             zb[c] = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
                         }
-                        uint32_t gk[4];
+                        uint32_t gk[2];
                         if (k == 0) {
-#pragma unroll
-                            for (int i2 = 0; i2 < 4; ++i2) gk[i2] = gc[i2];
+                            gk[0] = gc[2 * HF];
+                            gk[1] = gc[2 * HF + 1];
                         } else {
-                            shift_ahead4<W>(k, gc, gn, gk);
-#pragma unroll
-                            for (int i2 = 0; i2 < 4; ++i2) gk[i2] = (!M || k < ahead) ? gk[i2] : 0u;
+                            uint32_t g4[4];
+                            shift_ahead4<W>(k, gc, gn, g4);
+                            gk[0] = (!M || k < ahead) ? g4[2 * HF] : 0u;
+                            gk[1] = (!M || k < ahead) ? g4[2 * HF + 1] : 0u;
                         }
+                        const float c0 = k == 0 ? p.rho : 0.f;
+                        floatx4 cw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua[k][0], zb[0],
+                                                                             floatx4{c0, c0, c0, c0}, 0, 0, 0);
+                        cw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua[k][1], zb[1], cw, 0, 0, 0);
 #pragma unroll
-                        for (int t = 0; t < 2; ++t) {
-                            const float c0 = k == 0 ? p.rho : 0.f;
-                            floatx4 cw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua[j][t][0], zb[0],
-                                                                                 floatx4{c0, c0, c0, c0}, 0, 0, 0);
-                            cw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua[j][t][1], zb[1], cw, 0, 0, 0);
-#pragma unroll
-                            for (int jj = 0; jj < 4; ++jj) {
-                                const int c = 4 * t + jj;
-                                const float gv = (c & 1) ? bf16_hi(gk[c >> 1]) : bf16_lo(gk[c >> 1]);
-                                acc[c] = j == 0 ? cw[jj] * gv : __builtin_fmaf(cw[jj], gv, acc[c]);
-                            }
+                        for (int jj = 0; jj < 4; ++jj) {
+                            const float gv = (jj & 1) ? bf16_hi(gk[jj >> 1]) : bf16_lo(gk[jj >> 1]);
+                            acc[jj] = k == 0 ? cw[jj] * gv : __builtin_fmaf(cw[jj], gv, acc[jj]);
                         }
                     }
-                    if constexpr (HF == 1) {
-                        float4 *d = reinterpret_cast<float4 *>(dxx + (16 * ps + tok) * L::PX + 32 * q);
-                        d[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-                        d[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-                    } else {
-#pragma unroll
-                        for (int c = 0; c < 8; ++c) accp[ps][c] = acc[c];
-                    }
-
+                    *reinterpret_cast<uint2 *>(dxtp + (16 * ps + tok) * 256 + 16 * ((4 * slice + q) ^ tok) + 8 * HF) =
+                        make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
                 };
                 if (fast) dwc_part(MaskTag<false>{}); else dwc_part(MaskTag<true>{});
                 xr[prv] = fetch_x(s + P - 1);  // x of step s-1 is no longer read
@@ -387,26 +380,7 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
                 gr[cur] = fetch_g(s + P);      // dy of step s is no longer read
 
                 if (ps == 1) {
-                    lds_barrier();  // the pair's dx parts, dz partials and dwc^T rows of every wave
-                    if constexpr (HF == 0) {
-                        // dx of the pair's two steps: this wave's part plus the second wave's,
-                        // into the block's tile (stored at the next pair's start)
-#pragma unroll
-                        for (int sp = 0; sp < 2; ++sp) {
-                            const float4 *src = reinterpret_cast<const float4 *>(dxx + (16 * sp + tok) * L::PX + 32 * q);
-                            const float4 a = src[0], b = src[1];
-                            const float o[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-                            float v8[8];
-#pragma unroll
-                            for (int c = 0; c < 8; ++c) v8[c] = accp[sp][c] + o[c];
-                            uint4 v;
-                            v.x = pack_bf16x2(v8[0], v8[1]);
-                            v.y = pack_bf16x2(v8[2], v8[3]);
-                            v.z = pack_bf16x2(v8[4], v8[5]);
-                            v.w = pack_bf16x2(v8[6], v8[7]);
-                            *reinterpret_cast<uint4 *>(dxt + (16 * sp + tok) * 256 + 16 * ((4 * slice + q) ^ tok)) = v;
-                        }
-                    }
+                    lds_barrier();  // the pair's dx tile, dz partials and dwc^T rows of every wave
                     // dU_k^T[ch, r] += sum over the pair's 32 tokens of dwc_k^T[ch, tok] z[tok, r],
                     // operands re-read transposed (lane = channel / rank, registers = tokens)
                     const int trow = 8 * q + (i16 >> 2);
@@ -453,8 +427,10 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
 #pragma unroll
                     for (int it = 0; it < 4; ++it) {
                         const int tl = wid + 8 * it;
+                        // the token's row offset is wave-uniform: the scalar offset operand
                         if (lane < R && npair0 + tl < nend)
-                            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v[it], rdz, 4 * (tl * R + lane), 0, 0);
+                            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+                                v[it], rdz, 4 * lane, __builtin_amdgcn_readfirstlane(4 * tl * R), 0);
                     }
                     lds_barrier();  // every wave has read the exchange buffers before the next pair writes them
                 }
