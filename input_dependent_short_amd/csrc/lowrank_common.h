@@ -92,6 +92,33 @@ __device__ __forceinline__ void shift_ahead4(int k, const uint32_t (&cur)[4], co
     }
 }
 
+// The same shifts of two packed registers.
+template <int W, int K = 1>
+__device__ __forceinline__ void shift_back2(int k, const uint32_t (&cur)[2], const uint32_t (&prev)[2],
+                                            uint32_t (&out)[2]) {
+    if constexpr (K < W) {
+        if (k == K) {
+            out[0] = shift_in_row<K>(cur[0], prev[0]);
+            out[1] = shift_in_row<K>(cur[1], prev[1]);
+        } else {
+            shift_back2<W, K + 1>(k, cur, prev, out);
+        }
+    }
+}
+
+template <int W, int K = 1>
+__device__ __forceinline__ void shift_ahead2(int k, const uint32_t (&cur)[2], const uint32_t (&next)[2],
+                                             uint32_t (&out)[2]) {
+    if constexpr (K < W) {
+        if (k == K) {
+            out[0] = shift_ahead_in_row<K>(cur[0], next[0]);
+            out[1] = shift_ahead_in_row<K>(cur[1], next[1]);
+        } else {
+            shift_ahead2<W, K + 1>(k, cur, next, out);
+        }
+    }
+}
+
 __device__ __forceinline__ bf16x8 bf16x8_from_u32(const uint32_t (&v)[4]) {
     uint4 q = make_uint4(v[0], v[1], v[2], v[3]);
     return __builtin_bit_cast(bf16x8, q);

@@ -13,29 +13,29 @@
 //   dU[r,d*W+k] = sum_n z[n,r] dwc[n,d,k]
 //
 // Design.  A block of 8 waves owns 4 slices of 32 channels and a token range
-// walked in 16-token steps.  The two waves of a slice split its work two
-// ways: for dx by channels (wave HF takes channels 4HF..4HF+3 of every
-// 8-channel chunk, over every tap), for dz and dU by taps (the first wave
-// takes the taps [0, KH), the second [KH, W)).  Each wave keeps the U
-// operands of dx for its channels and of dz for its taps, and the dU tiles of
-// its taps, half of what one wave doing all of the slice needs, so that two
-// waves fit per SIMD and one wave's matrix-core products overlap the other's
-// vector work.  Per step a wave forms
-//   * dwc of its taps (x shifted back by k), which is directly the B operand
-//     of dz^T += U_k dwc_k, and stages dwc^T in LDS for dU;
-//   * w of every tap for its channels and tokens n+k on the matrix cores
-//     (U_k^T z, the z rows read from one LDS ring shared by the block) and dx
-//     of its channels with dy shifted ahead by k (DPP row moves, filled from
-//     the next step), written as bf16 into the pair's dx tile in LDS.
+// walked in 16-token steps.  The two waves of a slice split it by channels:
+// wave HF takes channels 4HF .. 4HF+3 of every 8-channel chunk, for dx, dwc,
+// dz and dU alike, and loads only those 8 bytes of each x and dy row (the
+// two waves together read each row once).  Each wave keeps the U operands of
+// its 16 channels (both matrix-core layouts) and their dU tiles, half of what
+// one wave doing the whole slice needs, so that two waves fit per SIMD and
+// one wave's matrix-core products overlap the other's vector work.  Per step
+// a wave forms
+//   * dwc of every tap (x shifted back by k): by pairs of taps the B operand
+//     of dz^T += U dwc, and staged as dwc^T in LDS for dU;
+//   * w of every tap for tokens n+k on the matrix cores (U_k^T z, the z rows
+//     read from one LDS ring shared by the block) and dx with dy shifted ahead
+//     by k (DPP row moves, filled from the next step), written as bf16 into
+//     the pair's dx tile in LDS.
 // The x refill is issued between the two parts and the dy refill after them,
 // so each load is in flight while half a step runs.  Per 32-token pair the
 // block meets two barriers (LDS only: loads and stores in flight stay in
 // flight).  At the next pair's start all threads store the pair's dx tile as
 // whole rows of the block's 128 channels (two tiles, pairs alternate).
-// Between the barriers every wave adds the pair's dU of its taps on the
-// matrix cores (operands re-read transposed from LDS), and the dz partials of
-// the 8 waves are summed in LDS and added to an fp32 accumulator with one
-// atomic per (token, rank).  The z ring (8 slots of 16 rows and a copy of
+// Between the barriers every wave adds the pair's dU on the matrix cores
+// (operands re-read transposed from LDS), and the dz partials of the 8 waves
+// are summed in LDS in a fixed order and added to an fp32 accumulator with
+// one atomic per (token, rank).  The z ring (8 slots of 16 rows and a copy of
 // slot 0, so that every step's rows and the W-1 after them are contiguous)
 // is written two pairs ahead by all threads of the block.  dU stays in
 // registers over the whole range and is added with coalesced atomics at the
@@ -47,21 +47,31 @@ namespace {
 
 constexpr int kTapWaves = 8;
 constexpr int kTapThreads = kTapWaves * kWave;
-#ifndef DSC_TAP_RING
-#define DSC_TAP_RING 2
+// Register rings of x and dy, in steps.  dy's is the deeper one: a step
+// reads dy of the next step too, so with 4 slots that load has been in
+// flight for about 3 steps; x's 2 slots keep it in flight for half a step.
+// The walk unrolls kTapRing steps (a multiple of both and of the pair).
+#ifndef DSC_TAP_RING_X
+#define DSC_TAP_RING_X 2
 #endif
-constexpr int kTapRing = DSC_TAP_RING;  // register ring of x and dy, in steps
+#ifndef DSC_TAP_RING_G
+#define DSC_TAP_RING_G 2
+#endif
+constexpr int kTapRingX = DSC_TAP_RING_X;
+constexpr int kTapRingG = DSC_TAP_RING_G;
+constexpr int kTapRing = kTapRingX > kTapRingG ? kTapRingX : kTapRingG;
+static_assert(kTapRing % kTapRingX == 0 && kTapRing % kTapRingG == 0 && kTapRing % 2 == 0, "ring depths");
 
 template <int V> struct HalfTag { static constexpr int value = V; };
 
 template <int W>
 struct TapLds {
-    static constexpr int KH = (W + 1) / 2;  // taps of the first wave of a slice
+    static constexpr int KP = (W + 1) / 2;  // pairs of taps (the K groups of dz's products)
     static constexpr int RP = 64;           // padded rank
     static constexpr int PZ = 2 * RP + 8;   // bytes per z row
     static constexpr int kZ = 9 * 16 * PZ;  // 8 slots of 16 rows + a copy of slot 0
-    static constexpr int PW = 72;           // bytes per token row of dwc^T (32 channels + pad)
-    static constexpr int kDwcWave = KH * 32 * PW;
+    static constexpr int PW = 40;           // bytes per token row of dwc^T (the wave's 16 channels + pad)
+    static constexpr int kDwcWave = W * 32 * PW;
     static constexpr int PD = 4 * RP + 16;  // bytes per token row of dz partials
     static constexpr int kDzWave = 32 * PD;
     static constexpr int oDwc = kZ;
@@ -79,8 +89,9 @@ struct TapLds {
 template <int W, bool ZV>
 __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_t nslices, int64_t tpb) {
     using L = TapLds<W>;
-    constexpr int KH = L::KH;
-    constexpr int P = kTapRing;
+    constexpr int P = kTapRing;    // steps per unrolled walk iteration
+    constexpr int PX = kTapRingX;  // x ring slots
+    constexpr int PG = kTapRingG;  // dy ring slots
     constexpr int RT = 4;  // 16-row rank tiles
     __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBytes];
     __shared__ uint32_t seq_words[kTapWaves][kSeqWords];
@@ -101,7 +112,9 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
     const int tok = lane & 15;
     const int q = lane >> 4;
     const int i16 = lane & 15;
-    const int64_t cbase = d0 + 8 * q;
+    // the wave's 4 channels of the lane's 8-channel chunk: the two waves of a
+    // slice take its channels 4*half .. 4*half+3 of every chunk
+    const int64_t cbase = d0 + 8 * q + 4 * half;
     const bool chan_ok = cbase < p.D;
     const int R = p.R;
     const int64_t N = p.N;
@@ -115,7 +128,7 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
     uint16_t *dxg = static_cast<uint16_t *>(p.dx);
 
     unsigned char *zring = lds;
-    unsigned char *dwcT = lds + L::oDwc + wid * L::kDwcWave;  // [tap slot][32 tokens][PW]
+    unsigned char *dwcT = lds + L::oDwc + wid * L::kDwcWave;  // [tap][32 tokens][PW]
     unsigned char *dzb = lds + L::oDz + wid * L::kDzWave;     // [32 tokens][PD]
     // dx of a pair, [32 tokens][16 chunks of 8 channels], chunk c of row r at
     // position c ^ (r & 15) (16 rows at one chunk hit distinct banks); pair p
@@ -132,9 +145,8 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
     const __amdgpu_buffer_rsrc_t rx = make_stream(xg + nbeg * D, (N - nbeg) * D * 2);
     const __amdgpu_buffer_rsrc_t rg = make_stream(gg + nbeg * D, (N - nbeg) * D * 2);
     const __amdgpu_buffer_rsrc_t rdx = make_stream(dxg + nbeg * D, (nend - nbeg) * D * 2);
-    const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
-    auto fetch_x = [&](int64_t step) { return buf_load16<kLrNtX>(rx, xoff + (uint32_t)step * act_step); };
-    auto fetch_g = [&](int64_t step) { return buf_load16<kLrNtG>(rg, xoff + (uint32_t)step * act_step); };
+    auto fetch_x = [&](int64_t step) { return buf_load8<kLrNtX>(rx, xoff + (uint32_t)step * act_step); };
+    auto fetch_g = [&](int64_t step) { return buf_load8<kLrNtG>(rg, xoff + (uint32_t)step * act_step); };
     // the pair's dx tile to memory as whole rows of the block's 128 channels
     // (256 bytes, two cache lines): thread = row tid/16, position tid%16
     uint32_t dxt_off;
@@ -181,19 +193,19 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
     write_zp(1, fetch_zp(1));
     uint2 zpf = fetch_zp(2);
 
-    // ---- register rings: x step s in slot s % P (read with slot s-1), dy
-    // step s in slot s % P (read with slot s+1)
-    uint4 xr[P], gr[P];
+    // ---- register rings: x step s in slot s % PX (read with slot s-1), dy
+    // step s in slot s % PG (read with slot s+1)
+    uint2 xr[PX], gr[PG];
 #pragma unroll
-    for (int j = 0; j < P - 1; ++j) xr[j] = fetch_x(j);
-    xr[P - 1] = zero4;  // step -1: only its last W-1 tokens are read
+    for (int j = 0; j < PX - 1; ++j) xr[j] = fetch_x(j);
+    xr[PX - 1] = make_uint2(0u, 0u);  // step -1: only its last W-1 tokens are read
     {
         const int64_t n = nbeg - 16 + tok;
         if (n >= 0 && n < N && tok >= 16 - (W - 1) && chan_ok)
-            xr[P - 1] = *reinterpret_cast<const uint4 *>(xg + n * D + cbase);
+            xr[PX - 1] = *reinterpret_cast<const uint2 *>(xg + n * D + cbase);
     }
 #pragma unroll
-    for (int j = 0; j < P; ++j) gr[j] = fetch_g(j);
+    for (int j = 0; j < PG; ++j) gr[j] = fetch_g(j);
     lds_barrier();  // the ring's first two pairs
 
     // dz atomics: this thread's rank (= lane) and tokens wid + 8*it of a pair
@@ -201,16 +213,14 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
 
     auto walk = [&](auto half_tag) {
         constexpr int HF = decltype(half_tag)::value;
-        constexpr int K0 = HF * KH;                  // first tap of this wave
-        constexpr int NK = HF == 0 ? KH : W - KH;    // taps K0 .. K0+NK-1
-
-        // U operands kept in registers for the whole walk:
-        //   ua (dx, every tap, the wave's channel half HF of the slice): rows
-        //     channel d0 + 8(i>>2) + 4HF + (i&3), K rank 32c + 8(lane>>4) + e
-        //   ub (dz, the wave's taps): rows rank 16rt + (lane&15), K channel
-        //     d0 + 8(lane>>4) + e
+        // U operands kept in registers for the whole walk (the wave's channels
+        // d0 + 8c' + 4HF + j, j < 4, of every chunk c'):
+        //   ua (dx): rows channel d0 + 8(i>>2) + 4HF + (i&3), K rank 32c + 8(lane>>4) + e
+        //   ub (dz, taps 2kp and 2kp+1): rows rank 16rt + (lane&15), K element e of
+        //     lane group q = lane>>4: channel d0 + 8q + 4HF + (e&3), tap 2kp + (e>>2)
+        constexpr int KP = L::KP;
         bf16x8 ua[W][2];
-        bf16x8 ub[NK][RT];
+        bf16x8 ub[KP][RT];
         {
             const int64_t ch = d0 + 8 * (i16 >> 2) + 4 * HF + (i16 & 3);
 #pragma unroll
@@ -229,38 +239,31 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const int r = 16 * rt + i16;
-            uint32_t h[4 * W];
             const bool ok = r < R && chan_ok;  // else read U's start, zeroed by the mask
-            const uint32_t m = keep_mask(ok);
-            const uint4 *src = reinterpret_cast<const uint4 *>(U + (ok ? ((int64_t)r * D + cbase) * W : 0));
+            const uint16_t m = (uint16_t)keep_mask(ok);
+            uint16_t v[4][W];
 #pragma unroll
-            for (int j = 0; j < W; ++j) {
-                const uint4 v = src[j];
-                h[4 * j] = v.x & m; h[4 * j + 1] = v.y & m;
-                h[4 * j + 2] = v.z & m; h[4 * j + 3] = v.w & m;
-            }
+            for (int j = 0; j < 4; ++j) load_taps<W>(U + (ok ? ((int64_t)r * D + cbase + j) * W : 0), v[j]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
+            for (int kp = 0; kp < KP; ++kp)
 #pragma unroll
-                for (int j = 0; j < NK; ++j) {
-                    const int idx = e * W + K0 + j;  // element: channel e, tap K0 + j
-                    const uint16_t v = (uint16_t)((idx & 1) ? (h[idx >> 1] >> 16) : (h[idx >> 1] & 0xffffu));
-                    ub[j][rt][e] = __builtin_bit_cast(__bf16, v);
+                for (int e = 0; e < 8; ++e) {
+                    const int k = 2 * kp + (e >> 2);
+                    ub[kp][rt][e] = __builtin_bit_cast(__bf16, (uint16_t)(k < W ? (v[e & 3][k] & m) : 0u));
                 }
         }
-        floatx4 du[NK][2][RT];
+        floatx4 du[W][RT];  // dU_k^T of the wave's 16 channels (rows) and 16-rank tiles
 #pragma unroll
-        for (int j = 0; j < NK; ++j)
+        for (int k = 0; k < W; ++k)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) du[j][ct][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int rt = 0; rt < RT; ++rt) du[k][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
         for (int64_t s0 = 0; s0 < nsteps; s0 += P) {
             const int zs0 = (int)(s0 & 7);  // ring slot of step s0 (0 or 4)
 #pragma unroll
             for (int i = 0; i < P; ++i) {
-                const int cur = i, prv = (i + P - 1) % P, nxt = (i + 1) % P;
+                const int xcur = i % PX, xprv = (i + PX - 1) % PX;  // x slots of steps s, s-1
+                const int gcur = i % PG, gnxt = (i + 1) % PG;       // dy slots of steps s, s+1
                 const int ps = i & 1;
                 const int64_t s = s0 + i;
                 const int64_t nstep = nbeg + 16 * s;
@@ -294,37 +297,41 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
                 const unsigned char *zst = zring + 16 * (zs0 + i) * L::PZ;  // rows of step s
                 auto dwc_part = [&](auto mask_tag) {
                     constexpr bool M = decltype(mask_tag)::value;
-                    const uint32_t gc[4] = {gr[cur].x, gr[cur].y, gr[cur].z, gr[cur].w};
-                    const uint32_t xc[4] = {xr[cur].x, xr[cur].y, xr[cur].z, xr[cur].w};
-                    const uint32_t xp[4] = {xr[prv].x, xr[prv].y, xr[prv].z, xr[prv].w};
-                    // dwc of the wave's taps: dz^T partial on the matrix cores, dwc^T staged for dU
+                    const uint32_t gc[2] = {gr[gcur].x, gr[gcur].y};
+                    const uint32_t xc[2] = {xr[xcur].x, xr[xcur].y};
+                    const uint32_t xp[2] = {xr[xprv].x, xr[xprv].y};
+                    // dwc of every tap for the wave's channels: staged as dwc^T for dU,
+                    // and by pairs of taps the B operand of dz^T += U dwc
                     const bool own = n < nend;  // tokens outside this block's range contribute nothing
                     floatx4 cz[RT];
 #pragma unroll
                     for (int rt = 0; rt < RT; ++rt) cz[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int j = 0; j < NK; ++j) {
-                        const int k = K0 + j;
-                        uint32_t xk[4];
-                        if (k == 0) {
+                    for (int kp = 0; kp < KP; ++kp) {
+                        uint32_t b4[4] = {0u, 0u, 0u, 0u};  // taps 2kp and 2kp+1 (zero past W)
 #pragma unroll
-                            for (int i2 = 0; i2 < 4; ++i2) xk[i2] = xc[i2];
-                        } else {
-                            shift_back4<W>(k, xc, xp, xk);
-                        }
-                        uint32_t dw[4];
+                        for (int kk = 0; kk < 2; ++kk) {
+                            const int k = 2 * kp + kk;
+                            if (k >= W) continue;
+                            uint32_t xk[2];
+                            if (k == 0) {
+                                xk[0] = xc[0];
+                                xk[1] = xc[1];
+                            } else {
+                                shift_back2<W>(k, xc, xp, xk);
+                            }
 #pragma unroll
-                        for (int i2 = 0; i2 < 4; ++i2) {
-                            const uint32_t xv = (!M || (own && k <= back)) ? xk[i2] : 0u;
-                            dw[i2] = pack_bf16x2(bf16_lo(gc[i2]) * bf16_lo(xv), bf16_hi(gc[i2]) * bf16_hi(xv));
+                            for (int i2 = 0; i2 < 2; ++i2) {
+                                const uint32_t xv = (!M || (own && k <= back)) ? xk[i2] : 0u;
+                                b4[2 * kk + i2] = pack_bf16x2(bf16_lo(gc[i2]) * bf16_lo(xv), bf16_hi(gc[i2]) * bf16_hi(xv));
+                            }
+                            *reinterpret_cast<uint2 *>(dwcT + k * 32 * L::PW + (16 * ps + tok) * L::PW + 8 * q) =
+                                make_uint2(b4[2 * kk], b4[2 * kk + 1]);
                         }
-                        const bf16x8 b = bf16x8_from_u32(dw);
+                        const bf16x8 b = bf16x8_from_u32(b4);
 #pragma unroll
                         for (int rt = 0; rt < RT; ++rt)
-                            cz[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ub[j][rt], b, cz[rt], 0, 0, 0);
-                        uint2 *d = reinterpret_cast<uint2 *>(dwcT + j * 32 * L::PW + (16 * ps + tok) * L::PW + 16 * q);
-                        d[0] = make_uint2(dw[0], dw[1]);
-                        d[1] = make_uint2(dw[2], dw[3]);
+                            cz[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ub[kp][rt], b, cz[rt], 0, 0, 0);
                     }
                     // dz partials (rows r = 16rt + 4q + jj, column = token) for the block's sum
 #pragma unroll
@@ -335,8 +342,8 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
                 };
                 auto dx_part = [&](auto mask_tag) {
                     constexpr bool M = decltype(mask_tag)::value;
-                    const uint32_t gc[4] = {gr[cur].x, gr[cur].y, gr[cur].z, gr[cur].w};
-                    const uint32_t gn[4] = {gr[nxt].x, gr[nxt].y, gr[nxt].z, gr[nxt].w};
+                    const uint32_t gc[2] = {gr[gcur].x, gr[gcur].y};
+                    const uint32_t gn[2] = {gr[gnxt].x, gr[gnxt].y};
                     // dx of the wave's 4 channels of every 8-channel chunk: the sum over
                     // every tap of w[n+k] dy[n+k] (rho entering as the accumulator of tap
                     // 0's product), into the pair's dx tile
@@ -353,13 +360,12 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
                         }
                         uint32_t gk[2];
                         if (k == 0) {
-                            gk[0] = gc[2 * HF];
-                            gk[1] = gc[2 * HF + 1];
+                            gk[0] = gc[0];
+                            gk[1] = gc[1];
                         } else {
-                            uint32_t g4[4];
-                            shift_ahead4<W>(k, gc, gn, g4);
-                            gk[0] = (!M || k < ahead) ? g4[2 * HF] : 0u;
-                            gk[1] = (!M || k < ahead) ? g4[2 * HF + 1] : 0u;
+                            shift_ahead2<W>(k, gc, gn, gk);
+                            gk[0] = (!M || k < ahead) ? gk[0] : 0u;
+                            gk[1] = (!M || k < ahead) ? gk[1] : 0u;
                         }
                         const float c0 = k == 0 ? p.rho : 0.f;
                         floatx4 cw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua[k][0], zb[0],
@@ -375,9 +381,9 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
                         make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
                 };
                 if (fast) dwc_part(MaskTag<false>{}); else dwc_part(MaskTag<true>{});
-                xr[prv] = fetch_x(s + P - 1);  // x of step s-1 is no longer read
+                xr[xprv] = fetch_x(s + PX - 1);  // x of step s-1 is no longer read
                 if (fast) dx_part(MaskTag<false>{}); else dx_part(MaskTag<true>{});
-                gr[cur] = fetch_g(s + P);      // dy of step s is no longer read
+                gr[gcur] = fetch_g(s + PG);      // dy of step s is no longer read
 
                 if (ps == 1) {
                     lds_barrier();  // the pair's dx tile, dz partials and dwc^T rows of every wave
@@ -395,18 +401,15 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
                         zb[rt] = __builtin_bit_cast(bf16x8, make_uint4(h[0].x, h[0].y, h[1].x, h[1].y));
                     }
 #pragma unroll
-                    for (int j = 0; j < NK; ++j) {
+                    for (int k = 0; k < W; ++k) {
+                        uint2 h[2];
 #pragma unroll
-                        for (int ct = 0; ct < 2; ++ct) {
-                            uint2 h[2];
+                        for (int hh = 0; hh < 2; ++hh)
+                            h[hh] = lds_read_tr(dwcT + k * 32 * L::PW + (trow + 4 * hh) * L::PW + 2 * tcol);
+                        const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(h[0].x, h[0].y, h[1].x, h[1].y));
 #pragma unroll
-                            for (int hh = 0; hh < 2; ++hh)
-                                h[hh] = lds_read_tr(dwcT + j * 32 * L::PW + (trow + 4 * hh) * L::PW + 2 * (16 * ct + tcol));
-                            const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(h[0].x, h[0].y, h[1].x, h[1].y));
-#pragma unroll
-                            for (int rt = 0; rt < RT; ++rt)
-                                du[j][ct][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, zb[rt], du[j][ct][rt], 0, 0, 0);
-                        }
+                        for (int rt = 0; rt < RT; ++rt)
+                            du[k][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, zb[rt], du[k][rt], 0, 0, 0);
                     }
                     // dz of the pair: the 8 waves' partials summed, one fp32 atomic per
                     // (token, rank) below R and inside the block's range, each at an
@@ -443,16 +446,13 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
         __syncthreads();  // every wave is done with the loop's LDS regions
         float *dus = reinterpret_cast<float *>(lds + slice * L::kDuSlice);
 #pragma unroll
-        for (int j = 0; j < NK; ++j)
+        for (int k = 0; k < W; ++k)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int rt = 0; rt < RT; ++rt) {
+                const int r = 16 * rt + i16;
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    const int r = 16 * rt + i16;
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-                        dus[r * L::kDuPitch + (16 * ct + 4 * q + jj) * W + K0 + j] = du[j][ct][rt][jj];
-                }
+                for (int jj = 0; jj < 4; ++jj) dus[r * L::kDuPitch + (8 * q + 4 * HF + jj) * W + k] = du[k][rt][jj];
+            }
     };
     if (half == 0) walk(HalfTag<0>{}); else walk(HalfTag<1>{});
     __syncthreads();
