@@ -668,7 +668,28 @@ def main() -> int:
         "read_only": (c4.bytes("bwd"), 0),
         "write_only": (0, c4.x.numel() * 2)}, 10)
     out["copy_same_bytes_GBps"] = round(copy_rate(torch, dom["algorithmic_bytes"], flush), 1)
-    del cases, c4
+
+    # the low-rank layer of the ~2B block followed by the rotary embedding of
+    # its query and key channels ([0, 4096), heads of 128), forward and
+    # backward, beside the layer alone, in one loop
+    log("fused rotary embedding, ~2B low-rank")
+    l5 = cases[1]
+    hd2, rot2 = 128, 4096
+    table2 = torch.empty(l5.wl.N, hd2 // 2, 2, dtype=torch.float32, device="cuda")
+    binding.dsc_rope_table(table2, base=10000.0)
+    lkw2 = dict(W=l5.wl.W, rot=rot2, head_dim=hd2, table=table2, cu_seqlens=l5.cu, residual=l5.wl.residual)
+    tr2 = interleaved_s(torch, [
+        lambda: binding.dsc_lowrank_rope_fwd(l5.x, l5.z, l5.U, l5.y, **lkw2),
+        lambda: binding.dsc_lowrank_rope_bwd(l5.x, l5.z, l5.U, l5.dy, l5.dx, l5.dz, l5.dU, l5.ws, **lkw2),
+        l5.fwd, l5.bwd], max(5, K // 2))
+    b2 = l5.bytes("fwd") + l5.bytes("bwd")
+    rope2b = {"workload": f"{l5.wl.name} + rotary embedding of channels [0, {rot2}), heads of {hd2}",
+              "fwd_us": round(tr2[0] * 1e6, 1), "bwd_us": round(tr2[1] * 1e6, 1),
+              "GBps": round(b2 / (tr2[0] + tr2[1]) / 1e9, 1),
+              "frac_hbm_peak": round(b2 / (tr2[0] + tr2[1]) / 1e9 / PEAK_HBM_GBPS, 4),
+              "layer_alone_fwd_us": round(tr2[2] * 1e6, 1), "layer_alone_bwd_us": round(tr2[3] * 1e6, 1),
+              "unfused_extra_bytes": 2 * rot2 * l5.wl.N * l5.x.element_size()}
+    del cases, c4, l5, table2
     torch.cuda.empty_cache()
 
     # the QKV ~150M step (head-wise H=64 with residual, low-rank R=32) measured the same way
@@ -806,6 +827,7 @@ def main() -> int:
             "frac_hbm_peak": round(b / (tr[0] + tr[1]) / 1e9 / PEAK_HBM_GBPS, 4),
             "layer_alone_fwd_us": round(tr[2] * 1e6, 1), "layer_alone_bwd_us": round(tr[3] * 1e6, 1),
             "unfused_extra_bytes": 2 * rot * c.wl.N * c.x.element_size()}
+    rope["lowrank_2b"] = rope2b
     out["rope_fused"] = rope
     del table
 

@@ -180,12 +180,15 @@ hipError_t lowrank_zero(float *p, int64_t n, hipStream_t s);
 hipError_t lowrank_zero2(float *a, int64_t na, float *b, int64_t nb, hipStream_t s);
 hipError_t lowrank_round_bf16(const float *src, uint16_t *dst, int64_t n, hipStream_t s);
 // Backward of the bf16 low-rank layer for 32 < R <= 64 and 2 <= W <= 4 with
-// the taps of each 32-channel slice split over two waves (lowrank_taps.hip);
-// workspace as lowrank_bwd's (an fp32 (N, R) dz accumulator).
-// det: the reproducible split (dz per channel group and dU per token chunk in
-// regions of dz_acc, lowrank_bwd_taps_det_workspace bytes, added in order).
+// each 32-channel slice split between two waves by channels
+// (lowrank_taps.hip); workspace as lowrank_bwd's (an fp32 (N, R) dz
+// accumulator).  det: the reproducible split (dz per channel group and dU per
+// token chunk in regions of dz_acc, lowrank_bwd_taps_det_workspace bytes,
+// added in order).  _rope: the layer followed by the rotary embedding (p.rope,
+// p.rot, p.hd, p.npos set), fast split only.
 bool lowrank_bwd_taps_supported(Dtype dt, int64_t D, int32_t W, int32_t R);
 hipError_t lowrank_bwd_taps(const LrProblem &p, hipStream_t s, bool det);
+hipError_t lowrank_bwd_taps_rope(const LrProblem &p, hipStream_t s);
 size_t lowrank_bwd_taps_det_workspace(int64_t N, int64_t D, int32_t W, int32_t R);
 // dst = sum over parts j (ascending) of src[j*stride + i], as fp32 or rounded to bf16
 hipError_t lowrank_sum_parts(const float *src, int64_t nparts, int64_t stride, float *dst_f32, uint16_t *dst_bf16,

@@ -1324,7 +1324,11 @@ hipError_t rope_bwd_w(const LrProblem &pr, hipStream_t st) {
     if (pr.dtype == Dtype::F32) return generic_bwd<F32, W, true>(pr, st);
     if (!bwd_uses_mfma(Dtype::BF16, pr.D, W, pr.R)) return generic_bwd<BF16, W, true>(pr, st);
     if constexpr (W <= 4) {
-        if ((pr.R + 31) / 32 == 2) return mfma_bwd<W, 2, true>(pr, st, false);
+        if ((pr.R + 31) / 32 == 2) {
+            if (DSC_LR_TAPS && lowrank_bwd_taps_supported(Dtype::BF16, pr.D, W, pr.R))
+                return lowrank_bwd_taps_rope(pr, st);
+            return mfma_bwd<W, 2, true>(pr, st, false);
+        }
     }
     return mfma_bwd<W, 1, true>(pr, st, false);
 }

@@ -85,8 +85,12 @@ struct TapLds {
     static_assert(kBytes + kTapWaves * 4 * kSeqWords <= 160 * 1024, "the block must fit the LDS of a CU");
 };
 
-// ZV: R % 4 == 0, z rows move as 8-byte vectors.
-template <int W, bool ZV>
+// ZV: R % 4 == 0, z rows move as 8-byte vectors.  ROPE: the layer is followed
+// by the rotary embedding of channels [0, p.rot) (heads of p.hd), so dy is
+// turned back at each token's position before use: each step's dy as it is
+// first read (the dx part of the step before), with its cos, sin from the
+// table loaded at that step's start.
+template <int W, bool ZV, bool ROPE>
 __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_t nslices, int64_t tpb) {
     using L = TapLds<W>;
     constexpr int P = kTapRing;    // steps per unrolled walk iteration
@@ -138,6 +142,28 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
 
     StartBits<kSeqWords> starts;
     starts.build(seq_words[wid], p.seq, N, nbeg - 32, lane);
+    SeqPos sp{0};
+    if constexpr (ROPE) {
+        int64_t s_, e_;
+        p.seq.find(nbeg < N ? nbeg : N - 1, s_, e_);
+        sp.start = s_;
+    }
+    // dy of a step turned back by the rotation of its token's position (pairs
+    // (4j, 4j+1) of the wave's 4 channels; groups of 4 lie wholly inside or
+    // outside [0, rot) since rot is a multiple of the head size, a multiple of 8)
+    const bool rope_lane = ROPE && chan_ok && cbase < p.rot;
+    auto turn_back = [&](uint2 &v, const float (&cs)[4]) {
+        if (rope_lane) {
+            uint32_t w2[2] = {v.x, v.y};
+#pragma unroll
+            for (int i2 = 0; i2 < 2; ++i2) {
+                const float a = bf16_lo(w2[i2]), b = bf16_hi(w2[i2]);
+                const float c = cs[2 * i2], sn = cs[2 * i2 + 1];
+                w2[i2] = pack_bf16x2(a * c + b * sn, b * c - a * sn);
+            }
+            v = make_uint2(w2[0], w2[1]);
+        }
+    };
 
     // ---- x, dy and dx streams of the wave's slice, as in lowrank.hip
     const uint32_t act_step = (uint32_t)(16 * D * 2);
@@ -206,6 +232,11 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
     }
 #pragma unroll
     for (int j = 0; j < PG; ++j) gr[j] = fetch_g(j);
+    if constexpr (ROPE) {  // step 0's dy
+        float cs[4];
+        rope_cs<4>(p, sp.pos_and_advance(starts, nbeg, tok), cbase, cs);
+        turn_back(gr[0], cs);
+    }
     lds_barrier();  // the ring's first two pairs
 
     // dz atomics: this thread's rank (= lane) and tokens wid + 8*it of a pair
@@ -270,6 +301,8 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
                 const int64_t n = nstep + tok;
 
                 unsigned char *dxtp = dxt + ((s >> 1) & 1) * L::kDxt;  // this pair's dx tile
+                float csn[4];  // ROPE: cos, sin of the next step's tokens (table load issued here)
+                if constexpr (ROPE) rope_cs<4>(p, sp.pos_and_advance(starts, nstep + 16, tok), cbase, csn);
                 if (ps == 0) {  // z rows two pairs ahead into the ring, the next pair fetched
                     write_zp(s / 2 + 2, zpf);
                     zpf = fetch_zp(s / 2 + 3);
@@ -382,6 +415,7 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
                 };
                 if (fast) dwc_part(MaskTag<false>{}); else dwc_part(MaskTag<true>{});
                 xr[xprv] = fetch_x(s + PX - 1);  // x of step s-1 is no longer read
+                if constexpr (ROPE) turn_back(gr[gnxt], csn);  // the next step's dy, first read here
                 if (fast) dx_part(MaskTag<false>{}); else dx_part(MaskTag<true>{});
                 gr[gcur] = fetch_g(s + PG);      // dy of step s is no longer read
 
@@ -486,10 +520,10 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
     }
 }
 
-template <int W>
+template <int W, bool ROPE>
 const void *taps_kernel(bool zv) {
-    return zv ? reinterpret_cast<const void *>(&lr_bwd_taps<W, true>)
-              : reinterpret_cast<const void *>(&lr_bwd_taps<W, false>);
+    return zv ? reinterpret_cast<const void *>(&lr_bwd_taps<W, true, ROPE>)
+              : reinterpret_cast<const void *>(&lr_bwd_taps<W, false, ROPE>);
 }
 
 // Work split: ngroups blocks of 4 channel slices across D, token chunks of
@@ -507,7 +541,7 @@ TapPlan taps_plan(int64_t N, int64_t D, int64_t slots) {
 
 size_t det_dz_floats(const TapPlan &pl, int64_t N, int R) { return (((size_t)pl.ngroups * N * R + 3) / 4) * 4; }
 
-template <int W>
+template <int W, bool ROPE>
 hipError_t taps_bwd(const LrProblem &pr, hipStream_t st, bool det) {
     LrParams p = make_params<BF16>(pr);
     const bool zv = p.R % 4 == 0;
@@ -515,8 +549,8 @@ hipError_t taps_bwd(const LrProblem &pr, hipStream_t st, bool det) {
     const int64_t nz = p.N * p.R;
     int64_t slots = kDetSlots;  // the reproducible split: one block per CU of a 256-CU device
     if (!det) {
-        static const int bpc_v = blocks_per_cu(taps_kernel<W>(true), kTapThreads);
-        static const int bpc_g = blocks_per_cu(taps_kernel<W>(false), kTapThreads);
+        static const int bpc_v = blocks_per_cu(taps_kernel<W, ROPE>(true), kTapThreads);
+        static const int bpc_g = blocks_per_cu(taps_kernel<W, ROPE>(false), kTapThreads);
         slots = (int64_t)device_cus() * (zv ? bpc_v : bpc_g);
     }
     const TapPlan pl = taps_plan(p.N, p.D, slots);
@@ -534,9 +568,9 @@ hipError_t taps_bwd(const LrProblem &pr, hipStream_t st, bool det) {
     const dim3 grid((unsigned)(pl.tchunks * pl.ngroups));
     const int64_t nslices = (p.D + 31) / 32;
     if (zv)
-        hipLaunchKernelGGL((lr_bwd_taps<W, true>), grid, dim3(kTapThreads), 0, st, p, nslices, pl.len);
+        hipLaunchKernelGGL((lr_bwd_taps<W, true, ROPE>), grid, dim3(kTapThreads), 0, st, p, nslices, pl.len);
     else
-        hipLaunchKernelGGL((lr_bwd_taps<W, false>), grid, dim3(kTapThreads), 0, st, p, nslices, pl.len);
+        hipLaunchKernelGGL((lr_bwd_taps<W, false, ROPE>), grid, dim3(kTapThreads), 0, st, p, nslices, pl.len);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (det) {
@@ -556,9 +590,18 @@ bool lowrank_bwd_taps_supported(Dtype dt, int64_t D, int32_t W, int32_t R) {
 
 hipError_t lowrank_bwd_taps(const LrProblem &pr, hipStream_t st, bool det) {
     switch (pr.W) {
-        case 2: return taps_bwd<2>(pr, st, det);
-        case 3: return taps_bwd<3>(pr, st, det);
-        case 4: return taps_bwd<4>(pr, st, det);
+        case 2: return taps_bwd<2, false>(pr, st, det);
+        case 3: return taps_bwd<3, false>(pr, st, det);
+        case 4: return taps_bwd<4, false>(pr, st, det);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t lowrank_bwd_taps_rope(const LrProblem &pr, hipStream_t st) {
+    switch (pr.W) {
+        case 2: return taps_bwd<2, true>(pr, st, false);
+        case 3: return taps_bwd<3, true>(pr, st, false);
+        case 4: return taps_bwd<4, true>(pr, st, false);
         default: return hipErrorInvalidValue;
     }
 }

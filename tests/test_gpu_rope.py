@@ -184,6 +184,11 @@ LRP_CASES = [
     ("bf16", 1, 130, 256, 8, 8, 32, 256, True, (1, 40)),
     ("bf16", 2, 65, 2304, 4, 32, 64, 1536, False, None),   # the QKV ~150M layout at a short length
     ("bf16", 1, 400, 6144, 4, 64, 128, 4096, False, (1, 150)),  # the QKV ~2B layout, packed
+    # two waves per 32-channel slice (33 <= R <= 64, W = 2..4): a partial last
+    # slice with the rotation ending inside the block, and z rows gathered
+    # (R % 4 != 0) with every channel rotated
+    ("bf16", 2, 333, 136, 4, 40, 8, 64, True, (1, 50)),
+    ("bf16", 1, 300, 96, 2, 45, 16, 96, False, (1, 80)),
     ("bf16", 1, 1, 16, 3, 4, 8, 8, False, None),           # one token
     # several token walks per channel pair, walks starting inside a sequence
     ("bf16", 1, 4100, 64, 3, 36, 16, 64, True, (1, 700)),
