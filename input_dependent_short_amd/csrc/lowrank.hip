@@ -1215,8 +1215,8 @@ hipError_t mfma_bwd(const LrProblem &pr, hipStream_t st, bool det) {
 // Which bf16 shapes compute dz in launches of their own (split backward):
 // the matrix-core backward then runs without dz, so its blocks exchange
 // nothing and add no dz atomics.
-// Whether ranks 33..64 at W = 2..4 take the backward with the taps of a
-// slice split over two waves (lowrank_taps.hip).
+// Whether ranks 33..64 at W = 2..4 take the backward with each 32-channel
+// slice split between two waves by channels (lowrank_taps.hip).
 #ifndef DSC_LR_TAPS
 #define DSC_LR_TAPS 1
 #endif
