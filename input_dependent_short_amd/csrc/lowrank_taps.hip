@@ -47,10 +47,10 @@ namespace {
 
 constexpr int kTapWaves = 8;
 constexpr int kTapThreads = kTapWaves * kWave;
-// Register rings of x and dy, in steps.  dy's is the deeper one: a step
-// reads dy of the next step too, so with 4 slots that load has been in
-// flight for about 3 steps; x's 2 slots keep it in flight for half a step.
-// The walk unrolls kTapRing steps (a multiple of both and of the pair).
+// Register rings of x and dy, in steps (each load is in flight for about half
+// a step with 2 slots; with 4 slots for either, the walk unrolls 4 steps and
+// the W = 4 instances spill inside the loop).  The walk unrolls kTapRing
+// steps, a multiple of both depths and of the 2-step pair.
 #ifndef DSC_TAP_RING_X
 #define DSC_TAP_RING_X 2
 #endif
@@ -148,9 +148,10 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
         p.seq.find(nbeg < N ? nbeg : N - 1, s_, e_);
         sp.start = s_;
     }
-    // dy of a step turned back by the rotation of its token's position (pairs
-    // (4j, 4j+1) of the wave's 4 channels; groups of 4 lie wholly inside or
-    // outside [0, rot) since rot is a multiple of the head size, a multiple of 8)
+    // dy of a step turned back by the rotation of its token's position (the
+    // channel pairs (cbase, cbase+1) and (cbase+2, cbase+3); a group of 4 lies
+    // wholly inside or outside [0, rot) since rot is a multiple of the head
+    // size, itself a multiple of 8)
     const bool rope_lane = ROPE && chan_ok && cbase < p.rot;
     auto turn_back = [&](uint2 &v, const float (&cs)[4]) {
         if (rope_lane) {
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(kTapThreads, 1) void lr_bwd_taps(LrParams p, int64_
             for (int rt = 0; rt < RT; ++rt) du[k][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
         for (int64_t s0 = 0; s0 < nsteps; s0 += P) {
-            const int zs0 = (int)(s0 & 7);  // ring slot of step s0 (0 or 4)
+            const int zs0 = (int)(s0 & 7);  // ring slot of step s0 (even)
 #pragma unroll
             for (int i = 0; i < P; ++i) {
                 const int xcur = i % PX, xprv = (i + PX - 1) % PX;  // x slots of steps s, s-1
